@@ -1,0 +1,253 @@
+"""Pins of the oracle's attention, MoE, self-conditioning, encoder and step.
+
+Pinned against brute-force loops on tiny shapes (written independently of the
+vectorised oracle), closed forms (all keys equal -> mean of V; one key -> V;
+top_k = E -> the dense softmax mixture; one-hot / uniform probabilities in
+self-conditioning), GeLU's textbook values, and structural identities of the
+method (prefill + commit == prefill of the concatenation; bidirectional step is
+permutation-equivariant without positional encoding; causal queries ignore
+later keys).
+"""
+import math
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import synthetic
+from oracle import model as M
+
+
+def brute_attention(q, k, v, q_pos0, causal):
+    Hq, Mq, hd = q.shape
+    Hkv, L, _ = k.shape
+    out = np.zeros_like(q)
+    for j in range(Hq):
+        kv = j * Hkv // Hq
+        for i in range(Mq):
+            scores = []
+            for t in range(L):
+                if causal and t > q_pos0 + i:
+                    continue
+                s = 0.0
+                for c in range(hd):
+                    s += q[j, i, c] * k[kv, t, c]
+                scores.append((t, s / math.sqrt(hd)))
+            mx = max(s for _, s in scores)
+            w = [(t, math.exp(s - mx)) for t, s in scores]
+            z = sum(e for _, e in w)
+            for t, e in w:
+                for c in range(hd):
+                    out[j, i, c] += e / z * v[kv, t, c]
+    return out
+
+
+@given(seed=st.integers(0, 10**6), Hkv=st.sampled_from([1, 2]), g=st.sampled_from([1, 2]),
+       Mq=st.integers(1, 6), past=st.integers(0, 8), hd=st.sampled_from([1, 4, 8]), causal=st.booleans())
+@settings(max_examples=60, deadline=None)
+def test_attention_brute_force(seed, Hkv, g, Mq, past, hd, causal):
+    rng = np.random.default_rng(seed)
+    Hq = Hkv * g
+    L = past + Mq
+    q = rng.normal(size=(Hq, Mq, hd))
+    k = rng.normal(size=(Hkv, L, hd)) * 2
+    v = rng.normal(size=(Hkv, L, hd))
+    np.testing.assert_allclose(M.attention(q, k, v, past, causal), brute_attention(q, k, v, past, causal),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_attention_equal_keys_gives_mean_of_values():
+    rng = np.random.default_rng(0)
+    q = rng.normal(size=(4, 5, 8))
+    k = np.repeat(rng.normal(size=(2, 1, 8)), 9, axis=1)
+    v = rng.normal(size=(2, 9, 8))
+    out = M.attention(q, k, v, 4, causal=False)
+    for j in range(4):
+        np.testing.assert_allclose(out[j], np.broadcast_to(v[j // 2].mean(axis=0), (5, 8)), atol=1e-13)
+
+
+def test_attention_single_key_and_causal_first_query():
+    rng = np.random.default_rng(1)
+    q = rng.normal(size=(2, 3, 4))
+    k = rng.normal(size=(2, 3, 4))
+    v = rng.normal(size=(2, 3, 4))
+    out = M.attention(q[:, :1], k[:, :1], v[:, :1], 0, causal=False)
+    np.testing.assert_allclose(out[:, 0], v[:, 0], atol=1e-15)
+    out = M.attention(q, k, v, 0, causal=True)
+    np.testing.assert_allclose(out[:, 0], v[:, 0], atol=1e-15)  # position 0 sees only key 0
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 2] += 5.0
+    v2[:, 2] -= 3.0
+    out2 = M.attention(q, k2, v2, 0, causal=True)
+    np.testing.assert_allclose(out2[:, :2], out[:, :2], atol=0)  # later keys are invisible
+
+
+def test_gelu_textbook_values():
+    # x * Phi(x) with Phi the standard normal CDF
+    assert M.gelu(np.array(1.0)) == pytest.approx(0.8413447460685429, abs=1e-15)
+    assert M.gelu(np.array(-1.0)) == pytest.approx(-0.15865525393145707, abs=1e-15)
+    x = np.linspace(-6, 6, 101)
+    np.testing.assert_allclose(M.gelu(x) - M.gelu(-x), x, atol=1e-14)
+    assert M.gelu(np.array(0.0)) == 0.0
+
+
+def test_rms_norm_closed_form():
+    x = np.array([[3.0, 3.0, 3.0, 3.0], [1.0, -1.0, 1.0, -1.0]])
+    y = M.rms_norm(x, 1e-6)
+    np.testing.assert_allclose(y[0], 3.0 / math.sqrt(9.0 + 1e-6))
+    np.testing.assert_allclose(y[1], x[1] / math.sqrt(1.0 + 1e-6))
+
+
+TINY = dict(n_layers=2, d_model=16, n_q_heads=4, n_kv_heads=2, head_dim=4, n_experts=6, d_expert=8,
+            d_shared=12, gated=1, vocab=40, d_selfcond=10)
+
+
+def tiny_shape(top_k=2, gated=True, **kw):
+    s = dict(TINY, gated=int(gated), **kw)
+    return s, M.ModelShape(n_layers=s["n_layers"], d_model=s["d_model"], n_q_heads=s["n_q_heads"],
+                           n_kv_heads=s["n_kv_heads"], head_dim=s["head_dim"], n_experts=s["n_experts"],
+                           top_k=top_k, d_expert=s["d_expert"], d_shared=s["d_shared"], gated=gated,
+                           vocab=s["vocab"], d_selfcond=s["d_selfcond"], canvas=8)
+
+
+def brute_moe(h, lw, shape):
+    E = shape.n_experts
+    out = np.zeros_like(h)
+    for t in range(h.shape[0]):
+        r = [sum(h[t, c] * lw["wr"][e, c] for c in range(h.shape[1])) for e in range(E)]
+        mx = max(r)
+        z = sum(math.exp(x - mx) for x in r)
+        p = [math.exp(x - mx) / z for x in r]
+        chosen = []
+        for _ in range(shape.top_k):  # repeated selection of the largest, lowest index first
+            best = None
+            for e in range(E):
+                if e in chosen:
+                    continue
+                if best is None or r[e] > r[best]:
+                    best = e
+            chosen.append(best)
+        for e in chosen:
+            w = lw["experts"][e]
+            out[t] += p[e] * _brute_ffn(h[t], w, shape.gated, "")
+        out[t] += _brute_ffn(h[t], lw, shape.gated, "sh_")
+    return out
+
+
+def _brute_ffn(x, w, gated, pre):
+    up = w[pre + "up"] @ x
+    if gated:
+        g = w[pre + "gate"] @ x
+        a = np.array([0.5 * gi * (1 + math.erf(gi / math.sqrt(2))) * ui for gi, ui in zip(g, up)])
+    else:
+        a = np.array([0.5 * ui * (1 + math.erf(ui / math.sqrt(2))) for ui in up])
+    return w[pre + "down"] @ a
+
+
+@pytest.mark.parametrize("gated,top_k", [(True, 2), (False, 2), (True, 1), (True, 6)])
+def test_moe_brute_force(gated, top_k):
+    s, shape = tiny_shape(top_k=top_k, gated=gated)
+    W = synthetic.SyntheticWeights(s, seed=3, dtype="f32", sigma=0.5)
+    rng = np.random.default_rng(0)
+    h = rng.normal(size=(7, s["d_model"]))
+    y, info = M.moe(h, W["layers"][0], shape)
+    np.testing.assert_allclose(y, brute_moe(h, W["layers"][0], shape), rtol=1e-10, atol=1e-12)
+
+
+def test_moe_all_experts_is_dense_softmax_mixture():
+    s, shape = tiny_shape(top_k=6)
+    W = synthetic.SyntheticWeights(s, seed=4, dtype="f32", sigma=0.5)
+    lw = W["layers"][1]
+    h = np.random.default_rng(2).normal(size=(5, s["d_model"]))
+    p = M.softmax(h @ lw["wr"].T)
+    dense = sum(p[:, [e]] * M.ffn(h, lw["experts"][e], True) for e in range(6)) + M.ffn(h, lw, True, "sh_")
+    y, _ = M.moe(h, lw, shape)
+    np.testing.assert_allclose(y, dense, rtol=1e-12, atol=1e-13)
+
+
+def test_router_dominant_column_and_ties():
+    r = np.array([[0.0, 5.0, 5.0, 1.0, 5.0], [100.0, 1.0, 2.0, 3.0, 4.0]])
+    sel = M.topk_from_logits(r, 2)
+    assert sel[0].tolist() == [1, 2]  # ties: lowest index first
+    assert sel[1, 0] == 0
+    s, shape = tiny_shape(top_k=1)
+    W = synthetic.SyntheticWeights(s, seed=5, dtype="f32", sigma=0.5)
+    src = W["layers"][0]
+    lw = {k: src[k] for k in ("sh_gate", "sh_up", "sh_down")}
+    lw["experts"] = src["experts"]
+    hh = np.abs(np.random.default_rng(3).normal(size=(4, s["d_model"])))  # positive rows
+    lw["wr"] = np.zeros((6, s["d_model"]))
+    lw["wr"][4] = 100.0  # expert 4's logit dominates every row by >= 100
+    y, info = M.moe(hh, lw, shape)
+    assert (info["sel"][:, 0] == 4).all()
+    want = info["gates"][:, [0]] * M.ffn(hh, lw["experts"][4], True) + M.ffn(hh, lw, True, "sh_")
+    np.testing.assert_allclose(y, want, rtol=1e-12)
+
+
+def test_self_conditioning_one_hot_and_uniform():
+    s, shape = tiny_shape()
+    W = synthetic.SyntheticWeights(s, seed=6, dtype="f32", sigma=0.5)
+    V = s["vocab"]
+    p = np.zeros((3, V))
+    p[0, 7] = 1.0
+    p[1, :] = 1.0 / V
+    p[2, [1, 2]] = 0.5
+    E = W["embed"]
+    u_want = np.stack([E[7], E.mean(axis=0), 0.5 * (E[1] + E[2])])
+    sc = M.self_condition(W, p)
+    want = M.gelu(u_want @ W["sc_w1"].T) @ W["sc_w2"].T
+    np.testing.assert_allclose(sc, want, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_then_commit_equals_prefill_of_concatenation():
+    s, shape = tiny_shape()
+    W = synthetic.SyntheticWeights(s, seed=7, dtype="f32", sigma=0.3)
+    prompt = synthetic.uniform_ids(1, synthetic.TID_PROMPT, 9, s["vocab"])
+    block = synthetic.uniform_ids(2, synthetic.TID_PROMPT, 8, s["vocab"])
+    a = M.KVCache.empty(shape, 32)
+    M.encode(W, a, prompt, shape)
+    M.encode(W, a, block, shape)
+    b = M.KVCache.empty(shape, 32)
+    M.encode(W, b, np.concatenate([prompt, block]), shape)
+    c = M.KVCache.empty(shape, 32)
+    for t in np.concatenate([prompt, block]):  # token by token
+        M.encode(W, c, [t], shape)
+    assert a.length == b.length == c.length == 17
+    for l in range(shape.n_layers):
+        np.testing.assert_allclose(a.k[l], b.k[l], atol=1e-12)
+        np.testing.assert_allclose(a.v[l], b.v[l], atol=1e-12)
+        np.testing.assert_allclose(c.k[l], b.k[l], atol=1e-12)
+
+
+def test_capacity_is_enforced():
+    s, shape = tiny_shape()
+    W = synthetic.SyntheticWeights(s, seed=7, dtype="f32")
+    cache = M.KVCache.empty(shape, 10)
+    with pytest.raises(ValueError):
+        M.encode(W, cache, np.arange(11) % s["vocab"], shape)
+    assert cache.length == 0
+
+
+def test_denoise_step_is_permutation_equivariant_and_leaves_length():
+    s, shape = tiny_shape()
+    W = synthetic.SyntheticWeights(s, seed=8, dtype="f32", sigma=0.3)
+    cache = M.KVCache.empty(shape, 32)
+    M.encode(W, cache, synthetic.uniform_ids(1, synthetic.TID_PROMPT, 5, s["vocab"]), shape)
+    canvas = synthetic.uniform_ids(3, synthetic.TID_PROMPT, 8, s["vocab"])
+    perm = np.random.default_rng(0).permutation(8)
+    l1 = M.denoise_step(W, cache, canvas, None, shape)
+    l2 = M.denoise_step(W, cache, canvas[perm], None, shape)
+    np.testing.assert_allclose(l2, l1[perm], rtol=1e-10, atol=1e-12)
+    assert cache.length == 5
+
+
+def test_denoise_step_canvas_attends_bidirectionally():
+    s, shape = tiny_shape()
+    W = synthetic.SyntheticWeights(s, seed=9, dtype="f32", sigma=0.3)
+    cache = M.KVCache.empty(shape, 32)
+    canvas = synthetic.uniform_ids(4, synthetic.TID_PROMPT, 8, s["vocab"])
+    l1 = M.denoise_step(W, cache, canvas, None, shape)
+    c2 = canvas.copy()
+    c2[-1] = (c2[-1] + 1) % s["vocab"]
+    l2 = M.denoise_step(W, cache, c2, None, shape)
+    assert np.abs(l1[0] - l2[0]).max() > 1e-9  # the first position sees the last one
