@@ -1,0 +1,120 @@
+// Per-kernel timing with HIP events, for the benchmark and for tracing.
+//
+// When enabled, every launch site wrapped in a ProfScope records an event
+// before and after its kernel on the kernel's own stream. dg_profile_report
+// waits for the recorded events and returns per-kernel launch counts and
+// durations as JSON. Events come from a pool created at enable time, so the
+// timed region allocates nothing.
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dg_common.h"
+#include "prof.h"
+
+namespace dg {
+
+namespace {
+struct Pending { const char* name; hipEvent_t a, b; };
+struct ProfState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  std::vector<Pending> pending;
+};
+ProfState& state() {
+  static ProfState s;
+  return s;
+}
+}  // namespace
+
+bool prof_on() { return state().on; }
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s) {
+  ProfState& st = state();
+  if (!st.on) return;
+  std::lock_guard<std::mutex> g(st.mu);
+  if (st.next + 2 > st.pool.size()) return;  // pool exhausted: stop recording
+  a_ = st.pool[st.next++];
+  b_ = st.pool[st.next++];
+  (void)hipEventRecord(a_, stream_);
+  active_ = true;
+}
+
+ProfScope::~ProfScope() {
+  if (!active_) return;
+  (void)hipEventRecord(b_, stream_);
+  ProfState& st = state();
+  std::lock_guard<std::mutex> g(st.mu);
+  st.pending.push_back({name_, a_, b_});
+}
+
+static void destroy_pool(ProfState& st) {
+  for (hipEvent_t e : st.pool) (void)hipEventDestroy(e);
+  st.pool.clear();
+  st.pending.clear();
+  st.next = 0;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+int dg_profile_enable(int32_t on, int32_t max_launches) {
+  ProfState& st = state();
+  std::lock_guard<std::mutex> g(st.mu);
+  destroy_pool(st);
+  st.on = false;
+  if (!on) return DG_OK;
+  if (max_launches < 1 || max_launches > (1 << 22)) return fail(DG_ERR_INVALID, "max_launches out of range");
+  st.pool.resize(static_cast<size_t>(max_launches) * 2);
+  for (auto& e : st.pool) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      destroy_pool(st);
+      return hip_check(r, "hipEventCreate");
+    }
+  }
+  st.on = true;
+  return DG_OK;
+}
+
+int dg_profile_report(char* buf, size_t cap) {
+  ProfState& st = state();
+  std::lock_guard<std::mutex> g(st.mu);
+  if (buf == nullptr || cap == 0) return fail(DG_ERR_INVALID, "buffer required");
+  std::map<std::string, std::pair<long, double>> agg;
+  for (const Pending& p : st.pending) {
+    DG_HIP(hipEventSynchronize(p.b));
+    float ms = 0.f;
+    DG_HIP(hipEventElapsedTime(&ms, p.a, p.b));
+    auto& v = agg[p.name];
+    v.first += 1;
+    v.second += ms;
+  }
+  st.pending.clear();
+  st.next = 0;
+  std::string out = "{";
+  bool first = true;
+  for (auto& kv : agg) {
+    char tmp[256];
+    snprintf(tmp, sizeof tmp, "%s\"%s\": {\"count\": %ld, \"total_us\": %.3f, \"avg_us\": %.4f}", first ? "" : ", ",
+             kv.first.c_str(), kv.second.first, kv.second.second * 1e3, kv.second.second * 1e3 / kv.second.first);
+    out += tmp;
+    first = false;
+  }
+  out += "}";
+  if (out.size() + 1 > cap) return fail(DG_ERR_CAPACITY, "report buffer too small");
+  memcpy(buf, out.c_str(), out.size() + 1);
+  return DG_OK;
+}
+
+}  // extern "C"

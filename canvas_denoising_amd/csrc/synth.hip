@@ -1,0 +1,112 @@
+// Seeded synthetic inputs on the device (random-init weights, prompts,
+// planted-peak logits). No arithmetic of the denoising method lives here.
+//
+// Generator: hash64(seed, tid, i) = mix64(mix64(seed * G + tid) + (i + 1) * G)
+// with the SplitMix64 finaliser mix64 (Steele, Lea and Flood, OOPSLA 2014)
+// and G = 0x9E3779B97F4A7C15. A "normal" value is the Irwin-Hall sum of the
+// hash's four 16-bit fields minus 131070, times float(sigma / sqrt((2^32 - 1) / 3))
+// in one correctly rounded float multiply; bf16 rounds that to nearest-even.
+// A uniform id is ((hash >> 32) * V) >> 32. The host generator used by the
+// tests computes the same bits.
+#include <math.h>
+
+#include <algorithm>
+
+#include "dg_common.h"
+
+// Keep every multiply and add separately rounded (no FMA contraction) so the
+// values match the host generator bit for bit.
+#pragma clang fp contract(off)
+
+namespace dg {
+
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kTidLogits = 20, kTidPeak = 21;
+constexpr uint32_t kPeakFractionNum = 3006477107u;  // floor(0.7 * 2^32)
+
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__host__ __device__ inline uint64_t stream_key(uint64_t seed, uint64_t tid) { return mix64(seed * kGolden + tid); }
+
+__device__ inline float irwin_hall4(uint64_t h) {
+  const int64_t s = static_cast<int64_t>(h & 0xFFFF) + static_cast<int64_t>((h >> 16) & 0xFFFF) +
+                    static_cast<int64_t>((h >> 32) & 0xFFFF) + static_cast<int64_t>(h >> 48);
+  return static_cast<float>(s - 131070);
+}
+
+float normal_scale(float sigma) {
+  const double sd4 = std::sqrt((65536.0 * 65536.0 - 1.0) / 3.0);
+  return static_cast<float>(static_cast<double>(sigma) / sd4);
+}
+
+template <typename T>
+__global__ void synth_normal_kernel(uint64_t key, int64_t n, float scale, T* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = irwin_hall4(mix64(key + static_cast<uint64_t>(i + 1) * kGolden)) * scale;
+    if constexpr (sizeof(T) == 2) out[i] = f32_to_bf16(v);
+    else out[i] = v;
+  }
+}
+
+__global__ void synth_ids_kernel(uint64_t key, int64_t n, uint32_t vocab, int32_t* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint64_t h = mix64(key + static_cast<uint64_t>(i + 1) * kGolden);
+    out[i] = static_cast<int32_t>(((h >> 32) * vocab) >> 32);
+  }
+}
+
+__global__ void synth_logits_kernel(uint64_t key_bg, uint64_t key_pk, int rows, int64_t vocab, float scale,
+                                    float peak, bf16_t* __restrict__ out) {
+  const int64_t n = static_cast<int64_t>(rows) * vocab;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float v = irwin_hall4(mix64(key_bg + static_cast<uint64_t>(i + 1) * kGolden)) * scale;
+    const int64_t row = i / vocab, col = i - row * vocab;
+    const uint64_t h = mix64(key_pk + static_cast<uint64_t>(row + 1) * kGolden);
+    const bool planted = static_cast<uint32_t>(h) < kPeakFractionNum;
+    const int64_t pc = static_cast<int64_t>(((h >> 32) * static_cast<uint64_t>(vocab)) >> 32);
+    if (planted && col == pc) v = v + peak;
+    out[i] = f32_to_bf16(v);
+  }
+}
+
+static int grid_for(int64_t n) { return static_cast<int>(std::min<int64_t>(std::max<int64_t>(ceil_div(n, 256), 1), 65536)); }
+
+int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s) {
+  if (n == 0) return DG_OK;
+  const uint64_t key = stream_key(seed, tid);
+  const float scale = normal_scale(sigma);
+  if (dtype == DG_BF16)
+    synth_normal_kernel<bf16_t><<<grid_for(n), 256, 0, s>>>(key, n, scale, static_cast<bf16_t*>(out));
+  else
+    synth_normal_kernel<float><<<grid_for(n), 256, 0, s>>>(key, n, scale, static_cast<float*>(out));
+  DG_LAUNCH_CHECK("synth_normal_kernel");
+  return DG_OK;
+}
+
+int launch_synth_ids(uint64_t seed, uint64_t tid, int64_t n, int vocab, int32_t* out, hipStream_t s) {
+  if (n == 0) return DG_OK;
+  synth_ids_kernel<<<grid_for(n), 256, 0, s>>>(stream_key(seed, tid), n, static_cast<uint32_t>(vocab), out);
+  DG_LAUNCH_CHECK("synth_ids_kernel");
+  return DG_OK;
+}
+
+int launch_synth_logits(uint64_t seed, int step, int rows, int vocab, float sigma, float peak, void* out,
+                        hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(rows) * vocab;
+  if (n == 0) return DG_OK;
+  const uint64_t kb = stream_key(seed, kTidLogits + (static_cast<uint64_t>(step) << 8));
+  const uint64_t kp = stream_key(seed, kTidPeak + (static_cast<uint64_t>(step) << 8));
+  synth_logits_kernel<<<grid_for(n), 256, 0, s>>>(kb, kp, rows, vocab, normal_scale(sigma), peak,
+                                                  static_cast<bf16_t*>(out));
+  DG_LAUNCH_CHECK("synth_logits_kernel");
+  return DG_OK;
+}
+
+}  // namespace dg

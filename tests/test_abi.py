@@ -1,0 +1,80 @@
+"""The C ABI on the CPU: every symbol include/dg.h declares is exported, and
+argument validation rejects bad calls before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from canvas_denoising_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L.lib, n), n
+        assert n in L._SIGS, f"{n} has no ctypes signature"
+
+
+def test_temperature_matches_pages_schedule(L):
+    s = L.make_sched()
+    assert L.dg_temperature(s, 0) == np.float32(0.8)
+    assert L.dg_temperature(s, 47) == np.float32(0.4)
+    assert np.isnan(L.lib.dg_temperature(None, 0))
+
+
+def test_sampler_validation_errors(L):
+    s = L.make_sched()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cases = [
+        (dict(d_logits=None), L.DG_ERR_INVALID),
+        (dict(rows=0), L.DG_ERR_SHAPE),
+        (dict(vocab=0), L.DG_ERR_SHAPE),
+        (dict(dtype=7), L.DG_ERR_INVALID),
+        (dict(step=48), L.DG_ERR_INVALID),
+        (dict(step=-1), L.DG_ERR_INVALID),
+        (dict(ws_bytes=16), L.DG_ERR_CAPACITY),
+        (dict(d_logits=fake + 2), L.DG_ERR_INVALID),
+        (dict(d_workspace=fake + 16), L.DG_ERR_INVALID),
+        (dict(d_stop=None), L.DG_ERR_INVALID),
+    ]
+    for over, code in cases:
+        a = dict(d_logits=fake, dtype=0, rows=256, vocab=262144, step=0, ws_bytes=1 << 20, d_stop=fake,
+                 d_workspace=fake)
+        a.update(over)
+        with pytest.raises(L.DGError) as ei:
+            L.dg_sample_canvas(a["d_logits"], a["dtype"], a["rows"], a["vocab"], s, a["step"], 0, fake, fake,
+                               None, None, None, a["d_stop"], a["d_workspace"], a["ws_bytes"])
+        assert ei.value.code == code, (over, ei.value)
+
+
+def test_sched_validation(L):
+    for bad in (dict(max_steps=0), dict(t_start=0.0), dict(t_end=float("nan")), dict(stable_needed=-1)):
+        s = L.make_sched(**bad)
+        with pytest.raises(L.DGError) as ei:
+            L.dg_init_canvas(s, 0, 256, 4096, 1 << 20, None)
+        assert ei.value.code == L.DG_ERR_INVALID
+
+
+def test_workspace_size(L):
+    assert L.dg_sample_workspace_size(0, 10) == 0
+    assert L.dg_sample_workspace_size(256, 262144) >= 256 * 16
+    assert L.dg_sample_workspace_size(1, 1) == 16

@@ -1,0 +1,214 @@
+"""GPU parity of canvas init, the fused sampler and the stop rule against the oracle.
+
+Bar: argmax, accept mask, next canvas, stop state and step counts bit-exact
+(positions whose oracle entropy lies within 1e-4 of the 0.1 bound are flagged
+and excluded from the accept/canvas comparison); entropy within 1e-3 absolute
+(asserted tighter where noted); row max exact; ln Z within 1e-5 relative.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import philox
+from oracle.loop import denoise_block
+from oracle.sampler import Schedule, sample_step, temperature
+
+from gpu_util import announce, bf16_bits_of, need_gpu, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    need_gpu()
+    from canvas_denoising_amd import _lib, runtime
+    return _lib, runtime
+
+
+def make_logits(rows, V, seed, dtype):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 3, size=(rows, V)).astype(np.float32)
+    conf = rng.random(rows) < 0.4
+    cols = rng.integers(0, V, size=rows)
+    x[conf, cols[conf]] += 60.0                       # confident rows
+    tie = (~conf) & (rng.random(rows) < 0.3)
+    for r in np.nonzero(tie)[0]:                      # exact ties at the maximum
+        m = x[r].max() + 5.0
+        c = rng.choice(V, size=min(3, V), replace=False)
+        x[r, c] = m
+    if V > 4:
+        x[0, :] = 1.25                                # uniform row
+    t = torch.from_numpy(x)
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    return t.cuda()
+
+
+def compare_step(res, st, sched, tol_h=1e-3):
+    H = res.entropy
+    flagged = np.abs(H - sched.entropy_bound) <= 1e-4
+    g_H = to_f64(st.entropy)
+    assert np.abs(g_H - H).max() <= tol_h, np.abs(g_H - H).max()
+    assert np.array_equal(st.pred.cpu().numpy(), res.pred)
+    ok = ~flagged
+    assert np.array_equal(st.accept.cpu().numpy()[ok].astype(bool), res.accept[ok])
+    assert np.array_equal(st.canvas.cpu().numpy()[ok], res.next_canvas[ok])
+    return flagged
+
+
+@pytest.mark.parametrize("rows,V,dtype", [(256, 4096, "bf16"), (7, 4096, "f32"), (5, 1000, "bf16"),
+                                          (3, 2048 * 9 + 8, "bf16"), (1, 1, "f32"), (2, 24, "f32"),
+                                          (300, 2056, "bf16")])
+def test_sampler_matches_oracle(L, rows, V, dtype):
+    lib, rt = L
+    announce(f"sampler rows={rows} V={V} {dtype}")
+    sched = Schedule(seed=5)
+    csched = lib.make_sched(seed=5)
+    logits = make_logits(rows, V, rows * 31 + V, dtype)
+    st = rt.SamplerState(rows, V)
+    st.init(csched, 0)
+    step, block = 5, 2
+    prev = np.random.default_rng(0).integers(0, V, size=rows)
+    st.pred.copy_(torch.from_numpy(prev.astype(np.int32)))
+    st.stop[1] = 3  # stable_count carried in
+    st.sample(logits, csched, step, block)
+    torch.cuda.synchronize()
+    res = sample_step(to_f64(logits), step, block, sched, prev, 3)
+    compare_step(res, st, sched)
+    # row statistics: exact max, ln Z of the tempered distribution
+    lg = to_f64(logits)
+    T = temperature(step, sched)
+    rs = to_f64(st.row_stats)
+    assert np.array_equal(rs[:, 0], lg.max(axis=1))
+    z = np.log(np.exp((lg - lg.max(axis=1, keepdims=True)) / T).sum(axis=1))
+    assert np.allclose(rs[:, 1], z, rtol=1e-5, atol=1e-6)
+    s = st.stop_state()
+    assert s["steps_run"] == step + 1
+    assert s["stable_count"] == res.stable
+    assert s["stopped"] == int(res.stop)
+    assert abs(s["mean_entropy"] - res.mean_entropy) <= 1e-4
+
+
+def test_canvas_init_is_philox(L):
+    lib, rt = L
+    for seed, block, V in [(0, 0, 262144), (123456789012, 7, 4096), (2**64 - 1, 3, 1000)]:
+        announce(f"init seed={seed} block={block}")
+        st = rt.SamplerState(256, V)
+        st.stop.fill_(7)
+        st.init(lib.make_sched(seed=seed), block)
+        torch.cuda.synchronize()
+        assert np.array_equal(st.canvas.cpu().numpy(), philox.init_canvas(seed, 256, block, V))
+        s = st.stop_state()
+        assert s["stable_count"] == 0 and s["stopped"] == 0 and s["steps_run"] == 0 and math.isinf(s["mean_entropy"])
+
+
+@pytest.mark.parametrize("needed,stop_at", [(2, 2), (1, 1)])
+def test_stop_rule_and_no_op_after_stop(L, needed, stop_at):
+    lib, rt = L
+    announce(f"stop rule needed={needed}")
+    C, V = 64, 512
+    sched = Schedule(max_steps=8, stable_needed=needed, seed=9)
+    csched = lib.make_sched(max_steps=8, stable_needed=needed, seed=9)
+    target = (np.arange(C) * 5) % V
+    lg = np.zeros((C, V), np.float32)
+    lg[np.arange(C), target] = 40.0
+    logits = torch.from_numpy(lg).cuda()
+    st = rt.SamplerState(C, V)
+    st.init(csched, 1)
+    tr = denoise_block(lambda s, c, p, t: lg.astype(np.float64), sched, 1, C, V)
+    assert tr.steps == stop_at + 1
+    for s in range(8):
+        st.sample(logits, csched, s, 1)
+        torch.cuda.synchronize()
+        state = st.stop_state()
+        if s < stop_at:
+            assert state["stopped"] == 0
+        if s == stop_at:
+            assert state["stopped"] == 1 and state["steps_run"] == stop_at + 1
+            frozen = st.canvas.clone()
+    state = st.stop_state()
+    assert state["steps_run"] == tr.steps  # later calls were no-ops
+    assert np.array_equal(st.pred.cpu().numpy(), tr.block_ids)
+    assert torch.equal(st.canvas, frozen)
+
+
+def test_prediction_change_resets_stability(L):
+    lib, rt = L
+    announce("stability reset")
+    C, V = 32, 256
+    csched = lib.make_sched(seed=1)
+    st = rt.SamplerState(C, V)
+    st.init(csched, 0)
+    a = np.zeros((C, V), np.float32); a[np.arange(C), np.arange(C)] = 40.0
+    b = np.zeros((C, V), np.float32); b[np.arange(C), np.arange(C) + 1] = 40.0
+    seq = [a, b, b, b]
+    counts = []
+    for s, lg in enumerate(seq):
+        st.sample(torch.from_numpy(lg).cuda(), csched, s, 0)
+        counts.append(st.stop_state()["stable_count"])
+    assert counts[:3] == [0, 0, 1]
+    assert st.stop_state()["stopped"] == 1  # b,b,b with near-zero entropy
+
+
+def test_sampler_is_deterministic(L):
+    lib, rt = L
+    announce("determinism")
+    logits = make_logits(256, 32768, 3, "bf16")
+    csched = lib.make_sched(seed=3)
+    outs = []
+    for _ in range(2):
+        st = rt.SamplerState(256, 32768)
+        st.init(csched, 0)
+        st.sample(logits, csched, 4, 0)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (st.canvas, st.pred, st.entropy, st.row_stats, st.stop)])
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_synthetic_device_twin_is_bit_identical(L):
+    lib, rt = L
+    announce("synth twin")
+    n = 100003
+    for dtype, tdt in ((lib.DG_BF16, torch.bfloat16), (lib.DG_F32, torch.float32)):
+        out = torch.empty(n, dtype=tdt, device="cuda")
+        lib.dg_synth_normal(7, 12345, n, 0.02, dtype, out)
+        torch.cuda.synchronize()
+        if dtype == lib.DG_BF16:
+            assert np.array_equal(bf16_bits_of(out), synthetic.normal_bf16_bits(7, 12345, n, 0.02))
+        else:
+            assert np.array_equal(out.cpu().numpy(), synthetic.normal_f32(7, 12345, n, 0.02))
+    ids = torch.empty(n, dtype=torch.int32, device="cuda")
+    lib.dg_synth_uniform_ids(1, synthetic.TID_PROMPT, n, 262144, ids)
+    assert np.array_equal(ids.cpu().numpy(), synthetic.uniform_ids(1, synthetic.TID_PROMPT, n, 262144))
+    lg = torch.empty(4, 5000, dtype=torch.bfloat16, device="cuda")
+    lib.dg_synth_planted_logits(0, 3, 4, 5000, 3.0, 12.0, lg)
+    assert np.array_equal(bf16_bits_of(lg), synthetic.planted_logits_rows(0, 3, 4, 5000, range(4)))
+
+
+def test_sampler_full_size_planted_logits(L):
+    """256 x 262144 bf16 planted-peak logits, as timed by the benchmark: steps 0, 1 and 47."""
+    lib, rt = L
+    rows, V = 256, 262144
+    sched = Schedule(seed=0)
+    csched = lib.make_sched(seed=0)
+    st = rt.SamplerState(rows, V)
+    st.init(csched, 0)
+    prev, stable = None, 0
+    for step in (0, 1, 47):
+        announce(f"full-size sampler step {step}")
+        logits = torch.empty(rows, V, dtype=torch.bfloat16, device="cuda")
+        lib.dg_synth_planted_logits(0, step, rows, V, 3.0, 12.0, logits)
+        st.sample(logits, csched, step, 0)
+        torch.cuda.synchronize()
+        host_bits = synthetic.planted_logits_rows(0, step, rows, V, range(rows))
+        assert np.array_equal(bf16_bits_of(logits), host_bits)
+        lg = synthetic.bf16_bits_to_f32(host_bits).astype(np.float64)
+        res = sample_step(lg, step, 0, sched, prev, stable)
+        compare_step(res, st, sched, tol_h=1e-3)
+        s = st.stop_state()
+        assert s["stable_count"] == res.stable and s["stopped"] == int(res.stop) == 0
+        assert abs(s["mean_entropy"] - res.mean_entropy) <= 1e-4
+        prev, stable = res.pred, res.stable
+        del logits
