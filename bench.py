@@ -153,15 +153,188 @@ def cpu_baseline_sampler(rows, V, S, budget_s):
                       f"for {steps} steps ({t_total:.1f} s of CPU time), scaled to whole 256-row canvas steps"}
 
 
-WORKLOADS = {"sampler": bench_sampler}
+# ------------------------------------------------------------- full denoise step
+EXPERT_KERNELS = ("expert_gateup", "expert_down")
+
+
+def bench_full(args):
+    """Whole hot path: self-conditioning, 30 MoE layers, LM head, sampler, stop read-back, block commit."""
+    import numpy as np
+    import torch
+    from canvas_denoising_amd import _lib as L
+    from canvas_denoising_amd import configs
+    from canvas_denoising_amd.runtime import Model, SamplerState, stop_dict
+
+    w = configs.full_loop_bf16(args.layers)
+    d = w.desc
+    C, V, S = d.canvas, d.vocab, w.max_steps
+    n_blocks = (args.steps + S - 1) // S + 1
+    capacity = w.prompt + (n_blocks + 1) * C
+    log(f"[bench] model {d.n_layers} layers, weights {L.dg_weights_bytes(d) / 1e9:.1f} GB, KV capacity {capacity}")
+    model = Model(d, capacity, seed=0)
+    prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
+    L.dg_synth_uniform_ids(4, 10, w.prompt, V, prompt)
+    t0 = time.perf_counter()
+    model.prefill(prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    log(f"[bench] prefill {w.prompt} tokens: {prefill_s:.2f} s")
+    sched = L.make_sched(max_steps=S, seed=0)
+    st = SamplerState(C, V)
+    logits = model.logits
+    block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
+    counters = {"steps": 0, "commits": 0, "stopped": 0}
+
+    def run(n_steps, block0):
+        """n_steps denoising steps; a canvas ends at its stop or after S steps and is then committed."""
+        s, block = 0, block0
+        st.init(sched, block)
+        for _ in range(n_steps):
+            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
+            model.denoise_step(st.canvas, s, *prev, logits=logits)
+            st.sample(logits, sched, s, block)
+            stop = st.stop.cpu()  # the 16-byte stop-state read-back of the loop
+            counters["steps"] += 1
+            s += 1
+            if int(stop[2]) or s == S:
+                counters["stopped"] += int(stop[2])
+                block_ids.copy_(st.pred)
+                model.commit(block_ids)
+                counters["commits"] += 1
+                block += 1
+                s = 0
+                st.init(sched, block)
+        return block
+
+    log(f"[bench] warmup {args.warmup}")
+    blk = run(args.warmup, 0)
+    torch.cuda.synchronize()
+    counters.update(steps=0, commits=0, stopped=0)
+    L.dg_profile_enable(True, 2000 * (args.steps + 2))
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps, blk)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    prof = L.dg_profile_report()
+    L.dg_profile_enable(False)
+    steps_per_s = args.steps / dt
+    # algorithmic bytes of the routed-expert kernels: every expert's weights, once per launch
+    es = 2
+    gu_bytes = d.n_experts * 2 * d.d_expert * d.d_model * es
+    dn_bytes = d.n_experts * d.d_model * d.d_expert * es
+    gu = prof["expert_gateup"]
+    achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
+    src = kernel_source_hash(["canvas_denoising_amd/csrc/moe.hip"])
+    # roofline of the whole step (derived bytes; activations excluded)
+    layer_bytes = (gu_bytes + dn_bytes + ((d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * d.d_model +
+                   d.n_q_heads * d.head_dim * d.d_model + d.n_experts * d.d_model + 3 * d.d_shared * d.d_model) * es)
+    kv_len = w.prompt + C
+    attn_bytes = 2 * d.n_kv_heads * kv_len * d.head_dim * es
+    step_bytes = d.n_layers * (layer_bytes + attn_bytes) + 2 * V * d.d_model * es + 3 * C * V * es
+    step_roof_s = step_bytes / (HBM_PEAK_GBS * 1e9)
+    out = {
+        "metric": "canvas denoise steps/s (256-token canvas)",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"full denoise loop: {d.n_layers} MoE layers d_model {d.d_model}, 16q/8kv x 128 heads, "
+                               f"128 experts top-8 (704, gated GeLU) + shared 2816, tied vocab {V}, self-conditioning "
+                               f"FFN {d.d_selfcond}, prompt KV {w.prompt}, canvas {C}, up to {S} steps per canvas, "
+                               "block commit after each canvas; random-init weights",
+                   "canvas_tokens_per_s": steps_per_s * C,
+                   "committed_tokens_per_s": counters["commits"] * C / dt,
+                   "commits": counters["commits"], "stops": counters["stopped"],
+                   "prefill_tokens_per_s": w.prompt / prefill_s,
+                   "step_roofline_ms": step_roof_s * 1e3,
+                   "step_roofline_frac": step_roof_s / (dt / args.steps),
+                   "kernels_us": {k: v["avg_us"] for k, v in sorted(prof.items())},
+                   "kernels_total_us_per_step": {k: v["total_us"] / args.steps for k, v in sorted(prof.items())}},
+        "roofline": {"kernel": "expert_gateup", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("expert_gateup", src),
+                     "algorithmic_bytes_per_launch": gu_bytes, "avg_us": gu["avg_us"]},
+    }
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_full(d, w.prompt, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_full(d, prompt, budget_s):
+    """Oracle time of one denoising step, extrapolated from one layer (x n_layers) plus LM head,
+    self-conditioning and sampler on a row sample; weights drawn with NumPy (values do not change the
+    oracle's arithmetic cost)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    from oracle import model as OM
+    from oracle.sampler import Schedule, sample_step
+    rng = np.random.default_rng(0)
+    shape = OM.ModelShape(n_layers=1, d_model=d.d_model, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                          head_dim=d.head_dim, n_experts=d.n_experts, top_k=d.top_k, d_expert=d.d_expert,
+                          d_shared=d.d_shared, gated=bool(d.gated), vocab=d.vocab, d_selfcond=d.d_selfcond)
+    D, hd, F, Fs = d.d_model, d.head_dim, d.d_expert, d.d_shared
+    g = lambda *s: rng.standard_normal(s) * 0.02
+    lw = {"wq": g(d.n_q_heads * hd, D), "wk": g(d.n_kv_heads * hd, D), "wv": g(d.n_kv_heads * hd, D),
+          "wo": g(D, d.n_q_heads * hd), "wr": g(d.n_experts, D), "sh_gate": g(Fs, D), "sh_up": g(Fs, D),
+          "sh_down": g(D, Fs), "experts": [{"gate": g(F, D), "up": g(F, D), "down": g(D, F)}
+                                           for _ in range(d.n_experts)]}
+    C = d.canvas
+    L = prompt + C
+    kc = rng.standard_normal((d.n_kv_heads, L, hd))
+    vc = rng.standard_normal((d.n_kv_heads, L, hd))
+    x = rng.standard_normal((C, D))
+    t0 = time.perf_counter()
+    OM.layer_forward(lw, x, kc, vc, prompt, shape, causal=False)
+    t_layer = time.perf_counter() - t0
+    rows = 16
+    E = rng.standard_normal((d.vocab, D)) * 0.02
+    W = {"embed": E, "sc_w1": g(d.d_selfcond, D), "sc_w2": g(D, d.d_selfcond)}
+    t0 = time.perf_counter()
+    lg = OM.lm_head(W, x[:rows], shape)
+    t_lm = (time.perf_counter() - t0) * C / rows
+    res = None
+    t0 = time.perf_counter()
+    res = sample_step(lg, 1, 0, Schedule(), None, 0, keep_probs=True)
+    t_samp = (time.perf_counter() - t0) * C / rows
+    t0 = time.perf_counter()
+    OM.self_condition(W, res.probs)
+    t_sc = (time.perf_counter() - t0) * C / rows
+    step_s = d.n_layers * t_layer + t_lm + t_samp + t_sc
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": min(cores, blas), "kind": "oracle",
+            "sample": f"oracle (NumPy fp64) one MoE layer over the {C}-row canvas with {L} keys "
+                      f"({t_layer:.2f} s) x {d.n_layers} layers, plus LM head ({t_lm:.2f} s), sampler "
+                      f"({t_samp:.2f} s) and self-conditioning ({t_sc:.2f} s) timed on {rows} rows and scaled to "
+                      f"{C}; host cores {cores}, BLAS threads {blas}"}
+
+
+WORKLOADS = {"sampler": bench_sampler, "full": bench_full}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=480)
-    ap.add_argument("--warmup", type=int, default=48)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="sampler")
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="full")
+    ap.add_argument("--layers", type=int, default=30, help="layers of the full workload (30 = the benchmark)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -169,6 +342,10 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the sharding plan is described in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = 480 if args.workload == "sampler" else 96
+    if args.warmup is None:
+        args.warmup = 48 if args.workload == "sampler" else 4
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (libdg runs only on MI355X).", file=sys.stderr)

@@ -66,7 +66,31 @@ _SIGS = {
     "dg_synth_normal": (ctypes.c_int, [_U64, _U64, _I64, _F32, _I32, _P, _P]),
     "dg_synth_uniform_ids": (ctypes.c_int, [_U64, _U64, _I64, _I32, _P, _P]),
     "dg_synth_planted_logits": (ctypes.c_int, [_U64, _I32, _I32, _I32, _F32, _F32, _P, _P]),
+    "dg_synth_fill_weights": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _U64, _F32, _P, _P]),
+    "dg_weights_bytes": (_SZ, [ctypes.POINTER(dg_model_desc)]),
+    "dg_weight_tensor": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _I32, _I32, _I32, ctypes.POINTER(_SZ),
+                                        ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "dg_prepare_weights": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P]),
+    "dg_kv_bytes": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
+    "dg_workspace_size": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
+    "dg_ctx_create": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P, _I64, _P, _SZ, ctypes.POINTER(_P)]),
+    "dg_ctx_destroy": (ctypes.c_int, [_P]),
+    "dg_kv_length": (_I64, [_P]),
+    "dg_kv_set_length": (ctypes.c_int, [_P, _I64]),
+    "dg_prefill_kv": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "dg_denoise_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _F32, _P, _P]),
+    "dg_commit_block": (ctypes.c_int, [_P, _P, _P]),
+    "dg_forward_layer": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P]),
+    "dg_generate_block": (ctypes.c_int, [_P, ctypes.POINTER(dg_sched), _I32, _P, _P, _I32, ctypes.POINTER(_I32), _P]),
+    "dg_ctx_buffer": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_SZ)]),
 }
+
+# weight kinds / context buffers (include/dg.h)
+(DG_W_EMBED, DG_W_EMBED_T, DG_W_SC1, DG_W_SC2, DG_W_Q, DG_W_K, DG_W_V, DG_W_O, DG_W_ROUTER, DG_W_SH_GATE,
+ DG_W_SH_UP, DG_W_SH_DOWN, DG_W_EX_GATE, DG_W_EX_UP, DG_W_EX_DOWN) = range(15)
+(DG_BUF_X, DG_BUF_H, DG_BUF_ROUTER_LOGITS, DG_BUF_SEL, DG_BUF_GATE, DG_BUF_SC, DG_BUF_CANVAS, DG_BUF_PRED,
+ DG_BUF_STOP, DG_BUF_ENTROPY, DG_BUF_ROW_STATS, DG_BUF_ACCEPT, DG_BUF_Q, DG_BUF_ATTN, DG_BUF_SHARED_ACT,
+ DG_BUF_SLOT_OUT, DG_BUF_SLOT_OF) = range(17)
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -160,3 +184,86 @@ def dg_synth_uniform_ids(seed, tid, n, vocab, d_out, stream=None):
 def dg_synth_planted_logits(seed, step, rows, vocab, sigma, peak, d_out, stream=None):
     return _check("dg_synth_planted_logits", lib.dg_synth_planted_logits(seed, step, rows, vocab, sigma, peak,
                                                                          ptr(d_out), stream_handle(stream)))
+
+
+def dg_synth_fill_weights(desc, seed, sigma, d_weights, stream=None):
+    return _check("dg_synth_fill_weights", lib.dg_synth_fill_weights(ctypes.byref(desc), seed, sigma, ptr(d_weights),
+                                                                     stream_handle(stream)))
+
+
+def dg_weights_bytes(desc) -> int:
+    return lib.dg_weights_bytes(ctypes.byref(desc))
+
+
+def dg_weight_tensor(desc, kind, layer=0, expert=0):
+    """(byte offset, rows, cols) of one tensor in the packed weight buffer."""
+    off, r, c = _SZ(), _I64(), _I64()
+    _check("dg_weight_tensor", lib.dg_weight_tensor(ctypes.byref(desc), kind, layer, expert, ctypes.byref(off),
+                                                    ctypes.byref(r), ctypes.byref(c)))
+    return off.value, r.value, c.value
+
+
+def dg_prepare_weights(desc, d_weights, stream=None):
+    return _check("dg_prepare_weights", lib.dg_prepare_weights(ctypes.byref(desc), ptr(d_weights),
+                                                               stream_handle(stream)))
+
+
+def dg_kv_bytes(desc, capacity) -> int:
+    return lib.dg_kv_bytes(ctypes.byref(desc), capacity)
+
+
+def dg_workspace_size(desc, capacity) -> int:
+    return lib.dg_workspace_size(ctypes.byref(desc), capacity)
+
+
+def dg_ctx_create(desc, d_weights, d_kv, capacity, d_workspace, ws_bytes) -> int:
+    out = _P()
+    _check("dg_ctx_create", lib.dg_ctx_create(ctypes.byref(desc), ptr(d_weights), ptr(d_kv), capacity,
+                                              ptr(d_workspace), ws_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def dg_ctx_destroy(ctx):
+    return _check("dg_ctx_destroy", lib.dg_ctx_destroy(ctx))
+
+
+def dg_kv_length(ctx) -> int:
+    return lib.dg_kv_length(ctx)
+
+
+def dg_kv_set_length(ctx, length):
+    return _check("dg_kv_set_length", lib.dg_kv_set_length(ctx, length))
+
+
+def dg_prefill_kv(ctx, d_prompt_ids, n_prompt, stream=None):
+    return _check("dg_prefill_kv", lib.dg_prefill_kv(ctx, ptr(d_prompt_ids), n_prompt, stream_handle(stream)))
+
+
+def dg_denoise_step(ctx, d_canvas, step, d_prev_logits, d_prev_row_stats, prev_temperature, d_logits, stream=None):
+    return _check("dg_denoise_step", lib.dg_denoise_step(ctx, ptr(d_canvas), step, ptr(d_prev_logits),
+                                                         ptr(d_prev_row_stats), prev_temperature, ptr(d_logits),
+                                                         stream_handle(stream)))
+
+
+def dg_commit_block(ctx, d_block_ids, stream=None):
+    return _check("dg_commit_block", lib.dg_commit_block(ctx, ptr(d_block_ids), stream_handle(stream)))
+
+
+def dg_forward_layer(ctx, layer, d_x, rows, causal, stream=None):
+    return _check("dg_forward_layer", lib.dg_forward_layer(ctx, layer, ptr(d_x), rows, int(causal),
+                                                           stream_handle(stream)))
+
+
+def dg_generate_block(ctx, sched, block, d_logits, d_block_out, commit=True, stream=None) -> int:
+    steps = _I32()
+    _check("dg_generate_block", lib.dg_generate_block(ctx, ctypes.byref(sched), block, ptr(d_logits),
+                                                      ptr(d_block_out), int(commit), ctypes.byref(steps),
+                                                      stream_handle(stream)))
+    return steps.value
+
+
+def dg_ctx_buffer(ctx, which):
+    """(device address, bytes) of a context buffer."""
+    p, n = _P(), _SZ()
+    _check("dg_ctx_buffer", lib.dg_ctx_buffer(ctx, which, ctypes.byref(p), ctypes.byref(n)))
+    return p.value, n.value

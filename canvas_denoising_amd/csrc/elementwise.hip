@@ -1,0 +1,180 @@
+// Row-wise and elementwise kernels of the denoising step: token-embedding
+// gather (+ the self-conditioning vector), RMSNorm, the tempered
+// probabilities fed to self-conditioning, and the embedding transpose.
+#include <math.h>
+
+#include <algorithm>
+
+#include "dg_common.h"
+#include "mfma.h"
+#include "prof.h"
+
+namespace dg {
+
+constexpr int kRowThreads = 256;
+
+__device__ inline float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float t = sh[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) t += sh[w];
+  __syncthreads();
+  return t;
+}
+
+// x[m] = E[ids[m]] (+ sc[m]); fp32 residual stream. Ids outside [0, V) are out of
+// contract; they are clamped so that a bad id cannot read outside the table.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void embed_kernel(const T* __restrict__ emb, const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ sc, float* __restrict__ x,
+                                                             int D, int V) {
+  const int m = blockIdx.x;
+  const int id = min(max(ids[m], 0), V - 1);
+  const T* e = emb + static_cast<int64_t>(id) * D;
+  for (int i = threadIdx.x; i < D; i += kRowThreads) {
+    float v = to_f32<T>(e[i]);
+    if (sc) v += sc[static_cast<int64_t>(m) * D + i];
+    x[static_cast<int64_t>(m) * D + i] = v;
+  }
+}
+
+// h = x / sqrt(mean(x^2) + eps) (unit gain); one workgroup per row, fixed summation order
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __restrict__ x, T* __restrict__ h, int D,
+                                                               float eps) {
+  __shared__ float sh[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const float* xr = x + static_cast<int64_t>(m) * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += kRowThreads) ss = fmaf(xr[i], xr[i], ss);
+  ss = block_sum(ss, sh);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  T* hr = h + static_cast<int64_t>(m) * D;
+  for (int i = threadIdx.x; i < D; i += kRowThreads) hr[i] = from_f32<T>(xr[i] * rs);
+}
+
+// P[m][v] = exp((l[m][v] - max_m) / T - lnZ_m): the sampler's tempered distribution,
+// rebuilt from its row statistics (max raw logit, ln of the tempered partition sum)
+template <typename T>
+__global__ void probs_kernel(const T* __restrict__ logits, const float* __restrict__ stats, float inv_t, int64_t V,
+                             int64_t n, T* __restrict__ P) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int64_t m = e / V;
+    const float mx = stats[2 * m], lz = stats[2 * m + 1];
+    const float v = to_f32<T>(logits[e]);
+    P[e] = from_f32<T>(__expf((v - mx) * inv_t - lz));
+  }
+}
+
+// vectorised variant: 8 bf16 per thread, V % 8 == 0
+__global__ void probs_bf16x8_kernel(const bf16_t* __restrict__ logits, const float* __restrict__ stats, float inv_t,
+                                    int64_t V, int64_t n8, bf16_t* __restrict__ P) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < n8; g += stride) {
+    const int64_t e = g * 8;
+    const int64_t m = e / V;
+    const float mx = stats[2 * m], lz = stats[2 * m + 1];
+    const uint4 q = *reinterpret_cast<const uint4*>(logits + e);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __expf((bf16lo(w[i]) - mx) * inv_t - lz);
+      const float b = __expf((bf16hi(w[i]) - mx) * inv_t - lz);
+      o[i] = pack_bf16x2(a, b);
+    }
+    *reinterpret_cast<uint4*>(P + e) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// out[c][r] = in[r][c]; 64 x 64 tiles through LDS
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t R, int64_t C,
+                                                        T* __restrict__ out) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = in[r * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (r < R && c < C) out[c * R + r] = tile[tx][i];
+  }
+}
+
+__global__ void zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------- host
+static int grid_for(int64_t n, int per = 256) {
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>((n + per - 1) / per, 1), 8192));
+}
+
+int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M, int D, int V, int dtype,
+          hipStream_t s) {
+  ProfScope ps("embed", s);
+  if (dtype == DG_BF16)
+    embed_kernel<bf16_t><<<M, kRowThreads, 0, s>>>(static_cast<const bf16_t*>(emb), ids, sc, x, D, V);
+  else
+    embed_kernel<float><<<M, kRowThreads, 0, s>>>(static_cast<const float*>(emb), ids, sc, x, D, V);
+  DG_LAUNCH_CHECK("embed_kernel");
+  return DG_OK;
+}
+
+int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s) {
+  ProfScope ps("rmsnorm", s);
+  if (dtype == DG_BF16) rmsnorm_kernel<bf16_t><<<M, kRowThreads, 0, s>>>(x, static_cast<bf16_t*>(h), D, eps);
+  else rmsnorm_kernel<float><<<M, kRowThreads, 0, s>>>(x, static_cast<float*>(h), D, eps);
+  DG_LAUNCH_CHECK("rmsnorm_kernel");
+  return DG_OK;
+}
+
+int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
+          hipStream_t s) {
+  ProfScope ps("sc_probs", s);
+  const int64_t n = static_cast<int64_t>(M) * V;
+  const float inv_t = 1.0f / temperature;
+  if (dtype == DG_BF16 && V % 8 == 0)
+    probs_bf16x8_kernel<<<grid_for(n / 8), 256, 0, s>>>(static_cast<const bf16_t*>(logits), stats, inv_t, V, n / 8,
+                                                         static_cast<bf16_t*>(P));
+  else if (dtype == DG_BF16)
+    probs_kernel<bf16_t><<<grid_for(n), 256, 0, s>>>(static_cast<const bf16_t*>(logits), stats, inv_t, V, n,
+                                                     static_cast<bf16_t*>(P));
+  else
+    probs_kernel<float><<<grid_for(n), 256, 0, s>>>(static_cast<const float*>(logits), stats, inv_t, V, n,
+                                                    static_cast<float*>(P));
+  DG_LAUNCH_CHECK("probs_kernel");
+  return DG_OK;
+}
+
+int transpose(const void* in, int64_t R, int64_t C, void* out, int dtype, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64));
+  if (grid.y > 65535) return fail(DG_ERR_UNSUPPORTED, "transpose: too many rows");
+  if (dtype == DG_BF16)
+    transpose_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, static_cast<bf16_t*>(out));
+  else
+    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, static_cast<float*>(out));
+  DG_LAUNCH_CHECK("transpose_kernel");
+  return DG_OK;
+}
+
+int zero_fill(void* p, size_t bytes, hipStream_t s) {
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(DG_ERR_INVALID, "zero_fill alignment");
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return DG_OK;
+  zero_kernel<<<grid_for(n16), 256, 0, s>>>(static_cast<uint4*>(p), n16);
+  DG_LAUNCH_CHECK("zero_kernel");
+  return DG_OK;
+}
+
+}  // namespace dg

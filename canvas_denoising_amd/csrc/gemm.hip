@@ -1,0 +1,323 @@
+// Dense GEMM on the MFMA units: C = A * B^T (A activations [M x K], B weights
+// stored [N x K]) with the epilogues the denoising step needs (store, residual
+// add, GeLU, gated GeLU over paired gate/up rows, QKV split into the query
+// buffer and the KV cache, MoE combine).
+//
+// Tiling: 256 threads = 4 waves in a 2 x 2 arrangement over a BM x BN tile;
+// each wave owns (BM/2) x (BN/2) as 16x16 MFMA tiles. A and B tiles of 128
+// bytes per row (BK = 64 bf16 or 32 fp32) are staged through LDS with a
+// register prefetch of the next k-tile (double buffer, one barrier per
+// k-tile); rows are padded by 16 bytes so the 16 lanes of a fragment read hit
+// distinct banks. Workgroups that share a B slice are mapped to the same XCD
+// (dispatch is round-robin over the 8 XCDs) so the slice is fetched from HBM
+// once and re-read from that XCD's L2. Split-K writes fp32 partials that a
+// second kernel reduces in a fixed order before the epilogue.
+#include <algorithm>
+
+#include "dg_common.h"
+#include "gemm.h"
+#include "mfma.h"
+#include "prof.h"
+
+namespace dg {
+
+template <typename T, int BM_, int BN_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BK = 128 / static_cast<int>(sizeof(T));
+  static constexpr int LDK = BK + 16 / static_cast<int>(sizeof(T));
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  static constexpr int CHUNKS = BK / VEC;  // 8 sixteen-byte chunks per row
+  static constexpr int A_LOADS = BM * CHUNKS / 256;
+  static constexpr int B_LOADS = BN * CHUNKS / 256;
+  static constexpr int KSTEPS = BK / 32;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for 256 threads");
+  static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile");
+};
+
+template <typename T>
+__device__ inline void epilogue(const GemmArgs& g, int row, int col, float v) {
+  switch (g.epi) {
+    case EPI_STORE:
+      static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] = from_f32<T>(v);
+      break;
+    case EPI_STORE_F32:
+      static_cast<float*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] = v;
+      break;
+    case EPI_ADD_F32:
+      static_cast<float*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] += v;
+      break;
+    case EPI_GELU:
+      static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] = from_f32<T>(gelu_erf(v));
+      break;
+    case EPI_QKV: {
+      if (col < g.q_cols) {
+        static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] = from_f32<T>(v);
+      } else {
+        const int c = col - g.q_cols;
+        const int per = g.n_kv * g.head_dim;
+        const int which = c / per, rem = c - which * per;
+        const int h = rem / g.head_dim, d = rem - h * g.head_dim;
+        T* base = static_cast<T*>(which == 0 ? g.kcache : g.vcache);
+        base[h * g.kv_head_stride + static_cast<int64_t>(g.pos0 + row) * g.head_dim + d] = from_f32<T>(v);
+      }
+      break;
+    }
+    case EPI_COMBINE: {
+      float s = v;
+      for (int j = 0; j < g.topk; ++j) s += g.slot_out[static_cast<int64_t>(g.slot_of[row * g.topk + j]) * g.N + col];
+      static_cast<float*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] += s;
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k_per_split) {
+  using C = GemmCfg<T, BM, BN>;
+  using F = Frag<T>;
+  __shared__ __align__(16) T sA[2][BM * C::LDK];
+  __shared__ __align__(16) T sB[2][BN * C::LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool paired = g.epi == EPI_GEGLU;
+
+  // ---- tile mapping: workgroups sharing an n-tile land on one XCD
+  const int nm = (g.M + BM - 1) / BM;
+  const int n_rows_b = g.N;  // rows of B visited (2F for paired)
+  const int nn = (n_rows_b + BN - 1) / BN;
+  const int b = blockIdx.x;
+  const int nn8 = (nn / 8) * 8;
+  int mt, nt;
+  if (b < nm * nn8) {
+    const int xcd = b & 7, j = b >> 3;
+    nt = (j / nm) * 8 + xcd;
+    mt = j % nm;
+  } else {
+    const int r = b - nm * nn8;
+    nt = nn8 + r / nm;
+    mt = r % nm;
+  }
+  const int m0 = mt * BM;
+  const int z = blockIdx.y;
+  const int k_begin = z * k_per_split;
+  const int k_end = min(g.K, k_begin + k_per_split);
+  const int nk = (k_end - k_begin) / C::BK;
+
+  // B row of tile column t
+  auto brow = [&](int t) -> int {
+    if (!paired) return nt * BN + t;
+    const int half = t / (BN / 2), c = t % (BN / 2);
+    const int j0 = nt * (BN / 2) + half * (BN / 4);
+    return c < BN / 4 ? j0 + c : g.pair_f + j0 + (c - BN / 4);
+  };
+
+  const T* A = static_cast<const T*>(g.A);
+  const T* B = static_cast<const T*>(g.B);
+  uint4 ra[C::A_LOADS], rb[C::B_LOADS];
+  int arow[C::A_LOADS], achk[C::A_LOADS], brw[C::B_LOADS], bchk[C::B_LOADS];
+  bool aok[C::A_LOADS], bok[C::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int q = tid + 256 * i;
+    arow[i] = q / C::CHUNKS;
+    achk[i] = q % C::CHUNKS;
+    aok[i] = m0 + arow[i] < g.M;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_LOADS; ++i) {
+    const int q = tid + 256 * i;
+    const int t = q / C::CHUNKS;
+    bchk[i] = q % C::CHUNKS;
+    brw[i] = t;
+    bok[i] = paired ? true : (nt * BN + t < g.N);
+  }
+  int bsrc[C::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::B_LOADS; ++i) bsrc[i] = bok[i] ? brow(brw[i]) : 0;
+
+  auto gload = [&](int kt) {
+    const int k0 = k_begin + kt * C::BK;
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      ra[i] = aok[i] ? *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(m0 + arow[i]) * g.lda + k0 +
+                                                        achk[i] * C::VEC)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      rb[i] = bok[i] ? *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(bsrc[i]) * g.ldb + k0 +
+                                                        bchk[i] * C::VEC)
+                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i)
+      *reinterpret_cast<uint4*>(&sA[buf][arow[i] * C::LDK + achk[i] * C::VEC]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i)
+      *reinterpret_cast<uint4*>(&sB[buf][brw[i] * C::LDK + bchk[i] * C::VEC]) = rb[i];
+  };
+
+  f32x4_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      typename F::type af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        af[i] = F::load(&sA[cur][(wm * C::WM + i * 16 + fr) * C::LDK + ks * 32 + fk]);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        bfr[j] = F::load(&sB[cur][(wn * C::WN + j * 16 + fr) * C::LDK + ks * 32 + fk]);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = F::mma(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const int rbase = m0 + wm * C::WM + (lane >> 4) * 4;
+  if (splits > 1) {
+    float* part = g.part + static_cast<int64_t>(z) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int col = nt * BN + wn * C::WN + j * 16 + fr;
+          if (row < g.M && col < g.N) part[static_cast<int64_t>(row) * g.N + col] = acc[i][j][r];
+        }
+    return;
+  }
+  if (paired) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN / 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int jj = nt * (BN / 2) + wn * (BN / 4) + j * 16 + fr;
+          if (row < g.M) {
+            const float v = gelu_erf(acc[i][j][r]) * acc[i][j + C::TN / 2][r];
+            static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + jj] = from_f32<T>(v);
+          }
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rbase + i * 16 + r;
+        const int col = nt * BN + wn * C::WN + j * 16 + fr;
+        if (row < g.M && col < g.N) epilogue<T>(g, row, col, acc[i][j][r]);
+      }
+}
+
+template <typename T>
+__global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
+  const int64_t n = static_cast<int64_t>(g.M) * g.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += g.part[z * n + e];
+    const int row = static_cast<int>(e / g.N), col = static_cast<int>(e - static_cast<int64_t>(row) * g.N);
+    epilogue<T>(g, row, col, v);
+  }
+}
+
+// ------------------------------------------------------------------- host
+struct TileChoice { int bm, bn; };
+
+static TileChoice pick_tile(int M, int N, bool paired) {
+  const int64_t t128 = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
+  if (!paired && M > 64 && t128 >= 512) return {128, 128};
+  return {64, 64};
+}
+
+int gemm_pick_splits(int M, int N, int K, int dtype, int64_t part_capacity, bool allow_split) {
+  if (!allow_split) return 1;
+  const int bk = dtype == DG_BF16 ? 64 : 32;
+  const TileChoice tc = pick_tile(M, N, false);
+  const int64_t tiles = static_cast<int64_t>((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
+  int s = 1;
+  const int ktiles = K / bk;
+  while (tiles * s < 256 && s * 2 <= 32 && ktiles / (s * 2) >= 4 &&
+         static_cast<int64_t>(s) * 2 * M * N <= part_capacity)
+    s *= 2;
+  return s;
+}
+
+template <typename T, int BM, int BN>
+static int launch_tile(const GemmArgs& g, int splits, int kps, hipStream_t s) {
+  const int nm = (g.M + BM - 1) / BM, nn = (g.N + BN - 1) / BN;
+  dim3 grid(static_cast<unsigned>(nm * nn), static_cast<unsigned>(splits));
+  gemm_kernel<T, BM, BN><<<grid, 256, 0, s>>>(g, splits, kps);
+  DG_LAUNCH_CHECK("gemm_kernel");
+  return DG_OK;
+}
+
+template <typename T>
+static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name) {
+  const bool paired = g.epi == EPI_GEGLU;
+  const int bk = 128 / static_cast<int>(sizeof(T));
+  if (g.K % bk != 0) return fail(DG_ERR_UNSUPPORTED, std::string(name) + ": K must be a multiple of the k-tile");
+  if (paired && splits != 1) return fail(DG_ERR_INVALID, "gated GeLU GEMM cannot split K");
+  const TileChoice tc = pick_tile(g.M, g.N, paired);
+  if (paired && (g.pair_f % (tc.bn / 2) != 0 || g.N != 2 * g.pair_f))
+    return fail(DG_ERR_UNSUPPORTED, std::string(name) + ": gated width must be a multiple of 32");
+  const int ktiles = g.K / bk;
+  const int kps = ((ktiles + splits - 1) / splits) * bk;
+  splits = (g.K + kps - 1) / kps;
+  if (splits > 1 && g.part == nullptr) return fail(DG_ERR_INVALID, "split-K needs scratch");
+  int rc;
+  {
+    ProfScope ps(name, s);
+    if (tc.bm == 128) rc = launch_tile<T, 128, 128>(g, splits, kps, s);
+    else rc = launch_tile<T, 64, 64>(g, splits, kps, s);
+  }
+  if (rc != DG_OK) return rc;
+  if (splits > 1) {
+    ProfScope ps("splitk_reduce", s);
+    const int64_t n = static_cast<int64_t>(g.M) * g.N;
+    const int grid = static_cast<int>(std::min<int64_t>((n + 255) / 256, 4096));
+    splitk_reduce_kernel<T><<<grid, 256, 0, s>>>(g, splits);
+    DG_LAUNCH_CHECK("splitk_reduce_kernel");
+  }
+  return DG_OK;
+}
+
+int gemm(const GemmArgs& g, int dtype, int splits, hipStream_t s, const char* name) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return DG_OK;
+  return dtype == DG_BF16 ? gemm_t<bf16_t>(g, splits, s, name) : gemm_t<float>(g, splits, s, name);
+}
+
+}  // namespace dg

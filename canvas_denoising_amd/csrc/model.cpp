@@ -1,0 +1,600 @@
+// Model context of libdg: packed weight layout, KV cache, workspace carving and
+// the host-side orchestration of the denoising step, the encoder pass (prompt
+// prefill and block commit) and the native denoising loop.
+//
+// One denoising step ([P3] "Encoder-denoiser design", "Inference mechanism";
+// [P4] "System architecture"):
+//   self-conditioning from the previous step (probabilities rebuilt from the
+//   sampler's row statistics, u = p E, sc = GeLU(u W1^T) W2^T),
+//   x = E[canvas] + sc,
+//   per layer: h = RMSNorm(x); [q k v] = h Wqkv^T with k, v written to the
+//   cache scratch slots; o = attention (bidirectional); x += o Wo^T;
+//   h = RMSNorm(x); router top-k; routed experts; shared expert;
+//   x += shared + sum_k gate * expert (fixed order),
+//   logits = RMSNorm(x) E^T.
+// The encoder pass runs the same layers causally over prompt / block chunks.
+#include <math.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "dg_common.h"
+#include "gemm.h"
+#include "prof.h"
+
+namespace dg {
+
+// kernels implemented in the .hip files
+int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M, int D, int V, int dtype,
+          hipStream_t s);
+int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s);
+int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
+          hipStream_t s);
+int transpose(const void* in, int64_t R, int64_t C, void* out, int dtype, hipStream_t s);
+int zero_fill(void* p, size_t bytes, hipStream_t s);
+int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
+              int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
+              int dtype, hipStream_t s);
+int attn_max_splits();
+int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel, float* gate, int32_t* offsets,
+              int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s);
+int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
+                const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
+                int dtype, hipStream_t s);
+int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s);
+size_t sample_workspace_bytes(int64_t rows, int64_t vocab);
+int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
+                       hipStream_t stream);
+int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp, const dg_sched& sc, int step,
+                  int block, int32_t* canvas, int32_t* pred, uint8_t* accept, float* entropy, float* row_stats,
+                  dg_stop_state* stop, void* ws, hipStream_t stream);
+float temperature(const dg_sched& s, int step);
+int check_sched(const dg_sched* s, int step);
+
+#define DG_TRY(x)            \
+  do {                       \
+    int rc__ = (x);          \
+    if (rc__ != DG_OK) return rc__; \
+  } while (0)
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static int esize(const dg_model_desc& d) { return d.dtype == DG_BF16 ? 2 : 4; }
+
+// ------------------------------------------------------------ weight layout
+struct WLayout {
+  size_t embed = 0, embed_t = 0, sc1 = 0, sc2 = 0;
+  std::vector<size_t> qkv, o, router, sh_gu, sh_down, ex_gu, ex_down;
+  size_t total = 0;
+};
+
+static WLayout weight_layout(const dg_model_desc& d) {
+  const size_t es = esize(d);
+  size_t cur = 0;
+  auto take = [&](int64_t elems) {
+    const size_t off = cur;
+    cur = align256(cur + static_cast<size_t>(elems) * es);
+    return off;
+  };
+  WLayout L;
+  const int64_t D = d.d_model, hd = d.head_dim;
+  L.embed = take(static_cast<int64_t>(d.vocab) * D);
+  L.embed_t = take(static_cast<int64_t>(d.vocab) * D);
+  L.sc1 = take(static_cast<int64_t>(d.d_selfcond) * D);
+  L.sc2 = take(static_cast<int64_t>(d.d_selfcond) * D);
+  const int g = d.gated ? 2 : 1;
+  for (int l = 0; l < d.n_layers; ++l) {
+    L.qkv.push_back(take(static_cast<int64_t>(d.n_q_heads + 2 * d.n_kv_heads) * hd * D));
+    L.o.push_back(take(static_cast<int64_t>(d.n_q_heads) * hd * D));
+    L.router.push_back(take(static_cast<int64_t>(d.n_experts) * D));
+    L.sh_gu.push_back(take(static_cast<int64_t>(g) * d.d_shared * D));
+    L.sh_down.push_back(take(static_cast<int64_t>(d.d_shared) * D));
+    L.ex_gu.push_back(take(static_cast<int64_t>(d.n_experts) * g * d.d_expert * D));
+    L.ex_down.push_back(take(static_cast<int64_t>(d.n_experts) * d.d_expert * D));
+  }
+  L.total = cur;
+  return L;
+}
+
+static int tensor_info(const dg_model_desc& d, const WLayout& L, int kind, int layer, int expert, size_t* off,
+                       int64_t* rows, int64_t* cols) {
+  const size_t es = esize(d);
+  const int64_t D = d.d_model, hd = d.head_dim;
+  const bool per_layer = kind >= DG_W_Q;
+  if (per_layer && (layer < 0 || layer >= d.n_layers)) return fail(DG_ERR_INVALID, "layer out of range");
+  if (kind >= DG_W_EX_GATE && (expert < 0 || expert >= d.n_experts)) return fail(DG_ERR_INVALID, "expert out of range");
+  const int64_t F = d.d_expert, Fs = d.d_shared;
+  const int64_t gu_stride = (d.gated ? 2 : 1) * F * D;
+  switch (kind) {
+    case DG_W_EMBED: *off = L.embed; *rows = d.vocab; *cols = D; break;
+    case DG_W_EMBED_T: *off = L.embed_t; *rows = D; *cols = d.vocab; break;
+    case DG_W_SC1: *off = L.sc1; *rows = d.d_selfcond; *cols = D; break;
+    case DG_W_SC2: *off = L.sc2; *rows = D; *cols = d.d_selfcond; break;
+    case DG_W_Q: *off = L.qkv[layer]; *rows = d.n_q_heads * hd; *cols = D; break;
+    case DG_W_K: *off = L.qkv[layer] + d.n_q_heads * hd * D * es; *rows = d.n_kv_heads * hd; *cols = D; break;
+    case DG_W_V:
+      *off = L.qkv[layer] + (d.n_q_heads + d.n_kv_heads) * hd * D * es; *rows = d.n_kv_heads * hd; *cols = D;
+      break;
+    case DG_W_O: *off = L.o[layer]; *rows = D; *cols = d.n_q_heads * hd; break;
+    case DG_W_ROUTER: *off = L.router[layer]; *rows = d.n_experts; *cols = D; break;
+    case DG_W_SH_GATE:
+      if (!d.gated) return fail(DG_ERR_INVALID, "ungated model has no gate weights");
+      *off = L.sh_gu[layer]; *rows = Fs; *cols = D; break;
+    case DG_W_SH_UP: *off = L.sh_gu[layer] + (d.gated ? Fs * D * es : 0); *rows = Fs; *cols = D; break;
+    case DG_W_SH_DOWN: *off = L.sh_down[layer]; *rows = D; *cols = Fs; break;
+    case DG_W_EX_GATE:
+      if (!d.gated) return fail(DG_ERR_INVALID, "ungated model has no gate weights");
+      *off = L.ex_gu[layer] + expert * gu_stride * es; *rows = F; *cols = D; break;
+    case DG_W_EX_UP:
+      *off = L.ex_gu[layer] + expert * gu_stride * es + (d.gated ? F * D * es : 0); *rows = F; *cols = D; break;
+    case DG_W_EX_DOWN: *off = L.ex_down[layer] + expert * D * F * es; *rows = D; *cols = F; break;
+    default: return fail(DG_ERR_INVALID, "unknown weight kind");
+  }
+  return DG_OK;
+}
+
+int check_desc(const dg_model_desc* d) {
+  if (d == nullptr) return fail(DG_ERR_INVALID, "desc is NULL");
+  if (d->dtype != DG_BF16 && d->dtype != DG_F32) return fail(DG_ERR_INVALID, "dtype must be DG_BF16 or DG_F32");
+  if (d->n_layers < 1) return fail(DG_ERR_SHAPE, "n_layers must be >= 1");
+  if (d->canvas < 1 || d->canvas > 256) return fail(DG_ERR_UNSUPPORTED, "canvas must be in [1, 256]");
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+    return fail(DG_ERR_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (d->dtype == DG_BF16 && d->head_dim != 64 && d->head_dim != 128)
+    return fail(DG_ERR_UNSUPPORTED, "bf16 head_dim must be 64 or 128");
+  if (d->dtype == DG_F32 && (d->head_dim < 8 || d->head_dim > 128 || d->head_dim % 8 != 0))
+    return fail(DG_ERR_UNSUPPORTED, "fp32 head_dim must be a multiple of 8 up to 128");
+  const int64_t dims[] = {d->d_model, static_cast<int64_t>(d->n_q_heads) * d->head_dim, d->d_expert, d->d_shared,
+                          d->d_selfcond, d->vocab};
+  for (int64_t v : dims)
+    if (v < 64 || v % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "d_model, q width, FFN widths and vocab must be multiples of 64");
+  if (d->n_experts < 1 || d->n_experts > 256) return fail(DG_ERR_UNSUPPORTED, "n_experts must be in [1, 256]");
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return fail(DG_ERR_UNSUPPORTED, "top_k must be in [1, min(16, n_experts)]");
+  if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return fail(DG_ERR_INVALID, "rms_eps must be finite and >= 0");
+  if (d->gated != 0 && d->gated != 1) return fail(DG_ERR_INVALID, "gated must be 0 or 1");
+  return DG_OK;
+}
+
+// ----------------------------------------------------------- workspace layout
+struct WsLayout {
+  size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
+      sc, u, sc_hid, P, gpart, canvas, pred, accept, entropy, row_stats, stop, samp, total;
+  int64_t gpart_floats;
+};
+
+static WsLayout ws_layout(const dg_model_desc& d) {
+  const size_t es = esize(d);
+  const int64_t C = d.canvas, D = d.d_model, QW = static_cast<int64_t>(d.n_q_heads) * d.head_dim;
+  const int64_t CK = C * d.top_k;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = cur;
+    cur = align256(cur + bytes);
+    return off;
+  };
+  WsLayout w;
+  w.x = take(C * D * 4);
+  w.h = take(C * D * es);
+  w.q = take(C * QW * es);
+  w.o = take(C * QW * es);
+  w.part_o = take(static_cast<size_t>(attn_max_splits()) * d.n_q_heads * C * d.head_dim * 4);
+  w.part_ml = take(static_cast<size_t>(attn_max_splits()) * d.n_q_heads * C * 2 * 4);
+  w.rlog = take(C * d.n_experts * 4);
+  w.sel = take(CK * 4);
+  w.gate = take(CK * 4);
+  w.offsets = take((d.n_experts + 1) * 4);
+  w.perm = take(CK * 4);
+  w.slot_of = take(CK * 4);
+  w.slot_gate = take(CK * 4);
+  w.act = take(CK * d.d_expert * es);
+  w.slot_out = take(CK * D * 4);
+  w.sh_act = take(C * d.d_shared * es);
+  w.sc = take(C * D * 4);
+  w.u = take(C * D * es);
+  w.sc_hid = take(C * d.d_selfcond * es);
+  w.P = take(static_cast<size_t>(C) * d.vocab * es);
+  w.gpart_floats = 32 * C * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
+  w.gpart = take(w.gpart_floats * 4);
+  w.canvas = take(C * 4);
+  w.pred = take(C * 4);
+  w.accept = take(C);
+  w.entropy = take(C * 4);
+  w.row_stats = take(C * 8);
+  w.stop = take(sizeof(dg_stop_state));
+  w.samp = take(sample_workspace_bytes(C, d.vocab));
+  w.total = cur;
+  return w;
+}
+
+}  // namespace dg
+
+struct dg_ctx {
+  dg_model_desc d;
+  char* w;
+  char* kv;
+  int64_t cap;
+  int64_t len;
+  char* ws;
+  size_t ws_bytes;
+  dg::WLayout wl;
+  dg::WsLayout wsl;
+};
+
+namespace dg {
+
+template <typename P> static P* wsp(dg_ctx* c, size_t off) { return reinterpret_cast<P*>(c->ws + off); }
+static void* wp(dg_ctx* c, size_t off) { return c->w + off; }
+
+static void* kv_k(dg_ctx* c, int l) {
+  const size_t es = esize(c->d);
+  return c->kv + static_cast<size_t>(l) * c->d.n_kv_heads * c->cap * c->d.head_dim * es;
+}
+static void* kv_v(dg_ctx* c, int l) {
+  const size_t es = esize(c->d);
+  return c->kv + static_cast<size_t>(c->d.n_layers + l) * c->d.n_kv_heads * c->cap * c->d.head_dim * es;
+}
+
+static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool allow_split) {
+  const int splits = gemm_pick_splits(g.M, g.N, g.K, c->d.dtype, c->wsl.gpart_floats, allow_split);
+  g.part = wsp<float>(c, c->wsl.gpart);
+  return gemm(g, c->d.dtype, splits, s, name);
+}
+
+// one layer over M rows of the residual stream x placed at cache positions pos0 ..
+// pos0+M-1; `kv_only` stops after the K/V projection (last encoder layer)
+static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causal, bool kv_only, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  const WsLayout& w = c->wsl;
+  const int D = d.d_model, hd = d.head_dim, QW = d.n_q_heads * hd;
+  void* h = wsp<void>(c, w.h);
+  DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
+  {
+    GemmArgs g;
+    g.A = h; g.lda = D;
+    g.B = wp(c, c->wl.qkv[l]); g.ldb = D;
+    g.M = M; g.N = (d.n_q_heads + 2 * d.n_kv_heads) * hd; g.K = D;
+    g.epi = EPI_QKV; g.out = wsp<void>(c, w.q); g.ldo = QW;
+    g.q_cols = kv_only ? 0 : QW; g.head_dim = hd; g.n_kv = d.n_kv_heads; g.pos0 = pos0;
+    g.kv_head_stride = c->cap * hd; g.kcache = kv_k(c, l); g.vcache = kv_v(c, l);
+    if (kv_only) {  // only the K/V rows of the fused projection
+      g.B = static_cast<const char*>(g.B) + static_cast<size_t>(QW) * D * esize(d);
+      g.N = 2 * d.n_kv_heads * hd;
+    }
+    DG_TRY(run_gemm(c, g, s, "qkv_proj", false));
+  }
+  if (kv_only) return DG_OK;
+  DG_TRY(attention(wsp<void>(c, w.q), QW, kv_k(c, l), kv_v(c, l), c->cap * hd, M, d.n_q_heads, d.n_kv_heads, hd,
+                   pos0, causal ? 1 : 0, wsp<float>(c, w.part_o), wsp<float>(c, w.part_ml), wsp<void>(c, w.o), QW,
+                   d.dtype, s));
+  {
+    GemmArgs g;
+    g.A = wsp<void>(c, w.o); g.lda = QW;
+    g.B = wp(c, c->wl.o[l]); g.ldb = QW;
+    g.M = M; g.N = D; g.K = QW;
+    g.epi = EPI_ADD_F32; g.out = x; g.ldo = D;
+    DG_TRY(run_gemm(c, g, s, "o_proj", true));
+  }
+  DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
+  {
+    GemmArgs g;
+    g.A = h; g.lda = D;
+    g.B = wp(c, c->wl.router[l]); g.ldb = D;
+    g.M = M; g.N = d.n_experts; g.K = D;
+    g.epi = EPI_STORE_F32; g.out = wsp<void>(c, w.rlog); g.ldo = d.n_experts;
+    DG_TRY(run_gemm(c, g, s, "router", true));
+  }
+  DG_TRY(moe_route(wsp<float>(c, w.rlog), M, d.n_experts, d.top_k, d.renorm_gates, wsp<int32_t>(c, w.sel),
+                   wsp<float>(c, w.gate), wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm),
+                   wsp<int32_t>(c, w.slot_of), wsp<float>(c, w.slot_gate), s));
+  DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
+                     wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
+                     wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, s));
+  {
+    GemmArgs g;
+    g.A = h; g.lda = D;
+    g.B = wp(c, c->wl.sh_gu[l]); g.ldb = D;
+    g.M = M; g.N = (d.gated ? 2 : 1) * d.d_shared; g.K = D;
+    g.epi = d.gated ? EPI_GEGLU : EPI_GELU; g.pair_f = d.d_shared;
+    g.out = wsp<void>(c, w.sh_act); g.ldo = d.d_shared;
+    DG_TRY(run_gemm(c, g, s, "shared_gateup", false));
+  }
+  {
+    GemmArgs g;
+    g.A = wsp<void>(c, w.sh_act); g.lda = d.d_shared;
+    g.B = wp(c, c->wl.sh_down[l]); g.ldb = d.d_shared;
+    g.M = M; g.N = D; g.K = d.d_shared;
+    g.epi = EPI_COMBINE; g.out = x; g.ldo = D;
+    g.slot_out = wsp<float>(c, w.slot_out); g.slot_of = wsp<int32_t>(c, w.slot_of); g.topk = d.top_k;
+    DG_TRY(run_gemm(c, g, s, "shared_down_combine", true));
+  }
+  return DG_OK;
+}
+
+static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  float* x = wsp<float>(c, c->wsl.x);
+  for (int c0 = 0; c0 < n; c0 += d.canvas) {
+    const int M = std::min(d.canvas, n - c0);
+    DG_TRY(embed(wp(c, c->wl.embed), ids + c0, nullptr, x, M, d.d_model, d.vocab, d.dtype, s));
+    for (int l = 0; l < d.n_layers; ++l)
+      DG_TRY(layer_forward(c, l, x, M, static_cast<int>(c->len), true, l == d.n_layers - 1, s));
+    c->len += M;
+  }
+  return DG_OK;
+}
+
+static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats, float prev_t,
+                   void* logits, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  const WsLayout& w = c->wsl;
+  const int C = d.canvas, D = d.d_model;
+  float* x = wsp<float>(c, w.x);
+  const float* sc = nullptr;
+  if (prev_logits != nullptr) {
+    DG_TRY(probs(prev_logits, prev_stats, prev_t, C, d.vocab, wsp<void>(c, w.P), d.dtype, s));
+    {
+      GemmArgs g;  // u = p E  (A = p [C x V], B = E^T [D x V])
+      g.A = wsp<void>(c, w.P); g.lda = d.vocab;
+      g.B = wp(c, c->wl.embed_t); g.ldb = d.vocab;
+      g.M = C; g.N = D; g.K = d.vocab;
+      g.epi = EPI_STORE; g.out = wsp<void>(c, w.u); g.ldo = D;
+      DG_TRY(run_gemm(c, g, s, "sc_embed", true));
+    }
+    {
+      GemmArgs g;
+      g.A = wsp<void>(c, w.u); g.lda = D;
+      g.B = wp(c, c->wl.sc1); g.ldb = D;
+      g.M = C; g.N = d.d_selfcond; g.K = D;
+      g.epi = EPI_GELU; g.out = wsp<void>(c, w.sc_hid); g.ldo = d.d_selfcond;
+      DG_TRY(run_gemm(c, g, s, "sc_ffn1", true));
+    }
+    {
+      GemmArgs g;
+      g.A = wsp<void>(c, w.sc_hid); g.lda = d.d_selfcond;
+      g.B = wp(c, c->wl.sc2); g.ldb = d.d_selfcond;
+      g.M = C; g.N = D; g.K = d.d_selfcond;
+      g.epi = EPI_STORE_F32; g.out = wsp<void>(c, w.sc); g.ldo = D;
+      DG_TRY(run_gemm(c, g, s, "sc_ffn2", true));
+    }
+    sc = wsp<float>(c, w.sc);
+  }
+  DG_TRY(embed(wp(c, c->wl.embed), canvas, sc, x, C, D, d.vocab, d.dtype, s));
+  for (int l = 0; l < d.n_layers; ++l)
+    DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), false, false, s));
+  void* h = wsp<void>(c, w.h);
+  DG_TRY(rmsnorm(x, h, C, D, d.rms_eps, d.dtype, s));
+  GemmArgs g;
+  g.A = h; g.lda = D;
+  g.B = wp(c, c->wl.embed); g.ldb = D;
+  g.M = C; g.N = d.vocab; g.K = D;
+  g.epi = EPI_STORE; g.out = logits; g.ldo = d.vocab;
+  return run_gemm(c, g, s, "lm_head", false);
+}
+
+static int check_ctx(const dg_ctx* c) {
+  if (c == nullptr) return fail(DG_ERR_INVALID, "ctx is NULL");
+  return DG_OK;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+size_t dg_weights_bytes(const dg_model_desc* desc) {
+  if (check_desc(desc) != DG_OK) return 0;
+  return weight_layout(*desc).total;
+}
+
+int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert, size_t* offset,
+                     int64_t* rows, int64_t* cols) {
+  DG_TRY(check_desc(desc));
+  if (!offset || !rows || !cols) return fail(DG_ERR_INVALID, "output pointers required");
+  const WLayout L = weight_layout(*desc);
+  return tensor_info(*desc, L, kind, layer, expert, offset, rows, cols);
+}
+
+int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream) {
+  DG_TRY(check_desc(desc));
+  if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
+  const WLayout L = weight_layout(*desc);
+  char* w = static_cast<char*>(d_weights);
+  return transpose(w + L.embed, desc->vocab, desc->d_model, w + L.embed_t, desc->dtype, as_stream(stream));
+}
+
+int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights, void* stream) {
+  DG_TRY(check_desc(desc));
+  if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
+  if (!isfinite(sigma) || sigma < 0.f) return fail(DG_ERR_INVALID, "sigma must be finite and >= 0");
+  const dg_model_desc& d = *desc;
+  const WLayout L = weight_layout(d);
+  hipStream_t s = as_stream(stream);
+  char* w = static_cast<char*>(d_weights);
+  auto fill = [&](int kind, int layer, int expert, uint64_t tid) -> int {
+    size_t off;
+    int64_t r, cl;
+    DG_TRY(tensor_info(d, L, kind, layer, expert, &off, &r, &cl));
+    return launch_synth_normal(seed, tid, r * cl, sigma, d.dtype, w + off, s);
+  };
+  const uint64_t kLayer = 1ull << 20, kExpert = 1ull << 32;
+  DG_TRY(fill(DG_W_EMBED, 0, 0, 1));
+  DG_TRY(fill(DG_W_SC1, 0, 0, 2));
+  DG_TRY(fill(DG_W_SC2, 0, 0, 3));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const uint64_t lb = kLayer + 64ull * l;
+    DG_TRY(fill(DG_W_Q, l, 0, lb + 0));
+    DG_TRY(fill(DG_W_K, l, 0, lb + 1));
+    DG_TRY(fill(DG_W_V, l, 0, lb + 2));
+    DG_TRY(fill(DG_W_O, l, 0, lb + 3));
+    DG_TRY(fill(DG_W_ROUTER, l, 0, lb + 4));
+    if (d.gated) DG_TRY(fill(DG_W_SH_GATE, l, 0, lb + 5));
+    DG_TRY(fill(DG_W_SH_UP, l, 0, lb + 6));
+    DG_TRY(fill(DG_W_SH_DOWN, l, 0, lb + 7));
+    for (int e = 0; e < d.n_experts; ++e) {
+      const uint64_t eb = kExpert + 8ull * (1024ull * l + e);
+      if (d.gated) DG_TRY(fill(DG_W_EX_GATE, l, e, eb + 0));
+      DG_TRY(fill(DG_W_EX_UP, l, e, eb + 1));
+      DG_TRY(fill(DG_W_EX_DOWN, l, e, eb + 2));
+    }
+  }
+  return transpose(w + L.embed, d.vocab, d.d_model, w + L.embed_t, d.dtype, s);
+}
+
+size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity) {
+  if (check_desc(desc) != DG_OK || capacity < 0) return 0;
+  return 2ull * desc->n_layers * desc->n_kv_heads * static_cast<size_t>(capacity) * desc->head_dim * esize(*desc);
+}
+
+size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity) {
+  if (check_desc(desc) != DG_OK || capacity < 0) return 0;
+  return ws_layout(*desc).total;
+}
+
+int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_t capacity, void* d_workspace,
+                  size_t ws_bytes, dg_ctx** out) {
+  DG_TRY(check_desc(desc));
+  if (!out) return fail(DG_ERR_INVALID, "out is NULL");
+  if (!d_weights || !d_kv || !d_workspace) return fail(DG_ERR_INVALID, "weights, KV cache and workspace are required");
+  if (capacity < desc->canvas) return fail(DG_ERR_CAPACITY, "KV capacity must hold at least one canvas");
+  if (capacity > (1ll << 30)) return fail(DG_ERR_CAPACITY, "KV capacity too large");
+  for (const void* p : {d_weights, d_kv, d_workspace})
+    if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return fail(DG_ERR_INVALID, "device buffers must be 256-byte aligned");
+  const WsLayout wl = ws_layout(*desc);
+  if (ws_bytes < wl.total) return fail(DG_ERR_CAPACITY, "workspace too small (see dg_workspace_size)");
+  DG_TRY(zero_fill(d_workspace, wl.total, nullptr));
+  DG_HIP(hipStreamSynchronize(nullptr));
+  dg_ctx* c = new dg_ctx;
+  c->d = *desc;
+  c->w = static_cast<char*>(d_weights);
+  c->kv = static_cast<char*>(d_kv);
+  c->cap = capacity;
+  c->len = 0;
+  c->ws = static_cast<char*>(d_workspace);
+  c->ws_bytes = ws_bytes;
+  c->wl = weight_layout(*desc);
+  c->wsl = wl;
+  *out = c;
+  return DG_OK;
+}
+
+int dg_ctx_destroy(dg_ctx* ctx) {
+  delete ctx;
+  return DG_OK;
+}
+
+int64_t dg_kv_length(const dg_ctx* ctx) { return ctx ? ctx->len : -1; }
+
+int dg_kv_set_length(dg_ctx* ctx, int64_t length) {
+  DG_TRY(check_ctx(ctx));
+  if (length < 0 || length > ctx->cap) return fail(DG_ERR_CAPACITY, "length outside [0, capacity]");
+  ctx->len = length;
+  return DG_OK;
+}
+
+int dg_prefill_kv(dg_ctx* ctx, const int32_t* d_prompt_ids, int32_t n_prompt, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  if (n_prompt < 0) return fail(DG_ERR_SHAPE, "n_prompt must be >= 0");
+  if (n_prompt > 0 && !d_prompt_ids) return fail(DG_ERR_INVALID, "d_prompt_ids is NULL");
+  if (ctx->len + n_prompt > ctx->cap) return fail(DG_ERR_CAPACITY, "prompt does not fit in the KV cache");
+  return encode(ctx, d_prompt_ids, n_prompt, as_stream(stream));
+}
+
+int dg_denoise_step(dg_ctx* ctx, const int32_t* d_canvas, int32_t step, const void* d_prev_logits,
+                    const float* d_prev_row_stats, float prev_temperature, void* d_logits, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  (void)step;
+  if (!d_canvas || !d_logits) return fail(DG_ERR_INVALID, "d_canvas and d_logits are required");
+  if (d_prev_logits && (!d_prev_row_stats || !(prev_temperature > 0.f) || !isfinite(prev_temperature)))
+    return fail(DG_ERR_INVALID, "self-conditioning needs row stats and a positive temperature");
+  if (ctx->len + ctx->d.canvas > ctx->cap) return fail(DG_ERR_CAPACITY, "no room for the canvas in the KV cache");
+  return denoise(ctx, d_canvas, d_prev_logits, d_prev_row_stats, prev_temperature, d_logits, as_stream(stream));
+}
+
+int dg_commit_block(dg_ctx* ctx, const int32_t* d_block_ids, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  if (!d_block_ids) return fail(DG_ERR_INVALID, "d_block_ids is NULL");
+  if (ctx->len + ctx->d.canvas > ctx->cap) return fail(DG_ERR_CAPACITY, "block does not fit in the KV cache");
+  return encode(ctx, d_block_ids, ctx->d.canvas, as_stream(stream));
+}
+
+int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32_t causal, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  if (layer < 0 || layer >= ctx->d.n_layers) return fail(DG_ERR_INVALID, "layer out of range");
+  if (!d_x) return fail(DG_ERR_INVALID, "d_x is NULL");
+  if (rows < 1 || rows > ctx->d.canvas) return fail(DG_ERR_SHAPE, "rows must be in [1, canvas]");
+  if (ctx->len + rows > ctx->cap) return fail(DG_ERR_CAPACITY, "rows do not fit in the KV cache");
+  return layer_forward(ctx, layer, d_x, rows, static_cast<int>(ctx->len), causal != 0, false, as_stream(stream));
+}
+
+int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d_logits, int32_t* d_block_out,
+                      int32_t commit, int32_t* steps_out, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  DG_TRY(check_sched(sched, 0));
+  if (!d_logits || !d_block_out) return fail(DG_ERR_INVALID, "d_logits and d_block_out are required");
+  if (block < 0) return fail(DG_ERR_INVALID, "block must be >= 0");
+  const int need = ctx->d.canvas * (commit ? 1 : 0);
+  if (ctx->len + ctx->d.canvas > ctx->cap || ctx->len + need > ctx->cap)
+    return fail(DG_ERR_CAPACITY, "no room for the canvas in the KV cache");
+  hipStream_t s = as_stream(stream);
+  const WsLayout& w = ctx->wsl;
+  const int C = ctx->d.canvas;
+  int32_t* canvas = wsp<int32_t>(ctx, w.canvas);
+  int32_t* pred = wsp<int32_t>(ctx, w.pred);
+  float* stats = wsp<float>(ctx, w.row_stats);
+  dg_stop_state* stop = wsp<dg_stop_state>(ctx, w.stop);
+  DG_TRY(launch_init_canvas(sched->seed, block, C, ctx->d.vocab, canvas, stop, s));
+  int steps = 0;
+  float prev_t = 0.f;
+  for (int step = 0; step < sched->max_steps; ++step) {
+    const float T = temperature(*sched, step);
+    DG_TRY(denoise(ctx, canvas, step > 0 ? d_logits : nullptr, stats, prev_t, d_logits, s));
+    DG_TRY(launch_sample(d_logits, ctx->d.dtype, C, ctx->d.vocab, T, *sched, step, block, canvas, pred,
+                         wsp<uint8_t>(ctx, w.accept), wsp<float>(ctx, w.entropy), stats, stop,
+                         wsp<void>(ctx, w.samp), s));
+    dg_stop_state host;
+    DG_HIP(hipMemcpyAsync(&host, stop, sizeof host, hipMemcpyDeviceToHost, s));
+    DG_HIP(hipStreamSynchronize(s));
+    steps = step + 1;
+    prev_t = T;
+    if (host.stopped) break;
+  }
+  DG_HIP(hipMemcpyAsync(d_block_out, pred, C * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  if (steps_out) *steps_out = steps;
+  if (commit) DG_TRY(encode(ctx, d_block_out, C, s));
+  return DG_OK;
+}
+
+int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes) {
+  if (!ctx || !d_ptr) return fail(DG_ERR_INVALID, "ctx and d_ptr are required");
+  const dg_model_desc& d = ctx->d;
+  const WsLayout& w = ctx->wsl;
+  const size_t C = d.canvas, es = esize(d);
+  size_t off, n;
+  switch (which) {
+    case DG_BUF_X: off = w.x; n = C * d.d_model * 4; break;
+    case DG_BUF_H: off = w.h; n = C * d.d_model * es; break;
+    case DG_BUF_ROUTER_LOGITS: off = w.rlog; n = C * d.n_experts * 4; break;
+    case DG_BUF_SEL: off = w.sel; n = C * d.top_k * 4; break;
+    case DG_BUF_GATE: off = w.gate; n = C * d.top_k * 4; break;
+    case DG_BUF_SC: off = w.sc; n = C * d.d_model * 4; break;
+    case DG_BUF_CANVAS: off = w.canvas; n = C * 4; break;
+    case DG_BUF_PRED: off = w.pred; n = C * 4; break;
+    case DG_BUF_STOP: off = w.stop; n = sizeof(dg_stop_state); break;
+    case DG_BUF_ENTROPY: off = w.entropy; n = C * 4; break;
+    case DG_BUF_ROW_STATS: off = w.row_stats; n = C * 8; break;
+    case DG_BUF_ACCEPT: off = w.accept; n = C; break;
+    case DG_BUF_Q: off = w.q; n = C * d.n_q_heads * d.head_dim * es; break;
+    case DG_BUF_ATTN: off = w.o; n = C * d.n_q_heads * d.head_dim * es; break;
+    case DG_BUF_SHARED_ACT: off = w.sh_act; n = C * d.d_shared * es; break;
+    case DG_BUF_SLOT_OUT: off = w.slot_out; n = C * d.top_k * d.d_model * 4; break;
+    case DG_BUF_SLOT_OF: off = w.slot_of; n = C * d.top_k * 4; break;
+    default: return fail(DG_ERR_INVALID, "unknown buffer");
+  }
+  *d_ptr = ctx->ws + off;
+  if (bytes) *bytes = n;
+  return DG_OK;
+}
+
+}  // extern "C"

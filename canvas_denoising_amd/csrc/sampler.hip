@@ -7,17 +7,25 @@
 // constants and the stop rule.
 //
 // Split-row design: a [rows x vocab] logits matrix has far too few rows for
-// 256 CUs, so every row is cut into `splits` chunks. One workgroup streams
-// one chunk once (16-byte coalesced loads) and reduces it to a record
-// (m = max logit, Z = sum 2^u, A = sum u 2^u with u = (l - m) * log2(e) / T,
-// argmax index). Records merge exactly:
+// 256 CUs, so every row is cut into `splits` chunks. A workgroup streams one
+// chunk once with 16-byte coalesced loads (the next batch is in flight while
+// the current one is reduced) and reduces it to a record (m = max logit,
+// Z = sum 2^u, A = sum u 2^u with u = (l - m) log2(e) / T, argmax). Records
+// merge exactly:
 //   m = max(m1, m2), d_i = (m_i - m) log2(e)/T,
 //   Z = Z1 2^d1 + Z2 2^d2,  A = 2^d1 (A1 + d1 Z1) + 2^d2 (A2 + d2 Z2),
-// so the finalize pass gets the row entropy H = ln Z - ln2 * A / Z without
-// a second read. The finalize kernel merges the records of each row in a
-// fixed order, applies the accept / re-noise rule with Philox, and reduces
-// the canvas mean entropy and the stop state in a fixed order (results are
-// bitwise reproducible).
+// and the row entropy is H = ln Z - ln2 * A / Z, so no second read is needed.
+// The argmax is not tracked per element: each thread remembers the batch in
+// which its running maximum first appeared and, if that maximum is the
+// chunk's, re-reads that one batch to find the lowest index holding it.
+//
+// A second, single-workgroup kernel merges each row's records in a fixed
+// tree order (one wave per row, one record per lane), applies the accept /
+// Philox re-noise rule, and reduces the canvas mean entropy and the
+// stability test in a fixed order into the stop state. (Folding this into
+// the first kernel with a last-workgroup atomic costs a cache write-back and
+// invalidate per workgroup at agent scope, far more than a second launch.)
+// Results are bitwise reproducible.
 #include <math.h>
 
 #include <algorithm>
@@ -35,12 +43,13 @@ struct Rec {
   int idx;   // lowest index attaining m
 };
 
+// merge y into x; `c` = log2(e) / T. Deterministic for a fixed merge order.
 __device__ inline void rec_merge(Rec& x, const Rec& y, float c) {
   if (y.z == 0.f) return;
   if (x.z == 0.f) { x = y; return; }
   const float m = fmaxf(x.m, y.m);
   const float dx = (x.m - m) * c, dy = (y.m - m) * c;
-  const float sx = exp2f(dx), sy = exp2f(dy);
+  const float sx = __builtin_amdgcn_exp2f(dx), sy = __builtin_amdgcn_exp2f(dy);
   const int idx = (x.m > y.m) ? x.idx : (y.m > x.m) ? y.idx : min(x.idx, y.idx);
   x.a = sx * (x.a + dx * x.z) + sy * (y.a + dy * y.z);
   x.z = x.z * sx + y.z * sy;
@@ -57,20 +66,44 @@ __device__ inline Rec rec_shfl_xor(const Rec& r, int mask) {
   return o;
 }
 
-// 8 consecutive logits as fp32
-template <typename T> struct Load8;
-template <> struct Load8<bf16_t> {
-  __device__ static inline void run(const bf16_t* p, float* v) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
-    v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+constexpr int kSampThreads = 256;
+constexpr int kVec = 8;      // elements per 16-byte (bf16) / 32-byte (fp32) group
+constexpr int kUnroll = 4;   // groups per thread per batch
+constexpr int kBatch = kSampThreads * kVec * kUnroll;  // elements per workgroup batch
+constexpr int kMaxSplits = 64;
+
+// raw storage of one thread's batch: kUnroll groups of 8 elements
+template <typename T> struct Raw;
+template <> struct Raw<bf16_t> {
+  uint4 q[kUnroll];
+  __device__ inline void load(const bf16_t* p) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = *reinterpret_cast<const uint4*>(p + u * kSampThreads * kVec);
+  }
+  __device__ inline void unpack(float* v) const {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      v[u * 8 + 0] = bf16lo(q[u].x); v[u * 8 + 1] = bf16hi(q[u].x);
+      v[u * 8 + 2] = bf16lo(q[u].y); v[u * 8 + 3] = bf16hi(q[u].y);
+      v[u * 8 + 4] = bf16lo(q[u].z); v[u * 8 + 5] = bf16hi(q[u].z);
+      v[u * 8 + 6] = bf16lo(q[u].w); v[u * 8 + 7] = bf16hi(q[u].w);
+    }
   }
 };
-template <> struct Load8<float> {
-  __device__ static inline void run(const float* p, float* v) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+template <> struct Raw<float> {
+  float4 q[2 * kUnroll];
+  __device__ inline void load(const float* p) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      q[2 * u] = *reinterpret_cast<const float4*>(p + u * kSampThreads * kVec);
+      q[2 * u + 1] = *reinterpret_cast<const float4*>(p + u * kSampThreads * kVec + 4);
+    }
+  }
+  __device__ inline void unpack(float* v) const {
+#pragma unroll
+    for (int u = 0; u < 2 * kUnroll; ++u) {
+      v[u * 4 + 0] = q[u].x; v[u * 4 + 1] = q[u].y; v[u * 4 + 2] = q[u].z; v[u * 4 + 3] = q[u].w;
+    }
   }
 };
 
@@ -78,31 +111,22 @@ template <typename T> __device__ inline float load1(const T* p);
 template <> __device__ inline float load1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 template <> __device__ inline float load1<float>(const float* p) { return *p; }
 
-constexpr int kSampThreads = 256;
-constexpr int kVec = 8;      // elements per vector load
-constexpr int kUnroll = 4;   // vector loads per thread per batch
-constexpr int kBatch = kSampThreads * kVec * kUnroll;  // elements per workgroup batch
-
-// Accumulate N fp32 values into the running record. Value j sits at logit index
-// idx0 + (j / 8) * gstride + (j % 8); within the thread indices grow with j, so
-// the first strictly larger value is the lowest index of the batch maximum.
+// fold N values into the running (m, z, a); returns true when the running max grew
 template <int N>
-__device__ inline void accumulate(const float* v, int64_t idx0, int64_t gstride, float c, Rec& r) {
+__device__ inline bool fold(const float* v, float c, Rec& r) {
   float bm = v[0];
-  int bk = 0;
 #pragma unroll
-  for (int j = 1; j < N; ++j) {
-    if (v[j] > bm) { bm = v[j]; bk = j; }
-  }
-  if (bm > r.m) {  // new running max: rescale what was accumulated so far
+  for (int j = 1; j < N; ++j) bm = fmaxf(bm, v[j]);
+  bool grew = false;
+  if (bm > r.m) {
     if (r.z != 0.f) {
       const float d = (r.m - bm) * c;
-      const float s = exp2f(d);
+      const float s = __builtin_amdgcn_exp2f(d);
       r.a = s * (r.a + d * r.z);
       r.z *= s;
     }
     r.m = bm;
-    r.idx = static_cast<int>(idx0 + (bk >> 3) * gstride + (bk & 7));
+    grew = true;
   }
   const float off = -r.m * c;
   float z = 0.f, a = 0.f;
@@ -115,112 +139,226 @@ __device__ inline void accumulate(const float* v, int64_t idx0, int64_t gstride,
   }
   r.z += z;
   r.a += a;
+  return grew;
 }
 
-// grid (splits, rows); each workgroup reduces logits[row, sp*chunk : (sp+1)*chunk)
+struct SampleArgs {
+  const void* logits;
+  int64_t vocab;
+  int64_t chunk;
+  int rows, splits;
+  float c;  // log2(e) / T
+  float bound, stop_thr;
+  int stable_needed;
+  uint64_t seed;
+  int step, block;
+  int32_t* canvas;
+  int32_t* pred;
+  uint8_t* accept;
+  float* entropy;
+  float* row_stats;
+  dg_stop_state* stop;
+  Rec* recs;  // scratch [rows][splits]
+};
+
+// grid (splits, rows)
 template <typename T, bool kVecPath>
-__global__ __launch_bounds__(kSampThreads) void sample_partial_kernel(
-    const T* __restrict__ logits, int64_t vocab, int64_t chunk, float c,
-    const dg_stop_state* __restrict__ stop, Rec* __restrict__ recs) {
-  if (stop != nullptr && stop->stopped) return;
+__global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
+  if (g.stop->stopped) return;
   const int sp = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const int64_t begin = sp * chunk;
-  const int64_t end = min(begin + chunk, vocab);
-  const T* p = logits + static_cast<int64_t>(row) * vocab;
+  const int lane = tid & 63, wave = tid >> 6;
+  const float c = g.c;
+  const int64_t begin = sp * g.chunk;
+  const int64_t end = min(begin + g.chunk, g.vocab);
+  const T* p = static_cast<const T*>(g.logits) + static_cast<int64_t>(row) * g.vocab;
   Rec r{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
+  __shared__ Rec sh[kSampThreads / 64];
+  __shared__ int sh_idx[kSampThreads / 64];
 
   if (kVecPath) {
-    // full batches: every thread owns kUnroll groups of 8 consecutive elements
-    int64_t base = begin;
-    for (; base + kBatch <= end; base += kBatch) {
-      float v[kUnroll * kVec];
-      const int64_t t0 = base + static_cast<int64_t>(tid) * kVec;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) Load8<T>::run(p + t0 + static_cast<int64_t>(u) * kSampThreads * kVec, v + u * kVec);
-      accumulate<kUnroll * kVec>(v, t0, static_cast<int64_t>(kSampThreads) * kVec, c, r);
+    // whole batches, software-pipelined: batch b+1 is loaded while batch b is folded
+    const int64_t nb = (end - begin) / kBatch;
+    const T* tp = p + begin + static_cast<int64_t>(tid) * kVec;
+    int64_t first = -1;  // batch where this thread's running max first appeared
+    Raw<T> qa, qb;
+    if (nb > 0) qa.load(tp);
+    for (int64_t b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) qb.load(tp + (b + 1) * kBatch);
+      {
+        float v[kUnroll * kVec];
+        qa.unpack(v);
+        if (fold<kUnroll * kVec>(v, c, r)) first = b;
+      }
+      if (b + 1 < nb) {
+        if (b + 2 < nb) qa.load(tp + (b + 2) * kBatch);
+        float v[kUnroll * kVec];
+        qb.unpack(v);
+        if (fold<kUnroll * kVec>(v, c, r)) first = b + 1;
+      }
     }
-    // tail: whole groups of 8 (vocab % 8 == 0 on this path)
-    for (int64_t e0 = base + static_cast<int64_t>(tid) * kVec; e0 < end; e0 += static_cast<int64_t>(kSampThreads) * kVec) {
+    // tail: whole groups of 8 (vocab % 8 == 0 on this path), index tracked directly
+    const int64_t tail0 = begin + nb * kBatch;
+    int tail_idx = 0x7FFFFFFF;
+    for (int64_t e0 = tail0 + static_cast<int64_t>(tid) * kVec; e0 < end; e0 += static_cast<int64_t>(kSampThreads) * kVec) {
       float v[kVec];
-      Load8<T>::run(p + e0, v);
-      accumulate<kVec>(v, e0, 0, c, r);
+      if constexpr (sizeof(T) == 2) {
+        const uint4 q = *reinterpret_cast<const uint4*>(p + e0);
+        v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+        v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) v[j] = load1<T>(p + e0 + j);
+      }
+      float bm = v[0];
+      int bj = 0;
+#pragma unroll
+      for (int j = 1; j < kVec; ++j)
+        if (v[j] > bm) { bm = v[j]; bj = j; }
+      if (fold<kVec>(v, c, r)) { first = -1; tail_idx = static_cast<int>(e0 + bj); }
+    }
+    // wave / workgroup merge of (m, z, a) in a fixed order
+    Rec w = r;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const Rec o = rec_shfl_xor(w, m);
+      rec_merge(w, o, c);
+    }
+    if (lane == 0) sh[wave] = w;
+    __syncthreads();
+    Rec tot = sh[0];
+#pragma unroll
+    for (int i = 1; i < kSampThreads / 64; ++i) rec_merge(tot, sh[i], c);
+    // argmax: lowest index holding the chunk maximum
+    int my_idx = 0x7FFFFFFF;
+    if (r.z != 0.f && r.m == tot.m) {
+      if (first >= 0) {
+        Raw<T> q;
+        q.load(tp + first * kBatch);
+        float v[kUnroll * kVec];
+        q.unpack(v);
+#pragma unroll
+        for (int j = kUnroll * kVec - 1; j >= 0; --j)
+          if (v[j] == tot.m) my_idx = static_cast<int>(begin + first * kBatch + tid * kVec + (j / kVec) * kSampThreads * kVec + (j % kVec));
+      } else {
+        my_idx = tail_idx;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) my_idx = min(my_idx, shfl_xor(my_idx, m));
+    if (lane == 0) sh_idx[wave] = my_idx;
+    __syncthreads();
+    if (tid == 0) {
+      int bi = sh_idx[0];
+#pragma unroll
+      for (int i = 1; i < kSampThreads / 64; ++i) bi = min(bi, sh_idx[i]);
+      tot.idx = bi;
+      g.recs[static_cast<int64_t>(row) * g.splits + sp] = tot;
     }
   } else {
+    // scalar path (vocab not a multiple of 8): index tracked per element
     for (int64_t e = begin + tid; e < end; e += kSampThreads) {
       float v[1] = {load1<T>(p + e)};
-      accumulate<1>(v, e, 0, c, r);
+      if (fold<1>(v, c, r)) r.idx = static_cast<int>(e);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const Rec o = rec_shfl_xor(r, m);
+      rec_merge(r, o, c);
+    }
+    if (lane == 0) sh[wave] = r;
+    __syncthreads();
+    if (tid == 0) {
+      Rec tot = sh[0];
+      for (int i = 1; i < kSampThreads / 64; ++i) rec_merge(tot, sh[i], c);
+      g.recs[static_cast<int64_t>(row) * g.splits + sp] = tot;
     }
   }
 
-  // wave then workgroup reduction (fixed butterfly / fixed wave order)
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const Rec o = rec_shfl_xor(r, m);
-    rec_merge(r, o, c);
-  }
-  __shared__ Rec sh[kSampThreads / 64];
-  const int wave = tid >> 6, lane = tid & 63;
-  if (lane == 0) sh[wave] = r;
-  __syncthreads();
-  if (tid == 0) {
-    Rec acc = sh[0];
-    for (int w = 1; w < kSampThreads / 64; ++w) rec_merge(acc, sh[w], c);
-    recs[static_cast<int64_t>(row) * gridDim.x + sp] = acc;
-  }
 }
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinRows = 4;  // rows per wave per pass (their record loads are issued together)
 
-// one workgroup: merge split records per row, accept / re-noise, canvas stats, stop rule
-__global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(
-    const Rec* __restrict__ recs, int rows, int splits, float c, float inv_temp,
-    float bound, float stop_thr, int stable_needed, uint64_t seed, int step, int block, uint32_t vocab,
-    int32_t* __restrict__ canvas, int32_t* __restrict__ pred, uint8_t* __restrict__ accept,
-    float* __restrict__ entropy, float* __restrict__ row_stats, dg_stop_state* __restrict__ stop) {
-  if (stop != nullptr && stop->stopped) return;
-  const int tid = threadIdx.x;
-  float hsum = 0.f;
+// One workgroup. Phase A: wave w merges the split records of rows w, w + 16, ... (lane s loads
+// record s; fixed butterfly) into LDS. Phase B: thread t finalises row t (accept, Philox re-noise,
+// outputs). Then the canvas mean entropy, the stability test and the stop rule are reduced in a
+// fixed order.
+__global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs g) {
+  if (g.stop->stopped) return;
+  __shared__ Rec merged[kFinThreads];
+  __shared__ float shs[kFinWaves];
+  __shared__ int shq[kFinWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float c = g.c;
+  float hs = 0.f;
   int same = 1;
-  for (int row = tid; row < rows; row += kFinThreads) {
-    Rec r = recs[static_cast<int64_t>(row) * splits];
-    for (int s = 1; s < splits; ++s) rec_merge(r, recs[static_cast<int64_t>(row) * splits + s], c);
-    const float lnz = logf(r.z);
-    const float H = lnz - kLn2 * r.a / r.z;
-    const bool acc = H <= bound;
-    const int32_t prv = pred[row];
-    same &= (prv == r.idx) ? 1 : 0;
-    pred[row] = r.idx;
-    canvas[row] = acc ? r.idx
-                      : draw_token(seed, static_cast<uint32_t>(row), static_cast<uint32_t>(step),
-                                   static_cast<uint32_t>(block), kPurposeRenoise, vocab);
-    if (accept) accept[row] = acc ? 1 : 0;
-    if (entropy) entropy[row] = H;
-    if (row_stats) {
-      row_stats[2 * row] = r.m;
-      row_stats[2 * row + 1] = lnz;
+  for (int base = 0; base < g.rows; base += kFinThreads) {
+    const int nrows = min(kFinThreads, g.rows - base);
+    for (int r0 = wave; r0 < nrows; r0 += kFinWaves * kFinRows) {
+      Rec rr[kFinRows];
+#pragma unroll
+      for (int j = 0; j < kFinRows; ++j) {
+        const int row = r0 + j * kFinWaves;
+        rr[j] = Rec{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
+        if (row < nrows && lane < g.splits) rr[j] = g.recs[static_cast<int64_t>(base + row) * g.splits + lane];
+      }
+#pragma unroll
+      for (int j = 0; j < kFinRows; ++j)
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+          const Rec o = rec_shfl_xor(rr[j], m);
+          rec_merge(rr[j], o, c);
+        }
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kFinRows; ++j)
+          if (r0 + j * kFinWaves < nrows) merged[r0 + j * kFinWaves] = rr[j];
+      }
     }
-    hsum += H;
+    __syncthreads();
+    if (tid < nrows) {
+      const int row = base + tid;
+      const Rec r = merged[tid];
+      // The fold evaluates u = fma(l, c, -round(m c)): every u of a chunk carries the residual
+      // delta = m c - round(m c); it cancels in H but not in ln Z.
+      const float mc = r.m * c;
+      const float delta = fmaf(r.m, c, -mc);
+      const float lz = logf(r.z);
+      const float H = lz - kLn2 * r.a / r.z;
+      const bool acc = H <= g.bound;
+      same &= g.pred[row] == r.idx ? 1 : 0;
+      g.pred[row] = r.idx;
+      g.canvas[row] = acc ? r.idx
+                          : draw_token(g.seed, static_cast<uint32_t>(row), static_cast<uint32_t>(g.step),
+                                       static_cast<uint32_t>(g.block), kPurposeRenoise,
+                                       static_cast<uint32_t>(g.vocab));
+      if (g.accept) g.accept[row] = acc ? 1 : 0;
+      if (g.entropy) g.entropy[row] = H;
+      if (g.row_stats) {
+        g.row_stats[2 * row] = r.m;
+        g.row_stats[2 * row + 1] = lz - delta * kLn2;
+      }
+      hs += H;
+    }
+    __syncthreads();
   }
-  (void)inv_temp;
-  hsum = wave_sum(hsum);
-  // wave-wide AND of `same`
+  hs = wave_sum(hs);
+#pragma unroll
   for (int m = 32; m >= 1; m >>= 1) same &= shfl_xor(same, m);
-  __shared__ float shs[kFinThreads / 64];
-  __shared__ int shq[kFinThreads / 64];
-  const int wave = tid >> 6, lane = tid & 63;
-  if (lane == 0) { shs[wave] = hsum; shq[wave] = same; }
+  if (lane == 0) { shs[wave] = hs; shq[wave] = same; }
   __syncthreads();
   if (tid == 0) {
-    float tot = shs[0];
+    float t = shs[0];
     int all = shq[0];
-    for (int w = 1; w < kFinThreads / 64; ++w) { tot += shs[w]; all &= shq[w]; }
-    const float meanH = tot / static_cast<float>(rows);
-    dg_stop_state st = *stop;
-    st.stable_count = (step > 0 && all) ? st.stable_count + 1 : 0;
+    for (int w = 1; w < kFinWaves; ++w) { t += shs[w]; all &= shq[w]; }
+    const float meanH = t / static_cast<float>(g.rows);
+    dg_stop_state st = *g.stop;
+    st.stable_count = (g.step > 0 && all) ? st.stable_count + 1 : 0;
     st.mean_entropy = meanH;
-    st.stopped = (meanH < stop_thr && st.stable_count >= stable_needed) ? 1 : 0;
-    st.steps_run = step + 1;
-    *stop = st;
+    st.stopped = (meanH < g.stop_thr && st.stable_count >= g.stable_needed) ? 1 : 0;
+    st.steps_run = g.step + 1;
+    *g.stop = st;
   }
 }
 
@@ -242,23 +380,26 @@ __global__ void init_canvas_kernel(uint64_t seed, int block, int n, uint32_t voc
 struct SplitPlan { int64_t splits, chunk; };
 
 static SplitPlan plan_splits(int64_t rows, int64_t vocab) {
-  const int64_t gran = kSampThreads * kVec;  // 2048
+  const int64_t gran = kBatch;  // 8192 elements: whole batches
   const int64_t target_wgs = 4096;
   int64_t s = std::max<int64_t>(1, std::min<int64_t>(ceil_div(vocab, gran), ceil_div(target_wgs, rows)));
-  int64_t chunk = ceil_div(ceil_div(vocab, s), gran) * gran;
+  s = std::min<int64_t>(s, kMaxSplits);
+  int64_t chunk = ceil_div(ceil_div(vocab, s), kVec) * kVec;
+  if (chunk >= gran) chunk = ceil_div(chunk, gran) * gran;
   s = ceil_div(vocab, chunk);
   return {s, chunk};
 }
 
 size_t sample_workspace_bytes(int64_t rows, int64_t vocab) {
   const SplitPlan p = plan_splits(rows, vocab);
-  return static_cast<size_t>(rows * p.splits) * sizeof(Rec);
+  return (static_cast<size_t>(rows * p.splits) * sizeof(Rec) + 255) / 256 * 256;
 }
 
 int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
                        hipStream_t stream) {
   const int threads = 256;
   const int grid = std::max(1, static_cast<int>(ceil_div(n, threads)));
+  ProfScope ps("init_canvas", stream);
   init_canvas_kernel<<<grid, threads, 0, stream>>>(seed, block, n, static_cast<uint32_t>(vocab), canvas, stop);
   DG_LAUNCH_CHECK("init_canvas_kernel");
   return DG_OK;
@@ -268,32 +409,37 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
                   int block, int32_t* canvas, int32_t* pred, uint8_t* accept, float* entropy, float* row_stats,
                   dg_stop_state* stop, void* ws, hipStream_t stream) {
   const SplitPlan p = plan_splits(rows, vocab);
-  const float c = kLog2e / temp;
-  Rec* recs = static_cast<Rec*>(ws);
+  SampleArgs g;
+  g.logits = logits;
+  g.vocab = vocab;
+  g.chunk = p.chunk;
+  g.rows = rows;
+  g.splits = static_cast<int>(p.splits);
+  g.c = kLog2e / temp;
+  g.bound = sc.entropy_bound;
+  g.stop_thr = sc.stop_mean_entropy;
+  g.stable_needed = sc.stable_needed;
+  g.seed = sc.seed;
+  g.step = step;
+  g.block = block;
+  g.canvas = canvas; g.pred = pred; g.accept = accept; g.entropy = entropy; g.row_stats = row_stats; g.stop = stop;
+  g.recs = static_cast<Rec*>(ws);
   dim3 grid(static_cast<unsigned>(p.splits), static_cast<unsigned>(rows));
   {
-  ProfScope ps("sample_partial", stream);
-  if (dtype == DG_BF16) {
-    const bf16_t* l = static_cast<const bf16_t*>(logits);
-    if (vocab % kVec == 0)
-      sample_partial_kernel<bf16_t, true><<<grid, kSampThreads, 0, stream>>>(l, vocab, p.chunk, c, stop, recs);
-    else
-      sample_partial_kernel<bf16_t, false><<<grid, kSampThreads, 0, stream>>>(l, vocab, p.chunk, c, stop, recs);
-  } else {
-    const float* l = static_cast<const float*>(logits);
-    if (vocab % kVec == 0)
-      sample_partial_kernel<float, true><<<grid, kSampThreads, 0, stream>>>(l, vocab, p.chunk, c, stop, recs);
-    else
-      sample_partial_kernel<float, false><<<grid, kSampThreads, 0, stream>>>(l, vocab, p.chunk, c, stop, recs);
+    ProfScope ps("sample_partial", stream);
+    const bool vec = vocab % kVec == 0;
+    if (dtype == DG_BF16) {
+      if (vec) sample_kernel<bf16_t, true><<<grid, kSampThreads, 0, stream>>>(g);
+      else sample_kernel<bf16_t, false><<<grid, kSampThreads, 0, stream>>>(g);
+    } else {
+      if (vec) sample_kernel<float, true><<<grid, kSampThreads, 0, stream>>>(g);
+      else sample_kernel<float, false><<<grid, kSampThreads, 0, stream>>>(g);
+    }
   }
-  }
-  DG_LAUNCH_CHECK("sample_partial_kernel");
+  DG_LAUNCH_CHECK("sample_kernel");
   {
-  ProfScope ps("sample_finalize", stream);
-  sample_finalize_kernel<<<1, kFinThreads, 0, stream>>>(
-      recs, rows, static_cast<int>(p.splits), c, 1.0f / temp, sc.entropy_bound, sc.stop_mean_entropy,
-      sc.stable_needed, sc.seed, step, block, static_cast<uint32_t>(vocab), canvas, pred, accept, entropy,
-      row_stats, stop);
+    ProfScope ps("sample_finalize", stream);
+    sample_finalize_kernel<<<1, kFinThreads, 0, stream>>>(g);
   }
   DG_LAUNCH_CHECK("sample_finalize_kernel");
   return DG_OK;

@@ -26,18 +26,93 @@ class SamplerState:
         self.row_stats = torch.zeros(rows, 2, dtype=torch.float32, device=device)
         self.stop = torch.zeros(4, dtype=torch.int32, device=device)  # dg_stop_state
         self.ws_bytes = max(256, L.dg_sample_workspace_size(rows, vocab))
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.workspace = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)  # counters start at zero
 
     def init(self, sched, block: int, stream=None):
         L.dg_init_canvas(sched, block, self.rows, self.vocab, self.canvas, self.stop, stream)
 
     def sample(self, logits: torch.Tensor, sched, step: int, block: int, stream=None):
         dt = L.DG_BF16 if logits.dtype == torch.bfloat16 else L.DG_F32
-        L.dg_sample_canvas(logits, dt, self.rows, self.vocab, sched, step, block, self.canvas, self.pred,
-                           self.accept, self.entropy, self.row_stats, self.stop, self.workspace, self.ws_bytes,
-                           stream)
+        if not hasattr(self, "_ptrs"):  # device addresses never change: marshal them once
+            self._ptrs = tuple(t.data_ptr() for t in (self.canvas, self.pred, self.accept, self.entropy,
+                                                      self.row_stats, self.stop, self.workspace))
+        L.dg_sample_canvas(logits.data_ptr(), dt, self.rows, self.vocab, sched, step, block, *self._ptrs,
+                           self.ws_bytes, stream)
 
     def stop_state(self) -> dict:
-        s = self.stop.cpu()
-        return {"mean_entropy": s[0:1].view(torch.float32).item(), "stable_count": int(s[1]),
-                "stopped": int(s[2]), "steps_run": int(s[3])}
+        return stop_dict(self.stop)
+
+
+def stop_dict(stop: torch.Tensor) -> dict:
+    s = stop.cpu()
+    return {"mean_entropy": s[0:1].view(torch.float32).item(), "stable_count": int(s[1]),
+            "stopped": int(s[2]), "steps_run": int(s[3])}
+
+
+class Model:
+    """A libdg context over torch-allocated weights, KV cache and workspace."""
+
+    def __init__(self, desc, capacity: int, seed: int | None = 0, sigma: float = 0.02, device="cuda"):
+        self.desc = desc
+        self.capacity = capacity
+        self.dtype = torch_dtype(desc.dtype)
+        self.weights = torch.empty(L.dg_weights_bytes(desc), dtype=torch.uint8, device=device)
+        if seed is not None:
+            L.dg_synth_fill_weights(desc, seed, sigma, self.weights)
+        self.kv = torch.zeros(L.dg_kv_bytes(desc, capacity), dtype=torch.uint8, device=device)
+        self.ws_bytes = L.dg_workspace_size(desc, capacity)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+        self.ctx = L.dg_ctx_create(desc, self.weights, self.kv, capacity, self.workspace, self.ws_bytes)
+        self.logits = torch.empty(desc.canvas, desc.vocab, dtype=self.dtype, device=device)
+
+    def close(self):
+        if self.ctx:
+            L.dg_ctx_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # --- views
+    def tensor(self, kind, layer=0, expert=0) -> torch.Tensor:
+        off, r, c = L.dg_weight_tensor(self.desc, kind, layer, expert)
+        es = 2 if self.desc.dtype == L.DG_BF16 else 4
+        return self.weights[off:off + r * c * es].view(self.dtype).view(r, c)
+
+    def kv_view(self):
+        """(K, V) as [n_layers, n_kv_heads, capacity, head_dim] tensors."""
+        d = self.desc
+        t = self.kv.view(self.dtype).view(2, d.n_layers, d.n_kv_heads, self.capacity, d.head_dim)
+        return t[0], t[1]
+
+    def buffer(self, which, dtype, shape) -> torch.Tensor:
+        ptr, nbytes = L.dg_ctx_buffer(self.ctx, which)
+        base = self.workspace.data_ptr()
+        off = ptr - base
+        return self.workspace[off:off + nbytes].view(dtype).view(*shape)
+
+    @property
+    def length(self) -> int:
+        return L.dg_kv_length(self.ctx)
+
+    # --- calls
+    def prefill(self, ids: torch.Tensor):
+        L.dg_prefill_kv(self.ctx, ids, ids.numel())
+
+    def denoise_step(self, canvas, step, prev_logits=None, prev_row_stats=None, prev_temperature=0.0, logits=None):
+        out = self.logits if logits is None else logits
+        L.dg_denoise_step(self.ctx, canvas, step, prev_logits, prev_row_stats, prev_temperature, out)
+        return out
+
+    def commit(self, ids):
+        L.dg_commit_block(self.ctx, ids)
+
+    def forward_layer(self, layer, x, rows, causal=False):
+        L.dg_forward_layer(self.ctx, layer, x, rows, causal)
+
+    def generate_block(self, sched, block, block_out, commit=True) -> int:
+        return L.dg_generate_block(self.ctx, sched, block, self.logits, block_out, commit)

@@ -148,7 +148,9 @@ int dg_init_canvas(const dg_sched* sched, int32_t block, int32_t canvas, int32_t
  *  d_pred      int32[rows], in: previous step's argmax; out: this step's.
  *  d_accept    uint8[rows], d_entropy float[rows], d_row_stats float[rows x 2]
  *              (any of these three may be NULL).
- *  d_workspace >= dg_sample_workspace_size(rows, vocab) bytes, 256-aligned.
+ *  d_workspace >= dg_sample_workspace_size(rows, vocab) bytes, 256-aligned
+ *              (per-chunk partial records); calls sharing it must not overlap.
+ * Two kernels: a split-row partial pass and a one-workgroup finalize.
  * rows in [1, 65535], vocab in [1, 2^31 - 1]. */
 int dg_sample_canvas(const void* d_logits, int32_t dtype, int32_t rows, int32_t vocab,
                      const dg_sched* sched, int32_t step, int32_t block,
@@ -171,6 +173,138 @@ int dg_synth_uniform_ids(uint64_t seed, uint64_t tid, int64_t n, int32_t vocab,
  * column in about 70% of the rows (buffer index `step` selects the stream). */
 int dg_synth_planted_logits(uint64_t seed, int32_t step, int32_t rows, int32_t vocab,
                             float sigma, float peak, void* d_out, void* stream);
+/* Fill a packed weight buffer (see dg_weight_tensor) with synthetic values of
+ * standard deviation sigma: tensor (kind, layer, expert) uses stream
+ * tid = 1 (embedding), 2 / 3 (self-conditioning W1 / W2),
+ * 2^20 + 64 layer + {0 q, 1 k, 2 v, 3 o, 4 router, 5 shared gate, 6 shared up,
+ * 7 shared down}, 2^32 + 8 (1024 layer + expert) + {0 gate, 1 up, 2 down};
+ * element i is the row-major index inside the tensor. Then derives the
+ * transposed embedding (dg_prepare_weights). */
+int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights,
+                          void* stream);
+
+/* --------------------------------------------------------------- model */
+/* Weight tensors inside the packed, caller-owned weight buffer. */
+enum {
+  DG_W_EMBED = 0,    /* [vocab x d_model], tied input embedding and LM head */
+  DG_W_EMBED_T = 1,  /* [d_model x vocab], derived copy of EMBED transposed */
+  DG_W_SC1 = 2,      /* [d_selfcond x d_model] self-conditioning FFN, first */
+  DG_W_SC2 = 3,      /* [d_model x d_selfcond] self-conditioning FFN, second */
+  DG_W_Q = 4,        /* [n_q_heads*head_dim x d_model] (per layer) */
+  DG_W_K = 5,        /* [n_kv_heads*head_dim x d_model] */
+  DG_W_V = 6,        /* [n_kv_heads*head_dim x d_model] */
+  DG_W_O = 7,        /* [d_model x n_q_heads*head_dim] */
+  DG_W_ROUTER = 8,   /* [n_experts x d_model] */
+  DG_W_SH_GATE = 9,  /* [d_shared x d_model] (gated models only) */
+  DG_W_SH_UP = 10,   /* [d_shared x d_model] */
+  DG_W_SH_DOWN = 11, /* [d_model x d_shared] */
+  DG_W_EX_GATE = 12, /* [d_expert x d_model] (per layer and expert; gated only) */
+  DG_W_EX_UP = 13,   /* [d_expert x d_model] */
+  DG_W_EX_DOWN = 14  /* [d_model x d_expert] */
+};
+
+/* Total bytes of the packed weight buffer (every tensor 256-byte aligned). */
+size_t dg_weights_bytes(const dg_model_desc* desc);
+/* Byte offset and [rows x cols] shape of one tensor; layer / expert are
+ * ignored where they do not apply. Q, K and V of a layer are adjacent (one
+ * fused projection), as are gate and up of the shared expert and of each
+ * routed expert. */
+int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
+                     size_t* offset, int64_t* rows, int64_t* cols);
+/* Rebuild DG_W_EMBED_T from DG_W_EMBED (call after loading weights). */
+int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream);
+
+/* KV cache: keys then values, each [n_layers][n_kv_heads][capacity][head_dim]
+ * in the model dtype. */
+size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
+/* Scratch the context needs: activations of one canvas (or one prompt chunk
+ * of up to `canvas` rows), MoE routing tables, split-K partials,
+ * self-conditioning buffers and the sampler state of dg_generate_block. */
+size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity);
+
+/* Create a context over caller-owned weights, KV cache and workspace (none is
+ * copied; all must outlive the context). Zero-fills the workspace (blocking,
+ * on the default stream). capacity = KV positions. The committed length
+ * starts at 0. Limits: canvas <= 256, head_dim 64 or 128 (bf16), d_model,
+ * head dims and FFN widths multiples of 64 (bf16) / 32 (fp32), n_experts <=
+ * 256, top_k <= 16. */
+int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_t capacity,
+                  void* d_workspace, size_t ws_bytes, dg_ctx** out);
+int dg_ctx_destroy(dg_ctx* ctx);  /* frees the host descriptor only */
+int64_t dg_kv_length(const dg_ctx* ctx);
+/* Declare the first `length` cache positions valid without computing them
+ * (for caches filled by the caller). */
+int dg_kv_set_length(dg_ctx* ctx, int64_t length);
+
+/* Encoder mode over the prompt ([P3] "Encoder-denoiser design": the query is
+ * processed the standard, causal way and its KV cache is shared with the
+ * denoiser; [P4] "System architecture": prefill builds the KV cache). Runs the
+ * layers causally over d_prompt_ids (int32[n_prompt]) in chunks of `canvas`
+ * rows appended at the committed length, then length += n_prompt.
+ * DG_ERR_CAPACITY (nothing enqueued) if length + n_prompt > capacity. */
+int dg_prefill_kv(dg_ctx* ctx, const int32_t* d_prompt_ids, int32_t n_prompt, void* stream);
+
+/* Denoiser mode, one step ([P3] "Encoder-denoiser design": bidirectional
+ * attention over the whole canvas, logits at every canvas position; [P3]
+ * "Inference mechanism": self-conditioning). With C = canvas:
+ *   if d_prev_logits != NULL: p = softmax(prev_logits / prev_temperature)
+ *     rebuilt from d_prev_row_stats (dg_sample_canvas output), u = p E,
+ *     sc = GeLU(u W1^T) W2^T; else sc = 0;
+ *   x = E[canvas] + sc; every layer: attention of the C rows over cache
+ *   positions [0, length) and the C canvas rows (no mask; the canvas K/V go
+ *   to cache slots [length, length + C) as scratch), then the MoE FFN;
+ *   logits = RMSNorm(x) E^T -> d_logits [C x vocab] (model dtype).
+ * d_prev_logits may alias d_logits (it is read before the LM head writes).
+ * Needs length + C <= capacity. `step` is informational. */
+int dg_denoise_step(dg_ctx* ctx, const int32_t* d_canvas, int32_t step, const void* d_prev_logits,
+                    const float* d_prev_row_stats, float prev_temperature, void* d_logits,
+                    void* stream);
+
+/* Block commit ([P3] "Inference mechanism": multi-canvas sampling appends the
+ * finished 256 tokens to the prompt and reuses the encoder KV cache; [P4]
+ * "Block Diffusion"): encoder pass over d_block_ids (int32[canvas]) at the
+ * committed length, then length += canvas. DG_ERR_CAPACITY if it does not fit. */
+int dg_commit_block(dg_ctx* ctx, const int32_t* d_block_ids, void* stream);
+
+/* One layer on a caller-provided fp32 residual d_x [rows x d_model] (in/out),
+ * rows <= canvas, attending to cache [0, length) plus the rows (causal or
+ * not); the rows' K/V are written at [length, length + rows); length is not
+ * changed. */
+int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32_t causal,
+                     void* stream);
+
+/* Native denoising loop of one canvas ([P4] "Reverse diffusion process" and
+ * "Two-Fold Adaptive Stopping"): dg_init_canvas, then for step = 0 ..
+ * max_steps-1: dg_denoise_step (self-conditioned on the previous step),
+ * dg_sample_canvas, and a 16-byte read-back of the stop state; the block is
+ * the final step's argmax, copied to d_block_out (int32[canvas]); with
+ * commit != 0 it is then committed. d_logits: [canvas x vocab] caller
+ * scratch. *steps_out (host) receives the number of steps run. Blocks the
+ * calling thread on `stream` once per step. */
+int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d_logits,
+                      int32_t* d_block_out, int32_t commit, int32_t* steps_out, void* stream);
+
+/* Device addresses of context buffers, for inspection by tests and tools. */
+enum {
+  DG_BUF_X = 0,             /* float [canvas x d_model] residual stream */
+  DG_BUF_H = 1,             /* dtype [canvas x d_model] normalised activations */
+  DG_BUF_ROUTER_LOGITS = 2, /* float [canvas x n_experts] (last layer run) */
+  DG_BUF_SEL = 3,           /* int32 [canvas x top_k] selected experts */
+  DG_BUF_GATE = 4,          /* float [canvas x top_k] gates */
+  DG_BUF_SC = 5,            /* float [canvas x d_model] self-conditioning vector */
+  DG_BUF_CANVAS = 6,        /* int32 [canvas] loop canvas */
+  DG_BUF_PRED = 7,          /* int32 [canvas] loop argmax */
+  DG_BUF_STOP = 8,          /* dg_stop_state of the loop */
+  DG_BUF_ENTROPY = 9,       /* float [canvas] */
+  DG_BUF_ROW_STATS = 10,    /* float [canvas x 2] */
+  DG_BUF_ACCEPT = 11,       /* uint8 [canvas] */
+  DG_BUF_Q = 12,            /* dtype [canvas x n_q_heads*head_dim] queries (last layer run) */
+  DG_BUF_ATTN = 13,         /* dtype [canvas x n_q_heads*head_dim] attention output */
+  DG_BUF_SHARED_ACT = 14,   /* dtype [canvas x d_shared] shared-expert hidden activation */
+  DG_BUF_SLOT_OUT = 15,     /* float [canvas*top_k x d_model] gated routed-expert outputs, expert-major slots */
+  DG_BUF_SLOT_OF = 16       /* int32 [canvas x top_k] slot of each (row, choice) */
+};
+int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
 
 #ifdef __cplusplus
 }

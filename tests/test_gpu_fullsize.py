@@ -1,0 +1,138 @@
+"""Parity at the benchmark's full sizes, on sampled outputs the oracle computes one by one.
+
+* One MoE denoiser layer (d_model 2816, 16q/8kv x 128 heads, 128 experts top-8 of
+  width 704 gated + shared 2816) over a 256-row canvas attending to 4096 cached
+  positions plus the canvas: canvas K for every row, router logits for every row
+  (exact top-8 teacher-forced on the GPU's logits), and the layer output on
+  sampled rows.
+* The 30-layer, 262144-vocab step: the sampler teacher-forced on the GPU's
+  logits (exact), and LM-head logits on sampled (row, vocab) pairs from the
+  GPU's final normalised activations.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import model as OM
+from oracle import sampler as OS
+
+from gpu_util import announce, need_gpu, to_f64, torch
+from test_gpu_model import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def libs():
+    need_gpu()
+    from canvas_denoising_amd import _lib, configs, runtime
+    return _lib, configs, runtime
+
+
+def test_moe_layer_full_size(libs):
+    L, configs, runtime = libs
+    announce("full-size MoE layer (d 2816, 128 experts, 4096 cached)")
+    w = configs.moe_layer_bf16()
+    d = w.desc
+    model = runtime.Model(d, w.capacity, seed=0, sigma=0.02)
+    past, C, D, hd = w.prompt, d.canvas, d.d_model, d.head_dim
+    kv_n = d.n_kv_heads * past * hd
+    kb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
+    vb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT + 1, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
+    K, V = model.kv_view()
+    K[0, :, :past] = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
+    V[0, :, :past] = torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16)
+    L.dg_kv_set_length(model.ctx, past)
+    x0 = synthetic.normal_f32(2, synthetic.TID_X_INPUT, C * D, 1.0).reshape(C, D)
+    x = torch.from_numpy(x0.copy()).cuda()
+    model.forward_layer(0, x, C, False)
+    torch.cuda.synchronize()
+
+    W = synthetic.SyntheticWeights(configs.shape_dict(d), seed=0, dtype="bf16", sigma=0.02, cache_experts=False)
+    lw = W["layers"][0]
+    shape = OM.ModelShape(n_layers=1, d_model=D, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads, head_dim=hd,
+                          n_experts=d.n_experts, top_k=d.top_k, d_expert=d.d_expert, d_shared=d.d_shared,
+                          gated=True, vocab=d.vocab, d_selfcond=d.d_selfcond)
+    xf = x0.astype(np.float64)
+    h = OM.rms_norm(xf, shape.rms_eps)
+    k = (h @ lw["wk"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
+    v = (h @ lw["wv"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
+    assert_close(to_f64(K[0, :, past:past + C]), k, 2e-2, "canvas K (all rows)")
+    kc = np.concatenate([synthetic.bf16_bits_to_f32(kb).astype(np.float64), k], axis=1)
+    vc = np.concatenate([synthetic.bf16_bits_to_f32(vb).astype(np.float64), v], axis=1)
+    # teacher-forced routing on every row
+    r_gpu = to_f64(model.buffer(L.DG_BUF_ROUTER_LOGITS, torch.float32, (C, d.n_experts)))
+    sel_gpu = model.buffer(L.DG_BUF_SEL, torch.int32, (C, d.top_k)).cpu().numpy()
+    assert np.array_equal(OM.topk_from_logits(r_gpu, d.top_k), sel_gpu)
+    counts = np.bincount(sel_gpu.ravel(), minlength=d.n_experts)
+    print(f"tokens per expert: min {counts.min()} max {counts.max()}")
+    # sampled rows through the whole layer
+    rows = np.array([0, 97, 255])
+    hq = h[rows]
+    q = (hq @ lw["wq"].T).reshape(len(rows), d.n_q_heads, hd).transpose(1, 0, 2)
+    o = np.empty((d.n_q_heads, len(rows), hd))
+    G = d.n_q_heads // d.n_kv_heads
+    for j in range(d.n_q_heads):
+        s = q[j] @ kc[j // G].T / np.sqrt(hd)
+        o[j] = OM.softmax(s) @ vc[j // G]
+    o = o.transpose(1, 0, 2).reshape(len(rows), d.n_q_heads * hd)
+    x1 = xf[rows] + o @ lw["wo"].T
+    h2 = OM.rms_norm(x1, shape.rms_eps)
+    r = h2 @ lw["wr"].T
+    assert_close(r_gpu[rows], r, 2e-2, "router logits (sampled rows)")
+    sel = OM.topk_from_logits(r, d.top_k)
+    gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
+    y = OM.ffn(h2, lw, True, prefix="sh_")
+    for i in range(len(rows)):
+        for j in range(d.top_k):
+            y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
+    ref = x1 + y
+    keep = OM.router_margin(r, d.top_k) > 1e-2
+    print(f"sampled rows kept (no router near-tie): {int(keep.sum())} of {len(rows)}")
+    assert_close(to_f64(x)[rows][keep], ref[keep], 2e-2, "layer output (sampled rows)")
+    model.close()
+
+
+@pytest.mark.slow
+def test_full_step_sampled(libs):
+    L, configs, runtime = libs
+    w = configs.full_loop_bf16()
+    d = w.desc
+    C, V, D = d.canvas, d.vocab, d.d_model
+    announce("full-size 30-layer step: prefill 8192, denoise, sample, self-conditioned step, commit")
+    model = runtime.Model(d, w.prompt + 2 * C, seed=0, sigma=0.02)
+    prompt = torch.from_numpy(synthetic.uniform_ids(4, synthetic.TID_PROMPT, w.prompt, V)).cuda()
+    model.prefill(prompt)
+    sched = L.make_sched(max_steps=48, seed=0)
+    st = runtime.SamplerState(C, V)
+    st.init(sched, 0)
+    logits = model.denoise_step(st.canvas, 0)
+    torch.cuda.synchronize()
+    # LM head on sampled (row, vocab) pairs from the GPU's final normalised activations
+    h = to_f64(model.buffer(L.DG_BUF_H, torch.bfloat16, (C, D)))
+    rng = np.random.default_rng(0)
+    cols = np.sort(rng.choice(V, size=2048, replace=False))
+    idx = (cols[:, None].astype(np.uint64) * np.uint64(D) + np.arange(D, dtype=np.uint64)[None, :]).ravel()
+    E_cols = synthetic.bf16_bits_to_f32(synthetic.normal_bf16_bits(0, synthetic.TID_EMBED, idx, 0.02))
+    E_cols = E_cols.astype(np.float64).reshape(len(cols), D)
+    assert_close(to_f64(logits[:, torch.from_numpy(cols).cuda()]), h @ E_cols.T, 2e-2, "LM head (sampled vocab)")
+    # sampler teacher-forced on the GPU's logits: exact discrete outputs
+    st.sample(logits, sched, 0, 0)
+    torch.cuda.synchronize()
+    lg = to_f64(logits)
+    res = OS.sample_step(lg, 0, 0, OS.Schedule(seed=0), None, 0)
+    assert np.array_equal(st.pred.cpu().numpy(), res.pred)
+    flag = np.abs(res.entropy - 0.1) <= 1e-4
+    assert np.array_equal(st.canvas.cpu().numpy()[~flag], res.next_canvas[~flag])
+    assert np.abs(to_f64(st.entropy) - res.entropy).max() < 1e-3
+    print(f"mean entropy {res.mean_entropy:.3f} (ln V = {np.log(V):.3f}), accepted {int(res.accept.sum())}")
+    # a self-conditioned step and a commit run at full size
+    T0 = L.dg_temperature(sched, 0)
+    logits1 = model.denoise_step(st.canvas, 1, logits, st.row_stats, T0, logits=torch.empty_like(logits))
+    model.commit(st.pred)
+    torch.cuda.synchronize()
+    assert model.length == w.prompt + C
+    assert torch.isfinite(logits1.float()).all()
+    sc = to_f64(model.buffer(L.DG_BUF_SC, torch.float32, (C, D)))
+    assert np.isfinite(sc).all() and np.abs(sc).max() > 0
+    model.close()

@@ -1,0 +1,273 @@
+"""GPU parity of the denoiser / encoder passes against the float64 oracle.
+
+Small models (several GEMM tiles, ragged prompt chunks, both dtypes, gated and
+plain FFNs) are compared row by row and element by element: logits,
+activations and KV entries within a relative error of tol per row
+(||gpu - ref|| / ||ref||) and |gpu - ref| <= 4 tol (|ref| + rms(ref row)) per
+element, tol = 2e-2 for bf16 and 2e-4 for fp32. Router decisions are checked bit-exact teacher-forced
+(the oracle's top-k on the GPU's router logits), and against the oracle's own
+router except tokens whose 8th/9th (k-th/k+1-th) logits are within 1e-2.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import model as OM
+from oracle import sampler as OS
+
+from gpu_util import announce, need_gpu, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def libs():
+    need_gpu()
+    from canvas_denoising_amd import _lib, configs, runtime
+    return _lib, configs, runtime
+
+
+def tol_for(dtype):
+    return 2e-2 if dtype == "bf16" else 2e-4
+
+
+def assert_close(gpu, ref, tol, what="", elem_factor=4.0):
+    """'rel tol' read per row (last axis): ||gpu - ref|| / ||ref|| <= tol; plus an
+    elementwise guard |gpu - ref| <= elem_factor * tol * (|ref| + rms(ref row)) that
+    catches localised errors the norm would average away."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    diff = gpu - ref
+    row_rel = np.linalg.norm(diff, axis=-1) / (np.linalg.norm(ref, axis=-1) + 1e-30)
+    worst_row = float(row_rel.max())
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    err = np.abs(diff) / (np.abs(ref) + rms + 1e-30)
+    worst = float(err.max())
+    assert worst_row <= tol, (f"{what}: row relative error {worst_row:.3g} > {tol} at row "
+                              f"{np.unravel_index(row_rel.argmax(), row_rel.shape)}")
+    assert worst <= elem_factor * tol, (f"{what}: elementwise scaled error {worst:.3g} > {elem_factor * tol} at "
+                                        f"{np.unravel_index(err.argmax(), err.shape)}")
+    return worst_row
+
+
+def build(libs, dtype="bf16", gated=1, n_layers=2, d=256, Hq=4, Hkv=2, hd=64, E=8, k=2, F=128, Fs=256, V=512,
+          dsc=128, canvas=64, capacity=512, seed=3, sigma=0.05):
+    L, configs, runtime = libs
+    dt = L.DG_BF16 if dtype == "bf16" else L.DG_F32
+    desc = configs.desc(n_layers, d, Hq, Hkv, hd, E, k, F, Fs, gated, V, dsc, dt, canvas=canvas)
+    model = runtime.Model(desc, capacity, seed=seed, sigma=sigma)
+    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=seed, dtype=dtype, sigma=sigma)
+    shape = OM.ModelShape(n_layers=n_layers, d_model=d, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, n_experts=E,
+                          top_k=k, d_expert=F, d_shared=Fs, gated=bool(gated), vocab=V, d_selfcond=dsc,
+                          canvas=canvas)
+    return model, W, shape
+
+
+def ids_tensor(seed, n, V):
+    return torch.from_numpy(synthetic.uniform_ids(seed, synthetic.TID_PROMPT, n, V)).cuda()
+
+
+def gpu_kv(model, n_layers, upto):
+    K, V = model.kv_view()
+    return to_f64(K[:, :, :upto]), to_f64(V[:, :, :upto])
+
+
+CASES = [("bf16", 1), ("bf16", 0), ("f32", 0), ("f32", 1)]
+
+
+def router_flags(infos, top_k, thr=1e-2):
+    """Rows whose k-th / (k+1)-th router logits are within thr in any layer (near-ties)."""
+    f = None
+    for info in infos:
+        m = OM.router_margin(info["router_logits"], top_k) <= thr
+        f = m if f is None else (f | m)
+    return f
+
+
+def keep_axis(a, keep, axis):
+    return np.compress(keep, a, axis=axis)
+
+
+@pytest.mark.parametrize("dtype,gated", CASES)
+def test_prefill_denoise_commit_match_oracle(libs, dtype, gated):
+    """Prefill (ragged chunks), denoise step 0, self-conditioned step 1, commit.
+
+    Tokens flagged as router near-ties in any layer (k-th vs (k+1)-th logit within
+    1e-2 in the oracle) are excluded from the continuous comparisons: rounding may
+    legitimately give them a different expert, which changes their activations
+    outright. Their count is reported.
+    """
+    L, configs, runtime = libs
+    announce(f"model {dtype} gated={gated}")
+    model, W, shape = build(libs, dtype=dtype, gated=gated)
+    tol = tol_for(dtype)
+    n_prompt = 100  # two chunks of the 64-row canvas, the second ragged
+    prompt = ids_tensor(1, n_prompt, shape.vocab)
+    model.prefill(prompt)
+    torch.cuda.synchronize()
+    assert model.length == n_prompt
+    cache = OM.KVCache.empty(shape, 512)
+    pinfo = []
+    OM.encode(W, cache, prompt.cpu().numpy(), shape, infos=pinfo)
+    pflag = router_flags(pinfo, shape.top_k)
+    print(f"prompt router near-ties: {int(pflag.sum())} of {n_prompt}")
+    keep = ~pflag
+    gk, gv = gpu_kv(model, shape.n_layers, n_prompt)
+    for l in range(shape.n_layers):
+        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n_prompt], keep, 1), tol, f"prefill K {l}")
+        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n_prompt], keep, 1), tol, f"prefill V {l}")
+
+    # denoising step 0 (no self-conditioning)
+    canvas = ids_tensor(2, shape.canvas, shape.vocab)
+    logits = model.denoise_step(canvas, 0)
+    torch.cuda.synchronize()
+    ref_cache = cache.copy()
+    ref0, x_ref, infos = OM.denoise_step(W, ref_cache, canvas.cpu().numpy(), None, shape, return_info=True)
+    cflag = router_flags(infos, shape.top_k)
+    print(f"canvas router near-ties: {int(cflag.sum())} of {shape.canvas}")
+    assert_close(to_f64(logits)[~cflag], ref0[~cflag], tol, "step-0 logits")
+    assert model.length == n_prompt  # canvas K/V are scratch
+    gk, gv = gpu_kv(model, shape.n_layers, n_prompt + shape.canvas)
+    assert_close(keep_axis(gk[-1][:, n_prompt:], ~cflag, 1),
+                 keep_axis(ref_cache.k[-1][:, n_prompt:n_prompt + shape.canvas], ~cflag, 1), tol, "canvas K")
+    # router of the last layer, teacher-forced: the oracle's top-k of the GPU's router logits
+    r_gpu = to_f64(model.buffer(L.DG_BUF_ROUTER_LOGITS, torch.float32, (shape.canvas, shape.n_experts)))
+    sel_gpu = model.buffer(L.DG_BUF_SEL, torch.int32, (shape.canvas, shape.top_k)).cpu().numpy()
+    assert np.array_equal(OM.topk_from_logits(r_gpu, shape.top_k), sel_gpu)
+    gate_gpu = to_f64(model.buffer(L.DG_BUF_GATE, torch.float32, (shape.canvas, shape.top_k)))
+    p = OM.softmax(r_gpu)
+    np.testing.assert_allclose(gate_gpu, np.take_along_axis(p, sel_gpu, axis=1), rtol=2e-5, atol=1e-7)
+    # against the oracle's own router, near-ties flagged
+    same = np.array([set(a) == set(b) for a, b in zip(sel_gpu, infos[-1]["sel"])])
+    assert same[~cflag].all(), f"router mismatch on {np.nonzero(~same & ~cflag)[0]}"
+
+    # step 1 with self-conditioning from step 0, teacher-forced on the GPU's logits and row stats
+    sched = L.make_sched(max_steps=8, seed=4)
+    st = runtime.SamplerState(shape.canvas, shape.vocab)
+    st.init(sched, 0)
+    st.sample(logits, sched, 0, 0)
+    prev_logits = logits.clone()
+    T0 = L.dg_temperature(sched, 0)
+    canvas1 = st.canvas.clone()
+    logits1 = model.denoise_step(canvas1, 1, prev_logits, st.row_stats, T0, logits=torch.empty_like(logits))
+    torch.cuda.synchronize()
+    probs = OS.tempered_probs(to_f64(prev_logits), T0)
+    sc_ref = OM.self_condition(W, probs)
+    sc_gpu = to_f64(model.buffer(L.DG_BUF_SC, torch.float32, (shape.canvas, shape.d_model)))
+    assert_close(sc_gpu, sc_ref, tol * 2 if dtype == "bf16" else tol, "self-conditioning vector")
+    ref1, _, infos1 = OM.denoise_step(W, cache.copy(), canvas1.cpu().numpy(), sc_ref, shape, return_info=True)
+    f1 = router_flags(infos1, shape.top_k)
+    assert_close(to_f64(logits1)[~f1], ref1[~f1], tol, "step-1 logits")
+    # in-place self-conditioning (prev logits aliasing the output) gives the same result
+    alias = prev_logits.clone()
+    model.denoise_step(canvas1, 1, alias, st.row_stats, T0, logits=alias)
+    torch.cuda.synchronize()
+    assert torch.equal(alias, logits1)
+
+    # commit a block: causal encoder pass, length grows by the canvas
+    block = ids_tensor(5, shape.canvas, shape.vocab)
+    model.commit(block)
+    torch.cuda.synchronize()
+    assert model.length == n_prompt + shape.canvas
+    binfo = []
+    OM.encode(W, cache, block.cpu().numpy(), shape, infos=binfo)
+    keep = ~np.concatenate([pflag, router_flags(binfo, shape.top_k)])
+    gk, gv = gpu_kv(model, shape.n_layers, model.length)
+    for l in range(shape.n_layers):
+        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :model.length], keep, 1), tol, f"commit K {l}")
+        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :model.length], keep, 1), tol, f"commit V {l}")
+    model.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_layer_heavy_expert(libs, dtype, causal):
+    """Two experts, top-1: each expert gets far more than 64 tokens (several passes)."""
+    L, configs, runtime = libs
+    announce(f"forward_layer heavy expert {dtype} causal={causal}")
+    model, W, shape = build(libs, dtype=dtype, gated=1, n_layers=1, E=2, k=1, canvas=256, capacity=512, d=128,
+                            Hq=2, Hkv=1, hd=64, F=192, Fs=128, V=256, dsc=64)
+    past = 37
+    Kc, Vc = model.kv_view()
+    kv_ref = OM.KVCache.empty(shape, 512)
+    rng = np.random.default_rng(7)
+    kp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
+    vp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
+    Kc[0, :, :past] = torch.from_numpy(kp).to(model.dtype)
+    Vc[0, :, :past] = torch.from_numpy(vp).to(model.dtype)
+    kv_ref.k[0][:, :past] = to_f64(Kc[0, :, :past])
+    kv_ref.v[0][:, :past] = to_f64(Vc[0, :, :past])
+    L.dg_kv_set_length(model.ctx, past)
+    x = torch.from_numpy(rng.normal(size=(256, shape.d_model)).astype(np.float32)).cuda()
+    x_ref = to_f64(x)
+    model.forward_layer(0, x, 256, causal)
+    torch.cuda.synchronize()
+    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, causal)
+    keep = OM.router_margin(info["router_logits"], shape.top_k) > 1e-2
+    assert_close(to_f64(x)[keep], y_ref[keep], tol_for(dtype), "layer output")
+    counts = np.bincount(info["sel"][:, 0], minlength=2)
+    assert counts.max() > 64
+    gk, gv = gpu_kv(model, 1, past + 256)
+    assert_close(gk[0][:, past:], kv_ref.k[0][:, past:past + 256], tol_for(dtype), "layer K")
+    model.close()
+
+
+def test_generate_block_matches_sampler_on_final_logits(libs):
+    L, configs, runtime = libs
+    announce("generate_block")
+    model, W, shape = build(libs, dtype="bf16", gated=1, n_layers=1, canvas=64, capacity=512)
+    prompt = ids_tensor(1, 80, shape.vocab)
+    model.prefill(prompt)
+    sched = L.make_sched(max_steps=4, seed=11)
+    out = torch.empty(shape.canvas, dtype=torch.int32, device="cuda")
+    steps = model.generate_block(sched, 0, out, commit=True)
+    torch.cuda.synchronize()
+    assert steps == 4  # a random-init model never reaches the stop (entropy ~ ln V)
+    assert model.length == 80 + shape.canvas
+    # the committed block is the sampler's argmax of the final step's logits
+    res = OS.sample_step(to_f64(model.logits), 3, 0, OS.Schedule(max_steps=4, seed=11), None, 0)
+    assert np.array_equal(out.cpu().numpy(), res.pred)
+    stop = runtime.stop_dict(model.buffer(L.DG_BUF_STOP, torch.int32, (4,)))
+    assert stop["steps_run"] == 4 and stop["stopped"] == 0
+    assert abs(stop["mean_entropy"] - res.mean_entropy) < 1e-3
+    # the committed KV equals an encoder pass over the block (teacher-forced ids)
+    cache = OM.KVCache.empty(shape, 512)
+    OM.encode(W, cache, np.concatenate([prompt.cpu().numpy(), out.cpu().numpy()]), shape)
+    gk, gv = gpu_kv(model, 1, model.length)
+    assert_close(gk[0], cache.k[0][:, :model.length], 2e-2, "generated-block K")
+    model.close()
+
+
+def test_denoise_step_is_deterministic(libs):
+    L, configs, runtime = libs
+    announce("denoise determinism")
+    model, W, shape = build(libs, dtype="bf16", gated=1, n_layers=2, canvas=64)
+    model.prefill(ids_tensor(1, 70, shape.vocab))
+    canvas = ids_tensor(2, shape.canvas, shape.vocab)
+    a = model.denoise_step(canvas, 0, logits=torch.empty(shape.canvas, shape.vocab, dtype=torch.bfloat16,
+                                                         device="cuda"))
+    b = model.denoise_step(canvas, 0, logits=torch.empty_like(a))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    model.close()
+
+
+def test_capacity_errors_leave_state(libs):
+    L, configs, runtime = libs
+    announce("capacity errors")
+    model, W, shape = build(libs, dtype="bf16", gated=1, n_layers=1, canvas=64, capacity=128)
+    model.prefill(ids_tensor(1, 64, shape.vocab))
+    with pytest.raises(L.DGError) as ei:
+        model.prefill(ids_tensor(1, 65, shape.vocab))
+    assert ei.value.code == L.DG_ERR_CAPACITY and model.length == 64
+    model.commit(ids_tensor(2, 64, shape.vocab))
+    assert model.length == 128
+    with pytest.raises(L.DGError) as ei:
+        model.commit(ids_tensor(2, 64, shape.vocab))
+    assert ei.value.code == L.DG_ERR_CAPACITY and model.length == 128
+    with pytest.raises(L.DGError):
+        model.denoise_step(ids_tensor(3, 64, shape.vocab), 0)
+    model.close()

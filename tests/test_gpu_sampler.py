@@ -82,7 +82,7 @@ def test_sampler_matches_oracle(L, rows, V, dtype):
     rs = to_f64(st.row_stats)
     assert np.array_equal(rs[:, 0], lg.max(axis=1))
     z = np.log(np.exp((lg - lg.max(axis=1, keepdims=True)) / T).sum(axis=1))
-    assert np.allclose(rs[:, 1], z, rtol=1e-5, atol=1e-6)
+    assert np.allclose(rs[:, 1], z, rtol=1e-5, atol=1e-5)
     s = st.stop_state()
     assert s["steps_run"] == step + 1
     assert s["stable_count"] == res.stable
