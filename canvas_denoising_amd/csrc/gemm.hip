@@ -242,6 +242,187 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
       }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 variant with a deep asynchronous pipeline. Loaded HBM latency is a few
+// microseconds while one 64-deep k-tile of MFMA work takes a fraction of one,
+// so a register double buffer leaves the kernel latency-bound. Here every
+// wave issues global_load_lds_dwordx4 (gfx950: 16 bytes per lane straight
+// into LDS, no registers) for k-tiles NS-1 ahead into a ring of NS LDS stages,
+// waits with a counted s_waitcnt for the oldest stage only, and crosses one
+// barrier per k-tile. A tile row is 128 bytes (8 chunks of 16); chunk q of row
+// r is stored at position q ^ (r % 8) so the 16 rows a fragment read touches
+// fall on different banks. Rows past M (or N) re-read the last valid row;
+// their results are not stored.
+__device__ inline void wait_vm(int n) {
+  // s_waitcnt with vmcnt = n (gfx9 encoding: low 4 bits + bits 14..15), exp/lgkm counters untouched
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // conservative: wait for everything
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
+
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, int k_per_split) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  constexpr int ROWB = 128;  // bytes per tile row: 64 bf16
+  constexpr int SA = BM * ROWB, SB = BN * ROWB, SS = SA + SB;
+  constexpr int ALPW = BM / 32, BLPW = BN / 32;  // load instructions per wave per stage (8 rows each)
+  constexpr int LPS = ALPW + BLPW;
+  static_assert(TN % 2 == 0 && ALPW >= 1 && BLPW >= 1, "tile");
+  __shared__ __align__(16) unsigned char smem[NS * SS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool paired = g.epi == EPI_GEGLU;
+  const int nm = (g.M + BM - 1) / BM;
+  const int nn = (g.N + BN - 1) / BN;
+  const int b = blockIdx.x;
+  const int nn8 = (nn / 8) * 8;
+  int mt, nt;
+  if (b < nm * nn8) {
+    const int xcd = b & 7, j = b >> 3;
+    nt = (j / nm) * 8 + xcd;
+    mt = j % nm;
+  } else {
+    const int r = b - nm * nn8;
+    nt = nn8 + r / nm;
+    mt = r % nm;
+  }
+  const int m0 = mt * BM;
+  const int z = blockIdx.y;
+  const int k_begin = z * k_per_split;
+  const int k_end = min(g.K, k_begin + k_per_split);
+  const int nk = (k_end - k_begin) / 64;
+
+  auto brow = [&](int t) -> int {
+    if (!paired) return min(nt * BN + t, g.N - 1);
+    const int half = t / (BN / 2), c = t % (BN / 2);
+    const int j0 = nt * (BN / 2) + half * (BN / 4);
+    return c < BN / 4 ? j0 + c : g.pair_f + j0 + (c - BN / 4);
+  };
+  const bf16_t* A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* B = static_cast<const bf16_t*>(g.B);
+  const bf16_t* asrc[ALPW];
+  const bf16_t* bsrc[BLPW];
+#pragma unroll
+  for (int i = 0; i < ALPW; ++i) {
+    const int r = (wave * ALPW + i) * 8 + (lane >> 3);
+    const int q = (lane & 7) ^ (r & 7);
+    asrc[i] = A + static_cast<int64_t>(min(m0 + r, g.M - 1)) * g.lda + q * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < BLPW; ++i) {
+    const int t = (wave * BLPW + i) * 8 + (lane >> 3);
+    const int q = (lane & 7) ^ (t & 7);
+    bsrc[i] = B + static_cast<int64_t>(brow(t)) * g.ldb + q * 8;
+  }
+  auto issue = [&](int kt, int slot) {
+    const int k0 = k_begin + kt * 64;
+    unsigned char* base = smem + slot * SS;
+#pragma unroll
+    for (int i = 0; i < ALPW; ++i)
+      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(asrc[i] + k0),
+                                       (lds_void_t*)(base + (wave * ALPW + i) * 8 * ROWB), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BLPW; ++i)
+      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(bsrc[i] + k0),
+                                       (lds_void_t*)(base + SA + (wave * BLPW + i) * 8 * ROWB),
+                                       16, 0, 0);
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int younger = min(NS - 2, nk - 1 - kt);  // stages issued after this one
+    wait_vm(younger * LPS);
+    // Stage kt is complete for every wave, and every wave is done reading stage kt-1
+    // (its fragments were consumed by MFMAs already issued). A bare s_barrier: the
+    // fence of __syncthreads() would wait for all outstanding loads, draining the ring.
+    __builtin_amdgcn_s_barrier();
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const unsigned char* sa = smem + (kt % NS) * SS;
+    const unsigned char* sb = sa + SA;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[TM], bfr[TN];
+      const int q = ks * 4 + g4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((q ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WN + j * 16 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * ROWB + ((q ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Frag<bf16_t>::mma(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  // ---- epilogue (same mapping as gemm_kernel)
+  const int rbase = m0 + wm * WM + (lane >> 4) * 4;
+  if (splits > 1) {
+    float* part = g.part + static_cast<int64_t>(z) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int col = nt * BN + wn * WN + j * 16 + fr;
+          if (row < g.M && col < g.N) part[static_cast<int64_t>(row) * g.N + col] = acc[i][j][r];
+        }
+    return;
+  }
+  if (paired) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int jj = nt * (BN / 2) + wn * (BN / 4) + j * 16 + fr;
+          if (row < g.M) {
+            const float v = gelu_erf(acc[i][j][r]) * acc[i][j + TN / 2][r];
+            static_cast<bf16_t*>(g.out)[static_cast<int64_t>(row) * g.ldo + jj] = f32_to_bf16(v);
+          }
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rbase + i * 16 + r;
+        const int col = nt * BN + wn * WN + j * 16 + fr;
+        if (row < g.M && col < g.N) epilogue<bf16_t>(g, row, col, acc[i][j][r]);
+      }
+}
+
 template <typename T>
 __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
   const int64_t n = static_cast<int64_t>(g.M) * g.N;
@@ -301,9 +482,18 @@ static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name
   int rc;
   {
     ProfScope ps(name, s);
-    if (tc.bm == 128) rc = launch_tile<T, 128, 128>(g, splits, kps, s);
-    else rc = launch_tile<T, 64, 64>(g, splits, kps, s);
+    if constexpr (sizeof(T) == 2) {
+      const int nm = (g.M + tc.bm - 1) / tc.bm, nn = (g.N + tc.bn - 1) / tc.bn;
+      dim3 grid(static_cast<unsigned>(nm * nn), static_cast<unsigned>(splits));
+      if (tc.bm == 128) gemm_dma_kernel<128, 128, 4><<<grid, 256, 0, s>>>(g, splits, kps);
+      else gemm_dma_kernel<64, 64, 4><<<grid, 256, 0, s>>>(g, splits, kps);
+      rc = DG_OK;
+    } else {
+      if (tc.bm == 128) rc = launch_tile<T, 128, 128>(g, splits, kps, s);
+      else rc = launch_tile<T, 64, 64>(g, splits, kps, s);
+    }
   }
+  DG_LAUNCH_CHECK("gemm_dma_kernel");
   if (rc != DG_OK) return rc;
   if (splits > 1) {
     ProfScope ps("splitk_reduce", s);

@@ -3,21 +3,24 @@
 // active plus 1 shared; [P3] "Encoder-denoiser design": the denoiser is the
 // Gemma 4 26B-A4B MoE backbone).
 //
-// Routing (one workgroup): per row, softmax over the E router logits and the
-// top-k chosen on the logits themselves (largest first, lowest index on
-// ties); the gate is the selected softmax probability. Every (token, expert)
-// pair sets a bit in a per-expert token mask in LDS; popcounts give expert
-// sizes, an exclusive scan gives offsets, and a token's rank inside its
-// expert is the popcount of the mask bits below it. The slot order is
-// therefore expert-major and token-ascending whatever the thread timing.
+// Routing, two kernels. (1) One wave per row: softmax over the E router logits
+// and the top-k chosen on the logits themselves (largest first, lowest index
+// on ties); the gate is the selected softmax probability. (2) One workgroup:
+// every (token, expert) pair sets a bit in a per-expert token mask in LDS;
+// popcounts give expert sizes, an exclusive scan gives offsets, and a token's
+// rank inside its expert is the popcount of the mask bits below it. The slot
+// order is therefore expert-major and token-ascending whatever the timing.
 //
 // Expert GEMMs: with a 256-token canvas an expert sees about 16 tokens, so
-// the work is a stream of expert weights (arithmetic intensity ~16 flop/B).
-// Each wave owns 16 output features of one expert and streams their weight
-// rows straight from HBM into MFMA B fragments (16-byte loads, 4 k-steps
-// of 32 in flight), while the expert's gathered token rows (A fragments) come
-// from L2. Up to 64 tokens are kept in accumulators per pass; an expert with
-// more tokens takes further passes. No LDS, no barriers: waves are independent.
+// the work is a stream of expert weights (arithmetic intensity ~16 flop/B):
+// HBM-bound, and with a loaded HBM latency of a few microseconds it is
+// latency-bound unless many bytes are in flight. Each wave owns 16 output
+// features of one expert and streams their weight rows straight from HBM
+// into MFMA B fragments through a ring of register stages (64 k per stage,
+// two stages ahead of the one being multiplied), together with the expert's
+// gathered token rows (A fragments, from L2). Up to 32 tokens are held in
+// accumulators per pass; an expert with more tokens takes further passes.
+// No LDS and no barriers: waves are independent.
 #include <math.h>
 
 #include <algorithm>
@@ -28,77 +31,78 @@
 
 namespace dg {
 
-constexpr int kRouteThreads = 1024;
-constexpr int kMaxTokens = 256;     // rows per routing call
+constexpr int kMaxTokens = 256;  // rows per routing call
 constexpr int kMaskWords = kMaxTokens / 32;
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float* __restrict__ logits, int M, int E, int k, int renorm,
-    int32_t* __restrict__ sel, float* __restrict__ gate, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ slot_of, float* __restrict__ slot_gate) {
-  __shared__ uint32_t mask[256 * kMaskWords];  // E <= 256
-  __shared__ int32_t offs[257];
-  __shared__ int32_t lsel[kMaxTokens * 16];     // k <= 16
-  __shared__ float lgate[kMaxTokens * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < E * kMaskWords; i += kRouteThreads) mask[i] = 0u;
-  __syncthreads();
-
-  constexpr int kPer = 4;  // values per lane (E <= 256)
-  for (int row = wave; row < M; row += kRouteThreads / 64) {
-    float v[kPer];
-    float mx = -INFINITY;
+// grid ceil(M / 4), 256 threads: wave w of the workgroup routes row 4 * blockIdx.x + w
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int M, int E, int k,
+                                                   int renorm, int32_t* __restrict__ sel,
+                                                   float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  constexpr int kPer = 4;  // E <= 256
+  float v[kPer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[static_cast<int64_t>(row) * E + e] : -INFINITY;
+    mx = fmaxf(mx, v[i]);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sum += (lane + 64 * i < E) ? expf(v[i] - mx) : 0.f;
+  sum = wave_sum(sum);
+  float my_gate = 0.f;
+  int my_e = 0;
+  float gsum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    // wave argmax: largest value, lowest expert index on ties
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = lane + 64 * i;
-      v[i] = e < E ? logits[static_cast<int64_t>(row) * E + e] : -INFINITY;
-      mx = fmaxf(mx, v[i]);
+      if (e < E && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) sum += (lane + 64 * i < E) ? expf(v[i] - mx) : 0.f;
-    sum = wave_sum(sum);
-    float gsum = 0.f;
-    float gsel[16];
-    int esel[16];
-    for (int j = 0; j < k; ++j) {
-      // wave argmax: largest value, lowest expert index on ties
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = shfl_xor(bv, m);
-        const int oe = shfl_xor(be, m);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i == be) v[i] = -INFINITY;
-      const float g = expf(bv - mx) / sum;
-      gsel[j] = g;
-      esel[j] = be;
-      gsum += g;
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = shfl_xor(bv, m);
+      const int oe = shfl_xor(be, m);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
     }
-    if (lane == 0) {
-      for (int j = 0; j < k; ++j) {
-        const float g = renorm ? gsel[j] / gsum : gsel[j];
-        sel[row * k + j] = esel[j];
-        gate[row * k + j] = g;
-        lsel[row * k + j] = esel[j];
-        lgate[row * k + j] = g;
-        atomicOr(&mask[esel[j] * kMaskWords + (row >> 5)], 1u << (row & 31));
-      }
-    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane + 64 * i == be) v[i] = -INFINITY;
+    const float g = expf(bv - mx) / sum;
+    gsum += g;
+    if (lane == j) { my_gate = g; my_e = be; }  // lane j keeps choice j
+  }
+  if (lane < k) {
+    sel[row * k + lane] = my_e;
+    gate[row * k + lane] = renorm ? my_gate / gsum : my_gate;
+  }
+}
+
+// one workgroup: expert sizes, offsets and the expert-major, token-ascending slot order
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ sel,
+                                                       const float* __restrict__ gate, int M, int E, int k,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ slot_of,
+                                                       float* __restrict__ slot_gate) {
+  __shared__ uint32_t mask[256 * kMaskWords];  // E <= 256
+  __shared__ int32_t offs[257];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < E * kMaskWords; i += 1024) mask[i] = 0u;
+  __syncthreads();
+  for (int p = tid; p < M * k; p += 1024) {
+    const int row = p / k;
+    atomicOr(&mask[sel[p] * kMaskWords + (row >> 5)], 1u << (row & 31));
   }
   __syncthreads();
   if (wave == 0) {
-    // exclusive scan of expert sizes (E <= 256: 4 per lane)
     int cnt[4];
     int tot = 0;
 #pragma unroll
@@ -126,32 +130,117 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     if (lane == 63) offs[E] = incl;
   }
   __syncthreads();
-  for (int i = tid; i <= E; i += kRouteThreads) offsets[i] = offs[i];
-  for (int p = tid; p < M * k; p += kRouteThreads) {
+  for (int i = tid; i <= E; i += 1024) offsets[i] = offs[i];
+  for (int p = tid; p < M * k; p += 1024) {
     const int row = p / k;
-    const int e = lsel[p];
+    const int e = sel[p];
     int rank = 0;
     for (int w = 0; w < (row >> 5); ++w) rank += __popc(mask[e * kMaskWords + w]);
     rank += __popc(mask[e * kMaskWords + (row >> 5)] & ((1u << (row & 31)) - 1u));
     const int slot = offs[e] + rank;
     perm[slot] = row;
     slot_of[p] = slot;
-    slot_gate[slot] = lgate[p];
+    slot_gate[slot] = gate[p];
   }
 }
 
 // ------------------------------------------------------------------ experts
 constexpr int kExpWaves = 4;
-constexpr int kMT = 4;       // 16-token tiles held per pass (64 tokens)
-constexpr int kKC = 4;       // k-steps of 32 per loaded chunk
+constexpr int kMTP = 2;   // 16-token tiles held per pass (32 tokens)
+constexpr int kNS = 3;    // register stages (2 in flight while one is multiplied)
+constexpr int kKS = 64;   // k per stage: two MFMA k-steps
+
+// One pass of a wave over NT 16-token tiles of its expert: A (token rows) and B
+// (weight rows) fragments stream through kNS register stages. Loads are never
+// predicated (rows past the expert's tokens reuse its last token and their
+// results are not stored; prefetches past the last stage re-read it), so the
+// compiler can keep exactly kNS - 1 stages of loads outstanding.
+template <typename T, int NB, int NT>
+struct StreamPass {
+  using Fr = Frag<T>;
+  using FT = typename Fr::type;
+  struct Stage {
+    FT b[NB][2];
+    FT a[NT][2];
+  };
+  f32x4_t acc[NB][NT];
+
+  __device__ inline void run(const T* const* brow, const T* const* arow, int nst) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0, 0, 0, 0};
+    auto load = [&](Stage& S, int s) {
+      const int k0 = min(s, nst - 1) * kKS;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) S.b[m][kk] = Fr::load(brow[m] + k0 + kk * 32);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) S.a[t][kk] = Fr::load(arow[t] + k0 + kk * 32);
+      }
+    };
+    auto compute = [&](const Stage& S) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int m = 0; m < NB; ++m) acc[m][t] = Fr::mma(S.a[t][kk], S.b[m][kk], acc[m][t]);
+    };
+    Stage st[kNS];
+#pragma unroll
+    for (int u = 0; u < kNS - 1; ++u) load(st[u], u);
+    int s0 = 0;
+    for (; s0 + kNS <= nst; s0 += kNS) {
+#pragma unroll
+      for (int u = 0; u < kNS; ++u) {
+        load(st[(u + kNS - 1) % kNS], s0 + u + kNS - 1);
+        compute(st[u]);
+      }
+    }
+    // tail: the remaining (< kNS) stages are already loaded
+#pragma unroll
+    for (int u = 0; u < kNS - 1; ++u)
+      if (s0 + u < nst) compute(st[u]);
+  }
+};
 
 // act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j  (GATED) or GeLU(h W_up[e]^T)_j
 // for the slots of expert e. Grid: (ceil(F / 64), E); wave w owns features j0 .. j0+15.
+template <typename T, bool GATED, int NT>
+__device__ inline void gateup_pass(const T* h, int64_t ldh, const T* wg, const T* wu, int F, int D, int beg,
+                                   int cnt, int p0, const int32_t* perm, T* act, int j0, int lane) {
+  constexpr int NB = GATED ? 2 : 1;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const T* arow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int s = min(p0 + t * 16 + fr, cnt - 1);
+    arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
+  }
+  const T* brow[NB];
+  brow[0] = wu;
+  if constexpr (GATED) brow[1] = wg;
+  StreamPass<T, NB, NT> sp;
+  sp.run(brow, arow, D / kKS);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
+      if (s < cnt) {
+        const float u = sp.acc[0][t][i];
+        const float v = GATED ? gelu_erf(sp.acc[NB - 1][t][i]) * u : gelu_erf(u);
+        act[static_cast<int64_t>(beg + s) * F + j0 + fr] = from_f32<T>(v);
+      }
+    }
+}
+
 template <typename T, bool GATED>
 __global__ __launch_bounds__(256) void expert_gateup_kernel(
     const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int64_t expert_stride, int F, int D,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, T* __restrict__ act) {
-  using Fr = Frag<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.y;
   const int j0 = (blockIdx.x * kExpWaves + wave) * 16;
@@ -162,57 +251,32 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
   const T* wbase = w_gu + static_cast<int64_t>(e) * expert_stride;
   const T* wu = wbase + static_cast<int64_t>(GATED ? F + j0 + fr : j0 + fr) * D + fk;
   const T* wg = wbase + static_cast<int64_t>(j0 + fr) * D + fk;
-
-  for (int p0 = 0; p0 < cnt; p0 += kMT * 16) {
-    const int ntile = min(kMT, (cnt - p0 + 15) / 16);
-    const T* arow[kMT];
-    bool aok[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const int s = p0 + t * 16 + fr;
-      aok[t] = t < ntile && s < cnt;
-      arow[t] = h + static_cast<int64_t>(aok[t] ? perm[beg + s] : 0) * ldh + fk;
-    }
-    f32x4_t accg[kMT], accu[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) { accg[t] = f32x4_t{0, 0, 0, 0}; accu[t] = f32x4_t{0, 0, 0, 0}; }
-    for (int k0 = 0; k0 < D; k0 += 32 * kKC) {
-      typename Fr::type bu[kKC], bg[kKC];
-#pragma unroll
-      for (int c = 0; c < kKC; ++c) {
-        if (k0 + c * 32 < D) {
-          bu[c] = Fr::load(wu + k0 + c * 32);
-          if (GATED) bg[c] = Fr::load(wg + k0 + c * 32);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < kMT; ++t) {
-        if (t < ntile) {
-#pragma unroll
-          for (int c = 0; c < kKC; ++c) {
-            if (k0 + c * 32 < D) {
-              const typename Fr::type a = aok[t] ? Fr::load(arow[t] + k0 + c * 32) : Fr::zero();
-              accu[t] = Fr::mma(a, bu[c], accu[t]);
-              if (GATED) accg[t] = Fr::mma(a, bg[c], accg[t]);
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      if (t < ntile) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-          if (s < cnt) {
-            const float v = GATED ? gelu_erf(accg[t][i]) * accu[t][i] : gelu_erf(accu[t][i]);
-            act[static_cast<int64_t>(beg + s) * F + j0 + fr] = from_f32<T>(v);
-          }
-        }
-      }
-    }
+  for (int p0 = 0; p0 < cnt; p0 += kMTP * 16) {
+    if (cnt - p0 > 16) gateup_pass<T, GATED, 2>(h, ldh, wg, wu, F, D, beg, cnt, p0, perm, act, j0, lane);
+    else gateup_pass<T, GATED, 1>(h, ldh, wg, wu, F, D, beg, cnt, p0, perm, act, j0, lane);
   }
+}
+
+template <typename T, int NT>
+__device__ inline void down_pass(const T* act, const T* wrow, int F, int D, int beg, int cnt, int p0,
+                                 const float* slot_gate, float* out, int n0, int lane) {
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const T* arow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int s = min(p0 + t * 16 + fr, cnt - 1);
+    arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
+  }
+  const T* brow[1] = {wrow};
+  StreamPass<T, 1, NT> sp;
+  sp.run(brow, arow, F / kKS);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
+      if (s < cnt) out[static_cast<int64_t>(beg + s) * D + n0 + fr] = slot_gate[beg + s] * sp.acc[0][t][i];
+    }
 }
 
 // out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f]; grid (ceil(D / 64), E)
@@ -220,7 +284,6 @@ template <typename T>
 __global__ __launch_bounds__(256) void expert_down_kernel(
     const T* __restrict__ act, const T* __restrict__ w_down, int64_t expert_stride, int F, int D,
     const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate, float* __restrict__ out) {
-  using Fr = Frag<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.y;
   const int n0 = (blockIdx.x * kExpWaves + wave) * 16;
@@ -229,48 +292,9 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
   if (cnt == 0) return;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* wrow = w_down + static_cast<int64_t>(e) * expert_stride + static_cast<int64_t>(n0 + fr) * F + fk;
-
-  for (int p0 = 0; p0 < cnt; p0 += kMT * 16) {
-    const int ntile = min(kMT, (cnt - p0 + 15) / 16);
-    const T* arow[kMT];
-    bool aok[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const int s = p0 + t * 16 + fr;
-      aok[t] = t < ntile && s < cnt;
-      arow[t] = act + static_cast<int64_t>(beg + (aok[t] ? s : 0)) * F + fk;
-    }
-    f32x4_t acc[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) acc[t] = f32x4_t{0, 0, 0, 0};
-    for (int k0 = 0; k0 < F; k0 += 32 * kKC) {
-      typename Fr::type b[kKC];
-#pragma unroll
-      for (int c = 0; c < kKC; ++c)
-        if (k0 + c * 32 < F) b[c] = Fr::load(wrow + k0 + c * 32);
-#pragma unroll
-      for (int t = 0; t < kMT; ++t) {
-        if (t < ntile) {
-#pragma unroll
-          for (int c = 0; c < kKC; ++c) {
-            if (k0 + c * 32 < F) {
-              const typename Fr::type a = aok[t] ? Fr::load(arow[t] + k0 + c * 32) : Fr::zero();
-              acc[t] = Fr::mma(a, b[c], acc[t]);
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      if (t < ntile) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-          if (s < cnt) out[static_cast<int64_t>(beg + s) * D + n0 + fr] = slot_gate[beg + s] * acc[t][i];
-        }
-      }
-    }
+  for (int p0 = 0; p0 < cnt; p0 += kMTP * 16) {
+    if (cnt - p0 > 16) down_pass<T, 2>(act, wrow, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
+    else down_pass<T, 1>(act, wrow, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
   }
 }
 
@@ -278,16 +302,23 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
 int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel, float* gate, int32_t* offsets,
               int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s) {
   if (M > kMaxTokens || E > 256 || k > 16 || k > E) return fail(DG_ERR_UNSUPPORTED, "routing limits: M<=256, E<=256, k<=16");
-  ProfScope ps("moe_route", s);
-  route_kernel<<<1, kRouteThreads, 0, s>>>(logits, M, E, k, renorm, sel, gate, offsets, perm, slot_of, slot_gate);
-  DG_LAUNCH_CHECK("route_kernel");
+  {
+    ProfScope ps("moe_topk", s);
+    topk_kernel<<<(M + 3) / 4, 256, 0, s>>>(logits, M, E, k, renorm, sel, gate);
+  }
+  DG_LAUNCH_CHECK("topk_kernel");
+  {
+    ProfScope ps("moe_permute", s);
+    permute_kernel<<<1, 1024, 0, s>>>(sel, gate, M, E, k, offsets, perm, slot_of, slot_gate);
+  }
+  DG_LAUNCH_CHECK("permute_kernel");
   return DG_OK;
 }
 
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s) {
-  if (F % 16 != 0 || D % 32 != 0) return fail(DG_ERR_UNSUPPORTED, "expert widths must be multiples of 16 / 32");
+  if (F % kKS != 0 || D % kKS != 0) return fail(DG_ERR_UNSUPPORTED, "expert widths must be multiples of 64");
   const int64_t gu_stride = static_cast<int64_t>(gated ? 2 : 1) * F * D;
   const int64_t dn_stride = static_cast<int64_t>(D) * F;
   dim3 g1((F + 16 * kExpWaves - 1) / (16 * kExpWaves), E);
