@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sampler] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|copy] [--no-cpu-baseline]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
 workload's hot path over one batch of synthetic input that is already
@@ -13,6 +13,13 @@ resident in HBM:
   is N(0, 3)-like with a +12 peak planted in 70% of the rows. 48 distinct
   logits buffers (6.4 GB) rotate with the 48-step temperature schedule, so
   every step reads cold HBM rather than the 256 MB Infinity Cache.
+
+* ``full`` (default): the whole denoising loop of a 30-layer MoE model
+  over a 256-token canvas with an 8192-token prompt in the KV cache:
+  self-conditioning, 30 layers, LM head over 262144 tokens, the sampler,
+  the 16-byte stop read-back and a block commit whenever a canvas stops.
+* ``copy``: a plain 1 GiB device copy, the calibration run for the HBM
+  byte counters of the profiles.
 
 The roofline entry is for the dominant kernel, timed live with HIP events
 on its own stream through libdg's profiling hooks. The cpu_baseline entry
@@ -325,7 +332,29 @@ def cpu_baseline_full(d, prompt, budget_s):
                       f"{C}; host cores {cores}, BLAS threads {blas}"}
 
 
-WORKLOADS = {"sampler": bench_sampler, "full": bench_full}
+def bench_copy(args):
+    """Plain device-to-device copy of a known size: the calibration run for HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE per launch divided by the bytes copied)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return {"metric": "device copy bandwidth (read + write)", "value": 2 * n * args.steps / dt / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": dt * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": f"calibration copy of {n} bytes per launch"}}
+
+
+WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "copy": bench_copy}
 
 
 def main():
@@ -339,13 +368,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the sharding plan is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: libdg has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
-        args.steps = 480 if args.workload == "sampler" else 96
+        args.steps = {"sampler": 480, "copy": 20}.get(args.workload, 96)
     if args.warmup is None:
-        args.warmup = 48 if args.workload == "sampler" else 4
+        args.warmup = {"sampler": 48, "copy": 2}.get(args.workload, 4)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (libdg runs only on MI355X).", file=sys.stderr)

@@ -70,6 +70,7 @@ _SIGS = {
     "dg_weights_bytes": (_SZ, [ctypes.POINTER(dg_model_desc)]),
     "dg_weight_tensor": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _I32, _I32, _I32, ctypes.POINTER(_SZ),
                                         ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "dg_load_weight": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _I32, _I32, _I32, _P, _P, _P]),
     "dg_prepare_weights": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P]),
     "dg_kv_bytes": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
     "dg_workspace_size": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
@@ -201,6 +202,11 @@ def dg_weight_tensor(desc, kind, layer=0, expert=0):
     _check("dg_weight_tensor", lib.dg_weight_tensor(ctypes.byref(desc), kind, layer, expert, ctypes.byref(off),
                                                     ctypes.byref(r), ctypes.byref(c)))
     return off.value, r.value, c.value
+
+
+def dg_load_weight(desc, kind, layer, expert, d_src, d_weights, stream=None):
+    return _check("dg_load_weight", lib.dg_load_weight(ctypes.byref(desc), kind, layer, expert, ptr(d_src),
+                                                       ptr(d_weights), stream_handle(stream)))
 
 
 def dg_prepare_weights(desc, d_weights, stream=None):

@@ -1,6 +1,7 @@
 // Row-wise and elementwise kernels of the denoising step: token-embedding
 // gather (+ the self-conditioning vector), RMSNorm, the tempered
-// probabilities fed to self-conditioning, and the embedding transpose.
+// probabilities fed to self-conditioning, the embedding transpose and the
+// packing of row-major expert matrices into their fragment-tiled layout.
 #include <math.h>
 
 #include <algorithm>
@@ -8,6 +9,7 @@
 #include "dg_common.h"
 #include "mfma.h"
 #include "prof.h"
+#include "tiles.h"
 
 namespace dg {
 
@@ -165,6 +167,34 @@ int transpose(const void* in, int64_t R, int64_t C, void* out, int dtype, hipStr
   else
     transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, static_cast<float*>(out));
   DG_LAUNCH_CHECK("transpose_kernel");
+  return DG_OK;
+}
+
+// dst[tiled_index(r, k)] = src[r * K + k] for one matrix of a tile group (tiles.h)
+template <typename T>
+__global__ void pack_tiled_kernel(const T* __restrict__ src, int64_t R, int64_t K, int which, int gr, int gw,
+                                  T* __restrict__ dst) {
+  const int64_t n = R * K;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / K, k = i - r * K;
+    dst[tiled_index(r, k, which, K, gr, gw)] = src[i];
+  }
+}
+
+int pack_tiled(const void* src, int64_t R, int64_t K, int which, int gr, int gw, void* dst, int dtype,
+               hipStream_t s) {
+  if (R % (16 * gr) != 0 || K % 32 != 0 || which < 0 || which >= gw)
+    return fail(DG_ERR_INVALID, "pack_tiled: shape does not tile");
+  const int64_t n = R * K;
+  if (n == 0) return DG_OK;
+  if (dtype == DG_BF16)
+    pack_tiled_kernel<bf16_t><<<grid_for(n), 256, 0, s>>>(static_cast<const bf16_t*>(src), R, K, which, gr, gw,
+                                                          static_cast<bf16_t*>(dst));
+  else
+    pack_tiled_kernel<float><<<grid_for(n), 256, 0, s>>>(static_cast<const float*>(src), R, K, which, gr, gw,
+                                                         static_cast<float*>(dst));
+  DG_LAUNCH_CHECK("pack_tiled_kernel");
   return DG_OK;
 }
 

@@ -22,6 +22,7 @@
 #include "dg_common.h"
 #include "gemm.h"
 #include "prof.h"
+#include "tiles.h"
 
 namespace dg {
 
@@ -43,6 +44,10 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s);
 int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s);
+int launch_synth_tiled(uint64_t seed, const uint64_t* tids, int64_t R, int64_t K, int gr, int gw, float sigma,
+                       int dtype, void* out, hipStream_t s);
+int pack_tiled(const void* src, int64_t R, int64_t K, int which, int gr, int gw, void* dst, int dtype,
+               hipStream_t s);
 size_t sample_workspace_bytes(int64_t rows, int64_t vocab);
 int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
                        hipStream_t stream);
@@ -123,15 +128,25 @@ static int tensor_info(const dg_model_desc& d, const WLayout& L, int kind, int l
       *off = L.sh_gu[layer]; *rows = Fs; *cols = D; break;
     case DG_W_SH_UP: *off = L.sh_gu[layer] + (d.gated ? Fs * D * es : 0); *rows = Fs; *cols = D; break;
     case DG_W_SH_DOWN: *off = L.sh_down[layer]; *rows = D; *cols = Fs; break;
+    // routed experts: offset of the expert's fragment-tiled gate/up (or down) region
     case DG_W_EX_GATE:
       if (!d.gated) return fail(DG_ERR_INVALID, "ungated model has no gate weights");
       *off = L.ex_gu[layer] + expert * gu_stride * es; *rows = F; *cols = D; break;
-    case DG_W_EX_UP:
-      *off = L.ex_gu[layer] + expert * gu_stride * es + (d.gated ? F * D * es : 0); *rows = F; *cols = D; break;
+    case DG_W_EX_UP: *off = L.ex_gu[layer] + expert * gu_stride * es; *rows = F; *cols = D; break;
     case DG_W_EX_DOWN: *off = L.ex_down[layer] + expert * D * F * es; *rows = D; *cols = F; break;
     default: return fail(DG_ERR_INVALID, "unknown weight kind");
   }
   return DG_OK;
+}
+
+// Tile grouping of the fragment-tiled kinds (tiles.h); false for row-major kinds.
+static bool tiling_of(const dg_model_desc& d, int kind, int* which, int* gr, int* gw) {
+  switch (kind) {
+    case DG_W_EX_GATE: *which = 0; *gr = 1; *gw = 2; return true;
+    case DG_W_EX_UP: *which = d.gated ? 1 : 0; *gr = 1; *gw = d.gated ? 2 : 1; return true;
+    case DG_W_EX_DOWN: *which = 0; *gr = kDownGroup; *gw = 1; return true;
+    default: return false;
+  }
 }
 
 int check_desc(const dg_model_desc* d) {
@@ -396,6 +411,23 @@ int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int
   return tensor_info(*desc, L, kind, layer, expert, offset, rows, cols);
 }
 
+int dg_load_weight(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert, const void* d_src,
+                   void* d_weights, void* stream) {
+  DG_TRY(check_desc(desc));
+  if (!d_src || !d_weights) return fail(DG_ERR_INVALID, "d_src and d_weights are required");
+  if (kind == DG_W_EMBED_T) return fail(DG_ERR_INVALID, "DG_W_EMBED_T is derived by dg_prepare_weights");
+  const WLayout L = weight_layout(*desc);
+  size_t off;
+  int64_t r, c;
+  DG_TRY(tensor_info(*desc, L, kind, layer, expert, &off, &r, &c));
+  char* dst = static_cast<char*>(d_weights) + off;
+  hipStream_t s = as_stream(stream);
+  int which, gr, gw;
+  if (tiling_of(*desc, kind, &which, &gr, &gw)) return pack_tiled(d_src, r, c, which, gr, gw, dst, desc->dtype, s);
+  DG_HIP(hipMemcpyAsync(dst, d_src, static_cast<size_t>(r * c) * esize(*desc), hipMemcpyDeviceToDevice, s));
+  return DG_OK;
+}
+
 int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream) {
   DG_TRY(check_desc(desc));
   if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
@@ -432,11 +464,15 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
     if (d.gated) DG_TRY(fill(DG_W_SH_GATE, l, 0, lb + 5));
     DG_TRY(fill(DG_W_SH_UP, l, 0, lb + 6));
     DG_TRY(fill(DG_W_SH_DOWN, l, 0, lb + 7));
+    const size_t es = esize(d);
     for (int e = 0; e < d.n_experts; ++e) {
       const uint64_t eb = kExpert + 8ull * (1024ull * l + e);
-      if (d.gated) DG_TRY(fill(DG_W_EX_GATE, l, e, eb + 0));
-      DG_TRY(fill(DG_W_EX_UP, l, e, eb + 1));
-      DG_TRY(fill(DG_W_EX_DOWN, l, e, eb + 2));
+      const uint64_t gu_tids[2] = {d.gated ? eb + 0 : eb + 1, eb + 1};
+      const size_t gu_off = L.ex_gu[l] + static_cast<size_t>(e) * (d.gated ? 2 : 1) * d.d_expert * d.d_model * es;
+      DG_TRY(launch_synth_tiled(seed, gu_tids, d.d_expert, d.d_model, 1, d.gated ? 2 : 1, sigma, d.dtype, w + gu_off, s));
+      const uint64_t dn_tid[1] = {eb + 2};
+      const size_t dn_off = L.ex_down[l] + static_cast<size_t>(e) * d.d_model * d.d_expert * es;
+      DG_TRY(launch_synth_tiled(seed, dn_tid, d.d_model, d.d_expert, kDownGroup, 1, sigma, d.dtype, w + dn_off, s));
     }
   }
   return transpose(w + L.embed, d.vocab, d.d_model, w + L.embed_t, d.dtype, s);

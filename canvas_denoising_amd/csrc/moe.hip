@@ -14,10 +14,11 @@
 // Expert GEMMs: with a 256-token canvas an expert sees about 16 tokens, so
 // the work is a stream of expert weights (arithmetic intensity ~16 flop/B):
 // HBM-bound, and with a loaded HBM latency of a few microseconds it is
-// latency-bound unless many bytes are in flight. Each wave owns 16 output
-// features of one expert and streams their weight rows straight from HBM
-// into MFMA B fragments through a ring of register stages (64 k per stage,
-// two stages ahead of the one being multiplied), together with the expert's
+// latency-bound unless many bytes are in flight. The weights are stored
+// fragment-tiled (tiles.h), so each wave streams one contiguous run of
+// memory (gate/up: the 16-feature gate and up blocks, 2 x 16 rows; down: 64
+// output rows) with 1 KB per load instruction, straight into MFMA B
+// fragments through a ring of register stages, together with the expert's
 // gathered token rows (A fragments, from L2). Up to 32 tokens are held in
 // accumulators per pass; an expert with more tokens takes further passes.
 // No LDS and no barriers: waves are independent.
@@ -28,6 +29,7 @@
 #include "dg_common.h"
 #include "mfma.h"
 #include "prof.h"
+#include "tiles.h"
 
 namespace dg {
 
@@ -145,48 +147,79 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 }
 
 // ------------------------------------------------------------------ experts
+#ifndef DG_EXP_KSP_GU
+#define DG_EXP_KSP_GU 2
+#endif
+#ifndef DG_EXP_KSP_DN
+#define DG_EXP_KSP_DN 2
+#endif
+#ifndef DG_EXP_NS
+#define DG_EXP_NS 3
+#endif
 constexpr int kExpWaves = 4;
-constexpr int kMTP = 2;   // 16-token tiles held per pass (32 tokens)
-constexpr int kNS = 3;    // register stages (2 in flight while one is multiplied)
-constexpr int kKS = 64;   // k per stage: two MFMA k-steps
+constexpr int kKspGU = DG_EXP_KSP_GU;  // k-tiles per register stage, gate/up
+constexpr int kKspDN = DG_EXP_KSP_DN;  // k-tiles per register stage, down
+constexpr int kNS = DG_EXP_NS;         // register stages (NS - 1 in flight while one is multiplied)
 
-// One pass of a wave over NT 16-token tiles of its expert: A (token rows) and B
-// (weight rows) fragments stream through kNS register stages. Loads are never
-// predicated (rows past the expert's tokens reuse its last token and their
-// results are not stored; prefetches past the last stage re-read it), so the
-// compiler can keep exactly kNS - 1 stages of loads outstanding.
-template <typename T, int NB, int NT>
-struct StreamPass {
+// Block b of an expert grid -> (expert, block within the expert). Workgroups
+// of one expert read the same token rows, so with E a multiple of 8 they are
+// kept on one XCD (the dispatcher sends block b to XCD b % 8).
+__device__ inline void expert_of_block(int b, int per_e, int E, int* e, int* q) {
+  if ((E & 7) == 0) {
+    const int x = b & 7, j = b >> 3;
+    *e = (j / per_e) * 8 + x;
+    *q = j % per_e;
+  } else {
+    *e = b / per_e;
+    *q = b % per_e;
+  }
+}
+
+// One pass of a wave over one tile group of its expert's weights (G tiles per
+// k-tile, contiguous in memory, tiles.h) against NT 16-token tiles. Weight
+// and token fragments stream through NS register stages of KSP k-tiles.
+// Loads are never predicated (k-tiles past the end re-read the last one and
+// are not multiplied; token rows past the expert's count repeat its last
+// token and are not stored), so the compiler keeps exactly NS - 1 stages of
+// loads outstanding.
+template <typename T, int G, int NT, int KSP>
+struct GroupStream {
   using Fr = Frag<T>;
   using FT = typename Fr::type;
   struct Stage {
-    FT b[NB][2];
-    FT a[NT][2];
+    FT b[KSP][G];
+    FT a[KSP][NT];
   };
-  f32x4_t acc[NB][NT];
+  f32x4_t acc[G][NT];
 
-  __device__ inline void run(const T* const* brow, const T* const* arow, int nst) {
+  // bt: this lane's fragment in k-tile 0 of the group; arow[t]: this lane's
+  // token row of tile t at column 8 * (lane / 16); KT: k-tiles of 32.
+  __device__ inline void run(const T* bt, const T* const* arow, int KT) {
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0, 0, 0, 0};
+      for (int t = 0; t < NT; ++t) acc[g][t] = f32x4_t{0, 0, 0, 0};
+    const int nst = (KT + KSP - 1) / KSP;
     auto load = [&](Stage& S, int s) {
-      const int k0 = min(s, nst - 1) * kKS;
+      const int base = min(s, nst - 1) * KSP;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int u = 0; u < KSP; ++u) {
+        const int kt = min(base + u, KT - 1);
 #pragma unroll
-        for (int m = 0; m < NB; ++m) S.b[m][kk] = Fr::load(brow[m] + k0 + kk * 32);
+        for (int g = 0; g < G; ++g) S.b[u][g] = Fr::load(bt + (static_cast<int64_t>(kt) * G + g) * kTileElems);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) S.a[t][kk] = Fr::load(arow[t] + k0 + kk * 32);
+        for (int t = 0; t < NT; ++t) S.a[u][t] = Fr::load(arow[t] + kt * 32);
       }
     };
-    auto compute = [&](const Stage& S) {
+    auto compute = [&](const Stage& S, int s) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int u = 0; u < KSP; ++u)
+        if (s * KSP + u < KT) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int m = 0; m < NB; ++m) acc[m][t] = Fr::mma(S.a[t][kk], S.b[m][kk], acc[m][t]);
+            for (int g = 0; g < G; ++g) acc[g][t] = Fr::mma(S.a[u][t], S.b[u][g], acc[g][t]);
+        }
     };
     Stage st[kNS];
 #pragma unroll
@@ -196,22 +229,21 @@ struct StreamPass {
 #pragma unroll
       for (int u = 0; u < kNS; ++u) {
         load(st[(u + kNS - 1) % kNS], s0 + u + kNS - 1);
-        compute(st[u]);
+        compute(st[u], s0 + u);
       }
     }
-    // tail: the remaining (< kNS) stages are already loaded
+    // tail: the remaining (< NS) stages are already loaded
 #pragma unroll
     for (int u = 0; u < kNS - 1; ++u)
-      if (s0 + u < nst) compute(st[u]);
+      if (s0 + u < nst) compute(st[u], s0 + u);
   }
 };
 
-// act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j  (GATED) or GeLU(h W_up[e]^T)_j
-// for the slots of expert e. Grid: (ceil(F / 64), E); wave w owns features j0 .. j0+15.
-template <typename T, bool GATED, int NT>
-__device__ inline void gateup_pass(const T* h, int64_t ldh, const T* wg, const T* wu, int F, int D, int beg,
-                                   int cnt, int p0, const int32_t* perm, T* act, int j0, int lane) {
-  constexpr int NB = GATED ? 2 : 1;
+// act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j (G = 2) or GeLU(h W_up[e]^T)_j (G = 1)
+// for up to 16 NT slots of expert e starting at p0; the wave owns features j0 .. j0 + 15.
+template <typename T, int G, int NT>
+__device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, int KT, int beg, int cnt, int p0,
+                                   const int32_t* perm, T* act, int j0, int lane) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
 #pragma unroll
@@ -219,46 +251,46 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* wg, const T
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
   }
-  const T* brow[NB];
-  brow[0] = wu;
-  if constexpr (GATED) brow[1] = wg;
-  StreamPass<T, NB, NT> sp;
-  sp.run(brow, arow, D / kKS);
+  GroupStream<T, G, NT, kKspGU> sp;
+  sp.run(bt, arow, KT);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
       if (s < cnt) {
-        const float u = sp.acc[0][t][i];
-        const float v = GATED ? gelu_erf(sp.acc[NB - 1][t][i]) * u : gelu_erf(u);
+        const float v = G == 2 ? gelu_erf(sp.acc[0][t][i]) * sp.acc[G - 1][t][i] : gelu_erf(sp.acc[0][t][i]);
         act[static_cast<int64_t>(beg + s) * F + j0 + fr] = from_f32<T>(v);
       }
     }
 }
 
+// Grid: E * per_e workgroups of 4 waves; wave w of block q of expert e owns feature block 4 q + w
+// (16 features: one gate/up tile group).
 template <typename T, bool GATED>
 __global__ __launch_bounds__(256) void expert_gateup_kernel(
-    const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int64_t expert_stride, int F, int D,
+    const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, T* __restrict__ act) {
+  constexpr int G = GATED ? 2 : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.y;
-  const int j0 = (blockIdx.x * kExpWaves + wave) * 16;
-  if (j0 >= F) return;
+  int e, q;
+  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  const int fb = q * kExpWaves + wave;
+  if (fb * 16 >= F) return;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const T* wbase = w_gu + static_cast<int64_t>(e) * expert_stride;
-  const T* wu = wbase + static_cast<int64_t>(GATED ? F + j0 + fr : j0 + fr) * D + fk;
-  const T* wg = wbase + static_cast<int64_t>(j0 + fr) * D + fk;
-  for (int p0 = 0; p0 < cnt; p0 += kMTP * 16) {
-    if (cnt - p0 > 16) gateup_pass<T, GATED, 2>(h, ldh, wg, wu, F, D, beg, cnt, p0, perm, act, j0, lane);
-    else gateup_pass<T, GATED, 1>(h, ldh, wg, wu, F, D, beg, cnt, p0, perm, act, j0, lane);
+  const int KT = D / 32;
+  const T* bt = w_gu + static_cast<int64_t>(e) * G * F * D + static_cast<int64_t>(fb) * KT * G * kTileElems +
+                lane * 8;
+  for (int p0 = 0; p0 < cnt; p0 += 32) {
+    if (cnt - p0 > 16) gateup_pass<T, G, 2>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, fb * 16, lane);
+    else gateup_pass<T, G, 1>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, fb * 16, lane);
   }
 }
 
+// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 64 outputs n0 .. n0 + 63
 template <typename T, int NT>
-__device__ inline void down_pass(const T* act, const T* wrow, int F, int D, int beg, int cnt, int p0,
+__device__ inline void down_pass(const T* act, const T* bt, int F, int D, int beg, int cnt, int p0,
                                  const float* slot_gate, float* out, int n0, int lane) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
@@ -267,34 +299,42 @@ __device__ inline void down_pass(const T* act, const T* wrow, int F, int D, int 
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
   }
-  const T* brow[1] = {wrow};
-  StreamPass<T, 1, NT> sp;
-  sp.run(brow, arow, F / kKS);
+  GroupStream<T, kDownGroup, NT, kKspDN> sp;
+  sp.run(bt, arow, F / 32);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-      if (s < cnt) out[static_cast<int64_t>(beg + s) * D + n0 + fr] = slot_gate[beg + s] * sp.acc[0][t][i];
+      if (s < cnt) {
+        const float gs = slot_gate[beg + s];
+        float* o = out + static_cast<int64_t>(beg + s) * D + n0 + fr;
+#pragma unroll
+        for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * sp.acc[g][t][i];
+      }
     }
 }
 
-// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f]; grid (ceil(D / 64), E)
+// Grid: E * per_e workgroups of 4 waves; wave w of block q of expert e owns output group 4 q + w
+// (kDownGroup * 16 rows of W_down).
 template <typename T>
 __global__ __launch_bounds__(256) void expert_down_kernel(
-    const T* __restrict__ act, const T* __restrict__ w_down, int64_t expert_stride, int F, int D,
+    const T* __restrict__ act, const T* __restrict__ w_down, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate, float* __restrict__ out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.y;
-  const int n0 = (blockIdx.x * kExpWaves + wave) * 16;
+  int e, q;
+  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  const int rg = q * kExpWaves + wave;
+  const int n0 = rg * kDownGroup * 16;
   if (n0 >= D) return;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const T* wrow = w_down + static_cast<int64_t>(e) * expert_stride + static_cast<int64_t>(n0 + fr) * F + fk;
-  for (int p0 = 0; p0 < cnt; p0 += kMTP * 16) {
-    if (cnt - p0 > 16) down_pass<T, 2>(act, wrow, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
-    else down_pass<T, 1>(act, wrow, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
+  const int KT = F / 32;
+  const T* bt = w_down + static_cast<int64_t>(e) * D * F + static_cast<int64_t>(rg) * KT * kDownGroup * kTileElems +
+                lane * 8;
+  for (int p0 = 0; p0 < cnt; p0 += 32) {
+    if (cnt - p0 > 16) down_pass<T, 2>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
+    else down_pass<T, 1>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
   }
 }
 
@@ -318,27 +358,24 @@ int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s) {
-  if (F % kKS != 0 || D % kKS != 0) return fail(DG_ERR_UNSUPPORTED, "expert widths must be multiples of 64");
-  const int64_t gu_stride = static_cast<int64_t>(gated ? 2 : 1) * F * D;
-  const int64_t dn_stride = static_cast<int64_t>(D) * F;
-  dim3 g1((F + 16 * kExpWaves - 1) / (16 * kExpWaves), E);
-  dim3 g2((D + 16 * kExpWaves - 1) / (16 * kExpWaves), E);
+  if (F % 64 != 0 || D % (16 * kDownGroup) != 0) return fail(DG_ERR_UNSUPPORTED, "expert widths must be multiples of 64");
+  const int per_gu = ceil_div(F / 16, kExpWaves);
+  const int per_dn = ceil_div(D / (16 * kDownGroup), kExpWaves);
+  const dim3 g1(E * per_gu), g2(E * per_dn);
   {
     ProfScope ps("expert_gateup", s);
     if (dtype == DG_BF16) {
-      if (gated)
-        expert_gateup_kernel<bf16_t, true><<<g1, 256, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
-            static_cast<const bf16_t*>(w_gu), gu_stride, F, D, offsets, perm, static_cast<bf16_t*>(act));
-      else
-        expert_gateup_kernel<bf16_t, false><<<g1, 256, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
-            static_cast<const bf16_t*>(w_gu), gu_stride, F, D, offsets, perm, static_cast<bf16_t*>(act));
+      const bf16_t* hh = static_cast<const bf16_t*>(h);
+      const bf16_t* w = static_cast<const bf16_t*>(w_gu);
+      bf16_t* a = static_cast<bf16_t*>(act);
+      if (gated) expert_gateup_kernel<bf16_t, true><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
+      else expert_gateup_kernel<bf16_t, false><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
     } else {
-      if (gated)
-        expert_gateup_kernel<float, true><<<g1, 256, 0, s>>>(static_cast<const float*>(h), ldh,
-            static_cast<const float*>(w_gu), gu_stride, F, D, offsets, perm, static_cast<float*>(act));
-      else
-        expert_gateup_kernel<float, false><<<g1, 256, 0, s>>>(static_cast<const float*>(h), ldh,
-            static_cast<const float*>(w_gu), gu_stride, F, D, offsets, perm, static_cast<float*>(act));
+      const float* hh = static_cast<const float*>(h);
+      const float* w = static_cast<const float*>(w_gu);
+      float* a = static_cast<float*>(act);
+      if (gated) expert_gateup_kernel<float, true><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
+      else expert_gateup_kernel<float, false><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
     }
   }
   DG_LAUNCH_CHECK("expert_gateup_kernel");
@@ -346,10 +383,10 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
     ProfScope ps("expert_down", s);
     if (dtype == DG_BF16)
       expert_down_kernel<bf16_t><<<g2, 256, 0, s>>>(static_cast<const bf16_t*>(act),
-          static_cast<const bf16_t*>(w_down), dn_stride, F, D, offsets, slot_gate, out);
+          static_cast<const bf16_t*>(w_down), E, F, D, per_dn, offsets, slot_gate, out);
     else
       expert_down_kernel<float><<<g2, 256, 0, s>>>(static_cast<const float*>(act),
-          static_cast<const float*>(w_down), dn_stride, F, D, offsets, slot_gate, out);
+          static_cast<const float*>(w_down), E, F, D, per_dn, offsets, slot_gate, out);
   }
   DG_LAUNCH_CHECK("expert_down_kernel");
   return DG_OK;

@@ -13,6 +13,7 @@
 #include <algorithm>
 
 #include "dg_common.h"
+#include "tiles.h"
 
 // Keep every multiply and add separately rounded (no FMA contraction) so the
 // values match the host generator bit for bit.
@@ -53,6 +54,24 @@ __global__ void synth_normal_kernel(uint64_t key, int64_t n, float scale, T* __r
   }
 }
 
+// Fill of a fragment-tiled tensor group (tiles.h): physical element p holds
+// the value that stream keys[which] gives row-major element r * K + k of its
+// matrix, i.e. the same values as synth_normal_kernel over each matrix.
+template <typename T>
+__global__ void synth_tiled_kernel(uint64_t key0, uint64_t key1, int64_t n, int64_t K, int gr, int gw, float scale,
+                                   T* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; p < n; p += stride) {
+    int which;
+    int64_t r, k;
+    tiled_coords(p, K, gr, gw, &which, &r, &k);
+    const uint64_t key = which ? key1 : key0;
+    const float v = irwin_hall4(mix64(key + static_cast<uint64_t>(r * K + k + 1) * kGolden)) * scale;
+    if constexpr (sizeof(T) == 2) out[p] = f32_to_bf16(v);
+    else out[p] = v;
+  }
+}
+
 __global__ void synth_ids_kernel(uint64_t key, int64_t n, uint32_t vocab, int32_t* __restrict__ out) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -87,6 +106,22 @@ int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int
   else
     synth_normal_kernel<float><<<grid_for(n), 256, 0, s>>>(key, n, scale, static_cast<float*>(out));
   DG_LAUNCH_CHECK("synth_normal_kernel");
+  return DG_OK;
+}
+
+// gw (1 or 2) matrices of R x K, streams tids[0 .. gw-1], stored tiled with gr row blocks per group
+int launch_synth_tiled(uint64_t seed, const uint64_t* tids, int64_t R, int64_t K, int gr, int gw, float sigma,
+                       int dtype, void* out, hipStream_t s) {
+  const int64_t n = R * K * gw;
+  if (n == 0) return DG_OK;
+  const uint64_t k0 = stream_key(seed, tids[0]);
+  const uint64_t k1 = gw > 1 ? stream_key(seed, tids[1]) : k0;
+  const float scale = normal_scale(sigma);
+  if (dtype == DG_BF16)
+    synth_tiled_kernel<bf16_t><<<grid_for(n), 256, 0, s>>>(k0, k1, n, K, gr, gw, scale, static_cast<bf16_t*>(out));
+  else
+    synth_tiled_kernel<float><<<grid_for(n), 256, 0, s>>>(k0, k1, n, K, gr, gw, scale, static_cast<float*>(out));
+  DG_LAUNCH_CHECK("synth_tiled_kernel");
   return DG_OK;
 }
 

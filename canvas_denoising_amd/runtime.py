@@ -79,9 +79,19 @@ class Model:
 
     # --- views
     def tensor(self, kind, layer=0, expert=0) -> torch.Tensor:
+        """Row-major [rows, cols] view of one weight tensor (routed-expert tensors are tiled: use load_weight)."""
+        if kind in (L.DG_W_EX_GATE, L.DG_W_EX_UP, L.DG_W_EX_DOWN):
+            raise ValueError("routed-expert weights are stored fragment-tiled; write them with load_weight")
         off, r, c = L.dg_weight_tensor(self.desc, kind, layer, expert)
         es = 2 if self.desc.dtype == L.DG_BF16 else 4
         return self.weights[off:off + r * c * es].view(self.dtype).view(r, c)
+
+    def load_weight(self, kind, src: torch.Tensor, layer=0, expert=0):
+        """Store a row-major device tensor of the model dtype as weight (kind, layer, expert)."""
+        _, r, c = L.dg_weight_tensor(self.desc, kind, layer, expert)
+        if tuple(src.shape) != (r, c) or src.dtype != self.dtype or not src.is_cuda or not src.is_contiguous():
+            raise ValueError(f"expected a contiguous {self.dtype} CUDA tensor of shape ({r}, {c})")
+        L.dg_load_weight(self.desc, kind, layer, expert, src, self.weights)
 
     def kv_view(self):
         """(K, V) as [n_layers, n_kv_heads, capacity, head_dim] tensors."""

@@ -178,8 +178,9 @@ int dg_synth_planted_logits(uint64_t seed, int32_t step, int32_t rows, int32_t v
  * tid = 1 (embedding), 2 / 3 (self-conditioning W1 / W2),
  * 2^20 + 64 layer + {0 q, 1 k, 2 v, 3 o, 4 router, 5 shared gate, 6 shared up,
  * 7 shared down}, 2^32 + 8 (1024 layer + expert) + {0 gate, 1 up, 2 down};
- * element i is the row-major index inside the tensor. Then derives the
- * transposed embedding (dg_prepare_weights). */
+ * element i is the row-major index inside the tensor (routed-expert tensors
+ * are then stored fragment-tiled, as dg_load_weight would store them). Then
+ * derives the transposed embedding (dg_prepare_weights). */
 int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights,
                           void* stream);
 
@@ -205,12 +206,27 @@ enum {
 
 /* Total bytes of the packed weight buffer (every tensor 256-byte aligned). */
 size_t dg_weights_bytes(const dg_model_desc* desc);
-/* Byte offset and [rows x cols] shape of one tensor; layer / expert are
- * ignored where they do not apply. Q, K and V of a layer are adjacent (one
- * fused projection), as are gate and up of the shared expert and of each
- * routed expert. */
+/* Byte offset and logical [rows x cols] shape of one tensor; layer / expert
+ * are ignored where they do not apply. Q, K and V of a layer are adjacent
+ * (one fused projection), as are gate and up of the shared expert. Every
+ * tensor except the routed experts' is stored row-major at that offset.
+ * The routed experts' matrices (DG_W_EX_*) are stored fragment-tiled so the
+ * expert kernels stream contiguous memory: 16-row x 32-column tiles of 512
+ * elements in which element 8 l + j is row l % 16, column 8 (l / 16) + j;
+ * gate/up: tiles ordered [16-feature block][column tile][gate, up] (up
+ * alone when ungated), down: [64-row group][column tile][16-row block of
+ * the group]. For DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the
+ * expert's shared gate/up region. Write them with dg_load_weight. */
 int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
                      size_t* offset, int64_t* rows, int64_t* cols);
+/* Store one tensor from a row-major [rows x cols] device array d_src of the
+ * model dtype (shape as dg_weight_tensor reports) into the weight buffer,
+ * tiling the routed-expert kinds; asynchronous on `stream`; d_src must stay
+ * valid until the copy has run. DG_W_EMBED_T is rejected (derived by
+ * dg_prepare_weights). Errors: DG_ERR_INVALID for bad kind / layer / expert
+ * or NULL pointers. */
+int dg_load_weight(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
+                   const void* d_src, void* d_weights, void* stream);
 /* Rebuild DG_W_EMBED_T from DG_W_EMBED (call after loading weights). */
 int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream);
 

@@ -241,6 +241,45 @@ def test_generate_block_matches_sampler_on_final_logits(libs):
     model.close()
 
 
+@pytest.mark.parametrize("dtype,gated", [("bf16", 1), ("f32", 0)])
+def test_load_weight_reproduces_tiled_fill(libs, dtype, gated):
+    """Routed-expert matrices are stored fragment-tiled. dg_load_weight (row-major -> tiled via the
+    forward index map) of the host generator's matrices must rebuild, byte for byte, the region
+    dg_synth_fill_weights wrote (tiled position -> row-major index via the inverse map)."""
+    L, configs, runtime = libs
+    model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=2, E=8, F=128)
+    announce(f"load_weight tiled dtype={dtype} gated={gated}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    es = 2 if dtype == "bf16" else 4
+    layer, expert = 1, 5
+    d = model.desc
+    off_gu, _, _ = L.dg_weight_tensor(d, L.DG_W_EX_UP, layer, expert)
+    off_dn, _, _ = L.dg_weight_tensor(d, L.DG_W_EX_DOWN, layer, expert)
+    n_gu = (2 if gated else 1) * d.d_expert * d.d_model * es
+    n_dn = d.d_model * d.d_expert * es
+    torch.cuda.synchronize()
+    ref_gu = model.weights[off_gu:off_gu + n_gu].clone()
+    ref_dn = model.weights[off_dn:off_dn + n_dn].clone()
+    model.weights[off_gu:off_gu + n_gu].zero_()
+    model.weights[off_dn:off_dn + n_dn].zero_()
+    ex = W["layers"][layer]["experts"][expert]
+    names = (["gate"] if gated else []) + ["up", "down"]
+    kinds = {"gate": L.DG_W_EX_GATE, "up": L.DG_W_EX_UP, "down": L.DG_W_EX_DOWN}
+    srcs = []
+    for name in names:
+        src = torch.from_numpy(ex[name].astype(np.float32)).to(tdt).cuda().contiguous()
+        srcs.append(src)
+        model.load_weight(kinds[name], src, layer, expert)
+    torch.cuda.synchronize()
+    assert torch.equal(model.weights[off_gu:off_gu + n_gu], ref_gu)
+    assert torch.equal(model.weights[off_dn:off_dn + n_dn], ref_dn)
+    # the tiled layout is not row-major: a row-major copy would differ
+    assert not torch.equal(ref_dn.view(tdt).view(d.d_model, d.d_expert).cpu(), srcs[-1].cpu())
+    with pytest.raises(ValueError):
+        model.tensor(L.DG_W_EX_DOWN, layer, expert)
+    model.close()
+
+
 def test_denoise_step_is_deterministic(libs):
     L, configs, runtime = libs
     announce("denoise determinism")
