@@ -7,22 +7,26 @@
 // the query is processed the standard way). Scores are scaled by
 // 1/sqrt(head_dim); query head j reads KV head floor(j * Hkv / Hq).
 //
-// bf16 path (MFMA, split-KV flash attention). A workgroup owns 64 query rows
-// of one KV-head group (the Hq/Hkv query heads sharing that KV head are laid
-// side by side, so a K/V tile serves all of them) and one slice of the keys;
-// each of its 4 waves owns one 16-query tile (kQT; two tiles per wave double
-// the register footprint and halve occupancy). K and V^T tiles of
-// 64 keys are staged through LDS, and the next tile is already being fetched
-// into registers while the current one is multiplied. Each wave works on the
+// bf16 path (MFMA, split-KV flash attention). A workgroup owns 128 query
+// rows of one KV-head group (the Hq/Hkv query heads sharing that KV head are
+// laid side by side, so one K/V tile serves all of them) and one slice of
+// the keys; each of its 4 waves owns two 16-query tiles, so every K and V
+// fragment read from LDS feeds two MFMAs. K and V^T tiles of 32 keys stream
+// into a ring of 4 LDS stages by asynchronous global->LDS copies (dma.h),
+// three stages ahead of the one being multiplied, with one barrier per
+// stage. The V cache is stored transposed in 32-position blocks
+// (kvlayout.h), so a V^T stage is one contiguous copy and each V^T fragment
+// one 16-byte LDS read per lane; K rows are XOR-swizzled in LDS so the 16
+// rows a fragment read touches fall on distinct banks. Each wave works on the
 // transposed scores S^T = K Q^T: in the 16x16 accumulator layout every lane
 // then owns a single query column, so the online-softmax state (running max
 // and sum) is per lane and the rescale of O^T is a per-lane multiply. The
 // probabilities already sit in the lane/k arrangement the second MFMA wants
-// for P^T as its B operand (lane group g holds keys 4g..4g+3 of two adjacent
-// 16-key tiles, a permutation of the 32 keys of the k-step), and V^T is read
-// from LDS with the same key permutation, so P never goes through LDS.
-// Each workgroup writes (max, sum, unnormalised O) for its key slice; a merge
-// kernel (one wave per query row) combines the slices in a fixed order.
+// for P^T as its B operand (lane group g holds keys 4g..4g+3 of both 16-key
+// tiles), which is the slot order of the V cache blocks, so P never goes
+// through LDS. Each workgroup writes (max, sum, unnormalised O) for its key
+// slice and a merge kernel (one wave per query row) combines the slices in a
+// fixed order; with a single slice the kernel writes O itself.
 // Exponentials are base 2 with log2(e) folded into the scale.
 //
 // fp32 path: a direct kernel, one thread per (query row, head), online
@@ -33,6 +37,8 @@
 
 #include "dg_common.h"
 #include "mfma.h"
+#include "dma.h"
+#include "kvlayout.h"
 #include "prof.h"
 
 namespace dg {
@@ -40,35 +46,40 @@ namespace dg {
 struct AttnArgs {
   const void* q;        // [M x Hq*hd]
   int64_t ldq;
-  const void* kc;       // [Hkv][cap][hd] of this layer
-  const void* vc;
+  const void* kc;       // K [Hkv][cap][hd] of this layer
+  const void* vc;       // V [Hkv][cap/32][hd][32] (kvlayout.h)
   int64_t head_stride;  // cap * hd
   int M, Hq, Hkv, hd;
   int pos0;             // absolute position of query row 0; keys 0 .. pos0+M-1
   int causal;
   float scale_log2;     // log2(e) / sqrt(hd)
   int splits;
-  int key_chunk;        // keys per split (multiple of 64)
+  int key_chunk;        // keys per split (multiple of 32)
   float* part_o;        // [splits][Hq*M][hd]
   float* part_ml;       // [splits][Hq*M][2]
   void* o;              // [M x Hq*hd] output (merge)
   int64_t ldo;
 };
 
-constexpr int kKB = 64;                    // keys per LDS block
-constexpr int kQT = 1;                     // 16-query tiles per wave
-constexpr int kWGRows = 4 * kQT * 16;      // query rows per workgroup
+constexpr int kKS = 32;                   // keys per LDS stage
+constexpr int kStages = 4;                // LDS ring depth
+constexpr int kQT = 2;                    // 16-query tiles per wave
+constexpr int kWGRows = 4 * kQT * 16;     // query rows per workgroup
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KPAD = HD + 8;    // sK row pitch (bf16)
-  constexpr int VPAD = kKB + 8;   // sVt row pitch (bf16)
-  constexpr int HS = HD / 32;     // k-steps over head_dim
-  constexpr int HT = HD / 16;     // O^T tiles over head_dim
-  constexpr int CH = HD / 8;      // 16-byte chunks per key row
-  constexpr int LOADS = kKB * CH / 256;
-  __shared__ __align__(16) bf16_t sK[kKB * KPAD];
-  __shared__ __align__(16) bf16_t sVt[HD * VPAD];
+  constexpr int HS = HD / 32;             // k-steps over head_dim
+  constexpr int HT = HD / 16;             // O^T tiles over head_dim
+  constexpr int ROWB = HD * 2;            // bytes per K row
+  constexpr int CPR = ROWB / 16;          // 16-byte chunks per K row
+  constexpr int KBYTES = kKS * ROWB;      // K bytes per stage
+  constexpr int VBYTES = HD * kKS * 2;    // V^T bytes per stage
+  constexpr int SBYTES = KBYTES + VBYTES;
+  constexpr int KL = KBYTES / 4096;       // K copies per thread per stage (1 KB per wave copy)
+  constexpr int VL = VBYTES / 4096;
+  constexpr int LPS = KL + VL;
+  static_assert(KL >= 1 && VL >= 1 && 1024 % ROWB == 0, "stage shape");
+  __shared__ __align__(16) unsigned char smem[kStages * SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
@@ -76,13 +87,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int kvh = blockIdx.y;
   const int split = blockIdx.z;
   const int L = a.pos0 + a.M;
-  const int g4 = lane >> 4;
+  const int g4 = lane >> 4, fr = lane & 15;
 
   int qr[kQT], qhead[kQT], qm[kQT], qpos[kQT];
   bool qvalid[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
-    qr[t] = blockIdx.x * kWGRows + (wave * kQT + t) * 16 + (lane & 15);
+    qr[t] = blockIdx.x * kWGRows + (wave * kQT + t) * 16 + fr;
     qvalid[t] = qr[t] < rows_in_group;
     qhead[t] = kvh * G + (qvalid[t] ? qr[t] / a.M : 0);
     qm[t] = qvalid[t] ? qr[t] % a.M : 0;
@@ -99,6 +110,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     if (first_row / a.M == last_row / a.M) maxpos = a.pos0 + last_row % a.M;
     k_hi = min(k_hi, maxpos + 1);
   }
+  const int nst = k_hi > k_lo ? (k_hi - k_lo + kKS - 1) / kKS : 0;
 
   // Q^T fragments (B operand): lane supplies query qr, head dims 8*g4 .. of each 32-step
   bf16x8_t qf[kQT][HS];
@@ -119,65 +131,72 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     lrun[t] = 0.f;
   }
 
+  // Copy sources. K: wave copy c of a stage covers rows c*RPC .. of the stage; lane l fills LDS
+  // position l % CPR of row l / CPR with the row's chunk (l % CPR) ^ (row % 8). Rows past L re-read
+  // row L-1 (masked). V^T: the stage's 32-position block is contiguous.
   const bf16_t* kbase = static_cast<const bf16_t*>(a.kc) + kvh * a.head_stride;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.vc) + kvh * a.head_stride;
-  uint4 pk[LOADS], pv[LOADS];
-  auto gload = [&](int kb) {
+  constexpr int RPC = 1024 / ROWB;
+  int krow[KL], kchunk[KL];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / CH, ch = c % CH;
-      pk[i] = make_uint4(0, 0, 0, 0);
-      pv[i] = make_uint4(0, 0, 0, 0);
-      if (kb + key < k_hi) {
-        pk[i] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(kb + key) * HD + ch * 8);
-        pv[i] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(kb + key) * HD + ch * 8);
-      }
+  for (int i = 0; i < KL; ++i) {
+    const int r = (wave * KL + i) * RPC + lane / CPR;
+    krow[i] = r;
+    kchunk[i] = (lane % CPR) ^ (r & 7);
+  }
+  auto issue = [&](int st, int slot) {
+    const int key0 = k_lo + st * kKS;
+    unsigned char* base = smem + slot * SBYTES;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int key = min(key0 + krow[i], L - 1);
+      dma16(kbase + static_cast<int64_t>(key) * HD + kchunk[i] * 8, base + (wave * KL + i) * 1024);
     }
-  };
-  auto sstore = [&]() {
+    const bf16_t* vb = vbase + static_cast<int64_t>(key0 / kKS) * HD * kKS;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / CH, ch = c % CH;
-      *reinterpret_cast<uint4*>(&sK[key * KPAD + ch * 8]) = pk[i];
-      const uint32_t w[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(ch * 8 + 2 * e) * VPAD + key] = static_cast<bf16_t>(w[e] & 0xFFFF);
-        sVt[(ch * 8 + 2 * e + 1) * VPAD + key] = static_cast<bf16_t>(w[e] >> 16);
-      }
-    }
+    for (int i = 0; i < VL; ++i) dma16(vb + (wave * VL + i) * 512 + lane * 8, base + KBYTES + (wave * VL + i) * 1024);
   };
 
-  if (k_lo < k_hi) gload(k_lo);
-  for (int kb = k_lo; kb < k_hi; kb += kKB) {
-    __syncthreads();  // every wave is done with the previous block
-    sstore();
-    __syncthreads();
-    if (kb + kKB < k_hi) gload(kb + kKB);  // next block in flight during this one
+  // Q is in registers before the ring starts: the waits below then only count stage copies
+  wait_vm_n<0>();
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < nst) issue(u, u);
+  for (int st = 0; st < nst; ++st) {
+    wait_stages<LPS, kStages>(min(kStages - 2, nst - 1 - st));
+    // stage st is in LDS for every wave, and every wave is done with stage st-1
+    __builtin_amdgcn_s_barrier();
+    if (st + kStages - 1 < nst) issue(st + kStages - 1, (st + kStages - 1) % kStages);
+    const unsigned char* sk = smem + (st % kStages) * SBYTES;
+    const unsigned char* sv = sk + KBYTES;
+    const int key0 = k_lo + st * kKS;
 
+    // K fragments of the stage (A operand of S^T = K Q^T), shared by the wave's query tiles
+    bf16x8_t kf[2][HS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = kt * 16 + fr;
+#pragma unroll
+      for (int h = 0; h < HS; ++h)
+        kf[kt][h] = *reinterpret_cast<const bf16x8_t*>(sk + r * ROWB + (((h * 4 + g4) ^ (r & 7)) << 4));
+    }
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
-      // ---- S^T = K Q^T for 4 key tiles of 16
-      f32x4_t s[4];
+      f32x4_t s[2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < HS; ++h) {
-          const bf16x8_t kf = Frag<bf16_t>::load(&sK[(kt * 16 + (lane & 15)) * KPAD + h * 32 + g4 * 8]);
-          acc = Frag<bf16_t>::mma(kf, qf[t][h], acc);
-        }
+        for (int h = 0; h < HS; ++h) acc = Frag<bf16_t>::mma(kf[kt][h], qf[t][h], acc);
         s[kt] = acc;
       }
-      // scale, mask, block max (this lane's 16 keys, then the 4 lane groups)
+      // scale, mask, stage max (this lane's 8 keys, then the 4 lane groups)
       float bmax = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kb + kt * 16 + g4 * 4 + i;
+          const int key = key0 + kt * 16 + g4 * 4 + i;
           float v = s[kt][i] * a.scale_log2;
           const bool ok = key < k_hi && (!a.causal || key <= qpos[t]);
           v = ok ? v : -INFINITY;
@@ -190,55 +209,47 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // all masked so far: keep the base finite
       const float alpha = exp2f(mrun[t] - mref);
       float psum = 0.f;
+      bf16x8_t pf;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = exp2f(s[kt][i] - mref);
-          s[kt][i] = p;
           psum += p;
+          pf[kt * 4 + i] = static_cast<__bf16>(p);
         }
       psum += shfl_xor(psum, 16);
       psum += shfl_xor(psum, 32);
       lrun[t] = lrun[t] * alpha + psum;
       mrun[t] = mnew;
+      // O^T += V^T P^T: V^T fragment of head dims j*16 .. j*16+15, slots 8*g4 .. 8*g4+7
 #pragma unroll
-      for (int j = 0; j < HT; ++j) o[t][j] *= alpha;
-
-      // ---- O^T += V^T P^T, two k-steps of 32 keys
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t pf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pf[i] = static_cast<__bf16>(s[2 * ks][i]);
-          pf[4 + i] = static_cast<__bf16>(s[2 * ks + 1][i]);
-        }
-#pragma unroll
-        for (int j = 0; j < HT; ++j) {
-          const bf16_t* vr = &sVt[(j * 16 + (lane & 15)) * VPAD + ks * 32 + g4 * 4];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-          bf16x8_t vf;
-          const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-          __builtin_memcpy(&vf, w, 16);
-          o[t][j] = Frag<bf16_t>::mma(vf, pf, o[t][j]);
-        }
+      for (int j = 0; j < HT; ++j) {
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(sv + ((j * 16 + fr) * kKS + g4 * 8) * 2);
+        o[t][j] = Frag<bf16_t>::mma(vf, pf, o[t][j] * alpha);
       }
     }
   }
 
-  // ---- partial results: lane holds O^T[hd = j*16 + 4*g4 + i][query qr]
+  // ---- results: lane holds O^T[hd = j*16 + 4*g4 + i][query qr]
   const int64_t R = static_cast<int64_t>(a.Hq) * a.M;
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     if (!qvalid[t]) continue;
+    if (a.splits == 1) {
+      const float inv = lrun[t] > 0.f ? 1.0f / lrun[t] : 0.f;
+      bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(qm[t]) * a.ldo + qhead[t] * HD;
+#pragma unroll
+      for (int j = 0; j < HT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[j * 16 + g4 * 4 + i] = f32_to_bf16(o[t][j][i] * inv);
+      continue;
+    }
     const int64_t row = static_cast<int64_t>(qhead[t]) * a.M + qm[t];
     float* po = a.part_o + (split * R + row) * HD;
 #pragma unroll
     for (int j = 0; j < HT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) po[j * 16 + g4 * 4 + i] = o[t][j][i];
+      *reinterpret_cast<float4*>(po + j * 16 + g4 * 4) = make_float4(o[t][j][0], o[t][j][1], o[t][j][2], o[t][j][3]);
     if (g4 == 0) {
       a.part_ml[(split * R + row) * 2] = mrun[t];
       a.part_ml[(split * R + row) * 2 + 1] = lrun[t];
@@ -295,7 +306,7 @@ __global__ void attn_f32_kernel(AttnArgs a) {
     const float mn = fmaxf(mx, s);
     const float al = exp2f(mx - mn), p = exp2f(s - mn);
     l = l * al + p;
-    for (int d = 0; d < hd; ++d) acc[d] = acc[d] * al + p * vb[static_cast<int64_t>(t) * hd + d];
+    for (int d = 0; d < hd; ++d) acc[d] = acc[d] * al + p * vb[v_index(t, d, hd)];
     mx = mn;
   }
   float* o = static_cast<float*>(a.o) + static_cast<int64_t>(m) * a.ldo + j * hd;
@@ -326,10 +337,11 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   if (hd != 64 && hd != 128) return fail(DG_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
   const int G = Hq / Hkv;
   const int qtiles = (G * M + kWGRows - 1) / kWGRows;
-  // about 512 workgroups, at least two key blocks per split
-  int splits = std::max(1, std::min(attn_max_splits(), (512 + qtiles * Hkv - 1) / (qtiles * Hkv)));
-  splits = std::min(splits, std::max(1, (L + 2 * kKB - 1) / (2 * kKB)));
-  a.key_chunk = ((L + splits - 1) / splits + kKB - 1) / kKB * kKB;
+  // about 256 workgroups (one per CU; partial results cost HBM traffic per extra split), at least
+  // four key stages per split
+  int splits = std::max(1, std::min(attn_max_splits(), (256 + qtiles * Hkv - 1) / (qtiles * Hkv)));
+  splits = std::min(splits, std::max(1, (L + 4 * kKS - 1) / (4 * kKS)));
+  a.key_chunk = ((L + splits - 1) / splits + kKS - 1) / kKS * kKS;
   a.splits = (L + a.key_chunk - 1) / a.key_chunk;
   dim3 grid(qtiles, Hkv, a.splits);
   {
@@ -338,6 +350,7 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
     else attn_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
   }
   DG_LAUNCH_CHECK("attn_bf16_kernel");
+  if (a.splits == 1) return DG_OK;
   {
     ProfScope ps("attention_merge", s);
     const int64_t rows = static_cast<int64_t>(Hq) * M;

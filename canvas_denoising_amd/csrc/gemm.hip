@@ -17,6 +17,8 @@
 #include "dg_common.h"
 #include "gemm.h"
 #include "mfma.h"
+#include "dma.h"
+#include "kvlayout.h"
 #include "prof.h"
 
 namespace dg {
@@ -60,8 +62,11 @@ __device__ inline void epilogue(const GemmArgs& g, int row, int col, float v) {
         const int per = g.n_kv * g.head_dim;
         const int which = c / per, rem = c - which * per;
         const int h = rem / g.head_dim, d = rem - h * g.head_dim;
-        T* base = static_cast<T*>(which == 0 ? g.kcache : g.vcache);
-        base[h * g.kv_head_stride + static_cast<int64_t>(g.pos0 + row) * g.head_dim + d] = from_f32<T>(v);
+        const int64_t pos = g.pos0 + row;
+        if (which == 0)
+          static_cast<T*>(g.kcache)[h * g.kv_head_stride + pos * g.head_dim + d] = from_f32<T>(v);
+        else
+          static_cast<T*>(g.vcache)[h * g.kv_head_stride + v_index(pos, d, g.head_dim)] = from_f32<T>(v);
       }
       break;
     }
@@ -253,22 +258,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
 // r is stored at position q ^ (r % 8) so the 16 rows a fragment read touches
 // fall on different banks. Rows past M (or N) re-read the last valid row;
 // their results are not stored.
-__device__ inline void wait_vm(int n) {
-  // s_waitcnt with vmcnt = n (gfx9 encoding: low 4 bits + bits 14..15), exp/lgkm counters untouched
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // conservative: wait for everything
-  }
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_cvoid_t;
-
 template <int BM, int BN, int NS>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, int k_per_split) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
@@ -329,13 +318,10 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
     unsigned char* base = smem + slot * SS;
 #pragma unroll
     for (int i = 0; i < ALPW; ++i)
-      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(asrc[i] + k0),
-                                       (lds_void_t*)(base + (wave * ALPW + i) * 8 * ROWB), 16, 0, 0);
+      dma16(asrc[i] + k0, base + (wave * ALPW + i) * 8 * ROWB);
 #pragma unroll
     for (int i = 0; i < BLPW; ++i)
-      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(bsrc[i] + k0),
-                                       (lds_void_t*)(base + SA + (wave * BLPW + i) * 8 * ROWB),
-                                       16, 0, 0);
+      dma16(bsrc[i] + k0, base + SA + (wave * BLPW + i) * 8 * ROWB);
   };
 
   f32x4_t acc[TM][TN];
@@ -349,8 +335,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int younger = min(NS - 2, nk - 1 - kt);  // stages issued after this one
-    wait_vm(younger * LPS);
+    wait_stages<LPS, NS>(min(NS - 2, nk - 1 - kt));  // leave the stages issued after this one in flight
     // Stage kt is complete for every wave, and every wave is done reading stage kt-1
     // (its fragments were consumed by MFMAs already issued). A bare s_barrier: the
     // fence of __syncthreads() would wait for all outstanding loads, draining the ring.

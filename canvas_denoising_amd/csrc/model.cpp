@@ -22,6 +22,7 @@
 #include "dg_common.h"
 #include "gemm.h"
 #include "prof.h"
+#include "kvlayout.h"
 #include "tiles.h"
 
 namespace dg {
@@ -142,8 +143,8 @@ static int tensor_info(const dg_model_desc& d, const WLayout& L, int kind, int l
 // Tile grouping of the fragment-tiled kinds (tiles.h); false for row-major kinds.
 static bool tiling_of(const dg_model_desc& d, int kind, int* which, int* gr, int* gw) {
   switch (kind) {
-    case DG_W_EX_GATE: *which = 0; *gr = 1; *gw = 2; return true;
-    case DG_W_EX_UP: *which = d.gated ? 1 : 0; *gr = 1; *gw = d.gated ? 2 : 1; return true;
+    case DG_W_EX_GATE: *which = 0; *gr = kGuBlocks; *gw = 2; return true;
+    case DG_W_EX_UP: *which = d.gated ? 1 : 0; *gr = kGuBlocks; *gw = d.gated ? 2 : 1; return true;
     case DG_W_EX_DOWN: *which = 0; *gr = kDownGroup; *gw = 1; return true;
     default: return false;
   }
@@ -164,6 +165,7 @@ int check_desc(const dg_model_desc* d) {
                           d->d_selfcond, d->vocab};
   for (int64_t v : dims)
     if (v < 64 || v % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "d_model, q width, FFN widths and vocab must be multiples of 64");
+  if (d->d_model % (16 * kDownGroup) != 0) return fail(DG_ERR_UNSUPPORTED, "d_model must be a multiple of 64");
   if (d->n_experts < 1 || d->n_experts > 256) return fail(DG_ERR_UNSUPPORTED, "n_experts must be in [1, 256]");
   if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return fail(DG_ERR_UNSUPPORTED, "top_k must be in [1, min(16, n_experts)]");
   if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return fail(DG_ERR_INVALID, "rms_eps must be finite and >= 0");
@@ -469,7 +471,8 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
       const uint64_t eb = kExpert + 8ull * (1024ull * l + e);
       const uint64_t gu_tids[2] = {d.gated ? eb + 0 : eb + 1, eb + 1};
       const size_t gu_off = L.ex_gu[l] + static_cast<size_t>(e) * (d.gated ? 2 : 1) * d.d_expert * d.d_model * es;
-      DG_TRY(launch_synth_tiled(seed, gu_tids, d.d_expert, d.d_model, 1, d.gated ? 2 : 1, sigma, d.dtype, w + gu_off, s));
+      DG_TRY(launch_synth_tiled(seed, gu_tids, d.d_expert, d.d_model, kGuBlocks, d.gated ? 2 : 1, sigma, d.dtype,
+                                w + gu_off, s));
       const uint64_t dn_tid[1] = {eb + 2};
       const size_t dn_off = L.ex_down[l] + static_cast<size_t>(e) * d.d_model * d.d_expert * es;
       DG_TRY(launch_synth_tiled(seed, dn_tid, d.d_model, d.d_expert, kDownGroup, 1, sigma, d.dtype, w + dn_off, s));
@@ -495,11 +498,14 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
   if (!d_weights || !d_kv || !d_workspace) return fail(DG_ERR_INVALID, "weights, KV cache and workspace are required");
   if (capacity < desc->canvas) return fail(DG_ERR_CAPACITY, "KV capacity must hold at least one canvas");
   if (capacity > (1ll << 30)) return fail(DG_ERR_CAPACITY, "KV capacity too large");
+  if (capacity % kVBlock != 0) return fail(DG_ERR_CAPACITY, "KV capacity must be a multiple of 32");
   for (const void* p : {d_weights, d_kv, d_workspace})
     if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return fail(DG_ERR_INVALID, "device buffers must be 256-byte aligned");
   const WsLayout wl = ws_layout(*desc);
   if (ws_bytes < wl.total) return fail(DG_ERR_CAPACITY, "workspace too small (see dg_workspace_size)");
   DG_TRY(zero_fill(d_workspace, wl.total, nullptr));
+  // attention reads whole 32-position V blocks and weights unused positions by 0: keep them finite
+  DG_TRY(zero_fill(d_kv, dg_kv_bytes(desc, capacity), nullptr));
   DG_HIP(hipStreamSynchronize(nullptr));
   dg_ctx* c = new dg_ctx;
   c->d = *desc;

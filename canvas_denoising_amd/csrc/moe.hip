@@ -14,14 +14,16 @@
 // Expert GEMMs: with a 256-token canvas an expert sees about 16 tokens, so
 // the work is a stream of expert weights (arithmetic intensity ~16 flop/B):
 // HBM-bound, and with a loaded HBM latency of a few microseconds it is
-// latency-bound unless many bytes are in flight. The weights are stored
-// fragment-tiled (tiles.h), so each wave streams one contiguous run of
-// memory (gate/up: the 16-feature gate and up blocks, 2 x 16 rows; down: 64
-// output rows) with 1 KB per load instruction, straight into MFMA B
+// latency-bound unless many bytes are in flight, and DRAM-page-bound unless
+// those bytes come in long contiguous runs. The weights are stored
+// fragment-tiled (tiles.h): a workgroup owns one tile group (gate/up: 32
+// features, gate and up; down: 64 output rows), a contiguous stretch of
+// memory, and its 4 waves split the k-tiles so that each stage of loads is
+// one contiguous run with 1 KB per load instruction, straight into MFMA B
 // fragments through a ring of register stages, together with the expert's
-// gathered token rows (A fragments, from L2). Up to 32 tokens are held in
-// accumulators per pass; an expert with more tokens takes further passes.
-// No LDS and no barriers: waves are independent.
+// gathered token rows (A fragments, from L2). The waves' partial sums meet
+// in LDS at the end. Up to 32 tokens are held in accumulators per pass; an
+// expert with more tokens takes further passes.
 #include <math.h>
 
 #include <algorithm>
@@ -150,18 +152,18 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 #ifndef DG_EXP_KSP_GU
 #define DG_EXP_KSP_GU 2
 #endif
+#ifndef DG_EXP_NS_GU
+#define DG_EXP_NS_GU 2
+#endif
 #ifndef DG_EXP_KSP_DN
 #define DG_EXP_KSP_DN 2
 #endif
-#ifndef DG_EXP_NS
-#define DG_EXP_NS 3
+#ifndef DG_EXP_NS_DN
+#define DG_EXP_NS_DN 2
 #endif
 constexpr int kExpWaves = 4;
-constexpr int kKspGU = DG_EXP_KSP_GU;  // k-tiles per register stage, gate/up
-constexpr int kKspDN = DG_EXP_KSP_DN;  // k-tiles per register stage, down
-constexpr int kNS = DG_EXP_NS;         // register stages (NS - 1 in flight while one is multiplied)
 
-// Block b of an expert grid -> (expert, block within the expert). Workgroups
+// Block b of an expert grid -> (expert, unit within the expert). Workgroups
 // of one expert read the same token rows, so with E a multiple of 8 they are
 // kept on one XCD (the dispatcher sends block b to XCD b % 8).
 __device__ inline void expert_of_block(int b, int per_e, int E, int* e, int* q) {
@@ -175,15 +177,19 @@ __device__ inline void expert_of_block(int b, int per_e, int E, int* e, int* q) 
   }
 }
 
-// One pass of a wave over one tile group of its expert's weights (G tiles per
-// k-tile, contiguous in memory, tiles.h) against NT 16-token tiles. Weight
-// and token fragments stream through NS register stages of KSP k-tiles.
-// Loads are never predicated (k-tiles past the end re-read the last one and
-// are not multiplied; token rows past the expert's count repeat its last
-// token and are not stored), so the compiler keeps exactly NS - 1 stages of
-// loads outstanding.
-template <typename T, int G, int NT, int KSP>
-struct GroupStream {
+// One pass of a workgroup over one tile group of its expert's weights (G
+// tiles per k-tile, tiles.h) against NT 16-token tiles. The k-tiles are
+// split over the 4 waves in runs of KSP: stage s of wave w holds k-tiles
+// s * 4 KSP + w KSP + u (u < KSP), so the four waves' loads of one stage
+// cover 4 KSP consecutive k-tiles of the group, one contiguous run of memory
+// (whole DRAM pages rather than scattered pieces of them). Weight and token
+// fragments stream through NS register stages. Loads are never predicated
+// (k-tiles past the end re-read the last one and are not multiplied; token
+// rows past the expert's count repeat its last token and are not stored),
+// so the compiler keeps exactly NS - 1 stages of loads outstanding. Each
+// wave ends with the partial sums of its k-tiles.
+template <typename T, int G, int NT, int KSP, int NS>
+struct SplitStream {
   using Fr = Frag<T>;
   using FT = typename Fr::type;
   struct Stage {
@@ -194,14 +200,16 @@ struct GroupStream {
 
   // bt: this lane's fragment in k-tile 0 of the group; arow[t]: this lane's
   // token row of tile t at column 8 * (lane / 16); KT: k-tiles of 32.
-  __device__ inline void run(const T* bt, const T* const* arow, int KT) {
+  __device__ inline void run(const T* bt, const T* const* arow, int KT, int wave) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[g][t] = f32x4_t{0, 0, 0, 0};
-    const int nst = (KT + KSP - 1) / KSP;
+    constexpr int kPer = kExpWaves * KSP;
+    const int nst = (KT + kPer - 1) / kPer;
+    const int first = wave * KSP;
     auto load = [&](Stage& S, int s) {
-      const int base = min(s, nst - 1) * KSP;
+      const int base = min(s, nst - 1) * kPer + first;
 #pragma unroll
       for (int u = 0; u < KSP; ++u) {
         const int kt = min(base + u, KT - 1);
@@ -214,36 +222,56 @@ struct GroupStream {
     auto compute = [&](const Stage& S, int s) {
 #pragma unroll
       for (int u = 0; u < KSP; ++u)
-        if (s * KSP + u < KT) {
+        if (s * kPer + first + u < KT) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g][t] = Fr::mma(S.a[u][t], S.b[u][g], acc[g][t]);
         }
     };
-    Stage st[kNS];
+    Stage st[NS];
 #pragma unroll
-    for (int u = 0; u < kNS - 1; ++u) load(st[u], u);
+    for (int u = 0; u < NS - 1; ++u) load(st[u], u);
     int s0 = 0;
-    for (; s0 + kNS <= nst; s0 += kNS) {
+    for (; s0 + NS <= nst; s0 += NS) {
 #pragma unroll
-      for (int u = 0; u < kNS; ++u) {
-        load(st[(u + kNS - 1) % kNS], s0 + u + kNS - 1);
+      for (int u = 0; u < NS; ++u) {
+        load(st[(u + NS - 1) % NS], s0 + u + NS - 1);
         compute(st[u], s0 + u);
       }
     }
     // tail: the remaining (< NS) stages are already loaded
 #pragma unroll
-    for (int u = 0; u < kNS - 1; ++u)
+    for (int u = 0; u < NS - 1; ++u)
       if (s0 + u < nst) compute(st[u], s0 + u);
+  }
+
+  // Sum the partials of the 4 waves into wave 0's acc (red: 3 * G * NT * 64 f32x4 of LDS).
+  __device__ inline void reduce(f32x4_t* red, int wave, int lane) {
+    if (wave > 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[(((wave - 1) * G + g) * NT + t) * 64 + lane] = acc[g][t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < kExpWaves - 1; ++w)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[g][t] += red[((w * G + g) * NT + t) * 64 + lane];
+    }
   }
 };
 
-// act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j (G = 2) or GeLU(h W_up[e]^T)_j (G = 1)
-// for up to 16 NT slots of expert e starting at p0; the wave owns features j0 .. j0 + 15.
-template <typename T, int G, int NT>
+// act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j (gated) or GeLU(h W_up[e]^T)_j for up to
+// 16 NT slots of expert e starting at p0 and the 16 kGuBlocks features j0 .. of the tile group.
+template <typename T, bool GATED, int NT>
 __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, int KT, int beg, int cnt, int p0,
-                                   const int32_t* perm, T* act, int j0, int lane) {
+                                   const int32_t* perm, T* act, int j0, int wave, int lane, f32x4_t* red) {
+  constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
 #pragma unroll
@@ -251,47 +279,54 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, 
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
   }
-  GroupStream<T, G, NT, kKspGU> sp;
-  sp.run(bt, arow, KT);
+  SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU> sp;
+  sp.run(bt, arow, KT, wave);
+  sp.reduce(red, wave, lane);
+  if (wave == 0) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-      if (s < cnt) {
-        const float v = G == 2 ? gelu_erf(sp.acc[0][t][i]) * sp.acc[G - 1][t][i] : gelu_erf(sp.acc[0][t][i]);
-        act[static_cast<int64_t>(beg + s) * F + j0 + fr] = from_f32<T>(v);
+      for (int i = 0; i < 4; ++i) {
+        const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
+        if (s < cnt) {
+#pragma unroll
+          for (int b = 0; b < kGuBlocks; ++b) {
+            const float v = GATED ? gelu_erf(sp.acc[b][t][i]) * sp.acc[kGuBlocks + b][t][i]
+                                  : gelu_erf(sp.acc[b][t][i]);
+            act[static_cast<int64_t>(beg + s) * F + j0 + b * 16 + fr] = from_f32<T>(v);
+          }
+        }
       }
-    }
+  }
+  __syncthreads();  // red is reused by the next pass
 }
 
-// Grid: E * per_e workgroups of 4 waves; wave w of block q of expert e owns feature block 4 q + w
-// (16 features: one gate/up tile group).
+// Grid: E * (F / (16 kGuBlocks)) workgroups of 4 waves; block q of expert e owns feature group q.
 template <typename T, bool GATED>
 __global__ __launch_bounds__(256) void expert_gateup_kernel(
     const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, T* __restrict__ act) {
-  constexpr int G = GATED ? 2 : 1;
+  constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
+  __shared__ f32x4_t red[(kExpWaves - 1) * G * 2 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
-  const int fb = q * kExpWaves + wave;
-  if (fb * 16 >= F) return;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = D / 32;
-  const T* bt = w_gu + static_cast<int64_t>(e) * G * F * D + static_cast<int64_t>(fb) * KT * G * kTileElems +
-                lane * 8;
+  const T* bt = w_gu + static_cast<int64_t>(e) * (GATED ? 2 : 1) * F * D +
+                static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
+  const int j0 = q * 16 * kGuBlocks;
   for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16) gateup_pass<T, G, 2>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, fb * 16, lane);
-    else gateup_pass<T, G, 1>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, fb * 16, lane);
+    if (cnt - p0 > 16) gateup_pass<T, GATED, 2>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red);
+    else gateup_pass<T, GATED, 1>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red);
   }
 }
 
-// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 64 outputs n0 .. n0 + 63
+// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 16 kDownGroup outputs n0 ..
 template <typename T, int NT>
 __device__ inline void down_pass(const T* act, const T* bt, int F, int D, int beg, int cnt, int p0,
-                                 const float* slot_gate, float* out, int n0, int lane) {
+                                 const float* slot_gate, float* out, int n0, int wave, int lane, f32x4_t* red) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
 #pragma unroll
@@ -299,42 +334,44 @@ __device__ inline void down_pass(const T* act, const T* bt, int F, int D, int be
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
   }
-  GroupStream<T, kDownGroup, NT, kKspDN> sp;
-  sp.run(bt, arow, F / 32);
+  SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN> sp;
+  sp.run(bt, arow, F / 32, wave);
+  sp.reduce(red, wave, lane);
+  if (wave == 0) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-      if (s < cnt) {
-        const float gs = slot_gate[beg + s];
-        float* o = out + static_cast<int64_t>(beg + s) * D + n0 + fr;
+      for (int i = 0; i < 4; ++i) {
+        const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
+        if (s < cnt) {
+          const float gs = slot_gate[beg + s];
+          float* o = out + static_cast<int64_t>(beg + s) * D + n0 + fr;
 #pragma unroll
-        for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * sp.acc[g][t][i];
+          for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * sp.acc[g][t][i];
+        }
       }
-    }
+  }
+  __syncthreads();
 }
 
-// Grid: E * per_e workgroups of 4 waves; wave w of block q of expert e owns output group 4 q + w
-// (kDownGroup * 16 rows of W_down).
+// Grid: E * (D / (16 kDownGroup)) workgroups of 4 waves; block q of expert e owns output group q.
 template <typename T>
 __global__ __launch_bounds__(256) void expert_down_kernel(
     const T* __restrict__ act, const T* __restrict__ w_down, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate, float* __restrict__ out) {
+  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * 2 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
-  const int rg = q * kExpWaves + wave;
-  const int n0 = rg * kDownGroup * 16;
-  if (n0 >= D) return;
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = F / 32;
-  const T* bt = w_down + static_cast<int64_t>(e) * D * F + static_cast<int64_t>(rg) * KT * kDownGroup * kTileElems +
+  const T* bt = w_down + static_cast<int64_t>(e) * D * F + static_cast<int64_t>(q) * KT * kDownGroup * kTileElems +
                 lane * 8;
+  const int n0 = q * kDownGroup * 16;
   for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16) down_pass<T, 2>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
-    else down_pass<T, 1>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, lane);
+    if (cnt - p0 > 16) down_pass<T, 2>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red);
+    else down_pass<T, 1>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red);
   }
 }
 
@@ -358,9 +395,10 @@ int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s) {
-  if (F % 64 != 0 || D % (16 * kDownGroup) != 0) return fail(DG_ERR_UNSUPPORTED, "expert widths must be multiples of 64");
-  const int per_gu = ceil_div(F / 16, kExpWaves);
-  const int per_dn = ceil_div(D / (16 * kDownGroup), kExpWaves);
+  if (F % (16 * kGuBlocks) != 0 || D % (16 * kDownGroup) != 0)
+    return fail(DG_ERR_UNSUPPORTED, "expert width and d_model must be multiples of 32 and 64");
+  const int per_gu = F / (16 * kGuBlocks);
+  const int per_dn = D / (16 * kDownGroup);
   const dim3 g1(E * per_gu), g2(E * per_dn);
   {
     ProfScope ps("expert_gateup", s);

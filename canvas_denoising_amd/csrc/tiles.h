@@ -10,9 +10,10 @@
 // Tiles are grouped: a group holds `gr` consecutive 16-row blocks of each of
 // `gw` matrices stored together, G = gr * gw tiles per k-step, ordered
 // [group][k-tile][g] with g = which * gr + (row block % gr). The routed
-// experts use gate/up: gr = 1, gw = 2 (block j of the gate matrix next to
-// block j of the up matrix; gw = 1 without a gate), down: gr = 4, gw = 1. One
-// wave streams one group: a contiguous run of G * K * 32 elements.
+// experts use gate/up: gr = kGuBlocks, gw = 2 (blocks 2j, 2j+1 of the gate
+// matrix next to the same blocks of the up matrix; gw = 1 without a gate),
+// down: gr = kDownGroup, gw = 1. One workgroup streams one group: a
+// contiguous run of G * K * 32 elements.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,6 +22,7 @@
 namespace dg {
 
 constexpr int kTileElems = 512;
+constexpr int kGuBlocks = 2;   // 16-feature blocks per tile group of an expert's gate/up matrices
 constexpr int kDownGroup = 4;  // 16-row blocks per tile group of an expert's down matrix
 
 // Physical element index of element (r, k) of matrix `which` (K columns).

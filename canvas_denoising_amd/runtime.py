@@ -13,6 +13,10 @@ def torch_dtype(dg_dtype: int) -> torch.dtype:
     return torch.bfloat16 if dg_dtype == L.DG_BF16 else torch.float32
 
 
+
+# slot of position p % 32 inside a V cache block (include/dg.h)
+V_SLOT_OF_POS = [((p & 15) >> 2) * 8 + (p >> 4) * 4 + (p & 3) for p in range(32)]
+
 class SamplerState:
     """Buffers for dg_sample_canvas on one canvas: canvas, argmax, accept mask,
     entropies, row statistics, the 16-byte stop state and the sampler scratch."""
@@ -93,11 +97,32 @@ class Model:
             raise ValueError(f"expected a contiguous {self.dtype} CUDA tensor of shape ({r}, {c})")
         L.dg_load_weight(self.desc, kind, layer, expert, src, self.weights)
 
-    def kv_view(self):
-        """(K, V) as [n_layers, n_kv_heads, capacity, head_dim] tensors."""
+    def _kv_raw(self):
         d = self.desc
-        t = self.kv.view(self.dtype).view(2, d.n_layers, d.n_kv_heads, self.capacity, d.head_dim)
-        return t[0], t[1]
+        t = self.kv.view(self.dtype)
+        n = d.n_layers * d.n_kv_heads * self.capacity * d.head_dim
+        k = t[:n].view(d.n_layers, d.n_kv_heads, self.capacity, d.head_dim)
+        v = t[n:].view(d.n_layers, d.n_kv_heads, self.capacity // 32, d.head_dim, 32)
+        return k, v
+
+    def kv_view(self):
+        """(K, V) as [n_layers, n_kv_heads, capacity, head_dim]: K is a view of the cache, V a
+        copy un-tiled from its 32-position transposed blocks (include/dg.h)."""
+        k, v = self._kv_raw()
+        d = self.desc
+        slots = torch.tensor(V_SLOT_OF_POS, device=v.device)
+        vv = v.index_select(4, slots).permute(0, 1, 2, 4, 3).reshape(d.n_layers, d.n_kv_heads, self.capacity,
+                                                                     d.head_dim)
+        return k, vv
+
+    def kv_write(self, layer, k_rows, v_rows, start=0):
+        """Write positions start .. start+n-1 of one layer: k_rows / v_rows [n_kv_heads, n, head_dim]."""
+        k, v = self._kv_raw()
+        n = k_rows.shape[1]
+        k[layer, :, start:start + n] = k_rows.to(self.dtype)
+        pos = torch.arange(start, start + n, device=v.device)
+        slot = torch.tensor(V_SLOT_OF_POS, device=v.device)[pos % 32]
+        v[layer][:, pos // 32, :, slot] = v_rows.to(self.dtype).permute(1, 0, 2)
 
     def buffer(self, which, dtype, shape) -> torch.Tensor:
         ptr, nbytes = L.dg_ctx_buffer(self.ctx, which)

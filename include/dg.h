@@ -213,9 +213,10 @@ size_t dg_weights_bytes(const dg_model_desc* desc);
  * The routed experts' matrices (DG_W_EX_*) are stored fragment-tiled so the
  * expert kernels stream contiguous memory: 16-row x 32-column tiles of 512
  * elements in which element 8 l + j is row l % 16, column 8 (l / 16) + j;
- * gate/up: tiles ordered [16-feature block][column tile][gate, up] (up
- * alone when ungated), down: [64-row group][column tile][16-row block of
- * the group]. For DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the
+ * gate/up: tiles ordered [32-feature group][column tile][gate rows 0-15,
+ * gate rows 16-31, up rows 0-15, up rows 16-31 of the group] (up alone when
+ * ungated), down: [64-row group][column tile][the group's 4 16-row
+ * blocks]. For DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the
  * expert's shared gate/up region. Write them with dg_load_weight. */
 int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
                      size_t* offset, int64_t* rows, int64_t* cols);
@@ -230,8 +231,11 @@ int dg_load_weight(const dg_model_desc* desc, int32_t kind, int32_t layer, int32
 /* Rebuild DG_W_EMBED_T from DG_W_EMBED (call after loading weights). */
 int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream);
 
-/* KV cache: keys then values, each [n_layers][n_kv_heads][capacity][head_dim]
- * in the model dtype. */
+/* KV cache, in the model dtype: keys [n_layers][n_kv_heads][capacity][head_dim]
+ * (row-major), then values [n_layers][n_kv_heads][capacity / 32][head_dim][32]:
+ * V transposed in blocks of 32 positions, where inside a block slot 8 g + j
+ * (g = 0..3) holds position 4 g + j for j < 4 and 16 + 4 g + (j - 4) for
+ * j >= 4. capacity must be a multiple of 32. */
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
 /* Scratch the context needs: activations of one canvas (or one prompt chunk
  * of up to `canvas` rows), MoE routing tables, split-K partials,
@@ -239,8 +243,8 @@ size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
 size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity);
 
 /* Create a context over caller-owned weights, KV cache and workspace (none is
- * copied; all must outlive the context). Zero-fills the workspace (blocking,
- * on the default stream). capacity = KV positions. The committed length
+ * copied; all must outlive the context). Zero-fills the workspace and the KV
+ * cache (blocking, on the default stream). capacity = KV positions. The committed length
  * starts at 0. Limits: canvas <= 256, head_dim 64 or 128 (bf16), d_model,
  * head dims and FFN widths multiples of 64 (bf16) / 32 (fp32), n_experts <=
  * 256, top_k <= 16. */

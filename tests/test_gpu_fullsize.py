@@ -39,14 +39,14 @@ def test_moe_layer_full_size(libs):
     kv_n = d.n_kv_heads * past * hd
     kb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
     vb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT + 1, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
-    K, V = model.kv_view()
-    K[0, :, :past] = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
-    V[0, :, :past] = torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16)
+    model.kv_write(0, torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16),
+                   torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16), 0)
     L.dg_kv_set_length(model.ctx, past)
     x0 = synthetic.normal_f32(2, synthetic.TID_X_INPUT, C * D, 1.0).reshape(C, D)
     x = torch.from_numpy(x0.copy()).cuda()
     model.forward_layer(0, x, C, False)
     torch.cuda.synchronize()
+    K, V = model.kv_view()
 
     W = synthetic.SyntheticWeights(configs.shape_dict(d), seed=0, dtype="bf16", sigma=0.02, cache_experts=False)
     lw = W["layers"][0]

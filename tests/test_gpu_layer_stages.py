@@ -33,15 +33,15 @@ def test_layer_stages(libs, dtype, gated, causal, M, past):
     model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=1, canvas=64, capacity=256)
     tol = tol_for(dtype)
     rng = np.random.default_rng(M + past)
-    K, V = model.kv_view()
     if past:
-        K[0, :, :past] = torch.from_numpy(rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))).to(model.dtype)
-        V[0, :, :past] = torch.from_numpy(rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))).to(model.dtype)
+        model.kv_write(0, torch.from_numpy(rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))).cuda(),
+                       torch.from_numpy(rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))).cuda(), 0)
     L.dg_kv_set_length(model.ctx, past)
     x = torch.from_numpy(rng.normal(size=(M, shape.d_model)).astype(np.float32)).cuda()
     x0 = to_f64(x)
     model.forward_layer(0, x, M, causal)
     torch.cuda.synchronize()
+    K, V = model.kv_view()
 
     lw = W["layers"][0]
     hd, Hq, Hkv, D = shape.head_dim, shape.n_q_heads, shape.n_kv_heads, shape.d_model
@@ -55,6 +55,7 @@ def test_layer_stages(libs, dtype, gated, causal, M, past):
     kc = np.concatenate([to_f64(K[0, :, :past]), k], axis=1)
     vc = np.concatenate([to_f64(V[0, :, :past]), v], axis=1)
     assert_close(to_f64(K[0, :, past:past + M]), k, tol, "written K")
+    assert_close(to_f64(V[0, :, past:past + M]), v, tol, "written V")
     o = OM.attention(q.reshape(M, Hq, hd).transpose(1, 0, 2), kc, vc, past, causal).transpose(1, 0, 2).reshape(M, QW)
     o_gpu = to_f64(model.buffer(L.DG_BUF_ATTN, model.dtype, (64, QW)))[:M]
     assert_close(o_gpu, o, tol, "attention output")

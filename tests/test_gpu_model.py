@@ -191,13 +191,12 @@ def test_forward_layer_heavy_expert(libs, dtype, causal):
     model, W, shape = build(libs, dtype=dtype, gated=1, n_layers=1, E=2, k=1, canvas=256, capacity=512, d=128,
                             Hq=2, Hkv=1, hd=64, F=192, Fs=128, V=256, dsc=64)
     past = 37
-    Kc, Vc = model.kv_view()
     kv_ref = OM.KVCache.empty(shape, 512)
     rng = np.random.default_rng(7)
     kp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
     vp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
-    Kc[0, :, :past] = torch.from_numpy(kp).to(model.dtype)
-    Vc[0, :, :past] = torch.from_numpy(vp).to(model.dtype)
+    model.kv_write(0, torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), 0)
+    Kc, Vc = model.kv_view()
     kv_ref.k[0][:, :past] = to_f64(Kc[0, :, :past])
     kv_ref.v[0][:, :past] = to_f64(Vc[0, :, :past])
     L.dg_kv_set_length(model.ctx, past)
