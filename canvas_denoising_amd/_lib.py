@@ -58,6 +58,7 @@ _SIGS = {
     "dg_version": (ctypes.c_char_p, []),
     "dg_temperature": (_F32, [ctypes.POINTER(dg_sched), _I32]),
     "dg_profile_enable": (ctypes.c_int, [_I32, _I32]),
+    "dg_profile_only": (ctypes.c_int, [ctypes.c_char_p]),
     "dg_profile_report": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
     "dg_sample_workspace_size": (_SZ, [_I32, _I32]),
     "dg_init_canvas": (ctypes.c_int, [ctypes.POINTER(dg_sched), _I32, _I32, _I32, _P, _P, _P]),
@@ -146,6 +147,10 @@ def dg_temperature(sched: dg_sched, step: int) -> float:
 
 def dg_profile_enable(on: bool, max_launches: int = 0):
     return _check("dg_profile_enable", lib.dg_profile_enable(int(on), max_launches))
+
+
+def dg_profile_only(name=None):
+    return _check("dg_profile_only", lib.dg_profile_only(name.encode() if name else None))
 
 
 def dg_profile_report() -> dict:

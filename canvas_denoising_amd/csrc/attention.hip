@@ -12,9 +12,9 @@
 // laid side by side, so one K/V tile serves all of them) and one slice of
 // the keys; each of its 4 waves owns two 16-query tiles, so every K and V
 // fragment read from LDS feeds two MFMAs. K and V^T tiles of 32 keys stream
-// into a ring of 4 LDS stages by asynchronous global->LDS copies (dma.h),
-// three stages ahead of the one being multiplied, with one barrier per
-// stage. The V cache is stored transposed in 32-position blocks
+// into a ring of 8 LDS stages by asynchronous global->LDS copies (dma.h),
+// seven stages ahead of the one being multiplied (the loaded latency is a
+// few microseconds), with one barrier per stage. The V cache is stored transposed in 32-position blocks
 // (kvlayout.h), so a V^T stage is one contiguous copy and each V^T fragment
 // one 16-byte LDS read per lane; K rows are XOR-swizzled in LDS so the 16
 // rows a fragment read touches fall on distinct banks. Each wave works on the
@@ -54,6 +54,7 @@ struct AttnArgs {
   int causal;
   float scale_log2;     // log2(e) / sqrt(hd)
   int splits;
+  int qtiles;           // query-row tiles of kWGRows per KV-head group
   int key_chunk;        // keys per split (multiple of 32)
   float* part_o;        // [splits][Hq*M][hd]
   float* part_ml;       // [splits][Hq*M][2]
@@ -61,31 +62,57 @@ struct AttnArgs {
   int64_t ldo;
 };
 
-constexpr int kKS = 32;                   // keys per LDS stage
-constexpr int kStages = 4;                // LDS ring depth
-constexpr int kQT = 2;                    // 16-query tiles per wave
-constexpr int kWGRows = 4 * kQT * 16;     // query rows per workgroup
+#ifndef DG_ATT_KB2
+#define DG_ATT_KB2 2
+#endif
+constexpr int kVB = 32;                   // positions per V cache block (kvlayout.h)
+constexpr int kKB2 = DG_ATT_KB2;          // V blocks per LDS stage
+constexpr int kKS = kVB * kKB2;           // keys per LDS stage
+#ifndef DG_ATT_NS
+#define DG_ATT_NS 3
+#endif
+constexpr int kStages = DG_ATT_NS;        // LDS ring depth (NS - 1 stages in flight)
+#ifndef DG_ATT_NW
+#define DG_ATT_NW 8
+#endif
+constexpr int kNW = DG_ATT_NW;            // waves per workgroup (4 or 8)
+constexpr int kQT = 8 / kNW;              // 16-query tiles per wave
+constexpr int kWGRows = kNW * kQT * 16;   // query rows per workgroup (128)
+
+// 2^x with the hardware instruction (about 1 ulp; 2^-inf = 0). Arguments here are <= 0.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int HS = HD / 32;             // k-steps over head_dim
   constexpr int HT = HD / 16;             // O^T tiles over head_dim
   constexpr int ROWB = HD * 2;            // bytes per K row
   constexpr int CPR = ROWB / 16;          // 16-byte chunks per K row
   constexpr int KBYTES = kKS * ROWB;      // K bytes per stage
-  constexpr int VBYTES = HD * kKS * 2;    // V^T bytes per stage
+  constexpr int VBYTES = HD * kKS * 2;    // V^T bytes per stage (kKB2 blocks of [HD][32])
   constexpr int SBYTES = KBYTES + VBYTES;
-  constexpr int KL = KBYTES / 4096;       // K copies per thread per stage (1 KB per wave copy)
-  constexpr int VL = VBYTES / 4096;
-  constexpr int LPS = KL + VL;
-  static_assert(KL >= 1 && VL >= 1 && 1024 % ROWB == 0, "stage shape");
+  constexpr int CPW = SBYTES / (kNW * 1024);  // 1 KB wave copies per wave and stage
+  constexpr int LPS = CPW;                     // loads per thread and stage
+  static_assert(CPW >= 1 && CPW * kNW * 1024 == SBYTES && 1024 % ROWB == 0, "stage shape");
   __shared__ __align__(16) unsigned char smem[kStages * SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
   const int rows_in_group = G * a.M;
-  const int kvh = blockIdx.y;
-  const int split = blockIdx.z;
+  // block -> (query tile, KV head, split). The query tiles of one (KV head, split) read the same
+  // K/V stream, so with the unit count a multiple of 8 they run on one XCD (block b on XCD b % 8).
+  const int nunits = a.Hkv * a.splits;
+  int qt, unit;
+  if (nunits % 8 == 0) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    qt = j % a.qtiles;
+    unit = (j / a.qtiles) * 8 + x;
+  } else {
+    qt = blockIdx.x % a.qtiles;
+    unit = blockIdx.x / a.qtiles;
+  }
+  const int kvh = unit % a.Hkv;
+  const int split = unit / a.Hkv;
   const int L = a.pos0 + a.M;
   const int g4 = lane >> 4, fr = lane & 15;
 
@@ -93,7 +120,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   bool qvalid[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
-    qr[t] = blockIdx.x * kWGRows + (wave * kQT + t) * 16 + fr;
+    qr[t] = qt * kWGRows + (wave * kQT + t) * 16 + fr;
     qvalid[t] = qr[t] < rows_in_group;
     qhead[t] = kvh * G + (qvalid[t] ? qr[t] / a.M : 0);
     qm[t] = qvalid[t] ? qr[t] % a.M : 0;
@@ -104,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int k_lo = split * a.key_chunk;
   int k_hi = min(L, k_lo + a.key_chunk);
   if (a.causal) {
-    const int first_row = blockIdx.x * kWGRows;
+    const int first_row = qt * kWGRows;
     const int last_row = min(rows_in_group - 1, first_row + kWGRows - 1);
     int maxpos = a.pos0 + a.M - 1;
     if (first_row / a.M == last_row / a.M) maxpos = a.pos0 + last_row % a.M;
@@ -131,30 +158,42 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     lrun[t] = 0.f;
   }
 
-  // Copy sources. K: wave copy c of a stage covers rows c*RPC .. of the stage; lane l fills LDS
-  // position l % CPR of row l / CPR with the row's chunk (l % CPR) ^ (row % 8). Rows past L re-read
-  // row L-1 (masked). V^T: the stage's 32-position block is contiguous.
+  // Copy sources. A stage is SBYTES / 1 KB wave copies, CPW per wave (copy c = wave * CPW + i); the
+  // first KC are K: copy c covers rows c * RPC .. of the stage and lane l fills LDS position l % CPR
+  // of row l / CPR with the row's chunk (l % CPR) ^ (row % 8); rows past L re-read row L-1 (masked).
+  // The rest are V^T (the stage's contiguous 32-position block): copy c covers hd rows
+  // (c - KC) * 16 .., lane l fills position l % 4 of row l / 4 with chunk (l % 4) ^ ((row / 2) % 4).
   const bf16_t* kbase = static_cast<const bf16_t*>(a.kc) + kvh * a.head_stride;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.vc) + kvh * a.head_stride;
   constexpr int RPC = 1024 / ROWB;
-  int krow[KL], kchunk[KL];
+  constexpr int KC = KBYTES / 1024;
+  int csrc[CPW];  // K: row within the stage * HD + chunk * 8; V: element offset in the block
 #pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    const int r = (wave * KL + i) * RPC + lane / CPR;
-    krow[i] = r;
-    kchunk[i] = (lane % CPR) ^ (r & 7);
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave * CPW + i;
+    if (c < KC) {
+      const int r = c * RPC + lane / CPR;
+      csrc[i] = r * HD + ((lane % CPR) ^ (r & 7)) * 8;
+    } else {
+      const int r = (c - KC) * 16 + lane / 4;  // row of the stage's [kKB2 * HD][32] V^T rows
+      csrc[i] = r * kVB + ((lane % 4) ^ ((r >> 1) & 3)) * 8;
+    }
   }
   auto issue = [&](int st, int slot) {
     const int key0 = k_lo + st * kKS;
     unsigned char* base = smem + slot * SBYTES;
+    const bf16_t* vb = vbase + static_cast<int64_t>(key0 / kVB) * HD * kVB;
+    const int kmax = (L - 1 - key0) * HD;  // element offset of row L-1 relative to key0
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int key = min(key0 + krow[i], L - 1);
-      dma16(kbase + static_cast<int64_t>(key) * HD + kchunk[i] * 8, base + (wave * KL + i) * 1024);
+    for (int i = 0; i < CPW; ++i) {
+      const int c = wave * CPW + i;
+      if (c < KC) {
+        const int off = csrc[i] <= kmax + (HD - 1) ? csrc[i] : kmax + (csrc[i] % HD);
+        dma16(kbase + static_cast<int64_t>(key0) * HD + off, base + c * 1024);
+      } else {
+        dma16(vb + csrc[i], base + c * 1024);
+      }
     }
-    const bf16_t* vb = vbase + static_cast<int64_t>(key0 / kKS) * HD * kKS;
-#pragma unroll
-    for (int i = 0; i < VL; ++i) dma16(vb + (wave * VL + i) * 512 + lane * 8, base + KBYTES + (wave * VL + i) * 1024);
   };
 
   // Q is in registers before the ring starts: the waits below then only count stage copies
@@ -170,11 +209,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     const unsigned char* sk = smem + (st % kStages) * SBYTES;
     const unsigned char* sv = sk + KBYTES;
     const int key0 = k_lo + st * kKS;
+    const bool need_mask = a.causal || key0 + kKS > k_hi;
 
     // K fragments of the stage (A operand of S^T = K Q^T), shared by the wave's query tiles
-    bf16x8_t kf[2][HS];
+    constexpr int KT = kKS / 16;  // 16-key tiles per stage
+    bf16x8_t kf[KT][HS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int r = kt * 16 + fr;
 #pragma unroll
       for (int h = 0; h < HS; ++h)
@@ -182,54 +223,75 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
-      f32x4_t s[2];
+      f32x4_t s[KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h = 0; h < HS; ++h) acc = Frag<bf16_t>::mma(kf[kt][h], qf[t][h], acc);
         s[kt] = acc;
       }
-      // scale, mask, stage max (this lane's 8 keys, then the 4 lane groups)
+      // scale, mask (only stages that reach past k_hi, or causal ones), stage max over this lane's
+      // keys and then the 4 lane groups
       float bmax = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + kt * 16 + g4 * 4 + i;
-          float v = s[kt][i] * a.scale_log2;
-          const bool ok = key < k_hi && (!a.causal || key <= qpos[t]);
-          v = ok ? v : -INFINITY;
-          s[kt][i] = v;
-          bmax = fmaxf(bmax, v);
-        }
-      bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + kt * 16 + g4 * 4 + i;
+            const bool ok = key < k_hi && (!a.causal || key <= qpos[t]);
+            s[kt][i] = ok ? s[kt][i] * a.scale_log2 : -INFINITY;
+            bmax = fmaxf(bmax, s[kt][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[kt][i] *= a.scale_log2;
+            bmax = fmaxf(bmax, s[kt][i]);
+          }
+      }
+      bmax = xrow_max(bmax);
       const float mnew = fmaxf(mrun[t], bmax);
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // all masked so far: keep the base finite
-      const float alpha = exp2f(mrun[t] - mref);
-      float psum = 0.f;
-      bf16x8_t pf;
+      // rescale O and this lane's partial l only when some lane's running max grew (alpha = 1 otherwise)
+      if (__any(mnew != mrun[t])) {
+        const float alpha = fast_exp2(mrun[t] - mref);
+        lrun[t] *= alpha;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(s[kt][i] - mref);
-          psum += p;
-          pf[kt * 4 + i] = static_cast<__bf16>(p);
-        }
-      psum += shfl_xor(psum, 16);
-      psum += shfl_xor(psum, 32);
-      lrun[t] = lrun[t] * alpha + psum;
+        for (int j = 0; j < HT; ++j) o[t][j] *= alpha;
+      }
       mrun[t] = mnew;
-      // O^T += V^T P^T: V^T fragment of head dims j*16 .. j*16+15, slots 8*g4 .. 8*g4+7
+      // O^T += V^T P^T per V block: the P^T fragment of block b is key tiles 2b, 2b+1 (lane group g
+      // holds keys 4g..4g+3 of each, the block's slot order); the V^T fragment of head dims
+      // j*16 .. j*16+15 is row b * HD + j * 16 + lane % 16, slots 8*g4 .. 8*g4+7
 #pragma unroll
-      for (int j = 0; j < HT; ++j) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(sv + ((j * 16 + fr) * kKS + g4 * 8) * 2);
-        o[t][j] = Frag<bf16_t>::mma(vf, pf, o[t][j] * alpha);
+      for (int b = 0; b < kKB2; ++b) {
+        bf16x8_t pf;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(s[2 * b + u][i] - mref);
+            lrun[t] += p;
+            pf[u * 4 + i] = static_cast<__bf16>(p);
+          }
+#pragma unroll
+        for (int j = 0; j < HT; ++j) {
+          const int vr = b * HD + j * 16 + fr;
+          const bf16x8_t vf =
+              *reinterpret_cast<const bf16x8_t*>(sv + (vr * kVB + ((g4 ^ ((vr >> 1) & 3)) << 3)) * 2);
+          o[t][j] = Frag<bf16_t>::mma(vf, pf, o[t][j]);
+        }
       }
     }
   }
+
+  // this lane's partial l covers its lane group's keys: sum the 4 groups
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) lrun[t] = xrow_sum(lrun[t]);
 
   // ---- results: lane holds O^T[hd = j*16 + 4*g4 + i][query qr]
   const int64_t R = static_cast<int64_t>(a.Hq) * a.M;
@@ -257,31 +319,44 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// combine the key slices, one wave per query row:
-// o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// combine the key slices, one wave per query row, splits in a fixed order:
+// o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Every lane reads the (m, l) of all slices (the
+// same addresses) so no cross-lane traffic is needed; lane l owns head dims 2l, 2l+1 (+128 ...).
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int hd) {
   const int64_t R = static_cast<int64_t>(a.Hq) * a.M;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= R) return;
-  float ms = -INFINITY, ls = 0.f;
-  if (lane < a.splits) {
-    ms = a.part_ml[(lane * R + row) * 2];
-    ls = a.part_ml[(lane * R + row) * 2 + 1];
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, ml[s * R + row].x);
+  const int nc = hd / 128;  // float2 columns per lane beyond the first
+  float l = 0.f;
+  float2 acc[2] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
+  for (int s = 0; s < a.splits; ++s) {
+    const float2 e = ml[s * R + row];
+    const float w = e.x == -INFINITY ? 0.f : exp2f(e.x - mx);
+    l += w * e.y;
+    const float2* po = reinterpret_cast<const float2*>(a.part_o + (s * R + row) * hd);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      if (c <= nc && 2 * (lane + 64 * c) < hd) {
+        const float2 v = po[lane + 64 * c];
+        acc[c].x += w * v.x;
+        acc[c].y += w * v.y;
+      }
   }
-  const float mx = wave_max(ms);
-  const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-  const float l = wave_sum(w * ls);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
   const int head = static_cast<int>(row / a.M), m = static_cast<int>(row % a.M);
-  for (int d = lane; d < hd; d += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ws = __shfl(w, s, 64);
-      if (ws != 0.f) acc += ws * a.part_o[(s * R + row) * hd + d];
+  T* out = static_cast<T*>(a.o) + static_cast<int64_t>(m) * a.ldo + head * hd;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int d = 2 * (lane + 64 * c);
+    if (c <= nc && d < hd) {
+      out[d] = from_f32<T>(acc[c].x * inv);
+      out[d + 1] = from_f32<T>(acc[c].y * inv);
     }
-    const float v = l > 0.f ? acc / l : 0.f;
-    static_cast<T*>(a.o)[static_cast<int64_t>(m) * a.ldo + head * hd + d] = from_f32<T>(v);
   }
 }
 
@@ -314,6 +389,10 @@ __global__ void attn_f32_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------- host
+#ifndef DG_ATT_WGS
+#define DG_ATT_WGS 256
+#endif
+constexpr int kAttnWGs = DG_ATT_WGS;  // target workgroups of a launch
 int attn_max_splits() { return 32; }
 
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
@@ -339,15 +418,16 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   const int qtiles = (G * M + kWGRows - 1) / kWGRows;
   // about 256 workgroups (one per CU; partial results cost HBM traffic per extra split), at least
   // four key stages per split
-  int splits = std::max(1, std::min(attn_max_splits(), (256 + qtiles * Hkv - 1) / (qtiles * Hkv)));
+  int splits = std::max(1, std::min(attn_max_splits(), (kAttnWGs + qtiles * Hkv - 1) / (qtiles * Hkv)));
   splits = std::min(splits, std::max(1, (L + 4 * kKS - 1) / (4 * kKS)));
   a.key_chunk = ((L + splits - 1) / splits + kKS - 1) / kKS * kKS;
   a.splits = (L + a.key_chunk - 1) / a.key_chunk;
-  dim3 grid(qtiles, Hkv, a.splits);
+  a.qtiles = qtiles;
+  const dim3 grid(qtiles * Hkv * a.splits);
   {
     ProfScope ps("attention", s);
-    if (hd == 128) attn_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
-    else attn_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    if (hd == 128) attn_bf16_kernel<128><<<grid, 64 * kNW, 0, s>>>(a);
+    else attn_bf16_kernel<64><<<grid, 64 * kNW, 0, s>>>(a);
   }
   DG_LAUNCH_CHECK("attn_bf16_kernel");
   if (a.splits == 1) return DG_OK;

@@ -57,6 +57,23 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 template <typename T>
 __device__ inline T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Combine a value across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48) with the
+// gfx950 row swaps: v_permlane16_swap / v_permlane32_swap given the same register twice return, in
+// one of their two results, the value of the partner row, so op(r0, r1) combines each pair (and,
+// op being commutative, every lane of the pair gets the same bits). VALU only, no LDS round trip.
+__device__ inline float xrow_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float xrow_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);

@@ -58,6 +58,47 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
   for (int i = threadIdx.x; i < D; i += kRowThreads) hr[i] = from_f32<T>(xr[i] * rs);
 }
 
+// Same, one wave per row with the row held in registers (D % 4 == 0, D <= 256 NV): one read of x,
+// float4 loads, a fixed-order sum (per lane over its float4s, then the wave butterfly).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const float* __restrict__ x, T* __restrict__ h, int M,
+                                                           int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int n4 = D / 4;
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<int64_t>(m) * D);
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  T* hr = h + static_cast<int64_t>(m) * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < n4) {
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(hr + 4 * c) =
+            make_uint2(pack_bf16x2(v[i].x * rs, v[i].y * rs), pack_bf16x2(v[i].z * rs, v[i].w * rs));
+      } else {
+        *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(v[i].x * rs, v[i].y * rs, v[i].z * rs, v[i].w * rs);
+      }
+    }
+  }
+}
+
 // P[m][v] = exp((l[m][v] - max_m) / T - lnZ_m): the sampler's tempered distribution,
 // rebuilt from its row statistics (max raw logit, ln of the tempered partition sum)
 template <typename T>
@@ -135,8 +176,18 @@ int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M,
 
 int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s) {
   ProfScope ps("rmsnorm", s);
-  if (dtype == DG_BF16) rmsnorm_kernel<bf16_t><<<M, kRowThreads, 0, s>>>(x, static_cast<bf16_t*>(h), D, eps);
-  else rmsnorm_kernel<float><<<M, kRowThreads, 0, s>>>(x, static_cast<float*>(h), D, eps);
+  constexpr int kNV = 12;  // float4 per lane: rows up to 3072 wide take the one-wave kernel
+  if (D % 4 == 0 && D <= 256 * kNV) {
+    const int grid = (M + 3) / 4;
+    if (dtype == DG_BF16)
+      rmsnorm_wave_kernel<bf16_t, kNV><<<grid, 256, 0, s>>>(x, static_cast<bf16_t*>(h), M, D, eps);
+    else
+      rmsnorm_wave_kernel<float, kNV><<<grid, 256, 0, s>>>(x, static_cast<float*>(h), M, D, eps);
+  } else if (dtype == DG_BF16) {
+    rmsnorm_kernel<bf16_t><<<M, kRowThreads, 0, s>>>(x, static_cast<bf16_t*>(h), D, eps);
+  } else {
+    rmsnorm_kernel<float><<<M, kRowThreads, 0, s>>>(x, static_cast<float*>(h), D, eps);
+  }
   DG_LAUNCH_CHECK("rmsnorm_kernel");
   return DG_OK;
 }

@@ -26,6 +26,7 @@ struct ProfState {
   std::vector<hipEvent_t> pool;
   size_t next = 0;
   std::vector<Pending> pending;
+  std::string only;  // record only launch sites of this name (empty: all)
 };
 ProfState& state() {
   static ProfState s;
@@ -39,6 +40,7 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s) 
   ProfState& st = state();
   if (!st.on) return;
   std::lock_guard<std::mutex> g(st.mu);
+  if (!st.only.empty() && st.only != name) return;
   if (st.next + 2 > st.pool.size()) return;  // pool exhausted: stop recording
   a_ = st.pool[st.next++];
   b_ = st.pool[st.next++];
@@ -84,6 +86,13 @@ int dg_profile_enable(int32_t on, int32_t max_launches) {
     }
   }
   st.on = true;
+  return DG_OK;
+}
+
+int dg_profile_only(const char* name) {
+  ProfState& st = state();
+  std::lock_guard<std::mutex> g(st.mu);
+  st.only = name ? name : "";
   return DG_OK;
 }
 

@@ -111,8 +111,11 @@ float dg_temperature(const dg_sched* sched, int32_t step);
  * it off and frees the pool. dg_profile_report waits for the recorded events
  * and writes a JSON object {kernel: {count, total_us, avg_us}} into buf
  * (host, cap bytes), then clears the record. Not for use during graph
- * capture. */
+ * capture. dg_profile_only(name) restricts recording to the launch sites of
+ * that name (as the report keys them; NULL: all), so a timed region can carry
+ * the events of one kernel only. */
 int dg_profile_enable(int32_t on, int32_t max_launches);
+int dg_profile_only(const char* name);
 int dg_profile_report(char* buf, size_t cap);
 
 /* ------------------------------------------------------------- sampler */
