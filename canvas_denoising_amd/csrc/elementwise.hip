@@ -27,19 +27,22 @@ __device__ inline float block_sum(float v, float* sh) {
   return t;
 }
 
-// x[m] = E[ids[m]] (+ sc[m]); fp32 residual stream. Ids outside [0, V) are out of
-// contract; they are clamped so that a bad id cannot read outside the table.
+// x[m] = E[ids[m]] (+ sc[m]); fp32 residual stream. E is stored fragment-tiled in groups of
+// kVocabGroup 16-row blocks (tiles.h): every 8 consecutive elements of a row are contiguous, so a
+// thread gathers 8 at a time. Ids outside [0, V) are out of contract; they are clamped so that a
+// bad id cannot read outside the table.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void embed_kernel(const T* __restrict__ emb, const int32_t* __restrict__ ids,
                                                              const float* __restrict__ sc, float* __restrict__ x,
                                                              int D, int V) {
   const int m = blockIdx.x;
   const int id = min(max(ids[m], 0), V - 1);
-  const T* e = emb + static_cast<int64_t>(id) * D;
-  for (int i = threadIdx.x; i < D; i += kRowThreads) {
-    float v = to_f32<T>(e[i]);
-    if (sc) v += sc[static_cast<int64_t>(m) * D + i];
-    x[static_cast<int64_t>(m) * D + i] = v;
+  for (int c = threadIdx.x; c < D / 8; c += kRowThreads) {
+    const T* e = emb + tiled_index(id, 8 * c, 0, D, kVocabGroup, 1);
+    float* xr = x + static_cast<int64_t>(m) * D + 8 * c;
+    const float* sr = sc ? sc + static_cast<int64_t>(m) * D + 8 * c : nullptr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xr[j] = to_f32<T>(e[j]) + (sr ? sr[j] : 0.f);
   }
 }
 
@@ -134,16 +137,17 @@ __global__ void probs_bf16x8_kernel(const bf16_t* __restrict__ logits, const flo
   }
 }
 
-// out[c][r] = in[r][c]; 64 x 64 tiles through LDS
+// out[c][r] = in[r][c]; 64 x 64 tiles through LDS. `in` is fragment-tiled with groups of gr 16-row
+// blocks (tiles.h) when gr > 0, row-major otherwise.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t R, int64_t C,
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t R, int64_t C, int gr,
                                                         T* __restrict__ out) {
   __shared__ T tile[64][65];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int i = ty; i < 64; i += 4) {
     const int64_t r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = in[r * C + c];
+    if (r < R && c < C) tile[i][tx] = in[gr > 0 ? tiled_index(r, c, 0, C, gr, 1) : r * C + c];
   }
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
@@ -210,13 +214,14 @@ int probs(const void* logits, const float* stats, float temperature, int M, int6
   return DG_OK;
 }
 
-int transpose(const void* in, int64_t R, int64_t C, void* out, int dtype, hipStream_t s) {
+int transpose(const void* in, int64_t R, int64_t C, int gr, void* out, int dtype, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64));
   if (grid.y > 65535) return fail(DG_ERR_UNSUPPORTED, "transpose: too many rows");
   if (dtype == DG_BF16)
-    transpose_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, static_cast<bf16_t*>(out));
+    transpose_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, gr,
+                                                  static_cast<bf16_t*>(out));
   else
-    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, static_cast<float*>(out));
+    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, gr, static_cast<float*>(out));
   DG_LAUNCH_CHECK("transpose_kernel");
   return DG_OK;
 }

@@ -13,7 +13,6 @@ enum GemmEpi : int {
   EPI_GELU = 3,       // out[T] = GeLU(v)
   EPI_GEGLU = 4,      // paired B rows: out[T][row*ldo + j] = GeLU(gate_j) * up_j
   EPI_QKV = 5,        // col < q_cols -> q out[T]; else K / V cache rows pos0 + row
-  EPI_COMBINE = 6,    // out[f32] += v + sum_j slot_out[slot_of[row*topk + j]][col]
 };
 
 struct GemmArgs {
@@ -32,10 +31,6 @@ struct GemmArgs {
   int64_t kv_head_stride = 0;  // elements between KV heads (capacity * head_dim)
   void* kcache = nullptr;
   void* vcache = nullptr;
-  // EPI_COMBINE
-  const float* slot_out = nullptr;
-  const int* slot_of = nullptr;
-  int topk = 0;
   // split-K scratch: splits * M * N floats
   float* part = nullptr;
 };

@@ -70,12 +70,6 @@ __device__ inline void epilogue(const GemmArgs& g, int row, int col, float v) {
       }
       break;
     }
-    case EPI_COMBINE: {
-      float s = v;
-      for (int j = 0; j < g.topk; ++j) s += g.slot_out[static_cast<int64_t>(g.slot_of[row * g.topk + j]) * g.N + col];
-      static_cast<float*>(g.out)[static_cast<int64_t>(row) * g.ldo + col] += s;
-      break;
-    }
     default:
       break;
   }

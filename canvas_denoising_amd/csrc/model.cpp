@@ -33,14 +33,18 @@ int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M,
 int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s);
 int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
           hipStream_t s);
-int transpose(const void* in, int64_t R, int64_t C, void* out, int dtype, hipStream_t s);
+int transpose(const void* in, int64_t R, int64_t C, int gr, void* out, int dtype, hipStream_t s);
 int zero_fill(void* p, size_t bytes, hipStream_t s);
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
               int dtype, hipStream_t s);
 int attn_max_splits();
+int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
+               hipStream_t s);
 int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel, float* gate, int32_t* offsets,
               int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s);
+int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* slot_of, int M, int D, int k,
+                hipStream_t s);
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s);
@@ -143,6 +147,7 @@ static int tensor_info(const dg_model_desc& d, const WLayout& L, int kind, int l
 // Tile grouping of the fragment-tiled kinds (tiles.h); false for row-major kinds.
 static bool tiling_of(const dg_model_desc& d, int kind, int* which, int* gr, int* gw) {
   switch (kind) {
+    case DG_W_EMBED: *which = 0; *gr = kVocabGroup; *gw = 1; return true;
     case DG_W_EX_GATE: *which = 0; *gr = kGuBlocks; *gw = 2; return true;
     case DG_W_EX_UP: *which = d.gated ? 1 : 0; *gr = kGuBlocks; *gw = d.gated ? 2 : 1; return true;
     case DG_W_EX_DOWN: *which = 0; *gr = kDownGroup; *gw = 1; return true;
@@ -176,7 +181,7 @@ int check_desc(const dg_model_desc* d) {
 // ----------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
-      sc, u, sc_hid, P, gpart, canvas, pred, accept, entropy, row_stats, stop, samp, total;
+      sc, u, sc_hid, P, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, total;
   int64_t gpart_floats;
 };
 
@@ -213,6 +218,8 @@ static WsLayout ws_layout(const dg_model_desc& d) {
   w.P = take(static_cast<size_t>(C) * d.vocab * es);
   w.gpart_floats = 32 * C * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
   w.gpart = take(w.gpart_floats * 4);
+  w.gpart_aux = take(w.gpart_floats * 4);  // split-K scratch of the second stream
+  w.y_sh = take(C * D * 4);
   w.canvas = take(C * 4);
   w.pred = take(C * 4);
   w.accept = take(C);
@@ -236,6 +243,9 @@ struct dg_ctx {
   size_t ws_bytes;
   dg::WLayout wl;
   dg::WsLayout wsl;
+  // second stream: the shared expert runs beside the routed experts (fork / join events)
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace dg {
@@ -252,9 +262,9 @@ static void* kv_v(dg_ctx* c, int l) {
   return c->kv + static_cast<size_t>(c->d.n_layers + l) * c->d.n_kv_heads * c->cap * c->d.head_dim * es;
 }
 
-static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool allow_split) {
+static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool allow_split, bool aux = false) {
   const int splits = gemm_pick_splits(g.M, g.N, g.K, c->d.dtype, c->wsl.gpart_floats, allow_split);
-  g.part = wsp<float>(c, c->wsl.gpart);
+  g.part = wsp<float>(c, aux ? c->wsl.gpart_aux : c->wsl.gpart);
   return gemm(g, c->d.dtype, splits, s, name);
 }
 
@@ -293,6 +303,28 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     DG_TRY(run_gemm(c, g, s, "o_proj", true));
   }
   DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
+  // fork: the shared expert (h -> y_sh) runs on the second stream while the router and the routed
+  // experts run here; both only read h, and each stream has its own split-K scratch
+  DG_HIP(hipEventRecord(c->ev_fork, s));
+  DG_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0));
+  {
+    GemmArgs g;
+    g.A = h; g.lda = D;
+    g.B = wp(c, c->wl.sh_gu[l]); g.ldb = D;
+    g.M = M; g.N = (d.gated ? 2 : 1) * d.d_shared; g.K = D;
+    g.epi = d.gated ? EPI_GEGLU : EPI_GELU; g.pair_f = d.d_shared;
+    g.out = wsp<void>(c, w.sh_act); g.ldo = d.d_shared;
+    DG_TRY(run_gemm(c, g, c->aux, "shared_gateup", false, true));
+  }
+  {
+    GemmArgs g;
+    g.A = wsp<void>(c, w.sh_act); g.lda = d.d_shared;
+    g.B = wp(c, c->wl.sh_down[l]); g.ldb = d.d_shared;
+    g.M = M; g.N = D; g.K = d.d_shared;
+    g.epi = EPI_STORE_F32; g.out = wsp<float>(c, w.y_sh); g.ldo = D;
+    DG_TRY(run_gemm(c, g, c->aux, "shared_down", true, true));
+  }
+  DG_HIP(hipEventRecord(c->ev_join, c->aux));
   {
     GemmArgs g;
     g.A = h; g.lda = D;
@@ -307,25 +339,10 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
   DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
                      wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, s));
-  {
-    GemmArgs g;
-    g.A = h; g.lda = D;
-    g.B = wp(c, c->wl.sh_gu[l]); g.ldb = D;
-    g.M = M; g.N = (d.gated ? 2 : 1) * d.d_shared; g.K = D;
-    g.epi = d.gated ? EPI_GEGLU : EPI_GELU; g.pair_f = d.d_shared;
-    g.out = wsp<void>(c, w.sh_act); g.ldo = d.d_shared;
-    DG_TRY(run_gemm(c, g, s, "shared_gateup", false));
-  }
-  {
-    GemmArgs g;
-    g.A = wsp<void>(c, w.sh_act); g.lda = d.d_shared;
-    g.B = wp(c, c->wl.sh_down[l]); g.ldb = d.d_shared;
-    g.M = M; g.N = D; g.K = d.d_shared;
-    g.epi = EPI_COMBINE; g.out = x; g.ldo = D;
-    g.slot_out = wsp<float>(c, w.slot_out); g.slot_of = wsp<int32_t>(c, w.slot_of); g.topk = d.top_k;
-    DG_TRY(run_gemm(c, g, s, "shared_down_combine", true));
-  }
-  return DG_OK;
+  // join, then x += shared + sum of the token's gated expert outputs (fixed order)
+  DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
+  return moe_combine(x, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of), M, D,
+                     d.top_k, s);
 }
 
 static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
@@ -381,12 +398,7 @@ static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, co
     DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), false, false, s));
   void* h = wsp<void>(c, w.h);
   DG_TRY(rmsnorm(x, h, C, D, d.rms_eps, d.dtype, s));
-  GemmArgs g;
-  g.A = h; g.lda = D;
-  g.B = wp(c, c->wl.embed); g.ldb = D;
-  g.M = C; g.N = d.vocab; g.K = D;
-  g.epi = EPI_STORE; g.out = logits; g.ldo = d.vocab;
-  return run_gemm(c, g, s, "lm_head", false);
+  return vocab_gemm(h, D, wp(c, c->wl.embed), C, d.vocab, D, logits, d.vocab, d.dtype, s);
 }
 
 static int check_ctx(const dg_ctx* c) {
@@ -435,7 +447,8 @@ int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream)
   if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
   const WLayout L = weight_layout(*desc);
   char* w = static_cast<char*>(d_weights);
-  return transpose(w + L.embed, desc->vocab, desc->d_model, w + L.embed_t, desc->dtype, as_stream(stream));
+  return transpose(w + L.embed, desc->vocab, desc->d_model, kVocabGroup, w + L.embed_t, desc->dtype,
+                   as_stream(stream));
 }
 
 int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights, void* stream) {
@@ -453,7 +466,10 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
     return launch_synth_normal(seed, tid, r * cl, sigma, d.dtype, w + off, s);
   };
   const uint64_t kLayer = 1ull << 20, kExpert = 1ull << 32;
-  DG_TRY(fill(DG_W_EMBED, 0, 0, 1));
+  {
+    const uint64_t tid[1] = {1};
+    DG_TRY(launch_synth_tiled(seed, tid, d.vocab, d.d_model, kVocabGroup, 1, sigma, d.dtype, w + L.embed, s));
+  }
   DG_TRY(fill(DG_W_SC1, 0, 0, 2));
   DG_TRY(fill(DG_W_SC2, 0, 0, 3));
   for (int l = 0; l < d.n_layers; ++l) {
@@ -478,7 +494,7 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
       DG_TRY(launch_synth_tiled(seed, dn_tid, d.d_model, d.d_expert, kDownGroup, 1, sigma, d.dtype, w + dn_off, s));
     }
   }
-  return transpose(w + L.embed, d.vocab, d.d_model, w + L.embed_t, d.dtype, s);
+  return transpose(w + L.embed, d.vocab, d.d_model, kVocabGroup, w + L.embed_t, d.dtype, s);
 }
 
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity) {
@@ -517,11 +533,23 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
   c->ws_bytes = ws_bytes;
   c->wl = weight_layout(*desc);
   c->wsl = wl;
+  if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
+    dg_ctx_destroy(c);
+    return fail(DG_ERR_HIP, "could not create the context's stream and events");
+  }
   *out = c;
   return DG_OK;
 }
 
 int dg_ctx_destroy(dg_ctx* ctx) {
+  if (ctx) {
+    if (ctx->aux) (void)hipStreamSynchronize(ctx->aux);
+    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+    if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
+  }
   delete ctx;
   return DG_OK;
 }

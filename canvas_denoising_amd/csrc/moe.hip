@@ -392,6 +392,38 @@ int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel
   return DG_OK;
 }
 
+// x[row][c] += y[row][c] + sum_j slot_out[slot_of[row * k + j]][c], j = 0 .. k-1 in order (the
+// shared expert's output, then the token's gated routed outputs); four columns per thread
+__global__ __launch_bounds__(256) void combine_kernel(float* __restrict__ x, const float* __restrict__ y,
+                                                      const float* __restrict__ slot_out,
+                                                      const int32_t* __restrict__ slot_of, int M, int D4, int k) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * D4) return;
+  const int row = static_cast<int>(i / D4), c4 = static_cast<int>(i - static_cast<int64_t>(row) * D4);
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  const float4* so = reinterpret_cast<const float4*>(slot_out);
+  float4 acc = y4[i];
+  for (int j = 0; j < k; ++j) {
+    const float4 v = so[static_cast<int64_t>(slot_of[row * k + j]) * D4 + c4];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  float4* x4 = reinterpret_cast<float4*>(x);
+  float4 xv = x4[i];
+  xv.x += acc.x; xv.y += acc.y; xv.z += acc.z; xv.w += acc.w;
+  x4[i] = xv;
+}
+
+int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* slot_of, int M, int D, int k,
+                hipStream_t s) {
+  if (D % 4 != 0) return fail(DG_ERR_UNSUPPORTED, "combine: d_model must be a multiple of 4");
+  const int64_t n = static_cast<int64_t>(M) * (D / 4);
+  if (n == 0) return DG_OK;
+  ProfScope ps("moe_combine", s);
+  combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(x, y, slot_out, slot_of, M, D / 4, k);
+  DG_LAUNCH_CHECK("combine_kernel");
+  return DG_OK;
+}
+
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, hipStream_t s) {

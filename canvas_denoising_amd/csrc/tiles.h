@@ -9,7 +9,8 @@
 //
 // Tiles are grouped: a group holds `gr` consecutive 16-row blocks of each of
 // `gw` matrices stored together, G = gr * gw tiles per k-step, ordered
-// [group][k-tile][g] with g = which * gr + (row block % gr). The routed
+// [group][k-tile][g] with g = which * gr + (row block % gr). The embedding
+// matrix (the LM head's weights) uses gr = kVocabGroup, gw = 1; the routed
 // experts use gate/up: gr = kGuBlocks, gw = 2 (blocks 2j, 2j+1 of the gate
 // matrix next to the same blocks of the up matrix; gw = 1 without a gate),
 // down: gr = kDownGroup, gw = 1. One workgroup streams one group: a
@@ -22,6 +23,7 @@
 namespace dg {
 
 constexpr int kTileElems = 512;
+constexpr int kVocabGroup = 2;  // 16-row blocks per tile group of the embedding (LM head) matrix
 constexpr int kGuBlocks = 2;   // 16-feature blocks per tile group of an expert's gate/up matrices
 constexpr int kDownGroup = 4;  // 16-row blocks per tile group of an expert's down matrix
 

@@ -1,0 +1,172 @@
+// LM head of the denoiser: logits[M x V] = h[M x D] E^T over the tied
+// embedding ([P3] "Encoder-denoiser design": logits are produced at every
+// canvas position; [P4] "Gemma-based MoE backbone", table: vocabulary of
+// 262144 tokens).
+//
+// With a canvas of M <= 256 rows the weight matrix E (V x D, 1.5 GB at the
+// benchmark shape) is the stream: every E row is read exactly once, straight
+// from HBM into MFMA B fragments. E is stored fragment-tiled with groups of
+// 32 rows (tiles.h), so a wave's stream is one contiguous run. The rows of
+// h are shared by every wave, so they are staged per 128-byte k-tile into an
+// LDS ring (asynchronous global->LDS copies, XOR-swizzled rows, dma.h) and
+// each wave multiplies all M rows against its 32 columns: 16 x 2 fragment
+// accumulators, every A fragment read from LDS feeding two MFMAs.
+//
+// One loop iteration per k-tile: wait until the copies of the k-tile have
+// landed (each wave issues exactly 8 loads per k-tile, 4 copies into LDS and
+// 4 register loads of E, so a fixed vmcnt leaves the younger k-tiles in
+// flight), one barrier, issue the k-tile NS-1 ahead (k-tiles past the end
+// re-read the last one and are never used), multiply.
+#include <algorithm>
+
+#include "dg_common.h"
+#include "dma.h"
+#include "mfma.h"
+#include "prof.h"
+#include "tiles.h"
+
+namespace dg {
+
+constexpr int kVW = 8;         // waves per workgroup
+constexpr int kVRows = 256;    // rows of h staged per k-tile (M <= 256)
+constexpr int kVNS = 3;        // ring depth (k-tiles)
+constexpr int kVRowB = 128;    // bytes of one h row per k-tile
+
+template <typename T>
+__device__ inline typename Frag<T>::type lds_frag(const unsigned char* stage, int r, int ks, int g4);
+
+template <>
+__device__ inline bf16x8_t lds_frag<bf16_t>(const unsigned char* stage, int r, int ks, int g4) {
+  const int q = ks * 4 + g4;
+  return *reinterpret_cast<const bf16x8_t*>(stage + r * kVRowB + ((q ^ (r & 7)) << 4));
+}
+
+template <>
+__device__ inline f32x8_t lds_frag<float>(const unsigned char* stage, int r, int ks, int g4) {
+  (void)ks;
+  const int q = 2 * g4;
+  const float4 lo = *reinterpret_cast<const float4*>(stage + r * kVRowB + ((q ^ (r & 7)) << 4));
+  const float4 hi = *reinterpret_cast<const float4*>(stage + r * kVRowB + (((q + 1) ^ (r & 7)) << 4));
+  f32x8_t f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+// Grid: ceil(V / (32 kVW)) workgroups of kVW waves; wave w of block b owns vocabulary group
+// b * kVW + w (E rows 32 g .. 32 g + 31).
+template <typename T>
+__global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restrict__ h, int64_t ldh,
+                                                             const T* __restrict__ E, int M, int V, int D,
+                                                             T* __restrict__ logits, int64_t ldo) {
+  constexpr int KE = kVRowB / static_cast<int>(sizeof(T));  // k elements per k-tile
+  constexpr int KS = KE / 32;                               // MFMA k-steps per k-tile
+  constexpr int SBYTES = kVRows * kVRowB;                   // 32 KB per stage
+  constexpr int CPW = SBYTES / (kVW * 1024);                // 1 KB copies per wave per k-tile (4)
+  constexpr int BF = 2 * KS;                                // B fragments per k-tile
+  using FT = typename Frag<T>::type;
+  static_assert(CPW == 4, "8 loads per k-tile: 4 copies + 4 register loads");
+  static_assert((sizeof(T) == 2 && BF == 4) || (sizeof(T) == 4 && BF == 2), "B loads per k-tile");
+  __shared__ __align__(16) unsigned char smem[kVNS * SBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int grp = blockIdx.x * kVW + wave;
+  const bool active = grp * 32 < V;  // idle waves run the loop on group 0 (uniform barriers), store nothing
+  const int KT = D / KE;
+
+  // A copies: copy c = wave * CPW + i covers rows 8c .. 8c+7 of the stage; lane l fills position l % 8
+  // of row 8c + l / 8 with the row's chunk (l % 8) ^ (row % 8). Rows past M re-read row M-1.
+  const T* asrc[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = (wave * CPW + i) * 8 + lane / 8;
+    asrc[i] = h + static_cast<int64_t>(min(r, M - 1)) * ldh + ((lane % 8) ^ (r & 7)) * (16 / sizeof(T));
+  }
+  // B: this lane's fragment of k-tile 0 of the wave's group (inactive waves re-read group 0)
+  const T* bsrc = E + static_cast<int64_t>(active ? grp : 0) * (D / 32) * 2 * kTileElems + lane * 8;
+
+  FT breg[kVNS][BF];
+  auto issue = [&](int kt, int slot) {
+    const int k = min(kt, KT - 1);
+    unsigned char* base = smem + slot * SBYTES;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) dma16(asrc[i] + static_cast<int64_t>(k) * KE, base + (wave * CPW + i) * 1024);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        breg[slot][s * 2 + n] = Frag<T>::load(bsrc + (static_cast<int64_t>(k * KS + s) * 2 + n) * kTileElems);
+  };
+
+  f32x4_t acc[16][2];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // all 16 row tiles are multiplied (rows past M repeat row M-1 and are not stored): no branches
+  // in the loop body, so the compiler's own waits for the E registers stay counted, not drained
+  auto compute = [&](int slot) {
+    const unsigned char* st = smem + slot * SBYTES;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const FT af = lds_frag<T>(st, m * 16 + fr, s, g4);
+        acc[m][0] = Frag<T>::mma(af, breg[slot][s * 2 + 0], acc[m][0]);
+        acc[m][1] = Frag<T>::mma(af, breg[slot][s * 2 + 1], acc[m][1]);
+      }
+    }
+  };
+  auto step = [&](int kt, int u) {
+    wait_vm_n<(kVNS - 2) * 8>();
+    __builtin_amdgcn_s_barrier();  // k-tile kt is in LDS for all waves; all are done with kt-1
+    issue(kt + kVNS - 1, (u + kVNS - 1) % kVNS);
+    compute(u);
+  };
+
+#pragma unroll
+  for (int u = 0; u < kVNS - 1; ++u) issue(u, u);
+  int k0 = 0;
+  for (; k0 + kVNS <= KT; k0 += kVNS) {
+#pragma unroll
+    for (int u = 0; u < kVNS; ++u) step(k0 + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < kVNS - 1; ++u)
+    if (k0 + u < KT) step(k0 + u, u);
+  wait_vm_n<0>();  // the trailing (never used) copies have landed before the workgroup retires
+  if (!active) return;
+  // lane holds C[row = m*16 + 4*g4 + i][col = 32 grp + n*16 + fr]
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m * 16 + g4 * 4 + i;
+      if (row < M) {
+        T* o = logits + static_cast<int64_t>(row) * ldo + grp * 32 + fr;
+        o[0] = from_f32<T>(acc[m][0][i]);
+        o[16] = from_f32<T>(acc[m][1][i]);
+      }
+    }
+}
+
+int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
+               hipStream_t s) {
+  if (M < 1 || M > kVRows) return fail(DG_ERR_UNSUPPORTED, "LM head: rows must be in [1, 256]");
+  const int ke = dtype == DG_BF16 ? 64 : 32;
+  if (D % ke != 0 || V % 32 != 0) return fail(DG_ERR_UNSUPPORTED, "LM head: d_model / vocab do not tile");
+  const int grid = (V / 32 + kVW - 1) / kVW;
+  ProfScope ps("lm_head", s);
+  if (dtype == DG_BF16)
+    vocab_gemm_kernel<bf16_t><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
+                                                         static_cast<const bf16_t*>(E), M, V, D,
+                                                         static_cast<bf16_t*>(logits), ldo);
+  else
+    vocab_gemm_kernel<float><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(h), ldh,
+                                                        static_cast<const float*>(E), M, V, D,
+                                                        static_cast<float*>(logits), ldo);
+  DG_LAUNCH_CHECK("vocab_gemm_kernel");
+  return DG_OK;
+}
+
+}  // namespace dg

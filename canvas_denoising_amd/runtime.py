@@ -83,9 +83,11 @@ class Model:
 
     # --- views
     def tensor(self, kind, layer=0, expert=0) -> torch.Tensor:
-        """Row-major [rows, cols] view of one weight tensor (routed-expert tensors are tiled: use load_weight)."""
-        if kind in (L.DG_W_EX_GATE, L.DG_W_EX_UP, L.DG_W_EX_DOWN):
-            raise ValueError("routed-expert weights are stored fragment-tiled; write them with load_weight")
+        """Row-major [rows, cols] view of one weight tensor (the embedding and the routed-expert tensors
+        are tiled: use load_weight)."""
+        if kind in (L.DG_W_EMBED, L.DG_W_EX_GATE, L.DG_W_EX_UP, L.DG_W_EX_DOWN):
+            raise ValueError("the embedding and routed-expert weights are stored fragment-tiled; "
+                             "write them with load_weight")
         off, r, c = L.dg_weight_tensor(self.desc, kind, layer, expert)
         es = 2 if self.desc.dtype == L.DG_BF16 else 4
         return self.weights[off:off + r * c * es].view(self.dtype).view(r, c)

@@ -212,11 +212,12 @@ size_t dg_weights_bytes(const dg_model_desc* desc);
 /* Byte offset and logical [rows x cols] shape of one tensor; layer / expert
  * are ignored where they do not apply. Q, K and V of a layer are adjacent
  * (one fused projection), as are gate and up of the shared expert. Every
- * tensor except the routed experts' is stored row-major at that offset.
- * The routed experts' matrices (DG_W_EX_*) are stored fragment-tiled so the
- * expert kernels stream contiguous memory: 16-row x 32-column tiles of 512
- * elements in which element 8 l + j is row l % 16, column 8 (l / 16) + j;
- * gate/up: tiles ordered [32-feature group][column tile][gate rows 0-15,
+ * tensor except the embedding and the routed experts' is stored row-major at
+ * that offset. DG_W_EMBED and the routed experts' matrices (DG_W_EX_*) are
+ * stored fragment-tiled so the LM head and expert kernels stream contiguous
+ * memory: 16-row x 32-column tiles of 512 elements in which element 8 l + j
+ * is row l % 16, column 8 (l / 16) + j; embedding: tiles ordered [32-row
+ * group][column tile][the group's 2 16-row blocks]; gate/up: tiles ordered [32-feature group][column tile][gate rows 0-15,
  * gate rows 16-31, up rows 0-15, up rows 16-31 of the group] (up alone when
  * ungated), down: [64-row group][column tile][the group's 4 16-row
  * blocks]. For DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the

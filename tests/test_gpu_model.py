@@ -272,6 +272,21 @@ def test_load_weight_reproduces_tiled_fill(libs, dtype, gated):
     torch.cuda.synchronize()
     assert torch.equal(model.weights[off_gu:off_gu + n_gu], ref_gu)
     assert torch.equal(model.weights[off_dn:off_dn + n_dn], ref_dn)
+    # the embedding (LM head weights) is tiled too; the transposed copy is rebuilt from it
+    off_e, _, _ = L.dg_weight_tensor(d, L.DG_W_EMBED)
+    off_et, _, _ = L.dg_weight_tensor(d, L.DG_W_EMBED_T)
+    n_e = d.vocab * d.d_model * es
+    ref_e = model.weights[off_e:off_e + n_e].clone()
+    ref_et = model.weights[off_et:off_et + n_e].clone()
+    model.weights[off_e:off_e + n_e].zero_()
+    model.weights[off_et:off_et + n_e].zero_()
+    model.load_weight(L.DG_W_EMBED, torch.from_numpy(W["embed"].astype(np.float32)).to(tdt).cuda().contiguous())
+    L.dg_prepare_weights(d, model.weights)
+    torch.cuda.synchronize()
+    assert torch.equal(model.weights[off_e:off_e + n_e], ref_e)
+    assert torch.equal(model.weights[off_et:off_et + n_e], ref_et)
+    et = ref_et.view(tdt).view(d.d_model, d.vocab).float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(et, W["embed"].T)
     # the tiled layout is not row-major: a row-major copy would differ
     assert not torch.equal(ref_dn.view(tdt).view(d.d_model, d.d_expert).cpu(), srcs[-1].cpu())
     with pytest.raises(ValueError):
