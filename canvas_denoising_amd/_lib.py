@@ -77,6 +77,7 @@ _SIGS = {
     "dg_workspace_size": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
     "dg_ctx_create": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P, _I64, _P, _SZ, ctypes.POINTER(_P)]),
     "dg_ctx_destroy": (ctypes.c_int, [_P]),
+    "dg_ctx_use_graphs": (ctypes.c_int, [_P, _I32]),
     "dg_kv_length": (_I64, [_P]),
     "dg_kv_set_length": (ctypes.c_int, [_P, _I64]),
     "dg_prefill_kv": (ctypes.c_int, [_P, _P, _I32, _P]),
@@ -236,6 +237,10 @@ def dg_ctx_create(desc, d_weights, d_kv, capacity, d_workspace, ws_bytes) -> int
 
 def dg_ctx_destroy(ctx):
     return _check("dg_ctx_destroy", lib.dg_ctx_destroy(ctx))
+
+
+def dg_ctx_use_graphs(ctx, on: bool):
+    return _check("dg_ctx_use_graphs", lib.dg_ctx_use_graphs(ctx, int(on)))
 
 
 def dg_kv_length(ctx) -> int:

@@ -75,9 +75,12 @@ constexpr int kStages = DG_ATT_NS;        // LDS ring depth (NS - 1 stages in fl
 #ifndef DG_ATT_NW
 #define DG_ATT_NW 8
 #endif
+#ifndef DG_ATT_QT
+#define DG_ATT_QT (8 / DG_ATT_NW)
+#endif
 constexpr int kNW = DG_ATT_NW;            // waves per workgroup (4 or 8)
-constexpr int kQT = 8 / kNW;              // 16-query tiles per wave
-constexpr int kWGRows = kNW * kQT * 16;   // query rows per workgroup (128)
+constexpr int kQT = DG_ATT_QT;            // 16-query tiles per wave (share every K/V fragment read)
+constexpr int kWGRows = kNW * kQT * 16;   // query rows per workgroup
 
 // 2^x with the hardware instruction (about 1 ulp; 2^-inf = 0). Arguments here are <= 0.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -57,33 +57,67 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 template <typename T>
 __device__ inline T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Combine a value across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48) with the
-// gfx950 row swaps: v_permlane16_swap / v_permlane32_swap given the same register twice return, in
-// one of their two results, the value of the partner row, so op(r0, r1) combines each pair (and,
-// op being commutative, every lane of the pair gets the same bits). VALU only, no LDS round trip.
+// Partner exchanges without the LDS permute network. Inside a 16-lane row, DPP moves: quad_perm
+// [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i <-> 7 - i within
+// 8: pairs the two quads of a half-row) and row_mirror (i <-> 15 - i: pairs the two halves). Across
+// rows, the gfx950 row swaps: v_permlane16_swap / v_permlane32_swap given the same register twice
+// return, in one of their two results, the value of the partner row (l ^ 16, l ^ 32). A symmetric
+// combine op(x, partner) at each of the six levels reduces the whole wave, and since op is
+// commutative every lane ends with the same bits.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+
+// partner value in the other 16-lane row of the 32-lane half (lane ^ 16) / other half (lane ^ 32)
+__device__ inline uint32_t xrow16_u32(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? a[0] : a[1];
+}
+__device__ inline uint32_t xrow32_u32(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? a[0] : a[1];
+}
+__device__ inline float xrow16_f32(float v) { return __uint_as_float(xrow16_u32(__float_as_uint(v))); }
+__device__ inline float xrow32_f32(float v) { return __uint_as_float(xrow32_u32(__float_as_uint(v))); }
+
+// Combine across the four 16-lane rows only (lanes l, l^16, l^32, l^48).
 __device__ inline float xrow_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = fmaxf(v, xrow16_f32(v));
+  return fmaxf(v, xrow32_f32(v));
 }
 __device__ inline float xrow_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  v += xrow16_f32(v);
+  return v + xrow32_f32(v);
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
-  return v;
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return xrow_sum(v);
 }
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return xrow_max(v);
+}
+
+__device__ inline int wave_min_i32(int v) {
+  v = min(v, static_cast<int>(dpp_u32<kDppXor1>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(dpp_u32<kDppXor2>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(dpp_u32<kDppHalfMirror>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(dpp_u32<kDppMirror>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(xrow16_u32(static_cast<uint32_t>(v))));
+  return min(v, static_cast<int>(xrow32_u32(static_cast<uint32_t>(v))));
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -102,6 +102,86 @@ __global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const float* __restri
   }
 }
 
+// Residual update fused with the next RMSNorm, one workgroup per row, the row in registers
+// (thread t holds float4 columns t, t + 256, ...; D % 4 == 0, D <= 1024 NV):
+//   x[m] += sum_z part[z][m]                                  (z = 0 .. splits-1, in order)
+//   x[m] += y[m] + sum_j slot_out[slot_of[m k + j]]           (when y != null; j in order)
+//   h[m]  = x[m] / sqrt(mean(x[m]^2) + eps)                   (fixed-order block sum)
+// The first line folds the split-K partials of a GEMM whose epilogue adds into x; the second is the
+// MoE combine (shared expert, then the token's gated routed outputs).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ x, const float* __restrict__ part,
+                                                            int splits, const float* __restrict__ y,
+                                                            const float* __restrict__ slot_out,
+                                                            const int32_t* __restrict__ slot_of, int k,
+                                                            T* __restrict__ h, int M, int D, float eps) {
+  __shared__ float sh[4];
+  const int tid = threadIdx.x;
+  const int m = blockIdx.x;
+  const int n4 = D / 4;
+  const int64_t plane = static_cast<int64_t>(M) * n4;  // float4s per partial
+  float4* xr = reinterpret_cast<float4*>(x + static_cast<int64_t>(m) * D);
+  const float4* p4 = reinterpret_cast<const float4*>(part);
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  const float4* s4 = reinterpret_cast<const float4*>(slot_out);
+  int slots[16];
+  if (y4)
+    for (int j = 0; j < k; ++j) slots[j] = slot_of[m * k + j];
+  float4 v[NV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + 256 * i;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < n4) {
+      float4 a = xr[c];
+      if (splits > 0) {
+        float4 t = p4[static_cast<int64_t>(m) * n4 + c];
+        for (int z = 1; z < splits; ++z) {
+          const float4 u = p4[z * plane + static_cast<int64_t>(m) * n4 + c];
+          t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        a.x += t.x; a.y += t.y; a.z += t.z; a.w += t.w;
+      }
+      if (y4) {
+        float4 t = y4[static_cast<int64_t>(m) * n4 + c];
+        for (int j = 0; j < k; ++j) {
+          const float4 u = s4[static_cast<int64_t>(slots[j]) * n4 + c];
+          t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        a.x += t.x; a.y += t.y; a.z += t.z; a.w += t.w;
+      }
+      xr[c] = a;
+      v[i] = a;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) sh[tid >> 6] = ss;
+  __syncthreads();
+  ss = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  T* hr = h + static_cast<int64_t>(m) * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + 256 * i;
+    if (c < n4) {
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(hr + 4 * c) =
+            make_uint2(pack_bf16x2(v[i].x * rs, v[i].y * rs), pack_bf16x2(v[i].z * rs, v[i].w * rs));
+      } else {
+        *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(v[i].x * rs, v[i].y * rs, v[i].z * rs, v[i].w * rs);
+      }
+    }
+  }
+}
+
 // P[m][v] = exp((l[m][v] - max_m) / T - lnZ_m): the sampler's tempered distribution,
 // rebuilt from its row statistics (max raw logit, ln of the tempered partition sum)
 template <typename T>
@@ -193,6 +273,23 @@ int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStre
     rmsnorm_kernel<float><<<M, kRowThreads, 0, s>>>(x, static_cast<float*>(h), D, eps);
   }
   DG_LAUNCH_CHECK("rmsnorm_kernel");
+  return DG_OK;
+}
+
+int residual_norm(float* x, const float* part, int splits, const float* y, const float* slot_out,
+                  const int32_t* slot_of, int k, void* h, int M, int D, float eps, int dtype, hipStream_t s,
+                  const char* name) {
+  constexpr int kNV = 3;
+  if (D % 4 != 0 || D > 1024 * kNV || k > 16)
+    return fail(DG_ERR_UNSUPPORTED, "residual_norm: d_model must be <= 3072 and a multiple of 4, top_k <= 16");
+  ProfScope ps(name, s);
+  if (dtype == DG_BF16)
+    residual_norm_kernel<bf16_t, kNV><<<M, 256, 0, s>>>(x, part, splits, y, slot_out, slot_of, k,
+                                                       static_cast<bf16_t*>(h), M, D, eps);
+  else
+    residual_norm_kernel<float, kNV><<<M, 256, 0, s>>>(x, part, splits, y, slot_out, slot_of, k,
+                                                      static_cast<float*>(h), M, D, eps);
+  DG_LAUNCH_CHECK("residual_norm_kernel");
   return DG_OK;
 }
 

@@ -33,6 +33,10 @@ struct GemmArgs {
   void* vcache = nullptr;
   // split-K scratch: splits * M * N floats
   float* part = nullptr;
+  // leave split-K partials unreduced (the caller folds them into a row kernel); gemm() then
+  // reports the split count through *splits_out
+  bool defer_reduce = false;
+  int* splits_out = nullptr;
 };
 
 // dtype: DG_BF16 / DG_F32. splits > 1 requires g.part and an epilogue other than GEGLU.

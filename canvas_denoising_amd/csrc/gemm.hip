@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
 
   // ---- epilogue
   const int rbase = m0 + wm * C::WM + (lane >> 4) * 4;
-  if (splits > 1) {
+  if (splits > 1) {  // partial sums [z][row][B row] (gate j and up j of a paired GEMM at j, pair_f + j)
     float* part = g.part + static_cast<int64_t>(z) * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = rbase + i * 16 + r;
-          const int col = nt * BN + wn * C::WN + j * 16 + fr;
+          const int t = wn * C::WN + j * 16 + fr;
+          const int col = paired ? brow(t) : nt * BN + t;
           if (row < g.M && col < g.N) part[static_cast<int64_t>(row) * g.N + col] = acc[i][j][r];
         }
     return;
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
 
   // ---- epilogue (same mapping as gemm_kernel)
   const int rbase = m0 + wm * WM + (lane >> 4) * 4;
-  if (splits > 1) {
+  if (splits > 1) {  // partial sums [z][row][B row], as gemm_kernel
     float* part = g.part + static_cast<int64_t>(z) * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -369,7 +370,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = rbase + i * 16 + r;
-          const int col = nt * BN + wn * WN + j * 16 + fr;
+          const int t = wn * WN + j * 16 + fr;
+          const int col = paired ? brow(t) : nt * BN + t;
           if (row < g.M && col < g.N) part[static_cast<int64_t>(row) * g.N + col] = acc[i][j][r];
         }
     return;
@@ -402,10 +404,26 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
       }
 }
 
+// Sum the split-K partials in split order and apply the epilogue; a paired (gated GeLU) GEMM
+// combines the gate sum at column j with the up sum at column pair_f + j.
 template <typename T>
 __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
   const int64_t n = static_cast<int64_t>(g.M) * g.N;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  if (g.epi == EPI_GEGLU) {
+    const int64_t nf = static_cast<int64_t>(g.M) * g.pair_f;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < nf; e += stride) {
+      const int row = static_cast<int>(e / g.pair_f), j = static_cast<int>(e - static_cast<int64_t>(row) * g.pair_f);
+      const int64_t gi = static_cast<int64_t>(row) * g.N + j;
+      float gs = 0.f, us = 0.f;
+      for (int z = 0; z < splits; ++z) {
+        gs += g.part[z * n + gi];
+        us += g.part[z * n + gi + g.pair_f];
+      }
+      static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + j] = from_f32<T>(gelu_erf(gs) * us);
+    }
+    return;
+  }
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
     float v = 0.f;
     for (int z = 0; z < splits; ++z) v += g.part[z * n + e];
@@ -417,16 +435,20 @@ __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
 // ------------------------------------------------------------------- host
 struct TileChoice { int bm, bn; };
 
-static TileChoice pick_tile(int M, int N, bool paired) {
+// 128 x 128 tiles halve the operand traffic of 64 x 64 ones; they pay where the grid stays large
+// (many column tiles) or K is long enough that split-K partials are small against the operands
+// (the self-conditioning product over the vocabulary). Elsewhere, with a 256-row canvas, 64 x 64
+// tiles give enough workgroups without splitting.
+static TileChoice pick_tile(int M, int N, int K) {
   const int64_t t128 = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
-  if (!paired && M > 64 && t128 >= 512) return {128, 128};
+  if (M > 64 && N >= 128 && (t128 >= 512 || K >= 16384)) return {128, 128};
   return {64, 64};
 }
 
 int gemm_pick_splits(int M, int N, int K, int dtype, int64_t part_capacity, bool allow_split) {
   if (!allow_split) return 1;
   const int bk = dtype == DG_BF16 ? 64 : 32;
-  const TileChoice tc = pick_tile(M, N, false);
+  const TileChoice tc = pick_tile(M, N, K);
   const int64_t tiles = static_cast<int64_t>((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
   int s = 1;
   const int ktiles = K / bk;
@@ -450,8 +472,7 @@ static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name
   const bool paired = g.epi == EPI_GEGLU;
   const int bk = 128 / static_cast<int>(sizeof(T));
   if (g.K % bk != 0) return fail(DG_ERR_UNSUPPORTED, std::string(name) + ": K must be a multiple of the k-tile");
-  if (paired && splits != 1) return fail(DG_ERR_INVALID, "gated GeLU GEMM cannot split K");
-  const TileChoice tc = pick_tile(g.M, g.N, paired);
+  const TileChoice tc = pick_tile(g.M, g.N, g.K);
   if (paired && (g.pair_f % (tc.bn / 2) != 0 || g.N != 2 * g.pair_f))
     return fail(DG_ERR_UNSUPPORTED, std::string(name) + ": gated width must be a multiple of 32");
   const int ktiles = g.K / bk;
@@ -474,7 +495,8 @@ static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name
   }
   DG_LAUNCH_CHECK("gemm_dma_kernel");
   if (rc != DG_OK) return rc;
-  if (splits > 1) {
+  if (g.splits_out) *g.splits_out = splits;
+  if (splits > 1 && !g.defer_reduce) {
     ProfScope ps("splitk_reduce", s);
     const int64_t n = static_cast<int64_t>(g.M) * g.N;
     const int grid = static_cast<int>(std::min<int64_t>((n + 255) / 256, 4096));

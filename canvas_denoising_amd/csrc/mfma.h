@@ -22,9 +22,16 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 template <typename T> struct Frag;
 
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
 template <> struct Frag<bf16_t> {
   using type = bf16x8_t;
   __device__ static inline type load(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+  // streamed-once operands (weights): a nontemporal load
+  __device__ static inline type load_nt(const bf16_t* p) {
+    const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
   __device__ static inline type zero() {
     type z;
 #pragma unroll
@@ -39,6 +46,7 @@ template <> struct Frag<bf16_t> {
 template <> struct Frag<float> {
   using type = f32x8_t;
   __device__ static inline type load(const float* p) { return *reinterpret_cast<const f32x8_t*>(p); }
+  __device__ static inline type load_nt(const float* p) { return load(p); }
   __device__ static inline type zero() {
     type z;
 #pragma unroll

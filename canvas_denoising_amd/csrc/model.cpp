@@ -31,6 +31,9 @@ namespace dg {
 int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M, int D, int V, int dtype,
           hipStream_t s);
 int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s);
+int residual_norm(float* x, const float* part, int splits, const float* y, const float* slot_out,
+                  const int32_t* slot_of, int k, void* h, int M, int D, float eps, int dtype, hipStream_t s,
+                  const char* name);
 int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
           hipStream_t s);
 int transpose(const void* in, int64_t R, int64_t C, int gr, void* out, int dtype, hipStream_t s);
@@ -178,6 +181,15 @@ int check_desc(const dg_model_desc* d) {
   return DG_OK;
 }
 
+// a captured denoising step body and what it was captured for
+struct StepGraph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  const int32_t* canvas = nullptr;
+  const void* logits = nullptr;
+  int64_t len = -1;
+};
+
 // ----------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
@@ -246,6 +258,10 @@ struct dg_ctx {
   // second stream: the shared expert runs beside the routed experts (fork / join events)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // graph replay of the denoising step body ([0]: without self-conditioning, [1]: with)
+  hipStream_t cap_stream = nullptr;
+  bool use_graphs = true;
+  dg::StepGraph graphs[2];
 };
 
 namespace dg {
@@ -268,14 +284,24 @@ static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool
   return gemm(g, c->d.dtype, splits, s, name);
 }
 
-// one layer over M rows of the residual stream x placed at cache positions pos0 ..
-// pos0+M-1; `kv_only` stops after the K/V projection (last encoder layer)
+// row kernels can hold a residual row in registers up to this width (residual_norm)
+#ifndef DG_FUSED_NORM
+#define DG_FUSED_NORM 1
+#endif
+static bool fused_norm_ok(const dg_model_desc& d) {
+  return DG_FUSED_NORM && d.d_model % 4 == 0 && d.d_model <= 3072;
+}
+
+// One layer over M rows of the residual stream x placed at cache positions pos0 .. pos0+M-1.
+// On entry h = RMSNorm(x); on exit x is the layer's output and h = RMSNorm(x) again (the next
+// layer's input norm, or the final norm before the LM head): every residual update is fused with
+// the norm that follows it. `kv_only` stops after the K/V projection (last encoder layer).
 static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causal, bool kv_only, hipStream_t s) {
   const dg_model_desc& d = c->d;
   const WsLayout& w = c->wsl;
   const int D = d.d_model, hd = d.head_dim, QW = d.n_q_heads * hd;
+  const bool fused = fused_norm_ok(d);
   void* h = wsp<void>(c, w.h);
-  DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
   {
     GemmArgs g;
     g.A = h; g.lda = D;
@@ -300,9 +326,17 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     g.B = wp(c, c->wl.o[l]); g.ldb = QW;
     g.M = M; g.N = D; g.K = QW;
     g.epi = EPI_ADD_F32; g.out = x; g.ldo = D;
+    int splits = 1;
+    g.defer_reduce = fused;
+    g.splits_out = &splits;
     DG_TRY(run_gemm(c, g, s, "o_proj", true));
+    // x += (sum of the split partials, if the GEMM left them); h = RMSNorm(x)
+    if (fused)
+      DG_TRY(residual_norm(x, wsp<float>(c, w.gpart), splits > 1 ? splits : 0, nullptr, nullptr, nullptr, 0, h, M,
+                           D, d.rms_eps, d.dtype, s, splits > 1 ? "o_reduce_norm" : "rmsnorm"));
+    else
+      DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
   }
-  DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
   // fork: the shared expert (h -> y_sh) runs on the second stream while the router and the routed
   // experts run here; both only read h, and each stream has its own split-K scratch
   DG_HIP(hipEventRecord(c->ev_fork, s));
@@ -339,10 +373,14 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
   DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
                      wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, s));
-  // join, then x += shared + sum of the token's gated expert outputs (fixed order)
+  // join, then x += shared + sum of the token's gated expert outputs (fixed order); h = RMSNorm(x)
   DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
-  return moe_combine(x, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of), M, D,
-                     d.top_k, s);
+  if (fused)
+    return residual_norm(x, nullptr, 0, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of),
+                         d.top_k, h, M, D, d.rms_eps, d.dtype, s, "combine_norm");
+  DG_TRY(moe_combine(x, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of), M, D,
+                     d.top_k, s));
+  return rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s);
 }
 
 static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
@@ -351,6 +389,7 @@ static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
   for (int c0 = 0; c0 < n; c0 += d.canvas) {
     const int M = std::min(d.canvas, n - c0);
     DG_TRY(embed(wp(c, c->wl.embed), ids + c0, nullptr, x, M, d.d_model, d.vocab, d.dtype, s));
+    DG_TRY(rmsnorm(x, wsp<void>(c, c->wsl.h), M, d.d_model, d.rms_eps, d.dtype, s));
     for (int l = 0; l < d.n_layers; ++l)
       DG_TRY(layer_forward(c, l, x, M, static_cast<int>(c->len), true, l == d.n_layers - 1, s));
     c->len += M;
@@ -358,15 +397,16 @@ static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
   return DG_OK;
 }
 
-static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats, float prev_t,
-                   void* logits, hipStream_t s) {
+// Everything of a denoising step after the tempered probabilities: self-conditioning from P (when
+// sc_on), the embedding, the layers and the LM head. Its launches depend only on the pointers,
+// sc_on and the committed KV length, so it can be captured once and replayed.
+static int denoise_body(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logits, hipStream_t s) {
   const dg_model_desc& d = c->d;
   const WsLayout& w = c->wsl;
   const int C = d.canvas, D = d.d_model;
   float* x = wsp<float>(c, w.x);
   const float* sc = nullptr;
-  if (prev_logits != nullptr) {
-    DG_TRY(probs(prev_logits, prev_stats, prev_t, C, d.vocab, wsp<void>(c, w.P), d.dtype, s));
+  if (sc_on) {
     {
       GemmArgs g;  // u = p E  (A = p [C x V], B = E^T [D x V])
       g.A = wsp<void>(c, w.P); g.lda = d.vocab;
@@ -393,12 +433,60 @@ static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, co
     }
     sc = wsp<float>(c, w.sc);
   }
-  DG_TRY(embed(wp(c, c->wl.embed), canvas, sc, x, C, D, d.vocab, d.dtype, s));
-  for (int l = 0; l < d.n_layers; ++l)
-    DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), false, false, s));
   void* h = wsp<void>(c, w.h);
+  DG_TRY(embed(wp(c, c->wl.embed), canvas, sc, x, C, D, d.vocab, d.dtype, s));
   DG_TRY(rmsnorm(x, h, C, D, d.rms_eps, d.dtype, s));
+  for (int l = 0; l < d.n_layers; ++l)  // each layer leaves h = RMSNorm(its output)
+    DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), false, false, s));
   return vocab_gemm(h, D, wp(c, c->wl.embed), C, d.vocab, D, logits, d.vocab, d.dtype, s);
+}
+
+static void drop_graph(StepGraph& g) {
+  if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  if (g.graph) (void)hipGraphDestroy(g.graph);
+  g = StepGraph{};
+}
+
+// Replay of denoise_body as a HIP graph: ~500 dependent launches per step cost launch gaps that
+// a graph removes. Captured on the context's own stream (the caller's may be the legacy default
+// stream, which cannot capture; the second stream joins through the fork event), launched on s.
+// While per-kernel profiling is on, steps run eagerly so every launch records its events.
+static int denoise_graphed(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logits, hipStream_t s) {
+  if (prof_on() || !c->use_graphs) return denoise_body(c, canvas, sc_on, logits, s);
+  StepGraph& g = c->graphs[sc_on ? 1 : 0];
+  if (!(g.exec && g.canvas == canvas && g.logits == logits && g.len == c->len)) {
+    drop_graph(g);
+    DG_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+    const int rc = denoise_body(c, canvas, sc_on, logits, c->cap_stream);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->cap_stream, &graph);
+    if (rc != DG_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return hip_check(e, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (ie != hipSuccess) {
+      (void)hipGraphDestroy(graph);
+      return hip_check(ie, "hipGraphInstantiate");
+    }
+    g.graph = graph;
+    g.exec = exec;
+    g.canvas = canvas;
+    g.logits = logits;
+    g.len = c->len;
+  }
+  DG_HIP(hipGraphLaunch(g.exec, s));
+  return DG_OK;
+}
+
+static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats, float prev_t,
+                   void* logits, hipStream_t s) {
+  const dg_model_desc& d = c->d;
+  if (prev_logits != nullptr)
+    DG_TRY(probs(prev_logits, prev_stats, prev_t, d.canvas, d.vocab, wsp<void>(c, c->wsl.P), d.dtype, s));
+  return denoise_graphed(c, canvas, prev_logits != nullptr, logits, s);
 }
 
 static int check_ctx(const dg_ctx* c) {
@@ -534,6 +622,7 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
   c->wl = weight_layout(*desc);
   c->wsl = wl;
   if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
     dg_ctx_destroy(c);
@@ -545,12 +634,25 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
 
 int dg_ctx_destroy(dg_ctx* ctx) {
   if (ctx) {
+    (void)hipDeviceSynchronize();
+    for (StepGraph& g : ctx->graphs) drop_graph(g);
+    if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
     if (ctx->aux) (void)hipStreamSynchronize(ctx->aux);
     if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
   }
   delete ctx;
+  return DG_OK;
+}
+
+int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on) {
+  DG_TRY(check_ctx(ctx));
+  ctx->use_graphs = on != 0;
+  if (!ctx->use_graphs) {
+    DG_HIP(hipDeviceSynchronize());
+    for (StepGraph& g : ctx->graphs) drop_graph(g);
+  }
   return DG_OK;
 }
 
@@ -595,7 +697,9 @@ int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32
   if (!d_x) return fail(DG_ERR_INVALID, "d_x is NULL");
   if (rows < 1 || rows > ctx->d.canvas) return fail(DG_ERR_SHAPE, "rows must be in [1, canvas]");
   if (ctx->len + rows > ctx->cap) return fail(DG_ERR_CAPACITY, "rows do not fit in the KV cache");
-  return layer_forward(ctx, layer, d_x, rows, static_cast<int>(ctx->len), causal != 0, false, as_stream(stream));
+  hipStream_t s = as_stream(stream);
+  DG_TRY(rmsnorm(d_x, wsp<void>(ctx, ctx->wsl.h), rows, ctx->d.d_model, ctx->d.rms_eps, ctx->d.dtype, s));
+  return layer_forward(ctx, layer, d_x, rows, static_cast<int>(ctx->len), causal != 0, false, s);
 }
 
 int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d_logits, int32_t* d_block_out,

@@ -38,6 +38,11 @@ namespace dg {
 constexpr int kMaxTokens = 256;  // rows per routing call
 constexpr int kMaskWords = kMaxTokens / 32;
 
+// keep the larger value, the lower expert index on ties (exact, so every lane agrees)
+__device__ inline void argmax_step(float& bv, int& be, float ov, int oe) {
+  if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+}
+
 // grid ceil(M / 4), 256 threads: wave w of the workgroup routes row 4 * blockIdx.x + w
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int M, int E, int k,
                                                    int renorm, int32_t* __restrict__ sel,
@@ -71,12 +76,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       const int e = lane + 64 * i;
       if (e < E && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = shfl_xor(bv, m);
-      const int oe = shfl_xor(be, m);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
+    argmax_step(bv, be, dpp_f32<kDppXor1>(bv), static_cast<int>(dpp_u32<kDppXor1>(static_cast<uint32_t>(be))));
+    argmax_step(bv, be, dpp_f32<kDppXor2>(bv), static_cast<int>(dpp_u32<kDppXor2>(static_cast<uint32_t>(be))));
+    argmax_step(bv, be, dpp_f32<kDppHalfMirror>(bv),
+                static_cast<int>(dpp_u32<kDppHalfMirror>(static_cast<uint32_t>(be))));
+    argmax_step(bv, be, dpp_f32<kDppMirror>(bv), static_cast<int>(dpp_u32<kDppMirror>(static_cast<uint32_t>(be))));
+    argmax_step(bv, be, xrow16_f32(bv), static_cast<int>(xrow16_u32(static_cast<uint32_t>(be))));
+    argmax_step(bv, be, xrow32_f32(bv), static_cast<int>(xrow32_u32(static_cast<uint32_t>(be))));
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (lane + 64 * i == be) v[i] = -INFINITY;
@@ -162,6 +168,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 #define DG_EXP_NS_DN 2
 #endif
 constexpr int kExpWaves = 4;
+#ifndef DG_EXP_NT
+#define DG_EXP_NT 0
+#endif
+constexpr bool kExpNT = DG_EXP_NT;  // nontemporal weight loads
 
 // Block b of an expert grid -> (expert, unit within the expert). Workgroups
 // of one expert read the same token rows, so with E a multiple of 8 they are
@@ -214,7 +224,10 @@ struct SplitStream {
       for (int u = 0; u < KSP; ++u) {
         const int kt = min(base + u, KT - 1);
 #pragma unroll
-        for (int g = 0; g < G; ++g) S.b[u][g] = Fr::load(bt + (static_cast<int64_t>(kt) * G + g) * kTileElems);
+        for (int g = 0; g < G; ++g) {
+          const T* bp = bt + (static_cast<int64_t>(kt) * G + g) * kTileElems;
+          S.b[u][g] = kExpNT ? Fr::load_nt(bp) : Fr::load(bp);
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) S.a[u][t] = Fr::load(arow[t] + kt * 32);
       }

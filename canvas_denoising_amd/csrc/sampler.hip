@@ -20,9 +20,9 @@
 // chunk's, re-reads that one batch to find the lowest index holding it.
 //
 // A second, single-workgroup kernel merges each row's records in a fixed
-// tree order (one wave per row, one record per lane), applies the accept /
-// Philox re-noise rule, and reduces the canvas mean entropy and the
-// stability test in a fixed order into the stop state. (Folding this into
+// order (a quad of threads per row), applies the accept / Philox re-noise
+// rule, and reduces the canvas mean entropy and the stability test in a
+// fixed order into the stop state. (Folding this into
 // the first kernel with a last-workgroup atomic costs a cache write-back and
 // invalidate per workgroup at agent scope, far more than a second launch.)
 // Results are bitwise reproducible.
@@ -57,13 +57,28 @@ __device__ inline void rec_merge(Rec& x, const Rec& y, float c) {
   x.idx = idx;
 }
 
-__device__ inline Rec rec_shfl_xor(const Rec& r, int mask) {
-  Rec o;
-  o.m = shfl_xor(r.m, mask);
-  o.z = shfl_xor(r.z, mask);
-  o.a = shfl_xor(r.a, mask);
-  o.idx = shfl_xor(r.idx, mask);
-  return o;
+template <int CTRL>
+__device__ inline Rec rec_dpp(const Rec& r) {
+  return Rec{dpp_f32<CTRL>(r.m), dpp_f32<CTRL>(r.z), dpp_f32<CTRL>(r.a),
+             static_cast<int>(dpp_u32<CTRL>(static_cast<uint32_t>(r.idx)))};
+}
+__device__ inline Rec rec_xrow16(const Rec& r) {
+  return Rec{xrow16_f32(r.m), xrow16_f32(r.z), xrow16_f32(r.a),
+             static_cast<int>(xrow16_u32(static_cast<uint32_t>(r.idx)))};
+}
+__device__ inline Rec rec_xrow32(const Rec& r) {
+  return Rec{xrow32_f32(r.m), xrow32_f32(r.z), xrow32_f32(r.a),
+             static_cast<int>(xrow32_u32(static_cast<uint32_t>(r.idx)))};
+}
+
+// Merge the records of all 64 lanes: six partner levels (dg_common.h), a fixed order per lane.
+__device__ inline void rec_wave_merge(Rec& w, float c) {
+  rec_merge(w, rec_dpp<kDppXor1>(w), c);
+  rec_merge(w, rec_dpp<kDppXor2>(w), c);
+  rec_merge(w, rec_dpp<kDppHalfMirror>(w), c);
+  rec_merge(w, rec_dpp<kDppMirror>(w), c);
+  rec_merge(w, rec_xrow16(w), c);
+  rec_merge(w, rec_xrow32(w), c);
 }
 
 constexpr int kSampThreads = 256;
@@ -74,11 +89,18 @@ constexpr int kMaxSplits = 64;
 
 // raw storage of one thread's batch: kUnroll groups of 8 elements
 template <typename T> struct Raw;
+// The logits are read once: nontemporal loads keep them from displacing reused lines in the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <> struct Raw<bf16_t> {
   uint4 q[kUnroll];
   __device__ inline void load(const bf16_t* p) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = *reinterpret_cast<const uint4*>(p + u * kSampThreads * kVec);
+    for (int u = 0; u < kUnroll; ++u) q[u] = load_nt(p + u * kSampThreads * kVec);
   }
   __device__ inline void unpack(float* v) const {
 #pragma unroll
@@ -218,11 +240,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
     }
     // wave / workgroup merge of (m, z, a) in a fixed order
     Rec w = r;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const Rec o = rec_shfl_xor(w, m);
-      rec_merge(w, o, c);
-    }
+    rec_wave_merge(w, c);
     if (lane == 0) sh[wave] = w;
     __syncthreads();
     Rec tot = sh[0];
@@ -243,8 +261,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
         my_idx = tail_idx;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) my_idx = min(my_idx, shfl_xor(my_idx, m));
+    my_idx = wave_min_i32(my_idx);
     if (lane == 0) sh_idx[wave] = my_idx;
     __syncthreads();
     if (tid == 0) {
@@ -260,11 +277,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
       float v[1] = {load1<T>(p + e)};
       if (fold<1>(v, c, r)) r.idx = static_cast<int>(e);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const Rec o = rec_shfl_xor(r, m);
-      rec_merge(r, o, c);
-    }
+    rec_wave_merge(r, c);
     if (lane == 0) sh[wave] = r;
     __syncthreads();
     if (tid == 0) {
@@ -278,48 +291,39 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
 
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / 64;
-constexpr int kFinRows = 4;  // rows per wave per pass (their record loads are issued together)
+constexpr int kFinParts = 4;                     // threads per row (one DPP quad)
+constexpr int kFinRecs = kMaxSplits / kFinParts;  // records per thread at most
 
-// One workgroup. Phase A: wave w merges the split records of rows w, w + 16, ... (lane s loads
-// record s; fixed butterfly) into LDS. Phase B: thread t finalises row t (accept, Philox re-noise,
-// outputs). Then the canvas mean entropy, the stability test and the stop rule are reduced in a
-// fixed order.
+// One workgroup; a quad of threads per row, 256 rows per pass. Thread part p of a row loads the
+// records p, p + 4, ... (all loads issued before any merge: one memory round trip) and merges them
+// in increasing order; the quad then merges its four partial records (lane ^ 1, then lane ^ 2) and
+// part 0 finalises the row (accept, Philox re-noise, outputs). The canvas mean entropy, the
+// stability test and the stop rule are reduced in a fixed order at the end.
 __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs g) {
   if (g.stop->stopped) return;
-  __shared__ Rec merged[kFinThreads];
   __shared__ float shs[kFinWaves];
   __shared__ int shq[kFinWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = tid % kFinParts;
   const float c = g.c;
   float hs = 0.f;
   int same = 1;
-  for (int base = 0; base < g.rows; base += kFinThreads) {
-    const int nrows = min(kFinThreads, g.rows - base);
-    for (int r0 = wave; r0 < nrows; r0 += kFinWaves * kFinRows) {
-      Rec rr[kFinRows];
+  for (int base = 0; base < g.rows; base += kFinThreads / kFinParts) {
+    const int row = base + tid / kFinParts;
+    const bool valid = row < g.rows;
+    Rec buf[kFinRecs];
 #pragma unroll
-      for (int j = 0; j < kFinRows; ++j) {
-        const int row = r0 + j * kFinWaves;
-        rr[j] = Rec{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
-        if (row < nrows && lane < g.splits) rr[j] = g.recs[static_cast<int64_t>(base + row) * g.splits + lane];
-      }
-#pragma unroll
-      for (int j = 0; j < kFinRows; ++j)
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-          const Rec o = rec_shfl_xor(rr[j], m);
-          rec_merge(rr[j], o, c);
-        }
-      if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < kFinRows; ++j)
-          if (r0 + j * kFinWaves < nrows) merged[r0 + j * kFinWaves] = rr[j];
-      }
+    for (int i = 0; i < kFinRecs; ++i) {
+      const int sp = part + kFinParts * i;
+      buf[i] = Rec{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
+      if (valid && sp < g.splits) buf[i] = g.recs[static_cast<int64_t>(row) * g.splits + sp];
     }
-    __syncthreads();
-    if (tid < nrows) {
-      const int row = base + tid;
-      const Rec r = merged[tid];
+    Rec r = buf[0];
+#pragma unroll
+    for (int i = 1; i < kFinRecs; ++i) rec_merge(r, buf[i], c);
+    rec_merge(r, rec_dpp<kDppXor1>(r), c);
+    rec_merge(r, rec_dpp<kDppXor2>(r), c);
+    if (valid && part == 0) {
       // The fold evaluates u = fma(l, c, -round(m c)): every u of a chunk carries the residual
       // delta = m c - round(m c); it cancels in H but not in ln Z.
       const float mc = r.m * c;
@@ -341,11 +345,9 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
       }
       hs += H;
     }
-    __syncthreads();
   }
   hs = wave_sum(hs);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) same &= shfl_xor(same, m);
+  same = wave_min_i32(same);
   if (lane == 0) { shs[wave] = hs; shq[wave] = same; }
   __syncthreads();
   if (tid == 0) {

@@ -248,13 +248,22 @@ size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity);
 
 /* Create a context over caller-owned weights, KV cache and workspace (none is
  * copied; all must outlive the context). Zero-fills the workspace and the KV
- * cache (blocking, on the default stream). capacity = KV positions. The committed length
- * starts at 0. Limits: canvas <= 256, head_dim 64 or 128 (bf16), d_model,
- * head dims and FFN widths multiples of 64 (bf16) / 32 (fp32), n_experts <=
- * 256, top_k <= 16. */
+ * cache (blocking, on the default stream) and creates two streams and two
+ * events of its own (default priority). capacity = KV positions, a multiple
+ * of 32. The committed length starts at 0. Limits: canvas <= 256, head_dim
+ * 64 or 128 (bf16), d_model, head dims, FFN widths and vocab multiples of
+ * 64, n_experts <= 256, top_k <= 16. */
 int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_t capacity,
                   void* d_workspace, size_t ws_bytes, dg_ctx** out);
-int dg_ctx_destroy(dg_ctx* ctx);  /* frees the host descriptor only */
+/* Waits for the device, then frees the context's own stream, events and
+ * graphs (never the caller's buffers). */
+int dg_ctx_destroy(dg_ctx* ctx);
+/* Graph replay of the denoising step (default on): the launches of a step
+ * after the tempered probabilities are captured once per (canvas, logits
+ * pointers, self-conditioning on/off, committed KV length) into a HIP graph
+ * and replayed; any change re-captures. Off (0): every launch is issued
+ * directly. Steps also run directly while dg_profile_enable is on. */
+int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
 int64_t dg_kv_length(const dg_ctx* ctx);
 /* Declare the first `length` cache positions valid without computing them
  * (for caches filled by the caller). */
@@ -311,7 +320,8 @@ int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d
 /* Device addresses of context buffers, for inspection by tests and tools. */
 enum {
   DG_BUF_X = 0,             /* float [canvas x d_model] residual stream */
-  DG_BUF_H = 1,             /* dtype [canvas x d_model] normalised activations */
+  DG_BUF_H = 1,             /* dtype [canvas x d_model] RMSNorm of the residual
+                               stream (after a layer: of the layer's output) */
   DG_BUF_ROUTER_LOGITS = 2, /* float [canvas x n_experts] (last layer run) */
   DG_BUF_SEL = 3,           /* int32 [canvas x top_k] selected experts */
   DG_BUF_GATE = 4,          /* float [canvas x top_k] gates */
