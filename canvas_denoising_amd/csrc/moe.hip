@@ -172,6 +172,10 @@ constexpr int kExpWaves = 4;
 #define DG_EXP_NT 0
 #endif
 constexpr bool kExpNT = DG_EXP_NT;  // nontemporal weight loads
+#ifndef DG_EXP_ROT
+#define DG_EXP_ROT 0
+#endif
+constexpr bool kExpRot = DG_EXP_ROT;  // per-workgroup rotation of the stage order
 
 // Block b of an expert grid -> (expert, unit within the expert). Workgroups
 // of one expert read the same token rows, so with E a multiple of 8 they are
@@ -210,7 +214,9 @@ struct SplitStream {
 
   // bt: this lane's fragment in k-tile 0 of the group; arow[t]: this lane's
   // token row of tile t at column 8 * (lane / 16); KT: k-tiles of 32.
-  __device__ inline void run(const T* bt, const T* const* arow, int KT, int wave) {
+  // rot: the stream starts at stage rot and wraps (workgroups running side by side then read
+  // different offsets of their groups instead of marching through the same address bits together)
+  __device__ inline void run(const T* bt, const T* const* arow, int KT, int wave, int rot) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -218,8 +224,10 @@ struct SplitStream {
     constexpr int kPer = kExpWaves * KSP;
     const int nst = (KT + kPer - 1) / kPer;
     const int first = wave * KSP;
+    rot %= nst;
+    auto rs = [&](int s) { const int r = s + rot; return r >= nst ? r - nst : r; };
     auto load = [&](Stage& S, int s) {
-      const int base = min(s, nst - 1) * kPer + first;
+      const int base = rs(min(s, nst - 1)) * kPer + first;
 #pragma unroll
       for (int u = 0; u < KSP; ++u) {
         const int kt = min(base + u, KT - 1);
@@ -233,9 +241,10 @@ struct SplitStream {
       }
     };
     auto compute = [&](const Stage& S, int s) {
+      const int base = rs(s) * kPer + first;
 #pragma unroll
       for (int u = 0; u < KSP; ++u)
-        if (s * kPer + first + u < KT) {
+        if (base + u < KT) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -293,7 +302,7 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, 
     arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
   }
   SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU> sp;
-  sp.run(bt, arow, KT, wave);
+  sp.run(bt, arow, KT, wave, kExpRot ? blockIdx.x : 0);
   sp.reduce(red, wave, lane);
   if (wave == 0) {
 #pragma unroll
@@ -348,7 +357,7 @@ __device__ inline void down_pass(const T* act, const T* bt, int F, int D, int be
     arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
   }
   SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN> sp;
-  sp.run(bt, arow, F / 32, wave);
+  sp.run(bt, arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
   sp.reduce(red, wave, lane);
   if (wave == 0) {
 #pragma unroll
@@ -446,19 +455,23 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
   const int per_dn = D / (16 * kDownGroup);
   const dim3 g1(E * per_gu), g2(E * per_dn);
   {
-    ProfScope ps("expert_gateup", s);
+    ProfScope ps("expert_gateup", s, true);
     if (dtype == DG_BF16) {
       const bf16_t* hh = static_cast<const bf16_t*>(h);
       const bf16_t* w = static_cast<const bf16_t*>(w_gu);
       bf16_t* a = static_cast<bf16_t*>(act);
-      if (gated) expert_gateup_kernel<bf16_t, true><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
-      else expert_gateup_kernel<bf16_t, false><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
+      if (gated) launch_timed(ps, expert_gateup_kernel<bf16_t, true>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+                          offsets, perm, a);
+      else launch_timed(ps, expert_gateup_kernel<bf16_t, false>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+                          offsets, perm, a);
     } else {
       const float* hh = static_cast<const float*>(h);
       const float* w = static_cast<const float*>(w_gu);
       float* a = static_cast<float*>(act);
-      if (gated) expert_gateup_kernel<float, true><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
-      else expert_gateup_kernel<float, false><<<g1, 256, 0, s>>>(hh, ldh, w, E, F, D, per_gu, offsets, perm, a);
+      if (gated) launch_timed(ps, expert_gateup_kernel<float, true>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+                          offsets, perm, a);
+      else launch_timed(ps, expert_gateup_kernel<float, false>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+                          offsets, perm, a);
     }
   }
   DG_LAUNCH_CHECK("expert_gateup_kernel");

@@ -428,14 +428,15 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
   g.recs = static_cast<Rec*>(ws);
   dim3 grid(static_cast<unsigned>(p.splits), static_cast<unsigned>(rows));
   {
-    ProfScope ps("sample_partial", stream);
+    ProfScope ps("sample_partial", stream, true);
     const bool vec = vocab % kVec == 0;
+    const dim3 block(kSampThreads);
     if (dtype == DG_BF16) {
-      if (vec) sample_kernel<bf16_t, true><<<grid, kSampThreads, 0, stream>>>(g);
-      else sample_kernel<bf16_t, false><<<grid, kSampThreads, 0, stream>>>(g);
+      if (vec) launch_timed(ps, sample_kernel<bf16_t, true>, grid, block, stream, g);
+      else launch_timed(ps, sample_kernel<bf16_t, false>, grid, block, stream, g);
     } else {
-      if (vec) sample_kernel<float, true><<<grid, kSampThreads, 0, stream>>>(g);
-      else sample_kernel<float, false><<<grid, kSampThreads, 0, stream>>>(g);
+      if (vec) launch_timed(ps, sample_kernel<float, true>, grid, block, stream, g);
+      else launch_timed(ps, sample_kernel<float, false>, grid, block, stream, g);
     }
   }
   DG_LAUNCH_CHECK("sample_kernel");
