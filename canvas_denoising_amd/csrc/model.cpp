@@ -44,8 +44,8 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
 int attn_max_splits();
 int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
                hipStream_t s);
-int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel, float* gate, int32_t* offsets,
-              int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s);
+int moe_route(const float* part, int splits, int M, int E, int k, int renorm, float* rlog, int32_t* sel,
+              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s);
 int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* slot_of, int M, int D, int k,
                 hipStream_t s);
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
@@ -296,6 +296,13 @@ static bool fused_norm_ok(const dg_model_desc& d) {
 // On entry h = RMSNorm(x); on exit x is the layer's output and h = RMSNorm(x) again (the next
 // layer's input norm, or the final norm before the LM head): every residual update is fused with
 // the norm that follows it. `kv_only` stops after the K/V projection (last encoder layer).
+// Where the shared expert runs: 0 on the main stream before the routing, 1 on the second stream
+// forked before the routing, 2 forked after it.
+#ifndef DG_SHARED_MODE
+#define DG_SHARED_MODE 1
+#endif
+constexpr int kSharedMode = DG_SHARED_MODE;
+
 static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causal, bool kv_only, hipStream_t s) {
   const dg_model_desc& d = c->d;
   const WsLayout& w = c->wsl;
@@ -337,44 +344,57 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     else
       DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
   }
-  // fork: the shared expert (h -> y_sh) runs on the second stream while the router and the routed
-  // experts run here; both only read h, and each stream has its own split-K scratch
-  DG_HIP(hipEventRecord(c->ev_fork, s));
-  DG_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0));
-  {
-    GemmArgs g;
-    g.A = h; g.lda = D;
-    g.B = wp(c, c->wl.sh_gu[l]); g.ldb = D;
-    g.M = M; g.N = (d.gated ? 2 : 1) * d.d_shared; g.K = D;
-    g.epi = d.gated ? EPI_GEGLU : EPI_GELU; g.pair_f = d.d_shared;
-    g.out = wsp<void>(c, w.sh_act); g.ldo = d.d_shared;
-    DG_TRY(run_gemm(c, g, c->aux, "shared_gateup", false, true));
-  }
-  {
+  // the shared expert: h -> y_sh
+  auto shared = [&](hipStream_t st, bool on_aux) -> int {
+    {
+      GemmArgs g;
+      g.A = h; g.lda = D;
+      g.B = wp(c, c->wl.sh_gu[l]); g.ldb = D;
+      g.M = M; g.N = (d.gated ? 2 : 1) * d.d_shared; g.K = D;
+      g.epi = d.gated ? EPI_GEGLU : EPI_GELU; g.pair_f = d.d_shared;
+      g.out = wsp<void>(c, w.sh_act); g.ldo = d.d_shared;
+      DG_TRY(run_gemm(c, g, st, "shared_gateup", false, on_aux));
+    }
     GemmArgs g;
     g.A = wsp<void>(c, w.sh_act); g.lda = d.d_shared;
     g.B = wp(c, c->wl.sh_down[l]); g.ldb = d.d_shared;
     g.M = M; g.N = D; g.K = d.d_shared;
     g.epi = EPI_STORE_F32; g.out = wsp<float>(c, w.y_sh); g.ldo = D;
-    DG_TRY(run_gemm(c, g, c->aux, "shared_down", true, true));
-  }
-  DG_HIP(hipEventRecord(c->ev_join, c->aux));
+    return run_gemm(c, g, st, "shared_down", true, on_aux);
+  };
+  // fork: the shared expert runs on the second stream beside the routing and the routed experts;
+  // both only read h, and each stream has its own split-K scratch
+  auto fork_shared = [&]() -> int {
+    DG_HIP(hipEventRecord(c->ev_fork, s));
+    DG_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0));
+    DG_TRY(shared(c->aux, true));
+    DG_HIP(hipEventRecord(c->ev_join, c->aux));
+    return DG_OK;
+  };
+  if (kSharedMode == 0) DG_TRY(shared(s, false));
+  if (kSharedMode == 1) DG_TRY(fork_shared());
   {
+    // router logits as split-k partials (summed in order by the routing kernel)
     GemmArgs g;
     g.A = h; g.lda = D;
     g.B = wp(c, c->wl.router[l]); g.ldb = D;
     g.M = M; g.N = d.n_experts; g.K = D;
     g.epi = EPI_STORE_F32; g.out = wsp<void>(c, w.rlog); g.ldo = d.n_experts;
+    int splits = 1;
+    g.defer_reduce = true;
+    g.splits_out = &splits;
     DG_TRY(run_gemm(c, g, s, "router", true));
+    DG_TRY(moe_route(splits > 1 ? wsp<float>(c, w.gpart) : wsp<float>(c, w.rlog), splits, M, d.n_experts, d.top_k,
+                     d.renorm_gates, wsp<float>(c, w.rlog), wsp<int32_t>(c, w.sel), wsp<float>(c, w.gate),
+                     wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<int32_t>(c, w.slot_of),
+                     wsp<float>(c, w.slot_gate), s));
   }
-  DG_TRY(moe_route(wsp<float>(c, w.rlog), M, d.n_experts, d.top_k, d.renorm_gates, wsp<int32_t>(c, w.sel),
-                   wsp<float>(c, w.gate), wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm),
-                   wsp<int32_t>(c, w.slot_of), wsp<float>(c, w.slot_gate), s));
+  if (kSharedMode == 2) DG_TRY(fork_shared());
   DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
                      wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, s));
   // join, then x += shared + sum of the token's gated expert outputs (fixed order); h = RMSNorm(x)
-  DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
+  if (kSharedMode != 0) DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
   if (fused)
     return residual_norm(x, nullptr, 0, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of),
                          d.top_k, h, M, D, d.rms_eps, d.dtype, s, "combine_norm");

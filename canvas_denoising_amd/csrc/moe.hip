@@ -3,13 +3,15 @@
 // active plus 1 shared; [P3] "Encoder-denoiser design": the denoiser is the
 // Gemma 4 26B-A4B MoE backbone).
 //
-// Routing, two kernels. (1) One wave per row: softmax over the E router logits
-// and the top-k chosen on the logits themselves (largest first, lowest index
-// on ties); the gate is the selected softmax probability. (2) One workgroup:
-// every (token, expert) pair sets a bit in a per-expert token mask in LDS;
-// popcounts give expert sizes, an exclusive scan gives offsets, and a token's
-// rank inside its expert is the popcount of the mask bits below it. The slot
-// order is therefore expert-major and token-ascending whatever the timing.
+// Routing after the router product r = h W_r^T (a split-k GEMM whose
+// partials are left unsummed), two kernels. (1) One wave per row: the
+// partials summed in split order, softmax over the E logits, top-k on the
+// logits themselves (largest first, lowest index on ties), the gate being
+// the selected softmax probability. (2) One workgroup: every (token, expert)
+// pair sets a bit in a per-expert token mask in LDS; popcounts give expert
+// sizes, an exclusive scan gives offsets, and a token's rank inside its
+// expert is the popcount of the mask bits below it. The slot order is
+// therefore expert-major and token-ascending whatever the timing.
 //
 // Expert GEMMs: with a 256-token canvas an expert sees about 16 tokens, so
 // the work is a stream of expert weights (arithmetic intensity ~16 flop/B):
@@ -43,20 +45,16 @@ __device__ inline void argmax_step(float& bv, int& be, float ov, int oe) {
   if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
 }
 
-// grid ceil(M / 4), 256 threads: wave w of the workgroup routes row 4 * blockIdx.x + w
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int M, int E, int k,
-                                                   int renorm, int32_t* __restrict__ sel,
-                                                   float* __restrict__ gate) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+// One wave routes one row of E <= 256 logits (lg, fp32): sel[0..k) the chosen experts in order,
+// gate[0..k) their softmax probabilities (renormalised over the k when renorm).
+__device__ inline void route_row(const float* lg, int E, int k, int renorm, int lane, int32_t* sel, float* gate) {
   constexpr int kPer = 4;  // E <= 256
   float v[kPer];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? logits[static_cast<int64_t>(row) * E + e] : -INFINITY;
+    v[i] = e < E ? lg[e] : -INFINITY;
     mx = fmaxf(mx, v[i]);
   }
   mx = wave_max(mx);
@@ -68,7 +66,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   int my_e = 0;
   float gsum = 0.f;
   for (int j = 0; j < k; ++j) {
-    // wave argmax: largest value, lowest expert index on ties
     float bv = -INFINITY;
     int be = 0x7FFFFFFF;
 #pragma unroll
@@ -91,12 +88,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (lane == j) { my_gate = g; my_e = be; }  // lane j keeps choice j
   }
   if (lane < k) {
-    sel[row * k + lane] = my_e;
-    gate[row * k + lane] = renorm ? my_gate / gsum : my_gate;
+    sel[lane] = my_e;
+    gate[lane] = renorm ? my_gate / gsum : my_gate;
   }
 }
 
-// one workgroup: expert sizes, offsets and the expert-major, token-ascending slot order
+// one workgroup of 1024 threads: expert sizes, offsets and the expert-major, token-ascending slot order
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ sel,
                                                        const float* __restrict__ gate, int M, int E, int k,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
@@ -152,6 +149,36 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     slot_of[p] = slot;
     slot_gate[slot] = gate[p];
   }
+}
+
+constexpr int kRouteSplits = 32;  // most split-k partials a routing call sums
+
+// Grid ceil(M / 4), 4 waves: wave w routes row 4 blockIdx.x + w. The logits are the sum of KS
+// partials part[q * M * E + row * E + e] (KS = 1: part holds the logits), written to rlog.
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* part, int M, int E, int k,
+                                                         int renorm, int KS, float* rlog,
+                                                         int32_t* __restrict__ sel, float* __restrict__ gate) {
+  __shared__ float lg[4 * 256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= M) return;
+  const int64_t pstride = static_cast<int64_t>(M) * E;
+  float* l = lg + wave * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    if (c < E) {
+      float v[kRouteSplits];
+#pragma unroll
+      for (int q = 0; q < kRouteSplits; ++q) v[q] = q < KS ? part[q * pstride + static_cast<int64_t>(row) * E + c] : 0.f;
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kRouteSplits; ++q) sum += v[q];
+      l[c] = sum;
+      rlog[static_cast<int64_t>(row) * E + c] = sum;
+    }
+  }
+  route_row(l, E, k, renorm, lane, sel + row * k, gate + row * k);
 }
 
 // ------------------------------------------------------------------ experts
@@ -398,14 +425,15 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
 }
 
 // ------------------------------------------------------------------- host
-int moe_route(const float* logits, int M, int E, int k, int renorm, int32_t* sel, float* gate, int32_t* offsets,
-              int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s) {
-  if (M > kMaxTokens || E > 256 || k > 16 || k > E) return fail(DG_ERR_UNSUPPORTED, "routing limits: M<=256, E<=256, k<=16");
+int moe_route(const float* part, int splits, int M, int E, int k, int renorm, float* rlog, int32_t* sel,
+              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s) {
+  if (M < 1 || M > kMaxTokens || E > 256 || k > 16 || k > E || splits < 1 || splits > kRouteSplits)
+    return fail(DG_ERR_UNSUPPORTED, "routing limits: 1<=M<=256, E<=256, k<=min(16,E), at most 32 partials");
   {
     ProfScope ps("moe_topk", s);
-    topk_kernel<<<(M + 3) / 4, 256, 0, s>>>(logits, M, E, k, renorm, sel, gate);
+    route_topk_kernel<<<(M + 3) / 4, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
   }
-  DG_LAUNCH_CHECK("topk_kernel");
+  DG_LAUNCH_CHECK("route_topk_kernel");
   {
     ProfScope ps("moe_permute", s);
     permute_kernel<<<1, 1024, 0, s>>>(sel, gate, M, E, k, offsets, perm, slot_of, slot_gate);
