@@ -217,11 +217,11 @@ __global__ void probs_bf16x8_kernel(const bf16_t* __restrict__ logits, const flo
   }
 }
 
-// out[c][r] = in[r][c]; 64 x 64 tiles through LDS. `in` is fragment-tiled with groups of gr 16-row
-// blocks (tiles.h) when gr > 0, row-major otherwise.
+// out[c][r] = in[r][c]; 64 x 64 tiles through LDS. `in` ([R x C]) is fragment-tiled with groups of gr
+// 16-row blocks (tiles.h) when gr > 0, row-major otherwise; likewise `out` ([C x R]) with gr_out.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t R, int64_t C, int gr,
-                                                        T* __restrict__ out) {
+                                                        int gr_out, T* __restrict__ out) {
   __shared__ T tile[64][65];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (r < R && c < C) out[c * R + r] = tile[tx][i];
+    if (r < R && c < C) out[gr_out > 0 ? tiled_index(c, r, 0, R, gr_out, 1) : c * R + r] = tile[tx][i];
   }
 }
 
@@ -311,14 +311,15 @@ int probs(const void* logits, const float* stats, float temperature, int M, int6
   return DG_OK;
 }
 
-int transpose(const void* in, int64_t R, int64_t C, int gr, void* out, int dtype, hipStream_t s) {
+int transpose(const void* in, int64_t R, int64_t C, int gr, int gr_out, void* out, int dtype, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64));
   if (grid.y > 65535) return fail(DG_ERR_UNSUPPORTED, "transpose: too many rows");
   if (dtype == DG_BF16)
-    transpose_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, gr,
+    transpose_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, gr, gr_out,
                                                   static_cast<bf16_t*>(out));
   else
-    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, gr, static_cast<float*>(out));
+    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), R, C, gr, gr_out,
+                                                 static_cast<float*>(out));
   DG_LAUNCH_CHECK("transpose_kernel");
   return DG_OK;
 }

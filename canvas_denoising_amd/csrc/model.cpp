@@ -36,7 +36,10 @@ int residual_norm(float* x, const float* part, int splits, const float* y, const
                   const char* name);
 int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
           hipStream_t s);
-int transpose(const void* in, int64_t R, int64_t C, int gr, void* out, int dtype, hipStream_t s);
+int transpose(const void* in, int64_t R, int64_t C, int gr, int gr_out, void* out, int dtype, hipStream_t s);
+int sc_embed_splits(int N, int64_t K, int dtype);
+int sc_embed(const void* P, int64_t ldp, const void* Et, int M, int N, int64_t K, float* part, void* u, int dtype,
+             hipStream_t s);
 int zero_fill(void* p, size_t bytes, hipStream_t s);
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
@@ -193,7 +196,7 @@ struct StepGraph {
 // ----------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
-      sc, u, sc_hid, P, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, total;
+      sc, u, sc_hid, P, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, total;
   int64_t gpart_floats;
 };
 
@@ -228,6 +231,7 @@ static WsLayout ws_layout(const dg_model_desc& d) {
   w.u = take(C * D * es);
   w.sc_hid = take(C * d.d_selfcond * es);
   w.P = take(static_cast<size_t>(C) * d.vocab * es);
+  w.scpart = take(static_cast<size_t>(sc_embed_splits(static_cast<int>(D), d.vocab, d.dtype)) * C * D * 4);
   w.gpart_floats = 32 * C * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
   w.gpart = take(w.gpart_floats * 4);
   w.gpart_aux = take(w.gpart_floats * 4);  // split-K scratch of the second stream
@@ -427,14 +431,9 @@ static int denoise_body(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logi
   float* x = wsp<float>(c, w.x);
   const float* sc = nullptr;
   if (sc_on) {
-    {
-      GemmArgs g;  // u = p E  (A = p [C x V], B = E^T [D x V])
-      g.A = wsp<void>(c, w.P); g.lda = d.vocab;
-      g.B = wp(c, c->wl.embed_t); g.ldb = d.vocab;
-      g.M = C; g.N = D; g.K = d.vocab;
-      g.epi = EPI_STORE; g.out = wsp<void>(c, w.u); g.ldo = D;
-      DG_TRY(run_gemm(c, g, s, "sc_embed", true));
-    }
+    // u = P E: P [C x V] row-major, E^T [D x V] tiled like the embedding
+    DG_TRY(sc_embed(wsp<void>(c, w.P), d.vocab, wp(c, c->wl.embed_t), C, D, d.vocab, wsp<float>(c, w.scpart),
+                    wsp<void>(c, w.u), d.dtype, s));
     {
       GemmArgs g;
       g.A = wsp<void>(c, w.u); g.lda = D;
@@ -555,7 +554,7 @@ int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream)
   if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
   const WLayout L = weight_layout(*desc);
   char* w = static_cast<char*>(d_weights);
-  return transpose(w + L.embed, desc->vocab, desc->d_model, kVocabGroup, w + L.embed_t, desc->dtype,
+  return transpose(w + L.embed, desc->vocab, desc->d_model, kVocabGroup, kVocabGroup, w + L.embed_t, desc->dtype,
                    as_stream(stream));
 }
 
@@ -602,7 +601,7 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
       DG_TRY(launch_synth_tiled(seed, dn_tid, d.d_model, d.d_expert, kDownGroup, 1, sigma, d.dtype, w + dn_off, s));
     }
   }
-  return transpose(w + L.embed, d.vocab, d.d_model, kVocabGroup, w + L.embed_t, d.dtype, s);
+  return transpose(w + L.embed, d.vocab, d.d_model, kVocabGroup, kVocabGroup, w + L.embed_t, d.dtype, s);
 }
 
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity) {

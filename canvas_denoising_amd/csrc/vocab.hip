@@ -12,6 +12,16 @@
 // each wave multiplies all M rows against its 32 columns: 16 x 2 fragment
 // accumulators, every A fragment read from LDS feeding two MFMAs.
 //
+// The self-conditioning product u = P E (P the tempered distribution,
+// [M x V]) has the same shape with the roles of the dimensions exchanged: P
+// is the staged operand, the transposed embedding E^T (D x V, tiled the same
+// way) the stream, and K = V. Its D / 256 column blocks alone would occupy
+// only a few compute units, so the vocabulary is also split into k shares;
+// the fp32 partials of the shares are summed in order by a second kernel.
+// The column blocks of one k share run on one XCD (the dispatcher sends
+// block b to XCD b % 8), so the P rows they all read are fetched into that
+// XCD's L2 once.
+//
 // One loop iteration per k-tile: wait until the copies of the k-tile have
 // landed (each wave issues exactly 8 loads per k-tile, 4 copies into LDS and
 // 4 register loads of E, so a fixed vmcnt leaves the younger k-tiles in
@@ -31,6 +41,7 @@ constexpr int kVW = 8;         // waves per workgroup
 constexpr int kVRows = 256;    // rows of h staged per k-tile (M <= 256)
 constexpr int kVNS = 3;        // ring depth (k-tiles)
 constexpr int kVRowB = 128;    // bytes of one h row per k-tile
+constexpr int kMaxSplitSum = 32;  // most k shares of the split form
 
 template <typename T>
 __device__ inline typename Frag<T>::type lds_frag(const unsigned char* stage, int r, int ks, int g4);
@@ -55,10 +66,14 @@ __device__ inline f32x8_t lds_frag<float>(const unsigned char* stage, int r, int
 
 // Grid: ceil(V / (32 kVW)) workgroups of kVW waves; wave w of block b owns vocabulary group
 // b * kVW + w (E rows 32 g .. 32 g + 31).
-template <typename T>
+// PART: the split-k form. Block b: slot q = (b % 8) J + b / 8 (J = grid / 8) names k share q / nblk
+// and column block q % nblk; its k-tiles are [KT s / S, KT (s + 1) / S); it stores fp32 partials
+// part[s][row][col] (row stride ldo) instead of T outputs.
+template <typename T, bool PART>
 __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restrict__ h, int64_t ldh,
                                                              const T* __restrict__ E, int M, int V, int D,
-                                                             T* __restrict__ logits, int64_t ldo) {
+                                                             T* __restrict__ logits, int64_t ldo,
+                                                             float* __restrict__ part, int S, int nblk) {
   constexpr int KE = kVRowB / static_cast<int>(sizeof(T));  // k elements per k-tile
   constexpr int KS = KE / 32;                               // MFMA k-steps per k-tile
   constexpr int SBYTES = kVRows * kVRowB;                   // 32 KB per stage
@@ -71,9 +86,19 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g4 = lane >> 4;
-  const int grp = blockIdx.x * kVW + wave;
+  int blk = blockIdx.x, ks = 0, kbeg = 0, KT = D / KE;
+  if constexpr (PART) {
+    const int J = gridDim.x / 8;
+    const int q = (blockIdx.x & 7) * J + (blockIdx.x >> 3);
+    if (q >= nblk * S) return;  // padding block of the XCD-aware grid: no barrier reached
+    ks = q / nblk;
+    blk = q - ks * nblk;
+    const int kt_all = KT;
+    kbeg = static_cast<int>(static_cast<int64_t>(kt_all) * ks / S);
+    KT = static_cast<int>(static_cast<int64_t>(kt_all) * (ks + 1) / S) - kbeg;
+  }
+  const int grp = blk * kVW + wave;
   const bool active = grp * 32 < V;  // idle waves run the loop on group 0 (uniform barriers), store nothing
-  const int KT = D / KE;
 
   // A copies: copy c = wave * CPW + i covers rows 8c .. 8c+7 of the stage; lane l fills position l % 8
   // of row 8c + l / 8 with the row's chunk (l % 8) ^ (row % 8). Rows past M re-read row M-1.
@@ -88,7 +113,7 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
 
   FT breg[kVNS][BF];
   auto issue = [&](int kt, int slot) {
-    const int k = min(kt, KT - 1);
+    const int k = kbeg + min(kt, KT - 1);
     unsigned char* base = smem + slot * SBYTES;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) dma16(asrc[i] + static_cast<int64_t>(k) * KE, base + (wave * CPW + i) * 1024);
@@ -143,11 +168,37 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
     for (int i = 0; i < 4; ++i) {
       const int row = m * 16 + g4 * 4 + i;
       if (row < M) {
-        T* o = logits + static_cast<int64_t>(row) * ldo + grp * 32 + fr;
-        o[0] = from_f32<T>(acc[m][0][i]);
-        o[16] = from_f32<T>(acc[m][1][i]);
+        if constexpr (PART) {
+          float* o = part + (static_cast<int64_t>(ks) * M + row) * ldo + grp * 32 + fr;
+          o[0] = acc[m][0][i];
+          o[16] = acc[m][1][i];
+        } else {
+          T* o = logits + static_cast<int64_t>(row) * ldo + grp * 32 + fr;
+          o[0] = from_f32<T>(acc[m][0][i]);
+          o[16] = from_f32<T>(acc[m][1][i]);
+        }
       }
     }
+}
+
+// out[row][col] = sum over s = 0 .. S-1, in order, of part[s][row][col] (N % 4 == 0); 4 columns per thread
+template <typename T>
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                        T* __restrict__ out) {
+  const int64_t i4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n4 = static_cast<int64_t>(M) * N / 4;
+  if (i4 >= n4) return;
+  const float4* p = reinterpret_cast<const float4*>(part);
+  float4 v[kMaxSplitSum];
+#pragma unroll
+  for (int q = 0; q < kMaxSplitSum; ++q) v[q] = q < S ? p[q * n4 + i4] : float4{0.f, 0.f, 0.f, 0.f};
+  float4 a = v[0];
+#pragma unroll
+  for (int q = 1; q < kMaxSplitSum; ++q) {
+    a.x += v[q].x; a.y += v[q].y; a.z += v[q].z; a.w += v[q].w;
+  }
+  T* o = out + i4 * 4;
+  o[0] = from_f32<T>(a.x); o[1] = from_f32<T>(a.y); o[2] = from_f32<T>(a.z); o[3] = from_f32<T>(a.w);
 }
 
 int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
@@ -158,14 +209,55 @@ int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, v
   const int grid = (V / 32 + kVW - 1) / kVW;
   ProfScope ps("lm_head", s);
   if (dtype == DG_BF16)
-    vocab_gemm_kernel<bf16_t><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
-                                                         static_cast<const bf16_t*>(E), M, V, D,
-                                                         static_cast<bf16_t*>(logits), ldo);
+    vocab_gemm_kernel<bf16_t, false><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
+                                                                static_cast<const bf16_t*>(E), M, V, D,
+                                                                static_cast<bf16_t*>(logits), ldo, nullptr, 1, 0);
   else
-    vocab_gemm_kernel<float><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(h), ldh,
-                                                        static_cast<const float*>(E), M, V, D,
-                                                        static_cast<float*>(logits), ldo);
+    vocab_gemm_kernel<float, false><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(h), ldh,
+                                                               static_cast<const float*>(E), M, V, D,
+                                                               static_cast<float*>(logits), ldo, nullptr, 1, 0);
   DG_LAUNCH_CHECK("vocab_gemm_kernel");
+  return DG_OK;
+}
+
+int sc_embed_splits(int N, int64_t K, int dtype) {
+  const int ke = dtype == DG_BF16 ? 64 : 32;
+  const int nblk = (N / 32 + kVW - 1) / kVW;
+  const int64_t kt = K / ke;
+  int S = std::max(1, std::min(kMaxSplitSum, 256 / nblk));
+  while (S > 1 && kt / S < 8) --S;  // at least 8 k-tiles per share
+  return S;
+}
+
+int sc_embed(const void* P, int64_t ldp, const void* Et, int M, int N, int64_t K, float* part, void* u, int dtype,
+             hipStream_t s) {
+  if (M < 1 || M > kVRows) return fail(DG_ERR_UNSUPPORTED, "self-conditioning: rows must be in [1, 256]");
+  const int ke = dtype == DG_BF16 ? 64 : 32;
+  if (K % ke != 0 || N % 32 != 0 || K > (int64_t{1} << 30))
+    return fail(DG_ERR_UNSUPPORTED, "self-conditioning: vocab / d_model do not tile");
+  const int nblk = (N / 32 + kVW - 1) / kVW;
+  const int S = sc_embed_splits(N, K, dtype);
+  const int grid = 8 * ((nblk * S + 7) / 8);
+  {
+    ProfScope ps("sc_embed", s);
+    if (dtype == DG_BF16)
+      vocab_gemm_kernel<bf16_t, true><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(P), ldp,
+                                                                 static_cast<const bf16_t*>(Et), M, N,
+                                                                 static_cast<int>(K), nullptr, N, part, S, nblk);
+    else
+      vocab_gemm_kernel<float, true><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(P), ldp,
+                                                                static_cast<const float*>(Et), M, N,
+                                                                static_cast<int>(K), nullptr, N, part, S, nblk);
+  }
+  DG_LAUNCH_CHECK("vocab_gemm_kernel");
+  {
+    ProfScope ps("sc_sum", s);
+    const int64_t n4 = static_cast<int64_t>(M) * N / 4;
+    const unsigned g = static_cast<unsigned>((n4 + 255) / 256);
+    if (dtype == DG_BF16) split_sum_kernel<bf16_t><<<g, 256, 0, s>>>(part, S, M, N, static_cast<bf16_t*>(u));
+    else split_sum_kernel<float><<<g, 256, 0, s>>>(part, S, M, N, static_cast<float*>(u));
+  }
+  DG_LAUNCH_CHECK("split_sum_kernel");
   return DG_OK;
 }
 

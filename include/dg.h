@@ -191,7 +191,7 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
 /* Weight tensors inside the packed, caller-owned weight buffer. */
 enum {
   DG_W_EMBED = 0,    /* [vocab x d_model], tied input embedding and LM head */
-  DG_W_EMBED_T = 1,  /* [d_model x vocab], derived copy of EMBED transposed */
+  DG_W_EMBED_T = 1,  /* [d_model x vocab], derived copy of EMBED transposed, stored tiled */
   DG_W_SC1 = 2,      /* [d_selfcond x d_model] self-conditioning FFN, first */
   DG_W_SC2 = 3,      /* [d_model x d_selfcond] self-conditioning FFN, second */
   DG_W_Q = 4,        /* [n_q_heads*head_dim x d_model] (per layer) */
@@ -220,8 +220,11 @@ size_t dg_weights_bytes(const dg_model_desc* desc);
  * group][column tile][the group's 2 16-row blocks]; gate/up: tiles ordered [32-feature group][column tile][gate rows 0-15,
  * gate rows 16-31, up rows 0-15, up rows 16-31 of the group] (up alone when
  * ungated), down: [64-row group][column tile][the group's 4 16-row
- * blocks]. For DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the
- * expert's shared gate/up region. Write them with dg_load_weight. */
+ * blocks]. DG_W_EMBED_T, the [d_model x vocab] operand of the
+ * self-conditioning product, is tiled like the embedding: [32-row group of
+ * d_model][vocabulary tile of 32][the group's 2 16-row blocks]. For
+ * DG_W_EX_GATE / DG_W_EX_UP the offset is the start of the expert's shared
+ * gate/up region. Write them with dg_load_weight. */
 int dg_weight_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
                      size_t* offset, int64_t* rows, int64_t* cols);
 /* Store one tensor from a row-major [rows x cols] device array d_src of the

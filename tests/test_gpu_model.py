@@ -285,13 +285,27 @@ def test_load_weight_reproduces_tiled_fill(libs, dtype, gated):
     torch.cuda.synchronize()
     assert torch.equal(model.weights[off_e:off_e + n_e], ref_e)
     assert torch.equal(model.weights[off_et:off_et + n_e], ref_et)
-    et = ref_et.view(tdt).view(d.d_model, d.vocab).float().cpu().numpy().astype(np.float64)
+    et = untile(ref_et.view(tdt).float().cpu().numpy().astype(np.float64), d.d_model, d.vocab, 2)
     assert np.array_equal(et, W["embed"].T)
     # the tiled layout is not row-major: a row-major copy would differ
     assert not torch.equal(ref_dn.view(tdt).view(d.d_model, d.d_expert).cpu(), srcs[-1].cpu())
     with pytest.raises(ValueError):
         model.tensor(L.DG_W_EX_DOWN, layer, expert)
     model.close()
+
+
+def untile(flat, R, K, gr):
+    """[R x K] matrix from its fragment-tiled storage (one matrix, groups of gr 16-row blocks): tile
+    (group, k-tile, block) holds rows 16 (gr group + block) .., columns 32 k-tile ..; element 8 l + j
+    of a tile is row l % 16, column 8 (l // 16) + j."""
+    p = np.arange(flat.size)
+    tile, inner = p // 512, p % 512
+    lane = inner // 8
+    g, t2 = tile % gr, tile // gr
+    kb, group = t2 % (K // 32), t2 // (K // 32)
+    out = np.empty((R, K))
+    out[(group * gr + g) * 16 + lane % 16, kb * 32 + (lane // 16) * 8 + inner % 8] = flat
+    return out
 
 
 def test_graph_replay_matches_direct_launches(libs):
