@@ -124,36 +124,72 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
   const float4* p4 = reinterpret_cast<const float4*>(part);
   const float4* y4 = reinterpret_cast<const float4*>(y);
   const float4* s4 = reinterpret_cast<const float4*>(slot_out);
-  int slots[16];
-  if (y4)
-    for (int j = 0; j < k; ++j) slots[j] = slot_of[m * k + j];
+  constexpr int B = 8;  // gathered rows whose loads are issued together
+  auto add4 = [](float4& t, const float4& u) { t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w; };
   float4 v[NV];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + 256 * i;
-    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < n4) {
-      float4 a = xr[c];
-      if (splits > 0) {
-        float4 t = p4[static_cast<int64_t>(m) * n4 + c];
-        for (int z = 1; z < splits; ++z) {
-          const float4 u = p4[z * plane + static_cast<int64_t>(m) * n4 + c];
-          t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (splits > 0) {  // t = part[0] + part[1] + ... (in order), x += t
+    float4 t[NV];
+    for (int z0 = 0; z0 < splits; z0 += B) {
+      float4 u[NV][B];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q) {
+          const int c = tid + 256 * i;
+          u[i][q] = (c < n4 && z0 + q < splits) ? p4[(z0 + q) * plane + static_cast<int64_t>(m) * n4 + c]
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        a.x += t.x; a.y += t.y; a.z += t.z; a.w += t.w;
-      }
-      if (y4) {
-        float4 t = y4[static_cast<int64_t>(m) * n4 + c];
-        for (int j = 0; j < k; ++j) {
-          const float4 u = s4[static_cast<int64_t>(slots[j]) * n4 + c];
-          t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q) {
+          if (z0 + q >= splits) break;
+          if (z0 + q == 0) t[i] = u[i][0];
+          else add4(t[i], u[i][q]);
         }
-        a.x += t.x; a.y += t.y; a.z += t.z; a.w += t.w;
-      }
-      xr[c] = a;
-      v[i] = a;
     }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) add4(v[i], t[i]);
+  }
+  if (y4) {  // t = y + slot_out[slot 0] + slot_out[slot 1] + ... (in order), x += t
+    float4 t[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = tid + 256 * i;
+      t[i] = c < n4 ? y4[static_cast<int64_t>(m) * n4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int j0 = 0; j0 < k; j0 += B) {
+      int sl[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) sl[q] = j0 + q < k ? slot_of[m * k + j0 + q] : 0;
+      float4 u[NV][B];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q) {
+          const int c = tid + 256 * i;
+          u[i][q] = (c < n4 && j0 + q < k) ? s4[static_cast<int64_t>(sl[q]) * n4 + c]
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q)
+          if (j0 + q < k) add4(t[i], u[i][q]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) add4(v[i], t[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + 256 * i;
+    if (c < n4 && (splits > 0 || y4)) xr[c] = v[i];
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {

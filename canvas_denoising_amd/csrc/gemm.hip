@@ -404,6 +404,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, i
       }
 }
 
+constexpr int kSumBatch = 8;
+
 // Sum the split-K partials in split order and apply the epilogue; a paired (gated GeLU) GEMM
 // combines the gate sum at column j with the up sum at column pair_f + j.
 template <typename T>
@@ -416,9 +418,15 @@ __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
       const int row = static_cast<int>(e / g.pair_f), j = static_cast<int>(e - static_cast<int64_t>(row) * g.pair_f);
       const int64_t gi = static_cast<int64_t>(row) * g.N + j;
       float gs = 0.f, us = 0.f;
-      for (int z = 0; z < splits; ++z) {
-        gs += g.part[z * n + gi];
-        us += g.part[z * n + gi + g.pair_f];
+      for (int z0 = 0; z0 < splits; z0 += kSumBatch) {  // loads issued together, summed in order
+        float a[kSumBatch], b[kSumBatch];
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q) {
+          a[q] = z0 + q < splits ? g.part[(z0 + q) * n + gi] : 0.f;
+          b[q] = z0 + q < splits ? g.part[(z0 + q) * n + gi + g.pair_f] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q) { gs += a[q]; us += b[q]; }
       }
       static_cast<T*>(g.out)[static_cast<int64_t>(row) * g.ldo + j] = from_f32<T>(gelu_erf(gs) * us);
     }
@@ -426,7 +434,13 @@ __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
   }
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
     float v = 0.f;
-    for (int z = 0; z < splits; ++z) v += g.part[z * n + e];
+    for (int z0 = 0; z0 < splits; z0 += kSumBatch) {  // loads issued together, summed in order
+      float a[kSumBatch];
+#pragma unroll
+      for (int q = 0; q < kSumBatch; ++q) a[q] = z0 + q < splits ? g.part[(z0 + q) * n + e] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kSumBatch; ++q) v += a[q];
+    }
     const int row = static_cast<int>(e / g.N), col = static_cast<int>(e - static_cast<int64_t>(row) * g.N);
     epilogue<T>(g, row, col, v);
   }
@@ -445,6 +459,11 @@ static TileChoice pick_tile(int M, int N, int K) {
   return {64, 64};
 }
 
+#ifndef DG_GEMM_WGS
+#define DG_GEMM_WGS 256
+#endif
+constexpr int64_t kGemmTargetWGs = DG_GEMM_WGS;  // split-K grows the grid towards this many workgroups
+
 int gemm_pick_splits(int M, int N, int K, int dtype, int64_t part_capacity, bool allow_split) {
   if (!allow_split) return 1;
   const int bk = dtype == DG_BF16 ? 64 : 32;
@@ -452,7 +471,7 @@ int gemm_pick_splits(int M, int N, int K, int dtype, int64_t part_capacity, bool
   const int64_t tiles = static_cast<int64_t>((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
   int s = 1;
   const int ktiles = K / bk;
-  while (tiles * s < 256 && s * 2 <= 32 && ktiles / (s * 2) >= 4 &&
+  while (tiles * s < kGemmTargetWGs && s * 2 <= 32 && ktiles / (s * 2) >= 4 &&
          static_cast<int64_t>(s) * 2 * M * N <= part_capacity)
     s *= 2;
   return s;
