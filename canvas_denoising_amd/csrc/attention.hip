@@ -325,30 +325,48 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
 // combine the key slices, one wave per query row, splits in a fixed order:
 // o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Every lane reads the (m, l) of all slices (the
 // same addresses) so no cross-lane traffic is needed; lane l owns head dims 2l, 2l+1 (+128 ...).
+// All slices' (m, l) loads are issued together, and the O rows in batches of 8 slices.
+constexpr int kMergeMax = 32;  // attn_max_splits()
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int hd) {
   const int64_t R = static_cast<int64_t>(a.Hq) * a.M;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= R) return;
+  const int S = a.splits;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+  float2 e[kMergeMax];
+#pragma unroll
+  for (int s = 0; s < kMergeMax; ++s) e[s] = s < S ? ml[s * R + row] : make_float2(-INFINITY, 0.f);
   float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, ml[s * R + row].x);
+#pragma unroll
+  for (int s = 0; s < kMergeMax; ++s) mx = fmaxf(mx, e[s].x);
   const int nc = hd / 128;  // float2 columns per lane beyond the first
   float l = 0.f;
   float2 acc[2] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
-  for (int s = 0; s < a.splits; ++s) {
-    const float2 e = ml[s * R + row];
-    const float w = e.x == -INFINITY ? 0.f : exp2f(e.x - mx);
-    l += w * e.y;
-    const float2* po = reinterpret_cast<const float2*>(a.part_o + (s * R + row) * hd);
+  constexpr int B = 8;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      if (c <= nc && 2 * (lane + 64 * c) < hd) {
-        const float2 v = po[lane + 64 * c];
-        acc[c].x += w * v.x;
-        acc[c].y += w * v.y;
+  for (int s0 = 0; s0 < kMergeMax; s0 += B) {
+    if (s0 >= S) break;
+    float2 v[B][2];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const float2* po = reinterpret_cast<const float2*>(a.part_o + ((s0 + q) * R + row) * hd);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        v[q][c] = (s0 + q < S && c <= nc && 2 * (lane + 64 * c) < hd) ? po[lane + 64 * c] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      if (s0 + q >= S) break;
+      const float w = e[s0 + q].x == -INFINITY ? 0.f : exp2f(e[s0 + q].x - mx);
+      l += w * e[s0 + q].y;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        acc[c].x += w * v[q][c].x;
+        acc[c].y += w * v[q][c].y;
       }
+    }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const int head = static_cast<int>(row / a.M), m = static_cast<int>(row % a.M);
@@ -396,7 +414,7 @@ __global__ void attn_f32_kernel(AttnArgs a) {
 #define DG_ATT_WGS 256
 #endif
 constexpr int kAttnWGs = DG_ATT_WGS;  // target workgroups of a launch
-int attn_max_splits() { return 32; }
+int attn_max_splits() { return kMergeMax; }
 
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
