@@ -253,14 +253,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
 // r is stored at position q ^ (r % 8) so the 16 rows a fragment read touches
 // fall on different banks. Rows past M (or N) re-read the last valid row;
 // their results are not stored.
-template <int BM, int BN, int NS>
-__global__ __launch_bounds__(256) void gemm_dma_kernel(GemmArgs g, int splits, int k_per_split) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+template <int BM, int BN, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(GemmArgs g, int splits, int k_per_split) {
+  // NW waves as (NW / 2) x 2 over the tile; every wave issues an equal share of the stage's copies
+  constexpr int WM = BM / (NW / 2), WN = BN / 2, TM = WM / 16, TN = WN / 16;
   constexpr int ROWB = 128;  // bytes per tile row: 64 bf16
   constexpr int SA = BM * ROWB, SB = BN * ROWB, SS = SA + SB;
-  constexpr int ALPW = BM / 32, BLPW = BN / 32;  // load instructions per wave per stage (8 rows each)
+  constexpr int ALPW = BM / (8 * NW), BLPW = BN / (8 * NW);  // load instructions per wave per stage (8 rows each)
   constexpr int LPS = ALPW + BLPW;
-  static_assert(TN % 2 == 0 && ALPW >= 1 && BLPW >= 1, "tile");
+  static_assert(TM >= 1 && TN % 2 == 0 && ALPW >= 1 && BLPW >= 1, "tile");
   __shared__ __align__(16) unsigned char smem[NS * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -459,6 +460,15 @@ static TileChoice pick_tile(int M, int N, int K) {
   return {64, 64};
 }
 
+#ifndef DG_GEMM_NS
+#define DG_GEMM_NS 4
+#endif
+constexpr int kGemmStages64 = DG_GEMM_NS;  // LDS ring depth of the 64 x 64 tile
+#ifndef DG_GEMM_NW
+#define DG_GEMM_NW 8
+#endif
+constexpr int kGemmWaves64 = DG_GEMM_NW;   // waves of the 64 x 64 tile (4 or 8)
+
 #ifndef DG_GEMM_WGS
 #define DG_GEMM_WGS 256
 #endif
@@ -504,8 +514,8 @@ static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name
     if constexpr (sizeof(T) == 2) {
       const int nm = (g.M + tc.bm - 1) / tc.bm, nn = (g.N + tc.bn - 1) / tc.bn;
       dim3 grid(static_cast<unsigned>(nm * nn), static_cast<unsigned>(splits));
-      if (tc.bm == 128) gemm_dma_kernel<128, 128, 4><<<grid, 256, 0, s>>>(g, splits, kps);
-      else gemm_dma_kernel<64, 64, 4><<<grid, 256, 0, s>>>(g, splits, kps);
+      if (tc.bm == 128) gemm_dma_kernel<128, 128, 4, 4><<<grid, 256, 0, s>>>(g, splits, kps);
+      else gemm_dma_kernel<64, 64, kGemmStages64, kGemmWaves64><<<grid, 64 * kGemmWaves64, 0, s>>>(g, splits, kps);
       rc = DG_OK;
     } else {
       if (tc.bm == 128) rc = launch_tile<T, 128, 128>(g, splits, kps, s);
