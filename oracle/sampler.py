@@ -22,6 +22,16 @@ Readings taken where the pages are silent (listed again in the design doc):
 * "predictions" compared by the stop rule are the argmax vector;
 * the stable counter counts consecutive equal argmax vectors; it is reset at
   step 0 and whenever a vector changes; two equalities are needed.
+
+Variants the pages also describe, each behind a Schedule flag (defaults off):
+* stop_either: [P3] "Inference mechanism" lets either condition stop the
+  canvas (stability for N steps, or the entropy threshold) where [P4] needs
+  both;
+* accept_cumulative: [P3] "Inference mechanism" accepts token groups by an
+  entropy-based confidence. Reading taken: positions are taken in increasing
+  entropy (lower position first on ties) and the group accepted is the
+  longest such run whose summed entropy stays within the bound (it may be
+  empty); the rest are re-noised.
 """
 from __future__ import annotations
 
@@ -42,6 +52,8 @@ class Schedule:
     stop_mean_entropy: float = 0.005
     stable_needed: int = 2
     seed: int = 0
+    stop_either: bool = False
+    accept_cumulative: bool = False
 
 
 def temperature(step: int, sched: Schedule) -> float:
@@ -68,6 +80,22 @@ def entropy_nats(p: np.ndarray) -> np.ndarray:
     return -t.sum(axis=-1)
 
 
+def cumulative_accept(H: np.ndarray, bound: float) -> np.ndarray:
+    """Group acceptance: walk the positions in increasing entropy (ties: lower position first),
+    adding each entropy to a running total; every position visited while the total is still
+    <= bound is accepted, and the walk ends at the first one that takes it past the bound."""
+    H = np.asarray(H, dtype=np.float64)
+    order = sorted(range(H.size), key=lambda i: (H[i], i))
+    accept = np.zeros(H.size, dtype=bool)
+    total = 0.0
+    for i in order:
+        total += H[i]
+        if total > bound:
+            break
+        accept[i] = True
+    return accept
+
+
 @dataclass
 class StepResult:
     entropy: np.ndarray      # [C] float64
@@ -91,7 +119,7 @@ def sample_step(logits: np.ndarray, step: int, block: int, sched: Schedule,
     p = tempered_probs(logits, T)
     H = entropy_nats(p)
     pred = np.argmax(logits, axis=-1).astype(np.int64)  # first maximum = lowest index
-    accept = H <= sched.entropy_bound
+    accept = cumulative_accept(H, sched.entropy_bound) if sched.accept_cumulative else H <= sched.entropy_bound
     noise = philox.draw_tokens(sched.seed, np.arange(C), step, block, philox.PURPOSE_RENOISE, V)
     nxt = np.where(accept, pred, noise)
     meanH = float(H.mean())
@@ -99,5 +127,6 @@ def sample_step(logits: np.ndarray, step: int, block: int, sched: Schedule,
         stable = stable + 1
     else:
         stable = 0
-    stop = (meanH < sched.stop_mean_entropy) and (stable >= sched.stable_needed)
+    confident, steady = meanH < sched.stop_mean_entropy, stable >= sched.stable_needed
+    stop = (confident or steady) if sched.stop_either else (confident and steady)
     return StepResult(H, pred, accept, nxt, meanH, stable, bool(stop), p if keep_probs else None)

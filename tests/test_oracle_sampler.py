@@ -15,7 +15,7 @@ from hypothesis import given, settings, strategies as st
 
 from oracle import philox
 from oracle.loop import denoise_block
-from oracle.sampler import Schedule, entropy_nats, sample_step, temperature, tempered_probs
+from oracle.sampler import Schedule, cumulative_accept, entropy_nats, sample_step, temperature, tempered_probs
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "sampling_settings.json")))
 
@@ -184,3 +184,78 @@ def test_budget_exit_commits_final_prediction():
     assert np.array_equal(tr.block_ids, (np.arange(C) * 7 + 4) % 512)
     # the first canvas is the block's Philox initialisation
     assert np.array_equal(tr.canvases[0], philox.init_canvas(0, C, 1, 512))
+
+
+# ------------------------------------------------------------- sampler variants
+# Either-condition stop ([P3] "Inference mechanism") and group acceptance by summed entropy
+# ([P3] same section: "token groups"); the readings are in the oracle's header.
+
+def test_either_stop_fires_on_entropy_alone():
+    C = 16
+    tr = denoise_block(_scripted(lambda s: (np.arange(C) + s) % 512), Schedule(stop_either=True), 0, C, 512)
+    assert tr.stopped and tr.steps == 1  # confident from step 0, predictions never repeat
+
+
+def test_either_stop_fires_on_stability_alone():
+    C = 16
+    fixed = np.arange(C)
+    tr = denoise_block(_scripted(lambda s: fixed, confident=False), Schedule(max_steps=8, stop_either=True), 0, C, 512)
+    assert tr.stopped and tr.steps == 3  # two equalities reached at s = 2; entropy stays high
+    assert all(r.mean_entropy > 0.005 for r in tr.results)
+
+
+def test_either_stop_needs_one_condition():
+    C = 16
+    tr = denoise_block(_scripted(lambda s: (np.arange(C) + s) % 512, confident=False),
+                       Schedule(max_steps=6, stop_either=True), 0, C, 512)
+    assert not tr.stopped and tr.steps == 6
+
+
+def test_group_acceptance_worked_example():
+    # increasing entropy: 0.01 (pos 1), 0.03 (pos 3), 0.04 (pos 4), 0.05 (pos 0), 0.2 (pos 2);
+    # running totals 0.01, 0.04, 0.08, 0.13 -> the fourth passes 0.1: positions 1, 3, 4 accepted
+    H = np.array([0.05, 0.01, 0.2, 0.03, 0.04])
+    assert cumulative_accept(H, 0.1).tolist() == [False, True, False, True, True]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_group_acceptance_equal_entropies_take_lowest_positions(k):
+    # eight positions of entropy 0.1 / k + tiny: exactly k - 1 fit when the unit is just above 0.1 / k
+    e = 0.1 / k * (1 + 1e-9)
+    H = np.full(8, e)
+    acc = cumulative_accept(H, 0.1)
+    assert acc.tolist() == [True] * (k - 1) + [False] * (9 - k)
+    # and exactly k when the unit is just below
+    acc = cumulative_accept(np.full(8, 0.1 / k * (1 - 1e-9)), 0.1)
+    assert acc.tolist() == [True] * k + [False] * (8 - k)
+
+
+def test_group_acceptance_edge_cases():
+    assert not cumulative_accept(np.array([0.5, 0.2, 0.3]), 0.1).any()        # nothing fits
+    assert cumulative_accept(np.zeros(6), 0.1).all()                           # zero entropy always fits
+    assert cumulative_accept(np.array([0.0, 0.1, 0.0]), 0.1).all()             # inclusive bound
+
+
+@given(seed=st.integers(0, 2**31), n=st.integers(1, 40), bound=st.floats(0.0, 2.0))
+@settings(max_examples=200, deadline=None)
+def test_group_acceptance_is_the_longest_fitting_prefix(seed, n, bound):
+    rng = np.random.default_rng(seed)
+    H = rng.choice([0.0, 0.02, 0.05, 0.1, 0.3], size=n) * rng.random(n).round(1)
+    acc = cumulative_accept(H, bound)
+    order = np.lexsort((np.arange(n), H))  # increasing entropy, lower position first on ties
+    # brute force over prefix lengths, each sum computed afresh
+    best = max(L for L in range(n + 1) if all(H[order[:j]].sum() <= bound for j in range(1, L + 1)))
+    assert acc.sum() == best
+    assert set(np.nonzero(acc)[0]) == set(order[:best].tolist())
+
+
+def test_group_acceptance_in_a_sampling_step():
+    C, V = 6, 64
+    logits = np.zeros((C, V))
+    logits[[0, 2, 5], [3, 7, 9]] = 1000.0   # one-hot rows: entropy 0
+    logits[4, :2] = 1000.0                   # two-way tie: ln 2 > bound
+    sched = Schedule(seed=3, accept_cumulative=True)
+    res = sample_step(logits, 4, 1, sched, None, 0)
+    assert res.accept.tolist() == [True, False, True, False, False, True]
+    noise = philox.draw_tokens(3, np.arange(C), 4, 1, philox.PURPOSE_RENOISE, V)
+    assert np.array_equal(res.next_canvas, np.where(res.accept, res.pred, noise))
