@@ -40,7 +40,8 @@ class dg_model_desc(ctypes.Structure):
 class dg_sched(ctypes.Structure):
     _fields_ = [("max_steps", ctypes.c_int32), ("t_start", ctypes.c_float), ("t_end", ctypes.c_float),
                 ("entropy_bound", ctypes.c_float), ("stop_mean_entropy", ctypes.c_float),
-                ("stable_needed", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("stable_needed", ctypes.c_int32), ("seed", ctypes.c_uint64), ("mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class dg_stop_state(ctypes.Structure):
@@ -48,7 +49,7 @@ class dg_stop_state(ctypes.Structure):
                 ("stopped", ctypes.c_int32), ("steps_run", ctypes.c_int32)]
 
 
-assert ctypes.sizeof(dg_sched) == 32 and ctypes.sizeof(dg_stop_state) == 16 and ctypes.sizeof(dg_model_desc) == 64
+assert ctypes.sizeof(dg_sched) == 40 and ctypes.sizeof(dg_stop_state) == 16 and ctypes.sizeof(dg_model_desc) == 64
 
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
@@ -128,9 +129,12 @@ def _check(name: str, rc: int) -> int:
     return rc
 
 
+DG_SCHED_STOP_EITHER, DG_SCHED_ACCEPT_GROUP = 1, 2
+
+
 def make_sched(max_steps=48, t_start=0.8, t_end=0.4, entropy_bound=0.1, stop_mean_entropy=0.005,
-               stable_needed=2, seed=0) -> dg_sched:
-    return dg_sched(max_steps, t_start, t_end, entropy_bound, stop_mean_entropy, stable_needed, seed)
+               stable_needed=2, seed=0, mode=0) -> dg_sched:
+    return dg_sched(max_steps, t_start, t_end, entropy_bound, stop_mean_entropy, stable_needed, seed, mode, 0)
 
 
 # ------------------------------------------------------------------ calls

@@ -172,6 +172,7 @@ struct SampleArgs {
   float c;  // log2(e) / T
   float bound, stop_thr;
   int stable_needed;
+  int mode;  // DG_SCHED_* flags
   uint64_t seed;
   int step, block;
   int32_t* canvas;
@@ -290,6 +291,12 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
 }
 
 constexpr int kFinThreads = 1024;
+constexpr int kGroupMaxRows = 4096;  // rows the group acceptance ranks in LDS
+
+__device__ inline int32_t renoise_token(const SampleArgs& g, int row) {
+  return draw_token(g.seed, static_cast<uint32_t>(row), static_cast<uint32_t>(g.step), static_cast<uint32_t>(g.block),
+                    kPurposeRenoise, static_cast<uint32_t>(g.vocab));
+}
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinParts = 4;                     // threads per row (one DPP quad)
 constexpr int kFinRecs = kMaxSplits / kFinParts;  // records per thread at most
@@ -303,6 +310,10 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
   if (g.stop->stopped) return;
   __shared__ float shs[kFinWaves];
   __shared__ int shq[kFinWaves];
+  __shared__ float gH[kGroupMaxRows];    // group acceptance: entropy per row, then in rank order
+  __shared__ int32_t gIdx[kGroupMaxRows];
+  __shared__ int gK;
+  const bool group = (g.mode & DG_SCHED_ACCEPT_GROUP) != 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = tid % kFinParts;
   const float c = g.c;
@@ -330,14 +341,16 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
       const float delta = fmaf(r.m, c, -mc);
       const float lz = logf(r.z);
       const float H = lz - kLn2 * r.a / r.z;
-      const bool acc = H <= g.bound;
       same &= g.pred[row] == r.idx ? 1 : 0;
       g.pred[row] = r.idx;
-      g.canvas[row] = acc ? r.idx
-                          : draw_token(g.seed, static_cast<uint32_t>(row), static_cast<uint32_t>(g.step),
-                                       static_cast<uint32_t>(g.block), kPurposeRenoise,
-                                       static_cast<uint32_t>(g.vocab));
-      if (g.accept) g.accept[row] = acc ? 1 : 0;
+      if (group) {
+        gH[row] = H;
+        gIdx[row] = r.idx;
+      } else {
+        const bool acc = H <= g.bound;
+        g.canvas[row] = acc ? r.idx : renoise_token(g, row);
+        if (g.accept) g.accept[row] = acc ? 1 : 0;
+      }
       if (g.entropy) g.entropy[row] = H;
       if (g.row_stats) {
         g.row_stats[2 * row] = r.m;
@@ -350,6 +363,57 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
   same = wave_min_i32(same);
   if (lane == 0) { shs[wave] = hs; shq[wave] = same; }
   __syncthreads();
+  if (group) {
+    // rank of each row in increasing (entropy, row) order; the rows' entropies in that order; one
+    // thread walks the running total; rows ranked below the count are accepted
+    int rk[kGroupMaxRows / kFinThreads];
+#pragma unroll
+    for (int i = 0; i < kGroupMaxRows / kFinThreads; ++i) {
+      const int row = tid + i * kFinThreads;
+      rk[i] = 0;
+      if (row < g.rows) {
+        const float h = gH[row];
+        int n = 0;
+        for (int j = 0; j < g.rows; ++j) {
+          const float o = gH[j];
+          n += (o < h || (o == h && j < row)) ? 1 : 0;
+        }
+        rk[i] = n;
+      }
+    }
+    __syncthreads();  // every rank is computed before gH is overwritten in rank order
+    float hv[kGroupMaxRows / kFinThreads];
+#pragma unroll
+    for (int i = 0; i < kGroupMaxRows / kFinThreads; ++i) {
+      const int row = tid + i * kFinThreads;
+      hv[i] = row < g.rows ? gH[row] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGroupMaxRows / kFinThreads; ++i)
+      if (tid + i * kFinThreads < g.rows) gH[rk[i]] = hv[i];
+    __syncthreads();
+    if (tid == 0) {
+      float total = 0.f;
+      int K = 0;
+      for (int k = 0; k < g.rows; ++k) {
+        total += gH[k];
+        if (total > g.bound) break;
+        K = k + 1;
+      }
+      gK = K;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGroupMaxRows / kFinThreads; ++i) {
+      const int row = tid + i * kFinThreads;
+      if (row < g.rows) {
+        const bool acc = rk[i] < gK;
+        g.canvas[row] = acc ? gIdx[row] : renoise_token(g, row);
+        if (g.accept) g.accept[row] = acc ? 1 : 0;
+      }
+    }
+  }
   if (tid == 0) {
     float t = shs[0];
     int all = shq[0];
@@ -358,7 +422,8 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
     dg_stop_state st = *g.stop;
     st.stable_count = (g.step > 0 && all) ? st.stable_count + 1 : 0;
     st.mean_entropy = meanH;
-    st.stopped = (meanH < g.stop_thr && st.stable_count >= g.stable_needed) ? 1 : 0;
+    const bool confident = meanH < g.stop_thr, steady = st.stable_count >= g.stable_needed;
+    st.stopped = ((g.mode & DG_SCHED_STOP_EITHER) ? (confident || steady) : (confident && steady)) ? 1 : 0;
     st.steps_run = g.step + 1;
     *g.stop = st;
   }
@@ -421,6 +486,9 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
   g.bound = sc.entropy_bound;
   g.stop_thr = sc.stop_mean_entropy;
   g.stable_needed = sc.stable_needed;
+  g.mode = sc.mode;
+  if ((sc.mode & DG_SCHED_ACCEPT_GROUP) && rows > kGroupMaxRows)
+    return fail(DG_ERR_UNSUPPORTED, "group acceptance: at most 4096 rows");
   g.seed = sc.seed;
   g.step = step;
   g.block = block;

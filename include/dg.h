@@ -83,7 +83,18 @@ typedef struct dg_sched {
   float stop_mean_entropy;  /* stop needs canvas mean entropy < this ... */
   int32_t stable_needed;    /* ... and this many consecutive equal predictions */
   uint64_t seed;            /* Philox key */
+  int32_t mode;             /* 0, or DG_SCHED_* flags: the sampler variants below */
+  int32_t reserved;         /* 0 */
 } dg_sched;
+
+/* Sampler variants ([P3] "Inference mechanism"), flags of dg_sched.mode:
+ * DG_SCHED_STOP_EITHER: the canvas stops when either condition holds (mean
+ *   entropy below the threshold, or stable_needed consecutive equal
+ *   predictions) instead of both;
+ * DG_SCHED_ACCEPT_GROUP: the accepted positions are a group: taken in
+ *   increasing entropy (lower position first on ties), the longest run whose
+ *   running entropy total (float, in that order) stays <= entropy_bound. */
+enum { DG_SCHED_STOP_EITHER = 1, DG_SCHED_ACCEPT_GROUP = 2 };
 
 /* Device-resident stop state, 16 bytes, updated by dg_sample_canvas. */
 typedef struct dg_stop_state {

@@ -212,3 +212,76 @@ def test_sampler_full_size_planted_logits(L):
         assert abs(s["mean_entropy"] - res.mean_entropy) <= 1e-4
         prev, stable = res.pred, res.stable
         del logits
+
+
+# ------------------------------------------------------------- sampler variants
+
+def _graded_logits(rows, V, seed):
+    """Rows with one planted peak of graded height: entropies spread from ~0 to well above the
+    bound, so the group acceptance has a clear boundary."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, size=(rows, V)).astype(np.float32)
+    heights = np.linspace(9.0, 2.0, rows)
+    rng.shuffle(heights)
+    x[np.arange(rows), rng.integers(0, V, size=rows)] += heights.astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("rows,V,dtype", [(256, 4096, "bf16"), (64, 2056, "f32"), (5, 1000, "bf16")])
+def test_group_acceptance_matches_oracle(L, rows, V, dtype):
+    lib, rt = L
+    announce(f"group acceptance rows={rows} V={V} {dtype}")
+    x = _graded_logits(rows, V, rows + V)
+    t = torch.from_numpy(x)
+    logits = (t.to(torch.bfloat16) if dtype == "bf16" else t).cuda()
+    lg = to_f64(logits)
+    step, block, seed = 3, 1, 17
+    T = temperature(step, Schedule())
+    H = sample_step(lg, step, block, Schedule(seed=seed), None, 0, T=T).entropy
+    # put the bound midway between two running totals of the increasing-entropy order, far (in
+    # units of the 1e-3 entropy tolerance) from both, so the accepted count is unambiguous
+    order = np.lexsort((np.arange(rows), H))
+    tot = np.cumsum(H[order])
+    gaps = [(tot[k + 1] - tot[k], k) for k in range(rows - 1) if tot[k + 1] - tot[k] > 8e-3 * (k + 2)]
+    assert gaps, "no clear boundary in the test rows"
+    k = gaps[len(gaps) // 2][1]
+    bound = float((tot[k] + tot[k + 1]) / 2)
+    sched = Schedule(seed=seed, entropy_bound=bound, accept_cumulative=True)
+    csched = lib.make_sched(seed=seed, entropy_bound=bound, mode=lib.DG_SCHED_ACCEPT_GROUP)
+    res = sample_step(lg, step, block, sched, None, 0)
+    assert res.accept.sum() == k + 1
+    st = rt.SamplerState(rows, V)
+    st.init(csched, block)
+    st.sample(logits, csched, step, block)
+    torch.cuda.synchronize()
+    assert np.abs(to_f64(st.entropy) - res.entropy).max() <= 1e-3
+    assert np.array_equal(st.pred.cpu().numpy(), res.pred)
+    assert np.array_equal(st.accept.cpu().numpy().astype(bool), res.accept)
+    assert np.array_equal(st.canvas.cpu().numpy(), res.next_canvas)
+
+
+@pytest.mark.parametrize("confident,changing,expect_stop", [(True, True, True), (False, False, True),
+                                                            (False, True, False), (True, False, True)])
+def test_either_stop_matches_oracle(L, confident, changing, expect_stop):
+    lib, rt = L
+    announce(f"either stop confident={confident} changing={changing}")
+    C, V = 32, 512
+    sched = Schedule(max_steps=6, seed=4, stop_either=True)
+    csched = lib.make_sched(max_steps=6, seed=4, mode=lib.DG_SCHED_STOP_EITHER)
+    height = 40.0 if confident else 0.05
+
+    def lgt(s):
+        a = np.zeros((C, V), np.float32)
+        a[np.arange(C), (np.arange(C) * 3 + (s if changing else 0)) % V] = height
+        return a
+
+    tr = denoise_block(lambda s, c, p, t: lgt(s).astype(np.float64), sched, 0, C, V)
+    assert tr.stopped == expect_stop
+    st = rt.SamplerState(C, V)
+    st.init(csched, 0)
+    for s in range(6):
+        st.sample(torch.from_numpy(lgt(s)).cuda(), csched, s, 0)
+    torch.cuda.synchronize()
+    state = st.stop_state()
+    assert state["stopped"] == int(tr.stopped) and state["steps_run"] == tr.steps
+    assert np.array_equal(st.pred.cpu().numpy(), tr.block_ids)
