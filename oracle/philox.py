@@ -29,6 +29,7 @@ MASK32 = 0xFFFFFFFF
 
 PURPOSE_INIT = 0
 PURPOSE_RENOISE = 1
+PURPOSE_GUMBEL = 2  # categorical sampling: purpose word 2 + 4 * (token // 4), output word token % 4
 
 
 def philox4x32_10(ctr, key):
@@ -82,3 +83,18 @@ def init_canvas(seed: int, canvas: int, block: int, vocab: int):
     uniformly random tokens); [P4] "Reverse diffusion process", step 1.
     """
     return draw_tokens(seed, np.arange(canvas), 0, block, PURPOSE_INIT, vocab)
+
+
+def uniform24(seed: int, positions, step: int, block: int, vocab: int):
+    """[len(positions), vocab] uniforms in (0, 1) for categorical sampling: token v of position i
+    takes output word v % 4 of the counter (i, step, block, 2 + 4 (v // 4)), keeps its top 24 bits
+    r and maps them to (r + 1/2) / 2**24 (exactly representable in float32 and float64)."""
+    pos = np.asarray(positions, dtype=np.uint64)
+    ng = (vocab + 3) // 4
+    P = np.repeat(pos[:, None], ng, axis=1)
+    G = np.repeat(np.arange(ng, dtype=np.uint64)[None, :], pos.size, axis=0)
+    z = np.zeros_like(P)
+    words = philox4x32_10((P, z + np.uint64(step), z + np.uint64(block), np.uint64(PURPOSE_GUMBEL) + np.uint64(4) * G),
+                          seed_key(seed))
+    w = np.stack(words, axis=-1).reshape(pos.size, ng * 4)[:, :vocab]
+    return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)

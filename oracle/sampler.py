@@ -32,6 +32,12 @@ Variants the pages also describe, each behind a Schedule flag (defaults off):
   entropy (lower position first on ties) and the group accepted is the
   longest such run whose summed entropy stays within the bound (it may be
   empty); the rest are re-noised.
+* categorical: [P4] "Standard sampling settings" explains the temperature
+  schedule as exploring early and settling late, i.e. sampling from the
+  tempered distribution. Reading taken: an accepted position keeps a token
+  drawn from softmax(l / T) (Gumbel-max: argmax_v l_v / T - ln(-ln u_v), u
+  from Philox, philox.uniform24) instead of the argmax; the predictions the
+  stop rule compares, and the committed block, stay the argmax.
 """
 from __future__ import annotations
 
@@ -54,6 +60,7 @@ class Schedule:
     seed: int = 0
     stop_either: bool = False
     accept_cumulative: bool = False
+    categorical: bool = False
 
 
 def temperature(step: int, sched: Schedule) -> float:
@@ -96,6 +103,16 @@ def cumulative_accept(H: np.ndarray, bound: float) -> np.ndarray:
     return accept
 
 
+def gumbel_sample(logits: np.ndarray, T: float, seed: int, step: int, block: int) -> np.ndarray:
+    """One token per row drawn from softmax(l / T) by the Gumbel-max rule: the index of the largest
+    l_v / T + g_v, g_v = -ln(-ln u_v), u_v from philox.uniform24 (lowest index on ties)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    C, V = logits.shape
+    u = philox.uniform24(seed, np.arange(C), step, block, V)
+    g = -np.log(-np.log(u))
+    return np.argmax(logits / np.float64(T) + g, axis=-1).astype(np.int64)
+
+
 @dataclass
 class StepResult:
     entropy: np.ndarray      # [C] float64
@@ -121,7 +138,8 @@ def sample_step(logits: np.ndarray, step: int, block: int, sched: Schedule,
     pred = np.argmax(logits, axis=-1).astype(np.int64)  # first maximum = lowest index
     accept = cumulative_accept(H, sched.entropy_bound) if sched.accept_cumulative else H <= sched.entropy_bound
     noise = philox.draw_tokens(sched.seed, np.arange(C), step, block, philox.PURPOSE_RENOISE, V)
-    nxt = np.where(accept, pred, noise)
+    keep = gumbel_sample(logits, T, sched.seed, step, block) if sched.categorical else pred
+    nxt = np.where(accept, keep, noise)
     meanH = float(H.mean())
     if step > 0 and prev_pred is not None and np.array_equal(pred, prev_pred):
         stable = stable + 1

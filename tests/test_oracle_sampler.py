@@ -259,3 +259,63 @@ def test_group_acceptance_in_a_sampling_step():
     assert res.accept.tolist() == [True, False, True, False, False, True]
     noise = philox.draw_tokens(3, np.arange(C), 4, 1, philox.PURPOSE_RENOISE, V)
     assert np.array_equal(res.next_canvas, np.where(res.accept, res.pred, noise))
+
+
+def test_categorical_frequencies_follow_the_tempered_softmax():
+    # the same four-token row at 4096 positions x 4 steps: Gumbel-max draws must follow softmax(l / T)
+    from scipy import stats
+    from oracle.sampler import gumbel_sample
+    l = np.array([0.0, 1.0, 2.0, 0.5])
+    T = 0.8
+    rows = np.tile(l, (4096, 1))
+    counts = np.zeros(4)
+    for step in range(4):
+        counts += np.bincount(gumbel_sample(rows, T, 21, step, 3), minlength=4)
+    p = np.exp(l / T) / np.exp(l / T).sum()
+    chi2 = ((counts - counts.sum() * p) ** 2 / (counts.sum() * p)).sum()
+    assert stats.chi2.sf(chi2, 3) > 1e-3, (counts / counts.sum(), p)
+    # the untempered distribution is clearly rejected (the draws do depend on T)
+    q = np.exp(l) / np.exp(l).sum()
+    chi2q = ((counts - counts.sum() * q) ** 2 / (counts.sum() * q)).sum()
+    assert stats.chi2.sf(chi2q, 3) < 1e-6
+
+
+def test_categorical_limits():
+    from oracle.sampler import gumbel_sample
+    rng = np.random.default_rng(2)
+    logits = rng.normal(0, 3, size=(64, 300))
+    # T -> 0: the draw is the argmax
+    assert np.array_equal(gumbel_sample(logits, 1e-6, 7, 0, 0), np.argmax(logits, axis=1))
+    # a one-hot row always draws its peak
+    oh = np.full((16, 300), -1000.0)
+    oh[np.arange(16), np.arange(16) * 7] = 0.0
+    for step in range(5):
+        assert np.array_equal(gumbel_sample(oh, 0.8, 7, step, 1), np.arange(16) * 7)
+    # draws differ between steps at a flat row (fresh noise every step)
+    flat = np.zeros((64, 300))
+    draws = [gumbel_sample(flat, 0.8, 7, s, 0) for s in range(3)]
+    assert not np.array_equal(draws[0], draws[1]) and not np.array_equal(draws[1], draws[2])
+
+
+def test_uniform24_is_uniform_on_a_24_bit_grid():
+    from scipy import stats
+    u = philox.uniform24(99, np.arange(64), 5, 2, 1000).ravel()
+    k = u * (1 << 24) - 0.5
+    assert np.array_equal(k, np.round(k)) and k.min() >= 0 and k.max() < (1 << 24)
+    assert stats.kstest(u, "uniform").pvalue > 1e-3
+
+
+def test_categorical_step_keeps_draws_only_where_accepted():
+    from oracle.sampler import gumbel_sample
+    C, V = 8, 64
+    logits = np.zeros((C, V))
+    logits[0:4, 5] = 1000.0                     # confident rows
+    logits[4:, :] = np.linspace(0, 1, V)       # flat-ish rows
+    sched = Schedule(seed=5, categorical=True)
+    res = sample_step(logits, 2, 1, sched, None, 0)
+    T = temperature(2, sched)
+    draws = gumbel_sample(logits, T, 5, 2, 1)
+    noise = philox.draw_tokens(5, np.arange(C), 2, 1, philox.PURPOSE_RENOISE, V)
+    assert res.accept.tolist() == [True] * 4 + [False] * 4
+    assert np.array_equal(res.next_canvas, np.where(res.accept, draws, noise))
+    assert np.array_equal(res.pred, np.argmax(logits, axis=1))
