@@ -129,7 +129,7 @@ def _check(name: str, rc: int) -> int:
     return rc
 
 
-DG_SCHED_STOP_EITHER, DG_SCHED_ACCEPT_GROUP = 1, 2
+DG_SCHED_STOP_EITHER, DG_SCHED_ACCEPT_GROUP, DG_SCHED_SAMPLE = 1, 2, 4
 
 
 def make_sched(max_steps=48, t_start=0.8, t_end=0.4, entropy_bound=0.1, stop_mean_entropy=0.005,

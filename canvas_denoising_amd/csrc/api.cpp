@@ -48,7 +48,8 @@ int check_sched(const dg_sched* s, int step) {
   if (!isfinite(s->entropy_bound) || !isfinite(s->stop_mean_entropy))
     return fail(DG_ERR_INVALID, "entropy thresholds must be finite");
   if (s->stable_needed < 0) return fail(DG_ERR_INVALID, "stable_needed must be >= 0");
-  if ((s->mode & ~(DG_SCHED_STOP_EITHER | DG_SCHED_ACCEPT_GROUP)) != 0) return fail(DG_ERR_INVALID, "unknown sched mode flag");
+  if ((s->mode & ~(DG_SCHED_STOP_EITHER | DG_SCHED_ACCEPT_GROUP | DG_SCHED_SAMPLE)) != 0)
+    return fail(DG_ERR_INVALID, "unknown sched mode flag");
   if (step < 0 || step >= s->max_steps) return fail(DG_ERR_INVALID, "step outside [0, max_steps)");
   return DG_OK;
 }

@@ -14,7 +14,8 @@
 
 namespace dg {
 
-enum : uint32_t { kPurposeInit = 0, kPurposeRenoise = 1 };
+// purpose 2: categorical sampling; token v uses purpose word 2 + 4 (v / 4) and output word v % 4
+enum : uint32_t { kPurposeInit = 0, kPurposeRenoise = 1, kPurposeGumbel = 2 };
 
 struct PhiloxOut { uint32_t w0, w1, w2, w3; };
 

@@ -81,6 +81,22 @@ __device__ inline void rec_wave_merge(Rec& w, float c) {
   rec_merge(w, rec_xrow32(w), c);
 }
 
+// Categorical sampling: the best Gumbel-perturbed score of a chunk and its (lowest) index.
+struct GRec {
+  float s;
+  int idx;
+};
+
+__device__ inline void gmax(float& bs, int& bi, float os, int oi) {
+  if (os > bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
+}
+
+// -ln(-ln u) for the 24-bit uniform u = (r >> 8 + 1/2) / 2^24 of Philox word r
+__device__ inline float gumbel_of(uint32_t r) {
+  const float u = (static_cast<float>(r >> 8) + 0.5f) * 5.9604644775390625e-8f;
+  return -logf(-logf(u));
+}
+
 constexpr int kSampThreads = 256;
 constexpr int kVec = 8;      // elements per 16-byte (bf16) / 32-byte (fp32) group
 constexpr int kUnroll = 4;   // groups per thread per batch
@@ -173,6 +189,7 @@ struct SampleArgs {
   float bound, stop_thr;
   int stable_needed;
   int mode;  // DG_SCHED_* flags
+  float inv_t;  // 1 / T (categorical sampling)
   uint64_t seed;
   int step, block;
   int32_t* canvas;
@@ -181,11 +198,29 @@ struct SampleArgs {
   float* entropy;
   float* row_stats;
   dg_stop_state* stop;
-  Rec* recs;  // scratch [rows][splits]
+  Rec* recs;    // scratch [rows][splits]
+  GRec* grecs;  // scratch [rows][splits] (categorical sampling)
 };
 
+// Gumbel scores of the 8 tokens e0 .. e0+7 (e0 % 8 == 0) of `row`, folded into (bs, bi)
+__device__ inline void gumbel_fold8(const SampleArgs& g, int row, int64_t e0, const float* v, float& bs, int& bi) {
+  const uint32_t k0 = static_cast<uint32_t>(g.seed), k1 = static_cast<uint32_t>(g.seed >> 32);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t q = static_cast<uint32_t>((e0 >> 2) + h);
+    const PhiloxOut o = philox4x32_10(static_cast<uint32_t>(row), static_cast<uint32_t>(g.step),
+                                      static_cast<uint32_t>(g.block), kPurposeGumbel + 4u * q, k0, k1);
+    const uint32_t w[4] = {o.w0, o.w1, o.w2, o.w3};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sc = fmaf(v[h * 4 + j], g.inv_t, gumbel_of(w[j]));
+      if (sc > bs) { bs = sc; bi = static_cast<int>(e0 + h * 4 + j); }  // ascending positions: first max kept
+    }
+  }
+}
+
 // grid (splits, rows)
-template <typename T, bool kVecPath>
+template <typename T, bool kVecPath, bool CAT>
 __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
   if (g.stop->stopped) return;
   const int sp = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -203,6 +238,14 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
     const int64_t nb = (end - begin) / kBatch;
     const T* tp = p + begin + static_cast<int64_t>(tid) * kVec;
     int64_t first = -1;  // batch where this thread's running max first appeared
+    float gs = -INFINITY;  // categorical: best Gumbel score of this thread and its index
+    int gi = 0x7FFFFFFF;
+    auto gumbel_batch = [&](const float* v, int64_t b) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        gumbel_fold8(g, row, begin + b * kBatch + static_cast<int64_t>(tid) * kVec + u * kSampThreads * kVec,
+                     v + u * kVec, gs, gi);
+    };
     Raw<T> qa, qb;
     if (nb > 0) qa.load(tp);
     for (int64_t b = 0; b < nb; b += 2) {
@@ -211,12 +254,14 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
         float v[kUnroll * kVec];
         qa.unpack(v);
         if (fold<kUnroll * kVec>(v, c, r)) first = b;
+        if constexpr (CAT) gumbel_batch(v, b);
       }
       if (b + 1 < nb) {
         if (b + 2 < nb) qa.load(tp + (b + 2) * kBatch);
         float v[kUnroll * kVec];
         qb.unpack(v);
         if (fold<kUnroll * kVec>(v, c, r)) first = b + 1;
+        if constexpr (CAT) gumbel_batch(v, b + 1);
       }
     }
     // tail: whole groups of 8 (vocab % 8 == 0 on this path), index tracked directly
@@ -238,6 +283,24 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
       for (int j = 1; j < kVec; ++j)
         if (v[j] > bm) { bm = v[j]; bj = j; }
       if (fold<kVec>(v, c, r)) { first = -1; tail_idx = static_cast<int>(e0 + bj); }
+      if constexpr (CAT) gumbel_fold8(g, row, e0, v, gs, gi);
+    }
+    if constexpr (CAT) {  // the chunk's best Gumbel score: wave (DPP / row swaps), then the 4 waves
+      gmax(gs, gi, dpp_f32<kDppXor1>(gs), static_cast<int>(dpp_u32<kDppXor1>(static_cast<uint32_t>(gi))));
+      gmax(gs, gi, dpp_f32<kDppXor2>(gs), static_cast<int>(dpp_u32<kDppXor2>(static_cast<uint32_t>(gi))));
+      gmax(gs, gi, dpp_f32<kDppHalfMirror>(gs), static_cast<int>(dpp_u32<kDppHalfMirror>(static_cast<uint32_t>(gi))));
+      gmax(gs, gi, dpp_f32<kDppMirror>(gs), static_cast<int>(dpp_u32<kDppMirror>(static_cast<uint32_t>(gi))));
+      gmax(gs, gi, xrow16_f32(gs), static_cast<int>(xrow16_u32(static_cast<uint32_t>(gi))));
+      gmax(gs, gi, xrow32_f32(gs), static_cast<int>(xrow32_u32(static_cast<uint32_t>(gi))));
+      __shared__ GRec shg[kSampThreads / 64];
+      if (lane == 0) shg[wave] = GRec{gs, gi};
+      __syncthreads();
+      if (tid == 0) {
+        GRec best = shg[0];
+#pragma unroll
+        for (int i = 1; i < kSampThreads / 64; ++i) gmax(best.s, best.idx, shg[i].s, shg[i].idx);
+        g.grecs[static_cast<int64_t>(row) * g.splits + sp] = best;
+      }
     }
     // wave / workgroup merge of (m, z, a) in a fixed order
     Rec w = r;
@@ -314,6 +377,7 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
   __shared__ int32_t gIdx[kGroupMaxRows];
   __shared__ int gK;
   const bool group = (g.mode & DG_SCHED_ACCEPT_GROUP) != 0;
+  const bool cat = (g.mode & DG_SCHED_SAMPLE) != 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = tid % kFinParts;
   const float c = g.c;
@@ -334,6 +398,21 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
     for (int i = 1; i < kFinRecs; ++i) rec_merge(r, buf[i], c);
     rec_merge(r, rec_dpp<kDppXor1>(r), c);
     rec_merge(r, rec_dpp<kDppXor2>(r), c);
+    int keep_cat = 0;  // categorical: the row's drawn token (records merged in split order, then the quad)
+    if (cat) {
+      float bs = -INFINITY;
+      int bi = 0x7FFFFFFF;
+      for (int i = 0; i < kFinRecs; ++i) {
+        const int sp = part + kFinParts * i;
+        if (valid && sp < g.splits) {
+          const GRec o = g.grecs[static_cast<int64_t>(row) * g.splits + sp];
+          gmax(bs, bi, o.s, o.idx);
+        }
+      }
+      gmax(bs, bi, dpp_f32<kDppXor1>(bs), static_cast<int>(dpp_u32<kDppXor1>(static_cast<uint32_t>(bi))));
+      gmax(bs, bi, dpp_f32<kDppXor2>(bs), static_cast<int>(dpp_u32<kDppXor2>(static_cast<uint32_t>(bi))));
+      keep_cat = bi;
+    }
     if (valid && part == 0) {
       // The fold evaluates u = fma(l, c, -round(m c)): every u of a chunk carries the residual
       // delta = m c - round(m c); it cancels in H but not in ln Z.
@@ -343,12 +422,13 @@ __global__ __launch_bounds__(kFinThreads) void sample_finalize_kernel(SampleArgs
       const float H = lz - kLn2 * r.a / r.z;
       same &= g.pred[row] == r.idx ? 1 : 0;
       g.pred[row] = r.idx;
+      const int keep = cat ? keep_cat : r.idx;  // the token an accepted position keeps
       if (group) {
         gH[row] = H;
-        gIdx[row] = r.idx;
+        gIdx[row] = keep;
       } else {
         const bool acc = H <= g.bound;
-        g.canvas[row] = acc ? r.idx : renoise_token(g, row);
+        g.canvas[row] = acc ? keep : renoise_token(g, row);
         if (g.accept) g.accept[row] = acc ? 1 : 0;
       }
       if (g.entropy) g.entropy[row] = H;
@@ -457,9 +537,14 @@ static SplitPlan plan_splits(int64_t rows, int64_t vocab) {
   return {s, chunk};
 }
 
-size_t sample_workspace_bytes(int64_t rows, int64_t vocab) {
+static size_t recs_bytes(int64_t rows, int64_t vocab) {
   const SplitPlan p = plan_splits(rows, vocab);
   return (static_cast<size_t>(rows * p.splits) * sizeof(Rec) + 255) / 256 * 256;
+}
+
+size_t sample_workspace_bytes(int64_t rows, int64_t vocab) {
+  const SplitPlan p = plan_splits(rows, vocab);
+  return recs_bytes(rows, vocab) + (static_cast<size_t>(rows * p.splits) * sizeof(GRec) + 255) / 256 * 256;
 }
 
 int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
@@ -489,22 +574,29 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
   g.mode = sc.mode;
   if ((sc.mode & DG_SCHED_ACCEPT_GROUP) && rows > kGroupMaxRows)
     return fail(DG_ERR_UNSUPPORTED, "group acceptance: at most 4096 rows");
+  if ((sc.mode & DG_SCHED_SAMPLE) && vocab % kVec != 0)
+    return fail(DG_ERR_UNSUPPORTED, "categorical sampling: vocab must be a multiple of 8");
   g.seed = sc.seed;
   g.step = step;
   g.block = block;
   g.canvas = canvas; g.pred = pred; g.accept = accept; g.entropy = entropy; g.row_stats = row_stats; g.stop = stop;
   g.recs = static_cast<Rec*>(ws);
+  g.grecs = reinterpret_cast<GRec*>(static_cast<char*>(ws) + recs_bytes(rows, vocab));
+  g.inv_t = 1.0f / temp;
   dim3 grid(static_cast<unsigned>(p.splits), static_cast<unsigned>(rows));
   {
     ProfScope ps("sample_partial", stream, true);
     const bool vec = vocab % kVec == 0;
+    const bool cat = (sc.mode & DG_SCHED_SAMPLE) != 0;
     const dim3 block(kSampThreads);
     if (dtype == DG_BF16) {
-      if (vec) launch_timed(ps, sample_kernel<bf16_t, true>, grid, block, stream, g);
-      else launch_timed(ps, sample_kernel<bf16_t, false>, grid, block, stream, g);
+      if (cat) launch_timed(ps, sample_kernel<bf16_t, true, true>, grid, block, stream, g);
+      else if (vec) launch_timed(ps, sample_kernel<bf16_t, true, false>, grid, block, stream, g);
+      else launch_timed(ps, sample_kernel<bf16_t, false, false>, grid, block, stream, g);
     } else {
-      if (vec) launch_timed(ps, sample_kernel<float, true>, grid, block, stream, g);
-      else launch_timed(ps, sample_kernel<float, false>, grid, block, stream, g);
+      if (cat) launch_timed(ps, sample_kernel<float, true, true>, grid, block, stream, g);
+      else if (vec) launch_timed(ps, sample_kernel<float, true, false>, grid, block, stream, g);
+      else launch_timed(ps, sample_kernel<float, false, false>, grid, block, stream, g);
     }
   }
   DG_LAUNCH_CHECK("sample_kernel");

@@ -93,8 +93,14 @@ typedef struct dg_sched {
  *   predictions) instead of both;
  * DG_SCHED_ACCEPT_GROUP: the accepted positions are a group: taken in
  *   increasing entropy (lower position first on ties), the longest run whose
- *   running entropy total (float, in that order) stays <= entropy_bound. */
-enum { DG_SCHED_STOP_EITHER = 1, DG_SCHED_ACCEPT_GROUP = 2 };
+ *   running entropy total (float, in that order) stays <= entropy_bound;
+ * DG_SCHED_SAMPLE: ([P4] "Standard sampling settings": the temperature
+ *   explores early) an accepted position keeps a token drawn from
+ *   softmax(l / T) by Gumbel-max, argmax_v l_v / T - ln(-ln u_v), instead of
+ *   the argmax; u_v = (r >> 8 + 1/2) / 2^24 with r = output word v % 4 of
+ *   Philox(seed; i, step, block, 2 + 4 (v / 4)). pred (the stop rule's
+ *   predictions) stays the argmax. Needs vocab % 8 == 0. */
+enum { DG_SCHED_STOP_EITHER = 1, DG_SCHED_ACCEPT_GROUP = 2, DG_SCHED_SAMPLE = 4 };
 
 /* Device-resident stop state, 16 bytes, updated by dg_sample_canvas. */
 typedef struct dg_stop_state {

@@ -285,3 +285,72 @@ def test_either_stop_matches_oracle(L, confident, changing, expect_stop):
     state = st.stop_state()
     assert state["stopped"] == int(tr.stopped) and state["steps_run"] == tr.steps
     assert np.array_equal(st.pred.cpu().numpy(), tr.block_ids)
+
+
+@pytest.mark.parametrize("rows,V,dtype", [(256, 4096, "bf16"), (37, 2056, "f32"), (8, 262144, "bf16")])
+def test_categorical_draws_match_oracle(L, rows, V, dtype):
+    """Every position accepted (bound far above any entropy), so the canvas holds each row's
+    Gumbel-max draw. Rows whose best two perturbed scores (oracle, float64) are within 1e-4 of
+    each other are only checked for validity: the GPU's pick must score within 1e-4 of the best."""
+    from oracle.sampler import gumbel_sample
+    lib, rt = L
+    announce(f"categorical rows={rows} V={V} {dtype}")
+    logits = make_logits(rows, V, rows * 7 + V, dtype)
+    lg = to_f64(logits)
+    step, block, seed = 6, 2, 77
+    sched = Schedule(seed=seed, entropy_bound=1e9, categorical=True)
+    csched = lib.make_sched(seed=seed, entropy_bound=1e9, mode=lib.DG_SCHED_SAMPLE)
+    st = rt.SamplerState(rows, V)
+    st.init(csched, block)
+    st.sample(logits, csched, step, block)
+    torch.cuda.synchronize()
+    T = temperature(step, sched)
+    res = sample_step(lg, step, block, sched, None, 0)
+    assert res.accept.all()
+    assert np.array_equal(st.pred.cpu().numpy(), res.pred)
+    got = st.canvas.cpu().numpy().astype(np.int64)
+    want = gumbel_sample(lg, T, seed, step, block)
+    assert np.array_equal(want, res.next_canvas)
+    u = philox.uniform24(seed, np.arange(rows), step, block, V)
+    score = lg / T - np.log(-np.log(u))
+    top2 = np.sort(score, axis=1)[:, -2:]
+    clear = top2[:, 1] - top2[:, 0] > 1e-4 * np.maximum(1.0, np.abs(top2[:, 1]))
+    assert clear.mean() > 0.9
+    assert np.array_equal(got[clear], want[clear])
+    best = score.max(axis=1)
+    picked = score[np.arange(rows), got]
+    assert np.all(best - picked <= 1e-4 * np.maximum(1.0, np.abs(best)))
+
+
+def test_group_acceptance_with_categorical_draws(L):
+    from oracle.sampler import gumbel_sample
+    lib, rt = L
+    announce("group + categorical")
+    rows, V = 64, 4096
+    x = _graded_logits(rows, V, 5)
+    logits = torch.from_numpy(x).cuda()
+    lg = to_f64(logits)
+    step, block, seed = 2, 0, 31
+    T = temperature(step, Schedule())
+    H = sample_step(lg, step, block, Schedule(seed=seed), None, 0, T=T).entropy
+    order = np.lexsort((np.arange(rows), H))
+    tot = np.cumsum(H[order])
+    gaps = [k for k in range(rows - 1) if tot[k + 1] - tot[k] > 8e-3 * (k + 2)]
+    k = gaps[len(gaps) // 2]
+    bound = float((tot[k] + tot[k + 1]) / 2)
+    sched = Schedule(seed=seed, entropy_bound=bound, accept_cumulative=True, categorical=True)
+    csched = lib.make_sched(seed=seed, entropy_bound=bound, mode=lib.DG_SCHED_ACCEPT_GROUP | lib.DG_SCHED_SAMPLE)
+    res = sample_step(lg, step, block, sched, None, 0)
+    st = rt.SamplerState(rows, V)
+    st.init(csched, block)
+    st.sample(logits, csched, step, block)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.accept.cpu().numpy().astype(bool), res.accept)
+    # accepted rows here are peaked (low entropy): their draws are unambiguous
+    draws = gumbel_sample(lg, T, seed, step, block)
+    u = philox.uniform24(seed, np.arange(rows), step, block, V)
+    score = lg / T - np.log(-np.log(u))
+    top2 = np.sort(score, axis=1)[:, -2:]
+    assert np.all((top2[:, 1] - top2[:, 0])[res.accept] > 1e-3)
+    assert np.array_equal(st.canvas.cpu().numpy(), res.next_canvas)
+    assert np.array_equal(res.next_canvas[res.accept], draws[res.accept])
