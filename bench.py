@@ -2,6 +2,7 @@
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|copy] [--no-cpu-baseline]
+                    [--sampler-mode M]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
 workload's hot path over one batch of synthetic input that is already
@@ -68,7 +69,7 @@ def bench_sampler(args):
     from canvas_denoising_amd.runtime import SamplerState
 
     rows, V, S = 256, 262144, 48
-    sched = L.make_sched(max_steps=S, seed=0)
+    sched = L.make_sched(max_steps=S, seed=0, mode=args.sampler_mode)
     log(f"[bench] generating {S} logits buffers {rows}x{V} bf16")
     bufs = []
     for s in range(S):
@@ -123,7 +124,7 @@ def bench_sampler(args):
         "data": "synthetic",
         "config": {"workload": "sampler-only: bf16 logits 256x262144, N(0,3)-like background, +12 peak in 70% "
                                "of rows, 48-step linear 0.8->0.4 schedule, 48 rotating buffers",
-                   "canvas": rows, "vocab": V, "max_steps": S,
+                   "canvas": rows, "vocab": V, "max_steps": S, "sampler_mode": args.sampler_mode,
                    "canvas_tokens_per_s": steps_per_s * rows,
                    "kernels_us": {k: v["avg_us"] for k, v in prof.items()},
                    "stopped_at_end": stop["stopped"]},
@@ -390,6 +391,8 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="full")
     ap.add_argument("--layers", type=int, default=30, help="layers of the full workload (30 = the benchmark)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sampler-mode", type=int, default=0,
+                    help="sampler workload: dg_sched.mode flags (1 either-stop, 2 group acceptance, 4 categorical)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -91,10 +91,13 @@ __device__ inline void gmax(float& bs, int& bi, float os, int oi) {
   if (os > bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
 }
 
-// -ln(-ln u) for the 24-bit uniform u = (r >> 8 + 1/2) / 2^24 of Philox word r
+// -ln(-ln u) for the 24-bit uniform u = (r >> 8 + 1/2) / 2^24 of Philox word r, with the hardware
+// base-2 logarithm (u and -ln u are normal floats here: u >= 2^-25, -ln u >= 2^-25)
 __device__ inline float gumbel_of(uint32_t r) {
+  constexpr float kLn2f = 0.693147180559945309f;
   const float u = (static_cast<float>(r >> 8) + 0.5f) * 5.9604644775390625e-8f;
-  return -logf(-logf(u));
+  const float e = -__builtin_amdgcn_logf(u) * kLn2f;  // -ln u > 0
+  return -__builtin_amdgcn_logf(e) * kLn2f;
 }
 
 constexpr int kSampThreads = 256;
