@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|copy] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|copy] [--no-cpu-baseline]
                     [--sampler-mode M]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
@@ -358,6 +358,77 @@ def cpu_baseline_full(d, prompt, budget_s):
                       f"{C}; host cores {cores}, BLAS threads {blas}"}
 
 
+def bench_blockar(args):
+    """Block-autoregressive generation: a 32768-token prompt prefilled (timed separately), then 8
+    canvases of 256, each denoised until its two-fold stop or 48 steps and committed to the KV cache
+    before the next one starts. Reports committed tokens/s over the 8 canvases (denoising + commits)."""
+    import torch
+    from canvas_denoising_amd import _lib as L
+    from canvas_denoising_amd import configs
+    from canvas_denoising_amd.runtime import Model, SamplerState
+
+    w = configs.block_ar_bf16()
+    d = w.desc
+    C, V, S = d.canvas, d.vocab, w.max_steps
+    log(f"[bench] model {d.n_layers} layers, KV capacity {w.capacity}")
+    model = Model(d, w.capacity, seed=0)
+    prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
+    L.dg_synth_uniform_ids(5, 10, w.prompt, V, prompt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    model.prefill(prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    log(f"[bench] prefill {w.prompt} tokens: {prefill_s:.2f} s")
+    sched = L.make_sched(max_steps=S, seed=0)
+    st = SamplerState(C, V)
+    logits = model.logits
+    block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
+
+    def canvas(block, max_steps, commit):
+        st.init(sched, block)
+        s = 0
+        while True:
+            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
+            model.denoise_step(st.canvas, s, *prev, logits=logits)
+            st.sample(logits, sched, s, block)
+            stop = st.stop.cpu()
+            s += 1
+            if int(stop[2]) or s == max_steps:
+                break
+        if commit:
+            block_ids.copy_(st.pred)
+            model.commit(block_ids)
+        return s, int(stop[2])
+
+    log(f"[bench] warmup {args.warmup} steps (not committed)")
+    canvas(0, max(1, args.warmup), False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    steps = stops = 0
+    for b in range(w.blocks):
+        n, stopped = canvas(b, S, True)
+        steps += n
+        stops += stopped
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "committed tokens/s (block-autoregressive, 8 canvases of 256)",
+        "value": w.blocks * C / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": dt * 1e3 / steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"block-AR: {d.n_layers} MoE layers as the full loop, prompt {w.prompt} prefilled "
+                               f"(untimed), {w.blocks} canvases of {C} denoised (<= {S} steps, two-fold stop) and "
+                               f"committed one after another, KV length {w.prompt} -> {w.prompt + w.blocks * C}; "
+                               "random-init weights",
+                   "denoise_steps_per_s": steps / dt, "canvas_tokens_per_s": steps * C / dt, "stops": stops,
+                   "prefill_tokens_per_s": w.prompt / prefill_s, "prefill_s": prefill_s},
+    }
+    model.close()
+    return out
+
+
 def bench_copy(args):
     """Plain device-to-device copy of a known size: the calibration run for HBM byte counters
     (FETCH_SIZE / WRITE_SIZE per launch divided by the bytes copied)."""
@@ -380,7 +451,7 @@ def bench_copy(args):
             "config": {"workload": f"calibration copy of {n} bytes per launch"}}
 
 
-WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "copy": bench_copy}
+WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "blockar": bench_blockar, "copy": bench_copy}
 
 
 def main():

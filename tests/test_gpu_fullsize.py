@@ -136,3 +136,80 @@ def test_full_step_sampled(libs):
     sc = to_f64(model.buffer(L.DG_BUF_SC, torch.float32, (C, D)))
     assert np.isfinite(sc).all() and np.abs(sc).max() > 0
     model.close()
+
+
+def _layer0_kv(ids, d):
+    """Layer-0 K and V of tokens `ids` at any positions: they depend only on the token itself
+    (RMSNorm of its embedding row times W_k / W_v; no positional encoding)."""
+    D, hd, H = d.d_model, d.head_dim, d.n_kv_heads
+    idx = (np.asarray(ids, dtype=np.uint64)[:, None] * np.uint64(D) + np.arange(D, dtype=np.uint64)[None, :]).ravel()
+    E = synthetic.bf16_bits_to_f32(synthetic.normal_bf16_bits(0, synthetic.TID_EMBED, idx, 0.02))
+    h = OM.rms_norm(E.astype(np.float64).reshape(len(ids), D), 1e-6)
+    n = H * hd * D
+    wk = synthetic.bf16_bits_to_f32(synthetic.normal_bf16_bits(0, synthetic.layer_tid(0, 1), n, 0.02))
+    wv = synthetic.bf16_bits_to_f32(synthetic.normal_bf16_bits(0, synthetic.layer_tid(0, 2), n, 0.02))
+    k = h @ wk.astype(np.float64).reshape(H * hd, D).T
+    v = h @ wv.astype(np.float64).reshape(H * hd, D).T
+    return k.reshape(len(ids), H, hd), v.reshape(len(ids), H, hd)
+
+
+def test_block_ar_full_size(libs):
+    """The block-autoregressive configuration at its full size: a 32768-token prompt, then canvases
+    of 256 committed one after another until the KV cache (32768 + 9 x 256 positions) is exactly full;
+    one more commit is refused. Checked: layer-0 K/V of sampled prompt and committed positions
+    (exact function of the token), the committed lengths, the sampler teacher-forced on the last
+    canvas's logits (exact), and the capacity error leaving the cache as it was."""
+    L, configs, runtime = libs
+    w = configs.block_ar_bf16()
+    d = w.desc
+    C, V = d.canvas, d.vocab
+    announce(f"block-AR full size: prompt {w.prompt}, capacity {w.capacity}")
+    model = runtime.Model(d, w.capacity, seed=0, sigma=0.02)
+    ids = synthetic.uniform_ids(5, synthetic.TID_PROMPT, w.prompt, V)
+    model.prefill(torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    assert model.length == w.prompt
+    rng = np.random.default_rng(4)
+    pos = np.sort(np.concatenate([[0, 1, w.prompt - 1], rng.choice(w.prompt, size=61, replace=False)]))
+    k_ref, v_ref = _layer0_kv(ids[pos], d)
+    K, Vc = model.kv_view()
+    p_t = torch.from_numpy(pos).cuda()
+    assert_close(to_f64(K[0][:, p_t].permute(1, 0, 2)), k_ref, 2e-2, "layer-0 K of prompt positions")
+    assert_close(to_f64(Vc[0][:, p_t].permute(1, 0, 2)), v_ref, 2e-2, "layer-0 V of prompt positions")
+    del K, Vc
+    sched = L.make_sched(max_steps=48, seed=0)
+    out = torch.empty(C, dtype=torch.int32, device="cuda")
+    n_fit = (w.capacity - w.prompt) // C
+    committed = []
+    for b in range(n_fit):
+        steps = model.generate_block(sched, b, out, commit=True)
+        torch.cuda.synchronize()
+        assert 1 <= steps <= 48
+        committed.append(out.cpu().numpy().copy())
+        assert model.length == w.prompt + (b + 1) * C
+    assert model.length == w.capacity
+    # the last canvas's final logits, sampler teacher-forced: exact discrete outputs
+    st = runtime.SamplerState(C, V)
+    st.init(sched, n_fit - 1)
+    st.sample(model.logits, sched, 47, n_fit - 1)
+    torch.cuda.synchronize()
+    res = OS.sample_step(to_f64(model.logits), 47, n_fit - 1, OS.Schedule(seed=0), None, 0)
+    assert np.array_equal(st.pred.cpu().numpy(), res.pred)
+    # committed blocks: layer-0 K/V at sampled positions of every block
+    K, Vc = model.kv_view()
+    for b, blk in enumerate(committed):
+        j = np.sort(rng.choice(C, size=8, replace=False))
+        k_ref, v_ref = _layer0_kv(blk[j].astype(np.int64), d)
+        p_t = torch.from_numpy(w.prompt + b * C + j).cuda()
+        assert_close(to_f64(K[0][:, p_t].permute(1, 0, 2)), k_ref, 2e-2, f"layer-0 K of block {b}")
+        assert_close(to_f64(Vc[0][:, p_t].permute(1, 0, 2)), v_ref, 2e-2, f"layer-0 V of block {b}")
+    del K, Vc
+    # the cache is full: the next canvas has no room and nothing changes
+    before = model.kv.clone()
+    with pytest.raises(L.DGError) as err:
+        model.generate_block(sched, n_fit, out, commit=True)
+    assert err.value.code == L.DG_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert model.length == w.capacity
+    assert torch.equal(model.kv, before)
+    model.close()
