@@ -2,7 +2,7 @@
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|copy] [--no-cpu-baseline]
-                    [--sampler-mode M]
+                    [--sampler-mode M] [--experts bf16|fp8]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
 workload's hot path over one batch of synthetic input that is already
@@ -19,6 +19,9 @@ resident in HBM:
   over a 256-token canvas with an 8192-token prompt in the KV cache:
   self-conditioning, 30 layers, LM head over 262144 tokens, the sampler,
   the 16-byte stop read-back and a block commit whenever a canvas stops.
+  ``--experts fp8`` runs it with the routed experts' weights stored as FP8
+  E4M3 with per-row scales (an opt-in mode at reduced weight precision,
+  reported under its own metric name, never as the bf16 figure).
 * ``copy``: a plain 1 GiB device copy, the calibration run for the HBM
   byte counters of the profiles.
 
@@ -185,6 +188,14 @@ def bench_full(args):
     capacity = w.prompt + (n_blocks + 1) * C
     log(f"[bench] model {d.n_layers} layers, weights {L.dg_weights_bytes(d) / 1e9:.1f} GB, KV capacity {capacity}")
     model = Model(d, capacity, seed=0)
+    fp8 = args.experts == "fp8"
+    if fp8:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        model.use_expert_fp8(True)
+        torch.cuda.synchronize()
+        log(f"[bench] FP8 experts: {L.dg_expert_fp8_bytes(d) / 1e9:.1f} GB quantized in {time.perf_counter() - t0:.2f} s")
+    gu_name = "expert_gateup_fp8" if fp8 else "expert_gateup"
     prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
     L.dg_synth_uniform_ids(4, 10, w.prompt, V, prompt)
     t0 = time.perf_counter()
@@ -235,7 +246,7 @@ def bench_full(args):
     # launch of the roofline kernel (on its stream): its live per-launch duration
     n_ev = min(args.steps, 48)
     L.dg_profile_enable(True, 64 * (n_ev + 2))
-    L.dg_profile_only("expert_gateup")
+    L.dg_profile_only(gu_name)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     blk = run(n_ev, blk)
@@ -251,13 +262,21 @@ def bench_full(args):
     prof = L.dg_profile_report()
     L.dg_profile_enable(False)
     steps_per_s = args.steps / dt
-    # algorithmic bytes of the routed-expert kernels: every expert's weights, once per launch
+    # algorithmic bytes of the routed-expert kernels: every expert's weights, once per launch (FP8:
+    # one byte per weight plus a float32 scale per row)
     es = 2
-    gu_bytes = d.n_experts * 2 * d.d_expert * d.d_model * es
-    dn_bytes = d.n_experts * d.d_model * d.d_expert * es
-    gu = live["expert_gateup"]
+    if fp8:
+        gu_bytes = d.n_experts * 2 * d.d_expert * (d.d_model + 4)
+        dn_bytes = d.n_experts * d.d_model * (d.d_expert + 4)
+    else:
+        gu_bytes = d.n_experts * 2 * d.d_expert * d.d_model * es
+        dn_bytes = d.n_experts * d.d_model * d.d_expert * es
+    gu = live[gu_name]
     achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
     src = kernel_source_hash(["canvas_denoising_amd/csrc/moe.hip"])
+    metric = "canvas denoise steps/s (256-token canvas)"
+    if fp8:
+        metric = "canvas denoise steps/s (256-token canvas, FP8 E4M3 routed-expert weights)"
     # roofline of the whole step (derived bytes; activations excluded)
     layer_bytes = (gu_bytes + dn_bytes + ((d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * d.d_model +
                    d.n_q_heads * d.head_dim * d.d_model + d.n_experts * d.d_model + 3 * d.d_shared * d.d_model) * es)
@@ -266,7 +285,7 @@ def bench_full(args):
     step_bytes = d.n_layers * (layer_bytes + attn_bytes) + 2 * V * d.d_model * es + 3 * C * V * es
     step_roof_s = step_bytes / (HBM_PEAK_GBS * 1e9)
     out = {
-        "metric": "canvas denoise steps/s (256-token canvas)",
+        "metric": metric,
         "value": steps_per_s,
         "unit": "steps/s",
         "n_gpus": 1,
@@ -282,6 +301,7 @@ def bench_full(args):
                                f"128 experts top-8 (704, gated GeLU) + shared 2816, tied vocab {V}, self-conditioning "
                                f"FFN {d.d_selfcond}, prompt KV {w.prompt}, canvas {C}, up to {S} steps per canvas, "
                                "block commit after each canvas; random-init weights",
+                   "expert_weights": "fp8 e4m3, per-row float32 scales" if fp8 else "bf16",
                    "canvas_tokens_per_s": steps_per_s * C,
                    "committed_tokens_per_s": commits * C / dt,
                    "commits": commits, "stops": stops,
@@ -290,9 +310,9 @@ def bench_full(args):
                    "step_roofline_frac": step_roof_s / (dt / args.steps),
                    "kernels_us": {k: v["avg_us"] for k, v in sorted(prof.items())},
                    "kernels_total_us_per_step": {k: v["total_us"] / n_prof for k, v in sorted(prof.items())}},
-        "roofline": {"kernel": "expert_gateup", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": gu_name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": load_traffic("expert_gateup", src),
+                     "traffic": load_traffic(gu_name, src),
                      "algorithmic_bytes_per_launch": gu_bytes, "avg_us": gu["avg_us"], "launches": gu["count"],
                      "timed_with": f"HIP events around each launch over {n_ev} steps issued directly "
                                    f"({dt_ev * 1e3 / n_ev:.2f} ms/step)"},
@@ -464,6 +484,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sampler-mode", type=int, default=0,
                     help="sampler workload: dg_sched.mode flags (1 either-stop, 2 group acceptance, 4 categorical)")
+    ap.add_argument("--experts", choices=["bf16", "fp8"], default="bf16",
+                    help="full workload: routed-expert weights in the model dtype or as FP8 E4M3 (opt-in mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -74,11 +74,16 @@ _SIGS = {
                                         ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "dg_load_weight": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _I32, _I32, _I32, _P, _P, _P]),
     "dg_prepare_weights": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P]),
+    "dg_expert_fp8_bytes": (_SZ, [ctypes.POINTER(dg_model_desc)]),
+    "dg_expert_fp8_tensor": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _I32, _I32, _I32, ctypes.POINTER(_SZ),
+                                            ctypes.POINTER(_SZ)]),
+    "dg_quantize_experts_fp8": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P, _P]),
     "dg_kv_bytes": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
     "dg_workspace_size": (_SZ, [ctypes.POINTER(dg_model_desc), _I64]),
     "dg_ctx_create": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P, _I64, _P, _SZ, ctypes.POINTER(_P)]),
     "dg_ctx_destroy": (ctypes.c_int, [_P]),
     "dg_ctx_use_graphs": (ctypes.c_int, [_P, _I32]),
+    "dg_ctx_use_expert_fp8": (ctypes.c_int, [_P, _P]),
     "dg_kv_length": (_I64, [_P]),
     "dg_kv_set_length": (ctypes.c_int, [_P, _I64]),
     "dg_prefill_kv": (ctypes.c_int, [_P, _P, _I32, _P]),
@@ -224,6 +229,23 @@ def dg_prepare_weights(desc, d_weights, stream=None):
                                                                stream_handle(stream)))
 
 
+def dg_expert_fp8_bytes(desc) -> int:
+    return lib.dg_expert_fp8_bytes(ctypes.byref(desc))
+
+
+def dg_expert_fp8_tensor(desc, kind, layer=0, expert=0):
+    """(code byte offset, scale byte offset) of one routed-expert matrix in the FP8 expert buffer."""
+    code, scale = _SZ(), _SZ()
+    _check("dg_expert_fp8_tensor", lib.dg_expert_fp8_tensor(ctypes.byref(desc), kind, layer, expert,
+                                                            ctypes.byref(code), ctypes.byref(scale)))
+    return code.value, scale.value
+
+
+def dg_quantize_experts_fp8(desc, d_weights, d_fp8, stream=None):
+    return _check("dg_quantize_experts_fp8", lib.dg_quantize_experts_fp8(ctypes.byref(desc), ptr(d_weights),
+                                                                         ptr(d_fp8), stream_handle(stream)))
+
+
 def dg_kv_bytes(desc, capacity) -> int:
     return lib.dg_kv_bytes(ctypes.byref(desc), capacity)
 
@@ -245,6 +267,10 @@ def dg_ctx_destroy(ctx):
 
 def dg_ctx_use_graphs(ctx, on: bool):
     return _check("dg_ctx_use_graphs", lib.dg_ctx_use_graphs(ctx, int(on)))
+
+
+def dg_ctx_use_expert_fp8(ctx, d_fp8):
+    return _check("dg_ctx_use_expert_fp8", lib.dg_ctx_use_expert_fp8(ctx, ptr(d_fp8)))
 
 
 def dg_kv_length(ctx) -> int:

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdg.so")
 
 SOURCES = ["api.cpp", "prof.cpp", "model.cpp", "sampler.hip", "synth.hip", "gemm.hip", "attention.hip", "moe.hip",
-           "elementwise.hip", "vocab.hip"]
+           "elementwise.hip", "vocab.hip", "fp8.hip"]
 
 
 def hipcc() -> str:

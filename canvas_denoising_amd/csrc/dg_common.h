@@ -27,6 +27,16 @@ int hip_check(hipError_t e, const char* what);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// FP8 (E4M3) codes and float32 per-row scales of one layer's routed experts: gate/up codes in the
+// paired-tile order of tiles.h (per expert gw * F * D bytes), down codes (per expert D * F bytes),
+// scales [E][gw][F] and [E][D].
+struct ExpertsFp8 {
+  const uint8_t* gu;
+  const uint8_t* dn;
+  const float* s_gu;
+  const float* s_dn;
+};
+
 // -------------------------------------------------------------- bf16 bits
 // bf16 is handled as raw 16-bit patterns (upper half of an fp32).
 typedef uint16_t bf16_t;

@@ -53,7 +53,9 @@ int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* 
                 hipStream_t s);
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
-                int dtype, hipStream_t s);
+                int dtype, const ExpertsFp8* q8, hipStream_t s);
+int quantize_fp8(const void* src, int64_t src_stride, void* codes, int64_t code_stride, float* scales, int E, int R,
+                 int K, int gr, int gw, hipStream_t s);
 int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s);
 int launch_synth_tiled(uint64_t seed, const uint64_t* tids, int64_t R, int64_t K, int gr, int gw, float sigma,
                        int dtype, void* out, hipStream_t s);
@@ -111,6 +113,38 @@ static WLayout weight_layout(const dg_model_desc& d) {
   }
   L.total = cur;
   return L;
+}
+
+// FP8 copies of the routed experts, per layer: gate/up codes, down codes, their scales
+struct Fp8Layout {
+  std::vector<size_t> gu, dn, s_gu, s_dn;
+  size_t total = 0;
+};
+
+static Fp8Layout fp8_layout(const dg_model_desc& d) {
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = cur;
+    cur = align256(cur + bytes);
+    return off;
+  };
+  const size_t E = d.n_experts, F = d.d_expert, D = d.d_model, gw = d.gated ? 2 : 1;
+  Fp8Layout L;
+  for (int l = 0; l < d.n_layers; ++l) {
+    L.gu.push_back(take(E * gw * F * D));
+    L.dn.push_back(take(E * D * F));
+    L.s_gu.push_back(take(E * gw * F * 4));
+    L.s_dn.push_back(take(E * D * 4));
+  }
+  L.total = cur;
+  return L;
+}
+
+static int check_fp8_desc(const dg_model_desc* d) {
+  if (d->dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "FP8 experts are built from a bf16 model");
+  if (d->d_expert % 64 != 0 || d->d_model % 64 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "FP8 experts need d_expert and d_model multiples of 64");
+  return DG_OK;
 }
 
 static int tensor_info(const dg_model_desc& d, const WLayout& L, int kind, int layer, int expert, size_t* off,
@@ -262,6 +296,9 @@ struct dg_ctx {
   // second stream: the shared expert runs beside the routed experts (fork / join events)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // FP8 routed experts in use (dg_ctx_use_expert_fp8), else null
+  const char* fp8 = nullptr;
+  dg::Fp8Layout fl;
   // graph replay of the denoising step body ([0]: without self-conditioning, [1]: with)
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
@@ -394,9 +431,16 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
                      wsp<float>(c, w.slot_gate), s));
   }
   if (kSharedMode == 2) DG_TRY(fork_shared());
+  ExpertsFp8 q8;
+  if (c->fp8) {
+    q8.gu = reinterpret_cast<const uint8_t*>(c->fp8 + c->fl.gu[l]);
+    q8.dn = reinterpret_cast<const uint8_t*>(c->fp8 + c->fl.dn[l]);
+    q8.s_gu = reinterpret_cast<const float*>(c->fp8 + c->fl.s_gu[l]);
+    q8.s_dn = reinterpret_cast<const float*>(c->fp8 + c->fl.s_dn[l]);
+  }
   DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
-                     wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, s));
+                     wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, c->fp8 ? &q8 : nullptr, s));
   // join, then x += shared + sum of the token's gated expert outputs (fixed order); h = RMSNorm(x)
   if (kSharedMode != 0) DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
   if (fused)
@@ -558,6 +602,56 @@ int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream)
                    as_stream(stream));
 }
 
+size_t dg_expert_fp8_bytes(const dg_model_desc* desc) {
+  if (check_desc(desc) != DG_OK || check_fp8_desc(desc) != DG_OK) return 0;
+  return fp8_layout(*desc).total;
+}
+
+int dg_expert_fp8_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert, size_t* code_offset,
+                         size_t* scale_offset) {
+  DG_TRY(check_desc(desc));
+  DG_TRY(check_fp8_desc(desc));
+  if (!code_offset || !scale_offset) return fail(DG_ERR_INVALID, "output pointers are NULL");
+  const dg_model_desc& d = *desc;
+  if (layer < 0 || layer >= d.n_layers) return fail(DG_ERR_INVALID, "layer out of range");
+  if (expert < 0 || expert >= d.n_experts) return fail(DG_ERR_INVALID, "expert out of range");
+  if (kind != DG_W_EX_UP && kind != DG_W_EX_DOWN && !(kind == DG_W_EX_GATE && d.gated))
+    return fail(DG_ERR_INVALID, "kind must be a routed-expert matrix of this model");
+  const Fp8Layout L = fp8_layout(d);
+  const size_t E = expert, F = d.d_expert, D = d.d_model, gw = d.gated ? 2 : 1;
+  if (kind == DG_W_EX_DOWN) {
+    *code_offset = L.dn[layer] + E * D * F;
+    *scale_offset = L.s_dn[layer] + E * D * 4;
+  } else {
+    const size_t which = (kind == DG_W_EX_UP && d.gated) ? 1 : 0;
+    *code_offset = L.gu[layer] + E * gw * F * D;
+    *scale_offset = L.s_gu[layer] + (E * gw + which) * F * 4;
+  }
+  return DG_OK;
+}
+
+int dg_quantize_experts_fp8(const dg_model_desc* desc, const void* d_weights, void* d_fp8, void* stream) {
+  DG_TRY(check_desc(desc));
+  DG_TRY(check_fp8_desc(desc));
+  if (!d_weights || !d_fp8) return fail(DG_ERR_INVALID, "d_weights and d_fp8 are required");
+  if (reinterpret_cast<uintptr_t>(d_weights) % 256 != 0 || reinterpret_cast<uintptr_t>(d_fp8) % 256 != 0)
+    return fail(DG_ERR_INVALID, "device buffers must be 256-byte aligned");
+  const dg_model_desc& d = *desc;
+  const WLayout W = weight_layout(d);
+  const Fp8Layout L = fp8_layout(d);
+  const char* w = static_cast<const char*>(d_weights);
+  char* q = static_cast<char*>(d_fp8);
+  hipStream_t s = as_stream(stream);
+  const int64_t F = d.d_expert, D = d.d_model, gw = d.gated ? 2 : 1;
+  for (int l = 0; l < d.n_layers; ++l) {
+    DG_TRY(quantize_fp8(w + W.ex_gu[l], gw * F * D, q + L.gu[l], gw * F * D, reinterpret_cast<float*>(q + L.s_gu[l]),
+                        d.n_experts, static_cast<int>(F), static_cast<int>(D), kGuBlocks, static_cast<int>(gw), s));
+    DG_TRY(quantize_fp8(w + W.ex_down[l], D * F, q + L.dn[l], D * F, reinterpret_cast<float*>(q + L.s_dn[l]),
+                        d.n_experts, static_cast<int>(D), static_cast<int>(F), kDownGroup, 1, s));
+  }
+  return DG_OK;
+}
+
 int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights, void* stream) {
   DG_TRY(check_desc(desc));
   if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
@@ -672,6 +766,19 @@ int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on) {
     DG_HIP(hipDeviceSynchronize());
     for (StepGraph& g : ctx->graphs) drop_graph(g);
   }
+  return DG_OK;
+}
+
+int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8) {
+  DG_TRY(check_ctx(ctx));
+  if (d_fp8) {
+    DG_TRY(check_fp8_desc(&ctx->d));
+    if (reinterpret_cast<uintptr_t>(d_fp8) % 256 != 0) return fail(DG_ERR_INVALID, "d_fp8 must be 256-byte aligned");
+  }
+  DG_HIP(hipDeviceSynchronize());
+  for (StepGraph& g : ctx->graphs) drop_graph(g);
+  ctx->fp8 = static_cast<const char*>(d_fp8);
+  if (d_fp8) ctx->fl = fp8_layout(ctx->d);
   return DG_OK;
 }
 

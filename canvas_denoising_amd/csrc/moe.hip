@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dg_common.h"
 #include "mfma.h"
@@ -218,6 +219,26 @@ __device__ inline void expert_of_block(int b, int per_e, int E, int* e, int* q) 
   }
 }
 
+// Sum the partials of the 4 waves into wave 0's acc (red: 3 * G * NT * 64 f32x4 of LDS).
+template <int G, int NT>
+__device__ inline void reduce_waves(f32x4_t (&acc)[G][NT], f32x4_t* red, int wave, int lane) {
+  if (wave > 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) red[(((wave - 1) * G + g) * NT + t) * 64 + lane] = acc[g][t];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kExpWaves - 1; ++w)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[g][t] += red[((w * G + g) * NT + t) * 64 + lane];
+  }
+}
+
 // One pass of a workgroup over one tile group of its expert's weights (G
 // tiles per k-tile, tiles.h) against NT 16-token tiles. The k-tiles are
 // split over the 4 waves in runs of KSP: stage s of wave w holds k-tiles
@@ -295,31 +316,119 @@ struct SplitStream {
       if (s0 + u < nst) compute(st[u], s0 + u);
   }
 
-  // Sum the partials of the 4 waves into wave 0's acc (red: 3 * G * NT * 64 f32x4 of LDS).
-  __device__ inline void reduce(f32x4_t* red, int wave, int lane) {
-    if (wave > 0) {
+  __device__ inline void reduce(f32x4_t* red, int wave, int lane) { reduce_waves<G, NT>(acc, red, wave, lane); }
+};
+
+#ifndef DG_EXP8_KP_GU
+#define DG_EXP8_KP_GU 1
+#endif
+#ifndef DG_EXP8_NS_GU
+#define DG_EXP8_NS_GU 2
+#endif
+#ifndef DG_EXP8_KP_DN
+#define DG_EXP8_KP_DN 1
+#endif
+#ifndef DG_EXP8_NS_DN
+#define DG_EXP8_NS_DN 2
+#endif
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// 8 E4M3 codes (two dwords, code j in byte j) -> the bf16 B fragment of one k-step. Every E4M3
+// value is exact in bf16 (3 fraction bits, exponents 2^-9 .. 2^8), so with a unit scale the
+// conversion is exact; the per-row scale multiplies the fp32 accumulators instead.
+__device__ inline bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  const bf16x4_t lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4_t hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// SplitStream over FP8 weights in the paired-tile order (tiles.h): the unit of the split is a
+// pair of k-tiles, whose G blocks arrive as one 16-byte load per lane each (a contiguous
+// kilobyte per wave, as in the bf16 stream); stage s of wave w holds pairs s * 4 KP + w KP + u.
+// The token fragments stay bf16. Same unpredicated-load discipline as SplitStream.
+template <int G, int NT, int KP, int NS>
+struct SplitStream8 {
+  using Fr = Frag<bf16_t>;
+  struct Stage {
+    u32x4v_t b[KP][G];
+    bf16x8_t a[2 * KP][NT];
+  };
+  f32x4_t acc[G][NT];
+
+  // bt: this lane's 16 bytes of pair 0 of the group; arow[t]: as in SplitStream; KT even.
+  __device__ inline void run(const uint8_t* bt, const bf16_t* const* arow, int KT, int wave, int rot) {
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) red[(((wave - 1) * G + g) * NT + t) * 64 + lane] = acc[g][t];
-    }
-    __syncthreads();
-    if (wave == 0) {
+      for (int t = 0; t < NT; ++t) acc[g][t] = f32x4_t{0, 0, 0, 0};
+    const int NP = KT / 2;
+    constexpr int kPer = kExpWaves * KP;
+    const int nst = (NP + kPer - 1) / kPer;
+    const int first = wave * KP;
+    rot %= nst;
+    auto rs = [&](int s) { const int r = s + rot; return r >= nst ? r - nst : r; };
+    auto load = [&](Stage& S, int s) {
+      const int base = rs(min(s, nst - 1)) * kPer + first;
 #pragma unroll
-      for (int w = 0; w < kExpWaves - 1; ++w)
+      for (int u = 0; u < KP; ++u) {
+        const int p = min(base + u, NP - 1);
 #pragma unroll
         for (int g = 0; g < G; ++g)
+          S.b[u][g] = *reinterpret_cast<const u32x4v_t*>(bt + (static_cast<int64_t>(p) * G + g) * 1024);
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[g][t] += red[((w * G + g) * NT + t) * 64 + lane];
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) S.a[2 * u + h][t] = Fr::load(arow[t] + (2 * p + h) * 32);
+      }
+    };
+    auto compute = [&](const Stage& S, int s) {
+      const int base = rs(s) * kPer + first;
+#pragma unroll
+      for (int u = 0; u < KP; ++u)
+        if (base + u < NP) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const bf16x8_t bf = fp8x8_to_bf16(S.b[u][g][2 * h], S.b[u][g][2 * h + 1]);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) acc[g][t] = Fr::mma(S.a[2 * u + h][t], bf, acc[g][t]);
+            }
+        }
+    };
+    Stage st[NS];
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) load(st[u], u);
+    int s0 = 0;
+    for (; s0 + NS <= nst; s0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        load(st[(u + NS - 1) % NS], s0 + u + NS - 1);
+        compute(st[u], s0 + u);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (s0 + u < nst) compute(st[u], s0 + u);
   }
+
+  __device__ inline void reduce(f32x4_t* red, int wave, int lane) { reduce_waves<G, NT>(acc, red, wave, lane); }
 };
 
 // act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j (gated) or GeLU(h W_up[e]^T)_j for up to
 // 16 NT slots of expert e starting at p0 and the 16 kGuBlocks features j0 .. of the tile group.
-template <typename T, bool GATED, int NT>
-__device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, int KT, int beg, int cnt, int p0,
-                                   const int32_t* perm, T* act, int j0, int wave, int lane, f32x4_t* red) {
+// FP8: bt points at E4M3 codes and the products are multiplied by this lane's row scales scl[g]
+// (gate blocks, then up blocks) before the activation.
+template <typename T, bool GATED, int NT, bool FP8>
+__device__ inline void gateup_pass(const T* h, int64_t ldh, const void* bt, int F, int KT, int beg, int cnt, int p0,
+                                   const int32_t* perm, T* act, int j0, int wave, int lane, f32x4_t* red,
+                                   const float* scl) {
   constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
@@ -328,8 +437,10 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, 
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
   }
-  SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU> sp;
-  sp.run(bt, arow, KT, wave, kExpRot ? blockIdx.x : 0);
+  std::conditional_t<FP8, SplitStream8<G, NT, DG_EXP8_KP_GU, DG_EXP8_NS_GU>,
+                     SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU>> sp;
+  if constexpr (FP8) sp.run(static_cast<const uint8_t*>(bt), arow, KT, wave, kExpRot ? blockIdx.x : 0);
+  else sp.run(static_cast<const T*>(bt), arow, KT, wave, kExpRot ? blockIdx.x : 0);
   sp.reduce(red, wave, lane);
   if (wave == 0) {
 #pragma unroll
@@ -340,8 +451,10 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const T* bt, int F, 
         if (s < cnt) {
 #pragma unroll
           for (int b = 0; b < kGuBlocks; ++b) {
-            const float v = GATED ? gelu_erf(sp.acc[b][t][i]) * sp.acc[kGuBlocks + b][t][i]
-                                  : gelu_erf(sp.acc[b][t][i]);
+            const float a0 = FP8 ? sp.acc[b][t][i] * scl[b] : sp.acc[b][t][i];
+            const float v = GATED ? gelu_erf(a0) * (FP8 ? sp.acc[kGuBlocks + b][t][i] * scl[kGuBlocks + b]
+                                                         : sp.acc[kGuBlocks + b][t][i])
+                                  : gelu_erf(a0);
             act[static_cast<int64_t>(beg + s) * F + j0 + b * 16 + fr] = from_f32<T>(v);
           }
         }
@@ -367,15 +480,47 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
                 static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
   const int j0 = q * 16 * kGuBlocks;
   for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16) gateup_pass<T, GATED, 2>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red);
-    else gateup_pass<T, GATED, 1>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red);
+    if (cnt - p0 > 16)
+      gateup_pass<T, GATED, 2, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, nullptr);
+    else gateup_pass<T, GATED, 1, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, nullptr);
+  }
+}
+
+// The same over FP8 codes (paired tiles, tiles.h) with per-row scales sc[E][gw][F].
+template <bool GATED>
+__global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
+    const bf16_t* __restrict__ h, int64_t ldh, const uint8_t* __restrict__ q_gu, const float* __restrict__ sc, int E,
+    int F, int D, int per_e, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+    bf16_t* __restrict__ act) {
+  constexpr int gw = GATED ? 2 : 1;
+  constexpr int G = gw * kGuBlocks;
+  __shared__ f32x4_t red[(kExpWaves - 1) * G * 2 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int e, q;
+  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+  if (cnt == 0) return;
+  const int KT = D / 32;
+  const int j0 = q * 16 * kGuBlocks;
+  float scl[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    scl[g] = sc[(static_cast<int64_t>(e) * gw + g / kGuBlocks) * F + j0 + (g % kGuBlocks) * 16 + (lane & 15)];
+  const uint8_t* bt = q_gu + static_cast<int64_t>(e) * gw * F * D + static_cast<int64_t>(q) * KT * G * kTileElems +
+                      lane * 16;
+  for (int p0 = 0; p0 < cnt; p0 += 32) {
+    if (cnt - p0 > 16)
+      gateup_pass<bf16_t, GATED, 2, true>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, scl);
+    else gateup_pass<bf16_t, GATED, 1, true>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, scl);
   }
 }
 
 // out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 16 kDownGroup outputs n0 ..
-template <typename T, int NT>
-__device__ inline void down_pass(const T* act, const T* bt, int F, int D, int beg, int cnt, int p0,
-                                 const float* slot_gate, float* out, int n0, int wave, int lane, f32x4_t* red) {
+// FP8: bt points at E4M3 codes and output row block g is multiplied by this lane's row scale scl[g].
+template <typename T, int NT, bool FP8>
+__device__ inline void down_pass(const T* act, const void* bt, int F, int D, int beg, int cnt, int p0,
+                                 const float* slot_gate, float* out, int n0, int wave, int lane, f32x4_t* red,
+                                 const float* scl) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
 #pragma unroll
@@ -383,8 +528,10 @@ __device__ inline void down_pass(const T* act, const T* bt, int F, int D, int be
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
   }
-  SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN> sp;
-  sp.run(bt, arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
+  std::conditional_t<FP8, SplitStream8<kDownGroup, NT, DG_EXP8_KP_DN, DG_EXP8_NS_DN>,
+                     SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN>> sp;
+  if constexpr (FP8) sp.run(static_cast<const uint8_t*>(bt), arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
+  else sp.run(static_cast<const T*>(bt), arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
   sp.reduce(red, wave, lane);
   if (wave == 0) {
 #pragma unroll
@@ -396,7 +543,7 @@ __device__ inline void down_pass(const T* act, const T* bt, int F, int D, int be
           const float gs = slot_gate[beg + s];
           float* o = out + static_cast<int64_t>(beg + s) * D + n0 + fr;
 #pragma unroll
-          for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * sp.acc[g][t][i];
+          for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * (FP8 ? sp.acc[g][t][i] * scl[g] : sp.acc[g][t][i]);
         }
       }
   }
@@ -419,8 +566,33 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
                 lane * 8;
   const int n0 = q * kDownGroup * 16;
   for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16) down_pass<T, 2>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red);
-    else down_pass<T, 1>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red);
+    if (cnt - p0 > 16) down_pass<T, 2, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, nullptr);
+    else down_pass<T, 1, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, nullptr);
+  }
+}
+
+// The same over FP8 codes (paired tiles, tiles.h) with per-row scales sc[E][D].
+__global__ __launch_bounds__(256) void expert_down_fp8_kernel(
+    const bf16_t* __restrict__ act, const uint8_t* __restrict__ q_down, const float* __restrict__ sc, int E, int F,
+    int D, int per_e, const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate,
+    float* __restrict__ out) {
+  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * 2 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int e, q;
+  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+  if (cnt == 0) return;
+  const int KT = F / 32;
+  const int n0 = q * kDownGroup * 16;
+  float scl[kDownGroup];
+#pragma unroll
+  for (int g = 0; g < kDownGroup; ++g) scl[g] = sc[static_cast<int64_t>(e) * D + n0 + g * 16 + (lane & 15)];
+  const uint8_t* bt = q_down + static_cast<int64_t>(e) * D * F +
+                      static_cast<int64_t>(q) * KT * kDownGroup * kTileElems + lane * 16;
+  for (int p0 = 0; p0 < cnt; p0 += 32) {
+    if (cnt - p0 > 16)
+      down_pass<bf16_t, 2, true>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, scl);
+    else down_pass<bf16_t, 1, true>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, scl);
   }
 }
 
@@ -474,14 +646,36 @@ int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* 
   return DG_OK;
 }
 
+// q8 (optional): FP8 codes and scales of the same layer's routed experts; when given, the expert
+// kernels stream those instead of w_gu / w_down (bf16 models only).
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
-                int dtype, hipStream_t s) {
+                int dtype, const ExpertsFp8* q8, hipStream_t s) {
   if (F % (16 * kGuBlocks) != 0 || D % (16 * kDownGroup) != 0)
     return fail(DG_ERR_UNSUPPORTED, "expert width and d_model must be multiples of 32 and 64");
   const int per_gu = F / (16 * kGuBlocks);
   const int per_dn = D / (16 * kDownGroup);
   const dim3 g1(E * per_gu), g2(E * per_dn);
+  if (q8) {
+    if (dtype != DG_BF16 || F % 64 != 0 || D % 64 != 0)
+      return fail(DG_ERR_UNSUPPORTED, "FP8 experts need a bf16 model and widths that are multiples of 64");
+    const bf16_t* hh = static_cast<const bf16_t*>(h);
+    bf16_t* a = static_cast<bf16_t*>(act);
+    {
+      ProfScope ps("expert_gateup_fp8", s, true);
+      if (gated) launch_timed(ps, expert_gateup_fp8_kernel<true>, g1, dim3(256), s, hh, ldh, q8->gu, q8->s_gu, E, F, D,
+                              per_gu, offsets, perm, a);
+      else launch_timed(ps, expert_gateup_fp8_kernel<false>, g1, dim3(256), s, hh, ldh, q8->gu, q8->s_gu, E, F, D,
+                        per_gu, offsets, perm, a);
+    }
+    DG_LAUNCH_CHECK("expert_gateup_fp8_kernel");
+    {
+      ProfScope ps("expert_down_fp8", s);
+      expert_down_fp8_kernel<<<g2, 256, 0, s>>>(a, q8->dn, q8->s_dn, E, F, D, per_dn, offsets, slot_gate, out);
+    }
+    DG_LAUNCH_CHECK("expert_down_fp8_kernel");
+    return DG_OK;
+  }
   {
     ProfScope ps("expert_gateup", s, true);
     if (dtype == DG_BF16) {

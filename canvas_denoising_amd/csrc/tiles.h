@@ -54,3 +54,23 @@ __host__ __device__ inline void tiled_coords(int64_t p, int64_t K, int gr, int g
 }
 
 }  // namespace dg
+
+namespace dg {
+
+// FP8 (E4M3) copies of the routed-expert matrices keep the tile order above
+// with one byte per element, but pair the k-tiles: for k-tile pair p the
+// 1 KiB block of tile g holds, for lane l at bytes 16 l .. 16 l + 15, the 8
+// codes of lane l in k-tile 2p followed by its 8 codes in k-tile 2p + 1, so a
+// 16-byte load per lane still moves a whole contiguous kilobyte per wave (two
+// k-steps of B fragments). K must be a multiple of 64. Byte index of element
+// (r, k) of matrix `which`:
+__host__ __device__ inline int64_t fp8_tiled_index(int64_t r, int64_t k, int which, int64_t K, int gr, int gw) {
+  const int64_t rb = r >> 4, kb = k >> 5;
+  const int64_t group = rb / gr;
+  const int g = which * gr + static_cast<int>(rb % gr);
+  const int64_t block = (group * (K >> 6) + (kb >> 1)) * (gr * gw) + g;
+  const int lane = static_cast<int>(r & 15) + 16 * static_cast<int>((k & 31) >> 3);
+  return block * 1024 + lane * 16 + (kb & 1) * 8 + (k & 7);
+}
+
+}  // namespace dg

@@ -99,6 +99,18 @@ class Model:
             raise ValueError(f"expected a contiguous {self.dtype} CUDA tensor of shape ({r}, {c})")
         L.dg_load_weight(self.desc, kind, layer, expert, src, self.weights)
 
+    def use_expert_fp8(self, on: bool = True):
+        """Quantize the routed experts to FP8 (once) and compute with them; False returns to the
+        model-dtype weights."""
+        if on:
+            if getattr(self, "expert_fp8", None) is None:
+                self.expert_fp8 = torch.empty(L.dg_expert_fp8_bytes(self.desc), dtype=torch.uint8,
+                                              device=self.weights.device)
+                L.dg_quantize_experts_fp8(self.desc, self.weights, self.expert_fp8)
+            L.dg_ctx_use_expert_fp8(self.ctx, self.expert_fp8)
+        else:
+            L.dg_ctx_use_expert_fp8(self.ctx, None)
+
     def _kv_raw(self):
         d = self.desc
         t = self.kv.view(self.dtype)

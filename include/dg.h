@@ -255,6 +255,43 @@ int dg_load_weight(const dg_model_desc* desc, int32_t kind, int32_t layer, int32
 /* Rebuild DG_W_EMBED_T from DG_W_EMBED (call after loading weights). */
 int dg_prepare_weights(const dg_model_desc* desc, void* d_weights, void* stream);
 
+/* FP8 routed experts (opt-in; [P2] "24GB GPU: practical adoption and
+ * running conditions" lists quantised GGUF builds of the model, the 8-bit
+ * one at about half the bf16 footprint, and [P1] "Summary" points local runs
+ * at them; the format here is this library's own 8-bit storage): a
+ * separate caller-owned device buffer holding every layer's routed-expert
+ * matrices as OCP E4M3 codes (bias 7, 3 fraction bits, subnormals in units
+ * of 2^-9, no infinities, largest finite 448) with one float32 scale per
+ * output row (a gate / up feature, a down output): s = max|w| / 448 (1 for
+ * an all-zero row), code = E4M3(w / s) rounded to nearest-even and saturated
+ * at +-448, both divisions the correctly rounded float32 ones; the model
+ * then computes with code * s. The bf16 weights stay in use for everything
+ * else. bf16 models with d_expert and d_model multiples of 64 only. */
+/* Bytes of the FP8 expert buffer (0 for an invalid or unsupported desc). Per
+ * layer, 256-byte aligned: gate/up codes [expert][gw * d_expert * d_model]
+ * (gw = 2 gated, 1 not), down codes [expert][d_model * d_expert], gate/up
+ * scales float32 [expert][gw][d_expert], down scales [expert][d_model]. The
+ * codes follow the routed experts' tile order (dg_weight_tensor) at one byte
+ * per element, with k-tiles paired: for column tiles 2p and 2p + 1 of one
+ * 16-row block, a 1024-byte block holds at bytes 16 l .. 16 l + 15 element
+ * slot l's 8 codes of tile 2p, then its 8 codes of tile 2p + 1 (slot l is row
+ * l % 16, columns 8 (l / 16) .. +7 of the tile); blocks ordered [row group]
+ * [column pair][the group's row blocks, gate before up]. */
+size_t dg_expert_fp8_bytes(const dg_model_desc* desc);
+/* Byte offsets inside the FP8 buffer of one routed-expert matrix: the
+ * expert's code region (for DG_W_EX_GATE / DG_W_EX_UP the shared gate/up
+ * region) and the first float32 scale of that matrix. Errors:
+ * DG_ERR_INVALID (bad kind / layer / expert, NULL outputs),
+ * DG_ERR_UNSUPPORTED (desc without FP8 support). */
+int dg_expert_fp8_tensor(const dg_model_desc* desc, int32_t kind, int32_t layer, int32_t expert,
+                         size_t* code_offset, size_t* scale_offset);
+/* Quantize every routed expert of the weight buffer into d_fp8
+ * (dg_expert_fp8_bytes, 256-byte aligned, caller-owned), asynchronously on
+ * `stream`; d_weights is only read. Deterministic: codes and scales depend on
+ * the weights alone. Errors: DG_ERR_INVALID (NULL / misaligned buffers),
+ * DG_ERR_UNSUPPORTED (fp32 model or widths not multiples of 64). */
+int dg_quantize_experts_fp8(const dg_model_desc* desc, const void* d_weights, void* d_fp8, void* stream);
+
 /* KV cache, in the model dtype: keys [n_layers][n_kv_heads][capacity][head_dim]
  * (row-major), then values [n_layers][n_kv_heads][capacity / 32][head_dim][32]:
  * V transposed in blocks of 32 positions, where inside a block slot 8 g + j
@@ -284,6 +321,13 @@ int dg_ctx_destroy(dg_ctx* ctx);
  * and replayed; any change re-captures. Off (0): every launch is issued
  * directly. Steps also run directly while dg_profile_enable is on. */
 int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
+/* Compute the routed experts from a filled FP8 expert buffer (see
+ * dg_quantize_experts_fp8; it must outlive its use and stay unmodified while
+ * steps run) in every later prefill, step and commit; NULL returns to the
+ * model-dtype weights. Waits for the device and drops captured graphs.
+ * Errors: DG_ERR_INVALID (misaligned), DG_ERR_UNSUPPORTED (model without
+ * FP8 support). */
+int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8);
 int64_t dg_kv_length(const dg_ctx* ctx);
 /* Declare the first `length` cache positions valid without computing them
  * (for caches filled by the caller). */

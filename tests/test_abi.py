@@ -78,3 +78,27 @@ def test_workspace_size(L):
     assert L.dg_sample_workspace_size(0, 10) == 0
     assert L.dg_sample_workspace_size(256, 262144) >= 256 * 16
     assert 16 <= L.dg_sample_workspace_size(1, 1) <= 4096
+
+
+def test_fp8_expert_buffer_layout_and_validation(L):
+    from canvas_denoising_amd import configs
+    d = configs.full_loop_bf16().desc
+    E, F, D, nl = d.n_experts, d.d_expert, d.d_model, d.n_layers
+    per_layer = 3 * E * F * D + 4 * E * (2 * F + D)  # codes, then scales; every part a multiple of 256 here
+    assert L.dg_expert_fp8_bytes(d) == nl * per_layer
+    assert L.dg_expert_fp8_bytes(configs.desc(1, 256, 4, 2, 64, 8, 2, 128, 256, 1, 512, 128, L.DG_F32)) == 0
+    assert L.dg_expert_fp8_bytes(configs.desc(1, 256, 4, 2, 64, 8, 2, 96, 256, 1, 512, 128, L.DG_BF16)) == 0
+    gate = L.dg_expert_fp8_tensor(d, L.DG_W_EX_GATE, 1, 5)
+    up = L.dg_expert_fp8_tensor(d, L.DG_W_EX_UP, 1, 5)
+    down = L.dg_expert_fp8_tensor(d, L.DG_W_EX_DOWN, 1, 5)
+    assert gate[0] == up[0] == per_layer + 5 * 2 * F * D  # gate and up share the expert's region
+    assert up[1] - gate[1] == 4 * F
+    assert down[0] == per_layer + 2 * E * F * D + 5 * D * F
+    assert down[1] == per_layer + 3 * E * F * D + 4 * E * 2 * F + 4 * 5 * D
+    for bad in [(L.DG_W_Q, 0, 0), (L.DG_W_EX_UP, nl, 0), (L.DG_W_EX_UP, 0, E)]:
+        with pytest.raises(L.DGError):
+            L.dg_expert_fp8_tensor(d, *bad)
+    with pytest.raises(L.DGError):
+        L.dg_quantize_experts_fp8(d, None, None)
+    with pytest.raises(L.DGError):
+        L.dg_ctx_use_expert_fp8(None, None)
