@@ -1,9 +1,10 @@
 """FP8 E4M3 storage of the routed experts' weights (an opt-in mode of the library).
 
-Source: the pages mention quantised deployments of the model (the Korean
-overview's local-run notes and the Hugging Face card); they give no format.
-Reading taken: the OCP 8-bit floating-point E4M3 format ("OFP8", the variant
-with no infinities): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+Source: [P2] "24GB GPU: practical adoption and running conditions" lists
+quantised GGUF builds of the model (the 8-bit one at about half the bf16
+footprint) and [P1] "Summary" points local runs at them; the pages fix no
+format for this library. Reading taken: the OCP 8-bit floating-point E4M3
+format ("OFP8", the variant with no infinities): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits; exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN, so the
 largest finite magnitude is 1.75 * 2^8 = 448. Values are rounded to nearest,
 ties to an even mantissa, and magnitudes beyond the rounding range of 448
