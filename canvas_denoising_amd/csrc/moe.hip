@@ -24,7 +24,7 @@
 // one contiguous run with 1 KB per load instruction, straight into MFMA B
 // fragments through a ring of register stages, together with the expert's
 // gathered token rows (A fragments, from L2). The waves' partial sums meet
-// in LDS at the end. Up to 32 tokens are held in accumulators per pass; an
+// in LDS at the end. Up to 48 tokens are held in accumulators per pass; an
 // expert with more tokens takes further passes.
 #include <math.h>
 
@@ -204,6 +204,24 @@ constexpr bool kExpNT = DG_EXP_NT;  // nontemporal weight loads
 #define DG_EXP_ROT 0
 #endif
 constexpr bool kExpRot = DG_EXP_ROT;  // per-workgroup rotation of the stage order
+#ifndef DG_EXP_MAX_NT
+#define DG_EXP_MAX_NT 3
+#endif
+// 16-token tiles one pass of an expert workgroup holds: an expert with more tokens streams its
+// weights once per pass, so the bound trades registers (accumulators) against weight re-reads
+constexpr int kExpMaxNT = DG_EXP_MAX_NT;
+
+// Calls f(std::integral_constant<int, NT>) with the fewest 16-token tiles (at most kExpMaxNT)
+// that cover `rem` tokens.
+template <typename F>
+__device__ inline void with_token_tiles(int rem, F&& f) {
+  if constexpr (kExpMaxNT >= 4)
+    if (rem > 48) return f(std::integral_constant<int, 4>());
+  if constexpr (kExpMaxNT >= 3)
+    if (rem > 32) return f(std::integral_constant<int, 3>());
+  if (rem > 16) return f(std::integral_constant<int, 2>());
+  f(std::integral_constant<int, 1>());
+}
 
 // Block b of an expert grid -> (expert, unit within the expert). Workgroups
 // of one expert read the same token rows, so with E a multiple of 8 they are
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
     const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, T* __restrict__ act) {
   constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
-  __shared__ f32x4_t red[(kExpWaves - 1) * G * 2 * 64];
+  __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
@@ -479,11 +497,11 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
   const T* bt = w_gu + static_cast<int64_t>(e) * (GATED ? 2 : 1) * F * D +
                 static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
   const int j0 = q * 16 * kGuBlocks;
-  for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16)
-      gateup_pass<T, GATED, 2, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, nullptr);
-    else gateup_pass<T, GATED, 1, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, nullptr);
-  }
+  for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
+    with_token_tiles(cnt - p0, [&](auto nt) {
+      gateup_pass<T, GATED, decltype(nt)::value, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane,
+                                                        red, nullptr);
+    });
 }
 
 // The same over FP8 codes (paired tiles, tiles.h) with per-row scales sc[E][gw][F].
@@ -494,7 +512,7 @@ __global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
     bf16_t* __restrict__ act) {
   constexpr int gw = GATED ? 2 : 1;
   constexpr int G = gw * kGuBlocks;
-  __shared__ f32x4_t red[(kExpWaves - 1) * G * 2 * 64];
+  __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
@@ -508,11 +526,11 @@ __global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
     scl[g] = sc[(static_cast<int64_t>(e) * gw + g / kGuBlocks) * F + j0 + (g % kGuBlocks) * 16 + (lane & 15)];
   const uint8_t* bt = q_gu + static_cast<int64_t>(e) * gw * F * D + static_cast<int64_t>(q) * KT * G * kTileElems +
                       lane * 16;
-  for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16)
-      gateup_pass<bf16_t, GATED, 2, true>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, scl);
-    else gateup_pass<bf16_t, GATED, 1, true>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane, red, scl);
-  }
+  for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
+    with_token_tiles(cnt - p0, [&](auto nt) {
+      gateup_pass<bf16_t, GATED, decltype(nt)::value, true>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave,
+                                                            lane, red, scl);
+    });
 }
 
 // out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 16 kDownGroup outputs n0 ..
@@ -555,7 +573,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void expert_down_kernel(
     const T* __restrict__ act, const T* __restrict__ w_down, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate, float* __restrict__ out) {
-  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * 2 * 64];
+  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
@@ -565,10 +583,11 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
   const T* bt = w_down + static_cast<int64_t>(e) * D * F + static_cast<int64_t>(q) * KT * kDownGroup * kTileElems +
                 lane * 8;
   const int n0 = q * kDownGroup * 16;
-  for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16) down_pass<T, 2, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, nullptr);
-    else down_pass<T, 1, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, nullptr);
-  }
+  for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
+    with_token_tiles(cnt - p0, [&](auto nt) {
+      down_pass<T, decltype(nt)::value, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red,
+                                               nullptr);
+    });
 }
 
 // The same over FP8 codes (paired tiles, tiles.h) with per-row scales sc[E][D].
@@ -576,7 +595,7 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
     const bf16_t* __restrict__ act, const uint8_t* __restrict__ q_down, const float* __restrict__ sc, int E, int F,
     int D, int per_e, const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate,
     float* __restrict__ out) {
-  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * 2 * 64];
+  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, &e, &q);
@@ -589,11 +608,11 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
   for (int g = 0; g < kDownGroup; ++g) scl[g] = sc[static_cast<int64_t>(e) * D + n0 + g * 16 + (lane & 15)];
   const uint8_t* bt = q_down + static_cast<int64_t>(e) * D * F +
                       static_cast<int64_t>(q) * KT * kDownGroup * kTileElems + lane * 16;
-  for (int p0 = 0; p0 < cnt; p0 += 32) {
-    if (cnt - p0 > 16)
-      down_pass<bf16_t, 2, true>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, scl);
-    else down_pass<bf16_t, 1, true>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red, scl);
-  }
+  for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
+    with_token_tiles(cnt - p0, [&](auto nt) {
+      down_pass<bf16_t, decltype(nt)::value, true>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red,
+                                                   scl);
+    });
 }
 
 // ------------------------------------------------------------------- host
