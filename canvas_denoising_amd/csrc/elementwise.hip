@@ -133,6 +133,8 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
     const int c = tid + 256 * i;
     v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // Gathered loads are unconditional (indices clamped into range, surplus values never added), so a
+  // batch of B rows is in flight at once instead of issued one by one behind uniform branches.
   if (splits > 0) {  // t = part[0] + part[1] + ... (in order), x += t
     float4 t[NV];
     for (int z0 = 0; z0 < splits; z0 += B) {
@@ -141,21 +143,23 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
       for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int q = 0; q < B; ++q) {
-          const int c = tid + 256 * i;
-          u[i][q] = (c < n4 && z0 + q < splits) ? p4[(z0 + q) * plane + static_cast<int64_t>(m) * n4 + c]
-                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          const int c = min(tid + 256 * i, n4 - 1);
+          u[i][q] = p4[min(z0 + q, splits - 1) * plane + static_cast<int64_t>(m) * n4 + c];
         }
+      // surplus values are replaced by zeros rather than skipped: a skipped value would let the
+      // compiler sink its load behind a branch
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int q = 0; q < B; ++q) {
-          if (z0 + q >= splits) break;
-          if (z0 + q == 0) t[i] = u[i][0];
-          else add4(t[i], u[i][q]);
+          const float4 w = z0 + q < splits ? u[i][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+          if (z0 + q == 0) t[i] = w;
+          else add4(t[i], w);
         }
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) add4(v[i], t[i]);
+    for (int i = 0; i < NV; ++i)
+      if (tid + 256 * i < n4) add4(v[i], t[i]);  // lanes past the row keep v = 0
   }
   if (y4) {  // t = y + slot_out[slot 0] + slot_out[slot 1] + ... (in order), x += t
     float4 t[NV];
@@ -167,24 +171,23 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
     for (int j0 = 0; j0 < k; j0 += B) {
       int sl[B];
 #pragma unroll
-      for (int q = 0; q < B; ++q) sl[q] = j0 + q < k ? slot_of[m * k + j0 + q] : 0;
+      for (int q = 0; q < B; ++q) sl[q] = slot_of[m * k + min(j0 + q, k - 1)];
       float4 u[NV][B];
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int q = 0; q < B; ++q) {
-          const int c = tid + 256 * i;
-          u[i][q] = (c < n4 && j0 + q < k) ? s4[static_cast<int64_t>(sl[q]) * n4 + c]
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+          const int c = min(tid + 256 * i, n4 - 1);
+          u[i][q] = s4[static_cast<int64_t>(sl[q]) * n4 + c];
         }
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int q = 0; q < B; ++q)
-          if (j0 + q < k) add4(t[i], u[i][q]);
+        for (int q = 0; q < B; ++q) add4(t[i], j0 + q < k ? u[i][q] : make_float4(0.f, 0.f, 0.f, 0.f));
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) add4(v[i], t[i]);
+    for (int i = 0; i < NV; ++i)
+      if (tid + 256 * i < n4) add4(v[i], t[i]);  // lanes past the row keep v = 0
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {

@@ -154,8 +154,11 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
 constexpr int kRouteSplits = 32;  // most split-k partials a routing call sums
 
-// Grid ceil(M / 4), 4 waves: wave w routes row 4 blockIdx.x + w. The logits are the sum of KS
-// partials part[q * M * E + row * E + e] (KS = 1: part holds the logits), written to rlog.
+// Grid ceil(M / 4), 4 waves: wave w routes row 4 blockIdx.x + w. The logits are the sum of KS <= NS
+// partials part[q * M * E + row * E + e] (KS = 1: part holds the logits), written to rlog. The NS
+// loads of a column are unconditional (slots past KS re-read the last one and are not added), so
+// they are all in flight together rather than issued one by one behind branches.
+template <int NS>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* part, int M, int E, int k,
                                                          int renorm, int KS, float* rlog,
                                                          int32_t* __restrict__ sel, float* __restrict__ gate) {
@@ -167,14 +170,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* part, int 
   float* l = lg + wave * 256;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = lane + 64 * i;
-    if (c < E) {
-      float v[kRouteSplits];
+    if (64 * i >= E) break;
+    const int c = min(lane + 64 * i, E - 1);
+    const float* pc = part + static_cast<int64_t>(row) * E + c;
+    float v[NS];
 #pragma unroll
-      for (int q = 0; q < kRouteSplits; ++q) v[q] = q < KS ? part[q * pstride + static_cast<int64_t>(row) * E + c] : 0.f;
-      float sum = 0.f;
+    for (int q = 0; q < NS; ++q) v[q] = pc[min(q, KS - 1) * pstride];
+    float sum = 0.f;
 #pragma unroll
-      for (int q = 0; q < kRouteSplits; ++q) sum += v[q];
+    for (int q = 0; q < NS; ++q) sum += q < KS ? v[q] : 0.f;
+    if (lane + 64 * i < E) {
       l[c] = sum;
       rlog[static_cast<int64_t>(row) * E + c] = sum;
     }
@@ -622,7 +627,10 @@ int moe_route(const float* part, int splits, int M, int E, int k, int renorm, fl
     return fail(DG_ERR_UNSUPPORTED, "routing limits: 1<=M<=256, E<=256, k<=min(16,E), at most 32 partials");
   {
     ProfScope ps("moe_topk", s);
-    route_topk_kernel<<<(M + 3) / 4, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    const unsigned g = (M + 3) / 4;
+    if (splits <= 8) route_topk_kernel<8><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    else if (splits <= 16) route_topk_kernel<16><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    else route_topk_kernel<kRouteSplits><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
   }
   DG_LAUNCH_CHECK("route_topk_kernel");
   {
