@@ -21,7 +21,9 @@ What the pages fix:
 Readings where the pages are silent (parity of these against the real model
 is unpinned; they are internal definitions shared with the HIP path and
 listed in the design doc): pre-norm RMSNorm (unit gain, eps) before attention, before the MoE and before
-the LM head; no positional encoding; no biases; attention scale 1/sqrt(hd);
+the LM head; no positional encoding by default (rope_theta = 0), or, as an
+option, rotary position embedding of queries and keys at their cache
+positions (see rope below); no biases; attention scale 1/sqrt(hd);
 GQA query head j reads KV head floor(j * Hkv / Hq); router = softmax over
 all experts, top-k chosen on the router logits (lowest index on ties), gate =
 the selected softmax probability (not renormalised), shared expert weight 1;
@@ -57,6 +59,7 @@ class ModelShape:
     canvas: int = 256
     rms_eps: float = 1e-6
     renorm_gates: bool = False
+    rope_theta: float = 0.0
 
 
 def rms_norm(x: np.ndarray, eps: float) -> np.ndarray:
@@ -93,6 +96,24 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos0: int, causal: 
             s = np.where(np.arange(L)[None, :] <= qpos, s, -np.inf)
         out[j] = softmax(s, axis=-1) @ v[kv]
     return out
+
+
+def rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """Rotary position embedding of x [..., M, hd] at the given M positions.
+
+    The pages give no positional scheme; they name a Gemma backbone ([P3]
+    "Encoder-denoiser design") with a context of up to 256K tokens ([P4]
+    "Gemma-based MoE backbone", table). Reading: the rotary embedding of the
+    Gemma family in its "rotate half" form: for j < hd/2 the pair
+    (x_j, x_{j+hd/2}) is turned by the angle pos * theta^(-2j/hd).
+    """
+    hd = x.shape[-1]
+    half = hd // 2
+    inv = float(theta) ** (-2.0 * np.arange(half) / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
 def ffn(h: np.ndarray, w: dict, gated: bool, prefix: str = "") -> np.ndarray:
@@ -161,6 +182,10 @@ def layer_forward(lw: dict, x: np.ndarray, cache_k: np.ndarray, cache_v: np.ndar
     q = (h @ lw["wq"].T).reshape(M, Hq, hd).transpose(1, 0, 2)
     k = (h @ lw["wk"].T).reshape(M, Hkv, hd).transpose(1, 0, 2)
     v = (h @ lw["wv"].T).reshape(M, Hkv, hd).transpose(1, 0, 2)
+    if shape.rope_theta > 0:
+        pos = pos0 + np.arange(M)
+        q = rope(q, pos, shape.rope_theta)
+        k = rope(k, pos, shape.rope_theta)
     cache_k[:, pos0:pos0 + M] = k
     cache_v[:, pos0:pos0 + M] = v
     L = pos0 + M

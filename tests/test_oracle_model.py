@@ -251,3 +251,57 @@ def test_denoise_step_canvas_attends_bidirectionally():
     c2[-1] = (c2[-1] + 1) % s["vocab"]
     l2 = M.denoise_step(W, cache, c2, None, shape)
     assert np.abs(l1[0] - l2[0]).max() > 1e-9  # the first position sees the last one
+
+
+# ------------------------------------------------------------------ rotary position embedding
+def test_rope_closed_forms():
+    x = np.array([[[1.0, 0.0]]])  # hd = 2: one pair, frequency theta^0 = 1
+    for p in (0.0, 1.0, 2.5, 1000.0):
+        assert np.allclose(M.rope(x, [p], 10000.0)[0, 0], [np.cos(p), np.sin(p)], atol=1e-12)
+    rng = np.random.default_rng(0)
+    y = rng.normal(size=(3, 5, 8))
+    assert np.array_equal(M.rope(y, np.zeros(5), 10000.0), y)  # position 0 is the identity
+    # hd = 4: the second pair turns at theta^(-1/2) per position, and pairs are (0, 2) and (1, 3)
+    z = np.array([[[0.0, 1.0, 0.0, 0.0]]])
+    w = 100.0 ** -0.5 * 3.0
+    assert np.allclose(M.rope(z, [3.0], 100.0)[0, 0], [0.0, np.cos(w), 0.0, np.sin(w)], atol=1e-12)
+
+
+def test_rope_is_a_rotation_and_depends_on_relative_position():
+    rng = np.random.default_rng(1)
+    q = rng.normal(size=(2, 6, 16))
+    k = rng.normal(size=(2, 6, 16))
+    pq = rng.integers(0, 5000, 6)
+    pk = rng.integers(0, 5000, 6)
+    rq = M.rope(q, pq, 10000.0)
+    # norms of every (j, j + hd/2) pair are kept
+    n0 = q[..., :8] ** 2 + q[..., 8:] ** 2
+    n1 = rq[..., :8] ** 2 + rq[..., 8:] ** 2
+    assert np.allclose(n0, n1)
+    # composition: turning by a then by b is turning by a + b
+    assert np.allclose(M.rope(M.rope(q, pq, 500.0), pk, 500.0), M.rope(q, pq + pk, 500.0))
+    # scores depend on the positions only through their difference
+    s0 = np.einsum("hmd,hmd->hm", rq, M.rope(k, pk, 10000.0))
+    s1 = np.einsum("hmd,hmd->hm", M.rope(q, pq + 777, 10000.0), M.rope(k, pk + 777, 10000.0))
+    assert np.allclose(s0, s1)
+
+
+def test_layer_with_rope_rotates_cached_keys_and_queries():
+    import dataclasses
+    s, shape0 = tiny_shape()
+    shape = dataclasses.replace(shape0, rope_theta=10000.0)
+    W = synthetic.SyntheticWeights(s, seed=9, dtype="f32", sigma=0.5)
+    lw = W["layers"][0]
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(5, shape.d_model))
+    ck = np.zeros((shape.n_kv_heads, 16, shape.head_dim))
+    cv = np.zeros_like(ck)
+    M.layer_forward(lw, x, ck, cv, 7, shape, causal=True)
+    h = M.rms_norm(x, shape.rms_eps)
+    k = (h @ lw["wk"].T).reshape(5, shape.n_kv_heads, shape.head_dim).transpose(1, 0, 2)
+    assert np.allclose(ck[:, 7:12], M.rope(k, np.arange(7, 12), 10000.0))
+    assert not np.allclose(ck[:, 7:12], k)
+    # without rope the same layer stores the plain keys
+    ck0 = np.zeros_like(ck)
+    M.layer_forward(lw, x, ck0, np.zeros_like(ck), 7, shape0, causal=True)
+    assert np.allclose(ck0[:, 7:12], k)
