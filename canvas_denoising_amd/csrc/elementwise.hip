@@ -401,3 +401,75 @@ int zero_fill(void* p, size_t bytes, hipStream_t s) {
 }
 
 }  // namespace dg
+
+namespace dg {
+
+// ------------------------------------------------------------ rotary positions
+// Rotary position embedding (optional; the model's reading: the Gemma family's "rotate half" form):
+// for j < hd / 2 the pair (x_j, x_{j + hd/2}) of every query and key head at cache position p is
+// turned by the angle p * theta^(-2j / hd). cos and sin of every (position, j) are tabulated once,
+// in double precision and rounded to float, so the rotation itself is a few multiplies.
+
+// table[p][j] = (cos, sin) of p * theta^(-2j/hd), p < n_pos, j < hd / 2
+__global__ void rope_table_kernel(double theta, int hd, int64_t n_pos, float2* __restrict__ table) {
+  const int half = hd / 2;
+  const int64_t n = n_pos * half;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int64_t p = e / half;
+    const int j = static_cast<int>(e - p * half);
+    const double a = static_cast<double>(p) * pow(theta, -2.0 * j / hd);
+    table[e] = make_float2(static_cast<float>(cos(a)), static_cast<float>(sin(a)));
+  }
+}
+
+// One thread per (row, head, pair): query heads of q (row-major [M][Hq * hd], ld ldq; skipped when q
+// is null) and key heads of the cache rows at positions pos0 .. pos0 + M - 1 ([Hkv][cap][hd], head
+// stride kv_stride), rotated in place in fp32 and rounded back to T.
+template <typename T>
+__global__ void rope_kernel(T* __restrict__ q, int64_t ldq, T* __restrict__ kc, int64_t kv_stride, int pos0, int M,
+                            int Hq, int Hkv, int hd, const float2* __restrict__ table) {
+  const int half = hd / 2;
+  const int H = (q ? Hq : 0) + Hkv;
+  const int64_t n = static_cast<int64_t>(M) * H * half;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int j = static_cast<int>(e % half);
+  const int64_t rh = e / half;
+  const int head = static_cast<int>(rh % H);
+  const int row = static_cast<int>(rh / H);
+  const int pos = pos0 + row;
+  T* x;
+  if (q && head < Hq) x = q + static_cast<int64_t>(row) * ldq + static_cast<int64_t>(head) * hd;
+  else x = kc + static_cast<int64_t>(head - (q ? Hq : 0)) * kv_stride + static_cast<int64_t>(pos) * hd;
+  const float2 cs = table[static_cast<int64_t>(pos) * half + j];
+  const float a = to_f32<T>(x[j]), b = to_f32<T>(x[j + half]);
+  x[j] = from_f32<T>(a * cs.x - b * cs.y);
+  x[j + half] = from_f32<T>(b * cs.x + a * cs.y);
+}
+
+int rope_table(double theta, int hd, int64_t n_pos, float2* table, hipStream_t s) {
+  const int64_t n = n_pos * (hd / 2);
+  if (n == 0) return DG_OK;
+  rope_table_kernel<<<grid_for(n), 256, 0, s>>>(theta, hd, n_pos, table);
+  DG_LAUNCH_CHECK("rope_table_kernel");
+  return DG_OK;
+}
+
+int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, int M, int Hq, int Hkv, int hd,
+               const float2* table, int dtype, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(M) * ((q ? Hq : 0) + Hkv) * (hd / 2);
+  if (n == 0) return DG_OK;
+  ProfScope ps("rope", s);
+  const unsigned grid = static_cast<unsigned>((n + 255) / 256);
+  if (dtype == DG_BF16)
+    rope_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<bf16_t*>(q), ldq, static_cast<bf16_t*>(kc), kv_stride, pos0,
+                                             M, Hq, Hkv, hd, table);
+  else
+    rope_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(q), ldq, static_cast<float*>(kc), kv_stride, pos0, M,
+                                            Hq, Hkv, hd, table);
+  DG_LAUNCH_CHECK("rope_kernel");
+  return DG_OK;
+}
+
+}  // namespace dg

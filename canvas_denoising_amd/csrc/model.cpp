@@ -54,6 +54,9 @@ int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* 
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, const ExpertsFp8* q8, hipStream_t s);
+int rope_table(double theta, int hd, int64_t n_pos, float2* table, hipStream_t s);
+int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, int M, int Hq, int Hkv, int hd,
+               const float2* table, int dtype, hipStream_t s);
 int quantize_fp8(const void* src, int64_t src_stride, void* codes, int64_t code_stride, float* scales, int E, int R,
                  int K, int gr, int gw, hipStream_t s);
 int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s);
@@ -215,6 +218,7 @@ int check_desc(const dg_model_desc* d) {
   if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return fail(DG_ERR_UNSUPPORTED, "top_k must be in [1, min(16, n_experts)]");
   if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return fail(DG_ERR_INVALID, "rms_eps must be finite and >= 0");
   if (d->gated != 0 && d->gated != 1) return fail(DG_ERR_INVALID, "gated must be 0 or 1");
+  if (!(d->rope_theta >= 0.f) || !isfinite(d->rope_theta)) return fail(DG_ERR_INVALID, "rope_theta must be finite and >= 0");
   return DG_OK;
 }
 
@@ -230,11 +234,12 @@ struct StepGraph {
 // ----------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
-      sc, u, sc_hid, P, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, total;
+      sc, u, sc_hid, P, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, rope,
+      total;
   int64_t gpart_floats;
 };
 
-static WsLayout ws_layout(const dg_model_desc& d) {
+static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   const size_t es = esize(d);
   const int64_t C = d.canvas, D = d.d_model, QW = static_cast<int64_t>(d.n_q_heads) * d.head_dim;
   const int64_t CK = C * d.top_k;
@@ -277,6 +282,8 @@ static WsLayout ws_layout(const dg_model_desc& d) {
   w.row_stats = take(C * 8);
   w.stop = take(sizeof(dg_stop_state));
   w.samp = take(sample_workspace_bytes(C, d.vocab));
+  // rotary embedding: (cos, sin) per cache position and frequency
+  w.rope = take(d.rope_theta > 0.f ? static_cast<size_t>(capacity) * (d.head_dim / 2) * 8 : 0);
   w.total = cur;
   return w;
 }
@@ -364,6 +371,9 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     }
     DG_TRY(run_gemm(c, g, s, "qkv_proj", false));
   }
+  if (d.rope_theta > 0.f)
+    DG_TRY(rope_apply(kv_only ? nullptr : wsp<void>(c, w.q), QW, kv_k(c, l), c->cap * hd, pos0, M, d.n_q_heads,
+                      d.n_kv_heads, hd, wsp<float2>(c, w.rope), d.dtype, s));
   if (kv_only) return DG_OK;
   DG_TRY(attention(wsp<void>(c, w.q), QW, kv_k(c, l), kv_v(c, l), c->cap * hd, M, d.n_q_heads, d.n_kv_heads, hd,
                    pos0, causal ? 1 : 0, wsp<float>(c, w.part_o), wsp<float>(c, w.part_ml), wsp<void>(c, w.o), QW,
@@ -705,7 +715,7 @@ size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity) {
 
 size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity) {
   if (check_desc(desc) != DG_OK || capacity < 0) return 0;
-  return ws_layout(*desc).total;
+  return ws_layout(*desc, capacity).total;
 }
 
 int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_t capacity, void* d_workspace,
@@ -718,11 +728,14 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
   if (capacity % kVBlock != 0) return fail(DG_ERR_CAPACITY, "KV capacity must be a multiple of 32");
   for (const void* p : {d_weights, d_kv, d_workspace})
     if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return fail(DG_ERR_INVALID, "device buffers must be 256-byte aligned");
-  const WsLayout wl = ws_layout(*desc);
+  const WsLayout wl = ws_layout(*desc, capacity);
   if (ws_bytes < wl.total) return fail(DG_ERR_CAPACITY, "workspace too small (see dg_workspace_size)");
   DG_TRY(zero_fill(d_workspace, wl.total, nullptr));
   // attention reads whole 32-position V blocks and weights unused positions by 0: keep them finite
   DG_TRY(zero_fill(d_kv, dg_kv_bytes(desc, capacity), nullptr));
+  if (desc->rope_theta > 0.f)
+    DG_TRY(rope_table(desc->rope_theta, desc->head_dim, capacity,
+                      reinterpret_cast<float2*>(static_cast<char*>(d_workspace) + wl.rope), nullptr));
   DG_HIP(hipStreamSynchronize(nullptr));
   dg_ctx* c = new dg_ctx;
   c->d = *desc;

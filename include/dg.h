@@ -70,6 +70,12 @@ typedef struct dg_model_desc {
   int32_t dtype;        /* DG_BF16 or DG_F32 */
   float rms_eps;
   int32_t renorm_gates; /* 0: gate = softmax prob of the expert (default) */
+  float rope_theta;     /* 0: no positional encoding (default); > 0: rotary
+                         * embedding of queries and keys at their cache
+                         * positions p, pairs (j, j + head_dim/2) turned by
+                         * p * rope_theta^(-2j/head_dim) (the Gemma family's
+                         * form; [P3] "Encoder-denoiser design" names the
+                         * backbone, the pages give no positional scheme) */
 } dg_model_desc;
 
 /* Sampler settings ([P4] "Standard sampling settings" table: 48 steps,

@@ -20,7 +20,7 @@ from oracle import fp8 as OF
 from oracle import model as OM
 
 from gpu_util import announce, need_gpu, to_f64, torch
-from test_gpu_model import assert_close, build, ids_tensor, router_flags
+from test_gpu_model import ROUTER_TIE, assert_close, build, ids_tensor, router_flags
 
 pytestmark = pytest.mark.gpu
 
@@ -112,7 +112,7 @@ def test_fp8_layer_matches_oracle(libs, gated):
     ref8, info = OM.layer_forward(V8["layers"][0], x0.astype(np.float64), kv.k[0], kv.v[0], 0, shape, False)
     kv = OM.KVCache.empty(shape, 512)
     ref16, _ = OM.layer_forward(W["layers"][0], x0.astype(np.float64), kv.k[0], kv.v[0], 0, shape, False)
-    keep = OM.router_margin(info["router_logits"], shape.top_k) > 1e-2
+    keep = OM.router_margin(info["router_logits"], shape.top_k) > ROUTER_TIE
     got = to_f64(x)[keep]
     assert_close(got, ref8[keep], 2e-2, "fp8 layer output")
     # the step from the input is what the experts changed: compare those deltas
@@ -202,20 +202,22 @@ def test_fp8_moe_layer_full_size(libs):
     hd, G = d.head_dim, d.n_q_heads // d.n_kv_heads
     k = (h @ lw["wk"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
     v = (h @ lw["wv"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
-    rows = np.array([7, 200])
+    rows = np.arange(3, C, 13)
     q = (h[rows] @ lw["wq"].T).reshape(len(rows), d.n_q_heads, hd).transpose(1, 0, 2)
     o = np.stack([OM.softmax(q[j] @ k[j // G].T / np.sqrt(hd)) @ v[j // G] for j in range(d.n_q_heads)])
     x1 = xf[rows] + o.transpose(1, 0, 2).reshape(len(rows), -1) @ lw["wo"].T
     h2 = OM.rms_norm(x1, shape.rms_eps)
     r = h2 @ lw["wr"].T
+    # the whole layer on the first 2 candidate rows whose k-th / (k+1)-th router logits are no near-tie
+    pick = np.flatnonzero(OM.router_margin(r, d.top_k) > ROUTER_TIE)[:2]
+    print(f"rows through the whole layer: {rows[pick].tolist()} ({len(pick)} of {len(rows)} candidates)")
+    assert len(pick) == 2
+    rows, x1, h2, r = rows[pick], x1[pick], h2[pick], r[pick]
     sel = OM.topk_from_logits(r, d.top_k)
     gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
     y = OM.ffn(h2, lw, True, prefix="sh_")
     for i in range(len(rows)):
         for j in range(d.top_k):
             y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
-    ref = x1 + y
-    keep = OM.router_margin(r, d.top_k) > 1e-2
-    print(f"sampled rows kept (no router near-tie): {int(keep.sum())} of {len(rows)}")
-    assert_close(to_f64(x)[rows][keep], ref[keep], 2e-2, "fp8 layer output (sampled rows)")
+    assert_close(to_f64(x)[rows], x1 + y, 2e-2, "fp8 layer output (sampled rows)")
     model.close()

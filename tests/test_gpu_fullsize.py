@@ -17,7 +17,7 @@ from oracle import model as OM
 from oracle import sampler as OS
 
 from gpu_util import announce, need_gpu, to_f64, torch
-from test_gpu_model import assert_close
+from test_gpu_model import ROUTER_TIE, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +29,13 @@ def libs():
     return _lib, configs, runtime
 
 
-def test_moe_layer_full_size(libs):
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+def test_moe_layer_full_size(libs, rope):
     L, configs, runtime = libs
-    announce("full-size MoE layer (d 2816, 128 experts, 4096 cached)")
+    announce(f"full-size MoE layer (d 2816, 128 experts, 4096 cached) rope={rope}")
     w = configs.moe_layer_bf16()
     d = w.desc
+    d.rope_theta = rope
     model = runtime.Model(d, w.capacity, seed=0, sigma=0.02)
     past, C, D, hd = w.prompt, d.canvas, d.d_model, d.head_dim
     kv_n = d.n_kv_heads * past * hd
@@ -57,6 +59,8 @@ def test_moe_layer_full_size(libs):
     h = OM.rms_norm(xf, shape.rms_eps)
     k = (h @ lw["wk"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
     v = (h @ lw["wv"].T).reshape(C, d.n_kv_heads, hd).transpose(1, 0, 2)
+    if rope > 0:
+        k = OM.rope(k, past + np.arange(C), rope)
     assert_close(to_f64(K[0, :, past:past + C]), k, 2e-2, "canvas K (all rows)")
     kc = np.concatenate([synthetic.bf16_bits_to_f32(kb).astype(np.float64), k], axis=1)
     vc = np.concatenate([synthetic.bf16_bits_to_f32(vb).astype(np.float64), v], axis=1)
@@ -66,10 +70,13 @@ def test_moe_layer_full_size(libs):
     assert np.array_equal(OM.topk_from_logits(r_gpu, d.top_k), sel_gpu)
     counts = np.bincount(sel_gpu.ravel(), minlength=d.n_experts)
     print(f"tokens per expert: min {counts.min()} max {counts.max()}")
-    # sampled rows through the whole layer
-    rows = np.array([0, 97, 255])
+    # sampled rows through the whole layer: the oracle's router on 24 candidate rows, then the whole
+    # layer on the first 3 of them whose k-th / (k+1)-th logits are not a near-tie
+    rows = np.arange(0, C, 11)
     hq = h[rows]
     q = (hq @ lw["wq"].T).reshape(len(rows), d.n_q_heads, hd).transpose(1, 0, 2)
+    if rope > 0:
+        q = OM.rope(q, past + rows, rope)
     o = np.empty((d.n_q_heads, len(rows), hd))
     G = d.n_q_heads // d.n_kv_heads
     for j in range(d.n_q_heads):
@@ -80,16 +87,17 @@ def test_moe_layer_full_size(libs):
     h2 = OM.rms_norm(x1, shape.rms_eps)
     r = h2 @ lw["wr"].T
     assert_close(r_gpu[rows], r, 2e-2, "router logits (sampled rows)")
+    pick = np.flatnonzero(OM.router_margin(r, d.top_k) > ROUTER_TIE)[:3]
+    print(f"rows through the whole layer: {rows[pick].tolist()} ({len(pick)} of {len(rows)} candidates)")
+    assert len(pick) == 3
+    rows, x1, h2, r = rows[pick], x1[pick], h2[pick], r[pick]
     sel = OM.topk_from_logits(r, d.top_k)
     gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
     y = OM.ffn(h2, lw, True, prefix="sh_")
     for i in range(len(rows)):
         for j in range(d.top_k):
             y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
-    ref = x1 + y
-    keep = OM.router_margin(r, d.top_k) > 1e-2
-    print(f"sampled rows kept (no router near-tie): {int(keep.sum())} of {len(rows)}")
-    assert_close(to_f64(x)[rows][keep], ref[keep], 2e-2, "layer output (sampled rows)")
+    assert_close(to_f64(x)[rows], x1 + y, 2e-2, "layer output (sampled rows)")
     model.close()
 
 

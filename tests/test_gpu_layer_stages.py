@@ -12,7 +12,7 @@ import synthetic
 from oracle import model as OM
 
 from gpu_util import announce, need_gpu, to_f64, torch
-from test_gpu_model import assert_close, build, tol_for
+from test_gpu_model import ROUTER_TIE, assert_close, build, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,7 @@ def test_layer_stages(libs, dtype, gated, causal, M, past):
                                 np.concatenate([to_f64(V[0, :, :past]), np.zeros((Hkv, 256 - past, hd))], axis=1),
                                 past, shape, causal)
     # the oracle routes on its own float64 logits: near-tie rows may pick another expert
-    keep = OM.router_margin(r, shape.top_k) > 1e-2
+    keep = OM.router_margin(r, shape.top_k) > ROUTER_TIE
     assert_close(to_f64(x)[keep], y_ref[keep], tol, "layer output")
     # the layer leaves h = RMSNorm(its output), the next layer's input
     h_gpu = to_f64(model.buffer(L.DG_BUF_H, model.dtype, (64, D)))[:M]

@@ -6,7 +6,7 @@ activations and KV entries within a relative error of tol per row
 (||gpu - ref|| / ||ref||) and |gpu - ref| <= 4 tol (|ref| + rms(ref row)) per
 element, tol = 2e-2 for bf16 and 2e-4 for fp32. Router decisions are checked bit-exact teacher-forced
 (the oracle's top-k on the GPU's router logits), and against the oracle's own
-router except tokens whose 8th/9th (k-th/k+1-th) logits are within 1e-2.
+router except tokens whose 8th/9th (k-th/k+1-th) logits are within ROUTER_TIE.
 """
 import numpy as np
 import pytest
@@ -54,15 +54,15 @@ def assert_close(gpu, ref, tol, what="", elem_factor=4.0):
 
 
 def build(libs, dtype="bf16", gated=1, n_layers=2, d=256, Hq=4, Hkv=2, hd=64, E=8, k=2, F=128, Fs=256, V=512,
-          dsc=128, canvas=64, capacity=512, seed=3, sigma=0.05):
+          dsc=128, canvas=64, capacity=512, seed=3, sigma=0.05, rope=0.0):
     L, configs, runtime = libs
     dt = L.DG_BF16 if dtype == "bf16" else L.DG_F32
-    desc = configs.desc(n_layers, d, Hq, Hkv, hd, E, k, F, Fs, gated, V, dsc, dt, canvas=canvas)
+    desc = configs.desc(n_layers, d, Hq, Hkv, hd, E, k, F, Fs, gated, V, dsc, dt, canvas=canvas, rope_theta=rope)
     model = runtime.Model(desc, capacity, seed=seed, sigma=sigma)
     W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=seed, dtype=dtype, sigma=sigma)
     shape = OM.ModelShape(n_layers=n_layers, d_model=d, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, n_experts=E,
                           top_k=k, d_expert=F, d_shared=Fs, gated=bool(gated), vocab=V, d_selfcond=dsc,
-                          canvas=canvas)
+                          canvas=canvas, rope_theta=rope)
     return model, W, shape
 
 
@@ -75,10 +75,17 @@ def gpu_kv(model, n_layers, upto):
     return to_f64(K[:, :, :upto]), to_f64(V[:, :, :upto])
 
 
-CASES = [("bf16", 1), ("bf16", 0), ("f32", 0), ("f32", 1)]
+# (dtype, gated, rotary base: 0 = no positional encoding)
+CASES = [("bf16", 1, 0.0), ("bf16", 0, 0.0), ("f32", 0, 0.0), ("f32", 1, 0.0), ("bf16", 1, 10000.0), ("f32", 0, 500.0)]
 
 
-def router_flags(infos, top_k, thr=1e-2):
+# Router near-tie width. The router's input h is rounded to bf16 (relative 2^-9 per element), so at
+# these shapes (K = 256, weights ~0.05, logits ~1) the difference of two router logits carries a
+# rounding error of about 5e-3 (one sigma); 3e-2 is about six sigma.
+ROUTER_TIE = 3e-2
+
+
+def router_flags(infos, top_k, thr=ROUTER_TIE):
     """Rows whose k-th / (k+1)-th router logits are within thr in any layer (near-ties)."""
     f = None
     for info in infos:
@@ -91,18 +98,18 @@ def keep_axis(a, keep, axis):
     return np.compress(keep, a, axis=axis)
 
 
-@pytest.mark.parametrize("dtype,gated", CASES)
-def test_prefill_denoise_commit_match_oracle(libs, dtype, gated):
+@pytest.mark.parametrize("dtype,gated,rope", CASES)
+def test_prefill_denoise_commit_match_oracle(libs, dtype, gated, rope):
     """Prefill (ragged chunks), denoise step 0, self-conditioned step 1, commit.
 
     Tokens flagged as router near-ties in any layer (k-th vs (k+1)-th logit within
-    1e-2 in the oracle) are excluded from the continuous comparisons: rounding may
+    ROUTER_TIE in the oracle) are excluded from the continuous comparisons: rounding may
     legitimately give them a different expert, which changes their activations
     outright. Their count is reported.
     """
     L, configs, runtime = libs
-    announce(f"model {dtype} gated={gated}")
-    model, W, shape = build(libs, dtype=dtype, gated=gated)
+    announce(f"model {dtype} gated={gated} rope={rope}")
+    model, W, shape = build(libs, dtype=dtype, gated=gated, rope=rope)
     tol = tol_for(dtype)
     n_prompt = 100  # two chunks of the 64-row canvas, the second ragged
     prompt = ids_tensor(1, n_prompt, shape.vocab)
@@ -205,7 +212,7 @@ def test_forward_layer_heavy_expert(libs, dtype, causal):
     model.forward_layer(0, x, 256, causal)
     torch.cuda.synchronize()
     y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, causal)
-    keep = OM.router_margin(info["router_logits"], shape.top_k) > 1e-2
+    keep = OM.router_margin(info["router_logits"], shape.top_k) > ROUTER_TIE
     assert_close(to_f64(x)[keep], y_ref[keep], tol_for(dtype), "layer output")
     counts = np.bincount(info["sel"][:, 0], minlength=2)
     assert counts.max() > 64
