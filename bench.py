@@ -2,7 +2,7 @@
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|copy] [--no-cpu-baseline]
-                    [--sampler-mode M] [--experts bf16|fp8]
+                    [--sampler-mode M] [--experts bf16|fp8] [--prefill-rows R]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
 workload's hot path over one batch of synthetic input that is already
@@ -183,6 +183,7 @@ def bench_full(args):
 
     w = configs.full_loop_bf16(args.layers)
     d = w.desc
+    d.prefill_rows = args.prefill_rows
     C, V, S = d.canvas, d.vocab, w.max_steps
     n_blocks = (args.steps + S - 1) // S + 1
     capacity = w.prompt + (n_blocks + 1) * C
@@ -305,7 +306,7 @@ def bench_full(args):
                    "canvas_tokens_per_s": steps_per_s * C,
                    "committed_tokens_per_s": commits * C / dt,
                    "commits": commits, "stops": stops,
-                   "prefill_tokens_per_s": w.prompt / prefill_s,
+                   "prefill_tokens_per_s": w.prompt / prefill_s, "prefill_rows": d.prefill_rows,
                    "step_roofline_ms": step_roof_s * 1e3,
                    "step_roofline_frac": step_roof_s / (dt / args.steps),
                    "kernels_us": {k: v["avg_us"] for k, v in sorted(prof.items())},
@@ -389,6 +390,7 @@ def bench_blockar(args):
 
     w = configs.block_ar_bf16()
     d = w.desc
+    d.prefill_rows = args.prefill_rows
     C, V, S = d.canvas, d.vocab, w.max_steps
     log(f"[bench] model {d.n_layers} layers, KV capacity {w.capacity}")
     model = Model(d, w.capacity, seed=0)
@@ -443,7 +445,8 @@ def bench_blockar(args):
                                f"committed one after another, KV length {w.prompt} -> {w.prompt + w.blocks * C}; "
                                "random-init weights",
                    "denoise_steps_per_s": steps / dt, "canvas_tokens_per_s": steps * C / dt, "stops": stops,
-                   "prefill_tokens_per_s": w.prompt / prefill_s, "prefill_s": prefill_s},
+                   "prefill_tokens_per_s": w.prompt / prefill_s, "prefill_s": prefill_s,
+                   "prefill_rows": d.prefill_rows},
     }
     model.close()
     return out
@@ -486,6 +489,9 @@ def main():
                     help="sampler workload: dg_sched.mode flags (1 either-stop, 2 group acceptance, 4 categorical)")
     ap.add_argument("--experts", choices=["bf16", "fp8"], default="bf16",
                     help="full workload: routed-expert weights in the model dtype or as FP8 E4M3 (opt-in mode)")
+    ap.add_argument("--prefill-rows", type=int, default=2048,
+                    help="rows per prefill chunk (0 = the canvas); chunks above 256 rows run the experts as "
+                         "token-tiled GEMMs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

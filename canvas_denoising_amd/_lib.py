@@ -34,7 +34,8 @@ class dg_model_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k", "d_expert",
         "d_shared", "gated", "vocab", "canvas", "d_selfcond", "dtype")] + [
-        ("rms_eps", ctypes.c_float), ("renorm_gates", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+        ("rms_eps", ctypes.c_float), ("renorm_gates", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+        ("prefill_rows", ctypes.c_int32)]
 
 
 class dg_sched(ctypes.Structure):
@@ -49,7 +50,7 @@ class dg_stop_state(ctypes.Structure):
                 ("stopped", ctypes.c_int32), ("steps_run", ctypes.c_int32)]
 
 
-assert ctypes.sizeof(dg_sched) == 40 and ctypes.sizeof(dg_stop_state) == 16 and ctypes.sizeof(dg_model_desc) == 68
+assert ctypes.sizeof(dg_sched) == 40 and ctypes.sizeof(dg_stop_state) == 16 and ctypes.sizeof(dg_model_desc) == 72
 
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t

@@ -15,9 +15,10 @@ from . import _lib as L
 
 
 def desc(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k, d_expert, d_shared, gated, vocab,
-         d_selfcond, dtype, canvas=256, rms_eps=1e-6, renorm_gates=0, rope_theta=0.0) -> L.dg_model_desc:
+         d_selfcond, dtype, canvas=256, rms_eps=1e-6, renorm_gates=0, rope_theta=0.0,
+         prefill_rows=0) -> L.dg_model_desc:
     return L.dg_model_desc(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k, d_expert, d_shared,
-                           gated, vocab, canvas, d_selfcond, dtype, rms_eps, renorm_gates, rope_theta)
+                           gated, vocab, canvas, d_selfcond, dtype, rms_eps, renorm_gates, rope_theta, prefill_rows)
 
 
 def shape_dict(d: L.dg_model_desc) -> dict:

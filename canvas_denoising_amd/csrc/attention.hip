@@ -416,6 +416,15 @@ __global__ void attn_f32_kernel(AttnArgs a) {
 constexpr int kAttnWGs = DG_ATT_WGS;  // target workgroups of a launch
 int attn_max_splits() { return kMergeMax; }
 
+// Upper bound of splits x M over the launches attention() makes for M query rows (the rows of its
+// partial buffers).
+int64_t attn_partial_rows(int M, int Hq, int Hkv) {
+  const int G = Hq / Hkv;
+  const int qtiles = (G * M + kWGRows - 1) / kWGRows;
+  const int splits = std::max(1, std::min(attn_max_splits(), (kAttnWGs + qtiles * Hkv - 1) / (qtiles * Hkv)));
+  return static_cast<int64_t>(splits) * M;
+}
+
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
               int dtype, hipStream_t s) {

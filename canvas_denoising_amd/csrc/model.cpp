@@ -45,15 +45,17 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
               int dtype, hipStream_t s);
 int attn_max_splits();
+int64_t attn_partial_rows(int M, int Hq, int Hkv);
 int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
                hipStream_t s);
 int moe_route(const float* part, int splits, int M, int E, int k, int renorm, float* rlog, int32_t* sel,
-              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s);
+              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, int32_t* tiles,
+              hipStream_t s);
 int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* slot_of, int M, int D, int k,
                 hipStream_t s);
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
-                int dtype, const ExpertsFp8* q8, hipStream_t s);
+                int dtype, const ExpertsFp8* q8, const int32_t* tiles, int M, int k, hipStream_t s);
 int rope_table(double theta, int hd, int64_t n_pos, float2* table, hipStream_t s);
 int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, int M, int Hq, int Hkv, int hd,
                const float2* table, int dtype, hipStream_t s);
@@ -219,6 +221,10 @@ int check_desc(const dg_model_desc* d) {
   if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return fail(DG_ERR_INVALID, "rms_eps must be finite and >= 0");
   if (d->gated != 0 && d->gated != 1) return fail(DG_ERR_INVALID, "gated must be 0 or 1");
   if (!(d->rope_theta >= 0.f) || !isfinite(d->rope_theta)) return fail(DG_ERR_INVALID, "rope_theta must be finite and >= 0");
+  if (d->prefill_rows != 0 && (d->prefill_rows < d->canvas || d->prefill_rows > 4096))
+    return fail(DG_ERR_UNSUPPORTED, "prefill_rows must be 0 or in [canvas, 4096]");
+  if (d->prefill_rows > 256 && d->n_experts > 128)
+    return fail(DG_ERR_UNSUPPORTED, "prefill chunks of more than 256 rows need n_experts <= 128");
   return DG_OK;
 }
 
@@ -235,13 +241,17 @@ struct StepGraph {
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
       sc, u, sc_hid, P, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, rope,
-      total;
+      tiles, total;
   int64_t gpart_floats;
 };
 
+// rows of one layer pass: a canvas, or a prefill / commit chunk
+static int64_t pass_rows(const dg_model_desc& d) { return std::max<int64_t>(d.canvas, d.prefill_rows); }
+
 static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   const size_t es = esize(d);
-  const int64_t C = d.canvas, D = d.d_model, QW = static_cast<int64_t>(d.n_q_heads) * d.head_dim;
+  const int64_t D = d.d_model, QW = static_cast<int64_t>(d.n_q_heads) * d.head_dim;
+  const int64_t C = pass_rows(d);  // activation rows (the canvas-only buffers below use d.canvas)
   const int64_t CK = C * d.top_k;
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -254,8 +264,10 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.h = take(C * D * es);
   w.q = take(C * QW * es);
   w.o = take(C * QW * es);
-  w.part_o = take(static_cast<size_t>(attn_max_splits()) * d.n_q_heads * C * d.head_dim * 4);
-  w.part_ml = take(static_cast<size_t>(attn_max_splits()) * d.n_q_heads * C * 2 * 4);
+  int64_t prow = 0;  // splits x rows of the attention partials, over every pass size up to C
+  for (int m = 1; m <= C; ++m) prow = std::max(prow, attn_partial_rows(m, d.n_q_heads, d.n_kv_heads));
+  w.part_o = take(static_cast<size_t>(prow) * d.n_q_heads * d.head_dim * 4);
+  w.part_ml = take(static_cast<size_t>(prow) * d.n_q_heads * 2 * 4);
   w.rlog = take(C * d.n_experts * 4);
   w.sel = take(CK * 4);
   w.gate = take(CK * 4);
@@ -266,24 +278,27 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.act = take(CK * d.d_expert * es);
   w.slot_out = take(CK * D * 4);
   w.sh_act = take(C * d.d_shared * es);
-  w.sc = take(C * D * 4);
-  w.u = take(C * D * es);
-  w.sc_hid = take(C * d.d_selfcond * es);
-  w.P = take(static_cast<size_t>(C) * d.vocab * es);
-  w.scpart = take(static_cast<size_t>(sc_embed_splits(static_cast<int>(D), d.vocab, d.dtype)) * C * D * 4);
-  w.gpart_floats = 32 * C * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
+  // canvas-only buffers: self-conditioning, split-K scratch, sampler state
+  const int64_t Cc = d.canvas;
+  w.sc = take(Cc * D * 4);
+  w.u = take(Cc * D * es);
+  w.sc_hid = take(Cc * d.d_selfcond * es);
+  w.P = take(static_cast<size_t>(Cc) * d.vocab * es);
+  w.scpart = take(static_cast<size_t>(sc_embed_splits(static_cast<int>(D), d.vocab, d.dtype)) * Cc * D * 4);
+  w.gpart_floats = 32 * Cc * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
   w.gpart = take(w.gpart_floats * 4);
   w.gpart_aux = take(w.gpart_floats * 4);  // split-K scratch of the second stream
   w.y_sh = take(C * D * 4);
-  w.canvas = take(C * 4);
-  w.pred = take(C * 4);
-  w.accept = take(C);
-  w.entropy = take(C * 4);
-  w.row_stats = take(C * 8);
+  w.canvas = take(Cc * 4);
+  w.pred = take(Cc * 4);
+  w.accept = take(Cc);
+  w.entropy = take(Cc * 4);
+  w.row_stats = take(Cc * 8);
   w.stop = take(sizeof(dg_stop_state));
-  w.samp = take(sample_workspace_bytes(C, d.vocab));
+  w.samp = take(sample_workspace_bytes(Cc, d.vocab));
   // rotary embedding: (cos, sin) per cache position and frequency
   w.rope = take(d.rope_theta > 0.f ? static_cast<size_t>(capacity) * (d.head_dim / 2) * 8 : 0);
+  w.tiles = take((2 + CK / 128 + d.n_experts + 8) * 4);  // token-tile list of a chunk
   w.total = cur;
   return w;
 }
@@ -438,7 +453,7 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     DG_TRY(moe_route(splits > 1 ? wsp<float>(c, w.gpart) : wsp<float>(c, w.rlog), splits, M, d.n_experts, d.top_k,
                      d.renorm_gates, wsp<float>(c, w.rlog), wsp<int32_t>(c, w.sel), wsp<float>(c, w.gate),
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<int32_t>(c, w.slot_of),
-                     wsp<float>(c, w.slot_gate), s));
+                     wsp<float>(c, w.slot_gate), M > 256 ? wsp<int32_t>(c, w.tiles) : nullptr, s));
   }
   if (kSharedMode == 2) DG_TRY(fork_shared());
   ExpertsFp8 q8;
@@ -450,7 +465,8 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
   }
   DG_TRY(moe_experts(h, D, wp(c, c->wl.ex_gu[l]), wp(c, c->wl.ex_down[l]), d.n_experts, d.d_expert, D, d.gated,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<float>(c, w.slot_gate),
-                     wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, c->fp8 ? &q8 : nullptr, s));
+                     wsp<void>(c, w.act), wsp<float>(c, w.slot_out), d.dtype, c->fp8 ? &q8 : nullptr,
+                     M > 256 ? wsp<int32_t>(c, w.tiles) : nullptr, M, d.top_k, s));
   // join, then x += shared + sum of the token's gated expert outputs (fixed order); h = RMSNorm(x)
   if (kSharedMode != 0) DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
   if (fused)
@@ -464,8 +480,9 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
 static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
   const dg_model_desc& d = c->d;
   float* x = wsp<float>(c, c->wsl.x);
-  for (int c0 = 0; c0 < n; c0 += d.canvas) {
-    const int M = std::min(d.canvas, n - c0);
+  const int chunk = static_cast<int>(pass_rows(d));
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int M = std::min(chunk, n - c0);
     DG_TRY(embed(wp(c, c->wl.embed), ids + c0, nullptr, x, M, d.d_model, d.vocab, d.dtype, s));
     DG_TRY(rmsnorm(x, wsp<void>(c, c->wsl.h), M, d.d_model, d.rms_eps, d.dtype, s));
     for (int l = 0; l < d.n_layers; ++l)
@@ -834,7 +851,7 @@ int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32
   DG_TRY(check_ctx(ctx));
   if (layer < 0 || layer >= ctx->d.n_layers) return fail(DG_ERR_INVALID, "layer out of range");
   if (!d_x) return fail(DG_ERR_INVALID, "d_x is NULL");
-  if (rows < 1 || rows > ctx->d.canvas) return fail(DG_ERR_SHAPE, "rows must be in [1, canvas]");
+  if (rows < 1 || rows > pass_rows(ctx->d)) return fail(DG_ERR_SHAPE, "rows must be in [1, max(canvas, prefill_rows)]");
   if (ctx->len + rows > ctx->cap) return fail(DG_ERR_CAPACITY, "rows do not fit in the KV cache");
   hipStream_t s = as_stream(stream);
   DG_TRY(rmsnorm(d_x, wsp<void>(ctx, ctx->wsl.h), rows, ctx->d.d_model, ctx->d.rms_eps, ctx->d.dtype, s));

@@ -32,14 +32,16 @@
 #include <type_traits>
 
 #include "dg_common.h"
+#include "dma.h"
 #include "mfma.h"
 #include "prof.h"
 #include "tiles.h"
 
 namespace dg {
 
-constexpr int kMaxTokens = 256;  // rows per routing call
-constexpr int kMaskWords = kMaxTokens / 32;
+constexpr int kMaxTokens = 256;        // rows per routing call of a canvas
+constexpr int kMaxTokensLarge = 4096;  // rows per routing call of a prefill chunk (E <= 128)
+constexpr int kTileTokens = 128;       // token rows per workgroup of the token-tiled expert kernels
 
 // keep the larger value, the lower expert index on ties (exact, so every lane agrees)
 __device__ inline void argmax_step(float& bv, int& be, float ov, int oe) {
@@ -94,57 +96,71 @@ __device__ inline void route_row(const float* lg, int E, int k, int renorm, int 
   }
 }
 
-// one workgroup of 1024 threads: expert sizes, offsets and the expert-major, token-ascending slot order
+// one workgroup of 1024 threads: expert sizes, offsets and the expert-major, token-ascending slot order.
+// MW mask words per expert cover 32 MW rows (E <= min(256, 16384 / MW)). With `tiles`, also the list of the
+// experts' 128-token tiles: tiles[0] = their number, tiles[1 + i] = e * 65536 + (tile within e),
+// experts in order.
+template <int MW>
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ sel,
                                                        const float* __restrict__ gate, int M, int E, int k,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ slot_of,
-                                                       float* __restrict__ slot_gate) {
-  __shared__ uint32_t mask[256 * kMaskWords];  // E <= 256
+                                                       float* __restrict__ slot_gate, int32_t* __restrict__ tiles) {
+  constexpr int kE = 16384 / MW < 256 ? 16384 / MW : 256;
+  __shared__ uint32_t mask[kE * MW];
   __shared__ int32_t offs[257];
+  __shared__ int32_t toffs[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < E * kMaskWords; i += 1024) mask[i] = 0u;
+  for (int i = tid; i < E * MW; i += 1024) mask[i] = 0u;
   __syncthreads();
   for (int p = tid; p < M * k; p += 1024) {
     const int row = p / k;
-    atomicOr(&mask[sel[p] * kMaskWords + (row >> 5)], 1u << (row & 31));
+    atomicOr(&mask[sel[p] * MW + (row >> 5)], 1u << (row & 31));
   }
   __syncthreads();
   if (wave == 0) {
     int cnt[4];
-    int tot = 0;
+    int tot = 0, ttot = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane * 4 + i;
       int c = 0;
       if (e < E)
-        for (int w = 0; w < kMaskWords; ++w) c += __popc(mask[e * kMaskWords + w]);
+        for (int w = 0; w < MW; ++w) c += __popc(mask[e * MW + w]);
       cnt[i] = c;
       tot += c;
+      ttot += (c + kTileTokens - 1) / kTileTokens;
     }
-    int incl = tot;
+    int incl = tot, tincl = ttot;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
+      const int to = __shfl_up(tincl, d, 64);
+      if (lane >= d) { incl += o; tincl += to; }
     }
-    int run = incl - tot;
+    int run = incl - tot, trun = tincl - ttot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane * 4 + i;
-      if (e < E) offs[e] = run;
+      if (e < E) { offs[e] = run; toffs[e] = trun; }
       run += cnt[i];
+      trun += (cnt[i] + kTileTokens - 1) / kTileTokens;
     }
-    if (lane == 63) offs[E] = incl;
+    if (lane == 63) { offs[E] = incl; toffs[E] = tincl; }
   }
   __syncthreads();
   for (int i = tid; i <= E; i += 1024) offsets[i] = offs[i];
+  if (tiles) {
+    if (tid == 0) tiles[0] = toffs[E];
+    for (int e = tid; e < E; e += 1024)
+      for (int j = toffs[e]; j < toffs[e + 1]; ++j) tiles[1 + j] = e * 65536 + (j - toffs[e]);
+  }
   for (int p = tid; p < M * k; p += 1024) {
     const int row = p / k;
     const int e = sel[p];
     int rank = 0;
-    for (int w = 0; w < (row >> 5); ++w) rank += __popc(mask[e * kMaskWords + w]);
-    rank += __popc(mask[e * kMaskWords + (row >> 5)] & ((1u << (row & 31)) - 1u));
+    for (int w = 0; w < (row >> 5); ++w) rank += __popc(mask[e * MW + w]);
+    rank += __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
     const int slot = offs[e] + rank;
     perm[slot] = row;
     slot_of[p] = slot;
@@ -620,11 +636,130 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
     });
 }
 
+// ------------------------------------------------------------ token-tiled experts (prefill chunks)
+// With a prefill chunk of thousands of rows an expert holds hundreds of tokens, and the product is
+// worth tiling like a dense GEMM rather than streaming the weights once per 48 tokens: a workgroup
+// takes one entry of the tile list (128 of one expert's tokens) against one tile group of its
+// weights (gate/up: 32 features of gate and up; down: 64 outputs) and runs K in stages of 64
+// through a 3-deep LDS ring filled by asynchronous copies: the 128 gathered token rows (128-byte
+// rows, XOR-swizzled as in the dense GEMM) and the group's 2 G weight tiles (already in fragment
+// order, so a lane reads its fragment at byte 16 l). Each of the 4 waves owns 32 tokens against
+// all G weight tiles, so a wave holds both the gate and the up sums of its features.
+constexpr int kTileStages = 3;
+
+template <bool DOWN, bool GATED>
+__global__ __launch_bounds__(256) void expert_tile_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ w, int F, int D, int per_e,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
+    const float* __restrict__ slot_gate, bf16_t* __restrict__ act, float* __restrict__ out) {
+  constexpr int gw = DOWN ? 1 : (GATED ? 2 : 1);
+  constexpr int G = DOWN ? kDownGroup : gw * kGuBlocks;
+  constexpr int ROWB = 128;                        // bytes per staged token row: 64 bf16
+  constexpr int SA = kTileTokens * ROWB;           // token rows of a stage
+  constexpr int SB = 2 * G * 1024;                 // weight tiles of a stage (2 k-tiles)
+  constexpr int SS = SA + SB;
+  constexpr int ALPW = kTileTokens / 8 / kExpWaves;  // token-row copies per wave per stage (8 rows each)
+  constexpr int BLPW = 2 * G / kExpWaves;          // weight-tile copies per wave per stage
+  constexpr int LPS = ALPW + BLPW;
+  static_assert(BLPW >= 1 && (2 * G) % kExpWaves == 0, "weight tiles per stage must split over the waves");
+  __shared__ __align__(16) unsigned char smem[kTileStages * SS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int ti = (j / per_e) * 8 + xcd, q = j % per_e;  // the tile's workgroups share an XCD (its L2)
+  if (ti >= tiles[0]) return;
+  const int entry = tiles[1 + ti];
+  const int e = entry >> 16, t0 = (entry & 0xFFFF) * kTileTokens;
+  const int beg = offsets[e], rows = min(kTileTokens, offsets[e + 1] - beg - t0);
+  const int K = DOWN ? F : D;
+  const int KT = K / 32, nk = K / 64;
+  const bf16_t* bg = w + static_cast<int64_t>(e) * (DOWN ? static_cast<int64_t>(D) * F : static_cast<int64_t>(gw) * F * D) +
+                     static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
+  const bf16_t* asrc[ALPW];
+#pragma unroll
+  for (int i = 0; i < ALPW; ++i) {
+    const int r = (wave * ALPW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    const int slot = beg + t0 + min(r, rows - 1);  // rows past the tile's tokens repeat its last one
+    const int64_t arow = DOWN ? slot : perm[slot];
+    asrc[i] = A + arow * lda + c * 8;
+  }
+  auto issue = [&](int st, int slot) {
+    unsigned char* base = smem + slot * SS;
+#pragma unroll
+    for (int i = 0; i < ALPW; ++i) dma16(asrc[i] + st * 64, base + (wave * ALPW + i) * 8 * ROWB);
+#pragma unroll
+    for (int i = 0; i < BLPW; ++i) {
+      const int tb = wave * BLPW + i;  // k-tile 2 st + tb / G, tile tb % G of the group
+      dma16(bg + (static_cast<int64_t>(2 * st + tb / G) * G + tb % G) * kTileElems, base + SA + tb * 1024);
+    }
+  };
+  f32x4_t acc[2][G];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < kTileStages - 1; ++st)
+    if (st < nk) issue(st, st);
+  for (int st = 0; st < nk; ++st) {
+    wait_stages<LPS, kTileStages>(min(kTileStages - 2, nk - 1 - st));
+    // stage st is in LDS for every wave and every wave has consumed stage st - 1 (a bare barrier:
+    // the fence of __syncthreads() would drain the copies still in flight)
+    __builtin_amdgcn_s_barrier();
+    if (st + kTileStages - 1 < nk) issue(st + kTileStages - 1, (st + kTileStages - 1) % kTileStages);
+    const unsigned char* sa = smem + (st % kTileStages) * SS;
+    const unsigned char* sb = sa + SA;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[2], bfr[G];
+      const int c = ks * 4 + g4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = wave * 32 + t * 16 + fr;
+        af[t] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((c ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) bfr[g] = *reinterpret_cast<const bf16x8_t*>(sb + (ks * G + g) * 1024 + lane * 16);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[t][g] = Frag<bf16_t>::mma(af[t], bfr[g], acc[t][g]);
+    }
+  }
+  // epilogue: lane holds tokens wave * 32 + 16 t + 4 (lane / 16) + i of the tile, group row 16 g + lane % 16
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 32 + t * 16 + g4 * 4 + i;
+      if (r < rows) {
+        const int64_t slot = beg + t0 + r;
+        if constexpr (DOWN) {
+          const float gs = slot_gate[slot];
+          float* o = out + slot * D + q * 16 * kDownGroup + fr;
+#pragma unroll
+          for (int g = 0; g < G; ++g) o[g * 16] = gs * acc[t][g][i];
+        } else {
+          bf16_t* o = act + slot * F + q * 16 * kGuBlocks + fr;
+#pragma unroll
+          for (int bb = 0; bb < kGuBlocks; ++bb)
+            o[bb * 16] = f32_to_bf16(GATED ? gelu_erf(acc[t][bb][i]) * acc[t][kGuBlocks + bb][i] : gelu_erf(acc[t][bb][i]));
+        }
+      }
+    }
+}
+
 // ------------------------------------------------------------------- host
+// tiles (may be null; needed for M > 256): the token-tile list of permute_kernel, 2 + M k / 128 + E ints
 int moe_route(const float* part, int splits, int M, int E, int k, int renorm, float* rlog, int32_t* sel,
-              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, hipStream_t s) {
-  if (M < 1 || M > kMaxTokens || E > 256 || k > 16 || k > E || splits < 1 || splits > kRouteSplits)
-    return fail(DG_ERR_UNSUPPORTED, "routing limits: 1<=M<=256, E<=256, k<=min(16,E), at most 32 partials");
+              float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, int32_t* tiles,
+              hipStream_t s) {
+  if (M < 1 || M > kMaxTokensLarge || E > 256 || k > 16 || k > E || splits < 1 || splits > kRouteSplits)
+    return fail(DG_ERR_UNSUPPORTED, "routing limits: 1<=M<=4096, E<=256, k<=min(16,E), at most 32 partials");
+  if (M > kMaxTokens && E > 16384 / (kMaxTokensLarge / 32))
+    return fail(DG_ERR_UNSUPPORTED, "routing more than 256 rows at once needs n_experts <= 128");
   {
     ProfScope ps("moe_topk", s);
     const unsigned g = (M + 3) / 4;
@@ -635,7 +770,11 @@ int moe_route(const float* part, int splits, int M, int E, int k, int renorm, fl
   DG_LAUNCH_CHECK("route_topk_kernel");
   {
     ProfScope ps("moe_permute", s);
-    permute_kernel<<<1, 1024, 0, s>>>(sel, gate, M, E, k, offsets, perm, slot_of, slot_gate);
+    if (M <= kMaxTokens)
+      permute_kernel<kMaxTokens / 32><<<1, 1024, 0, s>>>(sel, gate, M, E, k, offsets, perm, slot_of, slot_gate, tiles);
+    else
+      permute_kernel<kMaxTokensLarge / 32><<<1, 1024, 0, s>>>(sel, gate, M, E, k, offsets, perm, slot_of, slot_gate,
+                                                              tiles);
   }
   DG_LAUNCH_CHECK("permute_kernel");
   return DG_OK;
@@ -675,14 +814,39 @@ int moe_combine(float* x, const float* y, const float* slot_out, const int32_t* 
 
 // q8 (optional): FP8 codes and scales of the same layer's routed experts; when given, the expert
 // kernels stream those instead of w_gu / w_down (bf16 models only).
+// tiles (optional, bf16 only): the token-tile list of moe_route for M rows; the experts then run as
+// token-tiled GEMMs (M k / 128 + E tiles at most) instead of weight streams.
 int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down, int E, int F, int D, int gated,
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
-                int dtype, const ExpertsFp8* q8, hipStream_t s) {
+                int dtype, const ExpertsFp8* q8, const int32_t* tiles, int M, int k, hipStream_t s) {
   if (F % (16 * kGuBlocks) != 0 || D % (16 * kDownGroup) != 0)
     return fail(DG_ERR_UNSUPPORTED, "expert width and d_model must be multiples of 32 and 64");
   const int per_gu = F / (16 * kGuBlocks);
   const int per_dn = D / (16 * kDownGroup);
   const dim3 g1(E * per_gu), g2(E * per_dn);
+  if (tiles && !q8 && dtype == DG_BF16) {
+    if (F % 64 != 0 || D % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "token-tiled experts need widths that are multiples of 64");
+    const int t8 = (static_cast<int>((static_cast<int64_t>(M) * k + kTileTokens - 1) / kTileTokens) + E + 7) / 8 * 8;
+    const bf16_t* hh = static_cast<const bf16_t*>(h);
+    bf16_t* a = static_cast<bf16_t*>(act);
+    {
+      ProfScope ps("expert_tile_gateup", s);
+      if (gated)
+        expert_tile_kernel<false, true><<<t8 * per_gu, 256, 0, s>>>(hh, ldh, static_cast<const bf16_t*>(w_gu), F, D,
+                                                                    per_gu, offsets, perm, tiles, slot_gate, a, out);
+      else
+        expert_tile_kernel<false, false><<<t8 * per_gu, 256, 0, s>>>(hh, ldh, static_cast<const bf16_t*>(w_gu), F, D,
+                                                                     per_gu, offsets, perm, tiles, slot_gate, a, out);
+    }
+    DG_LAUNCH_CHECK("expert_tile_kernel (gate/up)");
+    {
+      ProfScope ps("expert_tile_down", s);
+      expert_tile_kernel<true, false><<<t8 * per_dn, 256, 0, s>>>(a, F, static_cast<const bf16_t*>(w_down), F, D,
+                                                                  per_dn, offsets, perm, tiles, slot_gate, a, out);
+    }
+    DG_LAUNCH_CHECK("expert_tile_kernel (down)");
+    return DG_OK;
+  }
   if (q8) {
     if (dtype != DG_BF16 || F % 64 != 0 || D % 64 != 0)
       return fail(DG_ERR_UNSUPPORTED, "FP8 experts need a bf16 model and widths that are multiples of 64");

@@ -76,6 +76,12 @@ typedef struct dg_model_desc {
                          * p * rope_theta^(-2j/head_dim) (the Gemma family's
                          * form; [P3] "Encoder-denoiser design" names the
                          * backbone, the pages give no positional scheme) */
+  int32_t prefill_rows; /* 0: prefill and commit run in chunks of `canvas`
+                         * rows; else chunk rows in [canvas, 4096] (more
+                         * than 256 needs n_experts <= 128): the workspace
+                         * grows with it, and chunks of more than 256 rows
+                         * run the routed experts (bf16) as token-tiled
+                         * GEMMs of 128 tokens per workgroup */
 } dg_model_desc;
 
 /* Sampler settings ([P4] "Standard sampling settings" table: 48 steps,
@@ -342,7 +348,7 @@ int dg_kv_set_length(dg_ctx* ctx, int64_t length);
 /* Encoder mode over the prompt ([P3] "Encoder-denoiser design": the query is
  * processed the standard, causal way and its KV cache is shared with the
  * denoiser; [P4] "System architecture": prefill builds the KV cache). Runs the
- * layers causally over d_prompt_ids (int32[n_prompt]) in chunks of `canvas`
+ * layers causally over d_prompt_ids (int32[n_prompt]) in chunks of `canvas` (or `prefill_rows`)
  * rows appended at the committed length, then length += n_prompt.
  * DG_ERR_CAPACITY (nothing enqueued) if length + n_prompt > capacity. */
 int dg_prefill_kv(dg_ctx* ctx, const int32_t* d_prompt_ids, int32_t n_prompt, void* stream);
@@ -370,7 +376,7 @@ int dg_denoise_step(dg_ctx* ctx, const int32_t* d_canvas, int32_t step, const vo
 int dg_commit_block(dg_ctx* ctx, const int32_t* d_block_ids, void* stream);
 
 /* One layer on a caller-provided fp32 residual d_x [rows x d_model] (in/out),
- * rows <= canvas, attending to cache [0, length) plus the rows (causal or
+ * rows <= max(canvas, prefill_rows), attending to cache [0, length) plus the rows (causal or
  * not); the rows' K/V are written at [length, length + rows); length is not
  * changed. */
 int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32_t causal,

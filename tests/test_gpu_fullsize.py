@@ -221,3 +221,59 @@ def test_block_ar_full_size(libs):
     assert model.length == w.capacity
     assert torch.equal(model.kv, before)
     model.close()
+
+
+def test_moe_layer_full_size_prefill_chunk(libs):
+    """A 2048-row causal chunk at full size (128 experts, ~128 tokens each): routing of 2048 rows and
+    the token-tiled expert GEMMs, on sampled rows."""
+    L, configs, runtime = libs
+    announce("full-size 2048-row causal chunk (token-tiled experts), 1024 cached")
+    w = configs.moe_layer_bf16()
+    d = w.desc
+    d.prefill_rows = 2048
+    past, M, D, hd = 1024, 2048, d.d_model, d.head_dim
+    model = runtime.Model(d, past + M, seed=0, sigma=0.02)
+    kv_n = d.n_kv_heads * past * hd
+    kb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
+    vb = synthetic.normal_bf16_bits(3, synthetic.TID_KV_INPUT + 1, kv_n, 1.0).reshape(d.n_kv_heads, past, hd)
+    model.kv_write(0, torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16),
+                   torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16), 0)
+    L.dg_kv_set_length(model.ctx, past)
+    x0 = synthetic.normal_f32(5, synthetic.TID_X_INPUT, M * D, 1.0).reshape(M, D)
+    x = torch.from_numpy(x0.copy()).cuda()
+    model.forward_layer(0, x, M, True)
+    torch.cuda.synchronize()
+    W = synthetic.SyntheticWeights(configs.shape_dict(d), seed=0, dtype="bf16", sigma=0.02, cache_experts=False)
+    lw = W["layers"][0]
+    shape = OM.ModelShape(n_layers=1, d_model=D, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads, head_dim=hd,
+                          n_experts=d.n_experts, top_k=d.top_k, d_expert=d.d_expert, d_shared=d.d_shared,
+                          gated=True, vocab=d.vocab, d_selfcond=d.d_selfcond)
+    xf = x0.astype(np.float64)
+    h = OM.rms_norm(xf, shape.rms_eps)
+    k = (h @ lw["wk"].T).reshape(M, d.n_kv_heads, hd).transpose(1, 0, 2)
+    v = (h @ lw["wv"].T).reshape(M, d.n_kv_heads, hd).transpose(1, 0, 2)
+    kc = np.concatenate([synthetic.bf16_bits_to_f32(kb).astype(np.float64), k], axis=1)
+    vc = np.concatenate([synthetic.bf16_bits_to_f32(vb).astype(np.float64), v], axis=1)
+    rows = np.arange(5, M, 97)
+    q = (h[rows] @ lw["wq"].T).reshape(len(rows), d.n_q_heads, hd).transpose(1, 0, 2)
+    G = d.n_q_heads // d.n_kv_heads
+    o = np.empty((d.n_q_heads, len(rows), hd))
+    for j in range(d.n_q_heads):
+        for i, r in enumerate(rows):  # causal: keys 0 .. past + r
+            s = q[j, i] @ kc[j // G, :past + r + 1].T / np.sqrt(hd)
+            o[j, i] = OM.softmax(s) @ vc[j // G, :past + r + 1]
+    x1 = xf[rows] + o.transpose(1, 0, 2).reshape(len(rows), -1) @ lw["wo"].T
+    h2 = OM.rms_norm(x1, shape.rms_eps)
+    r = h2 @ lw["wr"].T
+    pick = np.flatnonzero(OM.router_margin(r, d.top_k) > ROUTER_TIE)[:3]
+    print(f"rows through the whole layer: {rows[pick].tolist()} ({len(pick)} of {len(rows)} candidates)")
+    assert len(pick) == 3
+    rows, x1, h2, r = rows[pick], x1[pick], h2[pick], r[pick]
+    sel = OM.topk_from_logits(r, d.top_k)
+    gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
+    y = OM.ffn(h2, lw, True, prefix="sh_")
+    for i in range(len(rows)):
+        for j in range(d.top_k):
+            y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
+    assert_close(to_f64(x)[rows], x1 + y, 2e-2, "layer output of a 2048-row chunk (sampled rows)")
+    model.close()

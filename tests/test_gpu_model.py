@@ -383,3 +383,73 @@ def test_capacity_errors_leave_state(libs):
     with pytest.raises(L.DGError):
         model.denoise_step(ids_tensor(3, 64, shape.vocab), 0)
     model.close()
+
+
+@pytest.mark.parametrize("gated", [1, 0])
+def test_forward_layer_token_tiled_experts(libs, gated):
+    """Chunks of more than 256 rows: routing of up to 4096 rows and the token-tiled expert GEMMs (128
+    tokens per workgroup), with experts holding several ragged tiles."""
+    L, configs, runtime = libs
+    announce(f"forward_layer 1000 rows, token-tiled experts, gated={gated}")
+    # passes of up to 1024 rows (the canvas stays 64)
+    desc = configs.desc(1, 256, 4, 2, 64, 8, 2, 192, 128, gated, 256, 64, L.DG_BF16, canvas=64, prefill_rows=1024)
+    big = runtime.Model(desc, 2048, seed=3, sigma=0.05)
+    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=3, dtype="bf16", sigma=0.05)
+    shape = OM.ModelShape(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8, top_k=2,
+                          d_expert=192, d_shared=128, gated=bool(gated), vocab=256, d_selfcond=64, canvas=64)
+    past, rows = 37, 1000
+    rng = np.random.default_rng(5)
+    kp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
+    vp = rng.normal(size=(shape.n_kv_heads, past, shape.head_dim))
+    big.kv_write(0, torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), 0)
+    Kc, Vc = big.kv_view()
+    kv_ref = OM.KVCache.empty(shape, 2048)
+    kv_ref.k[0][:, :past] = to_f64(Kc[0, :, :past])
+    kv_ref.v[0][:, :past] = to_f64(Vc[0, :, :past])
+    L.dg_kv_set_length(big.ctx, past)
+    x = torch.from_numpy(rng.normal(size=(rows, shape.d_model)).astype(np.float32)).cuda()
+    x_ref = to_f64(x)
+    big.forward_layer(0, x, rows, True)
+    torch.cuda.synchronize()
+    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, True)
+    counts = np.bincount(info["sel"].ravel(), minlength=shape.n_experts)
+    print(f"tokens per expert: {counts.tolist()}")
+    assert counts.max() > 256  # several tiles of one expert
+    keep = OM.router_margin(info["router_logits"], shape.top_k) > ROUTER_TIE
+    assert_close(to_f64(x)[keep], y_ref[keep], 2e-2, "layer output (token-tiled experts)")
+    sel_gpu = big.buffer(L.DG_BUF_SEL, torch.int32, (64, shape.top_k))  # the first canvas-sized rows
+    r_gpu = to_f64(big.buffer(L.DG_BUF_ROUTER_LOGITS, torch.float32, (64, shape.n_experts)))
+    assert np.array_equal(OM.topk_from_logits(r_gpu, shape.top_k), sel_gpu.cpu().numpy())
+    big.close()
+
+
+def test_prefill_in_large_chunks_matches_oracle(libs):
+    """Prefill of 2500 tokens in chunks of 1024 rows (the last one ragged), then a denoising step."""
+    L, configs, runtime = libs
+    announce("prefill 2500 tokens in 1024-row chunks")
+    desc = configs.desc(2, 256, 4, 2, 64, 8, 2, 128, 256, 1, 512, 128, L.DG_BF16, canvas=64, prefill_rows=1024)
+    model = runtime.Model(desc, 2560 + 64, seed=3, sigma=0.05)
+    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=3, dtype="bf16", sigma=0.05)
+    shape = OM.ModelShape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8, top_k=2,
+                          d_expert=128, d_shared=256, gated=True, vocab=512, d_selfcond=128, canvas=64)
+    n = 2500
+    prompt = ids_tensor(1, n, shape.vocab)
+    model.prefill(prompt)
+    torch.cuda.synchronize()
+    assert model.length == n
+    cache = OM.KVCache.empty(shape, 2560 + 64)
+    infos = []
+    OM.encode(W, cache, prompt.cpu().numpy(), shape, infos=infos)
+    keep = ~router_flags(infos, shape.top_k)
+    print(f"prompt rows kept (no router near-tie): {int(keep.sum())} of {n}")
+    gk, gv = gpu_kv(model, shape.n_layers, n)
+    for l in range(shape.n_layers):
+        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n], keep, 1), 2e-2, f"prefill K {l}")
+        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n], keep, 1), 2e-2, f"prefill V {l}")
+    canvas = ids_tensor(2, shape.canvas, shape.vocab)
+    logits = model.denoise_step(canvas, 0)
+    torch.cuda.synchronize()
+    ref, _, cinfo = OM.denoise_step(W, cache.copy(), canvas.cpu().numpy(), None, shape, return_info=True)
+    cflag = router_flags(cinfo, shape.top_k)
+    assert_close(to_f64(logits)[~cflag], ref[~cflag], 2e-2, "step logits after a chunked prefill")
+    model.close()
