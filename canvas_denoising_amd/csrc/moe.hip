@@ -108,6 +108,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                                                        float* __restrict__ slot_gate, int32_t* __restrict__ tiles) {
   constexpr int kE = 16384 / MW < 256 ? 16384 / MW : 256;
   __shared__ uint32_t mask[kE * MW];
+  __shared__ uint16_t below[kE * MW];  // tokens of expert e in the mask words before word w
   __shared__ int32_t offs[257];
   __shared__ int32_t toffs[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -148,6 +149,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     }
     if (lane == 63) { offs[E] = incl; toffs[E] = tincl; }
   }
+  // running popcounts of each expert's mask words, so a token's rank is one lookup and one popcount
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int w = 0; w < MW; ++w) {
+      below[e * MW + w] = static_cast<uint16_t>(run);
+      run += __popc(mask[e * MW + w]);
+    }
+  }
   __syncthreads();
   for (int i = tid; i <= E; i += 1024) offsets[i] = offs[i];
   if (tiles) {
@@ -158,9 +167,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   for (int p = tid; p < M * k; p += 1024) {
     const int row = p / k;
     const int e = sel[p];
-    int rank = 0;
-    for (int w = 0; w < (row >> 5); ++w) rank += __popc(mask[e * MW + w]);
-    rank += __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
+    const int rank = below[e * MW + (row >> 5)] + __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
     const int slot = offs[e] + rank;
     perm[slot] = row;
     slot_of[p] = slot;
