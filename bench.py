@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|copy] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|prefill|copy]
+                    [--no-cpu-baseline]
                     [--sampler-mode M] [--experts bf16|fp8] [--prefill-rows R]
 
 Prints ONE JSON line (see the keys below). A step is one pass of the
@@ -22,6 +23,12 @@ resident in HBM:
   ``--experts fp8`` runs it with the routed experts' weights stored as FP8
   E4M3 with per-row scales (an opt-in mode at reduced weight precision,
   reported under its own metric name, never as the bf16 figure).
+* ``blockar``: block-autoregressive generation, a 32768-token prompt
+  prefilled (timed and reported separately), then 8 canvases denoised and
+  committed one after another; the value is committed tokens/s.
+* ``prefill``: encoder mode at scale, the 32768-token prompt of the
+  block-autoregressive workload prefilled into an empty cache in chunks of
+  ``--prefill-rows`` rows.
 * ``copy``: a plain 1 GiB device copy, the calibration run for the HBM
   byte counters of the profiles.
 
@@ -452,6 +459,44 @@ def bench_blockar(args):
     return out
 
 
+def bench_prefill(args):
+    """Encoder mode at scale: the 30-layer model prefills a 32768-token prompt (config 4's prologue) in
+    chunks of --prefill-rows rows; a step is one whole prefill into an empty cache."""
+    import torch
+    from canvas_denoising_amd import _lib as L
+    from canvas_denoising_amd import configs
+    from canvas_denoising_amd.runtime import Model
+
+    w = configs.block_ar_bf16()
+    d = w.desc
+    d.prefill_rows = args.prefill_rows
+    log(f"[bench] model {d.n_layers} layers, prompt {w.prompt}, chunks of {max(d.canvas, d.prefill_rows)} rows")
+    model = Model(d, w.prompt, seed=0)
+    prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
+    L.dg_synth_uniform_ids(5, 10, w.prompt, d.vocab, prompt)
+
+    def run(n):
+        for _ in range(n):
+            L.dg_kv_set_length(model.ctx, 0)
+            model.prefill(prompt)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    model.close()
+    return {
+        "metric": "prefill tokens/s (32768-token prompt)", "value": args.steps * w.prompt / dt, "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"encoder prefill of {w.prompt} uniform token ids, {d.n_layers} MoE layers "
+                               f"d_model {d.d_model}, 128 experts top-8, causal, random-init weights",
+                   "prefill_rows": max(d.canvas, d.prefill_rows)},
+    }
+
+
 def bench_copy(args):
     """Plain device-to-device copy of a known size: the calibration run for HBM byte counters
     (FETCH_SIZE / WRITE_SIZE per launch divided by the bytes copied)."""
@@ -474,7 +519,8 @@ def bench_copy(args):
             "config": {"workload": f"calibration copy of {n} bytes per launch"}}
 
 
-WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "blockar": bench_blockar, "copy": bench_copy}
+WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "blockar": bench_blockar, "prefill": bench_prefill,
+             "copy": bench_copy}
 
 
 def main():
@@ -498,9 +544,9 @@ def main():
         print("bench.py runs on exactly one GPU: libdg has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
-        args.steps = {"sampler": 480, "copy": 20}.get(args.workload, 96)
+        args.steps = {"sampler": 480, "copy": 20, "prefill": 3}.get(args.workload, 96)
     if args.warmup is None:
-        args.warmup = {"sampler": 48, "copy": 2}.get(args.workload, 4)
+        args.warmup = {"sampler": 48, "copy": 2, "prefill": 1}.get(args.workload, 4)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (libdg runs only on MI355X).", file=sys.stderr)
