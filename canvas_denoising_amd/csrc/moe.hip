@@ -653,25 +653,34 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
 // order, so a lane reads its fragment at byte 16 l). Each of the 4 waves owns 32 tokens against
 // all G weight tiles, so a wave holds both the gate and the up sums of its features.
 constexpr int kTileStages = 3;
+#ifndef DG_TILE_GROUPS
+#define DG_TILE_GROUPS 2
+#endif
+// weight tile groups per workgroup: each adds 4 waves and the group's weight tiles to a stage, and
+// divides the copies of the gathered token rows per flop by as much
+constexpr int kTileGroups = DG_TILE_GROUPS;
 
-template <bool DOWN, bool GATED>
-__global__ __launch_bounds__(256) void expert_tile_kernel(
+template <bool DOWN, bool GATED, int NG>
+__global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ w, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const float* __restrict__ slot_gate, bf16_t* __restrict__ act, float* __restrict__ out) {
+  constexpr int NW = kExpWaves * NG;
   constexpr int gw = DOWN ? 1 : (GATED ? 2 : 1);
   constexpr int G = DOWN ? kDownGroup : gw * kGuBlocks;
   constexpr int ROWB = 128;                        // bytes per staged token row: 64 bf16
   constexpr int SA = kTileTokens * ROWB;           // token rows of a stage
-  constexpr int SB = 2 * G * 1024;                 // weight tiles of a stage (2 k-tiles)
+  constexpr int SB = NG * 2 * G * 1024;            // weight tiles of a stage (NG groups x 2 k-tiles)
   constexpr int SS = SA + SB;
-  constexpr int ALPW = kTileTokens / 8 / kExpWaves;  // token-row copies per wave per stage (8 rows each)
-  constexpr int BLPW = 2 * G / kExpWaves;          // weight-tile copies per wave per stage
+  constexpr int ALPW = kTileTokens / 8 / NW;       // token-row copies per wave per stage (8 rows each)
+  constexpr int BLPW = NG * 2 * G / NW;            // weight-tile copies per wave per stage
   constexpr int LPS = ALPW + BLPW;
-  static_assert(BLPW >= 1 && (2 * G) % kExpWaves == 0, "weight tiles per stage must split over the waves");
+  static_assert(ALPW >= 1 && BLPW >= 1 && (NG * 2 * G) % NW == 0 && (kTileTokens / 8) % NW == 0,
+                "copies of a stage must split evenly over the waves");
   __shared__ __align__(16) unsigned char smem[kTileStages * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gi = wave / kExpWaves, wq = wave % kExpWaves;  // this wave's group and 32-token quarter
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   const int ti = (j / per_e) * 8 + xcd, q = j % per_e;  // the tile's workgroups share an XCD (its L2)
   if (ti >= tiles[0]) return;
@@ -681,7 +690,7 @@ __global__ __launch_bounds__(256) void expert_tile_kernel(
   const int K = DOWN ? F : D;
   const int KT = K / 32, nk = K / 64;
   const bf16_t* bg = w + static_cast<int64_t>(e) * (DOWN ? static_cast<int64_t>(D) * F : static_cast<int64_t>(gw) * F * D) +
-                     static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
+                     static_cast<int64_t>(q) * NG * KT * G * kTileElems + lane * 8;
   const bf16_t* asrc[ALPW];
 #pragma unroll
   for (int i = 0; i < ALPW; ++i) {
@@ -697,8 +706,10 @@ __global__ __launch_bounds__(256) void expert_tile_kernel(
     for (int i = 0; i < ALPW; ++i) dma16(asrc[i] + st * 64, base + (wave * ALPW + i) * 8 * ROWB);
 #pragma unroll
     for (int i = 0; i < BLPW; ++i) {
-      const int tb = wave * BLPW + i;  // k-tile 2 st + tb / G, tile tb % G of the group
-      dma16(bg + (static_cast<int64_t>(2 * st + tb / G) * G + tb % G) * kTileElems, base + SA + tb * 1024);
+      const int tb = wave * BLPW + i;  // group tb / 2G, k-tile 2 st + (tb % 2G) / G, tile tb % G
+      const int grp = tb / (2 * G), ks = (tb % (2 * G)) / G;
+      dma16(bg + (static_cast<int64_t>(grp) * KT * G + static_cast<int64_t>(2 * st + ks) * G + tb % G) * kTileElems,
+            base + SA + tb * 1024);
     }
   };
   f32x4_t acc[2][G];
@@ -717,14 +728,14 @@ __global__ __launch_bounds__(256) void expert_tile_kernel(
     __builtin_amdgcn_s_barrier();
     if (st + kTileStages - 1 < nk) issue(st + kTileStages - 1, (st + kTileStages - 1) % kTileStages);
     const unsigned char* sa = smem + (st % kTileStages) * SS;
-    const unsigned char* sb = sa + SA;
+    const unsigned char* sb = sa + SA + gi * 2 * G * 1024;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t af[2], bfr[G];
       const int c = ks * 4 + g4;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int r = wave * 32 + t * 16 + fr;
+        const int r = wq * 32 + t * 16 + fr;
         af[t] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((c ^ (r & 7)) << 4));
       }
 #pragma unroll
@@ -735,27 +746,40 @@ __global__ __launch_bounds__(256) void expert_tile_kernel(
         for (int g = 0; g < G; ++g) acc[t][g] = Frag<bf16_t>::mma(af[t], bfr[g], acc[t][g]);
     }
   }
-  // epilogue: lane holds tokens wave * 32 + 16 t + 4 (lane / 16) + i of the tile, group row 16 g + lane % 16
+  // epilogue: lane holds tokens wq * 32 + 16 t + 4 (lane / 16) + i of the tile, group row 16 g + lane % 16
+  const int qg = q * NG + gi;  // this wave's tile group within the expert
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wave * 32 + t * 16 + g4 * 4 + i;
+      const int r = wq * 32 + t * 16 + g4 * 4 + i;
       if (r < rows) {
         const int64_t slot = beg + t0 + r;
         if constexpr (DOWN) {
           const float gs = slot_gate[slot];
-          float* o = out + slot * D + q * 16 * kDownGroup + fr;
+          float* o = out + slot * D + qg * 16 * kDownGroup + fr;
 #pragma unroll
           for (int g = 0; g < G; ++g) o[g * 16] = gs * acc[t][g][i];
         } else {
-          bf16_t* o = act + slot * F + q * 16 * kGuBlocks + fr;
+          bf16_t* o = act + slot * F + qg * 16 * kGuBlocks + fr;
 #pragma unroll
           for (int bb = 0; bb < kGuBlocks; ++bb)
             o[bb * 16] = f32_to_bf16(GATED ? gelu_erf(acc[t][bb][i]) * acc[t][kGuBlocks + bb][i] : gelu_erf(acc[t][bb][i]));
         }
       }
     }
+}
+
+template <bool DOWN, bool GATED>
+static void launch_expert_tiles(int t8, int per_e, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* w,
+                                int F, int D, const int32_t* offsets, const int32_t* perm, const int32_t* tiles,
+                                const float* slot_gate, bf16_t* act, float* out) {
+  if (per_e % kTileGroups == 0)
+    expert_tile_kernel<DOWN, GATED, kTileGroups><<<t8 * (per_e / kTileGroups), 64 * kExpWaves * kTileGroups, 0, s>>>(
+        A, lda, w, F, D, per_e / kTileGroups, offsets, perm, tiles, slot_gate, act, out);
+  else
+    expert_tile_kernel<DOWN, GATED, 1><<<t8 * per_e, 64 * kExpWaves, 0, s>>>(A, lda, w, F, D, per_e, offsets, perm,
+                                                                           tiles, slot_gate, act, out);
 }
 
 // ------------------------------------------------------------------- host
@@ -839,17 +863,17 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
     {
       ProfScope ps("expert_tile_gateup", s);
       if (gated)
-        expert_tile_kernel<false, true><<<t8 * per_gu, 256, 0, s>>>(hh, ldh, static_cast<const bf16_t*>(w_gu), F, D,
-                                                                    per_gu, offsets, perm, tiles, slot_gate, a, out);
+        launch_expert_tiles<false, true>(t8, per_gu, s, hh, ldh, static_cast<const bf16_t*>(w_gu), F, D, offsets, perm,
+                                         tiles, slot_gate, a, out);
       else
-        expert_tile_kernel<false, false><<<t8 * per_gu, 256, 0, s>>>(hh, ldh, static_cast<const bf16_t*>(w_gu), F, D,
-                                                                     per_gu, offsets, perm, tiles, slot_gate, a, out);
+        launch_expert_tiles<false, false>(t8, per_gu, s, hh, ldh, static_cast<const bf16_t*>(w_gu), F, D, offsets, perm,
+                                          tiles, slot_gate, a, out);
     }
     DG_LAUNCH_CHECK("expert_tile_kernel (gate/up)");
     {
       ProfScope ps("expert_tile_down", s);
-      expert_tile_kernel<true, false><<<t8 * per_dn, 256, 0, s>>>(a, F, static_cast<const bf16_t*>(w_down), F, D,
-                                                                  per_dn, offsets, perm, tiles, slot_gate, a, out);
+      launch_expert_tiles<true, false>(t8, per_dn, s, a, F, static_cast<const bf16_t*>(w_down), F, D, offsets, perm,
+                                       tiles, slot_gate, a, out);
     }
     DG_LAUNCH_CHECK("expert_tile_kernel (down)");
     return DG_OK;
