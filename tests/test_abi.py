@@ -102,3 +102,27 @@ def test_fp8_expert_buffer_layout_and_validation(L):
         L.dg_quantize_experts_fp8(d, None, None)
     with pytest.raises(L.DGError):
         L.dg_ctx_use_expert_fp8(None, None)
+
+
+def test_prefill_rows_and_rope_validation(L):
+    from canvas_denoising_amd import configs
+    base = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8, top_k=2, d_expert=128,
+                d_shared=256, gated=1, vocab=512, d_selfcond=128, dtype=L.DG_BF16)
+
+    def mk(**kw):
+        a = dict(base, **kw)
+        return configs.desc(a["n_layers"], a["d_model"], a["n_q_heads"], a["n_kv_heads"], a["head_dim"],
+                            a["n_experts"], a["top_k"], a["d_expert"], a["d_shared"], a["gated"], a["vocab"],
+                            a["d_selfcond"], a["dtype"], canvas=64, rope_theta=a.get("rope", 0.0),
+                            prefill_rows=a.get("prefill_rows", 0))
+    ws0 = L.dg_workspace_size(mk(), 4096)
+    assert ws0 > 0
+    ws1 = L.dg_workspace_size(mk(prefill_rows=1024), 4096)
+    assert ws1 > ws0  # activations, routing tables and expert buffers grow with the chunk
+    assert L.dg_workspace_size(mk(prefill_rows=32), 4096) == 0      # below the canvas
+    assert L.dg_workspace_size(mk(prefill_rows=5000), 8192) == 0    # above 4096
+    assert L.dg_workspace_size(mk(prefill_rows=1024, n_experts=192), 4096) == 0  # > 256 rows needs E <= 128
+    assert L.dg_workspace_size(mk(prefill_rows=256, n_experts=192), 4096) > 0
+    # the rotary table is one (cos, sin) pair per cache position and frequency
+    assert L.dg_workspace_size(mk(rope=10000.0), 4096) - ws0 >= 4096 * 32 * 8
+    assert L.dg_workspace_size(mk(rope=-1.0), 4096) == 0

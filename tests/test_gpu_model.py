@@ -423,13 +423,16 @@ def test_forward_layer_token_tiled_experts(libs, gated):
     big.close()
 
 
-def test_prefill_in_large_chunks_matches_oracle(libs):
-    """Prefill of 2500 tokens in chunks of 1024 rows (the last one ragged), then a denoising step."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_in_large_chunks_matches_oracle(libs, dtype):
+    """Prefill of 2500 tokens in chunks of 1024 rows (the last one ragged), then a denoising step. bf16
+    runs the token-tiled experts; fp32 the weight-streaming passes over the 1024-row routing."""
     L, configs, runtime = libs
-    announce("prefill 2500 tokens in 1024-row chunks")
-    desc = configs.desc(2, 256, 4, 2, 64, 8, 2, 128, 256, 1, 512, 128, L.DG_BF16, canvas=64, prefill_rows=1024)
+    announce(f"prefill 2500 tokens in 1024-row chunks, {dtype}")
+    dt = L.DG_BF16 if dtype == "bf16" else L.DG_F32
+    desc = configs.desc(2, 256, 4, 2, 64, 8, 2, 128, 256, 1, 512, 128, dt, canvas=64, prefill_rows=1024)
     model = runtime.Model(desc, 2560 + 64, seed=3, sigma=0.05)
-    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=3, dtype="bf16", sigma=0.05)
+    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=3, dtype=dtype, sigma=0.05)
     shape = OM.ModelShape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8, top_k=2,
                           d_expert=128, d_shared=256, gated=True, vocab=512, d_selfcond=128, canvas=64)
     n = 2500
@@ -443,13 +446,14 @@ def test_prefill_in_large_chunks_matches_oracle(libs):
     keep = ~router_flags(infos, shape.top_k)
     print(f"prompt rows kept (no router near-tie): {int(keep.sum())} of {n}")
     gk, gv = gpu_kv(model, shape.n_layers, n)
+    tol = tol_for(dtype)
     for l in range(shape.n_layers):
-        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n], keep, 1), 2e-2, f"prefill K {l}")
-        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n], keep, 1), 2e-2, f"prefill V {l}")
+        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n], keep, 1), tol, f"prefill K {l}")
+        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n], keep, 1), tol, f"prefill V {l}")
     canvas = ids_tensor(2, shape.canvas, shape.vocab)
     logits = model.denoise_step(canvas, 0)
     torch.cuda.synchronize()
     ref, _, cinfo = OM.denoise_step(W, cache.copy(), canvas.cpu().numpy(), None, shape, return_info=True)
     cflag = router_flags(cinfo, shape.top_k)
-    assert_close(to_f64(logits)[~cflag], ref[~cflag], 2e-2, "step logits after a chunked prefill")
+    assert_close(to_f64(logits)[~cflag], ref[~cflag], tol, "step logits after a chunked prefill")
     model.close()
