@@ -221,3 +221,35 @@ def test_fp8_moe_layer_full_size(libs):
             y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
     assert_close(to_f64(x)[rows], x1 + y, 2e-2, "fp8 layer output (sampled rows)")
     model.close()
+
+
+def test_fp8_with_prefill_chunks(libs):
+    """FP8 experts in a 1024-row prefill chunk: the FP8 weight streams run over the 1024-row routing
+    (the token-tiled GEMMs are the bf16 path), then a denoising step; against the oracle with the
+    dequantised experts."""
+    L, configs, runtime = libs
+    announce("fp8 experts, prefill of 1500 tokens in 1024-row chunks")
+    desc = configs.desc(2, 256, 4, 2, 64, 8, 2, 128, 256, 1, 512, 128, L.DG_BF16, canvas=64, prefill_rows=1024)
+    model = runtime.Model(desc, 1600, seed=3, sigma=0.05)
+    model.use_expert_fp8(True)
+    W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=3, dtype="bf16", sigma=0.05)
+    V8 = OF.Fp8Weights(W)
+    shape = OM.ModelShape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8, top_k=2,
+                          d_expert=128, d_shared=256, gated=True, vocab=512, d_selfcond=128, canvas=64)
+    n = 1500
+    prompt = ids_tensor(1, n, shape.vocab)
+    model.prefill(prompt)
+    canvas = ids_tensor(2, shape.canvas, shape.vocab)
+    logits = model.denoise_step(canvas, 0)
+    torch.cuda.synchronize()
+    cache = OM.KVCache.empty(shape, 1600)
+    infos = []
+    OM.encode(V8, cache, prompt.cpu().numpy(), shape, infos=infos)
+    keep = ~router_flags(infos, shape.top_k)
+    K, _ = model.kv_view()
+    k_gpu = to_f64(K[1, :, :n])  # layer 1 keys depend on layer 0's experts
+    assert_close(k_gpu[:, keep], cache.k[1][:, :n][:, keep], 2e-2, "layer-1 keys after an FP8 chunked prefill")
+    ref, _, cinfo = OM.denoise_step(V8, cache.copy(), canvas.cpu().numpy(), None, shape, return_info=True)
+    cflag = router_flags(cinfo, shape.top_k)
+    assert_close(to_f64(logits)[~cflag], ref[~cflag], 2e-2, "fp8 step logits after a chunked prefill")
+    model.close()
