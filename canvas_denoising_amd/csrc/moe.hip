@@ -177,17 +177,23 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
 constexpr int kRouteSplits = 32;  // most split-k partials a routing call sums
 
-// Grid ceil(M / 4), 4 waves: wave w routes row 4 blockIdx.x + w. The logits are the sum of KS <= NS
+// Grid ceil(M / W), W = kRouteWaves waves: wave w routes row W blockIdx.x + w. The logits are the sum of KS <= NS
 // partials part[q * M * E + row * E + e] (KS = 1: part holds the logits), written to rlog. The NS
 // loads of a column are unconditional (slots past KS re-read the last one and are not added), so
 // they are all in flight together rather than issued one by one behind branches.
+#ifndef DG_ROUTE_WAVES
+#define DG_ROUTE_WAVES 2
+#endif
+constexpr int kRouteWaves = DG_ROUTE_WAVES;  // rows (one per wave) per workgroup
+
 template <int NS>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* part, int M, int E, int k,
-                                                         int renorm, int KS, float* rlog,
-                                                         int32_t* __restrict__ sel, float* __restrict__ gate) {
-  __shared__ float lg[4 * 256];
+__global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(const float* part, int M, int E, int k,
+                                                                      int renorm, int KS, float* rlog,
+                                                                      int32_t* __restrict__ sel,
+                                                                      float* __restrict__ gate) {
+  __shared__ float lg[kRouteWaves * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wave;
+  const int row = blockIdx.x * kRouteWaves + wave;
   if (row >= M) return;
   const int64_t pstride = static_cast<int64_t>(M) * E;
   float* l = lg + wave * 256;
@@ -793,10 +799,10 @@ int moe_route(const float* part, int splits, int M, int E, int k, int renorm, fl
     return fail(DG_ERR_UNSUPPORTED, "routing more than 256 rows at once needs n_experts <= 128");
   {
     ProfScope ps("moe_topk", s);
-    const unsigned g = (M + 3) / 4;
-    if (splits <= 8) route_topk_kernel<8><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
-    else if (splits <= 16) route_topk_kernel<16><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
-    else route_topk_kernel<kRouteSplits><<<g, 256, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    const unsigned g = (M + kRouteWaves - 1) / kRouteWaves, t = 64 * kRouteWaves;
+    if (splits <= 8) route_topk_kernel<8><<<g, t, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    else if (splits <= 16) route_topk_kernel<16><<<g, t, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
+    else route_topk_kernel<kRouteSplits><<<g, t, 0, s>>>(part, M, E, k, renorm, splits, rlog, sel, gate);
   }
   DG_LAUNCH_CHECK("route_topk_kernel");
   {
