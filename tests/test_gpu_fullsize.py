@@ -106,6 +106,7 @@ def test_full_step_sampled(libs):
     L, configs, runtime = libs
     w = configs.full_loop_bf16()
     d = w.desc
+    d.prefill_rows = 2048  # as bench.py runs it: the prompt prefilled in 2048-row chunks
     C, V, D = d.canvas, d.vocab, d.d_model
     announce("full-size 30-layer step: prefill 8192, denoise, sample, self-conditioned step, commit")
     model = runtime.Model(d, w.prompt + 2 * C, seed=0, sigma=0.02)
@@ -170,6 +171,7 @@ def test_block_ar_full_size(libs):
     L, configs, runtime = libs
     w = configs.block_ar_bf16()
     d = w.desc
+    d.prefill_rows = 2048  # as bench.py runs it
     C, V = d.canvas, d.vocab
     announce(f"block-AR full size: prompt {w.prompt}, capacity {w.capacity}")
     model = runtime.Model(d, w.capacity, seed=0, sigma=0.02)
