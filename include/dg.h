@@ -310,14 +310,16 @@ int dg_quantize_experts_fp8(const dg_model_desc* desc, const void* d_weights, vo
  * (g = 0..3) holds position 4 g + j for j < 4 and 16 + 4 g + (j - 4) for
  * j >= 4. capacity must be a multiple of 32. */
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
-/* Scratch the context needs: activations of one canvas (or one prompt chunk
- * of up to `canvas` rows), MoE routing tables, split-K partials,
+/* Scratch the context needs: activations of one layer pass (a canvas, or a
+ * prompt / commit chunk of up to max(canvas, prefill_rows) rows), MoE routing
+ * tables, the rotary table (capacity positions, when rope_theta > 0), split-K partials,
  * self-conditioning buffers and the sampler state of dg_generate_block. */
 size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity);
 
 /* Create a context over caller-owned weights, KV cache and workspace (none is
  * copied; all must outlive the context). Zero-fills the workspace and the KV
- * cache (blocking, on the default stream) and creates two streams and two
+ * cache, fills the rotary table when rope_theta > 0 (blocking, on the default
+ * stream) and creates two streams and two
  * events of its own (default priority). capacity = KV positions, a multiple
  * of 32. The committed length starts at 0. Limits: canvas <= 256, head_dim
  * 64 or 128 (bf16), d_model, head dims, FFN widths and vocab multiples of
