@@ -468,6 +468,14 @@ constexpr int kGemmStages64 = DG_GEMM_NS;  // LDS ring depth of the 64 x 64 tile
 #define DG_GEMM_NW 8
 #endif
 constexpr int kGemmWaves64 = DG_GEMM_NW;   // waves of the 64 x 64 tile (4 or 8)
+#ifndef DG_GEMM128_NS
+#define DG_GEMM128_NS 2
+#endif
+#ifndef DG_GEMM128_NW
+#define DG_GEMM128_NW 8
+#endif
+constexpr int kGemmStages128 = DG_GEMM128_NS;  // LDS ring depth of the 128 x 128 tile
+constexpr int kGemmWaves128 = DG_GEMM128_NW;   // waves of the 128 x 128 tile (4 or 8)
 
 #ifndef DG_GEMM_WGS
 #define DG_GEMM_WGS 256
@@ -514,7 +522,8 @@ static int gemm_t(const GemmArgs& g, int splits, hipStream_t s, const char* name
     if constexpr (sizeof(T) == 2) {
       const int nm = (g.M + tc.bm - 1) / tc.bm, nn = (g.N + tc.bn - 1) / tc.bn;
       dim3 grid(static_cast<unsigned>(nm * nn), static_cast<unsigned>(splits));
-      if (tc.bm == 128) gemm_dma_kernel<128, 128, 4, 4><<<grid, 256, 0, s>>>(g, splits, kps);
+      if (tc.bm == 128)
+        gemm_dma_kernel<128, 128, kGemmStages128, kGemmWaves128><<<grid, 64 * kGemmWaves128, 0, s>>>(g, splits, kps);
       else gemm_dma_kernel<64, 64, kGemmStages64, kGemmWaves64><<<grid, 64 * kGemmWaves64, 0, s>>>(g, splits, kps);
       rc = DG_OK;
     } else {
