@@ -654,13 +654,16 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
 // worth tiling like a dense GEMM rather than streaming the weights once per 48 tokens: a workgroup
 // takes one entry of the tile list (128 of one expert's tokens) against one tile group of its
 // weights (gate/up: 32 features of gate and up; down: 64 outputs) and runs K in stages of 64
-// through a 3-deep LDS ring filled by asynchronous copies: the 128 gathered token rows (128-byte
+// through an LDS ring filled by asynchronous copies: the 128 gathered token rows (128-byte
 // rows, XOR-swizzled as in the dense GEMM) and the group's 2 G weight tiles (already in fragment
 // order, so a lane reads its fragment at byte 16 l). Each of the 4 waves owns 32 tokens against
 // all G weight tiles, so a wave holds both the gate and the up sums of its features.
-constexpr int kTileStages = 3;
+#ifndef DG_TILE_STAGES
+#define DG_TILE_STAGES 2
+#endif
+constexpr int kTileStages = DG_TILE_STAGES;  // LDS ring depth of the token-tiled experts
 #ifndef DG_TILE_GROUPS
-#define DG_TILE_GROUPS 2
+#define DG_TILE_GROUPS 1
 #endif
 // weight tile groups per workgroup: each adds 4 waves and the group's weight tiles to a stage, and
 // divides the copies of the gathered token rows per flop by as much
