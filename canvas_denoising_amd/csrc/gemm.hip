@@ -454,9 +454,12 @@ struct TileChoice { int bm, bn; };
 // (many column tiles) or K is long enough that split-K partials are small against the operands
 // (the self-conditioning product over the vocabulary). Elsewhere, with a 256-row canvas, 64 x 64
 // tiles give enough workgroups without splitting.
+#ifndef DG_GEMM128_MIN_TILES
+#define DG_GEMM128_MIN_TILES 256
+#endif
 static TileChoice pick_tile(int M, int N, int K) {
   const int64_t t128 = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
-  if (M > 64 && N >= 128 && (t128 >= 512 || K >= 16384)) return {128, 128};
+  if (M > 64 && N >= 128 && (t128 >= DG_GEMM128_MIN_TILES || K >= 16384)) return {128, 128};
   return {64, 64};
 }
 
