@@ -114,9 +114,19 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < E * MW; i += 1024) mask[i] = 0u;
   __syncthreads();
-  for (int p = tid; p < M * k; p += 1024) {
-    const int row = p / k;
-    atomicOr(&mask[sel[p] * MW + (row >> 5)], 1u << (row & 31));
+  // (token, choice) pairs in batches of 8 per thread whose loads are issued together (clamped
+  // indices; surplus pairs are not used)
+  const int np = M * k;
+  constexpr int kPB = 8;
+  for (int p0 = tid; p0 < np; p0 += 1024 * kPB) {
+    int ev[kPB];
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) ev[i] = sel[min(p0 + 1024 * i, np - 1)];
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      const int p = p0 + 1024 * i, row = p / k;
+      if (p < np) atomicOr(&mask[ev[i] * MW + (row >> 5)], 1u << (row & 31));
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -164,14 +174,26 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     for (int e = tid; e < E; e += 1024)
       for (int j = toffs[e]; j < toffs[e + 1]; ++j) tiles[1 + j] = e * 65536 + (j - toffs[e]);
   }
-  for (int p = tid; p < M * k; p += 1024) {
-    const int row = p / k;
-    const int e = sel[p];
-    const int rank = below[e * MW + (row >> 5)] + __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
-    const int slot = offs[e] + rank;
-    perm[slot] = row;
-    slot_of[p] = slot;
-    slot_gate[slot] = gate[p];
+  for (int p0 = tid; p0 < np; p0 += 1024 * kPB) {
+    int ev[kPB];
+    float gv[kPB];
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      const int p = min(p0 + 1024 * i, np - 1);
+      ev[i] = sel[p];
+      gv[i] = gate[p];
+    }
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      const int p = p0 + 1024 * i, row = p / k, e = ev[i];
+      if (p < np) {
+        const int rank = below[e * MW + (row >> 5)] + __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
+        const int slot = offs[e] + rank;
+        perm[slot] = row;
+        slot_of[p] = slot;
+        slot_gate[slot] = gv[i];
+      }
+    }
   }
 }
 
