@@ -80,13 +80,19 @@ constexpr int kStages = DG_ATT_NS;        // LDS ring depth (NS - 1 stages in fl
 #endif
 constexpr int kNW = DG_ATT_NW;            // waves per workgroup (4 or 8)
 constexpr int kQT = DG_ATT_QT;            // 16-query tiles per wave (share every K/V fragment read)
-constexpr int kWGRows = kNW * kQT * 16;   // query rows per workgroup
+constexpr int kQTLarge = 2;               // the same for passes of more than 256 rows (prefill chunks)
+constexpr int kLargeRows = 256;
+// query tiles per wave for a pass of M rows: canvases keep one, so that their key range splits over
+// more workgroups; long prefill chunks have work enough and share each staged K/V block among more
+// queries
+inline int attn_qt(int M) { return M > kLargeRows ? kQTLarge : kQT; }
 
 // 2^x with the hardware instruction (about 1 ulp; 2^-inf = 0). Arguments here are <= 0.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int HD>
+template <int HD, int QT>
 __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int kWGRows = kNW * QT * 16;  // query rows per workgroup
   constexpr int HS = HD / 32;             // k-steps over head_dim
   constexpr int HT = HD / 16;             // O^T tiles over head_dim
   constexpr int ROWB = HD * 2;            // bytes per K row
@@ -119,11 +125,11 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
   const int L = a.pos0 + a.M;
   const int g4 = lane >> 4, fr = lane & 15;
 
-  int qr[kQT], qhead[kQT], qm[kQT], qpos[kQT];
-  bool qvalid[kQT];
+  int qr[QT], qhead[QT], qm[QT], qpos[QT];
+  bool qvalid[QT];
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    qr[t] = qt * kWGRows + (wave * kQT + t) * 16 + fr;
+  for (int t = 0; t < QT; ++t) {
+    qr[t] = qt * kWGRows + (wave * QT + t) * 16 + fr;
     qvalid[t] = qr[t] < rows_in_group;
     qhead[t] = kvh * G + (qvalid[t] ? qr[t] / a.M : 0);
     qm[t] = qvalid[t] ? qr[t] % a.M : 0;
@@ -143,18 +149,18 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
   const int nst = k_hi > k_lo ? (k_hi - k_lo + kKS - 1) / kKS : 0;
 
   // Q^T fragments (B operand): lane supplies query qr, head dims 8*g4 .. of each 32-step
-  bf16x8_t qf[kQT][HS];
+  bf16x8_t qf[QT][HS];
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
+  for (int t = 0; t < QT; ++t) {
     const bf16_t* qb = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(qm[t]) * a.ldq + qhead[t] * HD;
 #pragma unroll
     for (int h = 0; h < HS; ++h) qf[t][h] = qvalid[t] ? Frag<bf16_t>::load(qb + h * 32 + g4 * 8) : Frag<bf16_t>::zero();
   }
 
-  f32x4_t o[kQT][HT];
-  float mrun[kQT], lrun[kQT];
+  f32x4_t o[QT][HT];
+  float mrun[QT], lrun[QT];
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
+  for (int t = 0; t < QT; ++t) {
 #pragma unroll
     for (int j = 0; j < HT; ++j) o[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mrun[t] = -INFINITY;
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
         kf[kt][h] = *reinterpret_cast<const bf16x8_t*>(sk + r * ROWB + (((h * 4 + g4) ^ (r & 7)) << 4));
     }
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) {
+    for (int t = 0; t < QT; ++t) {
       f32x4_t s[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
@@ -294,12 +300,12 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
 
   // this lane's partial l covers its lane group's keys: sum the 4 groups
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) lrun[t] = xrow_sum(lrun[t]);
+  for (int t = 0; t < QT; ++t) lrun[t] = xrow_sum(lrun[t]);
 
   // ---- results: lane holds O^T[hd = j*16 + 4*g4 + i][query qr]
   const int64_t R = static_cast<int64_t>(a.Hq) * a.M;
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) {
+  for (int t = 0; t < QT; ++t) {
     if (!qvalid[t]) continue;
     if (a.splits == 1) {
       const float inv = lrun[t] > 0.f ? 1.0f / lrun[t] : 0.f;
@@ -420,7 +426,8 @@ int attn_max_splits() { return kMergeMax; }
 // partial buffers).
 int64_t attn_partial_rows(int M, int Hq, int Hkv) {
   const int G = Hq / Hkv;
-  const int qtiles = (G * M + kWGRows - 1) / kWGRows;
+  const int wg_rows = kNW * attn_qt(M) * 16;
+  const int qtiles = (G * M + wg_rows - 1) / wg_rows;
   const int splits = std::max(1, std::min(attn_max_splits(), (kAttnWGs + qtiles * Hkv - 1) / (qtiles * Hkv)));
   return static_cast<int64_t>(splits) * M;
 }
@@ -445,7 +452,9 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   }
   if (hd != 64 && hd != 128) return fail(DG_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
   const int G = Hq / Hkv;
-  const int qtiles = (G * M + kWGRows - 1) / kWGRows;
+  const int qt = attn_qt(M);
+  const int wg_rows = kNW * qt * 16;
+  const int qtiles = (G * M + wg_rows - 1) / wg_rows;
   // about 256 workgroups (one per CU; partial results cost HBM traffic per extra split), at least
   // four key stages per split
   int splits = std::max(1, std::min(attn_max_splits(), (kAttnWGs + qtiles * Hkv - 1) / (qtiles * Hkv)));
@@ -456,8 +465,13 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   const dim3 grid(qtiles * Hkv * a.splits);
   {
     ProfScope ps("attention", s);
-    if (hd == 128) attn_bf16_kernel<128><<<grid, 64 * kNW, 0, s>>>(a);
-    else attn_bf16_kernel<64><<<grid, 64 * kNW, 0, s>>>(a);
+    if (qt == kQTLarge) {
+      if (hd == 128) attn_bf16_kernel<128, kQTLarge><<<grid, 64 * kNW, 0, s>>>(a);
+      else attn_bf16_kernel<64, kQTLarge><<<grid, 64 * kNW, 0, s>>>(a);
+    } else {
+      if (hd == 128) attn_bf16_kernel<128, kQT><<<grid, 64 * kNW, 0, s>>>(a);
+      else attn_bf16_kernel<64, kQT><<<grid, 64 * kNW, 0, s>>>(a);
+    }
   }
   DG_LAUNCH_CHECK("attn_bf16_kernel");
   if (a.splits == 1) return DG_OK;
