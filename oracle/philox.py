@@ -10,7 +10,7 @@ the counter by two fixed odd constants, keeps the 64-bit products' high and
 low halves, and xors the high halves with the other two words and the
 round key; the key is bumped by two Weyl constants between rounds.
 
-Reading fixed for this build (both sides implement it separately):
+Reading taken (the oracle and the device code implement it separately):
 key = (seed low 32 bits, seed high 32 bits);
 counter = (position, step, block, purpose) with purpose 0 = canvas init and
 1 = re-noise; the draw uses output word 0;
