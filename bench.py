@@ -472,6 +472,9 @@ def bench_prefill(args):
     d.prefill_rows = args.prefill_rows
     log(f"[bench] model {d.n_layers} layers, prompt {w.prompt}, chunks of {max(d.canvas, d.prefill_rows)} rows")
     model = Model(d, w.prompt, seed=0)
+    fp8 = args.experts == "fp8"
+    if fp8:
+        model.use_expert_fp8(True)
     prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
     L.dg_synth_uniform_ids(5, 10, w.prompt, d.vocab, prompt)
 
@@ -488,12 +491,14 @@ def bench_prefill(args):
     dt = time.perf_counter() - t0
     model.close()
     return {
-        "metric": "prefill tokens/s (32768-token prompt)", "value": args.steps * w.prompt / dt, "unit": "tokens/s",
+        "metric": "prefill tokens/s (32768-token prompt" + (", FP8 E4M3 routed-expert weights)" if fp8 else ")"),
+        "value": args.steps * w.prompt / dt, "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"encoder prefill of {w.prompt} uniform token ids, {d.n_layers} MoE layers "
                                f"d_model {d.d_model}, 128 experts top-8, causal, random-init weights",
-                   "prefill_rows": max(d.canvas, d.prefill_rows)},
+                   "prefill_rows": max(d.canvas, d.prefill_rows),
+                   "expert_weights": "fp8 e4m3, per-row float32 scales" if fp8 else "bf16"},
     }
 
 
@@ -534,7 +539,8 @@ def main():
     ap.add_argument("--sampler-mode", type=int, default=0,
                     help="sampler workload: dg_sched.mode flags (1 either-stop, 2 group acceptance, 4 categorical)")
     ap.add_argument("--experts", choices=["bf16", "fp8"], default="bf16",
-                    help="full workload: routed-expert weights in the model dtype or as FP8 E4M3 (opt-in mode)")
+                    help="full / prefill workloads: routed-expert weights in the model dtype or as FP8 E4M3 "
+                         "(opt-in mode)")
     ap.add_argument("--prefill-rows", type=int, default=2048,
                     help="rows per prefill chunk (0 = the canvas); chunks above 256 rows run the experts as "
                          "token-tiled GEMMs")

@@ -691,22 +691,29 @@ constexpr int kTileStages = DG_TILE_STAGES;  // LDS ring depth of the token-tile
 // divides the copies of the gathered token rows per flop by as much
 constexpr int kTileGroups = DG_TILE_GROUPS;
 
-template <bool DOWN, bool GATED, int NG>
+// FP8: w holds E4M3 codes in the paired-tile order (tiles.h), whose 1 KiB block of a k-tile pair is
+// exactly one 64-column stage of a tile; the codes are converted to bf16 fragments as they leave
+// LDS and the row scales sc (gate/up [E][2][F], down [E][D]) multiply the sums in the epilogue.
+template <bool DOWN, bool GATED, int NG, bool FP8>
 __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ w, int F, int D, int per_e,
+    const bf16_t* __restrict__ A, int64_t lda, const void* __restrict__ wv, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-    const float* __restrict__ slot_gate, bf16_t* __restrict__ act, float* __restrict__ out) {
+    const float* __restrict__ slot_gate, const float* __restrict__ sc, bf16_t* __restrict__ act,
+    float* __restrict__ out) {
+  using WT = std::conditional_t<FP8, uint8_t, bf16_t>;
+  const WT* w = static_cast<const WT*>(wv);
   constexpr int NW = kExpWaves * NG;
   constexpr int gw = DOWN ? 1 : (GATED ? 2 : 1);
   constexpr int G = DOWN ? kDownGroup : gw * kGuBlocks;
+  constexpr int KB = FP8 ? 1 : 2;                  // 1 KiB copies per weight tile and stage
   constexpr int ROWB = 128;                        // bytes per staged token row: 64 bf16
   constexpr int SA = kTileTokens * ROWB;           // token rows of a stage
-  constexpr int SB = NG * 2 * G * 1024;            // weight tiles of a stage (NG groups x 2 k-tiles)
+  constexpr int SB = NG * KB * G * 1024;           // weight tiles of a stage (NG groups x 64 columns)
   constexpr int SS = SA + SB;
   constexpr int ALPW = kTileTokens / 8 / NW;       // token-row copies per wave per stage (8 rows each)
-  constexpr int BLPW = NG * 2 * G / NW;            // weight-tile copies per wave per stage
+  constexpr int BLPW = NG * KB * G / NW;           // weight-tile copies per wave per stage
   constexpr int LPS = ALPW + BLPW;
-  static_assert(ALPW >= 1 && BLPW >= 1 && (NG * 2 * G) % NW == 0 && (kTileTokens / 8) % NW == 0,
+  static_assert(ALPW >= 1 && BLPW >= 1 && (NG * KB * G) % NW == 0 && (kTileTokens / 8) % NW == 0,
                 "copies of a stage must split evenly over the waves");
   __shared__ __align__(16) unsigned char smem[kTileStages * SS];
 
@@ -720,8 +727,8 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
   const int beg = offsets[e], rows = min(kTileTokens, offsets[e + 1] - beg - t0);
   const int K = DOWN ? F : D;
   const int KT = K / 32, nk = K / 64;
-  const bf16_t* bg = w + static_cast<int64_t>(e) * (DOWN ? static_cast<int64_t>(D) * F : static_cast<int64_t>(gw) * F * D) +
-                     static_cast<int64_t>(q) * NG * KT * G * kTileElems + lane * 8;
+  const WT* bg = w + static_cast<int64_t>(e) * (DOWN ? static_cast<int64_t>(D) * F : static_cast<int64_t>(gw) * F * D) +
+                 static_cast<int64_t>(q) * NG * KT * G * kTileElems + lane * (FP8 ? 16 : 8);
   const bf16_t* asrc[ALPW];
 #pragma unroll
   for (int i = 0; i < ALPW; ++i) {
@@ -737,10 +744,14 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
     for (int i = 0; i < ALPW; ++i) dma16(asrc[i] + st * 64, base + (wave * ALPW + i) * 8 * ROWB);
 #pragma unroll
     for (int i = 0; i < BLPW; ++i) {
-      const int tb = wave * BLPW + i;  // group tb / 2G, k-tile 2 st + (tb % 2G) / G, tile tb % G
-      const int grp = tb / (2 * G), ks = (tb % (2 * G)) / G;
-      dma16(bg + (static_cast<int64_t>(grp) * KT * G + static_cast<int64_t>(2 * st + ks) * G + tb % G) * kTileElems,
-            base + SA + tb * 1024);
+      const int tb = wave * BLPW + i;  // group tb / (KB G), k-tile 2 st + (tb % (KB G)) / G, tile tb % G
+      const int grp = tb / (KB * G), ks = (tb % (KB * G)) / G;
+      if constexpr (FP8)  // the pair block of the stage: 1 KiB per tile
+        dma16(bg + static_cast<int64_t>(grp) * KT * G * kTileElems + (static_cast<int64_t>(st) * G + tb % G) * 1024,
+              base + SA + tb * 1024);
+      else
+        dma16(bg + (static_cast<int64_t>(grp) * KT * G + static_cast<int64_t>(2 * st + ks) * G + tb % G) * kTileElems,
+              base + SA + tb * 1024);
     }
   };
   f32x4_t acc[2][G];
@@ -759,7 +770,7 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
     __builtin_amdgcn_s_barrier();
     if (st + kTileStages - 1 < nk) issue(st + kTileStages - 1, (st + kTileStages - 1) % kTileStages);
     const unsigned char* sa = smem + (st % kTileStages) * SS;
-    const unsigned char* sb = sa + SA + gi * 2 * G * 1024;
+    const unsigned char* sb = sa + SA + gi * KB * G * 1024;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t af[2], bfr[G];
@@ -770,7 +781,14 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
         af[t] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((c ^ (r & 7)) << 4));
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) bfr[g] = *reinterpret_cast<const bf16x8_t*>(sb + (ks * G + g) * 1024 + lane * 16);
+      for (int g = 0; g < G; ++g) {
+        if constexpr (FP8) {
+          const u32x4v_t v = *reinterpret_cast<const u32x4v_t*>(sb + g * 1024 + lane * 16);
+          bfr[g] = fp8x8_to_bf16(v[2 * ks], v[2 * ks + 1]);
+        } else {
+          bfr[g] = *reinterpret_cast<const bf16x8_t*>(sb + (ks * G + g) * 1024 + lane * 16);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -779,6 +797,13 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
   }
   // epilogue: lane holds tokens wq * 32 + 16 t + 4 (lane / 16) + i of the tile, group row 16 g + lane % 16
   const int qg = q * NG + gi;  // this wave's tile group within the expert
+  float scl[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if constexpr (!FP8) scl[g] = 1.f;
+    else if constexpr (DOWN) scl[g] = sc[static_cast<int64_t>(e) * D + qg * 16 * kDownGroup + g * 16 + fr];
+    else scl[g] = sc[(static_cast<int64_t>(e) * gw + g / kGuBlocks) * F + qg * 16 * kGuBlocks + (g % kGuBlocks) * 16 + fr];
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -790,27 +815,31 @@ __global__ __launch_bounds__(64 * kExpWaves * NG) void expert_tile_kernel(
           const float gs = slot_gate[slot];
           float* o = out + slot * D + qg * 16 * kDownGroup + fr;
 #pragma unroll
-          for (int g = 0; g < G; ++g) o[g * 16] = gs * acc[t][g][i];
+          for (int g = 0; g < G; ++g) o[g * 16] = gs * (FP8 ? acc[t][g][i] * scl[g] : acc[t][g][i]);
         } else {
           bf16_t* o = act + slot * F + qg * 16 * kGuBlocks + fr;
 #pragma unroll
-          for (int bb = 0; bb < kGuBlocks; ++bb)
-            o[bb * 16] = f32_to_bf16(GATED ? gelu_erf(acc[t][bb][i]) * acc[t][kGuBlocks + bb][i] : gelu_erf(acc[t][bb][i]));
+          for (int bb = 0; bb < kGuBlocks; ++bb) {
+            const float a0 = FP8 ? acc[t][bb][i] * scl[bb] : acc[t][bb][i];
+            const float a1 = FP8 ? acc[t][kGuBlocks + bb][i] * scl[kGuBlocks + bb] : acc[t][kGuBlocks + bb][i];
+            o[bb * 16] = f32_to_bf16(GATED ? gelu_erf(a0) * a1 : gelu_erf(a0));
+          }
         }
       }
     }
 }
 
-template <bool DOWN, bool GATED>
-static void launch_expert_tiles(int t8, int per_e, hipStream_t s, const bf16_t* A, int64_t lda, const bf16_t* w,
+template <bool DOWN, bool GATED, bool FP8>
+static void launch_expert_tiles(int t8, int per_e, hipStream_t s, const bf16_t* A, int64_t lda, const void* w,
                                 int F, int D, const int32_t* offsets, const int32_t* perm, const int32_t* tiles,
-                                const float* slot_gate, bf16_t* act, float* out) {
+                                const float* slot_gate, const float* sc, bf16_t* act, float* out) {
   if (per_e % kTileGroups == 0)
-    expert_tile_kernel<DOWN, GATED, kTileGroups><<<t8 * (per_e / kTileGroups), 64 * kExpWaves * kTileGroups, 0, s>>>(
-        A, lda, w, F, D, per_e / kTileGroups, offsets, perm, tiles, slot_gate, act, out);
+    expert_tile_kernel<DOWN, GATED, kTileGroups, FP8><<<t8 * (per_e / kTileGroups), 64 * kExpWaves * kTileGroups, 0,
+                                                        s>>>(A, lda, w, F, D, per_e / kTileGroups, offsets, perm,
+                                                             tiles, slot_gate, sc, act, out);
   else
-    expert_tile_kernel<DOWN, GATED, 1><<<t8 * per_e, 64 * kExpWaves, 0, s>>>(A, lda, w, F, D, per_e, offsets, perm,
-                                                                           tiles, slot_gate, act, out);
+    expert_tile_kernel<DOWN, GATED, 1, FP8><<<t8 * per_e, 64 * kExpWaves, 0, s>>>(A, lda, w, F, D, per_e, offsets,
+                                                                                perm, tiles, slot_gate, sc, act, out);
 }
 
 // ------------------------------------------------------------------- host
@@ -886,25 +915,34 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
   const int per_gu = F / (16 * kGuBlocks);
   const int per_dn = D / (16 * kDownGroup);
   const dim3 g1(E * per_gu), g2(E * per_dn);
-  if (tiles && !q8 && dtype == DG_BF16) {
+  // token tiles: bf16 weights, or FP8 codes of a gated model (an ungated one's G = 2 weight tiles per
+  // stage do not split over 4 waves in whole kilobytes)
+  if (tiles && dtype == DG_BF16 && (!q8 || gated)) {
     if (F % 64 != 0 || D % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "token-tiled experts need widths that are multiples of 64");
     const int t8 = (static_cast<int>((static_cast<int64_t>(M) * k + kTileTokens - 1) / kTileTokens) + E + 7) / 8 * 8;
     const bf16_t* hh = static_cast<const bf16_t*>(h);
     bf16_t* a = static_cast<bf16_t*>(act);
     {
-      ProfScope ps("expert_tile_gateup", s);
-      if (gated)
-        launch_expert_tiles<false, true>(t8, per_gu, s, hh, ldh, static_cast<const bf16_t*>(w_gu), F, D, offsets, perm,
-                                         tiles, slot_gate, a, out);
+      ProfScope ps(q8 ? "expert_tile_gateup_fp8" : "expert_tile_gateup", s);
+      if (q8)
+        launch_expert_tiles<false, true, true>(t8, per_gu, s, hh, ldh, q8->gu, F, D, offsets, perm, tiles, slot_gate,
+                                               q8->s_gu, a, out);
+      else if (gated)
+        launch_expert_tiles<false, true, false>(t8, per_gu, s, hh, ldh, w_gu, F, D, offsets, perm, tiles, slot_gate,
+                                                nullptr, a, out);
       else
-        launch_expert_tiles<false, false>(t8, per_gu, s, hh, ldh, static_cast<const bf16_t*>(w_gu), F, D, offsets, perm,
-                                          tiles, slot_gate, a, out);
+        launch_expert_tiles<false, false, false>(t8, per_gu, s, hh, ldh, w_gu, F, D, offsets, perm, tiles, slot_gate,
+                                                 nullptr, a, out);
     }
     DG_LAUNCH_CHECK("expert_tile_kernel (gate/up)");
     {
-      ProfScope ps("expert_tile_down", s);
-      launch_expert_tiles<true, false>(t8, per_dn, s, a, F, static_cast<const bf16_t*>(w_down), F, D, offsets, perm,
-                                       tiles, slot_gate, a, out);
+      ProfScope ps(q8 ? "expert_tile_down_fp8" : "expert_tile_down", s);
+      if (q8)
+        launch_expert_tiles<true, false, true>(t8, per_dn, s, a, F, q8->dn, F, D, offsets, perm, tiles, slot_gate,
+                                               q8->s_dn, a, out);
+      else
+        launch_expert_tiles<true, false, false>(t8, per_dn, s, a, F, w_down, F, D, offsets, perm, tiles, slot_gate,
+                                                nullptr, a, out);
     }
     DG_LAUNCH_CHECK("expert_tile_kernel (down)");
     return DG_OK;

@@ -224,8 +224,8 @@ def test_fp8_moe_layer_full_size(libs):
 
 
 def test_fp8_with_prefill_chunks(libs):
-    """FP8 experts in a 1024-row prefill chunk: the FP8 weight streams run over the 1024-row routing
-    (the token-tiled GEMMs are the bf16 path), then a denoising step; against the oracle with the
+    """FP8 experts in a 1024-row prefill chunk (the token-tiled GEMMs over E4M3 codes, converted as
+    they leave LDS), then a denoising step (the FP8 weight streams); against the oracle with the
     dequantised experts."""
     L, configs, runtime = libs
     announce("fp8 experts, prefill of 1500 tokens in 1024-row chunks")
