@@ -341,6 +341,11 @@ static void* kv_v(dg_ctx* c, int l) {
   return c->kv + static_cast<size_t>(c->d.n_layers + l) * c->d.n_kv_heads * c->cap * c->d.head_dim * es;
 }
 
+#ifndef DG_QKV_SPLIT
+#define DG_QKV_SPLIT 0
+#endif
+constexpr bool kQkvSplit = DG_QKV_SPLIT;   // split-K for the fused QKV projection (reduce applies the cache epilogue)
+
 static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool allow_split, bool aux = false) {
   const int splits = gemm_pick_splits(g.M, g.N, g.K, c->d.dtype, c->wsl.gpart_floats, allow_split);
   g.part = wsp<float>(c, aux ? c->wsl.gpart_aux : c->wsl.gpart);
@@ -384,7 +389,7 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
       g.B = static_cast<const char*>(g.B) + static_cast<size_t>(QW) * D * esize(d);
       g.N = 2 * d.n_kv_heads * hd;
     }
-    DG_TRY(run_gemm(c, g, s, "qkv_proj", false));
+    DG_TRY(run_gemm(c, g, s, "qkv_proj", kQkvSplit));
   }
   if (d.rope_theta > 0.f)
     DG_TRY(rope_apply(kv_only ? nullptr : wsp<void>(c, w.q), QW, kv_k(c, l), c->cap * hd, pos0, M, d.n_q_heads,
