@@ -7,14 +7,15 @@
 // the query is processed the standard way). Scores are scaled by
 // 1/sqrt(head_dim); query head j reads KV head floor(j * Hkv / Hq).
 //
-// bf16 path (MFMA, split-KV flash attention). A workgroup owns 128 query
-// rows of one KV-head group (the Hq/Hkv query heads sharing that KV head are
-// laid side by side, so one K/V tile serves all of them) and one slice of
-// the keys; each of its 4 waves owns two 16-query tiles, so every K and V
-// fragment read from LDS feeds two MFMAs. K and V^T tiles of 32 keys stream
-// into a ring of 8 LDS stages by asynchronous global->LDS copies (dma.h),
-// seven stages ahead of the one being multiplied (the loaded latency is a
-// few microseconds), with one barrier per stage. The V cache is stored transposed in 32-position blocks
+// bf16 path (MFMA, split-KV flash attention). A workgroup of 8 waves owns
+// the query rows of one KV-head group (the Hq/Hkv query heads sharing that KV
+// head are laid side by side, so one K/V tile serves all of them) and one
+// slice of the keys; each wave owns one 16-query tile in canvas passes and
+// two in longer passes (prefill chunks), where every K and V fragment read
+// from LDS then feeds two MFMAs. K and V^T tiles stream into a ring of LDS
+// stages by asynchronous global->LDS copies (dma.h), one barrier per stage:
+// 128 keys in a ring of 2 for canvas passes, 64 keys in a ring of 3 for the
+// longer ones. The V cache is stored transposed in 32-position blocks
 // (kvlayout.h), so a V^T stage is one contiguous copy and each V^T fragment
 // one 16-byte LDS read per lane; K rows are XOR-swizzled in LDS so the 16
 // rows a fragment read touches fall on distinct banks. Each wave works on the
@@ -62,16 +63,26 @@ struct AttnArgs {
   int64_t ldo;
 };
 
+// Stage shape: V blocks per LDS stage (KB2, 32 keys each) and ring depth (NS, NS - 1 stages in
+// flight). Canvas passes (one query tile per wave) take 128-key stages in a ring of 2: half the
+// barriers of 64-key stages for the same bytes in flight. Passes with two query tiles per wave
+// (prefill chunks) keep 64-key stages in a ring of 3, whose fragments fit their registers.
 #ifndef DG_ATT_KB2
-#define DG_ATT_KB2 2
+#define DG_ATT_KB2 4
 #endif
-constexpr int kVB = 32;                   // positions per V cache block (kvlayout.h)
-constexpr int kKB2 = DG_ATT_KB2;          // V blocks per LDS stage
-constexpr int kKS = kVB * kKB2;           // keys per LDS stage
 #ifndef DG_ATT_NS
-#define DG_ATT_NS 3
+#define DG_ATT_NS 2
 #endif
-constexpr int kStages = DG_ATT_NS;        // LDS ring depth (NS - 1 stages in flight)
+#ifndef DG_ATT_KB2_LARGE
+#define DG_ATT_KB2_LARGE 2
+#endif
+#ifndef DG_ATT_NS_LARGE
+#define DG_ATT_NS_LARGE 3
+#endif
+constexpr int kVB = 32;  // positions per V cache block (kvlayout.h)
+__host__ __device__ constexpr int att_kb2(int qt) { return qt == 1 ? DG_ATT_KB2 : DG_ATT_KB2_LARGE; }
+__host__ __device__ constexpr int att_stages(int qt) { return qt == 1 ? DG_ATT_NS : DG_ATT_NS_LARGE; }
+__host__ __device__ constexpr int att_keys(int qt) { return kVB * att_kb2(qt); }  // keys per LDS stage
 #ifndef DG_ATT_NW
 #define DG_ATT_NW 8
 #endif
@@ -97,6 +108,9 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int HT = HD / 16;             // O^T tiles over head_dim
   constexpr int ROWB = HD * 2;            // bytes per K row
   constexpr int CPR = ROWB / 16;          // 16-byte chunks per K row
+  constexpr int kKB2 = att_kb2(QT);       // V blocks per stage
+  constexpr int kKS = att_keys(QT);       // keys per stage
+  constexpr int kStages = att_stages(QT); // LDS ring depth
   constexpr int KBYTES = kKS * ROWB;      // K bytes per stage
   constexpr int VBYTES = HD * kKS * 2;    // V^T bytes per stage (kKB2 blocks of [HD][32])
   constexpr int SBYTES = KBYTES + VBYTES;
@@ -200,6 +214,9 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
         const int off = csrc[i] <= kmax + (HD - 1) ? csrc[i] : kmax + (csrc[i] % HD);
         dma16(kbase + static_cast<int64_t>(key0) * HD + off, base + c * 1024);
       } else {
+        // whole V blocks: a key range's last stage may copy up to att_keys - 32 positions past the
+        // capacity, into the next head's blocks or the cache's tail (dg_kv_bytes); those keys are
+        // masked, so the finite values there are weighted by zero
         dma16(vb + csrc[i], base + c * 1024);
       }
     }
@@ -421,6 +438,7 @@ __global__ void attn_f32_kernel(AttnArgs a) {
 #endif
 constexpr int kAttnWGs = DG_ATT_WGS;  // target workgroups of a launch
 int attn_max_splits() { return kMergeMax; }
+int attn_v_overrun() { return std::max(att_keys(1), att_keys(kQTLarge)) - kVB; }
 
 // Upper bound of splits x M over the launches attention() makes for M query rows (the rows of its
 // partial buffers).
@@ -453,6 +471,7 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   if (hd != 64 && hd != 128) return fail(DG_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
   const int G = Hq / Hkv;
   const int qt = attn_qt(M);
+  const int kKS = att_keys(qt);
   const int wg_rows = kNW * qt * 16;
   const int qtiles = (G * M + wg_rows - 1) / wg_rows;
   // about 256 workgroups (one per CU; partial results cost HBM traffic per extra split), at least

@@ -45,6 +45,7 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
               int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
               int dtype, hipStream_t s);
 int attn_max_splits();
+int attn_v_overrun();
 int64_t attn_partial_rows(int M, int Hq, int Hkv);
 int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
                hipStream_t s);
@@ -732,7 +733,10 @@ int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma,
 
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity) {
   if (check_desc(desc) != DG_OK || capacity < 0) return 0;
-  return 2ull * desc->n_layers * desc->n_kv_heads * static_cast<size_t>(capacity) * desc->head_dim * esize(*desc);
+  // K and V of every layer and head, then a tail that the attention kernel's whole-stage V copies
+  // may read (never write) past the last head's blocks
+  const size_t kv = 2ull * desc->n_layers * desc->n_kv_heads * static_cast<size_t>(capacity) * desc->head_dim;
+  return (kv + static_cast<size_t>(attn_v_overrun()) * desc->head_dim) * esize(*desc);
 }
 
 size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity) {

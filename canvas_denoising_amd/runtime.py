@@ -116,7 +116,7 @@ class Model:
         t = self.kv.view(self.dtype)
         n = d.n_layers * d.n_kv_heads * self.capacity * d.head_dim
         k = t[:n].view(d.n_layers, d.n_kv_heads, self.capacity, d.head_dim)
-        v = t[n:].view(d.n_layers, d.n_kv_heads, self.capacity // 32, d.head_dim, 32)
+        v = t[n:2 * n].view(d.n_layers, d.n_kv_heads, self.capacity // 32, d.head_dim, 32)
         return k, v
 
     def kv_view(self):

@@ -308,7 +308,9 @@ int dg_quantize_experts_fp8(const dg_model_desc* desc, const void* d_weights, vo
  * (row-major), then values [n_layers][n_kv_heads][capacity / 32][head_dim][32]:
  * V transposed in blocks of 32 positions, where inside a block slot 8 g + j
  * (g = 0..3) holds position 4 g + j for j < 4 and 16 + 4 g + (j - 4) for
- * j >= 4. capacity must be a multiple of 32. */
+ * j >= 4. capacity must be a multiple of 32. The size includes a tail of
+ * 96 head_dim-wide positions after the values, which attention reads (whole
+ * 128-key stages of V blocks) but never writes or weights. */
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
 /* Scratch the context needs: activations of one layer pass (a canvas, or a
  * prompt / commit chunk of up to max(canvas, prefill_rows) rows), MoE routing

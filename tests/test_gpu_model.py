@@ -457,3 +457,32 @@ def test_prefill_in_large_chunks_matches_oracle(libs, dtype):
     cflag = router_flags(cinfo, shape.top_k)
     assert_close(to_f64(logits)[~cflag], ref[~cflag], tol, "step logits after a chunked prefill")
     model.close()
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_canvas_reaching_the_cache_end(libs, hd):
+    """Canvas keys that end exactly at a capacity of 7 V blocks (224 = 3.5 stages of 64 keys).
+
+    The attention kernel copies whole stages of V blocks; the last stage here covers blocks past
+    the capacity, which it must replace by the last block that holds keys (weighted by zero)
+    rather than read past the cache.
+    """
+    L, configs, runtime = libs
+    announce(f"canvas at the cache end, head_dim {hd}")
+    model, W, shape = build(libs, dtype="bf16", gated=1, n_layers=1, hd=hd, canvas=64, capacity=224)
+    tol = tol_for("bf16")
+    n_prompt = 160
+    prompt = ids_tensor(5, n_prompt, shape.vocab)
+    model.prefill(prompt)
+    canvas = ids_tensor(6, shape.canvas, shape.vocab)
+    logits = model.denoise_step(canvas, 0)
+    torch.cuda.synchronize()
+    cache = OM.KVCache.empty(shape, 224)
+    OM.encode(W, cache, prompt.cpu().numpy(), shape)
+    ref, _, infos = OM.denoise_step(W, cache, canvas.cpu().numpy(), None, shape, return_info=True)
+    cflag = router_flags(infos, shape.top_k)
+    print(f"canvas router near-ties: {int(cflag.sum())} of {shape.canvas}")
+    got = to_f64(logits)
+    assert np.isfinite(got).all()
+    assert_close(got[~cflag], ref[~cflag], tol, "logits at the cache end")
+    model.close()
