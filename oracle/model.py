@@ -125,10 +125,19 @@ def ffn(h: np.ndarray, w: dict, gated: bool, prefix: str = "") -> np.ndarray:
     return a @ w[prefix + "down"].T
 
 
-def route(h: np.ndarray, wr: np.ndarray, top_k: int, renorm: bool = False):
-    """Router: logits, selected experts (descending logit, lowest index on ties), gates."""
+def route(h: np.ndarray, wr: np.ndarray, top_k: int, renorm: bool = False, forced_sel=None):
+    """Router: logits, selected experts (descending logit, lowest index on ties), gates.
+
+    ``forced_sel`` [M, top_k] (teacher forcing, for comparisons where another
+    implementation's rounding legitimately picked a different expert at a
+    near-tie): use these experts instead of this router's own choice; the
+    gates are still this router's softmax probabilities of them.
+    """
     r = h @ wr.T
-    order = np.argsort(-r, axis=-1, kind="stable")[:, :top_k]
+    if forced_sel is None:
+        order = np.argsort(-r, axis=-1, kind="stable")[:, :top_k]
+    else:
+        order = np.asarray(forced_sel, dtype=np.int64).reshape(r.shape[0], top_k)
     p = softmax(r, axis=-1)
     gates = np.take_along_axis(p, order, axis=-1)
     if renorm:
@@ -141,9 +150,11 @@ def topk_from_logits(r: np.ndarray, top_k: int):
     return np.argsort(-np.asarray(r, dtype=np.float64), axis=-1, kind="stable")[:, :top_k]
 
 
-def moe(h: np.ndarray, lw: dict, shape: ModelShape):
-    """Sparse MoE FFN: sum over the k selected experts of gate * FFN_e(h), plus the shared expert."""
-    r, sel, gates = route(h, lw["wr"], shape.top_k, shape.renorm_gates)
+def moe(h: np.ndarray, lw: dict, shape: ModelShape, forced_sel=None):
+    """Sparse MoE FFN: sum over the k selected experts of gate * FFN_e(h), plus the shared expert.
+
+    ``forced_sel``: teacher-forced expert choice (see ``route``)."""
+    r, sel, gates = route(h, lw["wr"], shape.top_k, shape.renorm_gates, forced_sel)
     y = np.zeros_like(h)
     for e in np.unique(sel):
         rows, slot = np.nonzero(sel == e)
@@ -169,11 +180,12 @@ class KVCache:
 
 
 def layer_forward(lw: dict, x: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, pos0: int,
-                  shape: ModelShape, causal: bool):
+                  shape: ModelShape, causal: bool, forced_sel=None):
     """One transformer layer over M rows placed at positions pos0 .. pos0+M-1.
 
     The rows' keys/values are written into cache_k/cache_v (modified in place)
     at those positions, and attention reads positions 0 .. pos0+M-1.
+    ``forced_sel``: teacher-forced expert choice of the MoE (see ``route``).
     Returns (new x, info dict with the router decisions).
     """
     M = x.shape[0]
@@ -193,7 +205,7 @@ def layer_forward(lw: dict, x: np.ndarray, cache_k: np.ndarray, cache_v: np.ndar
     o = o.transpose(1, 0, 2).reshape(M, Hq * hd)
     x = x + o @ lw["wo"].T
     h2 = rms_norm(x, shape.rms_eps)
-    y, info = moe(h2, lw, shape)
+    y, info = moe(h2, lw, shape, forced_sel)
     info["h_attn"] = h
     info["h_moe"] = h2
     return x + y, info
@@ -215,28 +227,32 @@ def self_condition(W, probs: np.ndarray) -> np.ndarray:
 
 
 def denoise_step(W, cache: KVCache, canvas, sc: np.ndarray | None, shape: ModelShape,
-                 return_info: bool = False):
+                 return_info: bool = False, forced_sel=None):
     """Denoiser mode: bidirectional pass over the canvas, logits at every position.
 
     The canvas keys/values go to positions cache.length .. +C as scratch; the
-    committed length is not changed.
+    committed length is not changed. ``forced_sel``: None, or a list with one
+    teacher-forced expert choice [C, top_k] (or None) per layer.
     """
     x = embed(W, canvas)
     if sc is not None:
         x = x + sc
     infos = []
     for l in range(shape.n_layers):
-        x, info = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=False)
+        fs = None if forced_sel is None else forced_sel[l]
+        x, info = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=False,
+                                forced_sel=fs)
         infos.append(info)
     logits = lm_head(W, x, shape)
     return (logits, x, infos) if return_info else logits
 
 
-def encode(W, cache: KVCache, ids, shape: ModelShape, infos: list | None = None) -> None:
+def encode(W, cache: KVCache, ids, shape: ModelShape, infos: list | None = None, forced_sel=None) -> None:
     """Encoder mode: causal pass over ``ids`` appended at cache.length; extends the cache.
 
     Used for the prompt prefill and for committing a finished block. When
     ``infos`` is a list, each layer's router decisions are appended to it.
+    ``forced_sel``: as in ``denoise_step``, one entry per layer.
     """
     ids = np.asarray(ids, dtype=np.int64)
     n = len(ids)
@@ -244,7 +260,9 @@ def encode(W, cache: KVCache, ids, shape: ModelShape, infos: list | None = None)
         raise ValueError("KV capacity exceeded")
     x = embed(W, ids)
     for l in range(shape.n_layers):
-        x, info = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=True)
+        fs = None if forced_sel is None else forced_sel[l]
+        x, info = layer_forward(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, causal=True,
+                                forced_sel=fs)
         if infos is not None:
             infos.append(info)
     cache.length += n

@@ -127,9 +127,10 @@ def brute_moe(h, lw, shape):
                 if best is None or r[e] > r[best]:
                     best = e
             chosen.append(best)
+        mass = sum(p[e] for e in chosen) if shape.renorm_gates else 1.0
         for e in chosen:
             w = lw["experts"][e]
-            out[t] += p[e] * _brute_ffn(h[t], w, shape.gated, "")
+            out[t] += p[e] / mass * _brute_ffn(h[t], w, shape.gated, "")
         out[t] += _brute_ffn(h[t], lw, shape.gated, "sh_")
     return out
 
@@ -305,3 +306,244 @@ def test_layer_with_rope_rotates_cached_keys_and_queries():
     ck0 = np.zeros_like(ck)
     M.layer_forward(lw, x, ck0, np.zeros_like(ck), 7, shape0, causal=True)
     assert np.allclose(ck0[:, 7:12], k)
+
+
+# ------------------------------------------------------------------ the step's wiring, by brute force
+# A loops-only statement of one layer, the encoder pass and the denoising step, written without the
+# oracle's helpers (rms_norm, layer_forward, lm_head, self_condition, denoise_step): per-element
+# loops for the norms and the residual adds, matrix-vector products row by row, the brute-force
+# attention and MoE above. It fixes where self-conditioning enters (added to the input embedding,
+# before the first norm), the pre-norm placement before attention and before the MoE, both
+# residual adds, and the final norm before the tied LM head ([P3] "Encoder-denoiser design",
+# "Inference mechanism"; [P4] "Gemma-based MoE backbone"; readings 10 and 12).
+def _brute_rms(v, eps):
+    ms = sum(float(a) * float(a) for a in v) / len(v)
+    return np.array([a / math.sqrt(ms + eps) for a in v])
+
+
+def _brute_layer(lw, xs, ck, cv, pos0, shape, causal):
+    """xs: list of residual rows at positions pos0 ..; writes K/V into ck/cv [Hkv, cap, hd]."""
+    hd, Hq, Hkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    Mr = len(xs)
+    hs = [_brute_rms(x, shape.rms_eps) for x in xs]
+    q = np.zeros((Hq, Mr, hd))
+    for i, h in enumerate(hs):
+        qv, kv, vv = lw["wq"] @ h, lw["wk"] @ h, lw["wv"] @ h
+        for j in range(Hq):
+            q[j, i] = qv[j * hd:(j + 1) * hd]
+        for j in range(Hkv):
+            ck[j, pos0 + i] = kv[j * hd:(j + 1) * hd]
+            cv[j, pos0 + i] = vv[j * hd:(j + 1) * hd]
+    o = brute_attention(q, ck[:, :pos0 + Mr], cv[:, :pos0 + Mr], pos0, causal)
+    out_rows, h2s = [], []
+    for i in range(Mr):
+        ocat = np.concatenate([o[j, i] for j in range(Hq)])
+        proj = lw["wo"] @ ocat
+        x1 = np.array([xs[i][c] + proj[c] for c in range(len(xs[i]))])
+        h2s.append(_brute_rms(x1, shape.rms_eps))
+        out_rows.append(x1)
+    y = brute_moe(np.array(h2s), lw, shape)
+    return [np.array([out_rows[i][c] + y[i, c] for c in range(len(out_rows[i]))]) for i in range(Mr)]
+
+
+def _brute_encode(W, ck, cv, length, ids, shape):
+    xs = [np.array(W["embed"][int(t)]) for t in ids]
+    for l in range(shape.n_layers):
+        xs = _brute_layer(W["layers"][l], xs, ck[l], cv[l], length, shape, causal=True)
+    return length + len(ids)
+
+
+def brute_denoise_step(W, ck, cv, length, canvas, sc, shape):
+    E = W["embed"]
+    xs = []
+    for i, t in enumerate(canvas):
+        row = np.array(E[int(t)], dtype=np.float64)
+        if sc is not None:
+            row = np.array([row[c] + sc[i, c] for c in range(len(row))])
+        xs.append(row)
+    for l in range(shape.n_layers):
+        xs = _brute_layer(W["layers"][l], xs, ck[l], cv[l], length, shape, causal=False)
+    logits = np.zeros((len(canvas), E.shape[0]))
+    for i, x in enumerate(xs):
+        hf = _brute_rms(x, shape.rms_eps)
+        for v in range(E.shape[0]):
+            logits[i, v] = sum(hf[c] * E[v, c] for c in range(len(hf)))
+    return logits
+
+
+def brute_self_condition(W, p):
+    """u = sum_v p_v E[v] (loops over the vocabulary), then GeLU(u W1^T) W2^T."""
+    E = W["embed"]
+    out = np.zeros((p.shape[0], E.shape[1]))
+    for i in range(p.shape[0]):
+        u = np.zeros(E.shape[1])
+        for v in range(E.shape[0]):
+            u += p[i, v] * E[v]
+        a = W["sc_w1"] @ u
+        a = np.array([0.5 * z * (1 + math.erf(z / math.sqrt(2))) for z in a])
+        out[i] = W["sc_w2"] @ a
+    return out
+
+
+def _wiring_case(seed=11, rope=0.0, renorm=False, gated=True):
+    import dataclasses
+    s, shape = tiny_shape(top_k=2, gated=gated)
+    shape = dataclasses.replace(shape, canvas=6, renorm_gates=renorm)
+    W = synthetic.SyntheticWeights(s, seed=seed, dtype="f32", sigma=0.4)
+    prompt = synthetic.uniform_ids(seed, synthetic.TID_PROMPT, 5, s["vocab"])
+    canvas = synthetic.uniform_ids(seed + 1, synthetic.TID_PROMPT, 6, s["vocab"])
+    sc = np.random.default_rng(seed).normal(size=(6, s["d_model"]))
+    return s, shape, W, prompt, canvas, sc
+
+
+@pytest.mark.parametrize("with_sc", [False, True])
+@pytest.mark.parametrize("gated,renorm", [(True, False), (False, False), (True, True)])
+def test_denoise_step_matches_brute_force(with_sc, gated, renorm):
+    s, shape, W, prompt, canvas, sc = _wiring_case(gated=gated, renorm=renorm)
+    sc = sc if with_sc else None
+    cache = M.KVCache.empty(shape, 16)
+    M.encode(W, cache, prompt, shape)
+    ck = [np.zeros((shape.n_kv_heads, 16, shape.head_dim)) for _ in range(shape.n_layers)]
+    cv = [np.zeros_like(a) for a in ck]
+    n = _brute_encode(W, ck, cv, 0, prompt, shape)
+    assert n == cache.length == 5
+    for l in range(shape.n_layers):  # encoder pass: same K/V in every layer
+        np.testing.assert_allclose(cache.k[l][:, :5], ck[l][:, :5], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(cache.v[l][:, :5], cv[l][:, :5], rtol=1e-10, atol=1e-12)
+    got = M.denoise_step(W, cache, canvas, sc, shape)
+    want = brute_denoise_step(W, ck, cv, 5, canvas, sc, shape)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_self_condition_matches_brute_force():
+    s, shape, W, *_ = _wiring_case()
+    rng = np.random.default_rng(3)
+    p = rng.random((4, s["vocab"]))
+    p /= p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(M.self_condition(W, p), brute_self_condition(W, p), rtol=1e-10, atol=1e-13)
+
+
+def test_renormalised_gates_are_the_softmax_over_the_chosen_logits():
+    """With renormalisation the k gates sum to 1 and equal softmax over the k chosen logits alone
+    (softmax restricted to a subset is the full softmax divided by its mass on that subset)."""
+    rng = np.random.default_rng(5)
+    h = rng.normal(size=(9, 12))
+    wr = rng.normal(size=(7, 12))
+    r, sel, g = M.route(h, wr, 3, renorm=True)
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, atol=1e-14)
+    chosen = np.take_along_axis(r, sel, axis=1)
+    e = np.exp(chosen - chosen.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(g, e / e.sum(axis=1, keepdims=True), rtol=1e-13)
+    r0, sel0, g0 = M.route(h, wr, 3, renorm=False)
+    assert np.array_equal(sel, sel0) and np.array_equal(r, r0)
+    assert (g0.sum(axis=1) < 1.0).all()
+    # k = E: the renormalised gates are the plain softmax
+    _, _, gall = M.route(h, wr, 7, renorm=True)
+    _, sall, pall = M.route(h, wr, 7, renorm=False)
+    np.testing.assert_allclose(gall, pall, rtol=1e-13)
+
+
+def test_forced_routing_is_the_identity_on_the_own_choice():
+    """Teacher forcing with the router's own choice changes nothing; forcing other experts takes
+    this router's softmax probabilities of those experts as gates."""
+    s, shape, W, prompt, canvas, sc = _wiring_case()
+    lw = W["layers"][0]
+    h = np.random.default_rng(8).normal(size=(5, s["d_model"]))
+    y, info = M.moe(h, lw, shape)
+    y2, info2 = M.moe(h, lw, shape, forced_sel=info["sel"])
+    np.testing.assert_array_equal(y, y2)
+    other = (info["sel"] + 1) % shape.n_experts
+    _, info3 = M.moe(h, lw, shape, forced_sel=other)
+    assert np.array_equal(info3["sel"], other)
+    np.testing.assert_allclose(info3["gates"], np.take_along_axis(M.softmax(info["router_logits"]), other, axis=1))
+
+
+# Plausible wiring mistakes, planted in the oracle (on the CPU): each must make the brute-force
+# comparison fail, so the pin above is shown to see them.
+def _mut_no_final_norm(monkeypatch):
+    monkeypatch.setattr(M, "lm_head", lambda W, x, shape: x @ W["embed"].T)
+
+
+def _faulty_layer(lw, x, ck, cv, pos0, shape, causal, forced_sel=None, h_extra=None, attn_residual=True,
+                  moe_norm=True):
+    """The oracle's layer with one of its wiring choices switched: something added to the normalised
+    attention input, the attention residual dropped, or the MoE fed the un-normalised residual."""
+    Mr = x.shape[0]
+    hd, Hq, Hkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    h = M.rms_norm(x, shape.rms_eps)
+    if h_extra is not None:
+        h = h + h_extra
+    q = (h @ lw["wq"].T).reshape(Mr, Hq, hd).transpose(1, 0, 2)
+    ck[:, pos0:pos0 + Mr] = (h @ lw["wk"].T).reshape(Mr, Hkv, hd).transpose(1, 0, 2)
+    cv[:, pos0:pos0 + Mr] = (h @ lw["wv"].T).reshape(Mr, Hkv, hd).transpose(1, 0, 2)
+    o = M.attention(q, ck[:, :pos0 + Mr], cv[:, :pos0 + Mr], pos0, causal).transpose(1, 0, 2).reshape(Mr, -1)
+    x = (x if attn_residual else 0.0) + o @ lw["wo"].T
+    y, info = M.moe(M.rms_norm(x, shape.rms_eps) if moe_norm else x, lw, shape, forced_sel)
+    return x + y, info
+
+
+def _mut_sc_after_norm(monkeypatch):
+    def step(W, cache, canvas, sc, shape, return_info=False, forced_sel=None):
+        x = np.asarray(W["embed"])[np.asarray(canvas, dtype=np.int64)]  # sc not added to the embedding
+        for l in range(shape.n_layers):
+            x, _ = _faulty_layer(W["layers"][l], x, cache.k[l], cache.v[l], cache.length, shape, False,
+                                 h_extra=sc if l == 0 else None)  # ... but to the first normalised input
+        return M.lm_head(W, x, shape)
+    monkeypatch.setattr(M, "denoise_step", step)
+
+
+def _mut_no_attention_residual(monkeypatch):
+    monkeypatch.setattr(M, "layer_forward", lambda *a, **k: _faulty_layer(*a, attn_residual=False, **k))
+
+
+def _mut_no_moe_norm(monkeypatch):
+    monkeypatch.setattr(M, "layer_forward", lambda *a, **k: _faulty_layer(*a, moe_norm=False, **k))
+
+
+def _mut_gates_renormalised(monkeypatch):
+    orig = M.route
+    monkeypatch.setattr(M, "route", lambda h, wr, k, renorm=False, forced_sel=None: orig(h, wr, k, True, forced_sel))
+
+
+def _mut_sc_scaled(monkeypatch):
+    orig = M.self_condition
+    monkeypatch.setattr(M, "self_condition", lambda W, p: orig(W, p) * 0.5)
+
+
+def _mut_sc_no_gelu(monkeypatch):
+    monkeypatch.setattr(M, "self_condition", lambda W, p: ((p @ W["embed"]) @ W["sc_w1"].T) @ W["sc_w2"].T)
+
+
+@pytest.mark.parametrize("mutation", [_mut_no_final_norm, _mut_sc_after_norm, _mut_no_attention_residual,
+                                      _mut_no_moe_norm, _mut_gates_renormalised])
+def test_brute_force_step_catches_planted_wiring_mistakes(monkeypatch, mutation):
+    s, shape, W, prompt, canvas, sc = _wiring_case()
+    ck = [np.zeros((shape.n_kv_heads, 16, shape.head_dim)) for _ in range(shape.n_layers)]
+    cv = [np.zeros_like(a) for a in ck]
+    _brute_encode(W, ck, cv, 0, prompt, shape)
+    want = brute_denoise_step(W, [a.copy() for a in ck], [a.copy() for a in cv], 5, canvas, sc, shape)
+    cache = M.KVCache([a.copy() for a in ck], [a.copy() for a in cv], 5)
+    mutation(monkeypatch)
+    got = M.denoise_step(W, cache, canvas, sc, shape)
+    assert not np.allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("mutation", [_mut_sc_scaled, _mut_sc_no_gelu])
+def test_brute_force_self_condition_catches_planted_mistakes(monkeypatch, mutation):
+    s, shape, W, *_ = _wiring_case()
+    p = np.random.default_rng(3).random((3, s["vocab"]))
+    p /= p.sum(axis=1, keepdims=True)
+    want = brute_self_condition(W, p)
+    mutation(monkeypatch)
+    assert not np.allclose(M.self_condition(W, p), want, rtol=1e-6, atol=1e-8)
+
+
+def test_faulty_layer_without_a_fault_is_the_oracle_layer():
+    s, shape, W, prompt, canvas, sc = _wiring_case()
+    lw = W["layers"][1]
+    x = np.random.default_rng(2).normal(size=(4, s["d_model"]))
+    c1 = [np.zeros((shape.n_kv_heads, 8, shape.head_dim)) for _ in range(2)]
+    c2 = [a.copy() for a in c1]
+    y1, _ = M.layer_forward(lw, x, c1[0], c1[1], 3, shape, True)
+    y2, _ = _faulty_layer(lw, x, c2[0], c2[1], 3, shape, True)
+    np.testing.assert_array_equal(y1, y2)
