@@ -86,6 +86,7 @@ _SIGS = {
     "dg_ctx_use_graphs": (ctypes.c_int, [_P, _I32]),
     "dg_ctx_use_expert_fp8": (ctypes.c_int, [_P, _P]),
     "dg_kv_length": (_I64, [_P]),
+    "dg_ctx_graph_captures": (_I64, [_P]),
     "dg_kv_set_length": (ctypes.c_int, [_P, _I64]),
     "dg_prefill_kv": (ctypes.c_int, [_P, _P, _I32, _P]),
     "dg_denoise_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _F32, _P, _P]),
@@ -100,7 +101,7 @@ _SIGS = {
  DG_W_SH_UP, DG_W_SH_DOWN, DG_W_EX_GATE, DG_W_EX_UP, DG_W_EX_DOWN) = range(15)
 (DG_BUF_X, DG_BUF_H, DG_BUF_ROUTER_LOGITS, DG_BUF_SEL, DG_BUF_GATE, DG_BUF_SC, DG_BUF_CANVAS, DG_BUF_PRED,
  DG_BUF_STOP, DG_BUF_ENTROPY, DG_BUF_ROW_STATS, DG_BUF_ACCEPT, DG_BUF_Q, DG_BUF_ATTN, DG_BUF_SHARED_ACT,
- DG_BUF_SLOT_OUT, DG_BUF_SLOT_OF) = range(17)
+ DG_BUF_SLOT_OUT, DG_BUF_SLOT_OF, DG_BUF_SEL_LAYERS) = range(18)
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -276,6 +277,10 @@ def dg_ctx_use_expert_fp8(ctx, d_fp8):
 
 def dg_kv_length(ctx) -> int:
     return lib.dg_kv_length(ctx)
+
+
+def dg_ctx_graph_captures(ctx) -> int:
+    return lib.dg_ctx_graph_captures(ctx)
 
 
 def dg_kv_set_length(ctx, length):

@@ -52,6 +52,7 @@ struct AttnArgs {
   int64_t head_stride;  // cap * hd
   int M, Hq, Hkv, hd;
   int pos0;             // absolute position of query row 0; keys 0 .. pos0+M-1
+  const int* pos_dev;   // when set, pos0 is *pos_dev (read on the device) and key_chunk follows from it
   int causal;
   float scale_log2;     // log2(e) / sqrt(hd)
   int splits;
@@ -136,7 +137,14 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
   }
   const int kvh = unit % a.Hkv;
   const int split = unit / a.Hkv;
-  const int L = a.pos0 + a.M;
+  // the committed length may live on the device (a captured step serves every cache length): the
+  // split count is then fixed by the host and each split's key range follows from the length
+  int pos0 = a.pos0, key_chunk = a.key_chunk;
+  if (a.pos_dev) {
+    pos0 = *a.pos_dev;
+    key_chunk = ((pos0 + a.M + a.splits - 1) / a.splits + kKS - 1) / kKS * kKS;
+  }
+  const int L = pos0 + a.M;
   const int g4 = lane >> 4, fr = lane & 15;
 
   int qr[QT], qhead[QT], qm[QT], qpos[QT];
@@ -147,17 +155,17 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
     qvalid[t] = qr[t] < rows_in_group;
     qhead[t] = kvh * G + (qvalid[t] ? qr[t] / a.M : 0);
     qm[t] = qvalid[t] ? qr[t] % a.M : 0;
-    qpos[t] = a.pos0 + qm[t];
+    qpos[t] = pos0 + qm[t];
   }
 
   // key range of this split, clipped for causal attention to the workgroup's last position
-  const int k_lo = split * a.key_chunk;
-  int k_hi = min(L, k_lo + a.key_chunk);
+  const int k_lo = split * key_chunk;
+  int k_hi = min(L, k_lo + key_chunk);
   if (a.causal) {
     const int first_row = qt * kWGRows;
     const int last_row = min(rows_in_group - 1, first_row + kWGRows - 1);
-    int maxpos = a.pos0 + a.M - 1;
-    if (first_row / a.M == last_row / a.M) maxpos = a.pos0 + last_row % a.M;
+    int maxpos = pos0 + a.M - 1;
+    if (first_row / a.M == last_row / a.M) maxpos = pos0 + last_row % a.M;
     k_hi = min(k_hi, maxpos + 1);
   }
   const int nst = k_hi > k_lo ? (k_hi - k_lo + kKS - 1) / kKS : 0;
@@ -414,7 +422,8 @@ __global__ void attn_f32_kernel(AttnArgs a) {
   const float* q = static_cast<const float*>(a.q) + static_cast<int64_t>(m) * a.ldq + j * hd;
   const float* kb = static_cast<const float*>(a.kc) + kvh * a.head_stride;
   const float* vb = static_cast<const float*>(a.vc) + kvh * a.head_stride;
-  const int L = a.causal ? a.pos0 + m + 1 : a.pos0 + a.M;
+  const int pos0 = a.pos_dev ? *a.pos_dev : a.pos0;
+  const int L = a.causal ? pos0 + m + 1 : pos0 + a.M;
   float acc[128];
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   float mx = -INFINITY, l = 0.f;
@@ -438,7 +447,9 @@ __global__ void attn_f32_kernel(AttnArgs a) {
 #endif
 constexpr int kAttnWGs = DG_ATT_WGS;  // target workgroups of a launch
 int attn_max_splits() { return kMergeMax; }
-int attn_v_overrun() { return std::max(att_keys(1), att_keys(kQTLarge)) - kVB; }
+constexpr int kVOverrun = (att_keys(1) > att_keys(kQTLarge) ? att_keys(1) : att_keys(kQTLarge)) - kVB;
+static_assert(kVOverrun == 96, "the KV tail that dg.h documents (largest key stage - 32 positions)");
+int attn_v_overrun() { return kVOverrun; }
 
 // Upper bound of splits x M over the launches attention() makes for M query rows (the rows of its
 // partial buffers).
@@ -450,15 +461,17 @@ int64_t attn_partial_rows(int M, int Hq, int Hkv) {
   return static_cast<int64_t>(splits) * M;
 }
 
+// pos_dev (optional): the position of query row 0 is read on the device; the split count is then
+// chosen for the largest position pos_max, so one launch configuration serves every length up to it.
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
-              int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
-              int dtype, hipStream_t s) {
+              int Hkv, int hd, int pos0, const int* pos_dev, int pos_max, int causal, float* part_o,
+              float* part_ml, void* o, int64_t ldo, int dtype, hipStream_t s) {
   AttnArgs a;
   a.q = q; a.ldq = ldq; a.kc = kc; a.vc = vc; a.head_stride = head_stride;
-  a.M = M; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.pos0 = pos0; a.causal = causal;
+  a.M = M; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.pos0 = pos0; a.pos_dev = pos_dev; a.causal = causal;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(hd)));
   a.part_o = part_o; a.part_ml = part_ml; a.o = o; a.ldo = ldo;
-  const int L = pos0 + M;
+  const int L = (pos_dev ? pos_max : pos0) + M;
   if (dtype == DG_F32) {
     if (hd > 128) return fail(DG_ERR_UNSUPPORTED, "fp32 attention needs head_dim <= 128");
     a.splits = 1;
@@ -479,7 +492,9 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
   int splits = std::max(1, std::min(attn_max_splits(), (kAttnWGs + qtiles * Hkv - 1) / (qtiles * Hkv)));
   splits = std::min(splits, std::max(1, (L + 4 * kKS - 1) / (4 * kKS)));
   a.key_chunk = ((L + splits - 1) / splits + kKS - 1) / kKS * kKS;
-  a.splits = (L + a.key_chunk - 1) / a.key_chunk;
+  // a host length drops the splits a rounded-up chunk leaves empty; a device length keeps them
+  // (their key ranges depend on the length; an empty one contributes weight 0 to the merge)
+  a.splits = pos_dev ? splits : (L + a.key_chunk - 1) / a.key_chunk;
   a.qtiles = qtiles;
   const dim3 grid(qtiles * Hkv * a.splits);
   {

@@ -59,8 +59,14 @@ __host__ __device__ inline bf16_t f32_to_bf16(float f) {
 __device__ inline float bf16lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ inline float bf16hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
+// two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; same bits as f32_to_bf16
+// for finite values
+typedef __bf16 bf16x2_native_t __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  bf16x2_native_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ------------------------------------------------------ wave64 reductions

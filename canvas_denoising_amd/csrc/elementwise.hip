@@ -223,39 +223,6 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
 
 // P[m][v] = exp((l[m][v] - max_m) / T - lnZ_m): the sampler's tempered distribution,
 // rebuilt from its row statistics (max raw logit, ln of the tempered partition sum)
-template <typename T>
-__global__ void probs_kernel(const T* __restrict__ logits, const float* __restrict__ stats, float inv_t, int64_t V,
-                             int64_t n, T* __restrict__ P) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
-    const int64_t m = e / V;
-    const float mx = stats[2 * m], lz = stats[2 * m + 1];
-    const float v = to_f32<T>(logits[e]);
-    P[e] = from_f32<T>(__expf((v - mx) * inv_t - lz));
-  }
-}
-
-// vectorised variant: 8 bf16 per thread, V % 8 == 0
-__global__ void probs_bf16x8_kernel(const bf16_t* __restrict__ logits, const float* __restrict__ stats, float inv_t,
-                                    int64_t V, int64_t n8, bf16_t* __restrict__ P) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < n8; g += stride) {
-    const int64_t e = g * 8;
-    const int64_t m = e / V;
-    const float mx = stats[2 * m], lz = stats[2 * m + 1];
-    const uint4 q = *reinterpret_cast<const uint4*>(logits + e);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __expf((bf16lo(w[i]) - mx) * inv_t - lz);
-      const float b = __expf((bf16hi(w[i]) - mx) * inv_t - lz);
-      o[i] = pack_bf16x2(a, b);
-    }
-    *reinterpret_cast<uint4*>(P + e) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
 // out[c][r] = in[r][c]; 64 x 64 tiles through LDS. `in` ([R x C]) is fragment-tiled with groups of gr
 // 16-row blocks (tiles.h) when gr > 0, row-major otherwise; likewise `out` ([C x R]) with gr_out.
 template <typename T>
@@ -332,21 +299,20 @@ int residual_norm(float* x, const float* part, int splits, const float* y, const
   return DG_OK;
 }
 
-int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
-          hipStream_t s) {
-  ProfScope ps("sc_probs", s);
-  const int64_t n = static_cast<int64_t>(M) * V;
-  const float inv_t = 1.0f / temperature;
-  if (dtype == DG_BF16 && V % 8 == 0)
-    probs_bf16x8_kernel<<<grid_for(n / 8), 256, 0, s>>>(static_cast<const bf16_t*>(logits), stats, inv_t, V, n / 8,
-                                                         static_cast<bf16_t*>(P));
-  else if (dtype == DG_BF16)
-    probs_kernel<bf16_t><<<grid_for(n), 256, 0, s>>>(static_cast<const bf16_t*>(logits), stats, inv_t, V, n,
-                                                     static_cast<bf16_t*>(P));
-  else
-    probs_kernel<float><<<grid_for(n), 256, 0, s>>>(static_cast<const float*>(logits), stats, inv_t, V, n,
-                                                    static_cast<float*>(P));
-  DG_LAUNCH_CHECK("probs_kernel");
+// *p = v on `s` (a one-thread kernel: a value the host decides for device code that reads it later,
+// also from a captured graph, without a host-to-device copy)
+__global__ void store_i32_kernel(int32_t* p, int32_t v) { *p = v; }
+__global__ void store_f32_kernel(float* p, float v) { *p = v; }
+
+int store_i32(int32_t* p, int32_t v, hipStream_t s) {
+  store_i32_kernel<<<1, 1, 0, s>>>(p, v);
+  DG_LAUNCH_CHECK("store_i32_kernel");
+  return DG_OK;
+}
+
+int store_f32(float* p, float v, hipStream_t s) {
+  store_f32_kernel<<<1, 1, 0, s>>>(p, v);
+  DG_LAUNCH_CHECK("store_f32_kernel");
   return DG_OK;
 }
 
@@ -427,8 +393,9 @@ __global__ void rope_table_kernel(double theta, int hd, int64_t n_pos, float2* _
 // is null) and key heads of the cache rows at positions pos0 .. pos0 + M - 1 ([Hkv][cap][hd], head
 // stride kv_stride), rotated in place in fp32 and rounded back to T.
 template <typename T>
-__global__ void rope_kernel(T* __restrict__ q, int64_t ldq, T* __restrict__ kc, int64_t kv_stride, int pos0, int M,
-                            int Hq, int Hkv, int hd, const float2* __restrict__ table) {
+__global__ void rope_kernel(T* __restrict__ q, int64_t ldq, T* __restrict__ kc, int64_t kv_stride, int pos0,
+                            const int* __restrict__ pos_dev, int M, int Hq, int Hkv, int hd,
+                            const float2* __restrict__ table) {
   const int half = hd / 2;
   const int H = (q ? Hq : 0) + Hkv;
   const int64_t n = static_cast<int64_t>(M) * H * half;
@@ -438,7 +405,7 @@ __global__ void rope_kernel(T* __restrict__ q, int64_t ldq, T* __restrict__ kc, 
   const int64_t rh = e / half;
   const int head = static_cast<int>(rh % H);
   const int row = static_cast<int>(rh / H);
-  const int pos = pos0 + row;
+  const int pos = (pos_dev ? *pos_dev : pos0) + row;
   T* x;
   if (q && head < Hq) x = q + static_cast<int64_t>(row) * ldq + static_cast<int64_t>(head) * hd;
   else x = kc + static_cast<int64_t>(head - (q ? Hq : 0)) * kv_stride + static_cast<int64_t>(pos) * hd;
@@ -456,18 +423,18 @@ int rope_table(double theta, int hd, int64_t n_pos, float2* table, hipStream_t s
   return DG_OK;
 }
 
-int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, int M, int Hq, int Hkv, int hd,
-               const float2* table, int dtype, hipStream_t s) {
+int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, const int* pos_dev, int M, int Hq,
+               int Hkv, int hd, const float2* table, int dtype, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(M) * ((q ? Hq : 0) + Hkv) * (hd / 2);
   if (n == 0) return DG_OK;
   ProfScope ps("rope", s);
   const unsigned grid = static_cast<unsigned>((n + 255) / 256);
   if (dtype == DG_BF16)
     rope_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<bf16_t*>(q), ldq, static_cast<bf16_t*>(kc), kv_stride, pos0,
-                                             M, Hq, Hkv, hd, table);
+                                             pos_dev, M, Hq, Hkv, hd, table);
   else
-    rope_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(q), ldq, static_cast<float*>(kc), kv_stride, pos0, M,
-                                            Hq, Hkv, hd, table);
+    rope_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(q), ldq, static_cast<float*>(kc), kv_stride, pos0,
+                                            pos_dev, M, Hq, Hkv, hd, table);
   DG_LAUNCH_CHECK("rope_kernel");
   return DG_OK;
 }

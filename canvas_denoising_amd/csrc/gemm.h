@@ -28,6 +28,7 @@ struct GemmArgs {
   int pair_f = 0;
   // EPI_QKV
   int q_cols = 0, head_dim = 0, n_kv = 0, pos0 = 0;
+  const int* pos_dev = nullptr;  // when set, the cache position of row 0 is *pos_dev (read on the device)
   int64_t kv_head_stride = 0;  // elements between KV heads (capacity * head_dim)
   void* kcache = nullptr;
   void* vcache = nullptr;

@@ -77,6 +77,7 @@ __device__ inline void epilogue(const GemmArgs& g, int row, int col, float v) {
 
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k_per_split) {
+  if (g.epi == EPI_QKV && g.pos_dev) g.pos0 = *g.pos_dev;
   using C = GemmCfg<T, BM, BN>;
   using F = Frag<T>;
   __shared__ __align__(16) T sA[2][BM * C::LDK];
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int splits, int k
 // their results are not stored.
 template <int BM, int BN, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(GemmArgs g, int splits, int k_per_split) {
+  if (g.epi == EPI_QKV && g.pos_dev) g.pos0 = *g.pos_dev;
   // NW waves as (NW / 2) x 2 over the tile; every wave issues an equal share of the stage's copies
   constexpr int WM = BM / (NW / 2), WN = BN / 2, TM = WM / 16, TN = WN / 16;
   constexpr int ROWB = 128;  // bytes per tile row: 64 bf16
@@ -411,6 +413,7 @@ constexpr int kSumBatch = 8;
 // combines the gate sum at column j with the up sum at column pair_f + j.
 template <typename T>
 __global__ void splitk_reduce_kernel(GemmArgs g, int splits) {
+  if (g.epi == EPI_QKV && g.pos_dev) g.pos0 = *g.pos_dev;
   const int64_t n = static_cast<int64_t>(g.M) * g.N;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   if (g.epi == EPI_GEGLU) {

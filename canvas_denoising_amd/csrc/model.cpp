@@ -34,16 +34,16 @@ int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStre
 int residual_norm(float* x, const float* part, int splits, const float* y, const float* slot_out,
                   const int32_t* slot_of, int k, void* h, int M, int D, float eps, int dtype, hipStream_t s,
                   const char* name);
-int probs(const void* logits, const float* stats, float temperature, int M, int64_t V, void* P, int dtype,
-          hipStream_t s);
 int transpose(const void* in, int64_t R, int64_t C, int gr, int gr_out, void* out, int dtype, hipStream_t s);
 int sc_embed_splits(int N, int64_t K, int dtype);
-int sc_embed(const void* P, int64_t ldp, const void* Et, int M, int N, int64_t K, float* part, void* u, int dtype,
-             hipStream_t s);
+int sc_embed(const void* logits, int64_t ldl, const float* stats, const float* temp, const void* Et, int M, int N,
+             int64_t K, float* part, void* u, int dtype, hipStream_t s);
 int zero_fill(void* p, size_t bytes, hipStream_t s);
+int store_i32(int32_t* p, int32_t v, hipStream_t s);
+int store_f32(float* p, float v, hipStream_t s);
 int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_t head_stride, int M, int Hq,
-              int Hkv, int hd, int pos0, int causal, float* part_o, float* part_ml, void* o, int64_t ldo,
-              int dtype, hipStream_t s);
+              int Hkv, int hd, int pos0, const int* pos_dev, int pos_max, int causal, float* part_o,
+              float* part_ml, void* o, int64_t ldo, int dtype, hipStream_t s);
 int attn_max_splits();
 int attn_v_overrun();
 int64_t attn_partial_rows(int M, int Hq, int Hkv);
@@ -58,8 +58,8 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
                 const int32_t* offsets, const int32_t* perm, const float* slot_gate, void* act, float* out,
                 int dtype, const ExpertsFp8* q8, const int32_t* tiles, int M, int k, hipStream_t s);
 int rope_table(double theta, int hd, int64_t n_pos, float2* table, hipStream_t s);
-int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, int M, int Hq, int Hkv, int hd,
-               const float2* table, int dtype, hipStream_t s);
+int rope_apply(void* q, int64_t ldq, void* kc, int64_t kv_stride, int pos0, const int* pos_dev, int M, int Hq,
+               int Hkv, int hd, const float2* table, int dtype, hipStream_t s);
 int quantize_fp8(const void* src, int64_t src_stride, void* codes, int64_t code_stride, float* scales, int E, int R,
                  int K, int gr, int gw, hipStream_t s);
 int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s);
@@ -229,21 +229,24 @@ int check_desc(const dg_model_desc* d) {
   return DG_OK;
 }
 
-// a captured denoising step body and what it was captured for
+// a captured denoising step body and the caller's buffers it was captured for (the committed KV
+// length and the self-conditioning temperature are read on the device, so they are not part of it)
 struct StepGraph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   const int32_t* canvas = nullptr;
   const void* logits = nullptr;
-  int64_t len = -1;
+  const void* prev_logits = nullptr;
+  const float* prev_stats = nullptr;
 };
 
 // ----------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
-      sc, u, sc_hid, P, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, rope,
-      tiles, total;
+      sc, u, sc_hid, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, rope,
+      tiles, len_dev, sc_temp, total;
   int64_t gpart_floats;
+  int64_t sel_layer;  // elements between the layers' expert choices (and gates)
 };
 
 // rows of one layer pass: a canvas, or a prefill / commit chunk
@@ -270,8 +273,10 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.part_o = take(static_cast<size_t>(prow) * d.n_q_heads * d.head_dim * 4);
   w.part_ml = take(static_cast<size_t>(prow) * d.n_q_heads * 2 * 4);
   w.rlog = take(C * d.n_experts * 4);
-  w.sel = take(CK * 4);
-  w.gate = take(CK * 4);
+  // the expert choices and gates of every layer of the last pass (layer l at l * sel_layer)
+  w.sel_layer = CK;
+  w.sel = take(static_cast<size_t>(d.n_layers) * CK * 4);
+  w.gate = take(static_cast<size_t>(d.n_layers) * CK * 4);
   w.offsets = take((d.n_experts + 1) * 4);
   w.perm = take(CK * 4);
   w.slot_of = take(CK * 4);
@@ -284,7 +289,6 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.sc = take(Cc * D * 4);
   w.u = take(Cc * D * es);
   w.sc_hid = take(Cc * d.d_selfcond * es);
-  w.P = take(static_cast<size_t>(Cc) * d.vocab * es);
   w.scpart = take(static_cast<size_t>(sc_embed_splits(static_cast<int>(D), d.vocab, d.dtype)) * Cc * D * 4);
   w.gpart_floats = 32 * Cc * std::max<int64_t>(std::max<int64_t>(D, d.d_selfcond), d.n_experts);
   w.gpart = take(w.gpart_floats * 4);
@@ -300,6 +304,8 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   // rotary embedding: (cos, sin) per cache position and frequency
   w.rope = take(d.rope_theta > 0.f ? static_cast<size_t>(capacity) * (d.head_dim / 2) * 8 : 0);
   w.tiles = take((2 + CK / 128 + d.n_experts + 8) * 4);  // token-tile list of a chunk
+  w.len_dev = take(4);   // int32: the committed KV length, as the denoising step reads it
+  w.sc_temp = take(4);   // float: the temperature of the self-conditioning distribution
   w.total = cur;
   return w;
 }
@@ -326,6 +332,8 @@ struct dg_ctx {
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
   dg::StepGraph graphs[2];
+  int last_layer = 0;  // layer of the last routing (DG_BUF_SEL / DG_BUF_GATE)
+  int64_t captures = 0;  // step graphs captured so far
 };
 
 namespace dg {
@@ -361,7 +369,8 @@ static bool fused_norm_ok(const dg_model_desc& d) {
   return DG_FUSED_NORM && d.d_model % 4 == 0 && d.d_model <= 3072;
 }
 
-// One layer over M rows of the residual stream x placed at cache positions pos0 .. pos0+M-1.
+// One layer over M rows of the residual stream x placed at cache positions pos0 .. pos0+M-1 (pos_dev
+// non-null: pos0 is the committed length as the device holds it, so a captured launch serves any).
 // On entry h = RMSNorm(x); on exit x is the layer's output and h = RMSNorm(x) again (the next
 // layer's input norm, or the final norm before the LM head): every residual update is fused with
 // the norm that follows it. `kv_only` stops after the K/V projection (last encoder layer).
@@ -372,7 +381,8 @@ static bool fused_norm_ok(const dg_model_desc& d) {
 #endif
 constexpr int kSharedMode = DG_SHARED_MODE;
 
-static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causal, bool kv_only, hipStream_t s) {
+static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, const int* pos_dev, bool causal, bool kv_only,
+                         hipStream_t s) {
   const dg_model_desc& d = c->d;
   const WsLayout& w = c->wsl;
   const int D = d.d_model, hd = d.head_dim, QW = d.n_q_heads * hd;
@@ -385,7 +395,7 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     g.M = M; g.N = (d.n_q_heads + 2 * d.n_kv_heads) * hd; g.K = D;
     g.epi = EPI_QKV; g.out = wsp<void>(c, w.q); g.ldo = QW;
     g.q_cols = kv_only ? 0 : QW; g.head_dim = hd; g.n_kv = d.n_kv_heads; g.pos0 = pos0;
-    g.kv_head_stride = c->cap * hd; g.kcache = kv_k(c, l); g.vcache = kv_v(c, l);
+    g.kv_head_stride = c->cap * hd; g.kcache = kv_k(c, l); g.vcache = kv_v(c, l); g.pos_dev = pos_dev;
     if (kv_only) {  // only the K/V rows of the fused projection
       g.B = static_cast<const char*>(g.B) + static_cast<size_t>(QW) * D * esize(d);
       g.N = 2 * d.n_kv_heads * hd;
@@ -393,12 +403,12 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     DG_TRY(run_gemm(c, g, s, "qkv_proj", kQkvSplit));
   }
   if (d.rope_theta > 0.f)
-    DG_TRY(rope_apply(kv_only ? nullptr : wsp<void>(c, w.q), QW, kv_k(c, l), c->cap * hd, pos0, M, d.n_q_heads,
-                      d.n_kv_heads, hd, wsp<float2>(c, w.rope), d.dtype, s));
+    DG_TRY(rope_apply(kv_only ? nullptr : wsp<void>(c, w.q), QW, kv_k(c, l), c->cap * hd, pos0, pos_dev, M,
+                      d.n_q_heads, d.n_kv_heads, hd, wsp<float2>(c, w.rope), d.dtype, s));
   if (kv_only) return DG_OK;
   DG_TRY(attention(wsp<void>(c, w.q), QW, kv_k(c, l), kv_v(c, l), c->cap * hd, M, d.n_q_heads, d.n_kv_heads, hd,
-                   pos0, causal ? 1 : 0, wsp<float>(c, w.part_o), wsp<float>(c, w.part_ml), wsp<void>(c, w.o), QW,
-                   d.dtype, s));
+                   pos0, pos_dev, static_cast<int>(c->cap) - M, causal ? 1 : 0, wsp<float>(c, w.part_o),
+                   wsp<float>(c, w.part_ml), wsp<void>(c, w.o), QW, d.dtype, s));
   {
     GemmArgs g;
     g.A = wsp<void>(c, w.o); g.lda = QW;
@@ -456,8 +466,10 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, bool causa
     g.defer_reduce = true;
     g.splits_out = &splits;
     DG_TRY(run_gemm(c, g, s, "router", true));
+    c->last_layer = l;
     DG_TRY(moe_route(splits > 1 ? wsp<float>(c, w.gpart) : wsp<float>(c, w.rlog), splits, M, d.n_experts, d.top_k,
-                     d.renorm_gates, wsp<float>(c, w.rlog), wsp<int32_t>(c, w.sel), wsp<float>(c, w.gate),
+                     d.renorm_gates, wsp<float>(c, w.rlog), wsp<int32_t>(c, w.sel) + l * w.sel_layer,
+                     wsp<float>(c, w.gate) + l * w.sel_layer,
                      wsp<int32_t>(c, w.offsets), wsp<int32_t>(c, w.perm), wsp<int32_t>(c, w.slot_of),
                      wsp<float>(c, w.slot_gate), M > 256 ? wsp<int32_t>(c, w.tiles) : nullptr, s));
   }
@@ -492,25 +504,30 @@ static int encode(dg_ctx* c, const int32_t* ids, int n, hipStream_t s) {
     DG_TRY(embed(wp(c, c->wl.embed), ids + c0, nullptr, x, M, d.d_model, d.vocab, d.dtype, s));
     DG_TRY(rmsnorm(x, wsp<void>(c, c->wsl.h), M, d.d_model, d.rms_eps, d.dtype, s));
     for (int l = 0; l < d.n_layers; ++l)
-      DG_TRY(layer_forward(c, l, x, M, static_cast<int>(c->len), true, l == d.n_layers - 1, s));
+      DG_TRY(layer_forward(c, l, x, M, static_cast<int>(c->len), nullptr, true, l == d.n_layers - 1, s));
     c->len += M;
   }
-  return DG_OK;
+  // the denoising step reads the committed length on the device
+  return store_i32(wsp<int32_t>(c, c->wsl.len_dev), static_cast<int32_t>(c->len), s);
 }
 
-// Everything of a denoising step after the tempered probabilities: self-conditioning from P (when
-// sc_on), the embedding, the layers and the LM head. Its launches depend only on the pointers,
-// sc_on and the committed KV length, so it can be captured once and replayed.
-static int denoise_body(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logits, hipStream_t s) {
+// A denoising step: self-conditioning from the previous step's logits and row statistics (when
+// prev_logits is set; the tempered probabilities are formed inside the P E product with the
+// temperature the device holds), the embedding, the layers and the LM head. Its launches depend
+// only on the caller's pointers and on whether self-conditioning is on (the committed KV length and
+// the temperature are read on the device), so it is captured once and replayed.
+static int denoise_body(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats,
+                        void* logits, hipStream_t s) {
   const dg_model_desc& d = c->d;
   const WsLayout& w = c->wsl;
   const int C = d.canvas, D = d.d_model;
   float* x = wsp<float>(c, w.x);
   const float* sc = nullptr;
-  if (sc_on) {
-    // u = P E: P [C x V] row-major, E^T [D x V] tiled like the embedding
-    DG_TRY(sc_embed(wsp<void>(c, w.P), d.vocab, wp(c, c->wl.embed_t), C, D, d.vocab, wsp<float>(c, w.scpart),
-                    wsp<void>(c, w.u), d.dtype, s));
+  if (prev_logits) {
+    // u = P E: P [C x V] the tempered distribution of the previous logits (formed in the kernel),
+    // E^T [D x V] tiled like the embedding
+    DG_TRY(sc_embed(prev_logits, d.vocab, prev_stats, wsp<float>(c, w.sc_temp), wp(c, c->wl.embed_t), C, D,
+                    d.vocab, wsp<float>(c, w.scpart), wsp<void>(c, w.u), d.dtype, s));
     {
       GemmArgs g;
       g.A = wsp<void>(c, w.u); g.lda = D;
@@ -532,8 +549,9 @@ static int denoise_body(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logi
   void* h = wsp<void>(c, w.h);
   DG_TRY(embed(wp(c, c->wl.embed), canvas, sc, x, C, D, d.vocab, d.dtype, s));
   DG_TRY(rmsnorm(x, h, C, D, d.rms_eps, d.dtype, s));
+  const int* pos_dev = wsp<int32_t>(c, w.len_dev);
   for (int l = 0; l < d.n_layers; ++l)  // each layer leaves h = RMSNorm(its output)
-    DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), false, false, s));
+    DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), pos_dev, false, false, s));
   return vocab_gemm(h, D, wp(c, c->wl.embed), C, d.vocab, D, logits, d.vocab, d.dtype, s);
 }
 
@@ -547,13 +565,15 @@ static void drop_graph(StepGraph& g) {
 // a graph removes. Captured on the context's own stream (the caller's may be the legacy default
 // stream, which cannot capture; the second stream joins through the fork event), launched on s.
 // While per-kernel profiling is on, steps run eagerly so every launch records its events.
-static int denoise_graphed(dg_ctx* c, const int32_t* canvas, bool sc_on, void* logits, hipStream_t s) {
-  if (prof_on() || !c->use_graphs) return denoise_body(c, canvas, sc_on, logits, s);
-  StepGraph& g = c->graphs[sc_on ? 1 : 0];
-  if (!(g.exec && g.canvas == canvas && g.logits == logits && g.len == c->len)) {
+static int denoise_graphed(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats,
+                           void* logits, hipStream_t s) {
+  if (prof_on() || !c->use_graphs) return denoise_body(c, canvas, prev_logits, prev_stats, logits, s);
+  StepGraph& g = c->graphs[prev_logits ? 1 : 0];
+  if (!(g.exec && g.canvas == canvas && g.logits == logits && g.prev_logits == prev_logits &&
+        g.prev_stats == prev_stats)) {
     drop_graph(g);
     DG_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-    const int rc = denoise_body(c, canvas, sc_on, logits, c->cap_stream);
+    const int rc = denoise_body(c, canvas, prev_logits, prev_stats, logits, c->cap_stream);
     hipGraph_t graph = nullptr;
     const hipError_t e = hipStreamEndCapture(c->cap_stream, &graph);
     if (rc != DG_OK) {
@@ -571,7 +591,9 @@ static int denoise_graphed(dg_ctx* c, const int32_t* canvas, bool sc_on, void* l
     g.exec = exec;
     g.canvas = canvas;
     g.logits = logits;
-    g.len = c->len;
+    g.prev_logits = prev_logits;
+    g.prev_stats = prev_stats;
+    ++c->captures;
   }
   DG_HIP(hipGraphLaunch(g.exec, s));
   return DG_OK;
@@ -579,10 +601,8 @@ static int denoise_graphed(dg_ctx* c, const int32_t* canvas, bool sc_on, void* l
 
 static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats, float prev_t,
                    void* logits, hipStream_t s) {
-  const dg_model_desc& d = c->d;
-  if (prev_logits != nullptr)
-    DG_TRY(probs(prev_logits, prev_stats, prev_t, d.canvas, d.vocab, wsp<void>(c, c->wsl.P), d.dtype, s));
-  return denoise_graphed(c, canvas, prev_logits != nullptr, logits, s);
+  if (prev_logits != nullptr) DG_TRY(store_f32(wsp<float>(c, c->wsl.sc_temp), prev_t, s));
+  return denoise_graphed(c, canvas, prev_logits, prev_stats, logits, s);
 }
 
 static int check_ctx(const dg_ctx* c) {
@@ -823,9 +843,15 @@ int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8) {
 
 int64_t dg_kv_length(const dg_ctx* ctx) { return ctx ? ctx->len : -1; }
 
+int64_t dg_ctx_graph_captures(const dg_ctx* ctx) { return ctx ? ctx->captures : -1; }
+
 int dg_kv_set_length(dg_ctx* ctx, int64_t length) {
   DG_TRY(check_ctx(ctx));
   if (length < 0 || length > ctx->cap) return fail(DG_ERR_CAPACITY, "length outside [0, capacity]");
+  // the device copy is written behind everything already queued on any stream
+  DG_HIP(hipDeviceSynchronize());
+  DG_TRY(store_i32(wsp<int32_t>(ctx, ctx->wsl.len_dev), static_cast<int32_t>(length), nullptr));
+  DG_HIP(hipStreamSynchronize(nullptr));
   ctx->len = length;
   return DG_OK;
 }
@@ -864,7 +890,7 @@ int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32
   if (ctx->len + rows > ctx->cap) return fail(DG_ERR_CAPACITY, "rows do not fit in the KV cache");
   hipStream_t s = as_stream(stream);
   DG_TRY(rmsnorm(d_x, wsp<void>(ctx, ctx->wsl.h), rows, ctx->d.d_model, ctx->d.rms_eps, ctx->d.dtype, s));
-  return layer_forward(ctx, layer, d_x, rows, static_cast<int>(ctx->len), causal != 0, false, s);
+  return layer_forward(ctx, layer, d_x, rows, static_cast<int>(ctx->len), nullptr, causal != 0, false, s);
 }
 
 int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d_logits, int32_t* d_block_out,
@@ -910,13 +936,15 @@ int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes)
   const dg_model_desc& d = ctx->d;
   const WsLayout& w = ctx->wsl;
   const size_t C = d.canvas, es = esize(d);
+  const size_t K = d.top_k, sel_l = static_cast<size_t>(ctx->last_layer) * w.sel_layer * 4;
   size_t off, n;
   switch (which) {
     case DG_BUF_X: off = w.x; n = C * d.d_model * 4; break;
     case DG_BUF_H: off = w.h; n = C * d.d_model * es; break;
     case DG_BUF_ROUTER_LOGITS: off = w.rlog; n = C * d.n_experts * 4; break;
-    case DG_BUF_SEL: off = w.sel; n = C * d.top_k * 4; break;
-    case DG_BUF_GATE: off = w.gate; n = C * d.top_k * 4; break;
+    case DG_BUF_SEL: off = w.sel + sel_l; n = C * K * 4; break;
+    case DG_BUF_GATE: off = w.gate + sel_l; n = C * K * 4; break;
+    case DG_BUF_SEL_LAYERS: off = w.sel; n = static_cast<size_t>(d.n_layers) * w.sel_layer * 4; break;
     case DG_BUF_SC: off = w.sc; n = C * d.d_model * 4; break;
     case DG_BUF_CANVAS: off = w.canvas; n = C * 4; break;
     case DG_BUF_PRED: off = w.pred; n = C * 4; break;

@@ -12,21 +12,30 @@
 // each wave multiplies all M rows against its 32 columns: 16 x 2 fragment
 // accumulators, every A fragment read from LDS feeding two MFMAs.
 //
-// The self-conditioning product u = P E (P the tempered distribution,
-// [M x V]) has the same shape with the roles of the dimensions exchanged: P
-// is the staged operand, the transposed embedding E^T (D x V, tiled the same
-// way) the stream, and K = V. Its D / 256 column blocks alone would occupy
-// only a few compute units, so the vocabulary is also split into k shares;
-// the fp32 partials of the shares are summed in order by a second kernel.
-// The column blocks of one k share run on one XCD (the dispatcher sends
-// block b to XCD b % 8), so the P rows they all read are fetched into that
-// XCD's L2 once.
+// The self-conditioning product u = P E (P the tempered distribution of the
+// previous step, [M x V]; [P3] "Inference mechanism") has the same shape with
+// the roles of the dimensions exchanged: P is the staged operand, the
+// transposed embedding E^T (D x V, tiled the same way) the stream, and K = V.
+// P is never stored: the kernel loads the logits, forms
+// p = 2^(l c - b_r) with c = log2(e) / T and b_r = m_r c + ln(Z_r) log2(e)
+// from the sampler's row statistics (m_r, ln Z_r), and writes the bf16 / fp32
+// probabilities into the LDS ring where the LM head's copies would land. Its
+// D / 256 column blocks alone would occupy only a few compute units, so the
+// vocabulary is also split into k shares; the fp32 partials of the shares are
+// summed in order by a second kernel. The column blocks of one k share run on
+// one XCD (the dispatcher sends block b to XCD b % 8), so the logits rows
+// they all read are fetched into that XCD's L2 once.
 //
 // One loop iteration per k-tile: wait until the copies of the k-tile have
-// landed (each wave issues exactly 8 loads per k-tile, 4 copies into LDS and
-// 4 register loads of E, so a fixed vmcnt leaves the younger k-tiles in
-// flight), one barrier, issue the k-tile NS-1 ahead (k-tiles past the end
-// re-read the last one and are never used), multiply.
+// landed (each wave issues exactly 8 loads per k-tile, 4 copies into LDS and 4
+// register loads of E, so a fixed vmcnt leaves the younger k-tiles in flight),
+// one barrier, issue the k-tile NS-1 ahead (k-tiles past the end re-read the
+// last one and are never used), multiply. Self-conditioning copies the raw
+// logits the same way, one k-tile further ahead (a ring of 4): at iteration
+// kt, while the MFMAs of k-tile kt run, every lane turns the pieces its own
+// copies of k-tile kt+1 wrote into probabilities in place (its own wave's
+// vmcnt says they have landed, and no other lane touches them); the next
+// iteration's barrier publishes them.
 #include <algorithm>
 
 #include "dg_common.h"
@@ -39,7 +48,8 @@ namespace dg {
 
 constexpr int kVW = 8;         // waves per workgroup
 constexpr int kVRows = 256;    // rows of h staged per k-tile (M <= 256)
-constexpr int kVNS = 3;        // ring depth (k-tiles)
+constexpr int kVNS = 3;        // ring depth (k-tiles) of the LM head
+constexpr int kVNSsc = 4;      // ring depth of the self-conditioning product
 constexpr int kVRowB = 128;    // bytes of one h row per k-tile
 constexpr int kMaxSplitSum = 32;  // most k shares of the split form
 
@@ -64,16 +74,24 @@ __device__ inline f32x8_t lds_frag<float>(const unsigned char* stage, int r, int
   return f;
 }
 
+enum VocabMode : int { kLmHead = 0, kSelfCond = 1 };
+
 // Grid: ceil(V / (32 kVW)) workgroups of kVW waves; wave w of block b owns vocabulary group
 // b * kVW + w (E rows 32 g .. 32 g + 31).
-// PART: the split-k form. Block b: slot q = (b % 8) J + b / 8 (J = grid / 8) names k share q / nblk
-// and column block q % nblk; its k-tiles are [KT s / S, KT (s + 1) / S); it stores fp32 partials
-// part[s][row][col] (row stride ldo) instead of T outputs.
-template <typename T, bool PART>
+// kSelfCond: the split-k form. Block b: slot q = (b % 8) J + b / 8 (J = grid / 8) names k share q / nblk
+// and column block q % nblk; its k-tiles are [KT s / S, KT (s + 1) / S); `h` holds the logits [M x K]
+// (row stride ldh), stats [M x 2] their rows' (max, ln Z) and *temp the temperature; it stores fp32
+// partials part[s][row][col] (row stride ldo) instead of T outputs.
+template <typename T, int MODE>
 __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restrict__ h, int64_t ldh,
                                                              const T* __restrict__ E, int M, int V, int D,
                                                              T* __restrict__ logits, int64_t ldo,
-                                                             float* __restrict__ part, int S, int nblk) {
+                                                             float* __restrict__ part, int S, int nblk,
+                                                             const float* __restrict__ stats,
+                                                             const float* __restrict__ temp) {
+  constexpr bool SC = MODE == kSelfCond;
+  constexpr int NS = kVNS;                                  // register ring of E fragments (k-tiles)
+  constexpr int NA = SC ? kVNSsc : kVNS;                    // LDS ring of A stages
   constexpr int KE = kVRowB / static_cast<int>(sizeof(T));  // k elements per k-tile
   constexpr int KS = KE / 32;                               // MFMA k-steps per k-tile
   constexpr int SBYTES = kVRows * kVRowB;                   // 32 KB per stage
@@ -82,12 +100,12 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
   using FT = typename Frag<T>::type;
   static_assert(CPW == 4, "8 loads per k-tile: 4 copies + 4 register loads");
   static_assert((sizeof(T) == 2 && BF == 4) || (sizeof(T) == 4 && BF == 2), "B loads per k-tile");
-  __shared__ __align__(16) unsigned char smem[kVNS * SBYTES];
+  __shared__ __align__(16) unsigned char smem[NA * SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g4 = lane >> 4;
   int blk = blockIdx.x, ks = 0, kbeg = 0, KT = D / KE;
-  if constexpr (PART) {
+  if constexpr (SC) {
     const int J = gridDim.x / 8;
     const int q = (blockIdx.x & 7) * J + (blockIdx.x >> 3);
     if (q >= nblk * S) return;  // padding block of the XCD-aware grid: no barrier reached
@@ -101,27 +119,57 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
   const bool active = grp * 32 < V;  // idle waves run the loop on group 0 (uniform barriers), store nothing
 
   // A copies: copy c = wave * CPW + i covers rows 8c .. 8c+7 of the stage; lane l fills position l % 8
-  // of row 8c + l / 8 with the row's chunk (l % 8) ^ (row % 8). Rows past M re-read row M-1.
-  const T* asrc[CPW];
+  // of row 8c + l / 8 with the row's chunk (l % 8) ^ (row % 8). Rows past M re-read row M-1. (Element
+  // offsets from h: M <= 256 rows of at most 2^23 elements fit in 32 bits.)
+  int aoff[CPW];
+  float arow_b[CPW];  // self-conditioning: b_r = m_r c + ln(Z_r) log2(e) of the copy's row
+  float pc = 0.f;     // c = log2(e) / T
+  if constexpr (SC) pc = kLog2e / *temp;
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int r = (wave * CPW + i) * 8 + lane / 8;
-    asrc[i] = h + static_cast<int64_t>(min(r, M - 1)) * ldh + ((lane % 8) ^ (r & 7)) * (16 / sizeof(T));
+    const int rc = min(r, M - 1);
+    aoff[i] = rc * static_cast<int>(ldh) + ((lane % 8) ^ (r & 7)) * (16 / static_cast<int>(sizeof(T)));
+    if constexpr (SC) arow_b[i] = fmaf(stats[2 * rc], pc, stats[2 * rc + 1] * kLog2e);
+    else arow_b[i] = 0.f;
   }
   // B: this lane's fragment of k-tile 0 of the wave's group (inactive waves re-read group 0)
   const T* bsrc = E + static_cast<int64_t>(active ? grp : 0) * (D / 32) * 2 * kTileElems + lane * 8;
 
-  FT breg[kVNS][BF];
-  auto issue = [&](int kt, int slot) {
+  FT breg[NS][BF];
+  auto issue_a = [&](int kt, int aslot) {
     const int k = kbeg + min(kt, KT - 1);
-    unsigned char* base = smem + slot * SBYTES;
+    unsigned char* base = smem + aslot * SBYTES;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) dma16(asrc[i] + static_cast<int64_t>(k) * KE, base + (wave * CPW + i) * 1024);
+    for (int i = 0; i < CPW; ++i) dma16(h + aoff[i] + k * KE, base + (wave * CPW + i) * 1024);
+  };
+  auto issue_b = [&](int kt, int slot) {
+    const int k = kbeg + min(kt, KT - 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
         breg[slot][s * 2 + n] = Frag<T>::load(bsrc + (static_cast<int64_t>(k * KS + s) * 2 + n) * kTileElems);
+  };
+  // self-conditioning: the logits this lane's copies wrote into slot `slot` become probabilities in
+  // place. In 16 units (piece i, word j: two logits) so that compute() can interleave them with its MFMAs.
+  auto prob_word = [&](uint32_t w, float b) -> uint32_t {
+    if constexpr (sizeof(T) == 2) {
+      return pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(bf16lo(w), pc, -b)),
+                         __builtin_amdgcn_exp2f(fmaf(bf16hi(w), pc, -b)));
+    } else {
+      return __float_as_uint(__builtin_amdgcn_exp2f(fmaf(__uint_as_float(w), pc, -b)));
+    }
+  };
+  auto probs_in_place = [&](int slot) {
+    unsigned char* base = smem + slot * SBYTES + lane * 16;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      uint4* pp = reinterpret_cast<uint4*>(base + (wave * CPW + i) * 1024);
+      const uint4 v = *pp;
+      *pp = make_uint4(prob_word(v.x, arow_b[i]), prob_word(v.y, arow_b[i]), prob_word(v.z, arow_b[i]),
+                       prob_word(v.w, arow_b[i]));
+    }
   };
 
   f32x4_t acc[16][2];
@@ -130,8 +178,8 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
 
   // all 16 row tiles are multiplied (rows past M repeat row M-1 and are not stored): no branches
   // in the loop body, so the compiler's own waits for the E registers stay counted, not drained
-  auto compute = [&](int slot) {
-    const unsigned char* st = smem + slot * SBYTES;
+  auto compute = [&](int aslot, int slot) {
+    const unsigned char* st = smem + aslot * SBYTES;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -142,22 +190,87 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
       }
     }
   };
+  // self-conditioning: compute(aslot, slot) with the conversion of stage cslot spread between the
+  // MFMAs (a unit of two logits after every 32 / 16 = 2 fragment pairs), so that the exponentials run
+  // while the matrix cores work instead of after them
+  auto compute_sc = [&](int aslot, int slot, int cslot) {
+    const unsigned char* st = smem + aslot * SBYTES;
+    uint4* cp = reinterpret_cast<uint4*>(smem + cslot * SBYTES + lane * 16 + wave * CPW * 1024);
+    uint4 raw = cp[0], next = raw;  // piece i, and piece i+1 read ahead (1 KB apart: 64 uint4)
+    uint32_t out[4];
+    constexpr int kSteps = KS * 16;             // fragment pairs of one k-tile
+    constexpr int kEvery = kSteps / (CPW * 4);  // pairs between conversion units
+    static_assert(kEvery >= 1 && kSteps % (CPW * 4) == 0, "conversion units per k-tile");
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const FT af = lds_frag<T>(st, m * 16 + fr, s, g4);
+        acc[m][0] = Frag<T>::mma(af, breg[slot][s * 2 + 0], acc[m][0]);
+        acc[m][1] = Frag<T>::mma(af, breg[slot][s * 2 + 1], acc[m][1]);
+        const int t = s * 16 + m;
+        if (t % kEvery == kEvery - 1) {
+          const int q = t / kEvery, i = q / 4, j = q % 4;
+          if (j == 0 && i + 1 < CPW) next = cp[(i + 1) * 64];
+          const uint32_t w = j == 0 ? raw.x : j == 1 ? raw.y : j == 2 ? raw.z : raw.w;
+          out[j] = prob_word(w, arow_b[i]);
+          if (j == 3) {
+            cp[i * 64] = make_uint4(out[0], out[1], out[2], out[3]);
+            raw = next;
+          }
+        }
+      }
+    }
+  };
+  // u = kt % NS selects the E registers (compile-time); the LDS stage of k-tile kt is kt % NA.
+  // LM head: the copies of k-tile kt+2 go out with its E loads (8 loads a k-tile).
+  // Self-conditioning: iteration kt issues the copies of k-tile kt+3 and the E loads of kt+2, so
+  // at its start the oldest group in flight is (copies of kt+1, E of kt).
   auto step = [&](int kt, int u) {
-    wait_vm_n<(kVNS - 2) * 8>();
-    __builtin_amdgcn_s_barrier();  // k-tile kt is in LDS for all waves; all are done with kt-1
-    issue(kt + kVNS - 1, (u + kVNS - 1) % kVNS);
-    compute(u);
+    if constexpr (SC) {
+      wait_vm_n<8>();  // the copies of k-tile kt+1 and the E fragments of kt have landed
+      // this wave's conversion of k-tile kt (the previous iteration) has completed (lgkmcnt(0)); the
+      // compiler barriers keep every LDS access on its side of the workgroup barrier
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();  // k-tile kt is probabilities for all waves; all are done with kt-1
+      asm volatile("" ::: "memory");
+      issue_a(kt + 3, (kt + 3) % NA);
+      issue_b(kt + 2, (u + 2) % NS);
+      compute_sc(kt % NA, u, (kt + 1) % NA);  // k-tile kt, and k-tile kt+1 into probabilities
+    } else {
+      wait_vm_n<(NS - 2) * 8>();
+      __builtin_amdgcn_s_barrier();  // k-tile kt is in LDS for all waves; all are done with kt-1
+      issue_a(kt + NS - 1, (u + NS - 1) % NS);
+      issue_b(kt + NS - 1, (u + NS - 1) % NS);
+      compute(u, u);
+    }
   };
 
+  static_assert(!SC || (NS == 3 && NA == 4), "self-conditioning rings: E 2 k-tiles ahead, copies 3 ahead");
+  if constexpr (SC) {
+    issue_a(0, 0);
+    issue_a(1, 1);
+    issue_b(0, 0);
+    issue_a(2, 2);
+    issue_b(1, 1);
+    wait_vm_n<16>();  // the copies of k-tile 0 have landed
+    asm volatile("" ::: "memory");
+    probs_in_place(0);  // published by the first iteration's barrier
+  } else {
 #pragma unroll
-  for (int u = 0; u < kVNS - 1; ++u) issue(u, u);
+    for (int u = 0; u < NS - 1; ++u) {
+      issue_a(u, u);
+      issue_b(u, u);
+    }
+  }
   int k0 = 0;
-  for (; k0 + kVNS <= KT; k0 += kVNS) {
+  for (; k0 + NS <= KT; k0 += NS) {
 #pragma unroll
-    for (int u = 0; u < kVNS; ++u) step(k0 + u, u);
+    for (int u = 0; u < NS; ++u) step(k0 + u, u);
   }
 #pragma unroll
-  for (int u = 0; u < kVNS - 1; ++u)
+  for (int u = 0; u < NS - 1; ++u)
     if (k0 + u < KT) step(k0 + u, u);
   wait_vm_n<0>();  // the trailing (never used) copies have landed before the workgroup retires
   if (!active) return;
@@ -168,7 +281,7 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
     for (int i = 0; i < 4; ++i) {
       const int row = m * 16 + g4 * 4 + i;
       if (row < M) {
-        if constexpr (PART) {
+        if constexpr (SC) {
           float* o = part + (static_cast<int64_t>(ks) * M + row) * ldo + grp * 32 + fr;
           o[0] = acc[m][0][i];
           o[16] = acc[m][1][i];
@@ -206,16 +319,19 @@ int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, v
   if (M < 1 || M > kVRows) return fail(DG_ERR_UNSUPPORTED, "LM head: rows must be in [1, 256]");
   const int ke = dtype == DG_BF16 ? 64 : 32;
   if (D % ke != 0 || V % 32 != 0) return fail(DG_ERR_UNSUPPORTED, "LM head: d_model / vocab do not tile");
+  if (static_cast<int64_t>(M) * ldh + D > INT32_MAX) return fail(DG_ERR_UNSUPPORTED, "LM head: rows too long");
   const int grid = (V / 32 + kVW - 1) / kVW;
   ProfScope ps("lm_head", s);
   if (dtype == DG_BF16)
-    vocab_gemm_kernel<bf16_t, false><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
-                                                                static_cast<const bf16_t*>(E), M, V, D,
-                                                                static_cast<bf16_t*>(logits), ldo, nullptr, 1, 0);
+    vocab_gemm_kernel<bf16_t, kLmHead><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(h), ldh,
+                                                                  static_cast<const bf16_t*>(E), M, V, D,
+                                                                  static_cast<bf16_t*>(logits), ldo, nullptr, 1, 0,
+                                                                  nullptr, nullptr);
   else
-    vocab_gemm_kernel<float, false><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(h), ldh,
-                                                               static_cast<const float*>(E), M, V, D,
-                                                               static_cast<float*>(logits), ldo, nullptr, 1, 0);
+    vocab_gemm_kernel<float, kLmHead><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(h), ldh,
+                                                                 static_cast<const float*>(E), M, V, D,
+                                                                 static_cast<float*>(logits), ldo, nullptr, 1, 0,
+                                                                 nullptr, nullptr);
   DG_LAUNCH_CHECK("vocab_gemm_kernel");
   return DG_OK;
 }
@@ -229,25 +345,27 @@ int sc_embed_splits(int N, int64_t K, int dtype) {
   return S;
 }
 
-int sc_embed(const void* P, int64_t ldp, const void* Et, int M, int N, int64_t K, float* part, void* u, int dtype,
-             hipStream_t s) {
+int sc_embed(const void* logits, int64_t ldl, const float* stats, const float* temp, const void* Et, int M, int N,
+             int64_t K, float* part, void* u, int dtype, hipStream_t s) {
   if (M < 1 || M > kVRows) return fail(DG_ERR_UNSUPPORTED, "self-conditioning: rows must be in [1, 256]");
   const int ke = dtype == DG_BF16 ? 64 : 32;
   if (K % ke != 0 || N % 32 != 0 || K > (int64_t{1} << 30))
     return fail(DG_ERR_UNSUPPORTED, "self-conditioning: vocab / d_model do not tile");
+  if (static_cast<int64_t>(M) * ldl + K > INT32_MAX)
+    return fail(DG_ERR_UNSUPPORTED, "self-conditioning: canvas x vocab too large");
   const int nblk = (N / 32 + kVW - 1) / kVW;
   const int S = sc_embed_splits(N, K, dtype);
   const int grid = 8 * ((nblk * S + 7) / 8);
   {
     ProfScope ps("sc_embed", s);
     if (dtype == DG_BF16)
-      vocab_gemm_kernel<bf16_t, true><<<grid, 64 * kVW, 0, s>>>(static_cast<const bf16_t*>(P), ldp,
-                                                                 static_cast<const bf16_t*>(Et), M, N,
-                                                                 static_cast<int>(K), nullptr, N, part, S, nblk);
+      vocab_gemm_kernel<bf16_t, kSelfCond><<<grid, 64 * kVW, 0, s>>>(
+          static_cast<const bf16_t*>(logits), ldl, static_cast<const bf16_t*>(Et), M, N, static_cast<int>(K),
+          nullptr, N, part, S, nblk, stats, temp);
     else
-      vocab_gemm_kernel<float, true><<<grid, 64 * kVW, 0, s>>>(static_cast<const float*>(P), ldp,
-                                                                static_cast<const float*>(Et), M, N,
-                                                                static_cast<int>(K), nullptr, N, part, S, nblk);
+      vocab_gemm_kernel<float, kSelfCond><<<grid, 64 * kVW, 0, s>>>(
+          static_cast<const float*>(logits), ldl, static_cast<const float*>(Et), M, N, static_cast<int>(K),
+          nullptr, N, part, S, nblk, stats, temp);
   }
   DG_LAUNCH_CHECK("vocab_gemm_kernel");
   {

@@ -308,9 +308,11 @@ int dg_quantize_experts_fp8(const dg_model_desc* desc, const void* d_weights, vo
  * (row-major), then values [n_layers][n_kv_heads][capacity / 32][head_dim][32]:
  * V transposed in blocks of 32 positions, where inside a block slot 8 g + j
  * (g = 0..3) holds position 4 g + j for j < 4 and 16 + 4 g + (j - 4) for
- * j >= 4. capacity must be a multiple of 32. The size includes a tail of
- * 96 head_dim-wide positions after the values, which attention reads (whole
- * 128-key stages of V blocks) but never writes or weights. */
+ * j >= 4. capacity must be a multiple of 32. The size includes a tail after
+ * the values of (the attention kernel's largest key stage - 32) head_dim-wide
+ * positions, 128 - 32 = 96 in this build: attention copies whole stages of V
+ * blocks, so the last stage of a key range may read up to that many positions
+ * past the capacity (never written, always weighted by zero). */
 size_t dg_kv_bytes(const dg_model_desc* desc, int64_t capacity);
 /* Scratch the context needs: activations of one layer pass (a canvas, or a
  * prompt / commit chunk of up to max(canvas, prefill_rows) rows), MoE routing
@@ -331,11 +333,15 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
 /* Waits for the device, then frees the context's own stream, events and
  * graphs (never the caller's buffers). */
 int dg_ctx_destroy(dg_ctx* ctx);
-/* Graph replay of the denoising step (default on): the launches of a step
- * after the tempered probabilities are captured once per (canvas, logits
- * pointers, self-conditioning on/off, committed KV length) into a HIP graph
- * and replayed; any change re-captures. Off (0): every launch is issued
- * directly. Steps also run directly while dg_profile_enable is on. */
+/* Graph replay of the denoising step (default on): the launches of a step are
+ * captured into a HIP graph once per (d_canvas, d_logits, d_prev_logits,
+ * d_prev_row_stats) pointer set, one graph with self-conditioning and one
+ * without, and replayed; a change of those pointers re-captures. The committed
+ * KV length and the self-conditioning temperature are read on the device, so
+ * commits, prefills and the temperature schedule replay the same graph (a
+ * one-thread kernel writes each new value on the stream). Off (0): every
+ * launch is issued directly. Steps also run directly while dg_profile_enable
+ * is on. */
 int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
 /* Compute the routed experts from a filled FP8 expert buffer (see
  * dg_quantize_experts_fp8; it must outlive its use and stay unmodified while
@@ -345,6 +351,9 @@ int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
  * FP8 support). */
 int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8);
 int64_t dg_kv_length(const dg_ctx* ctx);
+/* Number of denoising-step graphs the context has captured so far (-1 for NULL): a replay
+ * re-captures only when the caller's pointers change (see dg_ctx_use_graphs). */
+int64_t dg_ctx_graph_captures(const dg_ctx* ctx);
 /* Declare the first `length` cache positions valid without computing them
  * (for caches filled by the caller). */
 int dg_kv_set_length(dg_ctx* ctx, int64_t length);
@@ -361,8 +370,8 @@ int dg_prefill_kv(dg_ctx* ctx, const int32_t* d_prompt_ids, int32_t n_prompt, vo
  * attention over the whole canvas, logits at every canvas position; [P3]
  * "Inference mechanism": self-conditioning). With C = canvas:
  *   if d_prev_logits != NULL: p = softmax(prev_logits / prev_temperature)
- *     rebuilt from d_prev_row_stats (dg_sample_canvas output), u = p E,
- *     sc = GeLU(u W1^T) W2^T; else sc = 0;
+ *     rebuilt from d_prev_row_stats (dg_sample_canvas output) inside the
+ *     u = p E product (p is never stored), sc = GeLU(u W1^T) W2^T; else sc = 0;
  *   x = E[canvas] + sc; every layer: attention of the C rows over cache
  *   positions [0, length) and the C canvas rows (no mask; the canvas K/V go
  *   to cache slots [length, length + C) as scratch), then the MoE FFN;
@@ -416,7 +425,10 @@ enum {
   DG_BUF_ATTN = 13,         /* dtype [canvas x n_q_heads*head_dim] attention output */
   DG_BUF_SHARED_ACT = 14,   /* dtype [canvas x d_shared] shared-expert hidden activation */
   DG_BUF_SLOT_OUT = 15,     /* float [canvas*top_k x d_model] gated routed-expert outputs, expert-major slots */
-  DG_BUF_SLOT_OF = 16       /* int32 [canvas x top_k] slot of each (row, choice) */
+  DG_BUF_SLOT_OF = 16,      /* int32 [canvas x top_k] slot of each (row, choice) */
+  DG_BUF_SEL_LAYERS = 17    /* int32 [n_layers][R][top_k], R = max(canvas, prefill_rows): the experts every
+                               layer chose for the rows of the last pass (a denoising step, or the last
+                               chunk of a prefill / commit, whose last layer computes only K and V) */
 };
 int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
 

@@ -126,3 +126,13 @@ def test_prefill_rows_and_rope_validation(L):
     # the rotary table is one (cos, sin) pair per cache position and frequency
     assert L.dg_workspace_size(mk(rope=10000.0), 4096) - ws0 >= 4096 * 32 * 8
     assert L.dg_workspace_size(mk(rope=-1.0), 4096) == 0
+
+
+@pytest.mark.parametrize("hd,dtype,es", [(128, 0, 2), (64, 0, 2), (64, 1, 4)])
+def test_kv_bytes_carry_the_documented_tail(L, hd, dtype, es):
+    """dg_kv_bytes = K and V of every layer and head, plus the tail dg.h documents: the attention
+    kernel's largest key stage (128) minus one V block (32) = 96 head_dim-wide positions."""
+    from canvas_denoising_amd import configs
+    d = configs.desc(3, 256, 4, 2, hd, 8, 2, 128, 256, 1, 512, 128, dtype, canvas=64)
+    for cap in (64, 224, 4096):
+        assert L.dg_kv_bytes(d, cap) - 2 * 3 * 2 * cap * hd * es == 96 * hd * es

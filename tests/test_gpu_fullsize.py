@@ -3,12 +3,19 @@
 * One MoE denoiser layer (d_model 2816, 16q/8kv x 128 heads, 128 experts top-8 of
   width 704 gated + shared 2816) over a 256-row canvas attending to 4096 cached
   positions plus the canvas: canvas K for every row, router logits for every row
-  (exact top-8 teacher-forced on the GPU's logits), and the layer output on
-  sampled rows.
+  (exact top-8 teacher-forced on the GPU's logits), every one of the 2048 gated
+  routed-expert slot outputs (all 128 experts of the dominant kernel's launch)
+  and the layer output of every row, the oracle teacher-forced on the GPU's
+  expert choice.
 * The 30-layer, 262144-vocab step: the sampler teacher-forced on the GPU's
-  logits (exact), and LM-head logits on sampled (row, vocab) pairs from the
-  GPU's final normalised activations.
+  logits (exact), LM-head logits on sampled (row, vocab) pairs from the GPU's
+  final normalised activations, the self-conditioning vector of sampled rows
+  (the embedding streamed through the host in vocabulary chunks), and the
+  committed block's K/V in deeper layers at sampled positions, teacher-forced
+  on the GPU's caches of the layers below.
 """
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 
@@ -17,9 +24,42 @@ from oracle import model as OM
 from oracle import sampler as OS
 
 from gpu_util import announce, need_gpu, to_f64, torch
-from test_gpu_model import ROUTER_TIE, assert_close
+from test_gpu_model import ROUTER_TIE, assert_close, check_routes, gpu_routes
 
 pytestmark = pytest.mark.gpu
+
+POOL = 16  # host threads for generating weights (NumPy releases the GIL inside its array operations)
+
+
+def expert_ffns(W, layer, rows_of, h, gated=True):
+    """{expert: FFN_e(h[rows])} for the experts in rows_of (expert -> row indices), weights generated
+    on a thread pool and dropped after use."""
+    def one(e):
+        ex = W["layers"][layer]["experts"][e]
+        return e, OM.ffn(h[rows_of[e]], {k: ex[k] for k in (("gate", "up", "down") if gated else ("up", "down"))},
+                         gated)
+    with cf.ThreadPoolExecutor(POOL) as pool:
+        return dict(pool.map(one, sorted(rows_of)))
+
+
+def embed_rows(ids, D, seed=0):
+    """Rows of the synthetic embedding (as the device fills it), float64."""
+    idx = (np.asarray(ids, dtype=np.uint64)[:, None] * np.uint64(D) + np.arange(D, dtype=np.uint64)[None, :]).ravel()
+    return synthetic.bf16_bits_to_f32(synthetic.normal_bf16_bits(seed, synthetic.TID_EMBED, idx, 0.02)).astype(
+        np.float64).reshape(len(ids), D)
+
+
+def probs_times_embedding(p, V, D, chunk=16384, seed=0):
+    """u = p E for p [rows x V], E streamed in vocabulary chunks generated on a thread pool."""
+    def part(c0):
+        c1 = min(V, c0 + chunk)
+        return p[:, c0:c1] @ embed_rows(np.arange(c0, c1), D, seed)
+    with cf.ThreadPoolExecutor(POOL) as pool:
+        parts = list(pool.map(part, range(0, V, chunk)))
+    u = np.zeros((p.shape[0], D))
+    for x in parts:  # fixed order
+        u += x
+    return u
 
 
 @pytest.fixture(scope="module")
@@ -69,35 +109,38 @@ def test_moe_layer_full_size(libs, rope):
     sel_gpu = model.buffer(L.DG_BUF_SEL, torch.int32, (C, d.top_k)).cpu().numpy()
     assert np.array_equal(OM.topk_from_logits(r_gpu, d.top_k), sel_gpu)
     counts = np.bincount(sel_gpu.ravel(), minlength=d.n_experts)
-    print(f"tokens per expert: min {counts.min()} max {counts.max()}")
-    # sampled rows through the whole layer: the oracle's router on 24 candidate rows, then the whole
-    # layer on the first 3 of them whose k-th / (k+1)-th logits are not a near-tie
-    rows = np.arange(0, C, 11)
-    hq = h[rows]
-    q = (hq @ lw["wq"].T).reshape(len(rows), d.n_q_heads, hd).transpose(1, 0, 2)
+    print(f"tokens per expert: min {counts.min()} max {counts.max()}, experts used {int((counts > 0).sum())}")
+    # every row through attention (the oracle's float64 over all 4352 keys)
+    q = (h @ lw["wq"].T).reshape(C, d.n_q_heads, hd).transpose(1, 0, 2)
     if rope > 0:
-        q = OM.rope(q, past + rows, rope)
-    o = np.empty((d.n_q_heads, len(rows), hd))
-    G = d.n_q_heads // d.n_kv_heads
-    for j in range(d.n_q_heads):
-        s = q[j] @ kc[j // G].T / np.sqrt(hd)
-        o[j] = OM.softmax(s) @ vc[j // G]
-    o = o.transpose(1, 0, 2).reshape(len(rows), d.n_q_heads * hd)
-    x1 = xf[rows] + o @ lw["wo"].T
+        q = OM.rope(q, past + np.arange(C), rope)
+    o = OM.attention(q, kc, vc, past, causal=False).transpose(1, 0, 2).reshape(C, d.n_q_heads * hd)
+    x1 = xf + o @ lw["wo"].T
     h2 = OM.rms_norm(x1, shape.rms_eps)
     r = h2 @ lw["wr"].T
-    assert_close(r_gpu[rows], r, 2e-2, "router logits (sampled rows)")
-    pick = np.flatnonzero(OM.router_margin(r, d.top_k) > ROUTER_TIE)[:3]
-    print(f"rows through the whole layer: {rows[pick].tolist()} ({len(pick)} of {len(rows)} candidates)")
-    assert len(pick) == 3
-    rows, x1, h2, r = rows[pick], x1[pick], h2[pick], r[pick]
-    sel = OM.topk_from_logits(r, d.top_k)
-    gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
-    y = OM.ffn(h2, lw, True, prefix="sh_")
-    for i in range(len(rows)):
+    assert_close(r_gpu, r, 2e-2, "router logits (all rows)")
+    check_routes([sel_gpu], [{"router_logits": r}], d.top_k, "full-size layer")
+    # every routed slot, teacher-forced on the GPU's experts: gate x FFN_e(h2) against DG_BUF_SLOT_OUT
+    gates = np.take_along_axis(OM.softmax(r), sel_gpu, axis=1)
+    rows_of = {}
+    for t in range(C):
         for j in range(d.top_k):
-            y[i] += gates[i, j] * OM.ffn(h2[i:i + 1], lw["experts"][int(sel[i, j])], True)[0]
-    assert_close(to_f64(x)[rows], x1 + y, 2e-2, "layer output (sampled rows)")
+            rows_of.setdefault(int(sel_gpu[t, j]), []).append(t)
+    outs = expert_ffns(W, 0, {e: np.array(v) for e, v in rows_of.items()}, h2)
+    slot_of = model.buffer(L.DG_BUF_SLOT_OF, torch.int32, (C, d.top_k)).cpu().numpy()
+    assert sorted(slot_of.ravel().tolist()) == list(range(C * d.top_k))
+    want = np.zeros((C * d.top_k, D))
+    y = OM.ffn(h2, lw, True, prefix="sh_")
+    pos_in = {e: {t: i for i, t in enumerate(v)} for e, v in rows_of.items()}
+    for t in range(C):
+        for j in range(d.top_k):
+            e = int(sel_gpu[t, j])
+            val = gates[t, j] * outs[e][pos_in[e][t]]
+            want[slot_of[t, j]] = val
+            y[t] += val
+    slot_out = to_f64(model.buffer(L.DG_BUF_SLOT_OUT, torch.float32, (C * d.top_k, D)))
+    assert_close(slot_out, want, 2e-2, "routed-expert slot outputs (all 2048 slots, all 128 experts)")
+    assert_close(to_f64(x), x1 + y, 2e-2, "layer output (all rows)")
     model.close()
 
 
@@ -135,15 +178,74 @@ def test_full_step_sampled(libs):
     assert np.array_equal(st.canvas.cpu().numpy()[~flag], res.next_canvas[~flag])
     assert np.abs(to_f64(st.entropy) - res.entropy).max() < 1e-3
     print(f"mean entropy {res.mean_entropy:.3f} (ln V = {np.log(V):.3f}), accepted {int(res.accept.sum())}")
-    # a self-conditioned step and a commit run at full size
+    # a self-conditioned step at full size: the self-conditioning vector of sampled rows against
+    # the oracle's p E (E streamed through the host in vocabulary chunks), teacher-forced on the
+    # GPU's step-0 logits
     T0 = L.dg_temperature(sched, 0)
     logits1 = model.denoise_step(st.canvas, 1, logits, st.row_stats, T0, logits=torch.empty_like(logits))
-    model.commit(st.pred)
     torch.cuda.synchronize()
-    assert model.length == w.prompt + C
     assert torch.isfinite(logits1.float()).all()
     sc = to_f64(model.buffer(L.DG_BUF_SC, torch.float32, (C, D)))
-    assert np.isfinite(sc).all() and np.abs(sc).max() > 0
+    rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
+    p = OS.tempered_probs(lg[rows], T0)
+    u = probs_times_embedding(p, V, D)
+    W = synthetic.SyntheticWeights(configs.shape_dict(d), seed=0, dtype="bf16", sigma=0.02, cache_experts=False)
+    sc_ref = OM.gelu(u @ W["sc_w1"].T) @ W["sc_w2"].T
+    assert_close(sc[rows], sc_ref, 2e-2, "self-conditioning vector (sampled rows, V = 262144)")
+    del lg, p
+    # the block commit, and the committed K/V of deeper layers at sampled positions: each layer's
+    # output for those positions from the oracle, teacher-forced on the GPU's cache of that layer
+    # (keys 0 .. p, checked at the positions below) and on the GPU's expert choice
+    block = st.pred.clone()
+    model.commit(block)
+    torch.cuda.synchronize()
+    assert model.length == w.prompt + C
+    routes = gpu_routes(L, model, C)
+    ids = block.cpu().numpy().astype(np.int64)
+    pick = np.array([0, 77, 190, 255])
+    pos = w.prompt + pick
+    K, Vc = model.kv_view()
+    shape = OM.ModelShape(n_layers=d.n_layers, d_model=D, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                          head_dim=d.head_dim, n_experts=d.n_experts, top_k=d.top_k, d_expert=d.d_expert,
+                          d_shared=d.d_shared, gated=True, vocab=V, d_selfcond=d.d_selfcond)
+    x = embed_rows(ids[pick], D)
+    G = d.n_q_heads // d.n_kv_heads
+    hd = d.head_dim
+    for l in range(4):
+        lw = W["layers"][l]
+        h = OM.rms_norm(x, shape.rms_eps)
+        k_ref = (h @ lw["wk"].T).reshape(len(pick), d.n_kv_heads, hd)
+        v_ref = (h @ lw["wv"].T).reshape(len(pick), d.n_kv_heads, hd)
+        p_t = torch.from_numpy(pos).cuda()
+        assert_close(to_f64(K[l][:, p_t].permute(1, 0, 2)), k_ref, 2e-2, f"committed K of layer {l}")
+        assert_close(to_f64(Vc[l][:, p_t].permute(1, 0, 2)), v_ref, 2e-2, f"committed V of layer {l}")
+        if l == 3:
+            break
+        q = (h @ lw["wq"].T).reshape(len(pick), d.n_q_heads, hd)
+        kl = to_f64(K[l][:, :model.length])
+        vl = to_f64(Vc[l][:, :model.length])
+        o = np.empty((len(pick), d.n_q_heads, hd))
+        for i, pp in enumerate(pos):  # causal: keys 0 .. pp
+            for j in range(d.n_q_heads):
+                sc_ = kl[j // G, :pp + 1] @ q[i, j] / np.sqrt(hd)
+                o[i, j] = OM.softmax(sc_) @ vl[j // G, :pp + 1]
+        x1 = x + o.reshape(len(pick), -1) @ lw["wo"].T
+        h2 = OM.rms_norm(x1, shape.rms_eps)
+        r = h2 @ lw["wr"].T
+        sel = routes[l][pick]
+        check_routes([sel], [{"router_logits": r}], d.top_k, f"commit layer {l}")
+        gates = np.take_along_axis(OM.softmax(r), sel, axis=1)
+        rows_of = {}
+        for i in range(len(pick)):
+            for j in range(d.top_k):
+                rows_of.setdefault(int(sel[i, j]), []).append(i)
+        outs = expert_ffns(W, l, {e: np.array(v) for e, v in rows_of.items()}, h2)
+        y = OM.ffn(h2, lw, True, prefix="sh_")
+        for i in range(len(pick)):
+            for j in range(d.top_k):
+                e = int(sel[i, j])
+                y[i] += gates[i, j] * outs[e][rows_of[e].index(i)]
+        x = x1 + y
     model.close()
 
 

@@ -12,7 +12,7 @@ import synthetic
 from oracle import model as OM
 
 from gpu_util import announce, need_gpu, to_f64, torch
-from test_gpu_model import ROUTER_TIE, assert_close, build, tol_for
+from test_gpu_model import assert_close, build, check_routes, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -24,13 +24,15 @@ def libs():
     return _lib, configs, runtime
 
 
-@pytest.mark.parametrize("dtype,gated,causal,M,past", [
-    ("bf16", 1, False, 64, 40), ("bf16", 1, True, 64, 0), ("bf16", 0, True, 50, 77),
-    ("f32", 0, False, 64, 40), ("f32", 1, True, 37, 5)])
-def test_layer_stages(libs, dtype, gated, causal, M, past):
+@pytest.mark.parametrize("dtype,gated,causal,M,past,renorm", [
+    ("bf16", 1, False, 64, 40, 0), ("bf16", 1, True, 64, 0, 0), ("bf16", 0, True, 50, 77, 0),
+    ("f32", 0, False, 64, 40, 0), ("f32", 1, True, 37, 5, 0), ("bf16", 1, False, 64, 40, 1),
+    ("f32", 0, True, 37, 5, 1)])
+def test_layer_stages(libs, dtype, gated, causal, M, past, renorm):
+    """renorm = 1: gates renormalised over the k chosen experts (dg_model_desc.renorm_gates)."""
     L, configs, runtime = libs
-    announce(f"layer stages {dtype} gated={gated} causal={causal} M={M} past={past}")
-    model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=1, canvas=64, capacity=256)
+    announce(f"layer stages {dtype} gated={gated} causal={causal} M={M} past={past} renorm={renorm}")
+    model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=1, canvas=64, capacity=256, renorm=renorm)
     tol = tol_for(dtype)
     rng = np.random.default_rng(M + past)
     if past:
@@ -71,6 +73,10 @@ def test_layer_stages(libs, dtype, gated, causal, M, past):
     sh_gpu = to_f64(model.buffer(L.DG_BUF_SHARED_ACT, model.dtype, (64, shape.d_shared)))[:M]
     assert_close(sh_gpu, sh, tol, "shared-expert activation")
     gates = np.take_along_axis(OM.softmax(r_gpu), sel, axis=1)
+    if renorm:
+        gates = gates / gates.sum(axis=1, keepdims=True)
+    gate_gpu = to_f64(model.buffer(L.DG_BUF_GATE, torch.float32, (64, shape.top_k)))[:M]
+    np.testing.assert_allclose(gate_gpu, gates, rtol=2e-5, atol=1e-7)
     slot_of = model.buffer(L.DG_BUF_SLOT_OF, torch.int32, (64, shape.top_k)).cpu().numpy()[:M]
     assert sorted(slot_of.ravel().tolist()) == list(range(M * shape.top_k))
     slot_out = to_f64(model.buffer(L.DG_BUF_SLOT_OUT, torch.float32, (64 * shape.top_k, D)))
@@ -82,14 +88,14 @@ def test_layer_stages(libs, dtype, gated, causal, M, past):
     # slots are expert-major and token-ascending
     order = sorted(range(M * shape.top_k), key=lambda p: (sel.ravel()[p], p // shape.top_k))
     assert [slot_of.ravel()[p] for p in order] == list(range(M * shape.top_k))
-    y_ref, _ = OM.layer_forward(lw, x0, np.concatenate([to_f64(K[0, :, :past]),
+    y_ref, info = OM.layer_forward(lw, x0, np.concatenate([to_f64(K[0, :, :past]),
                                                         np.zeros((Hkv, 256 - past, hd))], axis=1),
                                 np.concatenate([to_f64(V[0, :, :past]), np.zeros((Hkv, 256 - past, hd))], axis=1),
-                                past, shape, causal)
-    # the oracle routes on its own float64 logits: near-tie rows may pick another expert
-    keep = OM.router_margin(r, shape.top_k) > ROUTER_TIE
-    assert_close(to_f64(x)[keep], y_ref[keep], tol, "layer output")
+                                past, shape, causal, forced_sel=sel)
+    # the oracle teacher-forced on the GPU's experts (its own near-tie choices may differ)
+    check_routes([sel], [info], shape.top_k, "layer")
+    assert_close(to_f64(x), y_ref, tol, "layer output")
     # the layer leaves h = RMSNorm(its output), the next layer's input
     h_gpu = to_f64(model.buffer(L.DG_BUF_H, model.dtype, (64, D)))[:M]
-    assert_close(h_gpu[keep], OM.rms_norm(y_ref, shape.rms_eps)[keep], tol, "output RMSNorm")
+    assert_close(h_gpu, OM.rms_norm(y_ref, shape.rms_eps), tol, "output RMSNorm")
     model.close()

@@ -3,10 +3,14 @@
 Small models (several GEMM tiles, ragged prompt chunks, both dtypes, gated and
 plain FFNs) are compared row by row and element by element: logits,
 activations and KV entries within a relative error of tol per row
-(||gpu - ref|| / ||ref||) and |gpu - ref| <= 4 tol (|ref| + rms(ref row)) per
-element, tol = 2e-2 for bf16 and 2e-4 for fp32. Router decisions are checked bit-exact teacher-forced
-(the oracle's top-k on the GPU's router logits), and against the oracle's own
-router except tokens whose 8th/9th (k-th/k+1-th) logits are within ROUTER_TIE.
+(||gpu - ref|| / ||ref||) and |gpu - ref| <= tol (|ref| + rms(ref row)) per
+element, tol = 2e-2 for bf16 and 2e-4 for fp32. Router decisions are checked
+bit-exact teacher-forced (the oracle's top-k on the GPU's router logits), and
+against the oracle's own router except tokens whose k-th / (k+1)-th logits are
+within ROUTER_TIE (near-ties, where a rounding flip is legitimate). Every row is
+compared continuously: the oracle runs with the GPU's expert choice of every
+layer (teacher-forced routing, DG_BUF_SEL_LAYERS), so near-tie rows are checked
+like the others instead of being dropped.
 """
 import numpy as np
 import pytest
@@ -31,10 +35,19 @@ def tol_for(dtype):
     return 2e-2 if dtype == "bf16" else 2e-4
 
 
-def assert_close(gpu, ref, tol, what="", elem_factor=4.0):
+def assert_close(gpu, ref, tol, what="", elem_factor=None):
     """'rel tol' read per row (last axis): ||gpu - ref|| / ||ref|| <= tol; plus an
     elementwise guard |gpu - ref| <= elem_factor * tol * (|ref| + rms(ref row)) that
-    catches localised errors the norm would average away."""
+    catches localised errors the norm would average away.
+
+    elem_factor defaults to 1 for fp32 tolerances and to 3 for bf16 ones (tol >= 1e-2). Measured over
+    every bf16 comparison of the GPU suite, the row errors stay below 0.0105 and the largest element
+    error is 2.5 to 3.9 times its row's relative error (worst 0.0377 at a row error of 0.0097): the
+    maximum over n <= 16384 elements of a Gaussian-like rounding error, sqrt(2 ln n) <= 4.4 times its
+    RMS. A localised defect (an element or a column off by 0.2 rms or more) still exceeds 3 x 2e-2
+    several times over; fp32 comparisons pass factor 1 with a margin of 20."""
+    if elem_factor is None:
+        elem_factor = 3.0 if tol >= 1e-2 else 1.0
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
@@ -46,6 +59,7 @@ def assert_close(gpu, ref, tol, what="", elem_factor=4.0):
     rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
     err = np.abs(diff) / (np.abs(ref) + rms + 1e-30)
     worst = float(err.max())
+    print(f"[close] {what}: row {worst_row:.3g} elem {worst:.3g} (tol {tol})")
     assert worst_row <= tol, (f"{what}: row relative error {worst_row:.3g} > {tol} at row "
                               f"{np.unravel_index(row_rel.argmax(), row_rel.shape)}")
     assert worst <= elem_factor * tol, (f"{what}: elementwise scaled error {worst:.3g} > {elem_factor * tol} at "
@@ -54,16 +68,37 @@ def assert_close(gpu, ref, tol, what="", elem_factor=4.0):
 
 
 def build(libs, dtype="bf16", gated=1, n_layers=2, d=256, Hq=4, Hkv=2, hd=64, E=8, k=2, F=128, Fs=256, V=512,
-          dsc=128, canvas=64, capacity=512, seed=3, sigma=0.05, rope=0.0):
+          dsc=128, canvas=64, capacity=512, seed=3, sigma=0.05, rope=0.0, renorm=0):
     L, configs, runtime = libs
     dt = L.DG_BF16 if dtype == "bf16" else L.DG_F32
-    desc = configs.desc(n_layers, d, Hq, Hkv, hd, E, k, F, Fs, gated, V, dsc, dt, canvas=canvas, rope_theta=rope)
+    desc = configs.desc(n_layers, d, Hq, Hkv, hd, E, k, F, Fs, gated, V, dsc, dt, canvas=canvas, rope_theta=rope,
+                        renorm_gates=renorm)
     model = runtime.Model(desc, capacity, seed=seed, sigma=sigma)
     W = synthetic.SyntheticWeights(configs.shape_dict(desc), seed=seed, dtype=dtype, sigma=sigma)
     shape = OM.ModelShape(n_layers=n_layers, d_model=d, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, n_experts=E,
                           top_k=k, d_expert=F, d_shared=Fs, gated=bool(gated), vocab=V, d_selfcond=dsc,
-                          canvas=canvas, rope_theta=rope)
+                          canvas=canvas, rope_theta=rope, renorm_gates=bool(renorm))
     return model, W, shape
+
+
+def gpu_routes(L, model, rows, first=0):
+    """The experts every layer chose for rows first .. first+rows-1 of the last pass, [n_layers] of
+    [rows, top_k] (teacher forcing for the oracle)."""
+    d = model.desc
+    R = max(d.canvas, d.prefill_rows)
+    sel = model.buffer(L.DG_BUF_SEL_LAYERS, torch.int32, (d.n_layers, R, d.top_k)).cpu().numpy()
+    return [sel[l, first:first + rows].copy() for l in range(d.n_layers)]
+
+
+def check_routes(routes, infos, top_k, what):
+    """The GPU's expert sets equal the oracle's own choice on every row that is not a near-tie in that
+    layer (the oracle ran teacher-forced, so its router logits are the ones its inputs give)."""
+    for l, (sel, info) in enumerate(zip(routes, infos)):
+        tie = OM.router_margin(info["router_logits"], top_k) <= ROUTER_TIE
+        own = OM.topk_from_logits(info["router_logits"], top_k)
+        same = np.array([set(a) == set(b) for a, b in zip(sel, own)])
+        assert same[~tie].all(), f"{what}: layer {l} routes differ on rows {np.nonzero(~same & ~tie)[0]}"
+        print(f"{what}: layer {l} near-ties {int(tie.sum())}, of which routed differently {int((~same).sum())}")
 
 
 def ids_tensor(seed, n, V):
@@ -102,54 +137,52 @@ def keep_axis(a, keep, axis):
 def test_prefill_denoise_commit_match_oracle(libs, dtype, gated, rope):
     """Prefill (ragged chunks), denoise step 0, self-conditioned step 1, commit.
 
-    Tokens flagged as router near-ties in any layer (k-th vs (k+1)-th logit within
-    ROUTER_TIE in the oracle) are excluded from the continuous comparisons: rounding may
-    legitimately give them a different expert, which changes their activations
-    outright. Their count is reported.
+    Every row is compared: the oracle runs teacher-forced on the GPU's expert choice of every layer.
+    Separately, the GPU's choice must equal the oracle's own on every row that is not a near-tie
+    (k-th vs (k+1)-th router logit within ROUTER_TIE, where rounding may legitimately flip it).
     """
     L, configs, runtime = libs
     announce(f"model {dtype} gated={gated} rope={rope}")
     model, W, shape = build(libs, dtype=dtype, gated=gated, rope=rope)
     tol = tol_for(dtype)
-    n_prompt = 100  # two chunks of the 64-row canvas, the second ragged
+    n_prompt = 100  # two chunks of the 64-row canvas, the second ragged (two calls: same chunks as one)
     prompt = ids_tensor(1, n_prompt, shape.vocab)
-    model.prefill(prompt)
-    torch.cuda.synchronize()
-    assert model.length == n_prompt
     cache = OM.KVCache.empty(shape, 512)
-    pinfo = []
-    OM.encode(W, cache, prompt.cpu().numpy(), shape, infos=pinfo)
-    pflag = router_flags(pinfo, shape.top_k)
-    print(f"prompt router near-ties: {int(pflag.sum())} of {n_prompt}")
-    keep = ~pflag
+    for c0, c1 in ((0, 64), (64, n_prompt)):
+        model.prefill(prompt[c0:c1].contiguous())
+        torch.cuda.synchronize()
+        routes = gpu_routes(L, model, c1 - c0)
+        routes[-1] = None  # the last encoder layer computes K/V only
+        pinfo = []
+        OM.encode(W, cache, prompt[c0:c1].cpu().numpy(), shape, infos=pinfo, forced_sel=routes)
+        check_routes(routes[:-1], pinfo[:-1], shape.top_k, f"prefill rows {c0}..{c1}")
+    assert model.length == n_prompt
     gk, gv = gpu_kv(model, shape.n_layers, n_prompt)
     for l in range(shape.n_layers):
-        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n_prompt], keep, 1), tol, f"prefill K {l}")
-        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n_prompt], keep, 1), tol, f"prefill V {l}")
+        assert_close(gk[l], cache.k[l][:, :n_prompt], tol, f"prefill K {l}")
+        assert_close(gv[l], cache.v[l][:, :n_prompt], tol, f"prefill V {l}")
 
     # denoising step 0 (no self-conditioning)
     canvas = ids_tensor(2, shape.canvas, shape.vocab)
     logits = model.denoise_step(canvas, 0)
     torch.cuda.synchronize()
+    routes = gpu_routes(L, model, shape.canvas)
     ref_cache = cache.copy()
-    ref0, x_ref, infos = OM.denoise_step(W, ref_cache, canvas.cpu().numpy(), None, shape, return_info=True)
-    cflag = router_flags(infos, shape.top_k)
-    print(f"canvas router near-ties: {int(cflag.sum())} of {shape.canvas}")
-    assert_close(to_f64(logits)[~cflag], ref0[~cflag], tol, "step-0 logits")
+    ref0, x_ref, infos = OM.denoise_step(W, ref_cache, canvas.cpu().numpy(), None, shape, return_info=True,
+                                         forced_sel=routes)
+    check_routes(routes, infos, shape.top_k, "step 0")
+    assert_close(to_f64(logits), ref0, tol, "step-0 logits")
     assert model.length == n_prompt  # canvas K/V are scratch
     gk, gv = gpu_kv(model, shape.n_layers, n_prompt + shape.canvas)
-    assert_close(keep_axis(gk[-1][:, n_prompt:], ~cflag, 1),
-                 keep_axis(ref_cache.k[-1][:, n_prompt:n_prompt + shape.canvas], ~cflag, 1), tol, "canvas K")
+    assert_close(gk[-1][:, n_prompt:], ref_cache.k[-1][:, n_prompt:n_prompt + shape.canvas], tol, "canvas K")
     # router of the last layer, teacher-forced: the oracle's top-k of the GPU's router logits
     r_gpu = to_f64(model.buffer(L.DG_BUF_ROUTER_LOGITS, torch.float32, (shape.canvas, shape.n_experts)))
     sel_gpu = model.buffer(L.DG_BUF_SEL, torch.int32, (shape.canvas, shape.top_k)).cpu().numpy()
+    assert np.array_equal(sel_gpu, routes[-1])
     assert np.array_equal(OM.topk_from_logits(r_gpu, shape.top_k), sel_gpu)
     gate_gpu = to_f64(model.buffer(L.DG_BUF_GATE, torch.float32, (shape.canvas, shape.top_k)))
     p = OM.softmax(r_gpu)
     np.testing.assert_allclose(gate_gpu, np.take_along_axis(p, sel_gpu, axis=1), rtol=2e-5, atol=1e-7)
-    # against the oracle's own router, near-ties flagged
-    same = np.array([set(a) == set(b) for a, b in zip(sel_gpu, infos[-1]["sel"])])
-    assert same[~cflag].all(), f"router mismatch on {np.nonzero(~same & ~cflag)[0]}"
 
     # step 1 with self-conditioning from step 0, teacher-forced on the GPU's logits and row stats
     sched = L.make_sched(max_steps=8, seed=4)
@@ -161,13 +194,15 @@ def test_prefill_denoise_commit_match_oracle(libs, dtype, gated, rope):
     canvas1 = st.canvas.clone()
     logits1 = model.denoise_step(canvas1, 1, prev_logits, st.row_stats, T0, logits=torch.empty_like(logits))
     torch.cuda.synchronize()
+    routes1 = gpu_routes(L, model, shape.canvas)
     probs = OS.tempered_probs(to_f64(prev_logits), T0)
     sc_ref = OM.self_condition(W, probs)
     sc_gpu = to_f64(model.buffer(L.DG_BUF_SC, torch.float32, (shape.canvas, shape.d_model)))
-    assert_close(sc_gpu, sc_ref, tol * 2 if dtype == "bf16" else tol, "self-conditioning vector")
-    ref1, _, infos1 = OM.denoise_step(W, cache.copy(), canvas1.cpu().numpy(), sc_ref, shape, return_info=True)
-    f1 = router_flags(infos1, shape.top_k)
-    assert_close(to_f64(logits1)[~f1], ref1[~f1], tol, "step-1 logits")
+    assert_close(sc_gpu, sc_ref, tol, "self-conditioning vector")
+    ref1, _, infos1 = OM.denoise_step(W, cache.copy(), canvas1.cpu().numpy(), sc_ref, shape, return_info=True,
+                                      forced_sel=routes1)
+    check_routes(routes1, infos1, shape.top_k, "step 1")
+    assert_close(to_f64(logits1), ref1, tol, "step-1 logits")
     # in-place self-conditioning (prev logits aliasing the output) gives the same result
     alias = prev_logits.clone()
     model.denoise_step(canvas1, 1, alias, st.row_stats, T0, logits=alias)
@@ -179,13 +214,15 @@ def test_prefill_denoise_commit_match_oracle(libs, dtype, gated, rope):
     model.commit(block)
     torch.cuda.synchronize()
     assert model.length == n_prompt + shape.canvas
+    routes = gpu_routes(L, model, shape.canvas)
+    routes[-1] = None
     binfo = []
-    OM.encode(W, cache, block.cpu().numpy(), shape, infos=binfo)
-    keep = ~np.concatenate([pflag, router_flags(binfo, shape.top_k)])
+    OM.encode(W, cache, block.cpu().numpy(), shape, infos=binfo, forced_sel=routes)
+    check_routes(routes[:-1], binfo[:-1], shape.top_k, "commit")
     gk, gv = gpu_kv(model, shape.n_layers, model.length)
     for l in range(shape.n_layers):
-        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :model.length], keep, 1), tol, f"commit K {l}")
-        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :model.length], keep, 1), tol, f"commit V {l}")
+        assert_close(gk[l], cache.k[l][:, :model.length], tol, f"commit K {l}")
+        assert_close(gv[l], cache.v[l][:, :model.length], tol, f"commit V {l}")
     model.close()
 
 
@@ -211,9 +248,11 @@ def test_forward_layer_heavy_expert(libs, dtype, causal):
     x_ref = to_f64(x)
     model.forward_layer(0, x, 256, causal)
     torch.cuda.synchronize()
-    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, causal)
-    keep = OM.router_margin(info["router_logits"], shape.top_k) > ROUTER_TIE
-    assert_close(to_f64(x)[keep], y_ref[keep], tol_for(dtype), "layer output")
+    sel = model.buffer(L.DG_BUF_SEL, torch.int32, (256, shape.top_k)).cpu().numpy()
+    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, causal,
+                                   forced_sel=sel)
+    check_routes([sel], [info], shape.top_k, "heavy expert")
+    assert_close(to_f64(x), y_ref, tol_for(dtype), "layer output")
     counts = np.bincount(info["sel"][:, 0], minlength=2)
     assert counts.max() > 64
     gk, gv = gpu_kv(model, 1, past + 256)
@@ -318,39 +357,52 @@ def untile(flat, R, K, gr):
 def test_graph_replay_matches_direct_launches(libs):
     """The denoising step replayed from a captured HIP graph equals the directly issued step bit for
     bit, on every replay (with other GPU work and synchronisations between replays), with and without
-    self-conditioning, and again after a commit forces a re-capture."""
+    self-conditioning, at other temperatures, and after commits. The committed KV length and the
+    temperature are read on the device, so neither a commit nor a new temperature re-captures: two
+    graphs (with and without self-conditioning) serve the whole test."""
     L, configs, runtime = libs
     model, W, shape = build(libs, dtype="bf16", gated=1, n_layers=2)
+    direct, _, _ = build(libs, dtype="bf16", gated=1, n_layers=2)  # the same model, launches issued directly
+    L.dg_ctx_use_graphs(direct.ctx, False)
     announce("graph replay vs direct launches")
-    model.prefill(ids_tensor(1, 70, shape.vocab))
+    for m in (model, direct):
+        m.prefill(ids_tensor(1, 70, shape.vocab))
     canvas = ids_tensor(2, shape.canvas, shape.vocab)
     sched = L.make_sched(max_steps=8, seed=0)
     st = runtime.SamplerState(shape.canvas, shape.vocab)
-    T0 = L.dg_temperature(sched, 0)
+    l0_buf = torch.empty(shape.canvas, shape.vocab, dtype=torch.bfloat16, device="cuda")
+    l1_buf = torch.empty_like(l0_buf)
 
-    def direct():
-        L.dg_ctx_use_graphs(model.ctx, False)
-        l0 = model.denoise_step(canvas, 0).clone()
+    def run(m, T):
+        l0 = m.denoise_step(canvas, 0, logits=l0_buf).clone()
         st.init(sched, 0)
-        st.sample(l0, sched, 0, 0)
+        st.sample(l0_buf, sched, 0, 0)
         stats = st.row_stats.clone()
-        l1 = model.denoise_step(canvas, 1, l0, stats, T0).clone()
+        l1 = m.denoise_step(canvas, 1, l0_buf, st.row_stats, T, logits=l1_buf).clone()
         torch.cuda.synchronize()
         return l0, stats, l1
 
-    for _ in range(2):  # before and after a commit (new KV length: re-capture)
-        l0, stats, l1 = direct()
-        L.dg_ctx_use_graphs(model.ctx, True)
-        for rep in range(3):
-            g0 = model.denoise_step(canvas, 0).clone()
-            junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated work between replays
-            g1 = model.denoise_step(canvas, 1, l0, stats, T0).clone()
-            torch.cuda.synchronize()
-            assert torch.equal(g0, l0), f"replay {rep}: step without self-conditioning differs"
-            assert torch.equal(g1, l1), f"replay {rep}: self-conditioned step differs"
-            del junk
-        model.commit(ids_tensor(5, shape.canvas, shape.vocab))
+    base = L.dg_ctx_graph_captures(model.ctx)
+    for rnd in range(3):  # before and after commits (the length grows by the canvas each time)
+        for T in (L.dg_temperature(sched, 0), L.dg_temperature(sched, 5)):
+            l0, stats, l1 = run(direct, T)
+            for rep in range(3):
+                g0, gstats, g1 = run(model, T)
+                junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated work between replays
+                torch.cuda.synchronize()
+                assert torch.equal(g0, l0), f"round {rnd} T {T} replay {rep}: step without self-conditioning differs"
+                assert torch.equal(gstats, stats)
+                assert torch.equal(g1, l1), f"round {rnd} T {T} replay {rep}: self-conditioned step differs"
+                del junk
+        for m in (model, direct):
+            m.commit(ids_tensor(5 + rnd, shape.canvas, shape.vocab))
+        torch.cuda.synchronize()
+    # the first replays captured the two graphs; commits and temperatures re-used them
+    assert L.dg_ctx_graph_captures(model.ctx) == base + 2
+    assert L.dg_ctx_graph_captures(direct.ctx) == 0
+    assert model.length == direct.length == 70 + 3 * shape.canvas
     model.close()
+    direct.close()
 
 
 def test_denoise_step_is_deterministic(libs):
@@ -411,12 +463,14 @@ def test_forward_layer_token_tiled_experts(libs, gated):
     x_ref = to_f64(x)
     big.forward_layer(0, x, rows, True)
     torch.cuda.synchronize()
-    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, True)
+    routes = gpu_routes(L, big, rows)
+    y_ref, info = OM.layer_forward(W["layers"][0], x_ref, kv_ref.k[0], kv_ref.v[0], past, shape, True,
+                                   forced_sel=routes[0])
+    check_routes(routes, [info], shape.top_k, "1000-row chunk")
     counts = np.bincount(info["sel"].ravel(), minlength=shape.n_experts)
     print(f"tokens per expert: {counts.tolist()}")
     assert counts.max() > 256  # several tiles of one expert
-    keep = OM.router_margin(info["router_logits"], shape.top_k) > ROUTER_TIE
-    assert_close(to_f64(x)[keep], y_ref[keep], 2e-2, "layer output (token-tiled experts)")
+    assert_close(to_f64(x), y_ref, 2e-2, "layer output (token-tiled experts)")
     sel_gpu = big.buffer(L.DG_BUF_SEL, torch.int32, (64, shape.top_k))  # the first canvas-sized rows
     r_gpu = to_f64(big.buffer(L.DG_BUF_ROUTER_LOGITS, torch.float32, (64, shape.n_experts)))
     assert np.array_equal(OM.topk_from_logits(r_gpu, shape.top_k), sel_gpu.cpu().numpy())
@@ -437,35 +491,42 @@ def test_prefill_in_large_chunks_matches_oracle(libs, dtype):
                           d_expert=128, d_shared=256, gated=True, vocab=512, d_selfcond=128, canvas=64)
     n = 2500
     prompt = ids_tensor(1, n, shape.vocab)
-    model.prefill(prompt)
-    torch.cuda.synchronize()
-    assert model.length == n
     cache = OM.KVCache.empty(shape, 2560 + 64)
-    infos = []
-    OM.encode(W, cache, prompt.cpu().numpy(), shape, infos=infos)
-    keep = ~router_flags(infos, shape.top_k)
-    print(f"prompt rows kept (no router near-tie): {int(keep.sum())} of {n}")
+    # one chunk per call (the chunks a single call of 2500 would make), so each chunk's routing can
+    # be read back and the oracle teacher-forced on it
+    for c0, c1 in ((0, 1024), (1024, 2048), (2048, n)):
+        model.prefill(prompt[c0:c1].contiguous())
+        torch.cuda.synchronize()
+        routes = gpu_routes(L, model, c1 - c0)
+        routes[-1] = None
+        infos = []
+        OM.encode(W, cache, prompt[c0:c1].cpu().numpy(), shape, infos=infos, forced_sel=routes)
+        check_routes(routes[:-1], infos[:-1], shape.top_k, f"prefill rows {c0}..{c1}")
+    assert model.length == n
     gk, gv = gpu_kv(model, shape.n_layers, n)
     tol = tol_for(dtype)
     for l in range(shape.n_layers):
-        assert_close(keep_axis(gk[l], keep, 1), keep_axis(cache.k[l][:, :n], keep, 1), tol, f"prefill K {l}")
-        assert_close(keep_axis(gv[l], keep, 1), keep_axis(cache.v[l][:, :n], keep, 1), tol, f"prefill V {l}")
+        assert_close(gk[l], cache.k[l][:, :n], tol, f"prefill K {l}")
+        assert_close(gv[l], cache.v[l][:, :n], tol, f"prefill V {l}")
     canvas = ids_tensor(2, shape.canvas, shape.vocab)
     logits = model.denoise_step(canvas, 0)
     torch.cuda.synchronize()
-    ref, _, cinfo = OM.denoise_step(W, cache.copy(), canvas.cpu().numpy(), None, shape, return_info=True)
-    cflag = router_flags(cinfo, shape.top_k)
-    assert_close(to_f64(logits)[~cflag], ref[~cflag], tol, "step logits after a chunked prefill")
+    routes = gpu_routes(L, model, shape.canvas)
+    ref, _, cinfo = OM.denoise_step(W, cache.copy(), canvas.cpu().numpy(), None, shape, return_info=True,
+                                    forced_sel=routes)
+    check_routes(routes, cinfo, shape.top_k, "step after a chunked prefill")
+    assert_close(to_f64(logits), ref, tol, "step logits after a chunked prefill")
     model.close()
 
 
 @pytest.mark.parametrize("hd", [64, 128])
 def test_canvas_reaching_the_cache_end(libs, hd):
-    """Canvas keys that end exactly at a capacity of 7 V blocks (224 = 3.5 stages of 64 keys).
+    """Canvas keys that end exactly at a capacity of 7 V blocks (224 keys = 1.75 stages of 128).
 
-    The attention kernel copies whole stages of V blocks; the last stage here covers blocks past
-    the capacity, which it must replace by the last block that holds keys (weighted by zero)
-    rather than read past the cache.
+    The attention kernel copies whole stages of V blocks, so the last stage of the key range reads
+    32 positions past the capacity: into the next KV head's blocks, or for the last head into the
+    zeroed tail that dg_kv_bytes adds after the cache. Those keys are masked (weight 0); the logits
+    must still match the oracle.
     """
     L, configs, runtime = libs
     announce(f"canvas at the cache end, head_dim {hd}")
@@ -477,12 +538,13 @@ def test_canvas_reaching_the_cache_end(libs, hd):
     canvas = ids_tensor(6, shape.canvas, shape.vocab)
     logits = model.denoise_step(canvas, 0)
     torch.cuda.synchronize()
+    routes = gpu_routes(L, model, shape.canvas)
     cache = OM.KVCache.empty(shape, 224)
-    OM.encode(W, cache, prompt.cpu().numpy(), shape)
-    ref, _, infos = OM.denoise_step(W, cache, canvas.cpu().numpy(), None, shape, return_info=True)
-    cflag = router_flags(infos, shape.top_k)
-    print(f"canvas router near-ties: {int(cflag.sum())} of {shape.canvas}")
+    OM.encode(W, cache, prompt.cpu().numpy(), shape)  # one layer: its K/V do not depend on routing
+    ref, _, infos = OM.denoise_step(W, cache, canvas.cpu().numpy(), None, shape, return_info=True,
+                                    forced_sel=routes)
+    check_routes(routes, infos, shape.top_k, "cache end")
     got = to_f64(logits)
     assert np.isfinite(got).all()
-    assert_close(got[~cflag], ref[~cflag], tol, "logits at the cache end")
+    assert_close(got, ref, tol, "logits at the cache end")
     model.close()
