@@ -66,6 +66,8 @@ _SIGS = {
     "dg_init_canvas": (ctypes.c_int, [ctypes.POINTER(dg_sched), _I32, _I32, _I32, _P, _P, _P]),
     "dg_sample_canvas": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(dg_sched), _I32, _I32,
                                         _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_sample_canvas_static": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(dg_sched), _I32, _I32,
+                                               _P, _P, _P, _P, _P, _P, _P]),
     "dg_synth_normal": (ctypes.c_int, [_U64, _U64, _I64, _F32, _I32, _P, _P]),
     "dg_synth_uniform_ids": (ctypes.c_int, [_U64, _U64, _I64, _I32, _P, _P]),
     "dg_synth_planted_logits": (ctypes.c_int, [_U64, _I32, _I32, _I32, _F32, _F32, _P, _P]),
@@ -187,6 +189,13 @@ def dg_sample_canvas(d_logits, dtype, rows, vocab, sched, step, block, d_canvas,
         ptr(d_logits), dtype, rows, vocab, ctypes.byref(sched), step, block, ptr(d_canvas), ptr(d_pred),
         ptr(d_accept), ptr(d_entropy), ptr(d_row_stats), ptr(d_stop), ptr(d_workspace), ws_bytes,
         stream_handle(stream)))
+
+
+def dg_sample_canvas_static(d_logits, dtype, rows, vocab, sched, step, block, d_canvas, d_pred, d_accept, d_entropy,
+                            d_row_stats, d_stop, stream=None):
+    return _check("dg_sample_canvas_static", lib.dg_sample_canvas_static(
+        ptr(d_logits), dtype, rows, vocab, ctypes.byref(sched), step, block, ptr(d_canvas), ptr(d_pred),
+        ptr(d_accept), ptr(d_entropy), ptr(d_row_stats), ptr(d_stop), stream_handle(stream)))
 
 
 def dg_synth_normal(seed, tid, n, sigma, dtype, d_out, stream=None):

@@ -33,6 +33,8 @@ int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int
 int launch_synth_ids(uint64_t seed, uint64_t tid, int64_t n, int vocab, int32_t* out, hipStream_t s);
 int launch_synth_logits(uint64_t seed, int step, int rows, int vocab, float sigma, float peak, void* out,
                         hipStream_t s);
+size_t static_scratch_bytes();
+int static_scratch(void** out);
 
 float temperature(const dg_sched& s, int step) {
   const double t0 = s.t_start, t1 = s.t_end;
@@ -51,6 +53,20 @@ int check_sched(const dg_sched* s, int step) {
   if ((s->mode & ~(DG_SCHED_STOP_EITHER | DG_SCHED_ACCEPT_GROUP | DG_SCHED_SAMPLE)) != 0)
     return fail(DG_ERR_INVALID, "unknown sched mode flag");
   if (step < 0 || step >= s->max_steps) return fail(DG_ERR_INVALID, "step outside [0, max_steps)");
+  return DG_OK;
+}
+
+int check_sample_args(const void* d_logits, int32_t dtype, int32_t rows, int32_t vocab, const dg_sched* sched,
+                             int32_t step, int32_t block, const int32_t* d_canvas, const int32_t* d_pred,
+                             const dg_stop_state* d_stop) {
+  if (int rc = check_sched(sched, step)) return rc;
+  if (dtype != DG_BF16 && dtype != DG_F32) return fail(DG_ERR_INVALID, "dtype must be DG_BF16 or DG_F32");
+  if (rows < 1 || rows > 65535) return fail(DG_ERR_SHAPE, "rows must be in [1, 65535]");
+  if (vocab < 1) return fail(DG_ERR_SHAPE, "vocab must be >= 1");
+  if (block < 0) return fail(DG_ERR_INVALID, "block must be >= 0");
+  if (!d_logits || !d_canvas || !d_pred || !d_stop)
+    return fail(DG_ERR_INVALID, "d_logits, d_canvas, d_pred and d_stop are required");
+  if (reinterpret_cast<uintptr_t>(d_logits) % 16 != 0) return fail(DG_ERR_INVALID, "d_logits must be 16-byte aligned");
   return DG_OK;
 }
 
@@ -88,20 +104,29 @@ int dg_sample_canvas(const void* d_logits, int32_t dtype, int32_t rows, int32_t 
                      int32_t step, int32_t block, int32_t* d_canvas, int32_t* d_pred, uint8_t* d_accept,
                      float* d_entropy, float* d_row_stats, dg_stop_state* d_stop, void* d_workspace,
                      size_t ws_bytes, void* stream) {
-  if (int rc = check_sched(sched, step)) return rc;
-  if (dtype != DG_BF16 && dtype != DG_F32) return fail(DG_ERR_INVALID, "dtype must be DG_BF16 or DG_F32");
-  if (rows < 1 || rows > 65535) return fail(DG_ERR_SHAPE, "rows must be in [1, 65535]");
-  if (vocab < 1) return fail(DG_ERR_SHAPE, "vocab must be >= 1");
-  if (block < 0) return fail(DG_ERR_INVALID, "block must be >= 0");
-  if (!d_logits || !d_canvas || !d_pred || !d_stop || !d_workspace)
-    return fail(DG_ERR_INVALID, "d_logits, d_canvas, d_pred, d_stop and d_workspace are required");
-  if (reinterpret_cast<uintptr_t>(d_logits) % 16 != 0) return fail(DG_ERR_INVALID, "d_logits must be 16-byte aligned");
+  if (int rc = check_sample_args(d_logits, dtype, rows, vocab, sched, step, block, d_canvas, d_pred, d_stop))
+    return rc;
+  if (!d_workspace) return fail(DG_ERR_INVALID, "d_workspace is required");
   if (reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
     return fail(DG_ERR_INVALID, "d_workspace must be 256-byte aligned");
   if (ws_bytes < sample_workspace_bytes(rows, vocab)) return fail(DG_ERR_CAPACITY, "sampler workspace too small");
   const float T = temperature(*sched, step);
   return launch_sample(d_logits, dtype, rows, vocab, T, *sched, step, block, d_canvas, d_pred, d_accept, d_entropy,
                        d_row_stats, d_stop, d_workspace, as_stream(stream));
+}
+
+int dg_sample_canvas_static(const void* d_logits, int32_t dtype, int32_t rows, int32_t vocab, const dg_sched* sched,
+                            int32_t step, int32_t block, int32_t* d_canvas, int32_t* d_pred, uint8_t* d_accept,
+                            float* d_entropy, float* d_row_stats, dg_stop_state* d_stop, void* stream) {
+  if (int rc = check_sample_args(d_logits, dtype, rows, vocab, sched, step, block, d_canvas, d_pred, d_stop))
+    return rc;
+  if (sample_workspace_bytes(rows, vocab) > static_scratch_bytes())
+    return fail(DG_ERR_CAPACITY, "rows x vocab need more than the 1 MiB static sampler scratch (use dg_sample_canvas)");
+  void* ws = nullptr;
+  if (int rc = static_scratch(&ws)) return rc;
+  const float T = temperature(*sched, step);
+  return launch_sample(d_logits, dtype, rows, vocab, T, *sched, step, block, d_canvas, d_pred, d_accept, d_entropy,
+                       d_row_stats, d_stop, ws, as_stream(stream));
 }
 
 int dg_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int32_t dtype, void* d_out, void* stream) {

@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dg_common.h"
 #include "philox.h"
@@ -557,6 +558,37 @@ int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canv
   ProfScope ps("init_canvas", stream);
   init_canvas_kernel<<<grid, threads, 0, stream>>>(seed, block, n, static_cast<uint32_t>(vocab), canvas, stop);
   DG_LAUNCH_CHECK("init_canvas_kernel");
+  return DG_OK;
+}
+
+// ------------------------------------------------ static scratch (no allocation)
+// The partial records of dg_sample_canvas_static live here instead of in a caller workspace. In host
+// code `scratch` names a host-side stand-in, never the device array: the device address is taken
+// once per device with hipGetSymbolAddress (that device current) and used from then on. Every call on
+// one device shares that device's array; the partial kernel writes every record the finalize kernel
+// reads, so nothing in it has to start at zero, but calls that overlap in time on one device race.
+constexpr size_t kStaticScratchBytes = size_t{1} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+// device address of this device's scratch (looked up on the first call per device)
+int static_scratch(void** out) {
+  int dev = 0;
+  DG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    DG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(DG_ERR_HIP, "hipGetSymbolAddress returned no address for the sampler scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return DG_OK;
 }
 

@@ -190,6 +190,22 @@ int dg_sample_canvas(const void* d_logits, int32_t dtype, int32_t rows, int32_t 
                      float* d_row_stats, dg_stop_state* d_stop,
                      void* d_workspace, size_t ws_bytes, void* stream);
 
+/* dg_sample_canvas without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the per-chunk partial records live in a
+ * static device array of the library, 1 MiB per device (held until the process
+ * ends), whose address is looked up once per device on the first call there.
+ * Same arguments, results and limits as dg_sample_canvas otherwise; calls whose
+ * dg_sample_workspace_size(rows, vocab) exceeds 1 MiB fail with
+ * DG_ERR_CAPACITY before anything is enqueued (a canvas of up to 256 rows needs
+ * at most 96 KiB at any vocabulary). Nothing is
+ * allocated; every call on one device shares its array, so calls that overlap
+ * in time on one device race (serialise them on one stream). */
+int dg_sample_canvas_static(const void* d_logits, int32_t dtype, int32_t rows, int32_t vocab,
+                            const dg_sched* sched, int32_t step, int32_t block, int32_t* d_canvas,
+                            int32_t* d_pred, uint8_t* d_accept, float* d_entropy, float* d_row_stats,
+                            dg_stop_state* d_stop, void* stream);
+
 /* ------------------------------------------------- synthetic inputs */
 /* Seeded synthetic data (no method arithmetic): value i of stream (seed, tid)
  * is the Irwin-Hall sum of the four 16-bit fields of a SplitMix64-based hash,
