@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the canvas-denoising hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full|sampler|blockar|prefill|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload full|sampler|blockar|prefill|tiny|stream|copy]
                     [--no-cpu-baseline]
                     [--sampler-mode M] [--experts bf16|fp8] [--prefill-rows R]
 
@@ -29,11 +30,18 @@ resident in HBM:
 * ``prefill``: encoder mode at scale, the 32768-token prompt of the
   block-autoregressive workload prefilled into an empty cache in chunks of
   ``--prefill-rows`` rows.
+* ``tiny``: the small fp32 configuration (1 layer, d_model 256, 16 experts
+  top-2, vocab 4096, 64 prompt tokens, 8-step canvases over the prompt, one
+  canvas plus its commit timed on its own); a correctness configuration,
+  bound by launches, not by HBM.
+* ``stream``: a plain streaming read of 4 GiB (libdg's calibration kernel),
+  the ceiling a bandwidth-bound kernel can reach on the box.
 * ``copy``: a plain 1 GiB device copy, the calibration run for the HBM
   byte counters of the profiles.
 
 The roofline entry is for the dominant kernel, timed live with HIP events
-on its own stream through libdg's profiling hooks. The cpu_baseline entry
+(marker packets before and after each launch, on the kernel's own stream)
+through libdg's profiling hooks. The cpu_baseline entry
 times the CPU oracle (tests-only code) on a bounded sample of the same
 workload on the host cores.
 """
@@ -115,8 +123,9 @@ def bench_sampler(args):
     L.dg_profile_enable(False)
     stop = st.stop_state()
     part = live["sample_partial"]
+    part_us = part["avg_us"]
     bytes_per_launch = rows * V * 2
-    achieved = bytes_per_launch / (part["avg_us"] * 1e-6) / 1e9
+    achieved = bytes_per_launch / (part_us * 1e-6) / 1e9
     src = kernel_source_hash(["canvas_denoising_amd/csrc/sampler.hip"])
     steps_per_s = args.steps / dt
     out = {
@@ -141,7 +150,9 @@ def bench_sampler(args):
         "roofline": {"kernel": "sample_partial", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic("sample_partial", src),
-                     "algorithmic_bytes_per_launch": bytes_per_launch, "avg_us": part["avg_us"]},
+                     "algorithmic_bytes_per_launch": bytes_per_launch, "avg_us": part_us,
+                     "timed_with": "HIP events (marker packets) around each launch of the partial kernel in the "
+                                   "timed region"},
     }
     del bufs
     torch.cuda.empty_cache()
@@ -193,7 +204,7 @@ def bench_full(args):
     d.prefill_rows = args.prefill_rows
     C, V, S = d.canvas, d.vocab, w.max_steps
     n_blocks = (args.steps + S - 1) // S + 1
-    capacity = w.prompt + (n_blocks + 1) * C
+    capacity = w.prompt + (n_blocks + 2) * C  # + the separately timed committed canvas
     log(f"[bench] model {d.n_layers} layers, weights {L.dg_weights_bytes(d) / 1e9:.1f} GB, KV capacity {capacity}")
     model = Model(d, capacity, seed=0)
     fp8 = args.experts == "fp8"
@@ -238,6 +249,22 @@ def bench_full(args):
                 st.init(sched, block)
         return block
 
+    def one_canvas(block):
+        """One canvas from its init to its stop (or S steps), then its commit: the pages' unit of output."""
+        s = 0
+        st.init(sched, block)
+        while True:
+            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
+            model.denoise_step(st.canvas, s, *prev, logits=logits)
+            st.sample(logits, sched, s, block)
+            stop = st.stop.cpu()
+            s += 1
+            if int(stop[2]) or s == S:
+                break
+        block_ids.copy_(st.pred)
+        model.commit(block_ids)
+        return s, int(stop[2])
+
     log(f"[bench] warmup {args.warmup}")
     blk = run(args.warmup, 0)
     torch.cuda.synchronize()
@@ -250,24 +277,31 @@ def bench_full(args):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     commits, stops = counters["commits"], counters["stopped"]
-    # timed region 2: the same loop with launches issued directly and HIP events around every
-    # launch of the roofline kernel (on its stream): its live per-launch duration
-    n_ev = min(args.steps, 48)
-    L.dg_profile_enable(True, 64 * (n_ev + 2))
-    L.dg_profile_only(gu_name)
+    # timed region 4 (committed output): one whole canvas, init to stop or S steps, plus its commit
+    blk += 1
+    log(f"[bench] timing one committed canvas")
+    torch.cuda.synchronize()
+    t4 = time.perf_counter()
+    steps4, stopped4 = one_canvas(blk)
+    torch.cuda.synchronize()
+    dt4 = time.perf_counter() - t4
+    blk += 1
+    # timed region 2: the same loop with launches issued directly and HIP events (marker packets) around
+    # every launch, on each kernel's stream: the per-kernel table and the roofline kernel's live
+    # per-launch duration. (Recording every launch site keeps the launches as spread as in a replayed
+    # step; rocprofv3 measured the routed-expert kernel 4% slower when only its own launches carried
+    # events.)
+    n_ev = min(args.steps, 16)
+    L.dg_profile_only(None)
+    L.dg_profile_enable(True, 2000 * (n_ev + 2))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     blk = run(n_ev, blk)
     torch.cuda.synchronize()
     dt_ev = time.perf_counter() - t1
-    live = L.dg_profile_report()
-    # per-kernel table from a third pass with every launch site recorded
-    n_prof = min(args.steps, 8)
-    L.dg_profile_only(None)
-    L.dg_profile_enable(True, 2000 * (n_prof + 2))
-    run(n_prof, blk)
-    torch.cuda.synchronize()
     prof = L.dg_profile_report()
+    n_prof = n_ev
+    live = prof
     L.dg_profile_enable(False)
     steps_per_s = args.steps / dt
     # algorithmic bytes of the routed-expert kernels: every expert's weights, once per launch (FP8:
@@ -280,7 +314,8 @@ def bench_full(args):
         gu_bytes = d.n_experts * 2 * d.d_expert * d.d_model * es
         dn_bytes = d.n_experts * d.d_model * d.d_expert * es
     gu = live[gu_name]
-    achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
+    gu_us = gu["avg_us"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     src = kernel_source_hash(["canvas_denoising_amd/csrc/moe.hip"])
     metric = "canvas denoise steps/s (256-token canvas)"
     if fp8:
@@ -311,8 +346,11 @@ def bench_full(args):
                                "block commit after each canvas; random-init weights",
                    "expert_weights": "fp8 e4m3, per-row float32 scales" if fp8 else "bf16",
                    "canvas_tokens_per_s": steps_per_s * C,
-                   "committed_tokens_per_s": commits * C / dt,
-                   "commits": commits, "stops": stops,
+                   "committed_tokens_per_s": C / dt4,
+                   "committed_canvas": {"steps": steps4, "stopped": stopped4, "seconds": dt4,
+                                        "note": "one canvas from init to its stop (or the step budget) plus "
+                                                "its commit, timed on its own"},
+                   "commits_in_timed_steps": commits, "stops": stops,
                    "prefill_tokens_per_s": w.prompt / prefill_s, "prefill_rows": d.prefill_rows,
                    "step_roofline_ms": step_roof_s * 1e3,
                    "step_roofline_frac": step_roof_s / (dt / args.steps),
@@ -321,9 +359,9 @@ def bench_full(args):
         "roofline": {"kernel": gu_name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": load_traffic(gu_name, src),
-                     "algorithmic_bytes_per_launch": gu_bytes, "avg_us": gu["avg_us"], "launches": gu["count"],
-                     "timed_with": f"HIP events around each launch over {n_ev} steps issued directly "
-                                   f"({dt_ev * 1e3 / n_ev:.2f} ms/step)"},
+                     "algorithmic_bytes_per_launch": gu_bytes, "avg_us": gu_us, "launches": gu["count"],
+                     "timed_with": f"HIP events (marker packets) around every launch over {n_ev} steps issued "
+                                   f"directly ({dt_ev * 1e3 / n_ev:.2f} ms/step)"},
     }
     model.close()
     del model
@@ -502,6 +540,161 @@ def bench_prefill(args):
     }
 
 
+def bench_tiny(args):
+    """The tiny fp32 configuration: 1 layer, d_model 256, 4 heads x 64, 16 experts top-2 (plain GeLU FFN 512)
+    + shared 512, vocab 4096, self-conditioning 256; 64 prompt tokens prefilled; canvases of 8 steps
+    (temperature 0.8 -> 0.4), each committed before the next. A step = self-conditioning + the layer + LM
+    head + sampler + the 16-byte stop read-back."""
+    import torch
+    from canvas_denoising_amd import _lib as L
+    from canvas_denoising_amd import configs
+    from canvas_denoising_amd.runtime import Model, SamplerState
+
+    w = configs.tiny_f32()
+    d = w.desc
+    C, V, S = d.canvas, d.vocab, w.max_steps
+    model = Model(d, w.prompt + C, seed=0)
+    prompt = torch.empty(w.prompt, dtype=torch.int32, device="cuda")
+    L.dg_synth_uniform_ids(1, 10, w.prompt, V, prompt)
+    model.prefill(prompt)
+    sched = L.make_sched(max_steps=S, seed=0)
+    st = SamplerState(C, V)
+    logits = model.logits
+    block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
+    state = {"s": 0, "block": 0}
+
+    def run(n):
+        """n steps of canvases over the 64-token prompt (a canvas restarts after its stop or S steps)."""
+        for _ in range(n):
+            s = state["s"]
+            if s == 0:
+                st.init(sched, state["block"])
+            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
+            model.denoise_step(st.canvas, s, *prev, logits=logits)
+            st.sample(logits, sched, s, state["block"])
+            stop = st.stop.cpu()
+            state["s"] = s + 1
+            if int(stop[2]) or state["s"] == S:
+                state.update(s=0, block=state["block"] + 1)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # one canvas from init to its end plus its commit, timed on its own (the context then grows by it)
+    state["s"] = 0
+    t1 = time.perf_counter()
+    run(S)
+    block_ids.copy_(st.pred)
+    model.commit(block_ids)
+    torch.cuda.synchronize()
+    dt_canvas = time.perf_counter() - t1
+    L.dg_kv_set_length(model.ctx, w.prompt)
+    # per-kernel table (events) over one more canvas, issued directly
+    L.dg_profile_enable(True, 200 * S)
+    run(S)
+    torch.cuda.synchronize()
+    prof = L.dg_profile_report()
+    L.dg_profile_enable(False)
+    model.close()
+    steps_per_s = args.steps / dt
+    lm = prof.get("lm_head", {"avg_us": float("nan")})
+    lm_flops = 2 * C * d.d_model * V
+    out = {
+        "metric": "canvas denoise steps/s (tiny fp32 configuration)",
+        "value": steps_per_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": dt * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"tiny fp32: 1 layer d_model {d.d_model}, 4x64 heads over {w.prompt} prompt KV + "
+                               f"the canvas, 16 experts top-2 (plain GeLU {d.d_expert}) + shared {d.d_shared}, "
+                               f"vocab {V}, self-conditioning {d.d_selfcond}, {S}-step canvases over the prompt; "
+                               "committed tokens/s from one canvas plus its commit; random-init weights",
+                   "canvas_tokens_per_s": steps_per_s * C,
+                   "committed_tokens_per_s": C / dt_canvas,
+                   "kernels_us": {k: v["avg_us"] for k, v in sorted(prof.items())}},
+        "roofline": {"kernel": "lm_head", "bound": "mfma", "achieved": lm_flops / (lm["avg_us"] * 1e-6) / 1e12,
+                     "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": lm_flops / (lm["avg_us"] * 1e-6) / 1e12 / 157.3, "traffic": None,
+                     "algorithmic_flops_per_launch": lm_flops, "avg_us": lm["avg_us"],
+                     "note": "fp32 MFMA peak; the configuration is launch-bound (about 1.7 GFLOP a step)"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_tiny(d, w.prompt, S)
+    return out
+
+
+def cpu_baseline_tiny(d, prompt, S):
+    """The oracle's whole step of the tiny configuration (all 256 rows): self-conditioning, the layer, LM head
+    and sampler, with the seeded synthetic weights."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import synthetic
+    from canvas_denoising_amd import configs
+    from oracle import model as OM
+    from oracle.sampler import Schedule, sample_step, tempered_probs
+
+    shape = OM.ModelShape(n_layers=d.n_layers, d_model=d.d_model, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                          head_dim=d.head_dim, n_experts=d.n_experts, top_k=d.top_k, d_expert=d.d_expert,
+                          d_shared=d.d_shared, gated=bool(d.gated), vocab=d.vocab, d_selfcond=d.d_selfcond,
+                          canvas=d.canvas)
+    W = synthetic.SyntheticWeights(configs.shape_dict(d), seed=0, dtype="f32", sigma=0.02)
+    cache = OM.KVCache.empty(shape, prompt + d.canvas)
+    OM.encode(W, cache, synthetic.uniform_ids(1, 10, prompt, d.vocab), shape)
+    canvas = synthetic.uniform_ids(2, 10, d.canvas, d.vocab)
+    sched = Schedule(max_steps=S, seed=0)
+    prev, n, t = None, 0, 0.0
+    while n < S and t < 15.0:
+        t0 = time.perf_counter()
+        sc = None if prev is None else OM.self_condition(W, tempered_probs(prev, 0.8))
+        lg = OM.denoise_step(W, cache.copy(), canvas, sc, shape)
+        sample_step(lg, n, 0, sched, None, 0)
+        t += time.perf_counter() - t0
+        prev, n = lg, n + 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": n / t, "unit": "steps/s", "cores": min(cores, blas), "kind": "oracle",
+            "sample": f"oracle (NumPy fp64) whole steps of the tiny configuration, all {d.canvas} rows: "
+                      f"self-conditioning, the layer, LM head and sampler; {n} steps in {t:.1f} s; host cores "
+                      f"{cores}, BLAS threads {blas}"}
+
+
+def bench_stream(args):
+    """Calibration: libdg's plain streaming-read kernel over 4 GiB (nontemporal 16-byte loads, grid-stride),
+    at several grid sizes; the value is the best read bandwidth. A ceiling for the bandwidth-bound kernels."""
+    import torch
+    from canvas_denoising_amd import _lib as L
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    L.dg_synth_uniform_ids(7, 11, n // 4, 1 << 30, src)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    res = {}
+    for blocks in (1024, 2048, 4096, 8192, 16384):
+        for _ in range(args.warmup):
+            L.dg_stream_read(src, n, sink, blocks)
+        torch.cuda.synchronize()
+        L.dg_profile_enable(True, args.steps + 4)
+        for _ in range(args.steps):
+            L.dg_stream_read(src, n, sink, blocks)
+        prof = L.dg_profile_report()["stream_read"]
+        L.dg_profile_enable(False)
+        res[blocks] = n / (prof["avg_us"] * 1e-6) / 1e9
+    best = max(res, key=res.get)
+    return {"metric": "streaming read bandwidth (calibration kernel, 4 GiB)", "value": res[best], "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": n / res[best] / 1e6,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "plain streaming read of 4 GiB, nontemporal 16-byte loads, grid-stride",
+                       "gbs_by_workgroups": res, "best_workgroups": best},
+            "roofline": {"kernel": "stream_read", "bound": "hbm", "achieved": res[best], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": res[best] / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": n}}
+
+
 def bench_copy(args):
     """Plain device-to-device copy of a known size: the calibration run for HBM byte counters
     (FETCH_SIZE / WRITE_SIZE per launch divided by the bytes copied)."""
@@ -525,7 +718,7 @@ def bench_copy(args):
 
 
 WORKLOADS = {"sampler": bench_sampler, "full": bench_full, "blockar": bench_blockar, "prefill": bench_prefill,
-             "copy": bench_copy}
+             "tiny": bench_tiny, "stream": bench_stream, "copy": bench_copy}
 
 
 def main():
@@ -550,9 +743,9 @@ def main():
         print("bench.py runs on exactly one GPU: libdg has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
-        args.steps = {"sampler": 480, "copy": 20, "prefill": 3}.get(args.workload, 96)
+        args.steps = {"sampler": 480, "copy": 20, "prefill": 3, "tiny": 400, "stream": 10}.get(args.workload, 96)
     if args.warmup is None:
-        args.warmup = {"sampler": 48, "copy": 2, "prefill": 1}.get(args.workload, 4)
+        args.warmup = {"sampler": 48, "copy": 2, "prefill": 1, "tiny": 16, "stream": 2}.get(args.workload, 4)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (libdg runs only on MI355X).", file=sys.stderr)

@@ -70,6 +70,7 @@ _SIGS = {
                                                _P, _P, _P, _P, _P, _P, _P]),
     "dg_synth_normal": (ctypes.c_int, [_U64, _U64, _I64, _F32, _I32, _P, _P]),
     "dg_synth_uniform_ids": (ctypes.c_int, [_U64, _U64, _I64, _I32, _P, _P]),
+    "dg_stream_read": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
     "dg_synth_planted_logits": (ctypes.c_int, [_U64, _I32, _I32, _I32, _F32, _F32, _P, _P]),
     "dg_synth_fill_weights": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _U64, _F32, _P, _P]),
     "dg_weights_bytes": (_SZ, [ctypes.POINTER(dg_model_desc)]),
@@ -206,6 +207,10 @@ def dg_synth_normal(seed, tid, n, sigma, dtype, d_out, stream=None):
 def dg_synth_uniform_ids(seed, tid, n, vocab, d_out, stream=None):
     return _check("dg_synth_uniform_ids", lib.dg_synth_uniform_ids(seed, tid, n, vocab, ptr(d_out),
                                                                    stream_handle(stream)))
+
+
+def dg_stream_read(d_src, nbytes, d_sink, blocks, stream=None):
+    return _check("dg_stream_read", lib.dg_stream_read(ptr(d_src), nbytes, ptr(d_sink), blocks, stream_handle(stream)))
 
 
 def dg_synth_planted_logits(seed, step, rows, vocab, sigma, peak, d_out, stream=None):

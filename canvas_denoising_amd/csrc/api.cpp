@@ -33,6 +33,7 @@ int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int
 int launch_synth_ids(uint64_t seed, uint64_t tid, int64_t n, int vocab, int32_t* out, hipStream_t s);
 int launch_synth_logits(uint64_t seed, int step, int rows, int vocab, float sigma, float peak, void* out,
                         hipStream_t s);
+int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 size_t static_scratch_bytes();
 int static_scratch(void** out);
 
@@ -141,6 +142,14 @@ int dg_synth_uniform_ids(uint64_t seed, uint64_t tid, int64_t n, int32_t vocab, 
   if (n < 0 || vocab < 1) return fail(DG_ERR_SHAPE, "n must be >= 0 and vocab >= 1");
   if (n > 0 && d_out == nullptr) return fail(DG_ERR_INVALID, "d_out is NULL");
   return launch_synth_ids(seed, tid, n, vocab, d_out, as_stream(stream));
+}
+
+int dg_stream_read(const void* d_src, int64_t bytes, uint32_t* d_sink, int32_t blocks, void* stream) {
+  if (!d_src || !d_sink) return fail(DG_ERR_INVALID, "d_src and d_sink are required");
+  if (bytes < 16 || bytes % 16 != 0) return fail(DG_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(d_src) % 16 != 0) return fail(DG_ERR_INVALID, "d_src must be 16-byte aligned");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(DG_ERR_INVALID, "blocks must be in [1, 2^20]");
+  return launch_stream_read(d_src, bytes, d_sink, blocks, as_stream(stream));
 }
 
 int dg_synth_planted_logits(uint64_t seed, int32_t step, int32_t rows, int32_t vocab, float sigma, float peak,

@@ -412,10 +412,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int hd) {
   }
 }
 
-// fp32: one thread per (query row, head)
-__global__ void attn_f32_kernel(AttnArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.M * a.Hq) return;
+// fp32: one wave per (query row, head). Keys go 64 at a time, one per lane: the lane's score (its key
+// row against the query, which the wave keeps in LDS), the chunk's maximum and sum by wave reductions
+// into a running (max, sum) with the usual rescale. The chunk's probabilities go to LDS in the V cache's
+// slot order, and each lane then accumulates head dims lane and lane + 64 over the chunk's two V blocks,
+// reading the 32 contiguous slots of its dim's row in each block (kvlayout.h).
+constexpr int kF32Waves = 4;
+__global__ __launch_bounds__(64 * kF32Waves) void attn_f32_kernel(AttnArgs a) {
+  __shared__ float qs[kF32Waves][128];
+  __shared__ __align__(16) float ps[kF32Waves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int idx = blockIdx.x * kF32Waves + wave;
+  if (idx >= a.M * a.Hq) return;  // whole waves: no barrier below
   const int m = idx / a.Hq, j = idx % a.Hq;
   const int kvh = (j * a.Hkv) / a.Hq;
   const int hd = a.hd;
@@ -424,21 +432,63 @@ __global__ void attn_f32_kernel(AttnArgs a) {
   const float* vb = static_cast<const float*>(a.vc) + kvh * a.head_stride;
   const int pos0 = a.pos_dev ? *a.pos_dev : a.pos0;
   const int L = a.causal ? pos0 + m + 1 : pos0 + a.M;
-  float acc[128];
-  for (int d = 0; d < hd; ++d) acc[d] = 0.f;
-  float mx = -INFINITY, l = 0.f;
-  for (int t = 0; t < L; ++t) {
-    float s = 0.f;
-    for (int d = 0; d < hd; ++d) s += q[d] * kb[static_cast<int64_t>(t) * hd + d];
-    s *= a.scale_log2;
-    const float mn = fmaxf(mx, s);
-    const float al = exp2f(mx - mn), p = exp2f(s - mn);
-    l = l * al + p;
-    for (int d = 0; d < hd; ++d) acc[d] = acc[d] * al + p * vb[v_index(t, d, hd)];
-    mx = mn;
+  float* qw = qs[wave];
+  float* pw = ps[wave];
+  for (int d = lane; d < hd; d += 64) qw[d] = q[d];
+  // LDS written by this wave's own lanes is read by its other lanes after lgkmcnt(0); the compiler
+  // barriers keep the accesses on their side of each wait
+  auto lds_sync = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  };
+  lds_sync();
+  float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int t0 = 0; t0 < L; t0 += 64) {
+    const int t = t0 + lane;
+    float sc = -INFINITY;
+    if (t < L) {
+      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<int64_t>(t) * hd);
+      float acc = 0.f;
+      for (int d4 = 0; d4 < hd / 4; ++d4) {
+        const float4 kv = kr[d4];
+        acc += qw[4 * d4] * kv.x + qw[4 * d4 + 1] * kv.y + qw[4 * d4 + 2] * kv.z + qw[4 * d4 + 3] * kv.w;
+      }
+      sc = acc * a.scale_log2;
+    }
+    const float mnew = fmaxf(mrun, wave_max(sc));
+    const float alpha = exp2f(mrun - mnew);  // 0 on the first chunk (mrun = -inf)
+    const float p = t < L ? exp2f(sc - mnew) : 0.f;
+    lrun = lrun * alpha + wave_sum(p);
+    o0 *= alpha;
+    o1 *= alpha;
+    pw[(lane & 32) + v_slot(lane & 31)] = p;  // slot order inside each 32-position block
+    lds_sync();
+    const int nb = t0 + 32 < L ? 2 : 1;  // V blocks of the chunk holding keys (masked keys weigh 0)
+    for (int b = 0; b < nb; ++b) {
+      const float* blk = vb + (static_cast<int64_t>(t0 / 32 + b) * hd) * kVB;  // [hd][32] of the block
+      const float4* pv = reinterpret_cast<const float4*>(pw + 32 * b);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int d = lane + 64 * c;
+        if (d >= hd) break;
+        const float4* row = reinterpret_cast<const float4*>(blk + d * kVB);
+        float acc = 0.f;
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {
+          const float4 v = row[s4], pp = pv[s4];
+          acc += v.x * pp.x + v.y * pp.y + v.z * pp.z + v.w * pp.w;
+        }
+        if (c == 0) o0 += acc; else o1 += acc;
+      }
+    }
+    lds_sync();  // every lane has read pw before the next chunk writes it
+    mrun = mnew;
   }
   float* o = static_cast<float*>(a.o) + static_cast<int64_t>(m) * a.ldo + j * hd;
-  for (int d = 0; d < hd; ++d) o[d] = acc[d] / l;
+  if (lane < hd) o[lane] = o0 / lrun;
+  if (lane + 64 < hd) o[lane + 64] = o1 / lrun;
 }
 
 // ------------------------------------------------------------------- host
@@ -477,7 +527,7 @@ int attention(const void* q, int64_t ldq, const void* kc, const void* vc, int64_
     a.splits = 1;
     ProfScope ps("attention_f32", s);
     const int n = M * Hq;
-    attn_f32_kernel<<<(n + 127) / 128, 128, 0, s>>>(a);
+    attn_f32_kernel<<<(n + kF32Waves - 1) / kF32Waves, 64 * kF32Waves, 0, s>>>(a);
     DG_LAUNCH_CHECK("attn_f32_kernel");
     return DG_OK;
   }

@@ -953,10 +953,10 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
     const bf16_t* hh = static_cast<const bf16_t*>(h);
     bf16_t* a = static_cast<bf16_t*>(act);
     {
-      ProfScope ps("expert_gateup_fp8", s, true);
-      if (gated) launch_timed(ps, expert_gateup_fp8_kernel<true>, g1, dim3(256), s, hh, ldh, q8->gu, q8->s_gu, E, F, D,
+      ProfScope ps("expert_gateup_fp8", s);
+      if (gated) expert_gateup_fp8_kernel<true><<<g1, dim3(256), 0, s>>>(hh, ldh, q8->gu, q8->s_gu, E, F, D,
                               per_gu, offsets, perm, a);
-      else launch_timed(ps, expert_gateup_fp8_kernel<false>, g1, dim3(256), s, hh, ldh, q8->gu, q8->s_gu, E, F, D,
+      else expert_gateup_fp8_kernel<false><<<g1, dim3(256), 0, s>>>(hh, ldh, q8->gu, q8->s_gu, E, F, D,
                         per_gu, offsets, perm, a);
     }
     DG_LAUNCH_CHECK("expert_gateup_fp8_kernel");
@@ -968,22 +968,22 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
     return DG_OK;
   }
   {
-    ProfScope ps("expert_gateup", s, true);
+    ProfScope ps("expert_gateup", s);
     if (dtype == DG_BF16) {
       const bf16_t* hh = static_cast<const bf16_t*>(h);
       const bf16_t* w = static_cast<const bf16_t*>(w_gu);
       bf16_t* a = static_cast<bf16_t*>(act);
-      if (gated) launch_timed(ps, expert_gateup_kernel<bf16_t, true>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+      if (gated) expert_gateup_kernel<bf16_t, true><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
                           offsets, perm, a);
-      else launch_timed(ps, expert_gateup_kernel<bf16_t, false>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+      else expert_gateup_kernel<bf16_t, false><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
                           offsets, perm, a);
     } else {
       const float* hh = static_cast<const float*>(h);
       const float* w = static_cast<const float*>(w_gu);
       float* a = static_cast<float*>(act);
-      if (gated) launch_timed(ps, expert_gateup_kernel<float, true>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+      if (gated) expert_gateup_kernel<float, true><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
                           offsets, perm, a);
-      else launch_timed(ps, expert_gateup_kernel<float, false>, g1, dim3(256), s, hh, ldh, w, E, F, D, per_gu,
+      else expert_gateup_kernel<float, false><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
                           offsets, perm, a);
     }
   }

@@ -620,18 +620,18 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
   g.inv_t = 1.0f / temp;
   dim3 grid(static_cast<unsigned>(p.splits), static_cast<unsigned>(rows));
   {
-    ProfScope ps("sample_partial", stream, true);
+    ProfScope ps("sample_partial", stream);
     const bool vec = vocab % kVec == 0;
     const bool cat = (sc.mode & DG_SCHED_SAMPLE) != 0;
     const dim3 block(kSampThreads);
     if (dtype == DG_BF16) {
-      if (cat) launch_timed(ps, sample_kernel<bf16_t, true, true>, grid, block, stream, g);
-      else if (vec) launch_timed(ps, sample_kernel<bf16_t, true, false>, grid, block, stream, g);
-      else launch_timed(ps, sample_kernel<bf16_t, false, false>, grid, block, stream, g);
+      if (cat) sample_kernel<bf16_t, true, true><<<grid, block, 0, stream>>>(g);
+      else if (vec) sample_kernel<bf16_t, true, false><<<grid, block, 0, stream>>>(g);
+      else sample_kernel<bf16_t, false, false><<<grid, block, 0, stream>>>(g);
     } else {
-      if (cat) launch_timed(ps, sample_kernel<float, true, true>, grid, block, stream, g);
-      else if (vec) launch_timed(ps, sample_kernel<float, true, false>, grid, block, stream, g);
-      else launch_timed(ps, sample_kernel<float, false, false>, grid, block, stream, g);
+      if (cat) sample_kernel<float, true, true><<<grid, block, 0, stream>>>(g);
+      else if (vec) sample_kernel<float, true, false><<<grid, block, 0, stream>>>(g);
+      else sample_kernel<float, false, false><<<grid, block, 0, stream>>>(g);
     }
   }
   DG_LAUNCH_CHECK("sample_kernel");

@@ -13,6 +13,7 @@
 #include <algorithm>
 
 #include "dg_common.h"
+#include "prof.h"
 #include "tiles.h"
 
 // Keep every multiply and add separately rounded (no FMA contraction) so the
@@ -96,6 +97,43 @@ __global__ void synth_logits_kernel(uint64_t key_bg, uint64_t key_pk, int rows, 
 }
 
 static int grid_for(int64_t n) { return static_cast<int>(std::min<int64_t>(std::max<int64_t>(ceil_div(n, 256), 1), 65536)); }
+
+// Calibration: a plain streaming read of n16 16-byte words, the ceiling a bandwidth-bound kernel of
+// this library can aim at. Grid-stride, 4 nontemporal 16-byte loads in flight per thread per
+// iteration; each thread folds its words with XOR and its workgroup writes one word to sink[block],
+// so no load can be elided.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int t = 0; t < 256; ++t) r ^= red[t];
+    sink[blockIdx.x] = r;
+  }
+}
+
+int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
+  ProfScope ps("stream_read", s);
+  stream_read_kernel<<<blocks, 256, 0, s>>>(static_cast<const uint4*>(src), bytes / 16, sink);
+  DG_LAUNCH_CHECK("stream_read_kernel");
+  return DG_OK;
+}
 
 int launch_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int dtype, void* out, hipStream_t s) {
   if (n == 0) return DG_OK;

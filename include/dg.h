@@ -232,6 +232,14 @@ int dg_synth_planted_logits(uint64_t seed, int32_t step, int32_t rows, int32_t v
 int dg_synth_fill_weights(const dg_model_desc* desc, uint64_t seed, float sigma, void* d_weights,
                           void* stream);
 
+/* Calibration of memory bandwidth: read `bytes` (a multiple of 16) of d_src
+ * once with a plain streaming kernel (`blocks` workgroups of 256 threads,
+ * grid-stride nontemporal 16-byte loads) and write one XOR-folded word per
+ * workgroup to d_sink (uint32[blocks]). Its duration bounds what a streaming
+ * kernel of this library can reach on the device; it computes nothing of the
+ * method. */
+int dg_stream_read(const void* d_src, int64_t bytes, uint32_t* d_sink, int32_t blocks, void* stream);
+
 /* --------------------------------------------------------------- model */
 /* Weight tensors inside the packed, caller-owned weight buffer. */
 enum {
