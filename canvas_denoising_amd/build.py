@@ -37,6 +37,8 @@ def flags(debug: bool) -> list[str]:
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas", "-Wno-unused-command-line-argument"]
     f += ["-O1", "-g", "-DDG_DEBUG=1"] if debug else ["-O3", "-DNDEBUG"]
+    # extra preprocessor definitions for a measured variant build (DG_BUILD_DEFINES="NAME=VALUE ...")
+    f += [f"-D{d}" for d in os.environ.get("DG_BUILD_DEFINES", "").split()]
     return f
 
 
