@@ -277,7 +277,7 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.sel_layer = CK;
   w.sel = take(static_cast<size_t>(d.n_layers) * CK * 4);
   w.gate = take(static_cast<size_t>(d.n_layers) * CK * 4);
-  w.offsets = take((d.n_experts + 1) * 4);
+  w.offsets = take((2 * d.n_experts + 1) * 4);  // slot offsets, then the experts by token count
   w.perm = take(CK * 4);
   w.slot_of = take(CK * 4);
   w.slot_gate = take(CK * 4);

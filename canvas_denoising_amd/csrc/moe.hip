@@ -11,7 +11,9 @@
 // pair sets a bit in a per-expert token mask in LDS; popcounts give expert
 // sizes, an exclusive scan gives offsets, and a token's rank inside its
 // expert is the popcount of the mask bits below it. The slot order is
-// therefore expert-major and token-ascending whatever the timing.
+// therefore expert-major and token-ascending whatever the timing. The same
+// kernel ranks the experts by token count (largest first, lower index on
+// ties) for the expert kernels' block order.
 //
 // Expert GEMMs: with a 256-token canvas an expert sees about 16 tokens, so
 // the work is a stream of expert weights (arithmetic intensity ~16 flop/B):
@@ -97,6 +99,8 @@ __device__ inline void route_row(const float* lg, int E, int k, int renorm, int 
 }
 
 // one workgroup of 1024 threads: expert sizes, offsets and the expert-major, token-ascending slot order.
+// offsets holds E + 1 slot offsets followed by the E experts in order of decreasing token count
+// (lower index first on ties).
 // MW mask words per expert cover 32 MW rows (E <= min(256, 16384 / MW)). With `tiles`, also the list of the
 // experts' 128-token tiles: tiles[0] = their number, tiles[1 + i] = e * 65536 + (tile within e),
 // experts in order.
@@ -169,6 +173,15 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
   __syncthreads();
   for (int i = tid; i <= E; i += 1024) offsets[i] = offs[i];
+  for (int e = tid; e < E; e += 1024) {
+    const int c = offs[e + 1] - offs[e];
+    int r = 0;
+    for (int f = 0; f < E; ++f) {
+      const int cf = offs[f + 1] - offs[f];
+      r += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    }
+    offsets[E + 1 + r] = e;
+  }
   if (tiles) {
     if (tid == 0) tiles[0] = toffs[E];
     for (int e = tid; e < E; e += 1024)
@@ -279,18 +292,24 @@ __device__ inline void with_token_tiles(int rem, F&& f) {
   f(std::integral_constant<int, 1>());
 }
 
-// Block b of an expert grid -> (expert, unit within the expert). Workgroups
-// of one expert read the same token rows, so with E a multiple of 8 they are
-// kept on one XCD (the dispatcher sends block b to XCD b % 8).
-__device__ inline void expert_of_block(int b, int per_e, int E, int* e, int* q) {
+// Block b of an expert grid -> (expert, unit within the expert). Blocks are dispatched about in
+// index order; with `rank` (offsets + E + 1: the experts, most tokens first) the experts are taken
+// in that order, so an expert whose tokens take several passes over its weights starts early
+// instead of finishing last (gate/up, measured 4 % faster with a skewed routing; down, whose
+// units are a quarter as long, measured 3 % slower and keeps the index order). Workgroups of one
+// expert read the same token rows, so with E a multiple of 8 they are kept on one XCD (the
+// dispatcher sends block b to XCD b % 8).
+__device__ inline void expert_of_block(int b, int per_e, int E, const int32_t* rank, int* e, int* q) {
+  int r;
   if ((E & 7) == 0) {
     const int x = b & 7, j = b >> 3;
-    *e = (j / per_e) * 8 + x;
+    r = (j / per_e) * 8 + x;
     *q = j % per_e;
   } else {
-    *e = b / per_e;
+    r = b / per_e;
     *q = b % per_e;
   }
+  *e = rank ? rank[r] : r;
 }
 
 // Sum the partials of the 4 waves into wave 0's acc (red: 3 * G * NT * 64 f32x4 of LDS).
@@ -546,7 +565,7 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
   __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
-  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  expert_of_block(blockIdx.x, per_e, E, offsets + E + 1, &e, &q);
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = D / 32;
@@ -571,7 +590,7 @@ __global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
   __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
-  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  expert_of_block(blockIdx.x, per_e, E, offsets + E + 1, &e, &q);
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = D / 32;
@@ -632,7 +651,7 @@ __global__ __launch_bounds__(256) void expert_down_kernel(
   __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
-  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  expert_of_block(blockIdx.x, per_e, E, nullptr, &e, &q);
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = F / 32;
@@ -654,7 +673,7 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
   __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
-  expert_of_block(blockIdx.x, per_e, E, &e, &q);
+  expert_of_block(blockIdx.x, per_e, E, nullptr, &e, &q);
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = F / 32;
