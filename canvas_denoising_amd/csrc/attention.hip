@@ -93,7 +93,10 @@ __host__ __device__ constexpr int att_keys(int qt) { return kVB * att_kb2(qt); }
 constexpr int kNW = DG_ATT_NW;            // waves per workgroup (4 or 8)
 constexpr int kQT = DG_ATT_QT;            // 16-query tiles per wave (share every K/V fragment read)
 constexpr int kQTLarge = 2;               // the same for passes of more than 256 rows (prefill chunks)
-constexpr int kLargeRows = 256;
+#ifndef DG_ATT_LARGE_ROWS
+#define DG_ATT_LARGE_ROWS 256
+#endif
+constexpr int kLargeRows = DG_ATT_LARGE_ROWS;  // passes of more rows take two query tiles per wave
 // query tiles per wave for a pass of M rows: canvases keep one, so that their key range splits over
 // more workgroups; long prefill chunks have work enough and share each staged K/V block among more
 // queries

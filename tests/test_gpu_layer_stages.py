@@ -24,15 +24,17 @@ def libs():
     return _lib, configs, runtime
 
 
-@pytest.mark.parametrize("dtype,gated,causal,M,past,renorm", [
-    ("bf16", 1, False, 64, 40, 0), ("bf16", 1, True, 64, 0, 0), ("bf16", 0, True, 50, 77, 0),
-    ("f32", 0, False, 64, 40, 0), ("f32", 1, True, 37, 5, 0), ("bf16", 1, False, 64, 40, 1),
-    ("f32", 0, True, 37, 5, 1)])
-def test_layer_stages(libs, dtype, gated, causal, M, past, renorm):
+@pytest.mark.parametrize("dtype,gated,causal,M,past,renorm,E", [
+    ("bf16", 1, False, 64, 40, 0, 8), ("bf16", 1, True, 64, 0, 0, 8), ("bf16", 0, True, 50, 77, 0, 8),
+    ("f32", 0, False, 64, 40, 0, 8), ("f32", 1, True, 37, 5, 0, 8), ("bf16", 1, False, 64, 40, 1, 8),
+    ("f32", 0, True, 37, 5, 1, 8),
+    # wider routings: 64 experts; 128 with 37 rows and renormalised gates; 192, ungated and causal
+    ("bf16", 1, False, 64, 40, 0, 64), ("bf16", 1, True, 37, 5, 1, 128), ("bf16", 0, True, 50, 77, 0, 192)])
+def test_layer_stages(libs, dtype, gated, causal, M, past, renorm, E):
     """renorm = 1: gates renormalised over the k chosen experts (dg_model_desc.renorm_gates)."""
     L, configs, runtime = libs
-    announce(f"layer stages {dtype} gated={gated} causal={causal} M={M} past={past} renorm={renorm}")
-    model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=1, canvas=64, capacity=256, renorm=renorm)
+    announce(f"layer stages {dtype} gated={gated} causal={causal} M={M} past={past} renorm={renorm} E={E}")
+    model, W, shape = build(libs, dtype=dtype, gated=gated, n_layers=1, canvas=64, capacity=256, renorm=renorm, E=E)
     tol = tol_for(dtype)
     rng = np.random.default_rng(M + past)
     if past:
@@ -98,4 +100,13 @@ def test_layer_stages(libs, dtype, gated, causal, M, past, renorm):
     # the layer leaves h = RMSNorm(its output), the next layer's input
     h_gpu = to_f64(model.buffer(L.DG_BUF_H, model.dtype, (64, D)))[:M]
     assert_close(h_gpu, OM.rms_norm(y_ref, shape.rms_eps), tol, "output RMSNorm")
+    # a second launch on the same input, with the routing outputs cleared first, routes again
+    # identically
+    model.buffer(L.DG_BUF_SEL, torch.int32, (64, shape.top_k)).zero_()
+    model.buffer(L.DG_BUF_SLOT_OF, torch.int32, (64, shape.top_k)).zero_()
+    L.dg_kv_set_length(model.ctx, past)
+    model.forward_layer(0, torch.from_numpy(x0.astype(np.float32)).cuda(), M, causal)
+    torch.cuda.synchronize()
+    assert np.array_equal(model.buffer(L.DG_BUF_SEL, torch.int32, (64, shape.top_k)).cpu().numpy()[:M], sel)
+    assert np.array_equal(model.buffer(L.DG_BUF_SLOT_OF, torch.int32, (64, shape.top_k)).cpu().numpy()[:M], slot_of)
     model.close()
