@@ -6,6 +6,11 @@
 // and G = 0x9E3779B97F4A7C15. A "normal" value is the Irwin-Hall sum of the
 // hash's four 16-bit fields minus 131070, times float(sigma / sqrt((2^32 - 1) / 3))
 // in one correctly rounded float multiply; bf16 rounds that to nearest-even.
+// The background of the planted-peak logits sums the twelve fields of the
+// hashes of indices 3 i, 3 i + 1 and 3 i + 2 (minus 393210, times
+// float(sigma / sqrt(2^32 - 1))): tails to 6 sigma, so the largest of a row's
+// 262144 values (about 4.2 sigma) competes with a planted peak about as a
+// normal's would.
 // A uniform id is ((hash >> 32) * V) >> 32. The host generator used by the
 // tests computes the same bits.
 #include <math.h>
@@ -38,6 +43,23 @@ __device__ inline float irwin_hall4(uint64_t h) {
   const int64_t s = static_cast<int64_t>(h & 0xFFFF) + static_cast<int64_t>((h >> 16) & 0xFFFF) +
                     static_cast<int64_t>((h >> 32) & 0xFFFF) + static_cast<int64_t>(h >> 48);
   return static_cast<float>(s - 131070);
+}
+
+__device__ inline int64_t fields_sum(uint64_t h) {
+  return static_cast<int64_t>(h & 0xFFFF) + static_cast<int64_t>((h >> 16) & 0xFFFF) +
+         static_cast<int64_t>((h >> 32) & 0xFFFF) + static_cast<int64_t>(h >> 48);
+}
+
+// twelve-field sum for element i of stream `key` (hash indices 3 i .. 3 i + 2)
+__device__ inline float irwin_hall12(uint64_t key, int64_t i) {
+  const uint64_t j = 3 * static_cast<uint64_t>(i);
+  const int64_t s = fields_sum(mix64(key + (j + 1) * kGolden)) + fields_sum(mix64(key + (j + 2) * kGolden)) +
+                    fields_sum(mix64(key + (j + 3) * kGolden));
+  return static_cast<float>(s - 393210);
+}
+
+float normal12_scale(float sigma) {
+  return static_cast<float>(static_cast<double>(sigma) / std::sqrt(65536.0 * 65536.0 - 1.0));
 }
 
 float normal_scale(float sigma) {
@@ -86,7 +108,7 @@ __global__ void synth_logits_kernel(uint64_t key_bg, uint64_t key_pk, int rows, 
   const int64_t n = static_cast<int64_t>(rows) * vocab;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    float v = irwin_hall4(mix64(key_bg + static_cast<uint64_t>(i + 1) * kGolden)) * scale;
+    float v = irwin_hall12(key_bg, i) * scale;
     const int64_t row = i / vocab, col = i - row * vocab;
     const uint64_t h = mix64(key_pk + static_cast<uint64_t>(row + 1) * kGolden);
     const bool planted = static_cast<uint32_t>(h) < kPeakFractionNum;
@@ -176,7 +198,7 @@ int launch_synth_logits(uint64_t seed, int step, int rows, int vocab, float sigm
   if (n == 0) return DG_OK;
   const uint64_t kb = stream_key(seed, kTidLogits + (static_cast<uint64_t>(step) << 8));
   const uint64_t kp = stream_key(seed, kTidPeak + (static_cast<uint64_t>(step) << 8));
-  synth_logits_kernel<<<grid_for(n), 256, 0, s>>>(kb, kp, rows, vocab, normal_scale(sigma), peak,
+  synth_logits_kernel<<<grid_for(n), 256, 0, s>>>(kb, kp, rows, vocab, normal12_scale(sigma), peak,
                                                   static_cast<bf16_t*>(out));
   DG_LAUNCH_CHECK("synth_logits_kernel");
   return DG_OK;

@@ -217,8 +217,10 @@ int dg_synth_normal(uint64_t seed, uint64_t tid, int64_t n, float sigma, int32_t
 /* Uniform ids in [0, vocab). */
 int dg_synth_uniform_ids(uint64_t seed, uint64_t tid, int64_t n, int32_t vocab,
                          int32_t* d_out, void* stream);
-/* bf16 logits [rows x vocab]: background sigma, +peak added at one uniform
- * column in about 70% of the rows (buffer index `step` selects the stream). */
+/* bf16 logits [rows x vocab]: background of standard deviation sigma (the
+ * sum of twelve 16-bit hash fields, three hashes per value: tails to 6 sigma),
+ * +peak added at one uniform column in about 70% of the rows (buffer index
+ * `step` selects the stream). */
 int dg_synth_planted_logits(uint64_t seed, int32_t step, int32_t rows, int32_t vocab,
                             float sigma, float peak, void* d_out, void* stream);
 /* Fill a packed weight buffer (see dg_weight_tensor) with synthetic values of

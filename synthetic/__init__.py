@@ -18,6 +18,12 @@ bit-identical):
   correctly rounded float32 multiply, ``value = f32(c) * f32(sigma / SD4)``
   with ``SD4 = sqrt((65536**2 - 1) / 3)``. The result has mean 0 and standard
   deviation ``sigma`` and is bounded by about 3.46 sigma.
+* The background of the planted-peak logits uses twelve 16-bit fields, those of
+  the hashes of indices 3 i, 3 i + 1 and 3 i + 2: ``c = sum - 393210``,
+  ``value = f32(c) * f32(sigma / SD12)`` with ``SD12 = sqrt(65536**2 - 1)``.
+  Its tails reach 6 sigma; the largest of 262144 draws is about 4.2 sigma
+  (a normal's: 4.55 sigma; four fields': 3.3 sigma), which is what decides
+  how often a planted peak is the row's argmax.
 * bf16 values are the float32 value rounded to nearest-even on its upper 16
   bits.
 * Uniform ids are ``((hash >> 32) * V) >> 32``.
@@ -34,6 +40,7 @@ import numpy as np
 MASK64 = (1 << 64) - 1
 GOLDEN = 0x9E3779B97F4A7C15
 SD4 = math.sqrt((65536.0 * 65536.0 - 1.0) / 3.0)
+SD12 = math.sqrt(65536.0 * 65536.0 - 1.0)
 
 # tensor-id namespaces (kept disjoint by the high bits)
 TID_EMBED = 1
@@ -109,6 +116,20 @@ def normal_f32(seed: int, tid: int, n_or_idx, sigma: float) -> np.ndarray:
     return c * normal_scale(sigma)
 
 
+def _fields_sum(h: np.ndarray) -> np.ndarray:
+    f = np.uint64(0xFFFF)
+    return (h & f) + ((h >> np.uint64(16)) & f) + ((h >> np.uint64(32)) & f) + (h >> np.uint64(48))
+
+
+def normal12_f32(seed: int, tid: int, idx: np.ndarray, sigma: float) -> np.ndarray:
+    """float32 'normal' values from twelve 16-bit uniforms (hashes of 3 i, 3 i + 1, 3 i + 2)."""
+    i3 = np.asarray(idx, dtype=np.uint64) * np.uint64(3)
+    s = (_fields_sum(hash64(seed, tid, i3)) + _fields_sum(hash64(seed, tid, i3 + np.uint64(1)))
+         + _fields_sum(hash64(seed, tid, i3 + np.uint64(2))))
+    c = (s.astype(np.int64) - 393210).astype(np.float32)
+    return c * np.float32(sigma / SD12)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -131,8 +152,9 @@ def uniform_ids(seed: int, tid: int, n: int, vocab: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Planted-peak logits: background "normal" sigma, and in a fraction of rows
-# +peak added at one uniformly chosen column, then rounded to bf16.
+# Planted-peak logits: background "normal" sigma (twelve fields), and in a
+# fraction of rows +peak added at one uniformly chosen column, then rounded to
+# bf16.
 # ---------------------------------------------------------------------------
 PEAK_FRACTION_NUM = 3006477107  # floor(0.7 * 2**32)
 
@@ -154,7 +176,7 @@ def planted_logits_rows(seed: int, step: int, rows: int, vocab: int, row_ids,
     out = np.empty((len(row_ids), vocab), dtype=np.uint16)
     cols = np.arange(vocab, dtype=np.uint64)
     for j, r in enumerate(row_ids):
-        v = normal_f32(seed, TID_LOGITS + (step << 8), np.uint64(r) * np.uint64(vocab) + cols, sigma)
+        v = normal12_f32(seed, TID_LOGITS + (step << 8), np.uint64(r) * np.uint64(vocab) + cols, sigma)
         if planted[r]:
             v[col[r]] = np.float32(v[col[r]] + np.float32(peak))
         out[j] = f32_to_bf16_bits(v)

@@ -1,4 +1,6 @@
 """The seeded input generator: reproducible, moments as documented, bf16 rounding."""
+import math
+
 import numpy as np
 
 import synthetic as S
@@ -34,3 +36,19 @@ def test_planted_logits():
     assert rows.shape == (3, 1024)
     again = S.planted_logits_rows(0, 0, 16, 1024, [2])
     assert np.array_equal(rows[2], again[0])
+
+
+def test_twelve_field_background():
+    """The planted logits' background: mean 0, standard deviation sigma, tails past the four-field
+    bound (3.46 sigma), and values equal to the sum of the twelve 16-bit fields of the hashes of
+    3 i, 3 i + 1, 3 i + 2 recomputed here with Python integers."""
+    v = S.normal12_f32(5, 77, np.arange(262144, dtype=np.uint64), 3.0).astype(np.float64)
+    assert abs(v.mean()) < 0.03 and abs(v.std() - 3.0) < 0.03
+    assert 3.8 * 3.0 < np.abs(v).max() < 6.0 * 3.0
+    for i in (0, 1, 12345):
+        s = 0
+        for q in range(3):
+            h = int(S.hash64(5, 77, np.array([3 * i + q], dtype=np.uint64))[0])
+            s += sum((h >> (16 * f)) & 0xFFFF for f in range(4))
+        want = np.float32(s - 393210) * np.float32(3.0 / math.sqrt(65536.0 * 65536.0 - 1.0))
+        assert v[i] == np.float64(want)
