@@ -3,15 +3,18 @@
 // add, GeLU, gated GeLU over paired gate/up rows, QKV split into the query
 // buffer and the KV cache, MoE combine).
 //
-// Tiling: 256 threads = 4 waves in a 2 x 2 arrangement over a BM x BN tile;
-// each wave owns (BM/2) x (BN/2) as 16x16 MFMA tiles. A and B tiles of 128
-// bytes per row (BK = 64 bf16 or 32 fp32) are staged through LDS with a
-// register prefetch of the next k-tile (double buffer, one barrier per
-// k-tile); rows are padded by 16 bytes so the 16 lanes of a fragment read hit
-// distinct banks. Workgroups that share a B slice are mapped to the same XCD
+// Two tile kernels. bf16 (every GEMM of the benchmark model) runs
+// gemm_dma_kernel: 64 x 64 tiles (128 x 128 for long prefill chunks) by 8
+// waves, A and B rows of 128 bytes copied asynchronously from global memory
+// straight into a 4-deep LDS ring (global_load_lds), chunks XOR-swizzled so
+// fragment reads hit distinct banks, one counted wait and one barrier per
+// k-tile. fp32 runs gemm_kernel: 4 waves in a 2 x 2 arrangement over the
+// tile, rows padded by 16 bytes in LDS, a register prefetch of the next
+// k-tile. In both, workgroups that share a B slice are mapped to the same XCD
 // (dispatch is round-robin over the 8 XCDs) so the slice is fetched from HBM
-// once and re-read from that XCD's L2. Split-K writes fp32 partials that a
-// second kernel reduces in a fixed order before the epilogue.
+// once and re-read from that XCD's L2, and split-K writes fp32 partials that
+// a second kernel (or the caller's row kernel) reduces in a fixed order
+// before the epilogue.
 #include <algorithm>
 
 #include "dg_common.h"
