@@ -194,9 +194,12 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
 
   // Copy sources. A stage is SBYTES / 1 KB wave copies, CPW per wave (copy c = wave * CPW + i); the
   // first KC are K: copy c covers rows c * RPC .. of the stage and lane l fills LDS position l % CPR
-  // of row l / CPR with the row's chunk (l % CPR) ^ (row % 8); rows past L re-read row L-1 (masked).
+  // of row l / CPR with the row's chunk (l % CPR) ^ (row % CPR); rows past L re-read row L-1 (masked).
   // The rest are V^T (the stage's contiguous 32-position block): copy c covers hd rows
-  // (c - KC) * 16 .., lane l fills position l % 4 of row l / 4 with chunk (l % 4) ^ ((row / 2) % 4).
+  // (c - KC) * 16 .., lane l fills position l % 4 of row l / 4 with chunk (l % 4) ^ ((row / 4) % 4).
+  // With these swizzles the 16 rows a fragment read touches (16 lanes, 16 bytes each) fall on 16
+  // distinct 16-byte bank groups: K row r's chunk q sits at position q ^ (r % CPR), and V^T rows of
+  // 64 bytes put row r's chunk c at position c ^ ((r / 4) % 4).
   const bf16_t* kbase = static_cast<const bf16_t*>(a.kc) + kvh * a.head_stride;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.vc) + kvh * a.head_stride;
   constexpr int RPC = 1024 / ROWB;
@@ -207,10 +210,10 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
     const int c = wave * CPW + i;
     if (c < KC) {
       const int r = c * RPC + lane / CPR;
-      csrc[i] = r * HD + ((lane % CPR) ^ (r & 7)) * 8;
+      csrc[i] = r * HD + ((lane % CPR) ^ (r & (CPR - 1))) * 8;
     } else {
       const int r = (c - KC) * 16 + lane / 4;  // row of the stage's [kKB2 * HD][32] V^T rows
-      csrc[i] = r * kVB + ((lane % 4) ^ ((r >> 1) & 3)) * 8;
+      csrc[i] = r * kVB + ((lane % 4) ^ ((r >> 2) & 3)) * 8;
     }
   }
   auto issue = [&](int st, int slot) {
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
       const int r = kt * 16 + fr;
 #pragma unroll
       for (int h = 0; h < HS; ++h)
-        kf[kt][h] = *reinterpret_cast<const bf16x8_t*>(sk + r * ROWB + (((h * 4 + g4) ^ (r & 7)) << 4));
+        kf[kt][h] = *reinterpret_cast<const bf16x8_t*>(sk + r * ROWB + (((h * 4 + g4) ^ (r & (CPR - 1))) << 4));
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * kNW) void attn_bf16_kernel(AttnArgs a) {
         for (int j = 0; j < HT; ++j) {
           const int vr = b * HD + j * 16 + fr;
           const bf16x8_t vf =
-              *reinterpret_cast<const bf16x8_t*>(sv + (vr * kVB + ((g4 ^ ((vr >> 1) & 3)) << 3)) * 2);
+              *reinterpret_cast<const bf16x8_t*>(sv + (vr * kVB + ((g4 ^ ((vr >> 2) & 3)) << 3)) * 2);
           o[t][j] = Frag<bf16_t>::mma(vf, pf, o[t][j]);
         }
       }
