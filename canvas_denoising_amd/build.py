@@ -25,6 +25,12 @@ SOURCES = ["api.cpp", "prof.cpp", "model.cpp", "sampler.hip", "synth.hip", "gemm
            "elementwise.hip", "vocab.hip", "fp8.hip"]
 
 
+# per-source compiler flags: the routed-expert streams keep their MFMA accumulators in ordinary
+# VGPRs (with the accumulation registers the allocator gives every token-tile branch of a kernel
+# its own set, which halves the waves per SIMD)
+SOURCE_FLAGS: dict[str, list[str]] = {"moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -45,7 +51,9 @@ def flags(debug: bool) -> list[str]:
 def compile_one(src: str, debug: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc()] + flags(debug) + ["-c", path, "-o", obj]
+    cmd = [hipcc()] + flags(debug) + SOURCE_FLAGS.get(src, []) + ["-c", path, "-o", obj]
+    # extra compiler flags for one source of a measured variant build (DG_FLAGS_moe="...")
+    cmd[1:1] = os.environ.get("DG_FLAGS_" + src.split(".")[0], "").split()
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -20,14 +20,15 @@
 // HBM-bound, and with a loaded HBM latency of a few microseconds it is
 // latency-bound unless many bytes are in flight, and DRAM-page-bound unless
 // those bytes come in long contiguous runs. The weights are stored
-// fragment-tiled (tiles.h): a workgroup owns one tile group (gate/up: 32
-// features, gate and up; down: 64 output rows), a contiguous stretch of
-// memory, and its 4 waves split the k-tiles so that each stage of loads is
-// one contiguous run with 1 KB per load instruction, straight into MFMA B
-// fragments through a ring of register stages, together with the expert's
-// gathered token rows (A fragments, from L2). The waves' partial sums meet
-// in LDS at the end. Up to 48 tokens are held in accumulators per pass; an
-// expert with more tokens takes further passes.
+// fragment-tiled (tiles.h): a workgroup owns one or two tile groups (gate/up:
+// 32 features, gate and up; down: two groups of 64 output rows), each a
+// contiguous stretch of memory, and its 4 waves split the k-tiles so that
+// each stage of loads is one contiguous run per group with 1 KB per load
+// instruction, straight into MFMA B fragments through a ring of register
+// stages, together with the expert's gathered token rows (A fragments, from
+// L2). The waves' partial sums meet in LDS at the end. Up to 64 tokens are
+// held in accumulators per pass; an expert with more tokens takes further
+// passes.
 #include <math.h>
 
 #include <algorithm>
@@ -264,6 +265,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(const floa
 #ifndef DG_EXP_NS_DN
 #define DG_EXP_NS_DN 2
 #endif
+// tile groups per workgroup (1 or 2) of the gate/up and down streams, and the k-tiles per wave and
+// stage and register stages of the two-group form. Two groups halve the token bytes per weight
+// byte; measured on the benchmark shapes, down 2-4 us faster with two, gate/up no faster.
+#ifndef DG_EXP_GS_GU
+#define DG_EXP_GS_GU 1
+#endif
+#ifndef DG_EXP_GS_DN
+#define DG_EXP_GS_DN 2
+#endif
+#ifndef DG_EXP_KSP_GU2
+#define DG_EXP_KSP_GU2 1
+#endif
+#ifndef DG_EXP_NS_GU2
+#define DG_EXP_NS_GU2 2
+#endif
+#ifndef DG_EXP_KSP_DN2
+#define DG_EXP_KSP_DN2 1
+#endif
+#ifndef DG_EXP_NS_DN2
+#define DG_EXP_NS_DN2 2
+#endif
 constexpr int kExpWaves = 4;
 #ifndef DG_EXP_NT
 #define DG_EXP_NT 0
@@ -274,10 +296,12 @@ constexpr bool kExpNT = DG_EXP_NT;  // nontemporal weight loads
 #endif
 constexpr bool kExpRot = DG_EXP_ROT;  // per-workgroup rotation of the stage order
 #ifndef DG_EXP_MAX_NT
-#define DG_EXP_MAX_NT 3
+#define DG_EXP_MAX_NT 4
 #endif
 // 16-token tiles one pass of an expert workgroup holds: an expert with more tokens streams its
-// weights once per pass, so the bound trades registers (accumulators) against weight re-reads
+// weights once per pass, so the bound trades registers (accumulators) against weight re-reads.
+// Four tiles fit two waves per SIMD when the accumulators live in ordinary VGPRs (the build
+// compiles this file so); 48 tokens per pass measured 1 % slower on the benchmark routing.
 constexpr int kExpMaxNT = DG_EXP_MAX_NT;
 
 // Calls f(std::integral_constant<int, NT>) with the fewest 16-token tiles (at most kExpMaxNT)
@@ -312,59 +336,61 @@ __device__ inline void expert_of_block(int b, int per_e, int E, const int32_t* r
   *e = rank ? rank[r] : r;
 }
 
-// Sum the partials of the 4 waves into wave 0's acc (red: 3 * G * NT * 64 f32x4 of LDS).
+// The 4 waves' partial sums of token tile t meet in LDS (red: 4 * G * 64 f32x4): every wave
+// stores its own, then each output tile is summed by one wave, wave 0's partial first and then
+// waves 1, 2, 3 in order.
 template <int G, int NT>
-__device__ inline void reduce_waves(f32x4_t (&acc)[G][NT], f32x4_t* red, int wave, int lane) {
-  if (wave > 0) {
+__device__ inline void stash_partials(const f32x4_t (&acc)[G][NT], int t, f32x4_t* red, int wave, int lane) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) red[(((wave - 1) * G + g) * NT + t) * 64 + lane] = acc[g][t];
-  }
+  for (int g = 0; g < G; ++g) red[(wave * G + g) * 64 + lane] = acc[g][t];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < kExpWaves - 1; ++w)
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[g][t] += red[((w * G + g) * NT + t) * 64 + lane];
-  }
 }
 
-// One pass of a workgroup over one tile group of its expert's weights (G
-// tiles per k-tile, tiles.h) against NT 16-token tiles. The k-tiles are
+template <int G>
+__device__ inline f32x4_t sum_partials(const f32x4_t* red, int g, int lane) {
+  f32x4_t v = red[g * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kExpWaves; ++w) v += red[(w * G + g) * 64 + lane];
+  return v;
+}
+
+// One pass of a workgroup over GS consecutive tile groups of its expert's weights (G tiles per
+// k-tile each, tiles.h; GS G tiles per k-step in all) against NT 16-token tiles. The k-tiles are
 // split over the 4 waves in runs of KSP: stage s of wave w holds k-tiles
 // s * 4 KSP + w KSP + u (u < KSP), so the four waves' loads of one stage
 // cover 4 KSP consecutive k-tiles of the group, one contiguous run of memory
-// (whole DRAM pages rather than scattered pieces of them). Weight and token
+// (whole DRAM pages rather than scattered pieces of them; one run per group). Every token
+// fragment feeds GS G products, so with GS = 2 a workgroup loads half the token bytes per weight
+// byte that one group does (the expert's tokens are re-read by each of its workgroups). Weight and token
 // fragments stream through NS register stages. Loads are never predicated
 // (k-tiles past the end re-read the last one and are not multiplied; token
 // rows past the expert's count repeat its last token and are not stored),
 // so the compiler keeps exactly NS - 1 stages of loads outstanding. Each
 // wave ends with the partial sums of its k-tiles.
-template <typename T, int G, int NT, int KSP, int NS>
+template <typename T, int G, int NT, int KSP, int NS, int GS = 1>
 struct SplitStream {
   using Fr = Frag<T>;
   using FT = typename Fr::type;
+  static constexpr int GT = GS * G;  // weight tiles per k-step
   struct Stage {
-    FT b[KSP][G];
+    FT b[KSP][GT];
     FT a[KSP][NT];
   };
-  f32x4_t acc[G][NT];
+  f32x4_t acc[GT][NT];
 
-  // bt: this lane's fragment in k-tile 0 of the group; arow[t]: this lane's
+  // bt: this lane's fragment in k-tile 0 of the first group; arow[t]: this lane's
   // token row of tile t at column 8 * (lane / 16); KT: k-tiles of 32.
   // rot: the stream starts at stage rot and wraps (workgroups running side by side then read
   // different offsets of their groups instead of marching through the same address bits together)
   __device__ inline void run(const T* bt, const T* const* arow, int KT, int wave, int rot) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < GT; ++g)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[g][t] = f32x4_t{0, 0, 0, 0};
     constexpr int kPer = kExpWaves * KSP;
     const int nst = (KT + kPer - 1) / kPer;
     const int first = wave * KSP;
+    const int64_t gstride = static_cast<int64_t>(KT) * G * kTileElems;  // one group's elements
     rot %= nst;
     auto rs = [&](int s) { const int r = s + rot; return r >= nst ? r - nst : r; };
     auto load = [&](Stage& S, int s) {
@@ -373,8 +399,8 @@ struct SplitStream {
       for (int u = 0; u < KSP; ++u) {
         const int kt = min(base + u, KT - 1);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const T* bp = bt + (static_cast<int64_t>(kt) * G + g) * kTileElems;
+        for (int g = 0; g < GT; ++g) {
+          const T* bp = bt + (g / G) * gstride + (static_cast<int64_t>(kt) * G + g % G) * kTileElems;
           S.b[u][g] = kExpNT ? Fr::load_nt(bp) : Fr::load(bp);
         }
 #pragma unroll
@@ -389,7 +415,7 @@ struct SplitStream {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][t] = Fr::mma(S.a[u][t], S.b[u][g], acc[g][t]);
+            for (int g = 0; g < GT; ++g) acc[g][t] = Fr::mma(S.a[u][t], S.b[u][g], acc[g][t]);
         }
     };
     Stage st[NS];
@@ -409,7 +435,10 @@ struct SplitStream {
       if (s0 + u < nst) compute(st[u], s0 + u);
   }
 
-  __device__ inline void reduce(f32x4_t* red, int wave, int lane) { reduce_waves<G, NT>(acc, red, wave, lane); }
+  static constexpr int kTiles = GT;
+  __device__ inline void stash(int t, f32x4_t* red, int wave, int lane) {
+    stash_partials<GT, NT>(acc, t, red, wave, lane);
+  }
 };
 
 #ifndef DG_EXP8_KP_GU
@@ -511,18 +540,22 @@ struct SplitStream8 {
       if (s0 + u < nst) compute(st[u], s0 + u);
   }
 
-  __device__ inline void reduce(f32x4_t* red, int wave, int lane) { reduce_waves<G, NT>(acc, red, wave, lane); }
+  static constexpr int kTiles = G;
+  __device__ inline void stash(int t, f32x4_t* red, int wave, int lane) {
+    stash_partials<G, NT>(acc, t, red, wave, lane);
+  }
 };
 
 // act[slot][j] = GeLU(h W_gate[e]^T)_j * (h W_up[e]^T)_j (gated) or GeLU(h W_up[e]^T)_j for up to
-// 16 NT slots of expert e starting at p0 and the 16 kGuBlocks features j0 .. of the tile group.
-// FP8: bt points at E4M3 codes and the products are multiplied by this lane's row scales scl[g]
-// (gate blocks, then up blocks) before the activation.
-template <typename T, bool GATED, int NT, bool FP8>
+// 16 NT slots of expert e starting at p0 and the 16 kGuBlocks GS features j0 .. of GS tile groups.
+// FP8 (GS = 1): bt points at E4M3 codes and the products are multiplied by this lane's row scales
+// scl[g] (gate blocks, then up blocks) before the activation.
+template <typename T, bool GATED, int NT, bool FP8, int GS = 1>
 __device__ inline void gateup_pass(const T* h, int64_t ldh, const void* bt, int F, int KT, int beg, int cnt, int p0,
                                    const int32_t* perm, T* act, int j0, int wave, int lane, f32x4_t* red,
                                    const float* scl) {
   constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
+  static_assert(!FP8 || GS == 1, "the FP8 stream covers one tile group");
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const T* arow[NT];
 #pragma unroll
@@ -531,38 +564,44 @@ __device__ inline void gateup_pass(const T* h, int64_t ldh, const void* bt, int 
     arow[t] = h + static_cast<int64_t>(perm[beg + s]) * ldh + fk;
   }
   std::conditional_t<FP8, SplitStream8<G, NT, DG_EXP8_KP_GU, DG_EXP8_NS_GU>,
-                     SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU>> sp;
+                     std::conditional_t<GS == 1, SplitStream<T, G, NT, DG_EXP_KSP_GU, DG_EXP_NS_GU>,
+                                        SplitStream<T, G, NT, DG_EXP_KSP_GU2, DG_EXP_NS_GU2, GS>>> sp;
   if constexpr (FP8) sp.run(static_cast<const uint8_t*>(bt), arow, KT, wave, kExpRot ? blockIdx.x : 0);
   else sp.run(static_cast<const T*>(bt), arow, KT, wave, kExpRot ? blockIdx.x : 0);
-  sp.reduce(red, wave, lane);
-  if (wave == 0) {
+  constexpr int GT = decltype(sp)::kTiles;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) {
+    sp.stash(t, red, wave, lane);
+    // output tile pair pi (gate block, up block) is summed and stored by wave pi % 4
+#pragma unroll
+    for (int pi = 0; pi < GS * kGuBlocks; ++pi) {
+      if (pi % kExpWaves != wave) continue;
+      const int gi = pi / kGuBlocks, b = pi % kGuBlocks;
+      const int ga = gi * G + b, gb = gi * G + kGuBlocks + b;
+      const f32x4_t xg = sum_partials<GT>(red, ga, lane);
+      const f32x4_t xu = GATED ? sum_partials<GT>(red, gb, lane) : xg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
         if (s < cnt) {
-#pragma unroll
-          for (int b = 0; b < kGuBlocks; ++b) {
-            const float a0 = FP8 ? sp.acc[b][t][i] * scl[b] : sp.acc[b][t][i];
-            const float v = GATED ? gelu_erf(a0) * (FP8 ? sp.acc[kGuBlocks + b][t][i] * scl[kGuBlocks + b]
-                                                         : sp.acc[kGuBlocks + b][t][i])
-                                  : gelu_erf(a0);
-            act[static_cast<int64_t>(beg + s) * F + j0 + b * 16 + fr] = from_f32<T>(v);
-          }
+          const float a0 = FP8 ? xg[i] * scl[ga] : xg[i];
+          const float v = GATED ? gelu_erf(a0) * (FP8 ? xu[i] * scl[gb] : xu[i]) : gelu_erf(a0);
+          act[static_cast<int64_t>(beg + s) * F + j0 + pi * 16 + fr] = from_f32<T>(v);
         }
       }
+    }
+    __syncthreads();  // red is reused by the next tile or pass
   }
-  __syncthreads();  // red is reused by the next pass
 }
 
-// Grid: E * (F / (16 kGuBlocks)) workgroups of 4 waves; block q of expert e owns feature group q.
-template <typename T, bool GATED>
+// Grid: E * (F / (16 kGuBlocks GS)) workgroups of 4 waves; block q of expert e owns feature groups
+// GS q .. GS q + GS - 1.
+template <typename T, bool GATED, int GS>
 __global__ __launch_bounds__(256) void expert_gateup_kernel(
     const T* __restrict__ h, int64_t ldh, const T* __restrict__ w_gu, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, T* __restrict__ act) {
   constexpr int G = (GATED ? 2 : 1) * kGuBlocks;
-  __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
+  __shared__ f32x4_t red[kExpWaves * GS * G * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, offsets + E + 1, &e, &q);
@@ -570,12 +609,12 @@ __global__ __launch_bounds__(256) void expert_gateup_kernel(
   if (cnt == 0) return;
   const int KT = D / 32;
   const T* bt = w_gu + static_cast<int64_t>(e) * (GATED ? 2 : 1) * F * D +
-                static_cast<int64_t>(q) * KT * G * kTileElems + lane * 8;
-  const int j0 = q * 16 * kGuBlocks;
+                static_cast<int64_t>(q) * GS * KT * G * kTileElems + lane * 8;
+  const int j0 = q * GS * 16 * kGuBlocks;
   for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
     with_token_tiles(cnt - p0, [&](auto nt) {
-      gateup_pass<T, GATED, decltype(nt)::value, false>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave, lane,
-                                                        red, nullptr);
+      gateup_pass<T, GATED, decltype(nt)::value, false, GS>(h, ldh, bt, F, KT, beg, cnt, p0, perm, act, j0, wave,
+                                                            lane, red, nullptr);
     });
 }
 
@@ -587,7 +626,7 @@ __global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
     bf16_t* __restrict__ act) {
   constexpr int gw = GATED ? 2 : 1;
   constexpr int G = gw * kGuBlocks;
-  __shared__ f32x4_t red[(kExpWaves - 1) * G * kExpMaxNT * 64];
+  __shared__ f32x4_t red[kExpWaves * G * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, offsets + E + 1, &e, &q);
@@ -608,9 +647,10 @@ __global__ __launch_bounds__(256) void expert_gateup_fp8_kernel(
     });
 }
 
-// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 16 kDownGroup outputs n0 ..
-// FP8: bt points at E4M3 codes and output row block g is multiplied by this lane's row scale scl[g].
-template <typename T, int NT, bool FP8>
+// out[slot][n] = gate[slot] * sum_f act[slot][f] W_down[e][n][f] for the 16 kDownGroup GS outputs n0 ..
+// FP8 (GS = 1): bt points at E4M3 codes and output row block g is multiplied by this lane's row
+// scale scl[g].
+template <typename T, int NT, bool FP8, int GS = 1>
 __device__ inline void down_pass(const T* act, const void* bt, int F, int D, int beg, int cnt, int p0,
                                  const float* slot_gate, float* out, int n0, int wave, int lane, f32x4_t* red,
                                  const float* scl) {
@@ -621,47 +661,54 @@ __device__ inline void down_pass(const T* act, const void* bt, int F, int D, int
     const int s = min(p0 + t * 16 + fr, cnt - 1);
     arow[t] = act + static_cast<int64_t>(beg + s) * F + fk;
   }
+  static_assert(!FP8 || GS == 1, "the FP8 stream covers one tile group");
   std::conditional_t<FP8, SplitStream8<kDownGroup, NT, DG_EXP8_KP_DN, DG_EXP8_NS_DN>,
-                     SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN>> sp;
+                     std::conditional_t<GS == 1, SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN, DG_EXP_NS_DN>,
+                                        SplitStream<T, kDownGroup, NT, DG_EXP_KSP_DN2, DG_EXP_NS_DN2, GS>>> sp;
   if constexpr (FP8) sp.run(static_cast<const uint8_t*>(bt), arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
   else sp.run(static_cast<const T*>(bt), arow, F / 32, wave, kExpRot ? blockIdx.x : 0);
-  sp.reduce(red, wave, lane);
-  if (wave == 0) {
+  constexpr int GT = decltype(sp)::kTiles;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) {
+    sp.stash(t, red, wave, lane);
+    float gs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gs[i] = slot_gate[beg + min(p0 + t * 16 + (lane >> 4) * 4 + i, cnt - 1)];
+    // output tile g is summed and stored by wave g % 4
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (g % kExpWaves != wave) continue;
+      const f32x4_t x = sum_partials<GT>(red, g, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = p0 + t * 16 + (lane >> 4) * 4 + i;
-        if (s < cnt) {
-          const float gs = slot_gate[beg + s];
-          float* o = out + static_cast<int64_t>(beg + s) * D + n0 + fr;
-#pragma unroll
-          for (int g = 0; g < kDownGroup; ++g) o[g * 16] = gs * (FP8 ? sp.acc[g][t][i] * scl[g] : sp.acc[g][t][i]);
-        }
+        if (s < cnt) out[static_cast<int64_t>(beg + s) * D + n0 + g * 16 + fr] = gs[i] * (FP8 ? x[i] * scl[g] : x[i]);
       }
+    }
+    __syncthreads();  // red is reused by the next tile or pass
   }
-  __syncthreads();
 }
 
-// Grid: E * (D / (16 kDownGroup)) workgroups of 4 waves; block q of expert e owns output group q.
-template <typename T>
+// Grid: E * (D / (16 kDownGroup GS)) workgroups of 4 waves; block q of expert e owns output groups
+// GS q .. GS q + GS - 1.
+template <typename T, int GS>
 __global__ __launch_bounds__(256) void expert_down_kernel(
     const T* __restrict__ act, const T* __restrict__ w_down, int E, int F, int D, int per_e,
     const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate, float* __restrict__ out) {
-  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
+  __shared__ f32x4_t red[kExpWaves * GS * kDownGroup * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, nullptr, &e, &q);
   const int beg = offsets[e], cnt = offsets[e + 1] - beg;
   if (cnt == 0) return;
   const int KT = F / 32;
-  const T* bt = w_down + static_cast<int64_t>(e) * D * F + static_cast<int64_t>(q) * KT * kDownGroup * kTileElems +
-                lane * 8;
-  const int n0 = q * kDownGroup * 16;
+  const T* bt = w_down + static_cast<int64_t>(e) * D * F +
+                static_cast<int64_t>(q) * GS * KT * kDownGroup * kTileElems + lane * 8;
+  const int n0 = q * GS * kDownGroup * 16;
   for (int p0 = 0; p0 < cnt; p0 += 16 * kExpMaxNT)
     with_token_tiles(cnt - p0, [&](auto nt) {
-      down_pass<T, decltype(nt)::value, false>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane, red,
-                                               nullptr);
+      down_pass<T, decltype(nt)::value, false, GS>(act, bt, F, D, beg, cnt, p0, slot_gate, out, n0, wave, lane,
+                                                   red, nullptr);
     });
 }
 
@@ -670,7 +717,7 @@ __global__ __launch_bounds__(256) void expert_down_fp8_kernel(
     const bf16_t* __restrict__ act, const uint8_t* __restrict__ q_down, const float* __restrict__ sc, int E, int F,
     int D, int per_e, const int32_t* __restrict__ offsets, const float* __restrict__ slot_gate,
     float* __restrict__ out) {
-  __shared__ f32x4_t red[(kExpWaves - 1) * kDownGroup * kExpMaxNT * 64];
+  __shared__ f32x4_t red[kExpWaves * kDownGroup * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, q;
   expert_of_block(blockIdx.x, per_e, E, nullptr, &e, &q);
@@ -988,33 +1035,52 @@ int moe_experts(const void* h, int64_t ldh, const void* w_gu, const void* w_down
   }
   {
     ProfScope ps("expert_gateup", s);
+    // two groups per workgroup where the features split evenly (bf16 only: fp32 fragments take
+    // twice the registers)
+    constexpr bool kTwoGu = DG_EXP_GS_GU == 2;
+    const bool two = kTwoGu && dtype == DG_BF16 && F % (32 * kGuBlocks) == 0;
+    const dim3 g(two ? g1.x / 2 : g1.x);
+    const int per = two ? per_gu / 2 : per_gu;
     if (dtype == DG_BF16) {
       const bf16_t* hh = static_cast<const bf16_t*>(h);
       const bf16_t* w = static_cast<const bf16_t*>(w_gu);
       bf16_t* a = static_cast<bf16_t*>(act);
-      if (gated) expert_gateup_kernel<bf16_t, true><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
-                          offsets, perm, a);
-      else expert_gateup_kernel<bf16_t, false><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
-                          offsets, perm, a);
+      if constexpr (kTwoGu) {
+        if (two) {
+          if (gated) expert_gateup_kernel<bf16_t, true, 2><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
+          else expert_gateup_kernel<bf16_t, false, 2><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
+        }
+      }
+      if (!two) {
+        if (gated) expert_gateup_kernel<bf16_t, true, 1><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
+        else expert_gateup_kernel<bf16_t, false, 1><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
+      }
     } else {
       const float* hh = static_cast<const float*>(h);
       const float* w = static_cast<const float*>(w_gu);
       float* a = static_cast<float*>(act);
-      if (gated) expert_gateup_kernel<float, true><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
-                          offsets, perm, a);
-      else expert_gateup_kernel<float, false><<<g1, dim3(256), 0, s>>>(hh, ldh, w, E, F, D, per_gu,
-                          offsets, perm, a);
+      if (gated) expert_gateup_kernel<float, true, 1><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
+      else expert_gateup_kernel<float, false, 1><<<g, 256, 0, s>>>(hh, ldh, w, E, F, D, per, offsets, perm, a);
     }
   }
   DG_LAUNCH_CHECK("expert_gateup_kernel");
   {
     ProfScope ps("expert_down", s);
-    if (dtype == DG_BF16)
-      expert_down_kernel<bf16_t><<<g2, 256, 0, s>>>(static_cast<const bf16_t*>(act),
-          static_cast<const bf16_t*>(w_down), E, F, D, per_dn, offsets, slot_gate, out);
-    else
-      expert_down_kernel<float><<<g2, 256, 0, s>>>(static_cast<const float*>(act),
-          static_cast<const float*>(w_down), E, F, D, per_dn, offsets, slot_gate, out);
+    constexpr bool kTwoDn = DG_EXP_GS_DN == 2;
+    const bool two = kTwoDn && dtype == DG_BF16 && D % (32 * kDownGroup) == 0;
+    const dim3 g(two ? g2.x / 2 : g2.x);
+    const int per = two ? per_dn / 2 : per_dn;
+    if (dtype == DG_BF16) {
+      const bf16_t* a = static_cast<const bf16_t*>(act);
+      const bf16_t* w = static_cast<const bf16_t*>(w_down);
+      if constexpr (kTwoDn) {
+        if (two) expert_down_kernel<bf16_t, 2><<<g, 256, 0, s>>>(a, w, E, F, D, per, offsets, slot_gate, out);
+      }
+      if (!two) expert_down_kernel<bf16_t, 1><<<g, 256, 0, s>>>(a, w, E, F, D, per, offsets, slot_gate, out);
+    } else {
+      expert_down_kernel<float, 1><<<g, 256, 0, s>>>(static_cast<const float*>(act),
+          static_cast<const float*>(w_down), E, F, D, per, offsets, slot_gate, out);
+    }
   }
   DG_LAUNCH_CHECK("expert_down_kernel");
   return DG_OK;
