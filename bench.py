@@ -229,41 +229,28 @@ def bench_full(args):
     counters = {"steps": 0, "commits": 0, "stopped": 0}
 
     def run(n_steps, block0):
-        """n_steps denoising steps; a canvas ends at its stop or after S steps and is then committed."""
-        s, block = 0, block0
-        st.init(sched, block)
-        for _ in range(n_steps):
-            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
-            model.denoise_step(st.canvas, s, *prev, logits=logits)
-            st.sample(logits, sched, s, block)
-            stop = st.stop.cpu()  # the 16-byte stop-state read-back of the loop
-            counters["steps"] += 1
-            s += 1
-            if int(stop[2]) or s == S:
-                counters["stopped"] += int(stop[2])
+        """n_steps denoising steps; a canvas ends at its stop or after S steps and is then committed.
+        The 16-byte stop state of a step is read back whenever that step could have stopped
+        (Model.denoise_canvas)."""
+        block, left = block0, n_steps
+        while left > 0:
+            steps, stopped = model.denoise_canvas(st, sched, block, limit=left, logits=logits)
+            counters["steps"] += steps
+            left -= steps
+            if stopped or steps == S:
+                counters["stopped"] += int(stopped)
                 block_ids.copy_(st.pred)
                 model.commit(block_ids)
                 counters["commits"] += 1
                 block += 1
-                s = 0
-                st.init(sched, block)
         return block
 
     def one_canvas(block):
         """One canvas from its init to its stop (or S steps), then its commit: the pages' unit of output."""
-        s = 0
-        st.init(sched, block)
-        while True:
-            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
-            model.denoise_step(st.canvas, s, *prev, logits=logits)
-            st.sample(logits, sched, s, block)
-            stop = st.stop.cpu()
-            s += 1
-            if int(stop[2]) or s == S:
-                break
+        steps, stopped = model.denoise_canvas(st, sched, block, logits=logits)
         block_ids.copy_(st.pred)
         model.commit(block_ids)
-        return s, int(stop[2])
+        return steps, int(stopped)
 
     log(f"[bench] warmup {args.warmup}")
     blk = run(args.warmup, 0)
@@ -453,20 +440,11 @@ def bench_blockar(args):
     block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
 
     def canvas(block, max_steps, commit):
-        st.init(sched, block)
-        s = 0
-        while True:
-            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
-            model.denoise_step(st.canvas, s, *prev, logits=logits)
-            st.sample(logits, sched, s, block)
-            stop = st.stop.cpu()
-            s += 1
-            if int(stop[2]) or s == max_steps:
-                break
+        steps, stopped = model.denoise_canvas(st, sched, block, limit=max_steps, logits=logits)
         if commit:
             block_ids.copy_(st.pred)
             model.commit(block_ids)
-        return s, int(stop[2])
+        return steps, int(stopped)
 
     log(f"[bench] warmup {args.warmup} steps (not committed)")
     canvas(0, max(1, args.warmup), False)
@@ -561,21 +539,16 @@ def bench_tiny(args):
     st = SamplerState(C, V)
     logits = model.logits
     block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
-    state = {"s": 0, "block": 0}
+    state = {"block": 0}
 
     def run(n):
-        """n steps of canvases over the 64-token prompt (a canvas restarts after its stop or S steps)."""
-        for _ in range(n):
-            s = state["s"]
-            if s == 0:
-                st.init(sched, state["block"])
-            prev = (logits, st.row_stats, L.dg_temperature(sched, s - 1)) if s > 0 else (None, None, 0.0)
-            model.denoise_step(st.canvas, s, *prev, logits=logits)
-            st.sample(logits, sched, s, state["block"])
-            stop = st.stop.cpu()
-            state["s"] = s + 1
-            if int(stop[2]) or state["s"] == S:
-                state.update(s=0, block=state["block"] + 1)
+        """n steps of canvases over the 64-token prompt (a canvas restarts after its stop or S steps;
+        a canvas cut short by n starts afresh on the next call)."""
+        left = n
+        while left > 0:
+            steps, _ = model.denoise_canvas(st, sched, state["block"], limit=left, logits=logits)
+            left -= steps
+            state["block"] += 1
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -584,7 +557,6 @@ def bench_tiny(args):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     # one canvas from init to its end plus its commit, timed on its own (the context then grows by it)
-    state["s"] = 0
     t1 = time.perf_counter()
     run(S)
     block_ids.copy_(st.pred)

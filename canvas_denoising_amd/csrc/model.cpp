@@ -334,6 +334,11 @@ struct dg_ctx {
   dg::StepGraph graphs[2];
   int last_layer = 0;  // layer of the last routing (DG_BUF_SEL / DG_BUF_GATE)
   int64_t captures = 0;  // step graphs captured so far
+  // dg_generate_block's read-back of the stop state: one pinned host slot and one event per step in
+  // flight
+  static constexpr int kStopSlots = 16;
+  dg_stop_state* stop_host = nullptr;
+  hipEvent_t stop_ev[kStopSlots] = {};
 };
 
 namespace dg {
@@ -787,10 +792,17 @@ int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_
   if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
+      hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess ||
+      hipHostMalloc(reinterpret_cast<void**>(&c->stop_host), sizeof(dg_stop_state) * dg_ctx::kStopSlots,
+                    hipHostMallocDefault) != hipSuccess) {
     dg_ctx_destroy(c);
-    return fail(DG_ERR_HIP, "could not create the context's stream and events");
+    return fail(DG_ERR_HIP, "could not create the context's streams, events and pinned stop slots");
   }
+  for (hipEvent_t& e : c->stop_ev)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      dg_ctx_destroy(c);
+      return fail(DG_ERR_HIP, "could not create the stop read-back events");
+    }
   *out = c;
   return DG_OK;
 }
@@ -804,6 +816,9 @@ int dg_ctx_destroy(dg_ctx* ctx) {
     if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
+    for (hipEvent_t e : ctx->stop_ev)
+      if (e) (void)hipEventDestroy(e);
+    if (ctx->stop_host) (void)hipHostFree(ctx->stop_host);
   }
   delete ctx;
   return DG_OK;
@@ -901,21 +916,51 @@ int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d
   float* stats = wsp<float>(ctx, w.row_stats);
   dg_stop_state* stop = wsp<dg_stop_state>(ctx, w.stop);
   DG_TRY(launch_init_canvas(sched->seed, block, C, ctx->d.vocab, canvas, stop, s));
-  int steps = 0;
+  // Each step's stop state is copied to a pinned slot behind the step. The host reads a step's copy
+  // only when that step could have stopped: under the two-fold rule the stable count starts at 0 on
+  // step 0 and grows by at most one a step, so a step whose count cannot have reached stable_needed
+  // cannot stop, and the next step is launched without waiting for it (the device never idles
+  // between such steps). With the either-condition rule every step could stop and is read.
+  const bool either = (sched->mode & DG_SCHED_STOP_EITHER) != 0;
+  int known = -1, c_known = 0;  // the last step read, and its stable count
+  auto could_stop = [&](int j) {
+    const int cap = known < 0 ? j : c_known + (j - known);  // most the stable count can be at step j
+    return either || cap >= sched->stable_needed;
+  };
+  int enq = 0, steps = 0;
+  bool stopped = false;
   float prev_t = 0.f;
-  for (int step = 0; step < sched->max_steps; ++step) {
+  while (!stopped) {
+    // the earliest unread step that could have stopped must be read before another step starts;
+    // so must the oldest one when every slot holds an unread step
+    int j = known + 1;
+    while (j < enq && !could_stop(j)) ++j;
+    if (j == enq && enq - known > dg_ctx::kStopSlots - 1) j = known + 1;
+    if (j < enq) {
+      DG_HIP(hipEventSynchronize(ctx->stop_ev[j % dg_ctx::kStopSlots]));
+      const dg_stop_state& st = ctx->stop_host[j % dg_ctx::kStopSlots];
+      known = j;
+      c_known = st.stable_count;
+      if (st.stopped) {
+        stopped = true;
+        steps = j + 1;
+      }
+      continue;
+    }
+    if (enq == sched->max_steps) break;
+    const int step = enq;
     const float T = temperature(*sched, step);
     DG_TRY(denoise(ctx, canvas, step > 0 ? d_logits : nullptr, stats, prev_t, d_logits, s));
     DG_TRY(launch_sample(d_logits, ctx->d.dtype, C, ctx->d.vocab, T, *sched, step, block, canvas, pred,
                          wsp<uint8_t>(ctx, w.accept), wsp<float>(ctx, w.entropy), stats, stop,
                          wsp<void>(ctx, w.samp), s));
-    dg_stop_state host;
-    DG_HIP(hipMemcpyAsync(&host, stop, sizeof host, hipMemcpyDeviceToHost, s));
-    DG_HIP(hipStreamSynchronize(s));
-    steps = step + 1;
+    DG_HIP(hipMemcpyAsync(&ctx->stop_host[step % dg_ctx::kStopSlots], stop, sizeof(dg_stop_state),
+                          hipMemcpyDeviceToHost, s));
+    DG_HIP(hipEventRecord(ctx->stop_ev[step % dg_ctx::kStopSlots], s));
     prev_t = T;
-    if (host.stopped) break;
+    ++enq;
   }
+  if (!stopped) steps = enq;  // max_steps ran; none of them stopped
   DG_HIP(hipMemcpyAsync(d_block_out, pred, C * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
   if (steps_out) *steps_out = steps;
   if (commit) DG_TRY(encode(ctx, d_block_out, C, s));

@@ -165,3 +165,47 @@ class Model:
 
     def generate_block(self, sched, block, block_out, commit=True) -> int:
         return L.dg_generate_block(self.ctx, sched, block, self.logits, block_out, commit)
+
+    _STOP_SLOTS = 16
+
+    def denoise_canvas(self, st, sched, block, limit=None, logits=None):
+        """Denoising steps of one canvas, from its initial state, until it stops or `limit` steps ran
+        (at most sched.max_steps); returns (steps, stopped). Each step's stop state is copied to a
+        pinned slot behind the step, and the host reads a step's copy only when that step could have
+        stopped: under the two-fold rule the stable count is 0 on step 0 and grows by at most one a
+        step, so steps whose count cannot have reached stable_needed are launched back to back."""
+        out = self.logits if logits is None else logits
+        n = sched.max_steps if limit is None else min(limit, sched.max_steps)
+        if not hasattr(self, "_stop_host"):
+            self._stop_host = torch.zeros(self._STOP_SLOTS, 4, dtype=torch.int32, pin_memory=True)
+            self._stop_ev = [torch.cuda.Event() for _ in range(self._STOP_SLOTS)]
+        host, ev, k = self._stop_host, self._stop_ev, self._STOP_SLOTS
+        either = (sched.mode & L.DG_SCHED_STOP_EITHER) != 0
+        st.init(sched, block)
+        known, c_known, enq = -1, 0, 0
+        while True:
+            j = known + 1
+            while j < enq:
+                cap = j if known < 0 else c_known + (j - known)  # most the stable count can be at step j
+                if either or cap >= sched.stable_needed:
+                    break
+                j += 1
+            if j == enq and enq - known > k - 1:
+                j = known + 1
+            if j < enq:
+                ev[j % k].synchronize()
+                known, c_known = j, int(host[j % k, 1])
+                if int(host[j % k, 2]):
+                    return j + 1, True
+                continue
+            if enq == n:
+                return enq, False
+            s = enq
+            if s > 0:
+                self.denoise_step(st.canvas, s, out, st.row_stats, L.dg_temperature(sched, s - 1), logits=out)
+            else:
+                self.denoise_step(st.canvas, s, logits=out)
+            st.sample(out, sched, s, block)
+            host[s % k].copy_(st.stop, non_blocking=True)
+            ev[s % k].record()
+            enq += 1

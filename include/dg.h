@@ -349,15 +349,15 @@ size_t dg_workspace_size(const dg_model_desc* desc, int64_t capacity);
 /* Create a context over caller-owned weights, KV cache and workspace (none is
  * copied; all must outlive the context). Zero-fills the workspace and the KV
  * cache, fills the rotary table when rope_theta > 0 (blocking, on the default
- * stream) and creates two streams and two
- * events of its own (default priority). capacity = KV positions, a multiple
+ * stream) and creates two streams, events and 256 bytes of pinned host
+ * memory of its own (default priority). capacity = KV positions, a multiple
  * of 32. The committed length starts at 0. Limits: canvas <= 256, head_dim
  * 64 or 128 (bf16), d_model, head dims, FFN widths and vocab multiples of
  * 64, n_experts <= 256, top_k <= 16. */
 int dg_ctx_create(const dg_model_desc* desc, void* d_weights, void* d_kv, int64_t capacity,
                   void* d_workspace, size_t ws_bytes, dg_ctx** out);
-/* Waits for the device, then frees the context's own stream, events and
- * graphs (never the caller's buffers). */
+/* Waits for the device, then frees the context's own streams, events, pinned
+ * host slots and graphs (never the caller's buffers). */
 int dg_ctx_destroy(dg_ctx* ctx);
 /* Graph replay of the denoising step (default on): the launches of a step are
  * captured into a HIP graph once per (d_canvas, d_logits, d_prev_logits,
@@ -424,11 +424,16 @@ int dg_forward_layer(dg_ctx* ctx, int32_t layer, float* d_x, int32_t rows, int32
 /* Native denoising loop of one canvas ([P4] "Reverse diffusion process" and
  * "Two-Fold Adaptive Stopping"): dg_init_canvas, then for step = 0 ..
  * max_steps-1: dg_denoise_step (self-conditioned on the previous step),
- * dg_sample_canvas, and a 16-byte read-back of the stop state; the block is
- * the final step's argmax, copied to d_block_out (int32[canvas]); with
- * commit != 0 it is then committed. d_logits: [canvas x vocab] caller
- * scratch. *steps_out (host) receives the number of steps run. Blocks the
- * calling thread on `stream` once per step. */
+ * dg_sample_canvas, and a 16-byte copy of the stop state into a pinned host
+ * slot of the context; the block is the final step's argmax, copied to
+ * d_block_out (int32[canvas]); with commit != 0 it is then committed.
+ * d_logits: [canvas x vocab] caller scratch. *steps_out (host) receives the
+ * number of steps run. The calling thread waits for a step's copy only when
+ * that step could have stopped: the stable count is 0 on step 0 and grows by
+ * at most one a step, so under the two-fold rule a step whose count cannot
+ * have reached stable_needed cannot stop, and the next step is queued behind
+ * it without waiting (with DG_SCHED_STOP_EITHER every step is waited for). No
+ * step after the stopping one is launched. */
 int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d_logits,
                       int32_t* d_block_out, int32_t commit, int32_t* steps_out, void* stream);
 

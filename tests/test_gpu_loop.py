@@ -184,3 +184,65 @@ def test_tiny_config_trajectory(libs):
     assert_close(to_f64(gk[0, :, :model.length]), cache.k[0][:, :model.length], 2e-4, "committed K")
     assert_close(to_f64(gv[0, :, :model.length]), cache.v[0][:, :model.length], 2e-4, "committed V")
     model.close()
+
+
+@pytest.mark.parametrize("stable_needed,mode", [(3, 0), (2, 0), (0, 0), (3, 1)])
+def test_pipelined_loops_stop_where_the_step_loop_stops(libs, stable_needed, mode):
+    """The Python runtime's denoise_canvas and the native dg_generate_block read a step's stop state
+    only when that step could have stopped ([P4] "Two-Fold Adaptive Stopping": the stable count is 0
+    on step 0 and grows by one a step at most), launching the other steps back to back. With all
+    weights zero every row's logits are equal, so the argmax (lowest index) never changes and the
+    stable count is the step index; with a mean-entropy threshold above ln V the two-fold rule stops
+    the canvas on step stable_needed (either rule: on step 0). Both loops must stop on that step,
+    run no step after it, and leave the state the step-by-step loop (a read-back after every step)
+    leaves."""
+    L, configs, runtime = libs
+    w = configs.tiny_f32()
+    d = w.desc
+    C, V, S = d.canvas, d.vocab, w.max_steps
+    announce(f"pipelined stop read-back: stable_needed {stable_needed}, mode {mode}")
+    model = runtime.Model(d, w.capacity, seed=None)
+    model.weights.zero_()
+    model.prefill(ids_tensor(1, w.prompt, V))
+    sched = L.make_sched(max_steps=S, seed=0, stop_mean_entropy=1e9, stable_needed=stable_needed,
+                         mode=L.DG_SCHED_STOP_EITHER if mode else 0)
+    want = 1 if mode else stable_needed + 1
+    assert want < S
+    st = runtime.SamplerState(C, V)
+    logits = model.logits
+
+    # the step-by-step loop
+    st.init(sched, 0)
+    s = 0
+    while True:
+        if s > 0:
+            model.denoise_step(st.canvas, s, logits, st.row_stats, L.dg_temperature(sched, s - 1), logits=logits)
+        else:
+            model.denoise_step(st.canvas, s, logits=logits)
+        st.sample(logits, sched, s, 0)
+        stop = st.stop_state()
+        s += 1
+        if stop["stopped"] or s == S:
+            break
+    assert s == want and stop["stopped"] == 1 and stop["steps_run"] == want
+    ref = dict(pred=st.pred.clone(), canvas=st.canvas.clone(), logits=logits.clone(), stop=stop)
+
+    # the runtime's pipelined loop
+    logits.fill_(float("nan"))
+    steps, stopped = model.denoise_canvas(st, sched, 0)
+    torch.cuda.synchronize()
+    assert (steps, stopped) == (want, True)
+    assert st.stop_state() == ref["stop"]
+    assert torch.equal(st.pred, ref["pred"]) and torch.equal(st.canvas, ref["canvas"])
+    assert torch.equal(logits, ref["logits"])
+
+    # the native loop
+    logits.fill_(float("nan"))
+    out = torch.empty(C, dtype=torch.int32, device="cuda")
+    n = model.generate_block(sched, 0, out, commit=False)
+    torch.cuda.synchronize()
+    assert n == want
+    assert torch.equal(out, ref["pred"])
+    assert torch.equal(logits, ref["logits"])
+    assert runtime.stop_dict(model.buffer(L.DG_BUF_STOP, torch.int32, (4,))) == ref["stop"]
+    model.close()
