@@ -105,13 +105,14 @@ __global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const float* __restri
 // Residual update fused with the next RMSNorm, one workgroup per row, the row in registers
 // (thread t holds float4 columns t, t + 256, ...; D % 4 == 0, D <= 1024 NV):
 //   x[m] += sum_z part[z][m]                                  (z = 0 .. splits-1, in order)
-//   x[m] += y[m] + sum_j slot_out[slot_of[m k + j]]           (when y != null; j in order)
+//   x[m] += y[m] + sum_j slot_out[slot_of[m k + j]]           (when y != null; j in order; y[m] is
+//                                                              the in-order sum of y_planes planes)
 //   h[m]  = x[m] / sqrt(mean(x[m]^2) + eps)                   (fixed-order block sum)
 // The first line folds the split-K partials of a GEMM whose epilogue adds into x; the second is the
 // MoE combine (shared expert, then the token's gated routed outputs).
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ x, const float* __restrict__ part,
-                                                            int splits, const float* __restrict__ y,
+                                                            int splits, const float* __restrict__ y, int y_planes,
                                                             const float* __restrict__ slot_out,
                                                             const int32_t* __restrict__ slot_of, int k,
                                                             T* __restrict__ h, int M, int D, float eps) {
@@ -168,6 +169,12 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
       const int c = tid + 256 * i;
       t[i] = c < n4 ? y4[static_cast<int64_t>(m) * n4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    for (int p = 1; p < y_planes; ++p)  // y given as split partials: y = y[0] + y[1] + ... (in order)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = tid + 256 * i;
+        if (c < n4) add4(t[i], y4[p * plane + static_cast<int64_t>(m) * n4 + c]);
+      }
     for (int j0 = 0; j0 < k; j0 += B) {
       int sl[B];
 #pragma unroll
@@ -284,16 +291,17 @@ int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStre
 
 int residual_norm(float* x, const float* part, int splits, const float* y, const float* slot_out,
                   const int32_t* slot_of, int k, void* h, int M, int D, float eps, int dtype, hipStream_t s,
-                  const char* name) {
+                  const char* name, int y_planes) {
+  if (y_planes < 1) return fail(DG_ERR_INVALID, "residual_norm: y_planes must be >= 1");
   constexpr int kNV = 3;
   if (D % 4 != 0 || D > 1024 * kNV || k > 16)
     return fail(DG_ERR_UNSUPPORTED, "residual_norm: d_model must be <= 3072 and a multiple of 4, top_k <= 16");
   ProfScope ps(name, s);
   if (dtype == DG_BF16)
-    residual_norm_kernel<bf16_t, kNV><<<M, 256, 0, s>>>(x, part, splits, y, slot_out, slot_of, k,
+    residual_norm_kernel<bf16_t, kNV><<<M, 256, 0, s>>>(x, part, splits, y, y_planes, slot_out, slot_of, k,
                                                        static_cast<bf16_t*>(h), M, D, eps);
   else
-    residual_norm_kernel<float, kNV><<<M, 256, 0, s>>>(x, part, splits, y, slot_out, slot_of, k,
+    residual_norm_kernel<float, kNV><<<M, 256, 0, s>>>(x, part, splits, y, y_planes, slot_out, slot_of, k,
                                                       static_cast<float*>(h), M, D, eps);
   DG_LAUNCH_CHECK("residual_norm_kernel");
   return DG_OK;

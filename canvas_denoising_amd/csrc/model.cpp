@@ -33,7 +33,7 @@ int embed(const void* emb, const int32_t* ids, const float* sc, float* x, int M,
 int rmsnorm(const float* x, void* h, int M, int D, float eps, int dtype, hipStream_t s);
 int residual_norm(float* x, const float* part, int splits, const float* y, const float* slot_out,
                   const int32_t* slot_of, int k, void* h, int M, int D, float eps, int dtype, hipStream_t s,
-                  const char* name);
+                  const char* name, int y_planes = 1);
 int transpose(const void* in, int64_t R, int64_t C, int gr, int gr_out, void* out, int dtype, hipStream_t s);
 int sc_embed_splits(int N, int64_t K, int dtype);
 int sc_embed(const void* logits, int64_t ldl, const float* stats, const float* temp, const void* Et, int M, int N,
@@ -370,6 +370,12 @@ static int run_gemm(dg_ctx* c, GemmArgs g, hipStream_t s, const char* name, bool
 #ifndef DG_FUSED_NORM
 #define DG_FUSED_NORM 1
 #endif
+// the shared expert's down projection leaves its split-K partials to the combine instead of reducing
+// them in a kernel of its own on the second stream
+#ifndef DG_SHARED_DEFER
+#define DG_SHARED_DEFER 1
+#endif
+constexpr bool kSharedDeferReduce = DG_SHARED_DEFER;
 static bool fused_norm_ok(const dg_model_desc& d) {
   return DG_FUSED_NORM && d.d_model % 4 == 0 && d.d_model <= 3072;
 }
@@ -424,7 +430,9 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, const int*
     else
       DG_TRY(rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s));
   }
-  // the shared expert: h -> y_sh
+  // the shared expert: h -> y_sh, or (fused combine) its down projection's split-K partials, which
+  // the combine sums as the shared term (sh_planes of them, in order)
+  int sh_planes = 1;
   auto shared = [&](hipStream_t st, bool on_aux) -> int {
     {
       GemmArgs g;
@@ -440,6 +448,8 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, const int*
     g.B = wp(c, c->wl.sh_down[l]); g.ldb = d.d_shared;
     g.M = M; g.N = D; g.K = d.d_shared;
     g.epi = EPI_STORE_F32; g.out = wsp<float>(c, w.y_sh); g.ldo = D;
+    g.defer_reduce = fused && kSharedDeferReduce;
+    g.splits_out = &sh_planes;
     return run_gemm(c, g, st, "shared_down", true, on_aux);
   };
   // The shared expert runs on the second stream beside the routing and the routed experts (both
@@ -483,9 +493,12 @@ static int layer_forward(dg_ctx* c, int l, float* x, int M, int pos0, const int*
   DG_HIP(hipEventRecord(c->ev_join, c->aux));
   // join, then x += shared + sum of the token's gated expert outputs (fixed order); h = RMSNorm(x)
   DG_HIP(hipStreamWaitEvent(s, c->ev_join, 0));
-  if (fused)
-    return residual_norm(x, nullptr, 0, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of),
-                         d.top_k, h, M, D, d.rms_eps, d.dtype, s, "combine_norm");
+  if (fused) {
+    const bool planes = kSharedDeferReduce && sh_planes > 1;
+    return residual_norm(x, nullptr, 0, planes ? wsp<float>(c, w.gpart_aux) : wsp<float>(c, w.y_sh),
+                         wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of), d.top_k, h, M, D, d.rms_eps, d.dtype,
+                         s, "combine_norm", planes ? sh_planes : 1);
+  }
   DG_TRY(moe_combine(x, wsp<float>(c, w.y_sh), wsp<float>(c, w.slot_out), wsp<int32_t>(c, w.slot_of), M, D,
                      d.top_k, s));
   return rmsnorm(x, h, M, D, d.rms_eps, d.dtype, s);
