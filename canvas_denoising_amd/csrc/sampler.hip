@@ -15,9 +15,9 @@
 //   m = max(m1, m2), d_i = (m_i - m) log2(e)/T,
 //   Z = Z1 2^d1 + Z2 2^d2,  A = 2^d1 (A1 + d1 Z1) + 2^d2 (A2 + d2 Z2),
 // and the row entropy is H = ln Z - ln2 * A / Z, so no second read is needed.
-// The argmax is not tracked per element: each thread remembers the batch in
-// which its running maximum first appeared and, if that maximum is the
-// chunk's, re-reads that one batch to find the lowest index holding it.
+// Each thread keeps the first position of its running maximum (the values of
+// a batch are compared in increasing index order), so the chunk's argmax is
+// the lowest of the positions of the threads holding the chunk maximum.
 //
 // A second, single-workgroup kernel merges each row's records in a fixed
 // order (a quad of threads per row), applies the accept / Philox re-noise
@@ -153,12 +153,21 @@ template <typename T> __device__ inline float load1(const T* p);
 template <> __device__ inline float load1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 template <> __device__ inline float load1<float>(const float* p) { return *p; }
 
-// fold N values into the running (m, z, a); returns true when the running max grew
+// fold N values into the running (m, z, a); returns true when the running max grew. With `pos`,
+// *pos receives the first j holding the values' maximum (values in increasing index order).
 template <int N>
-__device__ inline bool fold(const float* v, float c, Rec& r) {
+__device__ inline bool fold(const float* v, float c, Rec& r, int* pos = nullptr) {
   float bm = v[0];
+  if (pos) {
+    int bj = 0;
 #pragma unroll
-  for (int j = 1; j < N; ++j) bm = fmaxf(bm, v[j]);
+    for (int j = 1; j < N; ++j)
+      if (v[j] > bm) { bm = v[j]; bj = j; }
+    *pos = bj;
+  } else {
+#pragma unroll
+    for (int j = 1; j < N; ++j) bm = fmaxf(bm, v[j]);
+  }
   bool grew = false;
   if (bm > r.m) {
     if (r.z != 0.f) {
@@ -241,7 +250,6 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
     // whole batches, software-pipelined: batch b+1 is loaded while batch b is folded
     const int64_t nb = (end - begin) / kBatch;
     const T* tp = p + begin + static_cast<int64_t>(tid) * kVec;
-    int64_t first = -1;  // batch where this thread's running max first appeared
     float gs = -INFINITY;  // categorical: best Gumbel score of this thread and its index
     int gi = 0x7FFFFFFF;
     auto gumbel_batch = [&](const float* v, int64_t b) {
@@ -250,6 +258,11 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
         gumbel_fold8(g, row, begin + b * kBatch + static_cast<int64_t>(tid) * kVec + u * kSampThreads * kVec,
                      v + u * kVec, gs, gi);
     };
+    // element j of a thread's batch b is token begin + b kBatch + (j / 8) 2048 + 8 tid + j % 8
+    auto token = [&](int64_t b, int j) {
+      return static_cast<int>(begin + b * kBatch + (j / kVec) * kSampThreads * kVec + static_cast<int64_t>(tid) * kVec +
+                              (j % kVec));
+    };
     Raw<T> qa, qb;
     if (nb > 0) qa.load(tp);
     for (int64_t b = 0; b < nb; b += 2) {
@@ -257,20 +270,21 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
       {
         float v[kUnroll * kVec];
         qa.unpack(v);
-        if (fold<kUnroll * kVec>(v, c, r)) first = b;
+        int j;
+        if (fold<kUnroll * kVec>(v, c, r, &j)) r.idx = token(b, j);
         if constexpr (CAT) gumbel_batch(v, b);
       }
       if (b + 1 < nb) {
         if (b + 2 < nb) qa.load(tp + (b + 2) * kBatch);
         float v[kUnroll * kVec];
         qb.unpack(v);
-        if (fold<kUnroll * kVec>(v, c, r)) first = b + 1;
+        int j;
+        if (fold<kUnroll * kVec>(v, c, r, &j)) r.idx = token(b + 1, j);
         if constexpr (CAT) gumbel_batch(v, b + 1);
       }
     }
     // tail: whole groups of 8 (vocab % 8 == 0 on this path), index tracked directly
     const int64_t tail0 = begin + nb * kBatch;
-    int tail_idx = 0x7FFFFFFF;
     for (int64_t e0 = tail0 + static_cast<int64_t>(tid) * kVec; e0 < end; e0 += static_cast<int64_t>(kSampThreads) * kVec) {
       float v[kVec];
       if constexpr (sizeof(T) == 2) {
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
 #pragma unroll
       for (int j = 1; j < kVec; ++j)
         if (v[j] > bm) { bm = v[j]; bj = j; }
-      if (fold<kVec>(v, c, r)) { first = -1; tail_idx = static_cast<int>(e0 + bj); }
+      if (fold<kVec>(v, c, r)) r.idx = static_cast<int>(e0 + bj);
       if constexpr (CAT) gumbel_fold8(g, row, e0, v, gs, gi);
     }
     if constexpr (CAT) {  // the chunk's best Gumbel score: wave (DPP / row swaps), then the 4 waves
@@ -314,23 +328,10 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
     Rec tot = sh[0];
 #pragma unroll
     for (int i = 1; i < kSampThreads / 64; ++i) rec_merge(tot, sh[i], c);
-    // argmax: lowest index holding the chunk maximum
-    int my_idx = 0x7FFFFFFF;
-    if (r.z != 0.f && r.m == tot.m) {
-      if (first >= 0) {
-        Raw<T> q;
-        q.load(tp + first * kBatch);
-        float v[kUnroll * kVec];
-        q.unpack(v);
-#pragma unroll
-        for (int j = kUnroll * kVec - 1; j >= 0; --j)
-          if (v[j] == tot.m) my_idx = static_cast<int>(begin + first * kBatch + tid * kVec + (j / kVec) * kSampThreads * kVec + (j % kVec));
-      } else {
-        my_idx = tail_idx;
-      }
-    }
-    my_idx = wave_min_i32(my_idx);
-    if (lane == 0) sh_idx[wave] = my_idx;
+    // argmax: lowest index holding the chunk maximum (each thread kept the first position of its own)
+    const int my_idx = (r.z != 0.f && r.m == tot.m) ? r.idx : 0x7FFFFFFF;
+    const int w_idx = wave_min_i32(my_idx);
+    if (lane == 0) sh_idx[wave] = w_idx;
     __syncthreads();
     if (tid == 0) {
       int bi = sh_idx[0];
