@@ -15,9 +15,11 @@
 //   m = max(m1, m2), d_i = (m_i - m) log2(e)/T,
 //   Z = Z1 2^d1 + Z2 2^d2,  A = 2^d1 (A1 + d1 Z1) + 2^d2 (A2 + d2 Z2),
 // and the row entropy is H = ln Z - ln2 * A / Z, so no second read is needed.
-// Each thread keeps the first position of its running maximum (the values of
-// a batch are compared in increasing index order), so the chunk's argmax is
-// the lowest of the positions of the threads holding the chunk maximum.
+// A batch's maximum is a tree of maxima; each thread notes the batch in which
+// its running maximum was last raised, and once the chunk maximum is known
+// the threads holding it find its first position in that batch (the last two
+// batches are still in registers), so the chunk's argmax is the lowest of
+// those positions.
 //
 // A second, single-workgroup kernel merges each row's records in a fixed
 // order (a quad of threads per row), applies the accept / Philox re-noise
@@ -107,6 +109,14 @@ constexpr int kUnroll = 4;   // groups per thread per batch
 constexpr int kBatch = kSampThreads * kVec * kUnroll;  // elements per workgroup batch
 constexpr int kMaxSplits = 64;
 
+// The two bf16 halves of a 32-bit word as floats, by the bf16 -> f32 conversion (exact, the same
+// bits as a shift): converted values are known to be canonical floats, so the compiler takes their
+// maxima without a quieting step per value.
+__device__ inline float widen_lo(uint32_t w) { return static_cast<float>(__builtin_bit_cast(__bf16, static_cast<uint16_t>(w))); }
+__device__ inline float widen_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(__bf16, static_cast<uint16_t>(w >> 16)));
+}
+
 // raw storage of one thread's batch: kUnroll groups of 8 elements
 template <typename T> struct Raw;
 // The logits are read once: nontemporal loads keep them from displacing reused lines in the caches.
@@ -125,10 +135,10 @@ template <> struct Raw<bf16_t> {
   __device__ inline void unpack(float* v) const {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      v[u * 8 + 0] = bf16lo(q[u].x); v[u * 8 + 1] = bf16hi(q[u].x);
-      v[u * 8 + 2] = bf16lo(q[u].y); v[u * 8 + 3] = bf16hi(q[u].y);
-      v[u * 8 + 4] = bf16lo(q[u].z); v[u * 8 + 5] = bf16hi(q[u].z);
-      v[u * 8 + 6] = bf16lo(q[u].w); v[u * 8 + 7] = bf16hi(q[u].w);
+      v[u * 8 + 0] = widen_lo(q[u].x); v[u * 8 + 1] = widen_hi(q[u].x);
+      v[u * 8 + 2] = widen_lo(q[u].y); v[u * 8 + 3] = widen_hi(q[u].y);
+      v[u * 8 + 4] = widen_lo(q[u].z); v[u * 8 + 5] = widen_hi(q[u].z);
+      v[u * 8 + 6] = widen_lo(q[u].w); v[u * 8 + 7] = widen_hi(q[u].w);
     }
   }
 };
@@ -153,21 +163,35 @@ template <typename T> __device__ inline float load1(const T* p);
 template <> __device__ inline float load1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 template <> __device__ inline float load1<float>(const float* p) { return *p; }
 
-// fold N values into the running (m, z, a); returns true when the running max grew. With `pos`,
-// *pos receives the first j holding the values' maximum (values in increasing index order).
+// largest of N values (N a power of two) by a tree of maxima: exact, so it equals the first
+// maximum of any order
 template <int N>
-__device__ inline bool fold(const float* v, float c, Rec& r, int* pos = nullptr) {
-  float bm = v[0];
-  if (pos) {
-    int bj = 0;
+__device__ inline float max_of(const float* v) {
+  static_assert((N & (N - 1)) == 0, "power of two");
+  float t[N];
 #pragma unroll
-    for (int j = 1; j < N; ++j)
-      if (v[j] > bm) { bm = v[j]; bj = j; }
-    *pos = bj;
-  } else {
+  for (int j = 0; j < N; ++j) t[j] = v[j];
 #pragma unroll
-    for (int j = 1; j < N; ++j) bm = fmaxf(bm, v[j]);
-  }
+  for (int s = N / 2; s >= 1; s /= 2)
+#pragma unroll
+    for (int j = 0; j < s; ++j) t[j] = fmaxf(t[j], t[j + s]);
+  return t[0];
+}
+
+// the first j with v[j] == m, for an m that is one of the N values
+template <int N>
+__device__ inline int first_of(const float* v, float m) {
+  int bj = N - 1;
+#pragma unroll
+  for (int j = N - 2; j >= 0; --j)
+    if (v[j] == m) bj = j;
+  return bj;
+}
+
+// fold N values into the running (m, z, a); returns true when the running max grew
+template <int N>
+__device__ inline bool fold(const float* v, float c, Rec& r) {
+  const float bm = max_of<N>(v);
   bool grew = false;
   if (bm > r.m) {
     if (r.z != 0.f) {
@@ -263,23 +287,24 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
       return static_cast<int>(begin + b * kBatch + (j / kVec) * kSampThreads * kVec + static_cast<int64_t>(tid) * kVec +
                               (j % kVec));
     };
+    // qa holds the even batches, qb the odd ones; bbest is the batch in which this thread's running
+    // maximum was last raised (-1 once the tail raised it: r.idx is then set)
     Raw<T> qa, qb;
+    int64_t bbest = -1;
     if (nb > 0) qa.load(tp);
     for (int64_t b = 0; b < nb; b += 2) {
       if (b + 1 < nb) qb.load(tp + (b + 1) * kBatch);
       {
         float v[kUnroll * kVec];
         qa.unpack(v);
-        int j;
-        if (fold<kUnroll * kVec>(v, c, r, &j)) r.idx = token(b, j);
+        if (fold<kUnroll * kVec>(v, c, r)) bbest = b;
         if constexpr (CAT) gumbel_batch(v, b);
       }
       if (b + 1 < nb) {
         if (b + 2 < nb) qa.load(tp + (b + 2) * kBatch);
         float v[kUnroll * kVec];
         qb.unpack(v);
-        int j;
-        if (fold<kUnroll * kVec>(v, c, r, &j)) r.idx = token(b + 1, j);
+        if (fold<kUnroll * kVec>(v, c, r)) bbest = b + 1;
         if constexpr (CAT) gumbel_batch(v, b + 1);
       }
     }
@@ -300,7 +325,10 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
 #pragma unroll
       for (int j = 1; j < kVec; ++j)
         if (v[j] > bm) { bm = v[j]; bj = j; }
-      if (fold<kVec>(v, c, r)) r.idx = static_cast<int>(e0 + bj);
+      if (fold<kVec>(v, c, r)) {
+        r.idx = static_cast<int>(e0 + bj);
+        bbest = -1;
+      }
       if constexpr (CAT) gumbel_fold8(g, row, e0, v, gs, gi);
     }
     if constexpr (CAT) {  // the chunk's best Gumbel score: wave (DPP / row swaps), then the 4 waves
@@ -328,8 +356,19 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(SampleArgs g) {
     Rec tot = sh[0];
 #pragma unroll
     for (int i = 1; i < kSampThreads / 64; ++i) rec_merge(tot, sh[i], c);
-    // argmax: lowest index holding the chunk maximum (each thread kept the first position of its own)
-    const int my_idx = (r.z != 0.f && r.m == tot.m) ? r.idx : 0x7FFFFFFF;
+    // argmax: lowest index holding the chunk maximum. A thread holding it finds the first position
+    // of its maximum in the batch where that was raised (values in increasing index order, and an
+    // equal value in a later batch did not raise it); the last two batches are still in registers.
+    const bool holds = r.z != 0.f && r.m == tot.m;
+    if (holds && bbest >= 0) {
+      Raw<T> q;
+      if (bbest >= nb - 2) q = (bbest % 2 == 0) ? qa : qb;
+      else q.load(tp + bbest * kBatch);
+      float v[kUnroll * kVec];
+      q.unpack(v);
+      r.idx = token(bbest, first_of<kUnroll * kVec>(v, r.m));
+    }
+    const int my_idx = holds ? r.idx : 0x7FFFFFFF;
     const int w_idx = wave_min_i32(my_idx);
     if (lane == 0) sh_idx[wave] = w_idx;
     __syncthreads();
@@ -533,7 +572,12 @@ struct SplitPlan { int64_t splits, chunk; };
 
 static SplitPlan plan_splits(int64_t rows, int64_t vocab) {
   const int64_t gran = kBatch;  // 8192 elements: whole batches
-  const int64_t target_wgs = 4096;
+// workgroups a call aims at (16 per canvas row at 256 rows); measured on 256 x 262144 bf16 logits,
+// 1024, 2048 and 8192 took 30.5, 29.3 and 35.4 us against 29.0
+#ifndef DG_SAMP_WGS
+#define DG_SAMP_WGS 4096
+#endif
+  const int64_t target_wgs = DG_SAMP_WGS;
   int64_t s = std::max<int64_t>(1, std::min<int64_t>(ceil_div(vocab, gran), ceil_div(target_wgs, rows)));
   s = std::min<int64_t>(s, kMaxSplits);
   int64_t chunk = ceil_div(ceil_div(vocab, s), kVec) * kVec;
