@@ -104,7 +104,7 @@ _SIGS = {
  DG_W_SH_UP, DG_W_SH_DOWN, DG_W_EX_GATE, DG_W_EX_UP, DG_W_EX_DOWN) = range(15)
 (DG_BUF_X, DG_BUF_H, DG_BUF_ROUTER_LOGITS, DG_BUF_SEL, DG_BUF_GATE, DG_BUF_SC, DG_BUF_CANVAS, DG_BUF_PRED,
  DG_BUF_STOP, DG_BUF_ENTROPY, DG_BUF_ROW_STATS, DG_BUF_ACCEPT, DG_BUF_Q, DG_BUF_ATTN, DG_BUF_SHARED_ACT,
- DG_BUF_SLOT_OUT, DG_BUF_SLOT_OF, DG_BUF_SEL_LAYERS) = range(18)
+ DG_BUF_SLOT_OUT, DG_BUF_SLOT_OF, DG_BUF_SEL_LAYERS, DG_BUF_OFFSETS) = range(19)
 
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

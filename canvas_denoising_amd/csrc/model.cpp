@@ -1006,6 +1006,7 @@ int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes)
     case DG_BUF_SHARED_ACT: off = w.sh_act; n = C * d.d_shared * es; break;
     case DG_BUF_SLOT_OUT: off = w.slot_out; n = C * d.top_k * d.d_model * 4; break;
     case DG_BUF_SLOT_OF: off = w.slot_of; n = C * d.top_k * 4; break;
+    case DG_BUF_OFFSETS: off = w.offsets; n = (2 * static_cast<size_t>(d.n_experts) + 1) * 4; break;
     default: return fail(DG_ERR_INVALID, "unknown buffer");
   }
   *d_ptr = ctx->ws + off;

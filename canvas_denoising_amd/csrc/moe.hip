@@ -116,14 +116,29 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   __shared__ uint16_t below[kE * MW];  // tokens of expert e in the mask words before word w
   __shared__ int32_t offs[257];
   __shared__ int32_t toffs[257];
+  __shared__ int32_t cnts[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < E * MW; i += 1024) mask[i] = 0u;
-  __syncthreads();
   // (token, choice) pairs in batches of 8 per thread whose loads are issued together (clamped
-  // indices; surplus pairs are not used)
+  // indices; surplus pairs are not used). The first batch's experts and gates stay in registers for
+  // the slot scatter at the end (a canvas has at most 2048 pairs: one batch covers them all).
   const int np = M * k;
   constexpr int kPB = 8;
-  for (int p0 = tid; p0 < np; p0 += 1024 * kPB) {
+  int ev0[kPB];
+  float gv0[kPB];
+#pragma unroll
+  for (int i = 0; i < kPB; ++i) {
+    const int p = min(tid + 1024 * i, np - 1);
+    ev0[i] = sel[p];
+    gv0[i] = gate[p];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPB; ++i) {
+    const int p = tid + 1024 * i, row = p / k;
+    if (p < np) atomicOr(&mask[ev0[i] * MW + (row >> 5)], 1u << (row & 31));
+  }
+  for (int p0 = tid + 1024 * kPB; p0 < np; p0 += 1024 * kPB) {
     int ev[kPB];
 #pragma unroll
     for (int i = 0; i < kPB; ++i) ev[i] = sel[min(p0 + 1024 * i, np - 1)];
@@ -158,7 +173,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane * 4 + i;
-      if (e < E) { offs[e] = run; toffs[e] = trun; }
+      if (e < E) { offs[e] = run; toffs[e] = trun; cnts[e] = cnt[i]; }
       run += cnt[i];
       trun += (cnt[i] + kTileTokens - 1) / kTileTokens;
     }
@@ -174,21 +189,45 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
   __syncthreads();
   for (int i = tid; i <= E; i += 1024) offsets[i] = offs[i];
-  for (int e = tid; e < E; e += 1024) {
-    const int c = offs[e + 1] - offs[e];
+  // rank of expert e (most tokens first, lower index on ties): 8 threads per expert each count the
+  // experts ahead of it in one eighth of the experts, summed across the 8 lanes
+  constexpr int kSl = 8;
+  const int per = (E + kSl - 1) / kSl;
+  for (int base = 0; base < E * kSl; base += 1024) {
+    const int t = base + tid, e = t / kSl, part = t % kSl;
     int r = 0;
-    for (int f = 0; f < E; ++f) {
-      const int cf = offs[f + 1] - offs[f];
-      r += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    if (e < E) {
+      const int c = cnts[e];
+      const int f1 = min(E, (part + 1) * per);
+      for (int f = part * per; f < f1; ++f) {
+        const int cf = cnts[f];
+        r += (cf > c || (cf == c && f < e)) ? 1 : 0;
+      }
     }
-    offsets[E + 1 + r] = e;
+    r += __shfl_xor(r, 1, 64);
+    r += __shfl_xor(r, 2, 64);
+    r += __shfl_xor(r, 4, 64);
+    if (e < E && part == 0) offsets[E + 1 + r] = e;
   }
   if (tiles) {
     if (tid == 0) tiles[0] = toffs[E];
     for (int e = tid; e < E; e += 1024)
       for (int j = toffs[e]; j < toffs[e + 1]; ++j) tiles[1 + j] = e * 65536 + (j - toffs[e]);
   }
-  for (int p0 = tid; p0 < np; p0 += 1024 * kPB) {
+  auto scatter = [&](int p, int e, float gv) {
+    const int row = p / k;
+    const int rank = below[e * MW + (row >> 5)] + __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
+    const int slot = offs[e] + rank;
+    perm[slot] = row;
+    slot_of[p] = slot;
+    slot_gate[slot] = gv;
+  };
+#pragma unroll
+  for (int i = 0; i < kPB; ++i) {
+    const int p = tid + 1024 * i;
+    if (p < np) scatter(p, ev0[i], gv0[i]);
+  }
+  for (int p0 = tid + 1024 * kPB; p0 < np; p0 += 1024 * kPB) {
     int ev[kPB];
     float gv[kPB];
 #pragma unroll
@@ -199,14 +238,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     }
 #pragma unroll
     for (int i = 0; i < kPB; ++i) {
-      const int p = p0 + 1024 * i, row = p / k, e = ev[i];
-      if (p < np) {
-        const int rank = below[e * MW + (row >> 5)] + __popc(mask[e * MW + (row >> 5)] & ((1u << (row & 31)) - 1u));
-        const int slot = offs[e] + rank;
-        perm[slot] = row;
-        slot_of[p] = slot;
-        slot_gate[slot] = gv[i];
-      }
+      const int p = p0 + 1024 * i;
+      if (p < np) scatter(p, ev[i], gv[i]);
     }
   }
 }

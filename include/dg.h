@@ -457,9 +457,12 @@ enum {
   DG_BUF_SHARED_ACT = 14,   /* dtype [canvas x d_shared] shared-expert hidden activation */
   DG_BUF_SLOT_OUT = 15,     /* float [canvas*top_k x d_model] gated routed-expert outputs, expert-major slots */
   DG_BUF_SLOT_OF = 16,      /* int32 [canvas x top_k] slot of each (row, choice) */
-  DG_BUF_SEL_LAYERS = 17    /* int32 [n_layers][R][top_k], R = max(canvas, prefill_rows): the experts every
+  DG_BUF_SEL_LAYERS = 17,   /* int32 [n_layers][R][top_k], R = max(canvas, prefill_rows): the experts every
                                layer chose for the rows of the last pass (a denoising step, or the last
                                chunk of a prefill / commit, whose last layer computes only K and V) */
+  DG_BUF_OFFSETS = 18       /* int32 [2 n_experts + 1] (last layer run): the experts' first slots and the
+                               slot count, then the experts by decreasing token count (lower index
+                               first on ties), the order the routed-expert launches take them in */
 };
 int dg_ctx_buffer(const dg_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
 

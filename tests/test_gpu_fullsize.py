@@ -129,6 +129,13 @@ def test_moe_layer_full_size(libs, rope):
     outs = expert_ffns(W, 0, {e: np.array(v) for e, v in rows_of.items()}, h2)
     slot_of = model.buffer(L.DG_BUF_SLOT_OF, torch.int32, (C, d.top_k)).cpu().numpy()
     assert sorted(slot_of.ravel().tolist()) == list(range(C * d.top_k))
+    order = sorted(range(C * d.top_k), key=lambda p: (sel_gpu.ravel()[p], p // d.top_k))
+    assert [slot_of.ravel()[p] for p in order] == list(range(C * d.top_k)), "slots expert-major, token-ascending"
+    E = d.n_experts
+    offs = model.buffer(L.DG_BUF_OFFSETS, torch.int32, (2 * E + 1,)).cpu().numpy()
+    counts = np.bincount(sel_gpu.ravel(), minlength=E)
+    assert np.array_equal(offs[:E + 1], np.concatenate([[0], np.cumsum(counts)]))
+    assert offs[E + 1:].tolist() == sorted(range(E), key=lambda e: (-counts[e], e)), "experts by token count"
     want = np.zeros((C * d.top_k, D))
     y = OM.ffn(h2, lw, True, prefix="sh_")
     pos_in = {e: {t: i for i, t in enumerate(v)} for e, v in rows_of.items()}

@@ -90,6 +90,12 @@ def test_layer_stages(libs, dtype, gated, causal, M, past, renorm, E):
     # slots are expert-major and token-ascending
     order = sorted(range(M * shape.top_k), key=lambda p: (sel.ravel()[p], p // shape.top_k))
     assert [slot_of.ravel()[p] for p in order] == list(range(M * shape.top_k))
+    # the experts' first slots, then the experts by decreasing token count (lower index on ties)
+    E = shape.n_experts
+    offs = model.buffer(L.DG_BUF_OFFSETS, torch.int32, (2 * E + 1,)).cpu().numpy()
+    counts = np.bincount(sel.ravel(), minlength=E)
+    assert np.array_equal(offs[:E + 1], np.concatenate([[0], np.cumsum(counts)]))
+    assert offs[E + 1:].tolist() == sorted(range(E), key=lambda e: (-counts[e], e))
     y_ref, info = OM.layer_forward(lw, x0, np.concatenate([to_f64(K[0, :, :past]),
                                                         np.zeros((Hkv, 256 - past, hd))], axis=1),
                                 np.concatenate([to_f64(V[0, :, :past]), np.zeros((Hkv, 256 - past, hd))], axis=1),
