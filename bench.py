@@ -223,6 +223,8 @@ def bench_full(args):
     prefill_s = time.perf_counter() - t0
     log(f"[bench] prefill {w.prompt} tokens: {prefill_s:.2f} s")
     sched = L.make_sched(max_steps=S, seed=0)
+    if args.sampler_records == "lm_head":
+        model.fuse_sampler_stats(sched)
     st = SamplerState(C, V)
     logits = model.logits
     block_ids = torch.empty(C, dtype=torch.int32, device="cuda")
@@ -332,6 +334,7 @@ def bench_full(args):
                                f"FFN {d.d_selfcond}, prompt KV {w.prompt}, canvas {C}, up to {S} steps per canvas, "
                                "block commit after each canvas; random-init weights",
                    "expert_weights": "fp8 e4m3, per-row float32 scales" if fp8 else "bf16",
+                   "sampler_records": args.sampler_records,
                    "canvas_tokens_per_s": steps_per_s * C,
                    "committed_tokens_per_s": C / dt4,
                    "committed_canvas": {"steps": steps4, "stopped": stopped4, "seconds": dt4,
@@ -709,6 +712,9 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=2048,
                     help="rows per prefill chunk (0 = the canvas); chunks above 256 rows run the experts as "
                          "token-tiled GEMMs")
+    ap.add_argument("--sampler-records", choices=["lm_head", "pass"], default="pass",
+                    help="full / blockar workloads: the sampler's split-row records made by the LM head as it "
+                         "writes the logits (dg_ctx_fuse_sampler_stats), or by the sampler's own pass over them")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -88,6 +88,9 @@ _SIGS = {
     "dg_ctx_destroy": (ctypes.c_int, [_P]),
     "dg_ctx_use_graphs": (ctypes.c_int, [_P, _I32]),
     "dg_ctx_use_expert_fp8": (ctypes.c_int, [_P, _P]),
+    "dg_ctx_fuse_sampler_stats": (ctypes.c_int, [_P, ctypes.POINTER(dg_sched)]),
+    "dg_sample_canvas_fused": (ctypes.c_int, [_P, ctypes.POINTER(dg_sched), _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                              _SZ, _P]),
     "dg_kv_length": (_I64, [_P]),
     "dg_ctx_graph_captures": (_I64, [_P]),
     "dg_kv_set_length": (ctypes.c_int, [_P, _I64]),
@@ -287,6 +290,19 @@ def dg_ctx_use_graphs(ctx, on: bool):
 
 def dg_ctx_use_expert_fp8(ctx, d_fp8):
     return _check("dg_ctx_use_expert_fp8", lib.dg_ctx_use_expert_fp8(ctx, ptr(d_fp8)))
+
+
+def dg_ctx_fuse_sampler_stats(ctx, sched):
+    """sched: a dg_sched (the LM head then also produces the sampler's records at its temperatures), or None."""
+    return _check("dg_ctx_fuse_sampler_stats",
+                  lib.dg_ctx_fuse_sampler_stats(ctx, ctypes.byref(sched) if sched is not None else None))
+
+
+def dg_sample_canvas_fused(ctx, sched, step, block, d_canvas, d_pred, d_accept, d_entropy, d_row_stats, d_stop,
+                           d_workspace, ws_bytes, stream=None):
+    return _check("dg_sample_canvas_fused", lib.dg_sample_canvas_fused(
+        ctx, ctypes.byref(sched), step, block, ptr(d_canvas), ptr(d_pred), ptr(d_accept), ptr(d_entropy),
+        ptr(d_row_stats), ptr(d_stop), ptr(d_workspace), ws_bytes, stream_handle(stream)))
 
 
 def dg_kv_length(ctx) -> int:

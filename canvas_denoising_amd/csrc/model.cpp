@@ -49,6 +49,9 @@ int attn_v_overrun();
 int64_t attn_partial_rows(int M, int Hq, int Hkv);
 int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo, int dtype,
                hipStream_t s);
+int vocab_gemm_stats(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo,
+                     const float* temp, void* recs, int dtype, hipStream_t s);
+int vocab_blocks(int V);
 int moe_route(const float* part, int splits, int M, int E, int k, int renorm, float* rlog, int32_t* sel,
               float* gate, int32_t* offsets, int32_t* perm, int32_t* slot_of, float* slot_gate, int32_t* tiles,
               hipStream_t s);
@@ -68,6 +71,10 @@ int launch_synth_tiled(uint64_t seed, const uint64_t* tids, int64_t R, int64_t K
 int pack_tiled(const void* src, int64_t R, int64_t K, int which, int gr, int gw, void* dst, int dtype,
                hipStream_t s);
 size_t sample_workspace_bytes(int64_t rows, int64_t vocab);
+int launch_sample_from_block_recs(const void* block_recs, int nblk, int rows, int vocab, float temp,
+                                  const dg_sched& sc, int step, int block, int32_t* canvas, int32_t* pred,
+                                  uint8_t* accept, float* entropy, float* row_stats, dg_stop_state* stop, void* ws,
+                                  hipStream_t stream);
 int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
                        hipStream_t stream);
 int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp, const dg_sched& sc, int step,
@@ -244,7 +251,7 @@ struct StepGraph {
 struct WsLayout {
   size_t x, h, q, o, part_o, part_ml, rlog, sel, gate, offsets, perm, slot_of, slot_gate, act, slot_out, sh_act,
       sc, u, sc_hid, scpart, gpart, gpart_aux, y_sh, canvas, pred, accept, entropy, row_stats, stop, samp, rope,
-      tiles, len_dev, sc_temp, total;
+      tiles, len_dev, sc_temp, lm_temp, vrecs, total;
   int64_t gpart_floats;
   int64_t sel_layer;  // elements between the layers' expert choices (and gates)
 };
@@ -306,6 +313,8 @@ static WsLayout ws_layout(const dg_model_desc& d, int64_t capacity) {
   w.tiles = take((2 + CK / 128 + d.n_experts + 8) * 4);  // token-tile list of a chunk
   w.len_dev = take(4);   // int32: the committed KV length, as the denoising step reads it
   w.sc_temp = take(4);   // float: the temperature of the self-conditioning distribution
+  w.lm_temp = take(4);   // float: the temperature of the LM head's sampler records
+  w.vrecs = take(static_cast<size_t>(Cc) * vocab_blocks(static_cast<int>(d.vocab)) * 16);  // [canvas][blocks] records
   w.total = cur;
   return w;
 }
@@ -332,6 +341,10 @@ struct dg_ctx {
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
   dg::StepGraph graphs[2];
+  // the LM head also folds its logits into the sampler's split-row records at this schedule's
+  // temperature (dg_ctx_fuse_sampler_stats), so the sampler need not read the logits again
+  bool fuse_stats = false;
+  dg_sched fuse_sched{};
   int last_layer = 0;  // layer of the last routing (DG_BUF_SEL / DG_BUF_GATE)
   int64_t captures = 0;  // step graphs captured so far
   // dg_generate_block's read-back of the stop state: one pinned host slot and one event per step in
@@ -561,6 +574,9 @@ static int denoise_body(dg_ctx* c, const int32_t* canvas, const void* prev_logit
   const int* pos_dev = wsp<int32_t>(c, w.len_dev);
   for (int l = 0; l < d.n_layers; ++l)  // each layer leaves h = RMSNorm(its output)
     DG_TRY(layer_forward(c, l, x, C, static_cast<int>(c->len), pos_dev, false, false, s));
+  if (c->fuse_stats)
+    return vocab_gemm_stats(h, D, wp(c, c->wl.embed), C, d.vocab, D, logits, d.vocab, wsp<float>(c, w.lm_temp),
+                            wsp<void>(c, w.vrecs), d.dtype, s);
   return vocab_gemm(h, D, wp(c, c->wl.embed), C, d.vocab, D, logits, d.vocab, d.dtype, s);
 }
 
@@ -608,10 +624,16 @@ static int denoise_graphed(dg_ctx* c, const int32_t* canvas, const void* prev_lo
   return DG_OK;
 }
 
-static int denoise(dg_ctx* c, const int32_t* canvas, const void* prev_logits, const float* prev_stats, float prev_t,
-                   void* logits, hipStream_t s) {
+static int denoise(dg_ctx* c, int step, const int32_t* canvas, const void* prev_logits, const float* prev_stats,
+                   float prev_t, void* logits, hipStream_t s) {
   if (prev_logits != nullptr) DG_TRY(store_f32(wsp<float>(c, c->wsl.sc_temp), prev_t, s));
+  if (c->fuse_stats) DG_TRY(store_f32(wsp<float>(c, c->wsl.lm_temp), temperature(c->fuse_sched, step), s));
   return denoise_graphed(c, canvas, prev_logits, prev_stats, logits, s);
+}
+
+// two schedules give every step the same temperature
+static bool same_temperatures(const dg_sched& a, const dg_sched& b) {
+  return a.max_steps == b.max_steps && a.t_start == b.t_start && a.t_end == b.t_end;
 }
 
 static int check_ctx(const dg_ctx* c) {
@@ -860,6 +882,42 @@ int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8) {
   return DG_OK;
 }
 
+int dg_ctx_fuse_sampler_stats(dg_ctx* ctx, const dg_sched* sched) {
+  DG_TRY(check_ctx(ctx));
+  if (sched) {
+    DG_TRY(check_sched(sched, 0));
+    if (ctx->d.dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "sampler records in the LM head: bf16 models only");
+    if (sched->mode & DG_SCHED_SAMPLE)
+      return fail(DG_ERR_UNSUPPORTED, "categorical sampling perturbs every logit: it needs the sampler's own pass");
+  }
+  DG_HIP(hipDeviceSynchronize());
+  for (StepGraph& g : ctx->graphs) drop_graph(g);  // the captured LM head launch changes
+  ctx->fuse_stats = sched != nullptr;
+  if (sched) ctx->fuse_sched = *sched;
+  return DG_OK;
+}
+
+int dg_sample_canvas_fused(dg_ctx* ctx, const dg_sched* sched, int32_t step, int32_t block, int32_t* d_canvas,
+                           int32_t* d_pred, uint8_t* d_accept, float* d_entropy, float* d_row_stats,
+                           dg_stop_state* d_stop, void* d_workspace, size_t ws_bytes, void* stream) {
+  DG_TRY(check_ctx(ctx));
+  DG_TRY(check_sched(sched, step));
+  if (!ctx->fuse_stats) return fail(DG_ERR_INVALID, "the LM head does not produce sampler records (dg_ctx_fuse_sampler_stats)");
+  if (!same_temperatures(ctx->fuse_sched, *sched))
+    return fail(DG_ERR_INVALID, "the schedule's temperatures differ from the LM head's sampler records");
+  if (sched->mode & DG_SCHED_SAMPLE)
+    return fail(DG_ERR_UNSUPPORTED, "categorical sampling perturbs every logit: it needs the sampler's own pass");
+  if (!d_canvas || !d_pred || !d_stop || !d_workspace)
+    return fail(DG_ERR_INVALID, "d_canvas, d_pred, d_stop and d_workspace are required");
+  if (block < 0) return fail(DG_ERR_INVALID, "block must be >= 0");
+  const int C = ctx->d.canvas;
+  if (ws_bytes < sample_workspace_bytes(C, ctx->d.vocab) || reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
+    return fail(DG_ERR_INVALID, "d_workspace must be 256-aligned and hold dg_sample_workspace_size(canvas, vocab) bytes");
+  return launch_sample_from_block_recs(wsp<void>(ctx, ctx->wsl.vrecs), vocab_blocks(ctx->d.vocab), C, ctx->d.vocab,
+                                       temperature(*sched, step), *sched, step, block, d_canvas, d_pred, d_accept,
+                                       d_entropy, d_row_stats, d_stop, d_workspace, as_stream(stream));
+}
+
 int64_t dg_kv_length(const dg_ctx* ctx) { return ctx ? ctx->len : -1; }
 
 int64_t dg_ctx_graph_captures(const dg_ctx* ctx) { return ctx ? ctx->captures : -1; }
@@ -886,12 +944,13 @@ int dg_prefill_kv(dg_ctx* ctx, const int32_t* d_prompt_ids, int32_t n_prompt, vo
 int dg_denoise_step(dg_ctx* ctx, const int32_t* d_canvas, int32_t step, const void* d_prev_logits,
                     const float* d_prev_row_stats, float prev_temperature, void* d_logits, void* stream) {
   DG_TRY(check_ctx(ctx));
-  (void)step;
   if (!d_canvas || !d_logits) return fail(DG_ERR_INVALID, "d_canvas and d_logits are required");
   if (d_prev_logits && (!d_prev_row_stats || !(prev_temperature > 0.f) || !isfinite(prev_temperature)))
     return fail(DG_ERR_INVALID, "self-conditioning needs row stats and a positive temperature");
   if (ctx->len + ctx->d.canvas > ctx->cap) return fail(DG_ERR_CAPACITY, "no room for the canvas in the KV cache");
-  return denoise(ctx, d_canvas, d_prev_logits, d_prev_row_stats, prev_temperature, d_logits, as_stream(stream));
+  if (ctx->fuse_stats && (step < 0 || step >= ctx->fuse_sched.max_steps))
+    return fail(DG_ERR_INVALID, "step outside the schedule the LM head's sampler records follow");
+  return denoise(ctx, step, d_canvas, d_prev_logits, d_prev_row_stats, prev_temperature, d_logits, as_stream(stream));
 }
 
 int dg_commit_block(dg_ctx* ctx, const int32_t* d_block_ids, void* stream) {
@@ -934,6 +993,10 @@ int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d
   // step 0 and grows by at most one a step, so a step whose count cannot have reached stable_needed
   // cannot stop, and the next step is launched without waiting for it (the device never idles
   // between such steps). With the either-condition rule every step could stop and is read.
+  // the LM head's records serve this schedule when they follow its temperatures
+  const bool fused = ctx->fuse_stats && same_temperatures(ctx->fuse_sched, *sched);
+  if (ctx->fuse_stats && !fused)
+    return fail(DG_ERR_INVALID, "the schedule's temperatures differ from the LM head's sampler records");
   const bool either = (sched->mode & DG_SCHED_STOP_EITHER) != 0;
   int known = -1, c_known = 0;  // the last step read, and its stable count
   auto could_stop = [&](int j) {
@@ -963,10 +1026,15 @@ int dg_generate_block(dg_ctx* ctx, const dg_sched* sched, int32_t block, void* d
     if (enq == sched->max_steps) break;
     const int step = enq;
     const float T = temperature(*sched, step);
-    DG_TRY(denoise(ctx, canvas, step > 0 ? d_logits : nullptr, stats, prev_t, d_logits, s));
-    DG_TRY(launch_sample(d_logits, ctx->d.dtype, C, ctx->d.vocab, T, *sched, step, block, canvas, pred,
-                         wsp<uint8_t>(ctx, w.accept), wsp<float>(ctx, w.entropy), stats, stop,
-                         wsp<void>(ctx, w.samp), s));
+    DG_TRY(denoise(ctx, step, canvas, step > 0 ? d_logits : nullptr, stats, prev_t, d_logits, s));
+    if (fused)
+      DG_TRY(launch_sample_from_block_recs(wsp<void>(ctx, w.vrecs), vocab_blocks(ctx->d.vocab), C, ctx->d.vocab, T,
+                                           *sched, step, block, canvas, pred, wsp<uint8_t>(ctx, w.accept),
+                                           wsp<float>(ctx, w.entropy), stats, stop, wsp<void>(ctx, w.samp), s));
+    else
+      DG_TRY(launch_sample(d_logits, ctx->d.dtype, C, ctx->d.vocab, T, *sched, step, block, canvas, pred,
+                           wsp<uint8_t>(ctx, w.accept), wsp<float>(ctx, w.entropy), stats, stop,
+                           wsp<void>(ctx, w.samp), s));
     DG_HIP(hipMemcpyAsync(&ctx->stop_host[step % dg_ctx::kStopSlots], stop, sizeof(dg_stop_state),
                           hipMemcpyDeviceToHost, s));
     DG_HIP(hipEventRecord(ctx->stop_ev[step % dg_ctx::kStopSlots], s));

@@ -34,55 +34,11 @@
 #include <mutex>
 
 #include "dg_common.h"
+#include "entrec.h"
 #include "philox.h"
 #include "prof.h"
 
 namespace dg {
-
-struct Rec {
-  float m;   // max raw logit (-inf when empty)
-  float z;   // sum 2^u
-  float a;   // sum u 2^u
-  int idx;   // lowest index attaining m
-};
-
-// merge y into x; `c` = log2(e) / T. Deterministic for a fixed merge order.
-__device__ inline void rec_merge(Rec& x, const Rec& y, float c) {
-  if (y.z == 0.f) return;
-  if (x.z == 0.f) { x = y; return; }
-  const float m = fmaxf(x.m, y.m);
-  const float dx = (x.m - m) * c, dy = (y.m - m) * c;
-  const float sx = __builtin_amdgcn_exp2f(dx), sy = __builtin_amdgcn_exp2f(dy);
-  const int idx = (x.m > y.m) ? x.idx : (y.m > x.m) ? y.idx : min(x.idx, y.idx);
-  x.a = sx * (x.a + dx * x.z) + sy * (y.a + dy * y.z);
-  x.z = x.z * sx + y.z * sy;
-  x.m = m;
-  x.idx = idx;
-}
-
-template <int CTRL>
-__device__ inline Rec rec_dpp(const Rec& r) {
-  return Rec{dpp_f32<CTRL>(r.m), dpp_f32<CTRL>(r.z), dpp_f32<CTRL>(r.a),
-             static_cast<int>(dpp_u32<CTRL>(static_cast<uint32_t>(r.idx)))};
-}
-__device__ inline Rec rec_xrow16(const Rec& r) {
-  return Rec{xrow16_f32(r.m), xrow16_f32(r.z), xrow16_f32(r.a),
-             static_cast<int>(xrow16_u32(static_cast<uint32_t>(r.idx)))};
-}
-__device__ inline Rec rec_xrow32(const Rec& r) {
-  return Rec{xrow32_f32(r.m), xrow32_f32(r.z), xrow32_f32(r.a),
-             static_cast<int>(xrow32_u32(static_cast<uint32_t>(r.idx)))};
-}
-
-// Merge the records of all 64 lanes: six partner levels (dg_common.h), a fixed order per lane.
-__device__ inline void rec_wave_merge(Rec& w, float c) {
-  rec_merge(w, rec_dpp<kDppXor1>(w), c);
-  rec_merge(w, rec_dpp<kDppXor2>(w), c);
-  rec_merge(w, rec_dpp<kDppHalfMirror>(w), c);
-  rec_merge(w, rec_dpp<kDppMirror>(w), c);
-  rec_merge(w, rec_xrow16(w), c);
-  rec_merge(w, rec_xrow32(w), c);
-}
 
 // Categorical sampling: the best Gumbel-perturbed score of a chunk and its (lowest) index.
 struct GRec {
@@ -591,9 +547,13 @@ static size_t recs_bytes(int64_t rows, int64_t vocab) {
   return (static_cast<size_t>(rows * p.splits) * sizeof(Rec) + 255) / 256 * 256;
 }
 
+size_t sample_fused_workspace_bytes(int64_t rows);
+
+// the partial pass's records (and Gumbel records), or the merged records of the LM head's blocks
 size_t sample_workspace_bytes(int64_t rows, int64_t vocab) {
   const SplitPlan p = plan_splits(rows, vocab);
-  return recs_bytes(rows, vocab) + (static_cast<size_t>(rows * p.splits) * sizeof(GRec) + 255) / 256 * 256;
+  const size_t own = recs_bytes(rows, vocab) + (static_cast<size_t>(rows * p.splits) * sizeof(GRec) + 255) / 256 * 256;
+  return std::max(own, sample_fused_workspace_bytes(rows));
 }
 
 int launch_init_canvas(uint64_t seed, int block, int n, int vocab, int32_t* canvas, dg_stop_state* stop,
@@ -680,6 +640,73 @@ int launch_sample(const void* logits, int dtype, int rows, int vocab, float temp
     }
   }
   DG_LAUNCH_CHECK("sample_kernel");
+  {
+    ProfScope ps("sample_finalize", stream);
+    sample_finalize_kernel<<<1, kFinThreads, 0, stream>>>(g);
+  }
+  DG_LAUNCH_CHECK("sample_finalize_kernel");
+  return DG_OK;
+}
+
+// ------------------------------------------------ records produced by the LM head
+// The LM head can fold its own output into split-row records, one per (row, 256-column vocabulary
+// block), in the same layout and arithmetic as the partial pass (vocab.hip). The records of a row
+// are merged here into kFusedSplits records, one wave per (row, run of consecutive blocks) in a
+// fixed order, and the finalize kernel runs on those as on the partial pass's: the logits are not
+// read again.
+constexpr int kFusedSplits = 16;
+
+__global__ __launch_bounds__(256) void merge_block_recs_kernel(SampleArgs g, const Rec* __restrict__ brec, int nblk) {
+  if (g.stop->stopped) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, group)
+  const int row = wv / kFusedSplits, grp = wv - row * kFusedSplits;
+  if (row >= g.rows) return;
+  const int per = (nblk + kFusedSplits - 1) / kFusedSplits;
+  const int b0 = grp * per, b1 = min(nblk, b0 + per);
+  Rec r{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
+  for (int b = b0 + lane; b < b1; b += 64) rec_merge(r, brec[static_cast<int64_t>(row) * nblk + b], g.c);
+  rec_wave_merge(r, g.c);
+  if (lane == 0) g.recs[static_cast<int64_t>(row) * kFusedSplits + grp] = r;
+}
+
+size_t sample_fused_workspace_bytes(int64_t rows) {
+  return (static_cast<size_t>(rows * kFusedSplits) * sizeof(Rec) + 255) / 256 * 256;
+}
+
+int launch_sample_from_block_recs(const void* block_recs, int nblk, int rows, int vocab, float temp,
+                                  const dg_sched& sc, int step, int block, int32_t* canvas, int32_t* pred,
+                                  uint8_t* accept, float* entropy, float* row_stats, dg_stop_state* stop, void* ws,
+                                  hipStream_t stream) {
+  if (sc.mode & DG_SCHED_SAMPLE)
+    return fail(DG_ERR_UNSUPPORTED, "records from the LM head: categorical sampling needs the partial pass");
+  if ((sc.mode & DG_SCHED_ACCEPT_GROUP) && rows > kGroupMaxRows)
+    return fail(DG_ERR_UNSUPPORTED, "group acceptance: at most 4096 rows");
+  if (nblk < 1) return fail(DG_ERR_INVALID, "no LM head records");
+  SampleArgs g;
+  g.logits = nullptr;
+  g.vocab = vocab;
+  g.chunk = vocab;
+  g.rows = rows;
+  g.splits = kFusedSplits;
+  g.c = kLog2e / temp;
+  g.bound = sc.entropy_bound;
+  g.stop_thr = sc.stop_mean_entropy;
+  g.stable_needed = sc.stable_needed;
+  g.mode = sc.mode;
+  g.seed = sc.seed;
+  g.step = step;
+  g.block = block;
+  g.canvas = canvas; g.pred = pred; g.accept = accept; g.entropy = entropy; g.row_stats = row_stats; g.stop = stop;
+  g.recs = static_cast<Rec*>(ws);
+  g.grecs = nullptr;
+  g.inv_t = 1.0f / temp;
+  {
+    ProfScope ps("sample_merge", stream);
+    const int waves = rows * kFusedSplits;
+    merge_block_recs_kernel<<<(waves + 3) / 4, 256, 0, stream>>>(g, static_cast<const Rec*>(block_recs), nblk);
+  }
+  DG_LAUNCH_CHECK("merge_block_recs_kernel");
   {
     ProfScope ps("sample_finalize", stream);
     sample_finalize_kernel<<<1, kFinThreads, 0, stream>>>(g);

@@ -40,6 +40,7 @@
 
 #include "dg_common.h"
 #include "dma.h"
+#include "entrec.h"
 #include "mfma.h"
 #include "prof.h"
 #include "tiles.h"
@@ -74,7 +75,7 @@ __device__ inline f32x8_t lds_frag<float>(const unsigned char* stage, int r, int
   return f;
 }
 
-enum VocabMode : int { kLmHead = 0, kSelfCond = 1 };
+enum VocabMode : int { kLmHead = 0, kSelfCond = 1, kLmHeadStats = 2 };
 
 // Grid: ceil(V / (32 kVW)) workgroups of kVW waves; wave w of block b owns vocabulary group
 // b * kVW + w (E rows 32 g .. 32 g + 31).
@@ -273,6 +274,83 @@ __global__ __launch_bounds__(64 * kVW) void vocab_gemm_kernel(const T* __restric
   for (int u = 0; u < NS - 1; ++u)
     if (k0 + u < KT) step(k0 + u, u);
   wait_vm_n<0>();  // the trailing (never used) copies have landed before the workgroup retires
+  if constexpr (MODE == kLmHeadStats) {
+    // The block's logits leave through LDS in two halves of 128 rows (each wave its 128 x 32 tile,
+    // 8 KB, in the ring's first 64 KB), so that every lane stores 64 contiguous bytes of a row and
+    // folds that row's 32 values (as stored, bf16) into a split-row record at temperature *temp;
+    // the 8 waves' records of a row then merge in wave order into the block's record,
+    // part[row * gridDim.x + blockIdx.x] (Rec layout).
+    const float c = kLog2e / *temp;
+    // lane indices re-derived here (opaque to the compiler), so that no epilogue address is computed
+    // ahead of the k-loop and held through it
+    int xl = lane, xt = tid;
+    asm volatile("" : "+v"(xl), "+v"(xt));
+    const int lane_e = xl, fr_e = xl & 15, g4_e = xl >> 4, tid_e = xt;
+    __syncthreads();  // every wave is done with the ring
+    unsigned char* tile = smem + wave * 8192;
+    Rec* wrec = reinterpret_cast<Rec*>(smem + kVW * 8192);  // [256 rows][kVW waves]
+    static_assert(kVW * 8192 + kVRows * kVW * sizeof(Rec) <= NA * SBYTES, "epilogue LDS");
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            reinterpret_cast<bf16_t*>(tile)[(mm * 16 + g4_e * 4 + i) * 32 + n * 16 + fr_e] =
+                f32_to_bf16(acc[half * 8 + mm][n][i]);
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rl = 2 * lane_e + q, row = half * 128 + rl;
+        const uint4* src = reinterpret_cast<const uint4*>(tile + rl * 64);
+        uint4 w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = src[k];
+        if (active && row < M) {
+          uint4* dst = reinterpret_cast<uint4*>(logits + static_cast<int64_t>(row) * ldo + grp * 32);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dst[k] = w[k];
+        }
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t x[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            v[k * 8 + 2 * h] = bf16lo(x[h]);
+            v[k * 8 + 2 * h + 1] = bf16hi(x[h]);
+          }
+        }
+        float m = v[0];
+#pragma unroll
+        for (int j = 1; j < 32; ++j) m = fmaxf(m, v[j]);
+        int first = 31;
+#pragma unroll
+        for (int j = 30; j >= 0; --j)
+          if (v[j] == m) first = j;
+        const float off = -m * c;
+        float z = 0.f, a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float u = fmaf(v[j], c, off);
+          const float e = __builtin_amdgcn_exp2f(u);
+          z += e;
+          a = fmaf(u, e, a);
+        }
+        wrec[row * kVW + wave] = active ? Rec{m, z, a, grp * 32 + first} : Rec{-INFINITY, 0.f, 0.f, 0x7FFFFFFF};
+      }
+      __syncthreads();  // the tiles are rewritten by the next half; the records are complete
+    }
+    if (tid_e < kVRows && tid_e < M) {
+      Rec r = wrec[tid_e * kVW];
+#pragma unroll
+      for (int w2 = 1; w2 < kVW; ++w2) rec_merge(r, wrec[tid_e * kVW + w2], c);
+      reinterpret_cast<Rec*>(part)[static_cast<int64_t>(tid_e) * gridDim.x + blockIdx.x] = r;
+    }
+    return;
+  }
   if (!active) return;
   // lane holds C[row = m*16 + 4*g4 + i][col = 32 grp + n*16 + fr]
 #pragma unroll
@@ -335,6 +413,25 @@ int vocab_gemm(const void* h, int64_t ldh, const void* E, int M, int V, int D, v
   DG_LAUNCH_CHECK("vocab_gemm_kernel");
   return DG_OK;
 }
+
+int vocab_gemm_stats(const void* h, int64_t ldh, const void* E, int M, int V, int D, void* logits, int64_t ldo,
+                     const float* temp, void* recs, int dtype, hipStream_t s) {
+  if (dtype != DG_BF16) return fail(DG_ERR_UNSUPPORTED, "LM head with sampler records: bf16 only");
+  if (M < 1 || M > kVRows) return fail(DG_ERR_UNSUPPORTED, "LM head: rows must be in [1, 256]");
+  if (D % 64 != 0 || V % 32 != 0) return fail(DG_ERR_UNSUPPORTED, "LM head: d_model / vocab do not tile");
+  if (ldo % 8 != 0 || reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "LM head with records: logits rows must be 16-byte aligned");
+  if (static_cast<int64_t>(M) * ldh + D > INT32_MAX) return fail(DG_ERR_UNSUPPORTED, "LM head: rows too long");
+  const int grid = (V / 32 + kVW - 1) / kVW;
+  ProfScope ps("lm_head", s);
+  vocab_gemm_kernel<bf16_t, kLmHeadStats><<<grid, 64 * kVW, 0, s>>>(
+      static_cast<const bf16_t*>(h), ldh, static_cast<const bf16_t*>(E), M, V, D, static_cast<bf16_t*>(logits), ldo,
+      static_cast<float*>(recs), 1, 0, nullptr, temp);
+  DG_LAUNCH_CHECK("vocab_gemm_kernel");
+  return DG_OK;
+}
+
+int vocab_blocks(int V) { return (V / 32 + kVW - 1) / kVW; }
 
 int sc_embed_splits(int N, int64_t K, int dtype) {
   const int ke = dtype == DG_BF16 ? 64 : 32;

@@ -43,6 +43,13 @@ class SamplerState:
         L.dg_sample_canvas(logits.data_ptr(), dt, self.rows, self.vocab, sched, step, block, *self._ptrs,
                            self.ws_bytes, stream)
 
+    def sample_fused(self, ctx, sched, step: int, block: int, stream=None):
+        """dg_sample_canvas_fused: the same outputs, from the records the context's LM head made."""
+        if not hasattr(self, "_ptrs"):
+            self._ptrs = tuple(t.data_ptr() for t in (self.canvas, self.pred, self.accept, self.entropy,
+                                                      self.row_stats, self.stop, self.workspace))
+        L.dg_sample_canvas_fused(ctx, sched, step, block, *self._ptrs, self.ws_bytes, stream)
+
     def stop_state(self) -> dict:
         return stop_dict(self.stop)
 
@@ -163,6 +170,12 @@ class Model:
     def forward_layer(self, layer, x, rows, causal=False):
         L.dg_forward_layer(self.ctx, layer, x, rows, causal)
 
+    def fuse_sampler_stats(self, sched):
+        """With a schedule, the LM head also produces the sampler's records at its temperatures and
+        denoise_canvas samples from them (dg_ctx_fuse_sampler_stats); None turns that off."""
+        L.dg_ctx_fuse_sampler_stats(self.ctx, sched)
+        self._fused_sched = sched
+
     def generate_block(self, sched, block, block_out, commit=True) -> int:
         return L.dg_generate_block(self.ctx, sched, block, self.logits, block_out, commit)
 
@@ -205,7 +218,10 @@ class Model:
                 self.denoise_step(st.canvas, s, out, st.row_stats, L.dg_temperature(sched, s - 1), logits=out)
             else:
                 self.denoise_step(st.canvas, s, logits=out)
-            st.sample(out, sched, s, block)
+            if getattr(self, "_fused_sched", None) is not None:
+                st.sample_fused(self.ctx, sched, s, block)
+            else:
+                st.sample(out, sched, s, block)
             host[s % k].copy_(st.stop, non_blocking=True)
             ev[s % k].record()
             enq += 1

@@ -376,6 +376,31 @@ int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
  * Errors: DG_ERR_INVALID (misaligned), DG_ERR_UNSUPPORTED (model without
  * FP8 support). */
 int dg_ctx_use_expert_fp8(dg_ctx* ctx, const void* d_fp8);
+/* The LM head and the sampler's statistics in one pass ([P3] "Encoder-denoiser
+ * design": logits at every canvas position; [P3] "Inference mechanism" and [P4]
+ * "Standard sampling settings": the entropy-bounded sampler over them). With a
+ * schedule, every later dg_denoise_step(step) also folds its logits, as
+ * stored (bf16), into the sampler's split-row records (max, sum 2^u, sum u
+ * 2^u, first argmax; u = (l - max) log2(e) / T) at T = the schedule's
+ * temperature of that step, one record per row and 256-token vocabulary block;
+ * dg_sample_canvas_fused and dg_generate_block then sample from those records
+ * instead of reading the logits again (the logits are still written: the next
+ * step's self-conditioning reads them). NULL turns this off. Waits for the
+ * device and drops captured graphs. Errors: DG_ERR_UNSUPPORTED (an fp32 model,
+ * or categorical sampling, whose scores perturb every logit); DG_ERR_INVALID
+ * (a bad schedule). dg_generate_block with a schedule of other temperatures
+ * fails with DG_ERR_INVALID while this is on. */
+int dg_ctx_fuse_sampler_stats(dg_ctx* ctx, const dg_sched* sched);
+/* dg_sample_canvas from the records the last dg_denoise_step of this context
+ * produced (dg_ctx_fuse_sampler_stats): the same outputs, workspace and
+ * arguments, without the logits. `sched` must give step `step` the
+ * temperature the records were made at (same max_steps, t_start, t_end), else
+ * DG_ERR_INVALID; DG_ERR_UNSUPPORTED for categorical sampling. The records of
+ * a row are merged in a fixed order, so the results are reproducible; they
+ * equal dg_sample_canvas's up to the rounding of the entropies' sums. */
+int dg_sample_canvas_fused(dg_ctx* ctx, const dg_sched* sched, int32_t step, int32_t block, int32_t* d_canvas,
+                           int32_t* d_pred, uint8_t* d_accept, float* d_entropy, float* d_row_stats,
+                           dg_stop_state* d_stop, void* d_workspace, size_t ws_bytes, void* stream);
 int64_t dg_kv_length(const dg_ctx* ctx);
 /* Number of denoising-step graphs the context has captured so far (-1 for NULL): a replay
  * re-captures only when the caller's pointers change (see dg_ctx_use_graphs). */

@@ -165,6 +165,7 @@ def test_full_step_sampled(libs):
     sched = L.make_sched(max_steps=48, seed=0)
     st = runtime.SamplerState(C, V)
     st.init(sched, 0)
+    canvas0 = st.canvas.clone()
     logits = model.denoise_step(st.canvas, 0)
     torch.cuda.synchronize()
     # LM head on sampled (row, vocab) pairs from the GPU's final normalised activations
@@ -185,6 +186,20 @@ def test_full_step_sampled(libs):
     assert np.array_equal(st.canvas.cpu().numpy()[~flag], res.next_canvas[~flag])
     assert np.abs(to_f64(st.entropy) - res.entropy).max() < 1e-3
     print(f"mean entropy {res.mean_entropy:.3f} (ln V = {np.log(V):.3f}), accepted {int(res.accept.sum())}")
+    # the LM head making the sampler's records itself (1024 vocabulary blocks a row, merged 64 at a
+    # time): the same logits, and the same decisions without a second read of them
+    model.fuse_sampler_stats(sched)
+    logits_f = model.denoise_step(canvas0, 0, logits=torch.empty_like(logits))
+    stf = runtime.SamplerState(C, V)
+    stf.init(sched, 0)
+    stf.sample_fused(model.ctx, sched, 0, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(logits_f, logits)
+    assert np.array_equal(stf.pred.cpu().numpy(), res.pred)
+    assert np.array_equal(stf.canvas.cpu().numpy()[~flag], res.next_canvas[~flag])
+    assert np.abs(to_f64(stf.entropy) - to_f64(st.entropy)).max() < 1e-5
+    assert np.allclose(to_f64(stf.row_stats), to_f64(st.row_stats), rtol=1e-5, atol=1e-5)
+    model.fuse_sampler_stats(None)
     # a self-conditioned step at full size: the self-conditioning vector of sampled rows against
     # the oracle's p E (E streamed through the host in vocabulary chunks), teacher-forced on the
     # GPU's step-0 logits
