@@ -222,6 +222,28 @@ def bench_full(args):
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t0
     log(f"[bench] prefill {w.prompt} tokens: {prefill_s:.2f} s")
+    placement = None
+    if args.placement_tries > 1:
+        # load-time choice among allocations of the weights: each copy is timed over a few steps
+        probe = torch.empty(C, dtype=torch.int32, device="cuda")
+        L.dg_synth_uniform_ids(5, 11, C, V, probe)
+
+        def measure(n=10):
+            model.denoise_step(probe, 0, logits=model.logits)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(n):
+                model.denoise_step(probe, 0, logits=model.logits)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) / n
+
+        t0 = time.perf_counter()
+        times, kept = model.place_weights(measure, args.placement_tries)
+        placement = {"tries": args.placement_tries, "ms_per_step": [round(1e3 * x, 3) for x in times],
+                     "kept": kept, "seconds": round(time.perf_counter() - t0, 2),
+                     "note": "the weights' speed follows their allocation; each candidate (the original and "
+                             "device copies) timed over 10 steps without self-conditioning, the fastest kept"}
+        log(f"[bench] weight placement: {placement['ms_per_step']} ms/step, kept {kept}")
     sched = L.make_sched(max_steps=S, seed=0)
     if args.sampler_records == "lm_head":
         model.fuse_sampler_stats(sched)
@@ -335,6 +357,7 @@ def bench_full(args):
                                "block commit after each canvas; random-init weights",
                    "expert_weights": "fp8 e4m3, per-row float32 scales" if fp8 else "bf16",
                    "sampler_records": args.sampler_records,
+                   "weights_placement": placement,
                    "canvas_tokens_per_s": steps_per_s * C,
                    "committed_tokens_per_s": C / dt4,
                    "committed_canvas": {"steps": steps4, "stopped": stopped4, "seconds": dt4,
@@ -712,6 +735,9 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=2048,
                     help="rows per prefill chunk (0 = the canvas); chunks above 256 rows run the experts as "
                          "token-tiled GEMMs")
+    ap.add_argument("--placement-tries", type=int, default=3,
+                    help="full workload: allocations of the weights timed at load time (the fastest is kept); "
+                         "1 keeps the first")
     ap.add_argument("--sampler-records", choices=["lm_head", "pass"], default="pass",
                     help="full / blockar workloads: the sampler's split-row records made by the LM head as it "
                          "writes the logits (dg_ctx_fuse_sampler_stats), or by the sampler's own pass over them")

@@ -87,6 +87,7 @@ _SIGS = {
     "dg_ctx_create": (ctypes.c_int, [ctypes.POINTER(dg_model_desc), _P, _P, _I64, _P, _SZ, ctypes.POINTER(_P)]),
     "dg_ctx_destroy": (ctypes.c_int, [_P]),
     "dg_ctx_use_graphs": (ctypes.c_int, [_P, _I32]),
+    "dg_ctx_set_weights": (ctypes.c_int, [_P, _P]),
     "dg_ctx_use_expert_fp8": (ctypes.c_int, [_P, _P]),
     "dg_ctx_fuse_sampler_stats": (ctypes.c_int, [_P, ctypes.POINTER(dg_sched)]),
     "dg_sample_canvas_fused": (ctypes.c_int, [_P, ctypes.POINTER(dg_sched), _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
@@ -286,6 +287,10 @@ def dg_ctx_destroy(ctx):
 
 def dg_ctx_use_graphs(ctx, on: bool):
     return _check("dg_ctx_use_graphs", lib.dg_ctx_use_graphs(ctx, int(on)))
+
+
+def dg_ctx_set_weights(ctx, d_weights):
+    return _check("dg_ctx_set_weights", lib.dg_ctx_set_weights(ctx, ptr(d_weights)))
 
 
 def dg_ctx_use_expert_fp8(ctx, d_fp8):

@@ -859,6 +859,17 @@ int dg_ctx_destroy(dg_ctx* ctx) {
   return DG_OK;
 }
 
+int dg_ctx_set_weights(dg_ctx* ctx, void* d_weights) {
+  DG_TRY(check_ctx(ctx));
+  if (!d_weights) return fail(DG_ERR_INVALID, "d_weights is NULL");
+  if (reinterpret_cast<uintptr_t>(d_weights) % 256 != 0)
+    return fail(DG_ERR_INVALID, "device buffers must be 256-byte aligned");
+  DG_HIP(hipDeviceSynchronize());
+  for (StepGraph& g : ctx->graphs) drop_graph(g);
+  ctx->w = static_cast<char*>(d_weights);
+  return DG_OK;
+}
+
 int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on) {
   DG_TRY(check_ctx(ctx));
   ctx->use_graphs = on != 0;

@@ -106,6 +106,34 @@ class Model:
             raise ValueError(f"expected a contiguous {self.dtype} CUDA tensor of shape ({r}, {c})")
         L.dg_load_weight(self.desc, kind, layer, expert, src, self.weights)
 
+    def set_weights(self, weights: torch.Tensor):
+        """Compute from another buffer holding the same weights (dg_ctx_set_weights)."""
+        if weights.dtype != torch.uint8 or weights.numel() != self.weights.numel() or not weights.is_cuda:
+            raise ValueError("expected a uint8 CUDA buffer of dg_weights_bytes bytes")
+        L.dg_ctx_set_weights(self.ctx, weights)
+        self.weights = weights
+
+    def place_weights(self, measure, tries: int = 3):
+        """Keep the fastest of `tries` allocations of the weights.
+
+        How fast the weight streams run depends on where their allocation lies in device memory, and
+        an allocation keeps its speed. The current buffer and tries - 1 device copies are each timed
+        with measure() (seconds, lower is better; it runs model work and synchronizes), the fastest
+        is kept and the others are freed. Returns (times, index of the kept buffer)."""
+        cands, times = [self.weights], [float(measure())]
+        for _ in range(1, tries):
+            cands.append(torch.empty_like(self.weights))
+            cands[-1].copy_(self.weights)
+            torch.cuda.synchronize()
+            self.set_weights(cands[-1])
+            times.append(float(measure()))
+        best = min(range(len(times)), key=times.__getitem__)
+        self.set_weights(cands[best])
+        cands.clear()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return times, best
+
     def use_expert_fp8(self, on: bool = True):
         """Quantize the routed experts to FP8 (once) and compute with them; False returns to the
         model-dtype weights."""

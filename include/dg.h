@@ -369,6 +369,18 @@ int dg_ctx_destroy(dg_ctx* ctx);
  * launch is issued directly. Steps also run directly while dg_profile_enable
  * is on. */
 int dg_ctx_use_graphs(dg_ctx* ctx, int32_t on);
+/* Point the context at another copy of its weights ([P3] "Encoder-denoiser
+ * design": the denoiser's parameters; [P4] "Gemma-based MoE backbone"):
+ * d_weights holds the same dg_weights_bytes bytes in the same layout (a
+ * device-to-device copy of the current buffer, or a buffer filled the same
+ * way), 256-byte aligned, caller-owned, and must outlive its use. Waits for
+ * the device and drops the captured step graphs (the next step re-captures);
+ * the KV cache, workspace and every other setting are kept. The old buffer
+ * is no longer read once this returns. Errors: DG_ERR_INVALID for NULL or a
+ * misaligned pointer. Use: the streaming speed of a weight buffer depends on
+ * where its allocation lies in device memory and stays with the allocation,
+ * so a caller may time a few copies and keep the fastest. */
+int dg_ctx_set_weights(dg_ctx* ctx, void* d_weights);
 /* Compute the routed experts from a filled FP8 expert buffer (see
  * dg_quantize_experts_fp8; it must outlive its use and stay unmodified while
  * steps run) in every later prefill, step and commit; NULL returns to the
