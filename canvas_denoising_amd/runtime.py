@@ -119,9 +119,13 @@ class Model:
         How fast the weight streams run depends on where their allocation lies in device memory, and
         an allocation keeps its speed. The current buffer and tries - 1 device copies are each timed
         with measure() (seconds, lower is better; it runs model work and synchronizes), the fastest
-        is kept and the others are freed. Returns (times, index of the kept buffer)."""
+        is kept and the others are freed (fewer copies when device memory would not hold another with
+        1 GiB to spare). Returns (times, index of the kept buffer)."""
         cands, times = [self.weights], [float(measure())]
         for _ in range(1, tries):
+            free, _total = torch.cuda.mem_get_info(self.weights.device)
+            if free < self.weights.numel() + (1 << 30):  # no room for another copy: keep the best so far
+                break
             cands.append(torch.empty_like(self.weights))
             cands[-1].copy_(self.weights)
             torch.cuda.synchronize()
