@@ -735,7 +735,7 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=2048,
                     help="rows per prefill chunk (0 = the canvas); chunks above 256 rows run the experts as "
                          "token-tiled GEMMs")
-    ap.add_argument("--placement-tries", type=int, default=3,
+    ap.add_argument("--placement-tries", type=int, default=4,
                     help="full workload: allocations of the weights timed at load time (the fastest is kept); "
                          "1 keeps the first")
     ap.add_argument("--sampler-records", choices=["lm_head", "pass"], default="pass",
