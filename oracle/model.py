@@ -20,7 +20,7 @@ What the pages fix:
 
 Readings where the pages are silent (parity of these against the real model
 is unpinned; they are internal definitions shared with the HIP path and
-listed in the design doc): pre-norm RMSNorm (unit gain, eps) before attention, before the MoE and before
+listed with the project's design notes): pre-norm RMSNorm (unit gain, eps) before attention, before the MoE and before
 the LM head; no positional encoding by default (rope_theta = 0), or, as an
 option, rotary position embedding of queries and keys at their cache
 positions (see rope below); no biases; attention scale 1/sqrt(hd);

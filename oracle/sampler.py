@@ -13,7 +13,7 @@ Sources:
 * [P4] "Reverse diffusion process": keep confident tokens, re-noise the
   others, re-evaluate the whole canvas every step (nothing is frozen).
 
-Readings taken where the pages are silent (listed again in the design doc):
+Readings taken where the pages are silent (also listed with the project's design notes):
 * temperature index runs over the step budget: T(s) = t0 + (t1 - t0) s/(S-1),
   evaluated in double and rounded once to float32 (T(0)=t0, T(S-1)=t1);
 * entropy in nats of the tempered distribution softmax(l / T);
