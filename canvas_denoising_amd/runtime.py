@@ -107,7 +107,8 @@ class Model:
         L.dg_load_weight(self.desc, kind, layer, expert, src, self.weights)
 
     def set_weights(self, weights: torch.Tensor):
-        """Compute from another buffer holding the same weights (dg_ctx_set_weights)."""
+        """Compute from another buffer holding the same weights (dg_ctx_set_weights); views taken
+        earlier with tensor() then refer to the old buffer."""
         if weights.dtype != torch.uint8 or weights.numel() != self.weights.numel() or not weights.is_cuda:
             raise ValueError("expected a uint8 CUDA buffer of dg_weights_bytes bytes")
         L.dg_ctx_set_weights(self.ctx, weights)
@@ -120,7 +121,8 @@ class Model:
         an allocation keeps its speed. The current buffer and tries - 1 device copies are each timed
         with measure() (seconds, lower is better; it runs model work and synchronizes), the fastest
         is kept and the others are freed (fewer copies when device memory would not hold another with
-        1 GiB to spare). Returns (times, index of the kept buffer)."""
+        1 GiB to spare). Views taken earlier with tensor() keep the buffer they came from alive and no
+        longer reach the model; take them again afterwards. Returns (times, index of the kept buffer)."""
         cands, times = [self.weights], [float(measure())]
         for _ in range(1, tries):
             free, _total = torch.cuda.mem_get_info(self.weights.device)
